@@ -1,0 +1,138 @@
+"""CPU oracle for the libred reductions (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The GPU library neither imports nor links it, and the
+two share no code. The arithmetic lives in oracle.c (plain C, float64
+compensated sum, exact int64 sum, scalar max loop); this module only loads
+it and marshals numpy arrays.
+
+Acceptance rule used with it (per row for the row-segmented forms): float
+sums within |gpu - S| <= 1e-5 * sum|x_i| + 1e-6, integers bit-exact, max
+exact by value.
+"""
+import ctypes
+import math
+import os
+
+import numpy as np
+
+from . import build as _build
+
+
+def _as(x, dtype):
+    a = np.asarray(x)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return np.ascontiguousarray(a)
+
+
+class Oracle:
+    """The oracle functions bound to one compiled copy of oracle.c."""
+
+    def __init__(self, libpath):
+        lib = ctypes.CDLL(libpath)
+        P = ctypes.c_void_p
+        Z = ctypes.c_size_t
+        D = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_sum_f32.argtypes = [P, Z, D, D]
+        lib.oracle_sum_f32.restype = None
+        lib.oracle_sum_i32_i64.argtypes = [P, Z]
+        lib.oracle_sum_i32_i64.restype = ctypes.c_int64
+        lib.oracle_max_f32.argtypes = [P, Z]
+        lib.oracle_max_f32.restype = ctypes.c_float
+        lib.oracle_rows_sum_f32.argtypes = [P, Z, Z, P, P]
+        lib.oracle_rows_sum_f32.restype = None
+        lib.oracle_rows_max_f32.argtypes = [P, Z, Z, P]
+        lib.oracle_rows_max_f32.restype = None
+        self.lib = lib
+        self.path = libpath
+
+    def sum_f32(self, x):
+        """Return (S, A): the float64 compensated sum of float32 x, and sum|x|."""
+        a = _as(x, np.float32).ravel()
+        s = ctypes.c_double()
+        ab = ctypes.c_double()
+        self.lib.oracle_sum_f32(a.ctypes.data, a.size, ctypes.byref(s), ctypes.byref(ab))
+        return s.value, ab.value
+
+    def sum_i32_i64(self, x):
+        """Return the exact int64 sum of int32 x as a Python int."""
+        a = _as(x, np.int32).ravel()
+        return int(self.lib.oracle_sum_i32_i64(a.ctypes.data, a.size))
+
+    def max_f32(self, x):
+        """Return the float32 maximum of x (NaN never wins; empty gives -inf)."""
+        a = _as(x, np.float32).ravel()
+        return np.float32(self.lib.oracle_max_f32(a.ctypes.data, a.size))
+
+    def rows_sum_f32(self, x):
+        """Per-row (S, A) of a 2-D float32 array: two float64 arrays."""
+        a = _as(x, np.float32)
+        if a.ndim != 2:
+            raise ValueError("rows_sum_f32 needs a 2-D array")
+        rows, cols = a.shape
+        s = np.empty(rows, np.float64)
+        ab = np.empty(rows, np.float64)
+        self.lib.oracle_rows_sum_f32(a.ctypes.data, rows, cols, s.ctypes.data, ab.ctypes.data)
+        return s, ab
+
+    def rows_max_f32(self, x):
+        """Per-row float32 maximum of a 2-D float32 array."""
+        a = _as(x, np.float32)
+        if a.ndim != 2:
+            raise ValueError("rows_max_f32 needs a 2-D array")
+        rows, cols = a.shape
+        out = np.empty(rows, np.float32)
+        self.lib.oracle_rows_max_f32(a.ctypes.data, rows, cols, out.ctypes.data)
+        return out
+
+
+_default = None
+
+
+def default():
+    """The oracle built from oracle.c in this directory (built if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def sum_f32(x):
+    return default().sum_f32(x)
+
+
+def sum_i32_i64(x):
+    return default().sum_i32_i64(x)
+
+
+def max_f32(x):
+    return default().max_f32(x)
+
+
+def rows_sum_f32(x):
+    return default().rows_sum_f32(x)
+
+
+def rows_max_f32(x):
+    return default().rows_max_f32(x)
+
+
+def sum_within_tolerance(gpu, S, A):
+    """The float-sum acceptance rule: |gpu - S| <= 1e-5*A + 1e-6 (in float64).
+
+    A non-finite S must be matched exactly (NaN by NaN, an infinity by the
+    same infinity)."""
+    g = float(gpu)
+    if math.isnan(S):
+        return math.isnan(g)
+    if math.isinf(S):
+        return g == S
+    return abs(g - S) <= 1e-5 * A + 1e-6
+
+
+def max_equal(gpu, expect):
+    """Max acceptance: equal by value (so -0 == +0); -inf must match -inf."""
+    return float(gpu) == float(expect)

@@ -1,0 +1,133 @@
+/*
+ * oracle.c -- CPU oracle for the libred reductions.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this code. The GPU library does not
+ * include, link or call it, and it shares no source with the GPU library.
+ *
+ * It is plain, slow and single-threaded on purpose. Each function states the
+ * definition it computes and the passage of the pages it follows:
+ *
+ *   [lesson] "03_shared_memory_sync_reduction.py -- shared memory, banks,
+ *            synchronisation and parallel reduction" (CS349E prereq P2),
+ *            demo 3 (parallel reduction): reduce n float32 values to one sum.
+ *            The page checks its GPU-style result against the float64 sum of
+ *            the same float32 inputs.
+ *   [simt]   "simt.py -- a SIMT GPU simulator in Python" (CMU 11-868
+ *            lecture 2), section 2 (device memory), DeviceArray.atomic_max:
+ *            the stored value is replaced only when the new value is strictly
+ *            greater.
+ *
+ * Build: gcc -O2 -std=c99 -fPIC -shared, never with -ffast-math (that would
+ * let the compiler delete the compensation term of the compensated sum).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+/*
+ * Sum of n float32 values, as the real sum of the inputs.
+ *
+ * Definition: S = x_0 + x_1 + ... + x_{n-1} over the reals ([lesson], demo 3,
+ * where the expected value is the float64 sum of the float32 inputs).
+ * Evaluation: each input is widened to double (exactly) and added with
+ * Neumaier's compensated summation (Neumaier 1974, "Rundungsfehleranalyse
+ * einiger Verfahren zur Summation endlicher Summen"): a running sum s and a
+ * running correction c that collects the low-order bits each addition
+ * loses. Whichever operand of s + x is larger in magnitude is the one whose
+ * low bits survive, so the lost part is recovered from the other one.
+ * The error of s + c is at most about one rounding of |S| plus a term of
+ * order n * eps^2 * sum|x_i|, far below the tolerance this sum is used for.
+ *
+ * Non-finite inputs follow IEEE arithmetic on the real sum: any NaN, or both
+ * +inf and -inf, gives NaN; otherwise an infinity of one sign gives that
+ * infinity. They are counted apart, since the compensation term itself
+ * would turn into NaN on an infinity.
+ *
+ * *abs_sum receives sum |x_i| over the finite inputs in plain double
+ * arithmetic (used only to scale a tolerance). n == 0 gives 0 and 0.
+ */
+static void neumaier_f32(const float *x, size_t n, double *sum, double *abs_sum)
+{
+    double s = 0.0, c = 0.0, a = 0.0;
+    int saw_nan = 0, saw_pinf = 0, saw_ninf = 0;
+    size_t i;
+
+    for (i = 0; i < n; ++i) {
+        double v = (double)x[i];
+        double t;
+        if (isnan(v)) { saw_nan = 1; continue; }
+        if (isinf(v)) {
+            if (v > 0) saw_pinf = 1; else saw_ninf = 1;
+            continue;
+        }
+        a += fabs(v);
+        t = s + v;
+        if (fabs(s) >= fabs(v))
+            c += (s - t) + v;   /* v's low bits were lost */
+        else
+            c += (v - t) + s;   /* s's low bits were lost */
+        s = t;
+    }
+    if (abs_sum) *abs_sum = a;
+    if (saw_nan || (saw_pinf && saw_ninf)) *sum = NAN;
+    else if (saw_pinf) *sum = INFINITY;
+    else if (saw_ninf) *sum = -INFINITY;
+    else *sum = s + c;
+}
+
+void oracle_sum_f32(const float *x, size_t n, double *sum, double *abs_sum)
+{
+    neumaier_f32(x, n, sum, abs_sum);
+}
+
+/*
+ * Sum of n int32 values, exact, as a 64-bit integer ([lesson], demo 3's
+ * reduction applied to integers). Accumulated in uint64_t so that a sum
+ * outside the int64 range wraps modulo 2^64 instead of being undefined;
+ * with |x_i| <= 2^31 that cannot happen for n < 2^32.
+ */
+int64_t oracle_sum_i32_i64(const int32_t *x, size_t n)
+{
+    uint64_t s = 0;
+    size_t i;
+    for (i = 0; i < n; ++i)
+        s += (uint64_t)(int64_t)x[i];
+    return (int64_t)s;
+}
+
+/*
+ * Maximum of n float32 values ([simt], section 2, DeviceArray.atomic_max:
+ * the running value is replaced only by a strictly greater one). Start from
+ * -inf. A NaN compares false, so it never replaces the running maximum; an
+ * empty or all-NaN input gives -inf. Ties keep the earlier value.
+ */
+float oracle_max_f32(const float *x, size_t n)
+{
+    float m = -INFINITY;
+    size_t i;
+    for (i = 0; i < n; ++i)
+        if (x[i] > m) m = x[i];
+    return m;
+}
+
+/*
+ * Row-segmented forms: x is rows x cols, row-major and contiguous (row r is
+ * x[r*cols .. r*cols + cols)). Each row is reduced on its own with the
+ * definitions above ([lesson], demo 3: one output per segment). rows == 0
+ * writes nothing; cols == 0 gives the empty-row values (0, 0, -inf).
+ */
+void oracle_rows_sum_f32(const float *x, size_t rows, size_t cols,
+                         double *sum, double *abs_sum)
+{
+    size_t r;
+    for (r = 0; r < rows; ++r)
+        neumaier_f32(x + r * cols, cols, &sum[r], abs_sum ? &abs_sum[r] : NULL);
+}
+
+void oracle_rows_max_f32(const float *x, size_t rows, size_t cols, float *out)
+{
+    size_t r;
+    for (r = 0; r < rows; ++r)
+        out[r] = oracle_max_f32(x + r * cols, cols);
+}
