@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of libred on one MI355X.
+
+Headline: achieved HBM GB/s of red_sum_f32 over 2^28 float32 elements
+(1 GiB, normal(0,1), seed 2), as a fraction of the 8 TB/s HBM3E peak. One
+step is one red_sum_f32 call over the resident array (load, peel, wave
+reduce, LDS combine, partial, last-block combine: the whole path in one
+kernel). The line also carries the roofline of that kernel, the CPU oracle
+timed on the host, and the other entry points at their own workloads.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
+METRIC = "achieved HBM GB/s (% of MI355X peak) for f32 sum over 2^28 elements"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["reduction_libred_amd/csrc/flat_reduce.hip",
+                  "reduction_libred_amd/csrc/device_common.hpp",
+                  "reduction_libred_amd/csrc/libred.cpp"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the sum kernel from the committed counter
+    runs, or None if the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("sum_f32_2p28_bytes_per_launch")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only: skip the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time budget of the CPU oracle baseline (0 to skip)")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on one stream around a region of `reps` enqueued calls."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def region_ms(self, fn, reps):
+        t = self.torch
+        e0 = t.cuda.Event(enable_timing=True)
+        e1 = t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(reps):
+            fn()
+        e1.record(self.stream)
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def per_launch_ms(self, fn, reps):
+        t = self.torch
+        ev = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        t.cuda.synchronize()
+        for a, b in ev:
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+        t.cuda.synchronize()
+        d = sorted(a.elapsed_time(b) for a, b in ev)
+        return d[len(d) // 2], d[0]
+
+
+def gbps(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the multi-GPU sharding is a design note, not code).", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import reduction_libred_amd as rl
+
+    if not os.path.exists(rl.LIB_PATH):
+        from reduction_libred_amd import build as lib_build
+        lib_build.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    timer = Timer(torch, stream)
+    cu, arch = rl.red_device_info()
+    log(f"device: {torch.cuda.get_device_name(dev)} {arch}, {cu} CUs; {rl.red_version()}")
+
+    # ---------------------------------------------------------- headline
+    name = "sum_max_f32_2p28"
+    log(f"generate {name}")
+    a = W.workload(name)
+    n = a.size
+    x = torch.from_numpy(a).to(dev)
+    out = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    policy = rl.red_default_flat_policy().as_dict()
+    grid = rl.red_flat_grid(n)
+    nbytes = 4 * n + 4
+
+    def step():
+        rl.red_sum_f32(x, out=out)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    eager = out.item()
+    log(f"timed {args.steps} steps")
+    ms = timer.region_ms(step, args.steps)
+    if out.item() != eager:
+        raise RuntimeError("red_sum_f32 is not reproducible run to run")
+    value = gbps(nbytes, ms)
+    med_ms, min_ms = timer.per_launch_ms(step, max(20, min(args.steps, 200)))
+    log(f"red_sum_f32: {ms * 1e3:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of peak); "
+        f"per-launch median {med_ms * 1e3:.1f} us")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": "sum_max_f32_2p28: float32 sum of 2^28 elements (1 GiB), normal(0,1), seed 2",
+            "n": n,
+            "entry_point": "red_sum_f32",
+            "input_dtype": "f32",
+            "accumulate_dtype": "f64",
+            "policy": policy,
+            "grid": grid,
+            "device": arch,
+            "cus": cu,
+        },
+        "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "elements_per_s": round(n / (ms * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(value, 2),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(value / PEAK_GBPS, 4),
+            "traffic": recorded_traffic(),
+            "kernel": f"flat_reduce_kernel<SumF32, {policy['block']}, {policy['unroll']}, "
+                      f"{'true' if policy['nontemporal'] else 'false'}>",
+            "algorithmic_bytes_per_launch": nbytes,
+            "avg_launch_us": round(ms * 1e3, 3),
+            "median_launch_us_events": round(med_ms * 1e3, 3),
+            "min_launch_us_events": round(min_ms * 1e3, 3),
+        },
+    }
+
+    # ---------------------------------------------------------- other entry points
+    others = {}
+    reps = 50
+
+    def measure(label, fn, nbytes_call, extra=None):
+        for _ in range(3):
+            fn()
+        t_ms = timer.region_ms(fn, reps)
+        rec = {"us": round(t_ms * 1e3, 3), "GB/s": round(gbps(nbytes_call, t_ms), 2),
+               "pct_of_peak": round(100 * gbps(nbytes_call, t_ms) / PEAK_GBPS, 2)}
+        if extra:
+            rec.update(extra)
+        others[label] = rec
+        log(f"{label}: {rec}")
+
+    mout = torch.empty((), dtype=torch.float32, device=dev)
+    measure("red_max_f32 sum_max_f32_2p28", lambda: rl.red_max_f32(x, out=mout), nbytes)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    measure("probe read sum_max_f32_2p28", lambda: rl.red_probe_read_f32(x, sink=sink), 4 * n)
+    y = torch.empty_like(x)
+    measure("probe copy sum_max_f32_2p28", lambda: rl.red_probe_copy_f32(x, y), 8 * n)
+    del y
+
+    if not args.quick:
+        # Rows: 65536 x 4096.
+        name4 = "rows_f32_65536x4096"
+        log(f"generate {name4}")
+        x4 = torch.from_numpy(W.workload(name4)).to(dev)
+        r4 = torch.empty(x4.shape[0], dtype=torch.float32, device=dev)
+        b4 = 4 * x4.numel() + 4 * x4.shape[0]
+        measure(f"red_rows_sum_f32 {name4}", lambda: rl.red_rows_sum_f32(x4, out=r4), b4)
+        measure(f"red_rows_max_f32 {name4}", lambda: rl.red_rows_max_f32(x4, out=r4), b4)
+        del x4
+
+        # Small, cache-resident sizes: batched (a HIP graph of 100 calls,
+        # replays checked against the eager result) and cold (a rotation
+        # over copies that together exceed the 256 MB Infinity Cache).
+        for name_s, fn_s, odt in (("sum_f32_2p20", rl.red_sum_f32, torch.float32),
+                                  ("sum_i32_2p24", rl.red_sum_i32_i64, torch.int64)):
+            log(f"generate {name_s}")
+            xs = torch.from_numpy(W.workload(name_s)).to(dev)
+            os_ = torch.empty((), dtype=odt, device=dev)
+            bs = xs.element_size() * xs.numel() + os_.element_size()
+            fn_s(xs, out=os_)
+            torch.cuda.synchronize()
+            eager_s = os_.item()
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                fn_s(xs, out=os_)          # workspace of the capture stream exists before capture
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=cap):
+                    for _ in range(100):
+                        fn_s(xs, out=os_)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                os_.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                if os_.item() != eager_s:
+                    raise RuntimeError(f"graph replay of {name_s} differs from the eager result")
+            t_ms = timer.region_ms(g.replay, 10) / 100
+            copies = max(2, -(-(1 << 30) // (bs - os_.element_size())))
+            xc = [xs.clone() for _ in range(copies)]
+            it = iter(range(1 << 30))
+            cold_ms = timer.region_ms(lambda: fn_s(xc[next(it) % copies], out=os_), 4 * copies)
+            others[f"{fn_s.__name__} {name_s}"] = {
+                "batched_us": round(t_ms * 1e3, 3),
+                "batched_GB/s": round(gbps(bs, t_ms), 2),
+                "cold_us": round(cold_ms * 1e3, 3),
+                "cold_GB/s": round(gbps(bs, cold_ms), 2),
+                "note": "fits in the 256 MB Infinity Cache; batched = 100 calls in one HIP graph",
+            }
+            log(f"{fn_s.__name__} {name_s}: {others[f'{fn_s.__name__} {name_s}']}")
+            del xc, xs
+
+        name5 = "sum_f32_1e9p7"
+        log(f"generate {name5}")
+        a5 = W.workload(name5)
+        x5 = torch.from_numpy(a5).to(dev)
+        del a5
+        o5 = torch.empty((), dtype=torch.float32, device=dev)
+        measure(f"red_sum_f32 {name5}", lambda: rl.red_sum_f32(x5, out=o5), 4 * x5.numel() + 4)
+        del x5
+        torch.cuda.empty_cache()
+    result["other_entry_points"] = others
+
+    # ---------------------------------------------------------- CPU oracle
+    if args.cpu_seconds > 0:
+        import oracle
+
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        passes = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.sum_f32(a)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        result["cpu_baseline"] = {
+            "value": round(gbps(nbytes * passes, el * 1e3), 3),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the single-threaded oracle (float64 Neumaier sum) "
+                      f"over the same 2^28-element host array, {el:.1f} s",
+            "host_cpu": _cpu_model(),
+            "host_threads": os.cpu_count(),
+        }
+    print(json.dumps(result), flush=True)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+if __name__ == "__main__":
+    main()

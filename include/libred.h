@@ -1,0 +1,125 @@
+/*
+ * libred.h -- block-level parallel reductions for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one the reduction lesson develops step by step
+ * ("03_shared_memory_sync_reduction.py -- shared memory, banks,
+ * synchronisation and parallel reduction", demo 3): reduce n values to one,
+ * with each thread block producing a partial and the partials then combined.
+ * Here the whole reduction, including the combine, runs on the GPU.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All data pointers are DEVICE pointers (memory of the current HIP device,
+ *    e.g. from hipMalloc or a PyTorch CUDA tensor). The caller allocates and
+ *    frees them; the library never frees caller memory.
+ *  - Inputs are contiguous, element-aligned arrays (4-byte aligned for float
+ *    and int32; 8-byte aligned for the int64 output). Any such address is
+ *    accepted: the 16-byte vector body is peeled internally.
+ *  - Lengths are size_t; at most RED_MAX_N elements per call.
+ *  - Calls are asynchronous: work is enqueued on `stream` (0 = the null
+ *    stream) and the call returns without waiting. The result is valid once
+ *    the stream has reached that point. A fault in a kernel surfaces at the
+ *    caller's next synchronisation.
+ *  - Argument errors are reported as RED_ERR_INVALID_ARG before any HIP call
+ *    is made: a null input with a non-zero length, a null output, a
+ *    misaligned pointer, an output that overlaps the input, a length above
+ *    RED_MAX_N, or rows * cols overflowing. Nothing is enqueued then.
+ *  - The single-value entry points use a small workspace owned by the library
+ *    (block partials plus a completion counter), allocated on the first call
+ *    per (device, stream) and kept until the process exits. Calls on one
+ *    stream are ordered, so they can share it; calls on different streams use
+ *    different workspaces and may run concurrently.
+ *  - Results are deterministic: for a given length and device the partials
+ *    are combined in a fixed index order, so repeated calls return the same
+ *    bits.
+ *  - Nothing throws across this interface.
+ */
+#ifndef LIBRED_H_
+#define LIBRED_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum red_status {
+    RED_OK = 0,
+    RED_ERR_INVALID_ARG = 1, /* bad pointer, length, shape or alignment */
+    RED_ERR_NO_DEVICE = 2,   /* no usable HIP device is current */
+    RED_ERR_HIP = 3,         /* a HIP call or kernel launch failed; see red_last_hip_error */
+    RED_ERR_ALLOC = 4        /* the library workspace could not be allocated */
+} red_status;
+
+/* Largest element count accepted by one call (2^40 elements, 4 TiB of float). */
+#define RED_MAX_N ((size_t)1 << 40)
+
+/*
+ * Sum of n float32 values: *out = x[0] + ... + x[n-1], rounded once to float.
+ *
+ * The reduction lesson's demo 3 computes this sum with block partials and
+ * checks it against the float64 sum of the same inputs. Here every element
+ * is widened to float64 as it is loaded and all partials stay in float64, so
+ * the only float32 rounding is the final one; the result is within about one
+ * float32 rounding of the exact sum (far inside |error| <= 1e-5 * sum|x|).
+ * NaN or infinite inputs follow IEEE arithmetic. n == 0 stores 0.0f (x may
+ * then be NULL).
+ */
+red_status red_sum_f32(const float *x, size_t n, float *out, hipStream_t stream);
+
+/*
+ * Sum of n int32 values into one int64: *out = x[0] + ... + x[n-1], exact
+ * (each element is sign-extended to 64 bits before it is added). The sum
+ * wraps modulo 2^64 only if it leaves the int64 range, which needs n > 2^32.
+ * n == 0 stores 0.
+ */
+red_status red_sum_i32_i64(const int32_t *x, size_t n, int64_t *out, hipStream_t stream);
+
+/*
+ * Maximum of n float32 values. The running maximum is replaced only by a
+ * strictly greater value (the rule of the SIMT simulator page "simt.py",
+ * section 2, DeviceArray.atomic_max), starting from -inf: a NaN never
+ * wins, and an empty or all-NaN input gives -inf. Between -0 and +0 either
+ * may be returned; they compare equal.
+ */
+red_status red_max_f32(const float *x, size_t n, float *out, hipStream_t stream);
+
+/*
+ * Per-row sum of a rows x cols float32 matrix stored row-major and
+ * contiguously (row r is x[r*cols .. r*cols + cols)):
+ * out[r] = x[r*cols] + ... + x[r*cols + cols - 1], for r < rows.
+ * One output per segment, as the lesson's block partials are one output
+ * per block. Accumulated in float64, rounded once per row. rows == 0 does
+ * nothing (out may be NULL); cols == 0 stores 0.0f in every out[r]. The
+ * library workspace is not used.
+ */
+red_status red_rows_sum_f32(const float *x, size_t rows, size_t cols, float *out,
+                            hipStream_t stream);
+
+/*
+ * Per-row maximum of the same layout, with the rule of red_max_f32 applied
+ * to each row; cols == 0 stores -inf in every out[r].
+ */
+red_status red_rows_max_f32(const float *x, size_t rows, size_t cols, float *out,
+                            hipStream_t stream);
+
+/* A static, human-readable name for a status code. */
+const char *red_status_string(red_status status);
+
+/*
+ * The last hipError_t seen by a red_* call that returned RED_ERR_HIP,
+ * RED_ERR_ALLOC or RED_ERR_NO_DEVICE on the calling thread (0 if none).
+ */
+int red_last_hip_error(void);
+
+/* Library version string, e.g. "libred 0.1.0 gfx950". */
+const char *red_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRED_H_ */

@@ -1,0 +1,37 @@
+/*
+ * libred_probe.h -- measurement probes and device facts.
+ *
+ * The simulator page ("simt_lab.py -- a numpy-simulated GPU", section 6,
+ * estimate_time) bounds a kernel's time below by its memory traffic over the
+ * device's bandwidth. These probes measure the two figures that bound needs
+ * on real hardware: what a plain copy of known size reads and writes (to
+ * scale hardware byte counters), and how fast a read-only stream runs.
+ * Conventions are those of libred.h.
+ */
+#ifndef LIBRED_PROBE_H_
+#define LIBRED_PROBE_H_
+
+#include "libred.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* y[i] = x[i] for i < n. x and y must be 16-byte aligned and must not
+ * overlap. */
+red_status red_probe_copy_f32(const float *x, float *y, size_t n, hipStream_t stream);
+
+/* Reads every 32-bit word of x[0..n) once and writes nothing unless the data
+ * hash to a fixed value (then one word at *sink). x and sink must be 16- and
+ * 4-byte aligned. */
+red_status red_probe_read_f32(const float *x, size_t n, unsigned int *sink, hipStream_t stream);
+
+/* Facts about the current device: compute-unit count and architecture name
+ * (e.g. "gfx950:sramecc+:xnack-"), copied into arch[0..arch_len). */
+red_status red_device_info(int *cu_count, char *arch, size_t arch_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBRED_PROBE_H_ */

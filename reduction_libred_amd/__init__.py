@@ -1,0 +1,267 @@
+"""libred: block-level parallel reductions on AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of libred.so (include/libred.h,
+include/libred_ablate.h, include/libred_probe.h). Each function here has the
+name of the C entry point it calls and only marshals arguments: it takes
+PyTorch tensors on a ROCm device (PyTorch supplies device memory and
+streams), passes their data pointers, sizes and a hipStream_t, and raises
+RedError on a non-zero status. Every step of every reduction runs in the HIP
+kernels of libred.so; there is no other implementation behind this module.
+
+The call is asynchronous on the stream (default: PyTorch's current stream of
+the tensor's device); the output tensor is ready once that stream is.
+"""
+import ctypes
+import os
+
+import torch  # first: the HIP runtime PyTorch loads is the one libred.so binds to
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libred.so")
+
+RED_OK = 0
+RED_ERR_INVALID_ARG = 1
+RED_ERR_NO_DEVICE = 2
+RED_ERR_HIP = 3
+RED_ERR_ALLOC = 4
+RED_MAX_N = 1 << 40
+
+
+class RedError(RuntimeError):
+    """A red_* call returned a non-zero red_status."""
+
+    def __init__(self, name, status, hip_error):
+        self.status = status
+        self.hip_error = hip_error
+        msg = lib().red_status_string(status).decode()
+        super().__init__(f"{name}: {msg} (hip error {hip_error})")
+
+
+class FlatPolicy(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int), ("blocks_per_cu", ctypes.c_int),
+                ("unroll", ctypes.c_int), ("nontemporal", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class RowsPolicy(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int), ("unroll", ctypes.c_int),
+                ("nontemporal", ctypes.c_int), ("max_blocks", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_P = ctypes.c_void_p
+_Z = ctypes.c_size_t
+_I = ctypes.c_int
+_S = ctypes.c_int  # red_status
+
+# name -> (restype, argtypes): every entry point declared in include/*.h.
+SIGNATURES = {
+    "red_sum_f32": (_S, [_P, _Z, _P, _P]),
+    "red_sum_i32_i64": (_S, [_P, _Z, _P, _P]),
+    "red_max_f32": (_S, [_P, _Z, _P, _P]),
+    "red_rows_sum_f32": (_S, [_P, _Z, _Z, _P, _P]),
+    "red_rows_max_f32": (_S, [_P, _Z, _Z, _P, _P]),
+    "red_status_string": (ctypes.c_char_p, [_S]),
+    "red_last_hip_error": (_I, []),
+    "red_version": (ctypes.c_char_p, []),
+    "red_ablate_sum_f32": (_S, [_I, _P, _Z, _P, _Z, _P, _P]),
+    "red_ablate_num_partials": (_Z, [_I, _Z]),
+    "red_default_flat_policy": (None, [ctypes.POINTER(FlatPolicy)]),
+    "red_default_rows_policy": (None, [ctypes.POINTER(RowsPolicy)]),
+    "red_flat_grid": (_Z, [_Z, ctypes.POINTER(FlatPolicy)]),
+    "red_sum_f32_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
+    "red_sum_i32_i64_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
+    "red_max_f32_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
+    "red_rows_sum_f32_with": (_S, [_P, _Z, _Z, _P, ctypes.POINTER(RowsPolicy), _P]),
+    "red_rows_max_f32_with": (_S, [_P, _Z, _Z, _P, ctypes.POINTER(RowsPolicy), _P]),
+    "red_probe_copy_f32": (_S, [_P, _P, _Z, _P]),
+    "red_probe_read_f32": (_S, [_P, _Z, _P, _P]),
+    "red_device_info": (_S, [ctypes.POINTER(_I), ctypes.c_char_p, _Z]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libred.so with argument types set. Raises ImportError if the
+    library has not been built (python -m reduction_libred_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run: python -m reduction_libred_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(name, status):
+    if status != RED_OK:
+        raise RedError(name, status, lib().red_last_hip_error())
+
+
+def _stream_handle(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _input(x, dtype, name):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise TypeError(f"{name}: input must be a tensor on a ROCm device")
+    if x.dtype != dtype:
+        raise TypeError(f"{name}: input dtype must be {dtype}, got {x.dtype}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: input must be contiguous")
+
+
+def _output(out, shape, dtype, device, name):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if out.dtype != dtype or out.device != device or out.numel() != int(torch.Size(shape).numel()):
+        raise ValueError(f"{name}: out must be {dtype} with {torch.Size(shape).numel()} elements on {device}")
+    if not out.is_contiguous():
+        raise ValueError(f"{name}: out must be contiguous")
+    return out
+
+
+def _policy(cls, p):
+    if p is None or isinstance(p, cls):
+        return p
+    return cls(**p)
+
+
+def _flat(name, cname, x, out, in_dtype, out_dtype, stream, policy=None):
+    _input(x, in_dtype, name)
+    out = _output(out, (), out_dtype, x.device, name)
+    with torch.cuda.device(x.device):
+        s = _stream_handle(stream, x.device)
+        if policy is None:
+            st = getattr(lib(), cname)(x.data_ptr(), x.numel(), out.data_ptr(), s)
+        else:
+            p = _policy(FlatPolicy, policy)
+            st = getattr(lib(), cname + "_with")(x.data_ptr(), x.numel(), out.data_ptr(),
+                                                 ctypes.byref(p), s)
+    _check(cname, st)
+    return out
+
+
+def red_sum_f32(x, out=None, stream=None, policy=None):
+    """Sum of a float32 tensor into a 0-d float32 tensor (float64 inside)."""
+    return _flat("red_sum_f32", "red_sum_f32", x, out, torch.float32, torch.float32, stream, policy)
+
+
+def red_sum_i32_i64(x, out=None, stream=None, policy=None):
+    """Exact sum of an int32 tensor into a 0-d int64 tensor."""
+    return _flat("red_sum_i32_i64", "red_sum_i32_i64", x, out, torch.int32, torch.int64, stream, policy)
+
+
+def red_max_f32(x, out=None, stream=None, policy=None):
+    """Maximum of a float32 tensor (NaN never wins; empty gives -inf)."""
+    return _flat("red_max_f32", "red_max_f32", x, out, torch.float32, torch.float32, stream, policy)
+
+
+def _rows(cname, x, out, stream, policy):
+    _input(x, torch.float32, cname)
+    if x.dim() != 2:
+        raise ValueError(f"{cname}: input must be 2-D (rows, cols)")
+    rows, cols = x.shape
+    out = _output(out, (rows,), torch.float32, x.device, cname)
+    with torch.cuda.device(x.device):
+        s = _stream_handle(stream, x.device)
+        if policy is None:
+            st = getattr(lib(), cname)(x.data_ptr(), rows, cols, out.data_ptr(), s)
+        else:
+            p = _policy(RowsPolicy, policy)
+            st = getattr(lib(), cname + "_with")(x.data_ptr(), rows, cols, out.data_ptr(),
+                                                 ctypes.byref(p), s)
+    _check(cname, st)
+    return out
+
+
+def red_rows_sum_f32(x, out=None, stream=None, policy=None):
+    """Per-row sum of a 2-D row-major float32 tensor -> float32[rows]."""
+    return _rows("red_rows_sum_f32", x, out, stream, policy)
+
+
+def red_rows_max_f32(x, out=None, stream=None, policy=None):
+    """Per-row max of a 2-D row-major float32 tensor -> float32[rows]."""
+    return _rows("red_rows_max_f32", x, out, stream, policy)
+
+
+def red_ablate_num_partials(rung, n):
+    return int(lib().red_ablate_num_partials(rung, n))
+
+
+def red_ablate_sum_f32(rung, x, partials=None, out=None, stream=None):
+    """Ablation rung 1..6 of the f32 sum. Returns (out, partials)."""
+    _input(x, torch.float32, "red_ablate_sum_f32")
+    n = x.numel()
+    np_ = max(red_ablate_num_partials(rung, n), 1)
+    if partials is None:
+        partials = torch.empty(np_, dtype=torch.float32, device=x.device)
+    out = _output(out, (), torch.float32, x.device, "red_ablate_sum_f32")
+    with torch.cuda.device(x.device):
+        st = lib().red_ablate_sum_f32(rung, x.data_ptr(), n, partials.data_ptr(), partials.numel(),
+                                      out.data_ptr(), _stream_handle(stream, x.device))
+    _check("red_ablate_sum_f32", st)
+    return out, partials
+
+
+def red_default_flat_policy():
+    p = FlatPolicy()
+    lib().red_default_flat_policy(ctypes.byref(p))
+    return p
+
+
+def red_default_rows_policy():
+    p = RowsPolicy()
+    lib().red_default_rows_policy(ctypes.byref(p))
+    return p
+
+
+def red_flat_grid(n, policy=None):
+    p = _policy(FlatPolicy, policy)
+    return int(lib().red_flat_grid(n, ctypes.byref(p) if p is not None else None))
+
+
+def red_probe_copy_f32(x, y, stream=None):
+    _input(x, torch.float32, "red_probe_copy_f32")
+    _input(y, torch.float32, "red_probe_copy_f32")
+    if y.numel() != x.numel():
+        raise ValueError("red_probe_copy_f32: x and y differ in size")
+    with torch.cuda.device(x.device):
+        st = lib().red_probe_copy_f32(x.data_ptr(), y.data_ptr(), x.numel(), _stream_handle(stream, x.device))
+    _check("red_probe_copy_f32", st)
+    return y
+
+
+def red_probe_read_f32(x, sink=None, stream=None):
+    _input(x, torch.float32, "red_probe_read_f32")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=x.device)
+    with torch.cuda.device(x.device):
+        st = lib().red_probe_read_f32(x.data_ptr(), x.numel(), sink.data_ptr(), _stream_handle(stream, x.device))
+    _check("red_probe_read_f32", st)
+    return sink
+
+
+def red_device_info():
+    """(compute-unit count, architecture name) of the current device."""
+    cu = ctypes.c_int()
+    buf = ctypes.create_string_buffer(64)
+    _check("red_device_info", lib().red_device_info(ctypes.byref(cu), buf, 64))
+    return cu.value, buf.value.decode()
+
+
+def red_version():
+    return lib().red_version().decode()

@@ -1,0 +1,79 @@
+// launch.hpp -- internal interface between the C ABI (libred.cpp) and the
+// kernel translation units. Every launcher enqueues on `stream` and returns
+// the hipError_t of the launch (hipGetLastError right after it).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace libred {
+
+// Launch shape of the single-value kernels. `block` threads per block
+// (256, 512 or 1024), at most `blocks_per_cu` blocks per compute unit,
+// `unroll` independent 16-byte loads in flight per thread per iteration
+// (1, 2, 4, 8 or 16), `nontemporal` marks the streaming loads as
+// non-temporal.
+struct FlatPolicy {
+    int block;
+    int blocks_per_cu;
+    int unroll;
+    int nontemporal;
+};
+
+// Launch shape of the row kernels: `block` threads (one row per 64-lane
+// wave at a time), `unroll` loads in flight per lane, `max_blocks` caps the
+// grid (rows beyond it are taken in a wave-uniform grid-stride loop).
+struct RowsPolicy {
+    int block;
+    int unroll;
+    int nontemporal;
+    int max_blocks;
+};
+
+// Library-owned scratch of one (device, stream): a completion counter that
+// is zero between calls, and room for `max_partials` 8-byte block partials.
+struct Workspace {
+    unsigned int* ticket;
+    void* partials;
+    size_t max_partials;
+};
+
+bool flat_policy_supported(const FlatPolicy& p);
+bool rows_policy_supported(const RowsPolicy& p);
+
+// Single-value reductions with `grid` blocks (1 <= grid <= ws.max_partials).
+hipError_t launch_sum_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
+                          const Workspace& ws, hipStream_t stream);
+hipError_t launch_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, int grid,
+                              const FlatPolicy& p, const Workspace& ws, hipStream_t stream);
+hipError_t launch_max_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
+                          const Workspace& ws, hipStream_t stream);
+
+// Zero `words` 32-bit words at p (used once, when a workspace is created).
+hipError_t launch_zero_words(unsigned int* p, size_t words, hipStream_t stream);
+
+// Row reductions (rows >= 1) with `grid` blocks.
+hipError_t launch_rows_sum_f32(const float* x, size_t rows, size_t cols, float* out, int grid,
+                               const RowsPolicy& p, hipStream_t stream);
+hipError_t launch_rows_max_f32(const float* x, size_t rows, size_t cols, float* out, int grid,
+                               const RowsPolicy& p, hipStream_t stream);
+
+// Ablation ladder: rung 1..5 writes one float partial per block of
+// kRungBlock threads into `partials`; then a one-block kernel sums the
+// partials in float64 into *out.
+constexpr int kRungBlock = 256;
+size_t rung_elems_per_block(int rung);
+hipError_t launch_rung(int rung, const float* x, size_t n, float* partials, size_t nblocks,
+                       hipStream_t stream);
+hipError_t launch_combine_partials_f32(const float* partials, size_t np, float* out,
+                                       hipStream_t stream);
+
+// Probes: a plain copy y = x, and a read-only stream over x that writes to
+// *sink only if the data hold an impossible pattern (so no load can be
+// dropped). Both use 16-byte accesses with a scalar head and tail.
+hipError_t launch_copy_f32(const float* x, float* y, size_t n, int grid, hipStream_t stream);
+hipError_t launch_read_f32(const float* x, size_t n, unsigned int* sink, int grid,
+                           hipStream_t stream);
+
+}  // namespace libred

@@ -1,0 +1,351 @@
+// libred.cpp -- the C ABI of libred: argument checks, device facts, the
+// per-(device, stream) workspace, launch shapes, and the calls into the
+// kernel translation units. Host code only.
+#include <stdint.h>
+#include <string.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "launch.hpp"
+#include "libred.h"
+#include "libred_ablate.h"
+#include "libred_probe.h"
+
+using libred::FlatPolicy;
+using libred::RowsPolicy;
+using libred::Workspace;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+red_status fail(hipError_t e, red_status code) {
+    g_last_hip = (int)e;
+    return code;
+}
+
+struct DeviceInfo {
+    int cu_count;
+    char arch[64];
+};
+
+// Workspace layout: the completion counter alone in the first 256 bytes,
+// then room for kMaxPartials 8-byte partials. The grid never exceeds
+// kMaxPartials blocks.
+constexpr size_t kTicketBytes = 256;
+constexpr size_t kMaxPartials = 8192;
+constexpr size_t kWorkspaceBytes = kTicketBytes + kMaxPartials * 8;
+
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_devices;
+std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
+
+// Defaults, chosen by measurement on MI355X (256 CUs).
+constexpr FlatPolicy kDefaultFlat = {256, 8, 4, 1};
+constexpr RowsPolicy kDefaultRows = {256, 4, 1, 1 << 20};
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t abytes, const void* b, size_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return abytes && bbytes && a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+red_status current_device(int* dev_out, DeviceInfo* info_out) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess || count <= 0) return fail(e == hipSuccess ? hipErrorNoDevice : e, RED_ERR_NO_DEVICE);
+    int dev = -1;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(e, RED_ERR_NO_DEVICE);
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_devices.find(dev);
+    if (it == g_devices.end()) {
+        DeviceInfo di;
+        memset(&di, 0, sizeof(di));
+        e = hipDeviceGetAttribute(&di.cu_count, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+        strncpy(di.arch, prop.gcnArchName, sizeof(di.arch) - 1);
+        if (di.cu_count <= 0) return fail(hipErrorInvalidDevice, RED_ERR_NO_DEVICE);
+        it = g_devices.emplace(dev, di).first;
+    }
+    *dev_out = dev;
+    *info_out = it->second;
+    return RED_OK;
+}
+
+red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    const auto key = std::make_pair(dev, stream);
+    auto it = g_workspaces.find(key);
+    if (it != g_workspaces.end()) {
+        *ws = it->second;
+        return RED_OK;
+    }
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, kWorkspaceBytes);
+    if (e != hipSuccess || p == nullptr) return fail(e, RED_ERR_ALLOC);
+    // Zeroed by a kernel on the caller's stream, so the counter is 0 before
+    // the first reduction on this stream runs.
+    e = libred::launch_zero_words(static_cast<unsigned int*>(p), kWorkspaceBytes / 4, stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return fail(e, RED_ERR_HIP);
+    }
+    Workspace w;
+    w.ticket = static_cast<unsigned int*>(p);
+    w.partials = static_cast<char*>(p) + kTicketBytes;
+    w.max_partials = kMaxPartials;
+    g_workspaces.emplace(key, w);
+    *ws = w;
+    return RED_OK;
+}
+
+FlatPolicy to_flat(const red_flat_policy* p) {
+    if (!p) return kDefaultFlat;
+    FlatPolicy f = {p->block, p->blocks_per_cu, p->unroll, p->nontemporal};
+    return f;
+}
+
+RowsPolicy to_rows(const red_rows_policy* p) {
+    if (!p) return kDefaultRows;
+    RowsPolicy r = {p->block, p->unroll, p->nontemporal, p->max_blocks};
+    return r;
+}
+
+// Blocks for n elements: enough for one unrolled loop trip per thread, at
+// most blocks_per_cu per CU and at most kMaxPartials.
+size_t flat_grid_for(size_t n, const FlatPolicy& p, int cu_count) {
+    const size_t per_block = (size_t)p.block * (size_t)p.unroll * 4;
+    size_t want = (n + per_block - 1) / per_block;
+    if (want < 1) want = 1;
+    size_t cap = (size_t)p.blocks_per_cu * (size_t)cu_count;
+    if (cap > kMaxPartials) cap = kMaxPartials;
+    return want < cap ? want : cap;
+}
+
+template <class In, class Out, class Launch>
+red_status flat_call(const In* x, size_t n, Out* out, const red_flat_policy* pol, hipStream_t stream,
+                     Launch launch) {
+    if (n > RED_MAX_N || (n > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
+    if (!aligned(x, sizeof(In)) || !aligned(out, sizeof(Out))) return RED_ERR_INVALID_ARG;
+    if (overlap(x, n * sizeof(In), out, sizeof(Out))) return RED_ERR_INVALID_ARG;
+    const FlatPolicy p = to_flat(pol);
+    if (!libred::flat_policy_supported(p)) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    Workspace ws;
+    st = get_workspace(dev, stream, &ws);
+    if (st != RED_OK) return st;
+    const int grid = (int)flat_grid_for(n, p, info.cu_count);
+    const hipError_t e = launch(x, n, out, grid, p, ws, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+template <class Launch>
+red_status rows_call(const float* x, size_t rows, size_t cols, float* out, const red_rows_policy* pol,
+                     hipStream_t stream, Launch launch) {
+    if (cols != 0 && rows > SIZE_MAX / cols) return RED_ERR_INVALID_ARG;
+    const size_t total = rows * cols;
+    if (total > RED_MAX_N || rows > RED_MAX_N) return RED_ERR_INVALID_ARG;
+    const RowsPolicy p = to_rows(pol);
+    if (!libred::rows_policy_supported(p)) return RED_ERR_INVALID_ARG;
+    if (rows == 0) return RED_OK;
+    if ((total > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
+    if (!aligned(x, sizeof(float)) || !aligned(out, sizeof(float))) return RED_ERR_INVALID_ARG;
+    if (overlap(x, total * sizeof(float), out, rows * sizeof(float))) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    const size_t waves_per_block = (size_t)p.block / 64;
+    size_t grid = (rows + waves_per_block - 1) / waves_per_block;
+    if (grid > (size_t)p.max_blocks) grid = (size_t)p.max_blocks;
+    const hipError_t e = launch(x, rows, cols, out, (int)grid, p, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+red_status red_sum_f32(const float* x, size_t n, float* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_sum_f32);
+}
+
+red_status red_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_sum_i32_i64);
+}
+
+red_status red_max_f32(const float* x, size_t n, float* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_max_f32);
+}
+
+red_status red_rows_sum_f32(const float* x, size_t rows, size_t cols, float* out, hipStream_t stream) {
+    return rows_call(x, rows, cols, out, nullptr, stream, libred::launch_rows_sum_f32);
+}
+
+red_status red_rows_max_f32(const float* x, size_t rows, size_t cols, float* out, hipStream_t stream) {
+    return rows_call(x, rows, cols, out, nullptr, stream, libred::launch_rows_max_f32);
+}
+
+const char* red_status_string(red_status status) {
+    switch (status) {
+        case RED_OK: return "RED_OK";
+        case RED_ERR_INVALID_ARG: return "RED_ERR_INVALID_ARG: bad pointer, length, shape or alignment";
+        case RED_ERR_NO_DEVICE: return "RED_ERR_NO_DEVICE: no usable HIP device";
+        case RED_ERR_HIP: return "RED_ERR_HIP: a HIP call or kernel launch failed";
+        case RED_ERR_ALLOC: return "RED_ERR_ALLOC: workspace allocation failed";
+    }
+    return "unknown red_status";
+}
+
+int red_last_hip_error(void) { return g_last_hip; }
+
+const char* red_version(void) { return "libred 0.1.0 gfx950"; }
+
+// ---------------------------------------------------------------- ablation
+
+size_t red_ablate_num_partials(int rung, size_t n) {
+    if (rung < 1 || rung > 5) return 0;
+    const size_t epb = libred::rung_elems_per_block(rung);
+    return (n + epb - 1) / epb;
+}
+
+red_status red_ablate_sum_f32(int rung, const float* x, size_t n, float* partials, size_t partials_cap,
+                              float* out, hipStream_t stream) {
+    if (rung == 6) return red_sum_f32(x, n, out, stream);
+    if (rung < 1 || rung > 5) return RED_ERR_INVALID_ARG;
+    if (n == 0 || n > ((size_t)1 << 31) || x == nullptr || partials == nullptr || out == nullptr)
+        return RED_ERR_INVALID_ARG;
+    if (!aligned(x, 4) || !aligned(partials, 4) || !aligned(out, 4)) return RED_ERR_INVALID_ARG;
+    const size_t np = red_ablate_num_partials(rung, n);
+    if (partials_cap < np) return RED_ERR_INVALID_ARG;
+    if (overlap(x, n * 4, partials, np * 4) || overlap(x, n * 4, out, 4) || overlap(partials, np * 4, out, 4))
+        return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    hipError_t e = libred::launch_rung(rung, x, n, partials, np, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    e = libred::launch_combine_partials_f32(partials, np, out, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+void red_default_flat_policy(red_flat_policy* p) {
+    if (!p) return;
+    p->block = kDefaultFlat.block;
+    p->blocks_per_cu = kDefaultFlat.blocks_per_cu;
+    p->unroll = kDefaultFlat.unroll;
+    p->nontemporal = kDefaultFlat.nontemporal;
+}
+
+void red_default_rows_policy(red_rows_policy* p) {
+    if (!p) return;
+    p->block = kDefaultRows.block;
+    p->unroll = kDefaultRows.unroll;
+    p->nontemporal = kDefaultRows.nontemporal;
+    p->max_blocks = kDefaultRows.max_blocks;
+}
+
+size_t red_flat_grid(size_t n, const red_flat_policy* pol) {
+    const FlatPolicy p = to_flat(pol);
+    if (!libred::flat_policy_supported(p)) return 0;
+    int dev;
+    DeviceInfo info;
+    if (current_device(&dev, &info) != RED_OK) return 0;
+    return flat_grid_for(n, p, info.cu_count);
+}
+
+red_status red_sum_f32_with(const float* x, size_t n, float* out, const red_flat_policy* p,
+                            hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    return flat_call(x, n, out, p, stream, libred::launch_sum_f32);
+}
+
+red_status red_sum_i32_i64_with(const int32_t* x, size_t n, int64_t* out, const red_flat_policy* p,
+                                hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    return flat_call(x, n, out, p, stream, libred::launch_sum_i32_i64);
+}
+
+red_status red_max_f32_with(const float* x, size_t n, float* out, const red_flat_policy* p,
+                            hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    return flat_call(x, n, out, p, stream, libred::launch_max_f32);
+}
+
+red_status red_rows_sum_f32_with(const float* x, size_t rows, size_t cols, float* out,
+                                 const red_rows_policy* p, hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    return rows_call(x, rows, cols, out, p, stream, libred::launch_rows_sum_f32);
+}
+
+red_status red_rows_max_f32_with(const float* x, size_t rows, size_t cols, float* out,
+                                 const red_rows_policy* p, hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    return rows_call(x, rows, cols, out, p, stream, libred::launch_rows_max_f32);
+}
+
+// ---------------------------------------------------------------- probes
+
+red_status red_probe_copy_f32(const float* x, float* y, size_t n, hipStream_t stream) {
+    if (n > RED_MAX_N || (n > 0 && (x == nullptr || y == nullptr))) return RED_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || overlap(x, n * 4, y, n * 4)) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    if (n == 0) return RED_OK;
+    size_t grid = (n / 4 + 255) / 256;
+    const size_t cap = (size_t)8 * info.cu_count;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    const hipError_t e = libred::launch_copy_f32(x, y, n, (int)grid, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+red_status red_probe_read_f32(const float* x, size_t n, unsigned int* sink, hipStream_t stream) {
+    if (n > RED_MAX_N || (n > 0 && x == nullptr) || sink == nullptr) return RED_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(sink, 4) || overlap(x, n * 4, sink, 4)) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    if (n == 0) return RED_OK;
+    size_t grid = (n / 4 + 1023) / 1024;
+    const size_t cap = (size_t)8 * info.cu_count;
+    if (grid > cap) grid = cap;
+    if (grid < 1) grid = 1;
+    const hipError_t e = libred::launch_read_f32(x, n, sink, (int)grid, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+red_status red_device_info(int* cu_count, char* arch, size_t arch_len) {
+    if (cu_count == nullptr) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    *cu_count = info.cu_count;
+    if (arch && arch_len) {
+        strncpy(arch, info.arch, arch_len - 1);
+        arch[arch_len - 1] = '\0';
+    }
+    return RED_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+"""The C ABI without a GPU: exported symbols, status strings, argument checks.
+
+Argument errors must be reported as RED_ERR_INVALID_ARG before any HIP call;
+on a machine without a GPU any HIP call would turn the status into
+RED_ERR_NO_DEVICE, so these checks also show the order. No call here
+reaches a kernel.
+"""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+import reduction_libred_amd as rl  # noqa: E402
+
+INVALID, NO_DEVICE = rl.RED_ERR_INVALID_ARG, rl.RED_ERR_NO_DEVICE
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(red_[a-z0-9_]+)\s*\(", text))
+    return names
+
+
+def exported_symbols():
+    out = subprocess.run(["nm", "-D", "--defined-only", rl.LIB_PATH], check=True,
+                         capture_output=True, text=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.split()[-2:-1] == ["T"]}
+
+
+def test_exports_match_headers():
+    rl.lib()
+    decl = declared_symbols()
+    assert len(decl) >= 21
+    assert decl == exported_symbols()
+    assert decl == set(rl.SIGNATURES)
+    for name in decl:
+        assert getattr(rl.lib(), name) is not None
+
+
+def test_status_strings_and_version():
+    L = rl.lib()
+    for code in range(5):
+        assert L.red_status_string(code)
+    assert L.red_status_string(99) == b"unknown red_status"
+    assert rl.red_version().startswith("libred")
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+A, B = 0x10000, 0x20000            # aligned fake addresses, never dereferenced
+
+
+def test_flat_argument_errors():
+    L = rl.lib()
+    for f in (L.red_sum_f32, L.red_max_f32, L.red_sum_i32_i64):
+        assert f(None, 4, _p(B), None) == INVALID                 # null x, n > 0
+        assert f(_p(A), 4, None, None) == INVALID                 # null out
+        assert f(_p(A + 1), 4, _p(B), None) == INVALID            # misaligned x
+        assert f(_p(A), 4, _p(B + 2), None) == INVALID            # misaligned out
+        assert f(_p(A), 4, _p(A + 8), None) == INVALID            # out inside x
+        assert f(_p(A), rl.RED_MAX_N + 1, _p(B), None) == INVALID
+    assert L.red_sum_i32_i64(_p(A), 4, _p(B + 4), None) == INVALID  # int64 out needs 8
+    bad = rl.FlatPolicy(100, 8, 4, 1)
+    assert L.red_sum_f32_with(_p(A), 4, _p(B), ctypes.byref(bad), None) == INVALID
+    bad = rl.FlatPolicy(256, 8, 3, 1)
+    assert L.red_max_f32_with(_p(A), 4, _p(B), ctypes.byref(bad), None) == INVALID
+    assert L.red_sum_f32_with(_p(A), 4, _p(B), None, None) == INVALID
+
+
+def test_rows_argument_errors():
+    L = rl.lib()
+    for f in (L.red_rows_sum_f32, L.red_rows_max_f32):
+        assert f(_p(A), 1 << 40, 1 << 40, _p(B), None) == INVALID       # rows*cols overflow
+        assert f(_p(A), 1 << 21, 1 << 21, _p(B), None) == INVALID       # above RED_MAX_N
+        assert f(None, 2, 3, _p(B), None) == INVALID
+        assert f(_p(A), 2, 3, None, None) == INVALID
+        assert f(_p(A + 2), 2, 3, _p(B), None) == INVALID
+        assert f(_p(A), 4, 4, _p(A + 16), None) == INVALID              # out inside x
+        assert f(None, 0, 5, None, None) == rl.RED_OK                   # rows == 0: no-op
+    bad = rl.RowsPolicy(96, 4, 1, 16)
+    assert L.red_rows_sum_f32_with(_p(A), 2, 3, _p(B), ctypes.byref(bad), None) == INVALID
+
+
+def test_ablate_argument_errors():
+    L = rl.lib()
+    assert L.red_ablate_num_partials(1, 1000) == 4
+    assert L.red_ablate_num_partials(4, 1000) == 2
+    assert L.red_ablate_num_partials(5, 1024) == 2
+    assert L.red_ablate_num_partials(9, 1000) == 0
+    P = 0x40000
+    assert L.red_ablate_sum_f32(0, _p(A), 1000, _p(P), 4, _p(B), None) == INVALID
+    assert L.red_ablate_sum_f32(7, _p(A), 1000, _p(P), 4, _p(B), None) == INVALID
+    assert L.red_ablate_sum_f32(1, _p(A), 1000, _p(P), 3, _p(B), None) == INVALID   # cap too small
+    assert L.red_ablate_sum_f32(1, _p(A), 0, _p(P), 4, _p(B), None) == INVALID
+    assert L.red_ablate_sum_f32(2, _p(A), (1 << 31) + 1, _p(P), 1 << 24, _p(B), None) == INVALID
+    assert L.red_ablate_sum_f32(3, _p(A), 1000, _p(A + 64), 4, _p(B), None) == INVALID  # overlap
+
+
+def test_probe_argument_errors():
+    L = rl.lib()
+    assert L.red_probe_copy_f32(_p(A + 4), _p(B), 8, None) == INVALID    # 16-byte alignment
+    assert L.red_probe_copy_f32(_p(A), _p(A + 16), 8, None) == INVALID   # overlap
+    assert L.red_probe_read_f32(_p(A), 8, None, None) == INVALID
+    assert L.red_device_info(None, None, 0) == INVALID
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="only meaningful where no GPU is visible")
+def test_no_device():
+    L = rl.lib()
+    assert L.red_sum_f32(_p(A), 4, _p(B), None) == NO_DEVICE
+    assert L.red_last_hip_error() != 0
+    assert L.red_rows_max_f32(_p(A), 2, 2, _p(B), None) == NO_DEVICE
+    cu = ctypes.c_int()
+    assert L.red_device_info(ctypes.byref(cu), None, 0) == NO_DEVICE

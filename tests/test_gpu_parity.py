@@ -1,0 +1,426 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Float sums must lie within |gpu - S| <= 1e-5 * sum|x| + 1e-6 of the oracle's
+float64 compensated sum (per row for the row sums); integer sums and every
+max must match exactly. Inputs are the seeded workloads of workloads.py and
+deterministic patterns. Views into larger buffers give misaligned heads and
+ragged tails, and the elements just outside each view hold NaN (or +inf for
+max), so reading one element too many changes the answer.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - collected only with a GPU
+    pytest.skip("no GPU visible", allow_module_level=True)
+
+import reduction_libred_amd as rl  # noqa: E402
+
+DEV = torch.device("cuda:0")
+RAGGED = [1, 2, 3, 4, 5, 7, 31, 63, 64, 65, 127, 255, 256, 257, 1023, 1024, 1025,
+          4095, 4096, 4097, 65535, 65537, 1_000_003, (1 << 22) + 5]
+OFFSETS = [0, 1, 2, 3]
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def device_view(a, offset=0, guard=float("nan")):
+    """Copy numpy array `a` into a fresh device buffer at element `offset`
+    and return the view; elements before and after it hold `guard`."""
+    dt = {np.float32: torch.float32, np.int32: torch.int32}[a.dtype.type]
+    n = a.size
+    buf = torch.empty(n + offset + 8, dtype=dt, device=DEV)
+    buf.fill_(guard if dt == torch.float32 else -(2 ** 31))
+    view = buf[offset:offset + n]
+    view.copy_(torch.from_numpy(np.ascontiguousarray(a.reshape(-1))))
+    return view.view(a.shape) if a.ndim > 1 else view
+
+
+def gpu_sum(x, **kw):
+    out = rl.red_sum_f32(x, **kw)
+    torch.cuda.synchronize()
+    return float(out.item())
+
+
+def assert_sum_ok(got, a):
+    S, A = oracle.sum_f32(a)
+    assert oracle.sum_within_tolerance(got, S, A), (got, S, A, a.size)
+
+
+# ----------------------------------------------------------------- f32 sum
+
+@pytest.mark.parametrize("offset", OFFSETS)
+def test_sum_f32_ragged_random(offset):
+    rng = np.random.default_rng(100 + offset)
+    for n in RAGGED:
+        say(f"sum_f32 n={n} offset={offset}")
+        a = rng.uniform(-1, 1, n).astype(np.float32)
+        x = device_view(a, offset)
+        got = gpu_sum(x)
+        assert_sum_ok(got, a)
+        assert gpu_sum(x) == got            # bitwise run-to-run
+
+
+def test_sum_f32_empty():
+    say("sum_f32 n=0")
+    out = torch.full((), 123.0, device=DEV)
+    rl.red_sum_f32(torch.empty(0, device=DEV), out=out)
+    torch.cuda.synchronize()
+    assert out.item() == 0.0
+
+
+def test_sum_f32_lesson_mod7_exact():
+    # The lesson's workload: with small non-negative integers every partial
+    # sum is exact in float32, so any order gives the exact total.
+    for row in __import__("oracle_pins").read_golden("lesson_demo3_mod7.txt"):
+        n, want = int(row["n"]), int(row["expected"])
+        say(f"sum_f32 mod7 n={n}")
+        assert gpu_sum(device_view(W.pattern_mod7(n))) == want
+
+
+@pytest.mark.parametrize("n", [1 << 20, (1 << 24) + 3, 100_000_007])
+def test_sum_f32_sparse_ones_exact(n):
+    say(f"sum_f32 sparse ones n={n}")
+    a = W.pattern_every(n, 64)
+    assert gpu_sum(device_view(a, 1)) == float(len(range(0, n, 64)))
+
+
+@pytest.mark.parametrize("offset", OFFSETS)
+def test_sum_f32_tags_exact(offset):
+    # Tags 2^k at the head, the tail and around vector, wave, block and grid
+    # boundaries; each must be counted exactly once.
+    n = (1 << 22) + 7
+    pos = sorted({0, 1, 2, 3, 4, 5, 63, 64, 1023, 1024, 4095, 4096, 4097,
+                  (1 << 20) - 1, 1 << 20, n - 4, n - 3, n - 2, n - 1, n // 2, 12345})
+    say(f"sum_f32 tags n={n} offset={offset}")
+    a = W.pattern_tags(n, pos)
+    assert gpu_sum(device_view(a, offset)) == float(2 ** len(pos) - 1)
+
+
+def test_sum_f32_nonfinite():
+    cases = [([1.0, float("nan"), 2.0], "nan"), ([float("inf"), float("-inf")], "nan"),
+             ([1.0, float("inf")], float("inf")), ([-3.0, float("-inf")], float("-inf"))]
+    for xs, want in cases:
+        for n_pad in (0, 5000):
+            a = np.concatenate([np.zeros(n_pad, np.float32), np.array(xs, np.float32)])
+            say(f"sum_f32 nonfinite {xs} pad={n_pad}")
+            got = gpu_sum(device_view(a, 0, guard=0.0))
+            assert (math.isnan(got) if want == "nan" else got == want), (xs, got)
+
+
+def test_sum_f32_all_policies_agree():
+    a = W.make("normal", (1 << 21) + 3, 77)
+    x = device_view(a, 2)
+    S, A = oracle.sum_f32(a)
+    for block in (256, 512, 1024):
+        for unroll in (1, 2, 4, 8, 16):
+            for nt in (0, 1):
+                for bpc in (1, 4, 8):
+                    say(f"sum_f32 policy block={block} unroll={unroll} nt={nt} bpc={bpc}")
+                    got = gpu_sum(x, policy=dict(block=block, blocks_per_cu=bpc, unroll=unroll,
+                                                 nontemporal=nt))
+                    assert oracle.sum_within_tolerance(got, S, A), (block, unroll, nt, bpc, got, S)
+
+
+def test_sum_f32_two_streams():
+    # Calls on different streams use different workspaces and may overlap.
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    a1 = W.make("normal", 1 << 22, 5)
+    a2 = W.make("uniform_pm1", (1 << 22) + 1, 6)
+    x1, x2 = device_view(a1), device_view(a2)
+    torch.cuda.synchronize()
+    o1 = torch.empty(64, device=DEV)
+    o2 = torch.empty(64, device=DEV)
+    say("sum_f32 two streams x64")
+    for k in range(64):
+        rl.red_sum_f32(x1, out=o1[k], stream=s1)
+        rl.red_sum_f32(x2, out=o2[k], stream=s2)
+    torch.cuda.synchronize()
+    for a, o in ((a1, o1), (a2, o2)):
+        vals = o.cpu().numpy()
+        assert np.all(vals == vals[0])
+        assert_sum_ok(vals[0], a)
+
+
+# ----------------------------------------------------------------- i32 -> i64
+
+@pytest.mark.parametrize("offset", OFFSETS)
+def test_sum_i32_ragged_random(offset):
+    rng = np.random.default_rng(200 + offset)
+    for n in RAGGED:
+        say(f"sum_i32 n={n} offset={offset}")
+        a = rng.integers(-(2 ** 31), 2 ** 31, n, dtype=np.int64).astype(np.int32)
+        out = rl.red_sum_i32_i64(device_view(a, offset))
+        torch.cuda.synchronize()
+        assert int(out.item()) == oracle.sum_i32_i64(a), n
+
+
+def test_sum_i32_closed_forms_and_empty():
+    n = 1 << 24
+    say("sum_i32 arange 2^24")
+    out = rl.red_sum_i32_i64(torch.arange(n, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert int(out.item()) == n * (n - 1) // 2
+    say("sum_i32 INT32_MIN x (2^20+3)")
+    m = (1 << 20) + 3
+    out = rl.red_sum_i32_i64(torch.full((m,), -(2 ** 31), dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    assert int(out.item()) == m * -(2 ** 31)
+    say("sum_i32 n=0")
+    out = torch.full((), 5, dtype=torch.int64, device=DEV)
+    rl.red_sum_i32_i64(torch.empty(0, dtype=torch.int32, device=DEV), out=out)
+    torch.cuda.synchronize()
+    assert int(out.item()) == 0
+
+
+# ----------------------------------------------------------------- max
+
+@pytest.mark.parametrize("offset", OFFSETS)
+def test_max_f32_planted(offset):
+    rng = np.random.default_rng(300 + offset)
+    for n in RAGGED:
+        for where in {0, n - 1, n // 2, min(n - 1, 3)}:
+            say(f"max_f32 n={n} offset={offset} at={where}")
+            a = rng.uniform(-100.0, -1.0, n).astype(np.float32)    # all negative
+            a[where] = -0.25
+            out = rl.red_max_f32(device_view(a, offset, guard=float("inf")))
+            torch.cuda.synchronize()
+            assert out.item() == -0.25 == float(oracle.max_f32(a)), (n, where)
+
+
+def test_max_f32_nan_inf_empty():
+    nan, inf = float("nan"), float("inf")
+    cases = [([nan, -7.0, -9.0], -7.0), ([-9.0, nan], -9.0), ([nan, nan], -inf),
+             ([-inf, -inf], -inf), ([-3.0, inf], inf), ([0.0, -0.0], 0.0)]
+    for xs, want in cases:
+        for n_pad in (0, 10_000):
+            a = np.concatenate([np.full(n_pad, -np.inf, np.float32), np.array(xs, np.float32)])
+            say(f"max_f32 {xs} pad={n_pad}")
+            out = rl.red_max_f32(device_view(a, 1, guard=inf if n_pad == 0 else -inf))
+            torch.cuda.synchronize()
+            assert out.item() == want == float(oracle.max_f32(a)), (xs, out.item())
+    say("max_f32 n=0")
+    out = rl.red_max_f32(torch.empty(0, device=DEV))
+    torch.cuda.synchronize()
+    assert out.item() == -inf
+
+
+def test_max_f32_all_policies():
+    a = W.make("normal", (1 << 21) + 1, 78)
+    a[(1 << 21) - 77] = 99.0
+    x = device_view(a, 3, guard=float("inf"))
+    for block in (256, 512, 1024):
+        for unroll in (1, 4, 16):
+            for nt in (0, 1):
+                say(f"max_f32 policy block={block} unroll={unroll} nt={nt}")
+                out = rl.red_max_f32(x, policy=dict(block=block, blocks_per_cu=8, unroll=unroll,
+                                                     nontemporal=nt))
+                torch.cuda.synchronize()
+                assert out.item() == 99.0
+
+
+# ----------------------------------------------------------------- rows
+
+ROW_SHAPES = [(1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
+              (5, 64), (6, 65), (257, 4096), (2, 100_003), (4097, 3)]
+
+
+@pytest.mark.parametrize("rows,cols", ROW_SHAPES)
+def test_rows_random(rows, cols):
+    rng = np.random.default_rng(rows * 7919 + cols)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    if cols:
+        a[np.arange(rows), np.arange(rows) % cols] = 50.0 + np.arange(rows)   # planted max
+    for offset in (0, 1):
+        say(f"rows {rows}x{cols} offset={offset}")
+        x = device_view(a, offset)
+        guard_out = torch.full((rows + 2,), 777.0, device=DEV)
+        out_s = guard_out[1:rows + 1]
+        rl.red_rows_sum_f32(x, out=out_s)
+        torch.cuda.synchronize()
+        assert guard_out[0].item() == 777.0 and guard_out[-1].item() == 777.0
+        S, A = oracle.rows_sum_f32(a)
+        got = out_s.cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - S) <= 1e-5 * A + 1e-6), (rows, cols)
+        out_m = rl.red_rows_max_f32(x)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_m.cpu().numpy(), oracle.rows_max_f32(a)), (rows, cols)
+
+
+def test_rows_mod7_exact():
+    rows, cols = 1031, 4097
+    say(f"rows mod7 {rows}x{cols}")
+    a = W.pattern_rows_mod7(rows, cols)
+    x = device_view(a, 2)
+    S, _ = oracle.rows_sum_f32(a)
+    out = rl.red_rows_sum_f32(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), S)
+
+
+def test_rows_zero_rows():
+    say("rows 0x5")
+    out = rl.red_rows_sum_f32(torch.empty((0, 5), device=DEV))
+    assert out.numel() == 0
+
+
+def test_rows_policies():
+    a = W.make("uniform01", 300 * 1027, 9).reshape(300, 1027)
+    S, A = oracle.rows_sum_f32(a)
+    M = oracle.rows_max_f32(a)
+    x = device_view(a, 1)
+    for block in (64, 128, 256, 512):
+        for unroll in (1, 2, 4, 8):
+            for nt in (0, 1):
+                for mb in (1, 7, 1 << 20):
+                    say(f"rows policy block={block} unroll={unroll} nt={nt} max_blocks={mb}")
+                    p = dict(block=block, unroll=unroll, nontemporal=nt, max_blocks=mb)
+                    s = rl.red_rows_sum_f32(x, policy=p)
+                    m = rl.red_rows_max_f32(x, policy=p)
+                    torch.cuda.synchronize()
+                    assert np.all(np.abs(s.cpu().numpy() - S) <= 1e-5 * A + 1e-6)
+                    assert np.array_equal(m.cpu().numpy(), M)
+
+
+# ----------------------------------------------------------------- ablation
+
+def _block_sums_mod7(n, span):
+    idx = np.arange(n, dtype=np.int64) % 7
+    nb = (n + span - 1) // span
+    pad = np.zeros(nb * span, np.int64)
+    pad[:n] = idx
+    return pad.reshape(nb, span).sum(axis=1).astype(np.float32)
+
+
+@pytest.mark.parametrize("rung", [1, 2, 3, 4, 5, 6])
+def test_ablation_rungs(rung):
+    for row in __import__("oracle_pins").read_golden("lesson_demo3_mod7.txt"):
+        n, want = int(row["n"]), int(row["expected"])
+        say(f"rung {rung} mod7 n={n}")
+        out, partials = rl.red_ablate_sum_f32(rung, device_view(W.pattern_mod7(n)))
+        torch.cuda.synchronize()
+        assert out.item() == want
+        if rung <= 5:
+            span = 512 if rung >= 4 else 256
+            assert np.array_equal(partials.cpu().numpy(), _block_sums_mod7(n, span))
+    for n in (1, 255, 257, 1000, (1 << 20) + 3):
+        say(f"rung {rung} random n={n}")
+        a = W.make("normal", n, 400 + n % 97)
+        out, _ = rl.red_ablate_sum_f32(rung, device_view(a, 1))
+        torch.cuda.synchronize()
+        assert_sum_ok(out.item(), a)
+
+
+# ----------------------------------------------------------------- probes
+
+def test_probes():
+    n = (1 << 20) + 3
+    say("probe copy/read")
+    a = W.make("normal", n, 12)
+    x = torch.from_numpy(a).to(DEV)
+    y = torch.empty_like(x)
+    rl.red_probe_copy_f32(x, y)
+    sink = rl.red_probe_read_f32(x)
+    torch.cuda.synchronize()
+    assert torch.equal(x, y)
+    assert sink.numel() == 1
+    cu, arch = rl.red_device_info()
+    assert cu > 0 and arch.startswith("gfx950")
+
+
+# ----------------------------------------------------------------- full sizes
+# The five workloads at their real sizes, with the default launch shapes
+# (the ones the benchmark times).
+
+def _load(name):
+    say(f"generate {name}")
+    a = W.workload(name)
+    say(f"upload {name}")
+    x = torch.from_numpy(a).to(DEV)
+    torch.cuda.synchronize()
+    return a, x
+
+
+def test_full_sum_f32_2p20():
+    a, x = _load("sum_f32_2p20")
+    say("red_sum_f32 sum_f32_2p20")
+    assert_sum_ok(gpu_sum(x), a)
+
+
+def test_full_sum_i32_2p24():
+    a, x = _load("sum_i32_2p24")
+    say("red_sum_i32_i64 sum_i32_2p24")
+    out = rl.red_sum_i32_i64(x)
+    torch.cuda.synchronize()
+    assert int(out.item()) == oracle.sum_i32_i64(a)
+
+
+def test_full_sum_max_f32_2p28():
+    a, x = _load("sum_max_f32_2p28")
+    say("red_sum_f32 sum_max_f32_2p28")
+    got = gpu_sum(x)
+    assert_sum_ok(got, a)
+    assert gpu_sum(x) == got
+    say("red_max_f32 sum_max_f32_2p28")
+    m = rl.red_max_f32(x)
+    torch.cuda.synchronize()
+    assert m.item() == float(oracle.max_f32(a))
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_sparse_ones_2p28():
+    n = 1 << 28
+    say("sum_f32 sparse ones (every 32nd) n=2^28")
+    x = torch.zeros(n, device=DEV)
+    x[::32] = 1.0
+    assert gpu_sum(x) == float(n // 32)
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_rows_65536x4096():
+    a, x = _load("rows_f32_65536x4096")
+    say("red_rows_sum_f32 / red_rows_max_f32 rows_f32_65536x4096")
+    s = rl.red_rows_sum_f32(x)
+    m = rl.red_rows_max_f32(x)
+    torch.cuda.synchronize()
+    S, A = oracle.rows_sum_f32(a)
+    assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
+    assert np.array_equal(m.cpu().numpy(), oracle.rows_max_f32(a))
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_sum_f32_1e9p7():
+    a, x = _load("sum_f32_1e9p7")
+    say("red_sum_f32 sum_f32_1e9p7")
+    got = gpu_sum(x)
+    say("oracle sum_f32_1e9p7")
+    assert_sum_ok(got, a)
+    say("red_sum_f32 sum_f32_1e9p7 offset view")
+    assert_sum_ok(gpu_sum(x[1:]), a[1:])
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_sparse_ones_1e9p7():
+    n = 1_000_000_007
+    say("sum_f32 sparse ones (every 64th) n=1e9+7")
+    x = torch.zeros(n, device=DEV)
+    x[::64] = 1.0
+    assert gpu_sum(x) == float(len(range(0, n, 64)))
+    assert gpu_sum(x[3:]) == float(len(range(64, n, 64)))
+    del x
+    torch.cuda.empty_cache()

@@ -4,10 +4,11 @@ This module only draws and lays out input arrays. It holds none of the
 reduction arithmetic, and it is the one piece of code that both the CPU
 oracle's tests and the GPU path's tests and benchmark use.
 
-Every random array comes from numpy's PCG64 (`numpy.random.default_rng`),
-drawn in fixed chunks of CHUNK = 2^24 elements from one generator and laid
-out in draw order, so the bytes depend only on (kind, n, seed) and not on how
-much memory the caller has. The five named workloads:
+Every random array comes from numpy's PCG64 in fixed chunks of CHUNK = 2^24
+elements: chunk k (elements [k*CHUNK, (k+1)*CHUNK)) is drawn by
+`default_rng(SeedSequence(seed, spawn_key=(k,)))`, so the bytes depend only on
+(kind, n, seed), and chunks can be filled by parallel threads. The five named
+workloads:
 
   sum_f32_2p20         2^20 float32, uniform[-1, 1), seed 0
   sum_i32_2p24         2^24 int32, integers in [-1000, 1000], seed 1
@@ -19,6 +20,9 @@ much memory the caller has. The five named workloads:
 The structured patterns at the end are deterministic, not random; the
 reduction lesson's own workload (the value i mod 7 at index i) is one.
 """
+import concurrent.futures as cf
+import os
+
 import numpy as np
 
 CHUNK = 1 << 24
@@ -65,13 +69,19 @@ def _fill_chunk(kind, rng, out):
         raise ValueError(f"unknown kind {kind!r}")
 
 
-def make(kind, n, seed, out=None, progress=None):
-    """Draw n elements of distribution `kind` from default_rng(seed).
+def chunk_rng(seed, k):
+    """The generator that draws chunk k of a workload with this seed."""
+    return np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(k,)))
 
-    Chunks of CHUNK elements (the last one shorter) are drawn in order, so
+
+def make(kind, n, seed, out=None, progress=None, threads=None):
+    """Draw n elements of distribution `kind` for `seed`, chunk by chunk.
+
+    Chunk k always holds the same values for a given seed, so
     make(kind, n, seed)[:m] equals make(kind, m, seed) whenever m is a
     multiple of CHUNK. `out` may be a preallocated array of the kind's dtype
-    and n elements. `progress`, if given, is called with the count done.
+    and n elements. `progress`, if given, is called with each finished chunk
+    count. `threads` defaults to min(16, cpu count).
     """
     dtype = DTYPES[kind]
     if out is None:
@@ -79,12 +89,24 @@ def make(kind, n, seed, out=None, progress=None):
     if out.dtype != dtype or out.size != n:
         raise ValueError("out has the wrong dtype or size")
     flat = out.reshape(-1)
-    rng = np.random.default_rng(seed)
-    for lo in range(0, n, CHUNK):
-        hi = min(n, lo + CHUNK)
-        _fill_chunk(kind, rng, flat[lo:hi])
-        if progress is not None:
-            progress(hi)
+    nchunks = (n + CHUNK - 1) // CHUNK
+
+    def fill(k):
+        lo = k * CHUNK
+        _fill_chunk(kind, chunk_rng(seed, k), flat[lo:min(n, lo + CHUNK)])
+        return k
+
+    threads = threads or min(16, os.cpu_count() or 1)
+    if nchunks <= 1 or threads <= 1:
+        for k in range(nchunks):
+            fill(k)
+            if progress is not None:
+                progress(k + 1)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            for done, _ in enumerate(ex.map(fill, range(nchunks)), 1):
+                if progress is not None:
+                    progress(done)
     return out
 
 
