@@ -3,10 +3,11 @@
 
 Headline: achieved HBM GB/s of red_sum_f32 over 2^28 float32 elements
 (1 GiB, normal(0,1), seed 2), as a fraction of the 8 TB/s HBM3E peak. One
-step is one red_sum_f32 call over the resident array (load, peel, wave
-reduce, LDS combine, partial, last-block combine: the whole path in one
-kernel). The line also carries the roofline of that kernel, the CPU oracle
-timed on the host, and the other entry points at their own workloads.
+step is one red_sum_f32 call over the resident array: the streaming kernel
+(load, peel, wave reduce, LDS combine, block partial) and the one-block
+combine launch. The line also carries the roofline of the streaming kernel
+(timed alone through red_sum_f32_partials), the CPU oracle timed on the
+host, and the other entry points at their own workloads.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 
@@ -52,7 +53,7 @@ def recorded_traffic():
         return None
     if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return rec.get("sum_f32_2p28_bytes_per_launch")
+    return rec.get("flat_reduce_kernel_sum_f32_2p28_bytes_per_launch")
 
 
 def parse_args():
@@ -136,7 +137,7 @@ def main():
     x = torch.from_numpy(a).to(dev)
     out = torch.empty((), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    policy = rl.red_default_flat_policy().as_dict()
+    policy = rl.red_default_flat_policy(n).as_dict()
     grid = rl.red_flat_grid(n)
     nbytes = 4 * n + 4
 
@@ -153,9 +154,25 @@ def main():
     if out.item() != eager:
         raise RuntimeError("red_sum_f32 is not reproducible run to run")
     value = gbps(nbytes, ms)
-    med_ms, min_ms = timer.per_launch_ms(step, max(20, min(args.steps, 200)))
-    log(f"red_sum_f32: {ms * 1e3:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of peak); "
+    log(f"red_sum_f32: {ms * 1e3:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of peak)")
+
+    # The dominant kernel alone: steps 1-5 (the streaming pass) without the
+    # one-block combine launch, via red_sum_f32_partials, same launch shape.
+    partials = torch.empty(grid, dtype=torch.float64, device=dev)
+
+    def pass1():
+        rl.red_sum_f32_partials(x, partials=partials)
+
+    for _ in range(args.warmup):
+        pass1()
+    k_ms = timer.region_ms(pass1, args.steps)
+    med_ms, min_ms = timer.per_launch_ms(pass1, max(20, min(args.steps, 200)))
+    achieved = gbps(nbytes, k_ms)
+    log(f"flat_reduce_kernel alone: {k_ms * 1e3:.1f} us/launch, {achieved:.1f} GB/s; "
         f"per-launch median {med_ms * 1e3:.1f} us")
+    kname = (f"flat_reduce_kernel<SumF32, {policy['block']}, {policy['unroll']}, "
+             f"{'true' if policy['nontemporal'] else 'false'}, {policy['layout']}, "
+             f"{'true' if policy['prefetch'] else 'false'}>")
 
     result = {
         "metric": METRIC,
@@ -185,17 +202,17 @@ def main():
         "elements_per_s": round(n / (ms * 1e-3), 1),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(value, 2),
+            "achieved": round(achieved, 2),
             "peak": PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(value / PEAK_GBPS, 4),
+            "frac": round(achieved / PEAK_GBPS, 4),
             "traffic": recorded_traffic(),
-            "kernel": f"flat_reduce_kernel<SumF32, {policy['block']}, {policy['unroll']}, "
-                      f"{'true' if policy['nontemporal'] else 'false'}>",
+            "kernel": kname,
             "algorithmic_bytes_per_launch": nbytes,
-            "avg_launch_us": round(ms * 1e3, 3),
+            "avg_launch_us": round(k_ms * 1e3, 3),
             "median_launch_us_events": round(med_ms * 1e3, 3),
             "min_launch_us_events": round(min_ms * 1e3, 3),
+            "step_us_with_combine_launch": round(ms * 1e3, 3),
         },
     }
 
@@ -233,9 +250,12 @@ def main():
         measure(f"red_rows_max_f32 {name4}", lambda: rl.red_rows_max_f32(x4, out=r4), b4)
         del x4
 
-        # Small, cache-resident sizes: batched (a HIP graph of 100 calls,
-        # replays checked against the eager result) and cold (a rotation
-        # over copies that together exceed the 256 MB Infinity Cache).
+        # Small, cache-resident sizes, through HIP graphs so that host call
+        # overhead is out of the measurement: "batched" replays 100 calls on
+        # one array (it stays in the 256 MB Infinity Cache); "cold" replays
+        # calls that rotate over copies totalling 1 GiB, so each call's input
+        # was evicted by the others. Replays are checked against the eager
+        # result.
         for name_s, fn_s, odt in (("sum_f32_2p20", rl.red_sum_f32, torch.float32),
                                   ("sum_i32_2p24", rl.red_sum_i32_i64, torch.int64)):
             log(f"generate {name_s}")
@@ -245,36 +265,36 @@ def main():
             fn_s(xs, out=os_)
             torch.cuda.synchronize()
             eager_s = os_.item()
-            g = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream()
-            cap.wait_stream(stream)
-            with torch.cuda.stream(cap):
-                fn_s(xs, out=os_)          # workspace of the capture stream exists before capture
-                torch.cuda.synchronize()
-                with torch.cuda.graph(g, stream=cap):
-                    for _ in range(100):
-                        fn_s(xs, out=os_)
-            torch.cuda.synchronize()
-            for _ in range(3):
-                os_.zero_()
-                g.replay()
-                torch.cuda.synchronize()
-                if os_.item() != eager_s:
-                    raise RuntimeError(f"graph replay of {name_s} differs from the eager result")
-            t_ms = timer.region_ms(g.replay, 10) / 100
             copies = max(2, -(-(1 << 30) // (bs - os_.element_size())))
             xc = [xs.clone() for _ in range(copies)]
-            it = iter(range(1 << 30))
-            cold_ms = timer.region_ms(lambda: fn_s(xc[next(it) % copies], out=os_), 4 * copies)
-            others[f"{fn_s.__name__} {name_s}"] = {
-                "batched_us": round(t_ms * 1e3, 3),
-                "batched_GB/s": round(gbps(bs, t_ms), 2),
-                "cold_us": round(cold_ms * 1e3, 3),
-                "cold_GB/s": round(gbps(bs, cold_ms), 2),
-                "note": "fits in the 256 MB Infinity Cache; batched = 100 calls in one HIP graph",
-            }
-            log(f"{fn_s.__name__} {name_s}: {others[f'{fn_s.__name__} {name_s}']}")
+            rec = {}
+            for label, inputs in (("batched", [xs] * 100), ("cold", xc)):
+                g = torch.cuda.CUDAGraph()
+                cap = torch.cuda.Stream()
+                cap.wait_stream(stream)
+                with torch.cuda.stream(cap):
+                    fn_s(xs, out=os_)      # the capture stream's workspace exists before capture
+                    torch.cuda.synchronize()
+                    with torch.cuda.graph(g, stream=cap):
+                        for xi in inputs:
+                            fn_s(xi, out=os_)
+                torch.cuda.synchronize()
+                for _ in range(3):
+                    os_.zero_()
+                    g.replay()
+                    torch.cuda.synchronize()
+                    if os_.item() != eager_s:
+                        raise RuntimeError(f"graph replay of {name_s} differs from the eager result")
+                t_ms = timer.region_ms(g.replay, 10) / len(inputs)
+                rec[f"{label}_us"] = round(t_ms * 1e3, 3)
+                rec[f"{label}_GB/s"] = round(gbps(bs, t_ms), 2)
+                del g
+            rec["note"] = ("fits in the 256 MB Infinity Cache; batched = 100 calls on one array in a HIP graph, "
+                           f"cold = {copies} calls on distinct copies (1 GiB in all) in a HIP graph")
+            others[f"{fn_s.__name__} {name_s}"] = rec
+            log(f"{fn_s.__name__} {name_s}: {rec}")
             del xc, xs
+            torch.cuda.empty_cache()
 
         name5 = "sum_f32_1e9p7"
         log(f"generate {name5}")

@@ -40,16 +40,29 @@ red_status red_ablate_sum_f32(int rung, const float *x, size_t n, float *partial
 size_t red_ablate_num_partials(int rung, size_t n);
 
 /*
- * Launch shape of the single-value kernels: `block` threads per block (256,
- * 512 or 1024), at most `blocks_per_cu` blocks per compute unit, `unroll`
- * independent 16-byte loads per thread per loop trip (1, 2, 4, 8 or 16),
- * `nontemporal` 1 to mark the streaming loads non-temporal.
+ * Launch shape of the single-value kernels.
+ *   block          threads per block
+ *   blocks_per_cu  at most this many blocks per compute unit
+ *   unroll         independent 16-byte loads per lane per loop trip
+ *   nontemporal    1: mark the streaming loads non-temporal
+ *   layout         0: grid-stride (thread i reads vectors i, i + G*T, ...);
+ *                  1: wave tiles (each wave reads whole tiles of 64*unroll
+ *                     contiguous vectors, tiles dealt round-robin to waves)
+ *   prefetch       layout 1 only: issue the next tile's loads before folding
+ *                  the current tile
+ *   combine        0: the last block to finish combines the partials in the
+ *                  same launch; 1: a second one-block launch combines them
+ * Compiled shapes: layout 0 with block 256/512/1024 and unroll 1/2/4/8/16
+ * (prefetch 0); layout 1 with block 64/256/512/1024 and unroll 4/8/16.
  */
 typedef struct red_flat_policy {
     int block;
     int blocks_per_cu;
     int unroll;
     int nontemporal;
+    int layout;
+    int prefetch;
+    int combine;
 } red_flat_policy;
 
 /* Launch shape of the row kernels: `block` threads (64, 128, 256 or 512; one
@@ -62,14 +75,25 @@ typedef struct red_rows_policy {
     int max_blocks;
 } red_rows_policy;
 
-/* The shapes red_sum_f32 / red_sum_i32_i64 / red_max_f32 and the row entry
- * points use. */
-void red_default_flat_policy(red_flat_policy *p);
+/* The shape red_sum_f32 / red_sum_i32_i64 / red_max_f32 use for n elements,
+ * and the shape of the row entry points. */
+void red_default_flat_policy(size_t n, red_flat_policy *p);
 void red_default_rows_policy(red_rows_policy *p);
 
 /* The number of blocks a single-value call of n elements launches with
  * policy p (NULL = default) on the current device; 0 on error. */
 size_t red_flat_grid(size_t n, const red_flat_policy *p);
+
+/*
+ * Steps 1-5 of red_sum_f32 alone: each block of the launch (policy p, NULL =
+ * the default for n) stores its float64 partial; *count receives the number
+ * of blocks np = red_flat_grid(n, p), and partials[0..np) the partials in
+ * block order. Their sum is the sum of x[0..n). No final combine is run and
+ * the library workspace is not used. partials_cap < np, a NULL partials or
+ * count, or partials overlapping x is RED_ERR_INVALID_ARG.
+ */
+red_status red_sum_f32_partials(const float *x, size_t n, double *partials, size_t partials_cap,
+                                const red_flat_policy *p, size_t *count, hipStream_t stream);
 
 /* The single-value and row entry points with an explicit launch shape.
  * An unsupported shape is RED_ERR_INVALID_ARG. Results obey the same

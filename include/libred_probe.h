@@ -21,9 +21,10 @@ extern "C" {
  * overlap. */
 red_status red_probe_copy_f32(const float *x, float *y, size_t n, hipStream_t stream);
 
-/* Reads every 32-bit word of x[0..n) once and writes nothing unless the data
- * hash to a fixed value (then one word at *sink). x and sink must be 16- and
- * 4-byte aligned. */
+/* Reads every 32-bit word of x[0..n) once, with the launch shape and kernel
+ * structure of red_sum_f32, and stores their xor at *sink: the reduction's
+ * load path with one integer op per element instead of the float64 adds.
+ * x and sink must be 4-byte aligned and must not overlap. */
 red_status red_probe_read_f32(const float *x, size_t n, unsigned int *sink, hipStream_t stream);
 
 /* Facts about the current device: compute-unit count and architecture name

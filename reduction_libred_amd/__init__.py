@@ -39,7 +39,9 @@ class RedError(RuntimeError):
 
 class FlatPolicy(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int), ("blocks_per_cu", ctypes.c_int),
-                ("unroll", ctypes.c_int), ("nontemporal", ctypes.c_int)]
+                ("unroll", ctypes.c_int), ("nontemporal", ctypes.c_int),
+                ("layout", ctypes.c_int), ("prefetch", ctypes.c_int),
+                ("combine", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -70,7 +72,8 @@ SIGNATURES = {
     "red_version": (ctypes.c_char_p, []),
     "red_ablate_sum_f32": (_S, [_I, _P, _Z, _P, _Z, _P, _P]),
     "red_ablate_num_partials": (_Z, [_I, _Z]),
-    "red_default_flat_policy": (None, [ctypes.POINTER(FlatPolicy)]),
+    "red_default_flat_policy": (None, [_Z, ctypes.POINTER(FlatPolicy)]),
+    "red_sum_f32_partials": (_S, [_P, _Z, _P, _Z, ctypes.POINTER(FlatPolicy), ctypes.POINTER(_Z), _P]),
     "red_default_rows_policy": (None, [ctypes.POINTER(RowsPolicy)]),
     "red_flat_grid": (_Z, [_Z, ctypes.POINTER(FlatPolicy)]),
     "red_sum_f32_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
@@ -134,10 +137,17 @@ def _output(out, shape, dtype, device, name):
     return out
 
 
-def _policy(cls, p):
+def _policy(cls, p, n=0):
+    """A policy struct from None, a struct, or a dict of fields (fields not
+    given take the library default for n elements)."""
     if p is None or isinstance(p, cls):
         return p
-    return cls(**p)
+    base = red_default_flat_policy(n) if cls is FlatPolicy else red_default_rows_policy()
+    for k, v in p.items():
+        if k not in base.as_dict():
+            raise KeyError(f"unknown policy field {k!r}")
+        setattr(base, k, int(v))
+    return base
 
 
 def _flat(name, cname, x, out, in_dtype, out_dtype, stream, policy=None):
@@ -148,7 +158,7 @@ def _flat(name, cname, x, out, in_dtype, out_dtype, stream, policy=None):
         if policy is None:
             st = getattr(lib(), cname)(x.data_ptr(), x.numel(), out.data_ptr(), s)
         else:
-            p = _policy(FlatPolicy, policy)
+            p = _policy(FlatPolicy, policy, x.numel())
             st = getattr(lib(), cname + "_with")(x.data_ptr(), x.numel(), out.data_ptr(),
                                                  ctypes.byref(p), s)
     _check(cname, st)
@@ -217,9 +227,10 @@ def red_ablate_sum_f32(rung, x, partials=None, out=None, stream=None):
     return out, partials
 
 
-def red_default_flat_policy():
+def red_default_flat_policy(n):
+    """The launch shape the single-value entry points use for n elements."""
     p = FlatPolicy()
-    lib().red_default_flat_policy(ctypes.byref(p))
+    lib().red_default_flat_policy(n, ctypes.byref(p))
     return p
 
 
@@ -229,8 +240,25 @@ def red_default_rows_policy():
     return p
 
 
+def red_sum_f32_partials(x, partials=None, policy=None, stream=None):
+    """Block partials (float64) of the f32 sum, no final combine. Returns the
+    partials tensor trimmed to the number of blocks launched."""
+    _input(x, torch.float32, "red_sum_f32_partials")
+    p = _policy(FlatPolicy, policy, x.numel())
+    cap = red_flat_grid(x.numel(), p)
+    if partials is None:
+        partials = torch.empty(max(cap, 1), dtype=torch.float64, device=x.device)
+    count = ctypes.c_size_t()
+    with torch.cuda.device(x.device):
+        st = lib().red_sum_f32_partials(x.data_ptr(), x.numel(), partials.data_ptr(), partials.numel(),
+                                        ctypes.byref(p) if p is not None else None, ctypes.byref(count),
+                                        _stream_handle(stream, x.device))
+    _check("red_sum_f32_partials", st)
+    return partials[:count.value]
+
+
 def red_flat_grid(n, policy=None):
-    p = _policy(FlatPolicy, policy)
+    p = _policy(FlatPolicy, policy, n)
     return int(lib().red_flat_grid(n, ctypes.byref(p) if p is not None else None))
 
 

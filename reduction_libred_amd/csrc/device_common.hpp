@@ -59,6 +59,19 @@ struct MaxF32 {
     static __device__ __forceinline__ out_t finish(acc_t a) { return a; }
 };
 
+// Read probe: xor of every 32-bit word. One cheap ALU op per element, so a
+// kernel built on it measures the load path alone.
+struct XorU32 {
+    using elem_t = uint32_t;
+    using vec_t = uint32_t __attribute__((ext_vector_type(4)));
+    using acc_t = uint32_t;
+    using out_t = uint32_t;
+    static __device__ __forceinline__ acc_t identity() { return 0u; }
+    static __device__ __forceinline__ acc_t lift(elem_t v) { return v; }
+    static __device__ __forceinline__ acc_t combine(acc_t a, acc_t b) { return a ^ b; }
+    static __device__ __forceinline__ out_t finish(acc_t a) { return a; }
+};
+
 // ---------------------------------------------------------------------------
 // Loads
 // ---------------------------------------------------------------------------

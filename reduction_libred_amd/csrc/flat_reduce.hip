@@ -1,49 +1,44 @@
 // flat_reduce.hip -- single-value reductions (sum f32, sum i32->i64, max f32).
 //
-// One launch does the whole reduction. The steps follow the block-partial
-// scheme of the reduction lesson ("03_shared_memory_sync_reduction.py",
-// demo 3), redesigned for wave64 and a persistent grid:
-//   1. grid-stride loop of 16-byte loads, `UNROLL` in flight per thread,
-//      every element folded into four private accumulators as it arrives
+// The steps follow the block-partial scheme of the reduction lesson
+// ("03_shared_memory_sync_reduction.py", demo 3), redesigned for wave64 and a
+// persistent grid:
+//   1. stream the 16-byte aligned body with `UNROLL` loads in flight per lane,
+//      folding every element into four private accumulators as it arrives
 //      (the lesson's version 4 adds while loading; here every load does);
 //   2. the misaligned head and the ragged tail (< 4 elements each) are read
-//      with scalar loads by block 0; out-of-range lanes contribute nothing;
+//      with scalar loads by block 0; lanes with nothing to read add nothing;
 //   3. wave reduce 64 -> 1 with DPP (the lesson's version 5 does this step
 //      with warp shuffles);
 //   4. one LDS word per wave, one barrier, wave 0 combines the waves;
 //   5. thread 0 stores the block partial;
-//   6. the block that finishes last (a counter bumped once per block) combines
-//      all partials in index order and stores the result. The lesson notes
-//      that blocks cannot wait for each other inside a kernel; the counter
-//      lets the last one to arrive do the final step without a second launch,
-//      and the fixed index order makes the result independent of which block
-//      that is (the simulator page "simt_lab.py", section 5, asks that a
-//      kernel's result never depend on block order).
+//   6. the partials are combined in index order, either by the block that
+//      finishes last in the same launch (a counter bumped once per block
+//      tells it that it is last), or by a one-block second launch. The lesson
+//      notes that blocks cannot wait for each other inside a kernel; both
+//      forms respect that, and the fixed index order makes the result
+//      independent of which block finishes when (the simulator page
+//      "simt_lab.py", section 5, asks that a kernel's result never depend on
+//      block order).
+//
+// Two layouts of step 1 are compiled:
+//   kGridStride: thread i of the grid reads vectors i, i + G*T, i + 2*G*T, ...
+//       (UNROLL of them per loop trip), so each wave load covers 1 KiB and the
+//       grid sweeps the array front to back in G*T*16-byte slabs;
+//   kWaveTiles: the body is cut into tiles of 64*UNROLL vectors (UNROLL KiB);
+//       wave w of the grid reads tiles w, w + nwaves, ... whole, one 16-byte
+//       vector per lane per load, so each wave streams contiguous memory.
+//       With `PREFETCH`, the next tile's loads are issued before the current
+//       tile is folded, keeping 2*UNROLL KiB in flight per wave.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace libred {
 
 template <class Op, int BLOCK, int UNROLL, bool NT>
-__global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
-    const typename Op::elem_t* __restrict__ x, size_t n,
-    typename Op::acc_t* __restrict__ partials, unsigned int* __restrict__ ticket,
-    typename Op::out_t* __restrict__ out) {
-    using acc_t = typename Op::acc_t;
+__device__ __forceinline__ void body_grid_stride(const typename Op::vec_t* __restrict__ xv, size_t nvec,
+                                                 typename Op::acc_t (&acc)[4]) {
     using vec_t = typename Op::vec_t;
-    using elem_t = typename Op::elem_t;
-    __shared__ acc_t lds[BLOCK / kWave];
-    __shared__ int is_last;
-
-    // Split x into head (scalar), 16-byte aligned body, tail (scalar).
-    const size_t head = head_elems(x, sizeof(elem_t), n);
-    const size_t nvec = (n - head) / 4;
-    const size_t tail0 = head + 4 * nvec;
-    const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x + head);
-
-    acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
-
-    // Step 1: grid-stride body. Each load of a wave covers 1 KiB contiguous.
     const size_t stride = (size_t)gridDim.x * BLOCK;
     size_t i = (size_t)blockIdx.x * BLOCK + threadIdx.x;
     for (; i + (size_t)(UNROLL - 1) * stride < nvec; i += (size_t)UNROLL * stride) {
@@ -54,6 +49,102 @@ __global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
         for (int u = 0; u < UNROLL; ++u) accumulate4<Op>(acc, v[u]);
     }
     for (; i < nvec; i += stride) accumulate4<Op>(acc, load_vec<NT>(xv + i));
+}
+
+// One tile of a wave: UNROLL loads, each of 64 lanes x 16 bytes = 1 KiB.
+template <bool NT, class V, int UNROLL>
+__device__ __forceinline__ void load_tile(V (&v)[UNROLL], const V* __restrict__ p) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
+}
+
+template <class Op, int UNROLL>
+__device__ __forceinline__ void fold_tile(typename Op::acc_t (&acc)[4],
+                                          const typename Op::vec_t (&v)[UNROLL]) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) accumulate4<Op>(acc, v[u]);
+}
+
+template <class Op, int BLOCK, int UNROLL, bool NT, bool PREFETCH>
+__device__ __forceinline__ void body_wave_tiles(const typename Op::vec_t* __restrict__ xv, size_t nvec,
+                                                typename Op::acc_t (&acc)[4]) {
+    using vec_t = typename Op::vec_t;
+    constexpr int W = BLOCK / kWave;
+    constexpr size_t TILE = (size_t)kWave * UNROLL;  // vectors per tile
+    const int lane = threadIdx.x % kWave;
+    const size_t wave = (size_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const size_t nwaves = (size_t)gridDim.x * W;
+    const size_t ntiles = nvec / TILE;
+    size_t t = (size_t)blockIdx.x * W + wave;  // wave-uniform
+
+    if constexpr (!PREFETCH) {
+        for (; t < ntiles; t += nwaves) {
+            const vec_t* __restrict__ p = xv + t * TILE + lane;
+            vec_t v[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) accumulate4<Op>(acc, v[u]);
+        }
+    } else if (t < ntiles) {
+        // Two register buffers, a and b, alternate: the loads of the next
+        // tile go into one while the other is folded, so the wait before a
+        // fold leaves the next tile's loads in flight.
+        vec_t a[UNROLL], b[UNROLL];
+        load_tile<NT>(a, xv + t * TILE + lane);
+        while (true) {
+            if (t + nwaves >= ntiles) {
+                fold_tile<Op>(acc, a);
+                break;
+            }
+            load_tile<NT>(b, xv + (t + nwaves) * TILE + lane);
+            fold_tile<Op>(acc, a);
+            t += nwaves;
+            if (t + nwaves >= ntiles) {
+                fold_tile<Op>(acc, b);
+                break;
+            }
+            load_tile<NT>(a, xv + (t + nwaves) * TILE + lane);
+            fold_tile<Op>(acc, b);
+            t += nwaves;
+        }
+    }
+    // Vectors after the last whole tile (fewer than one tile).
+    const size_t w = (size_t)blockIdx.x * W + wave;
+    for (size_t i = ntiles * TILE + w * kWave + lane; i < nvec; i += nwaves * kWave)
+        accumulate4<Op>(acc, load_vec<NT>(xv + i));
+}
+
+// mode: kCombineTicket (the last block combines), kCombineTwoPass (each
+// block stores its partial; combine_partials_kernel runs next; a grid of one
+// block stores the result directly) or kPartialsOnly (every block, even a
+// lone one, stores its partial).
+enum { kPartialsOnly = 2 };
+
+template <class Op, int BLOCK, int UNROLL, bool NT, int LAYOUT, bool PREFETCH>
+__global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
+    const typename Op::elem_t* __restrict__ x, size_t n,
+    typename Op::acc_t* __restrict__ partials, unsigned int* __restrict__ ticket,
+    typename Op::out_t* __restrict__ out, int mode) {
+    using acc_t = typename Op::acc_t;
+    using vec_t = typename Op::vec_t;
+    using elem_t = typename Op::elem_t;
+    __shared__ acc_t lds[BLOCK / kWave > 0 ? BLOCK / kWave : 1];
+    __shared__ int is_last;
+
+    // Split x into head (scalar), 16-byte aligned body, tail (scalar).
+    const size_t head = head_elems(x, sizeof(elem_t), n);
+    const size_t nvec = (n - head) / 4;
+    const size_t tail0 = head + 4 * nvec;
+    const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x + head);
+
+    acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
+
+    // Step 1: the body.
+    if constexpr (LAYOUT == kGridStride)
+        body_grid_stride<Op, BLOCK, UNROLL, NT>(xv, nvec, acc);
+    else
+        body_wave_tiles<Op, BLOCK, UNROLL, NT, PREFETCH>(xv, nvec, acc);
 
     // Step 2: head and tail.
     if (blockIdx.x == 0) {
@@ -65,8 +156,16 @@ __global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
     acc_t v = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
     v = block_reduce<Op, BLOCK>(v, lds);
 
+    if (mode == kPartialsOnly) {
+        if (threadIdx.x == 0) partials[blockIdx.x] = v;
+        return;
+    }
     if (gridDim.x == 1) {
         if (threadIdx.x == 0) out[0] = Op::finish(v);
+        return;
+    }
+    if (mode == kCombineTwoPass) {
+        if (threadIdx.x == 0) partials[blockIdx.x] = v;
         return;
     }
 
@@ -94,6 +193,20 @@ __global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
     }
 }
 
+// Step 6 as a second launch: one block combines np partials in index order.
+constexpr int kCombineBlock = 256;
+
+template <class Op>
+__global__ __launch_bounds__(kCombineBlock) void combine_partials_kernel(
+    const typename Op::acc_t* __restrict__ partials, unsigned int np, typename Op::out_t* __restrict__ out) {
+    using acc_t = typename Op::acc_t;
+    __shared__ acc_t lds[kCombineBlock / kWave];
+    acc_t w = Op::identity();
+    for (unsigned int j = threadIdx.x; j < np; j += kCombineBlock) w = Op::combine(w, partials[j]);
+    w = block_reduce<Op, kCombineBlock>(w, lds);
+    if (threadIdx.x == 0) out[0] = Op::finish(w);
+}
+
 __global__ void zero_words_kernel(unsigned int* p, size_t words) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
          i += (size_t)gridDim.x * blockDim.x)
@@ -106,48 +219,93 @@ hipError_t launch_zero_words(unsigned int* p, size_t words, hipStream_t stream) 
 }
 
 // ---------------------------------------------------------------------------
-// Policy dispatch: the (block, unroll, nontemporal) triples compiled in.
+// Policy dispatch: the (layout, block, unroll, nontemporal, prefetch) shapes
+// compiled in.
+//   grid-stride: block 256 / 512 / 1024, unroll 1 / 2 / 4 / 8 / 16
+//   wave tiles:  block 64 / 256 / 512 / 1024, unroll 4 / 8 / 16, prefetch 0 / 1
 // ---------------------------------------------------------------------------
 bool flat_policy_supported(const FlatPolicy& p) {
-    const bool b = p.block == 256 || p.block == 512 || p.block == 1024;
-    const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
-    return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.blocks_per_cu >= 1;
+    if (p.blocks_per_cu < 1 || (p.nontemporal != 0 && p.nontemporal != 1)) return false;
+    if (p.combine != (int)kCombineTicket && p.combine != (int)kCombineTwoPass) return false;
+    if (p.layout == kGridStride) {
+        const bool b = p.block == 256 || p.block == 512 || p.block == 1024;
+        const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
+        return b && u && p.prefetch == 0;
+    }
+    if (p.layout == kWaveTiles) {
+        const bool b = p.block == 64 || p.block == 256 || p.block == 512 || p.block == 1024;
+        const bool u = p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
+        return b && u && (p.prefetch == 0 || p.prefetch == 1);
+    }
+    return false;
 }
 
-template <class Op, int BLOCK, int UNROLL>
-static hipError_t launch_bu(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
-                            int grid, bool nt, const Workspace& ws, hipStream_t stream) {
+template <class Op, int BLOCK, int UNROLL, int LAYOUT, bool PREFETCH>
+static hipError_t launch_shape(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+                               int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
     auto* partials = static_cast<typename Op::acc_t*>(ws.partials);
-    if (nt)
-        hipLaunchKernelGGL((flat_reduce_kernel<Op, BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0,
-                           stream, x, n, partials, ws.ticket, out);
+    const int mode = out == nullptr ? (int)kPartialsOnly : p.combine;
+    if (p.nontemporal)
+        hipLaunchKernelGGL((flat_reduce_kernel<Op, BLOCK, UNROLL, true, LAYOUT, PREFETCH>), dim3(grid),
+                           dim3(BLOCK), 0, stream, x, n, partials, ws.ticket, out, mode);
     else
-        hipLaunchKernelGGL((flat_reduce_kernel<Op, BLOCK, UNROLL, false>), dim3(grid), dim3(BLOCK), 0,
-                           stream, x, n, partials, ws.ticket, out);
+        hipLaunchKernelGGL((flat_reduce_kernel<Op, BLOCK, UNROLL, false, LAYOUT, PREFETCH>), dim3(grid),
+                           dim3(BLOCK), 0, stream, x, n, partials, ws.ticket, out, mode);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || grid == 1 || mode != (int)kCombineTwoPass) return e;
+    hipLaunchKernelGGL((combine_partials_kernel<Op>), dim3(1), dim3(kCombineBlock), 0, stream,
+                       partials, (unsigned int)grid, out);
     return hipGetLastError();
 }
 
 template <class Op, int BLOCK>
-static hipError_t launch_b(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
-                           int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
-    const bool nt = p.nontemporal != 0;
+static hipError_t launch_grid_stride(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+                                     int grid, const FlatPolicy& p, const Workspace& ws,
+                                     hipStream_t stream) {
     switch (p.unroll) {
-        case 1: return launch_bu<Op, BLOCK, 1>(x, n, out, grid, nt, ws, stream);
-        case 2: return launch_bu<Op, BLOCK, 2>(x, n, out, grid, nt, ws, stream);
-        case 4: return launch_bu<Op, BLOCK, 4>(x, n, out, grid, nt, ws, stream);
-        case 8: return launch_bu<Op, BLOCK, 8>(x, n, out, grid, nt, ws, stream);
-        case 16: return launch_bu<Op, BLOCK, 16>(x, n, out, grid, nt, ws, stream);
+        case 1: return launch_shape<Op, BLOCK, 1, kGridStride, false>(x, n, out, grid, p, ws, stream);
+        case 2: return launch_shape<Op, BLOCK, 2, kGridStride, false>(x, n, out, grid, p, ws, stream);
+        case 4: return launch_shape<Op, BLOCK, 4, kGridStride, false>(x, n, out, grid, p, ws, stream);
+        case 8: return launch_shape<Op, BLOCK, 8, kGridStride, false>(x, n, out, grid, p, ws, stream);
+        case 16: return launch_shape<Op, BLOCK, 16, kGridStride, false>(x, n, out, grid, p, ws, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+template <class Op, int BLOCK, bool PREFETCH>
+static hipError_t launch_tiles_p(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+                                 int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
+    switch (p.unroll) {
+        case 4: return launch_shape<Op, BLOCK, 4, kWaveTiles, PREFETCH>(x, n, out, grid, p, ws, stream);
+        case 8: return launch_shape<Op, BLOCK, 8, kWaveTiles, PREFETCH>(x, n, out, grid, p, ws, stream);
+        case 16: return launch_shape<Op, BLOCK, 16, kWaveTiles, PREFETCH>(x, n, out, grid, p, ws, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class Op, int BLOCK>
+static hipError_t launch_tiles(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+                               int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
+    if (p.prefetch) return launch_tiles_p<Op, BLOCK, true>(x, n, out, grid, p, ws, stream);
+    return launch_tiles_p<Op, BLOCK, false>(x, n, out, grid, p, ws, stream);
 }
 
 template <class Op>
 static hipError_t launch_op(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
                             int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
+    if (p.layout == kGridStride) {
+        switch (p.block) {
+            case 256: return launch_grid_stride<Op, 256>(x, n, out, grid, p, ws, stream);
+            case 512: return launch_grid_stride<Op, 512>(x, n, out, grid, p, ws, stream);
+            case 1024: return launch_grid_stride<Op, 1024>(x, n, out, grid, p, ws, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (p.block) {
-        case 256: return launch_b<Op, 256>(x, n, out, grid, p, ws, stream);
-        case 512: return launch_b<Op, 512>(x, n, out, grid, p, ws, stream);
-        case 1024: return launch_b<Op, 1024>(x, n, out, grid, p, ws, stream);
+        case 64: return launch_tiles<Op, 64>(x, n, out, grid, p, ws, stream);
+        case 256: return launch_tiles<Op, 256>(x, n, out, grid, p, ws, stream);
+        case 512: return launch_tiles<Op, 512>(x, n, out, grid, p, ws, stream);
+        case 1024: return launch_tiles<Op, 1024>(x, n, out, grid, p, ws, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -165,6 +323,20 @@ hipError_t launch_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, int grid
 hipError_t launch_max_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
                           const Workspace& ws, hipStream_t stream) {
     return launch_op<MaxF32>(x, n, out, grid, p, ws, stream);
+}
+
+hipError_t launch_sum_f32_partials(const float* x, size_t n, double* partials, int grid,
+                                   const FlatPolicy& p, hipStream_t stream) {
+    Workspace ws;
+    ws.ticket = nullptr;
+    ws.partials = partials;
+    ws.max_partials = (size_t)grid;
+    return launch_op<SumF32>(x, n, nullptr, grid, p, ws, stream);
+}
+
+hipError_t launch_xor_u32(const uint32_t* x, size_t n, uint32_t* out, int grid, const FlatPolicy& p,
+                          const Workspace& ws, hipStream_t stream) {
+    return launch_op<XorU32>(x, n, out, grid, p, ws, stream);
 }
 
 }  // namespace libred

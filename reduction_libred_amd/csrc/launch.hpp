@@ -9,16 +9,23 @@
 
 namespace libred {
 
-// Launch shape of the single-value kernels. `block` threads per block
-// (256, 512 or 1024), at most `blocks_per_cu` blocks per compute unit,
-// `unroll` independent 16-byte loads in flight per thread per iteration
-// (1, 2, 4, 8 or 16), `nontemporal` marks the streaming loads as
-// non-temporal.
+// Launch shape of the single-value kernels: `block` threads per block, at
+// most `blocks_per_cu` blocks per compute unit, `unroll` independent 16-byte
+// loads in flight per lane per loop trip, `nontemporal` marks the streaming
+// loads non-temporal, `layout` 0 = grid-stride, 1 = wave tiles, `prefetch`
+// (wave tiles only) issues the next tile before folding the current one,
+// `combine` 0 = last block combines, 1 = a second one-block launch does.
+enum { kGridStride = 0, kWaveTiles = 1 };
+enum { kCombineTicket = 0, kCombineTwoPass = 1 };
+
 struct FlatPolicy {
     int block;
     int blocks_per_cu;
     int unroll;
     int nontemporal;
+    int layout;
+    int prefetch;
+    int combine;
 };
 
 // Launch shape of the row kernels: `block` threads (one row per 64-lane
@@ -50,6 +57,11 @@ hipError_t launch_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, int grid
 hipError_t launch_max_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
                           const Workspace& ws, hipStream_t stream);
 
+// Steps 1-5 of the float32 sum only: one float64 partial per block into
+// partials[0..grid), whatever p.combine says.
+hipError_t launch_sum_f32_partials(const float* x, size_t n, double* partials, int grid,
+                                   const FlatPolicy& p, hipStream_t stream);
+
 // Zero `words` 32-bit words at p (used once, when a workspace is created).
 hipError_t launch_zero_words(unsigned int* p, size_t words, hipStream_t stream);
 
@@ -69,11 +81,11 @@ hipError_t launch_rung(int rung, const float* x, size_t n, float* partials, size
 hipError_t launch_combine_partials_f32(const float* partials, size_t np, float* out,
                                        hipStream_t stream);
 
-// Probes: a plain copy y = x, and a read-only stream over x that writes to
-// *sink only if the data hold an impossible pattern (so no load can be
-// dropped). Both use 16-byte accesses with a scalar head and tail.
+// Probes: a plain copy y = x with 16-byte accesses and a scalar tail, and
+// the single-value kernel with an xor fold (*out = xor of all words), which
+// reads like the reductions but does one ALU op per element.
 hipError_t launch_copy_f32(const float* x, float* y, size_t n, int grid, hipStream_t stream);
-hipError_t launch_read_f32(const float* x, size_t n, unsigned int* sink, int grid,
-                           hipStream_t stream);
+hipError_t launch_xor_u32(const uint32_t* x, size_t n, uint32_t* out, int grid, const FlatPolicy& p,
+                          const Workspace& ws, hipStream_t stream);
 
 }  // namespace libred

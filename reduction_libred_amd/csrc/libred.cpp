@@ -42,9 +42,22 @@ std::mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 
-// Defaults, chosen by measurement on MI355X (256 CUs).
-constexpr FlatPolicy kDefaultFlat = {256, 8, 4, 1};
-constexpr RowsPolicy kDefaultRows = {256, 4, 1, 1 << 20};
+// Default launch shapes, chosen by measurement on MI355X (256 CUs, 8 TB/s):
+// single-wave blocks streaming 8 KiB tiles with the next tile in flight and
+// a second one-block launch for the combine. Arrays that fit in the 256 MB
+// Infinity Cache prefer fewer, larger blocks; tiny arrays fewer blocks.
+constexpr FlatPolicy kFlatSmall = {64, 1, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
+constexpr FlatPolicy kFlatCached = {1024, 1, 4, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
+constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
+constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
+constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
+constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024};
+
+FlatPolicy default_flat(size_t n) {
+    if (n <= kSmallMax) return kFlatSmall;
+    if (n <= kCachedMax) return kFlatCached;
+    return kFlatLarge;
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -106,9 +119,10 @@ red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
     return RED_OK;
 }
 
-FlatPolicy to_flat(const red_flat_policy* p) {
-    if (!p) return kDefaultFlat;
-    FlatPolicy f = {p->block, p->blocks_per_cu, p->unroll, p->nontemporal};
+FlatPolicy to_flat(const red_flat_policy* p, size_t n) {
+    if (!p) return default_flat(n);
+    FlatPolicy f = {p->block,  p->blocks_per_cu, p->unroll,  p->nontemporal,
+                    p->layout, p->prefetch,      p->combine};
     return f;
 }
 
@@ -135,7 +149,7 @@ red_status flat_call(const In* x, size_t n, Out* out, const red_flat_policy* pol
     if (n > RED_MAX_N || (n > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
     if (!aligned(x, sizeof(In)) || !aligned(out, sizeof(Out))) return RED_ERR_INVALID_ARG;
     if (overlap(x, n * sizeof(In), out, sizeof(Out))) return RED_ERR_INVALID_ARG;
-    const FlatPolicy p = to_flat(pol);
+    const FlatPolicy p = to_flat(pol, n);
     if (!libred::flat_policy_supported(p)) return RED_ERR_INVALID_ARG;
     int dev;
     DeviceInfo info;
@@ -243,12 +257,16 @@ red_status red_ablate_sum_f32(int rung, const float* x, size_t n, float* partial
     return RED_OK;
 }
 
-void red_default_flat_policy(red_flat_policy* p) {
+void red_default_flat_policy(size_t n, red_flat_policy* p) {
     if (!p) return;
-    p->block = kDefaultFlat.block;
-    p->blocks_per_cu = kDefaultFlat.blocks_per_cu;
-    p->unroll = kDefaultFlat.unroll;
-    p->nontemporal = kDefaultFlat.nontemporal;
+    const FlatPolicy d = default_flat(n);
+    p->block = d.block;
+    p->blocks_per_cu = d.blocks_per_cu;
+    p->unroll = d.unroll;
+    p->nontemporal = d.nontemporal;
+    p->layout = d.layout;
+    p->prefetch = d.prefetch;
+    p->combine = d.combine;
 }
 
 void red_default_rows_policy(red_rows_policy* p) {
@@ -260,12 +278,32 @@ void red_default_rows_policy(red_rows_policy* p) {
 }
 
 size_t red_flat_grid(size_t n, const red_flat_policy* pol) {
-    const FlatPolicy p = to_flat(pol);
+    const FlatPolicy p = to_flat(pol, n);
     if (!libred::flat_policy_supported(p)) return 0;
     int dev;
     DeviceInfo info;
     if (current_device(&dev, &info) != RED_OK) return 0;
     return flat_grid_for(n, p, info.cu_count);
+}
+
+red_status red_sum_f32_partials(const float* x, size_t n, double* partials, size_t partials_cap,
+                                const red_flat_policy* pol, size_t* count, hipStream_t stream) {
+    if (n > RED_MAX_N || (n > 0 && x == nullptr) || partials == nullptr || count == nullptr)
+        return RED_ERR_INVALID_ARG;
+    if (!aligned(x, sizeof(float)) || !aligned(partials, sizeof(double))) return RED_ERR_INVALID_ARG;
+    const FlatPolicy p = to_flat(pol, n);
+    if (!libred::flat_policy_supported(p)) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    const size_t grid = flat_grid_for(n, p, info.cu_count);
+    if (partials_cap < grid || overlap(x, n * sizeof(float), partials, grid * sizeof(double)))
+        return RED_ERR_INVALID_ARG;
+    *count = grid;
+    const hipError_t e = libred::launch_sum_f32_partials(x, n, partials, (int)grid, p, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
 }
 
 red_status red_sum_f32_with(const float* x, size_t n, float* out, const red_flat_policy* p,
@@ -318,20 +356,8 @@ red_status red_probe_copy_f32(const float* x, float* y, size_t n, hipStream_t st
 }
 
 red_status red_probe_read_f32(const float* x, size_t n, unsigned int* sink, hipStream_t stream) {
-    if (n > RED_MAX_N || (n > 0 && x == nullptr) || sink == nullptr) return RED_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(sink, 4) || overlap(x, n * 4, sink, 4)) return RED_ERR_INVALID_ARG;
-    int dev;
-    DeviceInfo info;
-    const red_status st = current_device(&dev, &info);
-    if (st != RED_OK) return st;
-    if (n == 0) return RED_OK;
-    size_t grid = (n / 4 + 1023) / 1024;
-    const size_t cap = (size_t)8 * info.cu_count;
-    if (grid > cap) grid = cap;
-    if (grid < 1) grid = 1;
-    const hipError_t e = libred::launch_read_f32(x, n, sink, (int)grid, stream);
-    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
-    return RED_OK;
+    return flat_call(reinterpret_cast<const uint32_t*>(x), n, reinterpret_cast<uint32_t*>(sink), nullptr,
+                     stream, libred::launch_xor_u32);
 }
 
 red_status red_device_info(int* cu_count, char* arch, size_t arch_len) {

@@ -77,6 +77,32 @@ def test_flat_argument_errors():
     assert L.red_sum_f32_with(_p(A), 4, _p(B), None, None) == INVALID
 
 
+def test_partials_argument_errors():
+    L = rl.lib()
+    cnt = ctypes.c_size_t()
+    P = 0x40000
+    assert L.red_sum_f32_partials(None, 4, _p(P), 8, None, ctypes.byref(cnt), None) == INVALID
+    assert L.red_sum_f32_partials(_p(A), 4, None, 8, None, ctypes.byref(cnt), None) == INVALID
+    assert L.red_sum_f32_partials(_p(A), 4, _p(P), 8, None, None, None) == INVALID
+    assert L.red_sum_f32_partials(_p(A), 4, _p(P + 4), 8, None, ctypes.byref(cnt), None) == INVALID
+    bad = rl.FlatPolicy(64, 1, 8, 1, 0, 0, 1)        # grid-stride has no 64-thread blocks
+    assert L.red_sum_f32_partials(_p(A), 4, _p(P), 8, ctypes.byref(bad), ctypes.byref(cnt), None) == INVALID
+    bad = rl.FlatPolicy(64, 1, 8, 1, 1, 1, 2)        # no combine mode 2
+    assert L.red_sum_f32_with(_p(A), 4, _p(B), ctypes.byref(bad), None) == INVALID
+
+
+def test_default_policies():
+    small, mid, big = rl.FlatPolicy(), rl.FlatPolicy(), rl.FlatPolicy()
+    rl.lib().red_default_flat_policy(1 << 20, ctypes.byref(small))
+    rl.lib().red_default_flat_policy(1 << 24, ctypes.byref(mid))
+    rl.lib().red_default_flat_policy(1 << 28, ctypes.byref(big))
+    for p in (small, mid, big):
+        assert p.layout == 1 and p.combine == 1 and p.nontemporal == 1
+    assert big.as_dict() == rl.red_default_flat_policy(1_000_000_007).as_dict()
+    r = rl.red_default_rows_policy()
+    assert r.block % 64 == 0 and r.max_blocks >= 1
+
+
 def test_rows_argument_errors():
     L = rl.lib()
     for f in (L.red_rows_sum_f32, L.red_rows_max_f32):

@@ -119,18 +119,49 @@ def test_sum_f32_nonfinite():
             assert (math.isnan(got) if want == "nan" else got == want), (xs, got)
 
 
+def all_flat_policies(bpcs=(1, 4)):
+    """Every compiled launch shape of the single-value kernels."""
+    shapes = []
+    for bpc in bpcs:
+        for nt in (0, 1):
+            for combine in (0, 1):
+                for block in (256, 512, 1024):
+                    for unroll in (1, 2, 4, 8, 16):
+                        shapes.append(dict(block=block, blocks_per_cu=bpc, unroll=unroll, nontemporal=nt,
+                                           layout=0, prefetch=0, combine=combine))
+                for block in (64, 256, 512, 1024):
+                    for unroll in (4, 8, 16):
+                        for pf in (0, 1):
+                            shapes.append(dict(block=block, blocks_per_cu=bpc, unroll=unroll,
+                                               nontemporal=nt, layout=1, prefetch=pf, combine=combine))
+    return shapes
+
+
 def test_sum_f32_all_policies_agree():
-    a = W.make("normal", (1 << 21) + 3, 77)
-    x = device_view(a, 2)
-    S, A = oracle.sum_f32(a)
-    for block in (256, 512, 1024):
-        for unroll in (1, 2, 4, 8, 16):
-            for nt in (0, 1):
-                for bpc in (1, 4, 8):
-                    say(f"sum_f32 policy block={block} unroll={unroll} nt={nt} bpc={bpc}")
-                    got = gpu_sum(x, policy=dict(block=block, blocks_per_cu=bpc, unroll=unroll,
-                                                 nontemporal=nt))
-                    assert oracle.sum_within_tolerance(got, S, A), (block, unroll, nt, bpc, got, S)
+    # Sizes that leave whole tiles, a partial tile and a ragged tail.
+    for n, off in (((1 << 21) + 3, 2), ((1 << 23) + 4099, 1)):
+        a = W.make("normal", n, 77)
+        x = device_view(a, off)
+        S, A = oracle.sum_f32(a)
+        for p in all_flat_policies():
+            say(f"sum_f32 n={n} policy {p}")
+            got = gpu_sum(x, policy=p)
+            assert oracle.sum_within_tolerance(got, S, A), (p, got, S)
+
+
+def test_sum_f32_partials():
+    # Steps 1-5 alone: one float64 partial per block; their sum is the sum.
+    for n, off in ((1, 0), (1000, 1), ((1 << 20) + 3, 2), ((1 << 24) + 5, 3), ((1 << 26) + 77, 1)):
+        a = W.make("normal", n, 500 + off)
+        x = device_view(a, off)
+        S, A = oracle.sum_f32(a)
+        for p in (None, dict(layout=0, block=256, blocks_per_cu=1, unroll=8, prefetch=0)):
+            say(f"sum_f32_partials n={n} policy={p}")
+            parts = rl.red_sum_f32_partials(x, policy=p)
+            torch.cuda.synchronize()
+            assert parts.numel() == rl.red_flat_grid(n, p)
+            got = math.fsum(parts.cpu().numpy().tolist())
+            assert abs(got - S) <= 1e-9 * A + 1e-12, (n, p, got, S)
 
 
 def test_sum_f32_two_streams():
@@ -220,14 +251,23 @@ def test_max_f32_all_policies():
     a = W.make("normal", (1 << 21) + 1, 78)
     a[(1 << 21) - 77] = 99.0
     x = device_view(a, 3, guard=float("inf"))
-    for block in (256, 512, 1024):
-        for unroll in (1, 4, 16):
-            for nt in (0, 1):
-                say(f"max_f32 policy block={block} unroll={unroll} nt={nt}")
-                out = rl.red_max_f32(x, policy=dict(block=block, blocks_per_cu=8, unroll=unroll,
-                                                     nontemporal=nt))
-                torch.cuda.synchronize()
-                assert out.item() == 99.0
+    for p in all_flat_policies(bpcs=(2,)):
+        say(f"max_f32 policy {p}")
+        out = rl.red_max_f32(x, policy=p)
+        torch.cuda.synchronize()
+        assert out.item() == 99.0, p
+
+
+def test_sum_i32_all_policies():
+    rng = np.random.default_rng(79)
+    a = rng.integers(-(2 ** 31), 2 ** 31, (1 << 21) + 5, dtype=np.int64).astype(np.int32)
+    want = oracle.sum_i32_i64(a)
+    x = device_view(a, 1)
+    for p in all_flat_policies(bpcs=(1,)):
+        say(f"sum_i32 policy {p}")
+        out = rl.red_sum_i32_i64(x, policy=p)
+        torch.cuda.synchronize()
+        assert int(out.item()) == want, p
 
 
 # ----------------------------------------------------------------- rows
@@ -331,10 +371,11 @@ def test_probes():
     x = torch.from_numpy(a).to(DEV)
     y = torch.empty_like(x)
     rl.red_probe_copy_f32(x, y)
-    sink = rl.red_probe_read_f32(x)
+    sink = rl.red_probe_read_f32(x[1:])
     torch.cuda.synchronize()
     assert torch.equal(x, y)
-    assert sink.numel() == 1
+    want = int(np.bitwise_xor.reduce(a[1:].view(np.uint32)))
+    assert int(sink.item()) & 0xFFFFFFFF == want
     cu, arch = rl.red_device_info()
     assert cu > 0 and arch.startswith("gfx950")
 
