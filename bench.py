@@ -27,31 +27,33 @@ PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "achieved HBM GB/s (% of MI355X peak) for f32 sum over 2^28 elements"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["reduction_libred_amd/csrc/flat_reduce.hip",
-                  "reduction_libred_amd/csrc/device_common.hpp",
-                  "reduction_libred_amd/csrc/libred.cpp"]
+                  "reduction_libred_amd/csrc/device_common.hpp"]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(policy):
+    """Identity of the streaming kernel as launched: its device sources and
+    the launch shape."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as fh:
             h.update(fh.read())
+    h.update(json.dumps(policy, sort_keys=True).encode())
     return h.hexdigest()
 
 
-def recorded_traffic():
+def recorded_traffic(policy):
     """HBM bytes per launch of the sum kernel from the committed counter
-    runs, or None if the kernel sources changed since they were taken."""
+    runs, or None if the kernel or its launch shape changed since then."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(policy):
         return None
     return rec.get("flat_reduce_kernel_sum_f32_2p28_bytes_per_launch")
 
@@ -64,7 +66,75 @@ def parse_args():
     ap.add_argument("--quick", action="store_true", help="headline only: skip the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the CPU oracle baseline (0 to skip)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of the headline: time the five-rung ladder and the production "
+                         "path on the 2^28 array, and the LDS bank probe; print one JSON line")
     return ap.parse_args()
+
+
+# Barriers per 256-thread block, by construction of each rung's kernel: one
+# after the LDS store, then one per tree step (8 steps from 256 to 1 for rungs
+# 1-4, one step from 256 to 128 for rung 5). The production kernel's default
+# 64-thread blocks need none; its combine pass has one.
+RUNG_BARRIERS = {1: 9, 2: 9, 3: 9, 4: 9, 5: 2}
+RUNG_NAMES = {1: "interleaved, divergent", 2: "interleaved, strided (bank conflicts)",
+              3: "sequential addressing", 4: "first add during load", 5: "wave64 shuffle finish",
+              6: "production (wave tiles + DPP)"}
+LDS_STRIDES = [1, 2, 4, 8, 16, 32, 64, 128, 3, 33, 65, 0, -1]
+
+
+def run_ablation(args, torch, rl, W, timer, dev):
+    name = "sum_max_f32_2p28"
+    log(f"generate {name}")
+    x = torch.from_numpy(W.workload(name)).to(dev)
+    n = x.numel()
+    rungs = []
+    out = torch.empty((), dtype=torch.float32, device=dev)
+    for rung in range(1, 6):
+        np_ = rl.red_ablate_num_partials(rung, n)
+        partials = torch.empty(np_, dtype=torch.float32, device=dev)
+
+        def kern():
+            rl.red_ablate_sum_f32(rung, x, partials=partials, partials_only=True)
+
+        for _ in range(args.warmup):
+            kern()
+        ms = timer.region_ms(kern, args.steps)
+        rl.red_ablate_sum_f32(rung, x, partials=partials, out=out)
+        torch.cuda.synchronize()
+        rungs.append({"rung": rung, "what": RUNG_NAMES[rung], "blocks": np_, "block_threads": 256,
+                      "barriers_per_block": RUNG_BARRIERS[rung], "kernel_us": round(ms * 1e3, 2),
+                      "GB/s": round(gbps(4 * n, ms), 1), "pct_of_peak": round(100 * gbps(4 * n, ms) / PEAK_GBPS, 2),
+                      "sum": out.item()})
+        log(f"rung {rung}: {rungs[-1]}")
+        del partials
+    pol = rl.red_default_flat_policy(n).as_dict()
+    grid = rl.red_flat_grid(n)
+    parts = torch.empty(grid, dtype=torch.float64, device=dev)
+    kern6 = lambda: rl.red_sum_f32_partials(x, partials=parts)
+    for _ in range(args.warmup):
+        kern6()
+    ms = timer.region_ms(kern6, args.steps)
+    rl.red_sum_f32(x, out=out)
+    torch.cuda.synchronize()
+    rungs.append({"rung": 6, "what": RUNG_NAMES[6], "blocks": grid, "block_threads": pol["block"],
+                  "barriers_per_block": 0 if pol["block"] == 64 else 1, "kernel_us": round(ms * 1e3, 2),
+                  "GB/s": round(gbps(4 * n, ms), 1), "pct_of_peak": round(100 * gbps(4 * n, ms) / PEAK_GBPS, 2),
+                  "sum": out.item(), "policy": pol})
+    log(f"rung 6: {rungs[-1]}")
+    del x
+    probe = []
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    iters = 4096
+    rl.red_probe_lds_stride(1, iters, sink)          # load the kernel before timing
+    for stride in LDS_STRIDES:
+        ms = timer.region_ms(lambda: rl.red_probe_lds_stride(stride, iters, sink), 5)
+        probe.append({"stride": stride, "us_per_launch": round(ms * 1e3, 2),
+                      "ns_per_read": round(ms * 1e6 / iters, 3)})
+        log(f"lds stride {stride}: {probe[-1]}")
+    print(json.dumps({"mode": "ablation", "workload": name, "n": n, "steps": args.steps,
+                      "rungs": rungs, "lds_probe": {"iters": iters, "words": 64 * 65, "strides": probe}}),
+          flush=True)
 
 
 class Timer:
@@ -128,6 +198,9 @@ def main():
     timer = Timer(torch, stream)
     cu, arch = rl.red_device_info()
     log(f"device: {torch.cuda.get_device_name(dev)} {arch}, {cu} CUs; {rl.red_version()}")
+    if args.ablation:
+        run_ablation(args, torch, rl, W, timer, dev)
+        return
 
     # ---------------------------------------------------------- headline
     name = "sum_max_f32_2p28"
@@ -206,7 +279,7 @@ def main():
             "peak": PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4),
-            "traffic": recorded_traffic(),
+            "traffic": recorded_traffic(policy),
             "kernel": kname,
             "algorithmic_bytes_per_launch": nbytes,
             "avg_launch_us": round(k_ms * 1e3, 3),

@@ -27,11 +27,13 @@ extern "C" {
  *
  * Rungs 1-5 write one float32 partial per block into partials[0..np), where
  * np = red_ablate_num_partials(rung, n), each partial summed in float32 by
- * an LDS tree as on the page (elements past n count as 0), and then *out =
- * the float64 sum of the partials, rounded once to float32 (the page does
- * this last step on the host). partials_cap is the capacity of `partials` in
- * elements; a capacity below np, a rung outside 1..6, n == 0 or
- * n > 2^31 for rungs 1-5 is RED_ERR_INVALID_ARG.
+ * an LDS tree as on the page (elements past n count as 0). Then, unless out
+ * is NULL, *out = the float64 sum of the partials rounded once to float32
+ * (the page does this last step on the host; here red_sum_f32 does it on
+ * the device). With out == NULL only the rung's own kernel runs, which is
+ * how it is timed. partials_cap is the capacity of `partials` in elements;
+ * a capacity below np, a rung outside 1..6, n == 0, n > 2^31 for rungs 1-5,
+ * or a NULL out for rung 6 is RED_ERR_INVALID_ARG.
  */
 red_status red_ablate_sum_f32(int rung, const float *x, size_t n, float *partials,
                               size_t partials_cap, float *out, hipStream_t stream);

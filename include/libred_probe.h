@@ -27,6 +27,18 @@ red_status red_probe_copy_f32(const float *x, float *y, size_t n, hipStream_t st
  * x and sink must be 4-byte aligned and must not overlap. */
 red_status red_probe_read_f32(const float *x, size_t n, unsigned int *sink, hipStream_t stream);
 
+/*
+ * LDS bank probe, after the reduction lesson's demo 1 (how many rounds one
+ * warp's shared-memory read takes for a given stride), for a 64-lane wave:
+ * one wave fills LDS word i with i (64 * 65 words), then each lane l reads
+ * word (l * stride) mod 4160 -- or word l / 2 when stride == -1 -- `iters`
+ * times, and the sum of everything read is added to *sink (which the caller
+ * zeroes). Stride 0 is a broadcast. The bank-conflict counters of this
+ * kernel, per stride, give the hardware's bank geometry. stride outside
+ * [-1, 2^20], iters outside [0, 2^24] or a NULL sink is RED_ERR_INVALID_ARG.
+ */
+red_status red_probe_lds_stride(int stride, int iters, unsigned int *sink, hipStream_t stream);
+
 /* Facts about the current device: compute-unit count and architecture name
  * (e.g. "gfx950:sramecc+:xnack-"), copied into arch[0..arch_len). */
 red_status red_device_info(int *cu_count, char *arch, size_t arch_len);

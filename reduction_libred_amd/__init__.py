@@ -84,6 +84,7 @@ SIGNATURES = {
     "red_probe_copy_f32": (_S, [_P, _P, _Z, _P]),
     "red_probe_read_f32": (_S, [_P, _Z, _P, _P]),
     "red_device_info": (_S, [ctypes.POINTER(_I), ctypes.c_char_p, _Z]),
+    "red_probe_lds_stride": (_S, [_I, _I, _P, _P]),
 }
 
 _lib = None
@@ -212,19 +213,22 @@ def red_ablate_num_partials(rung, n):
     return int(lib().red_ablate_num_partials(rung, n))
 
 
-def red_ablate_sum_f32(rung, x, partials=None, out=None, stream=None):
-    """Ablation rung 1..6 of the f32 sum. Returns (out, partials)."""
+def red_ablate_sum_f32(rung, x, partials=None, out=None, stream=None, partials_only=False):
+    """Ablation rung 1..6 of the f32 sum. Returns (out, partials); with
+    partials_only=True only the rung's kernel runs and out is None."""
     _input(x, torch.float32, "red_ablate_sum_f32")
     n = x.numel()
     np_ = max(red_ablate_num_partials(rung, n), 1)
     if partials is None:
         partials = torch.empty(np_, dtype=torch.float32, device=x.device)
-    out = _output(out, (), torch.float32, x.device, "red_ablate_sum_f32")
+    if not partials_only:
+        out = _output(out, (), torch.float32, x.device, "red_ablate_sum_f32")
     with torch.cuda.device(x.device):
         st = lib().red_ablate_sum_f32(rung, x.data_ptr(), n, partials.data_ptr(), partials.numel(),
-                                      out.data_ptr(), _stream_handle(stream, x.device))
+                                      None if partials_only else out.data_ptr(),
+                                      _stream_handle(stream, x.device))
     _check("red_ablate_sum_f32", st)
-    return out, partials
+    return (None if partials_only else out), partials
 
 
 def red_default_flat_policy(n):
@@ -280,6 +284,15 @@ def red_probe_read_f32(x, sink=None, stream=None):
     with torch.cuda.device(x.device):
         st = lib().red_probe_read_f32(x.data_ptr(), x.numel(), sink.data_ptr(), _stream_handle(stream, x.device))
     _check("red_probe_read_f32", st)
+    return sink
+
+
+def red_probe_lds_stride(stride, iters, sink, stream=None):
+    """LDS bank probe: one wave reads word (lane*stride) mod 4160 (lane/2 for
+    stride -1) `iters` times; the sum read is added to int32 tensor sink[0]."""
+    with torch.cuda.device(sink.device):
+        st = lib().red_probe_lds_stride(stride, iters, sink.data_ptr(), _stream_handle(stream, sink.device))
+    _check("red_probe_lds_stride", st)
     return sink
 
 

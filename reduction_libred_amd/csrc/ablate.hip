@@ -16,8 +16,9 @@
 //     8, 4, 2, 1 (the lesson folds to a 32-lane warp and shuffles five times;
 //     a gfx950 wave has 64 lanes, so here it is one fold and six shuffles).
 // Elements past n read as 0 (the lesson's ladder assumes n is a multiple of
-// the block's span; here any n works). A one-block kernel then sums the
-// partials in float64 and rounds once, as the lesson's host does.
+// the block's span; here any n works). The partials are then summed in
+// float64 and rounded once, as the lesson's host does (by the library's own
+// float sum, in the C ABI layer).
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -101,16 +102,6 @@ __global__ __launch_bounds__(B) void rung5_wave_shuffle(const float* __restrict_
     }
 }
 
-// Sum of np float partials in float64 with one block, rounded once.
-__global__ __launch_bounds__(B) void combine_partials_f32(const float* __restrict__ partials,
-                                                          size_t np, float* __restrict__ out) {
-    __shared__ double lds[B / kWave];
-    double v = 0.0;
-    for (size_t j = threadIdx.x; j < np; j += B) v += (double)partials[j];
-    v = block_reduce<SumF32, B>(v, lds);
-    if (threadIdx.x == 0) out[0] = (float)v;
-}
-
 size_t rung_elems_per_block(int rung) { return (rung == 4 || rung == 5) ? 2 * B : B; }
 
 hipError_t launch_rung(int rung, const float* x, size_t n, float* partials, size_t nblocks,
@@ -124,12 +115,6 @@ hipError_t launch_rung(int rung, const float* x, size_t n, float* partials, size
         case 5: hipLaunchKernelGGL(rung5_wave_shuffle, grid, block, 0, stream, x, n, partials); break;
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
-}
-
-hipError_t launch_combine_partials_f32(const float* partials, size_t np, float* out,
-                                       hipStream_t stream) {
-    hipLaunchKernelGGL(combine_partials_f32, dim3(1), dim3(B), 0, stream, partials, np, out);
     return hipGetLastError();
 }
 

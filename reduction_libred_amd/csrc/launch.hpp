@@ -72,14 +72,16 @@ hipError_t launch_rows_max_f32(const float* x, size_t rows, size_t cols, float* 
                                const RowsPolicy& p, hipStream_t stream);
 
 // Ablation ladder: rung 1..5 writes one float partial per block of
-// kRungBlock threads into `partials`; then a one-block kernel sums the
-// partials in float64 into *out.
+// kRungBlock threads into `partials`.
 constexpr int kRungBlock = 256;
 size_t rung_elems_per_block(int rung);
 hipError_t launch_rung(int rung, const float* x, size_t n, float* partials, size_t nblocks,
                        hipStream_t stream);
-hipError_t launch_combine_partials_f32(const float* partials, size_t np, float* out,
-                                       hipStream_t stream);
+
+// LDS bank probe: one wave reads LDS word (lane * stride) mod kLdsProbeWords
+// (stride -1: lane / 2) `iters` times; *sink = the sum of all values read.
+constexpr int kLdsProbeWords = 64 * 65;
+hipError_t launch_lds_stride(int stride, int iters, unsigned int* sink, hipStream_t stream);
 
 // Probes: a plain copy y = x with 16-byte accesses and a scalar tail, and
 // the single-value kernel with an xor fold (*out = xor of all words), which

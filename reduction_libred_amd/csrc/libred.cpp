@@ -239,22 +239,23 @@ red_status red_ablate_sum_f32(int rung, const float* x, size_t n, float* partial
                               float* out, hipStream_t stream) {
     if (rung == 6) return red_sum_f32(x, n, out, stream);
     if (rung < 1 || rung > 5) return RED_ERR_INVALID_ARG;
-    if (n == 0 || n > ((size_t)1 << 31) || x == nullptr || partials == nullptr || out == nullptr)
-        return RED_ERR_INVALID_ARG;
+    if (n == 0 || n > ((size_t)1 << 31) || x == nullptr || partials == nullptr) return RED_ERR_INVALID_ARG;
     if (!aligned(x, 4) || !aligned(partials, 4) || !aligned(out, 4)) return RED_ERR_INVALID_ARG;
     const size_t np = red_ablate_num_partials(rung, n);
     if (partials_cap < np) return RED_ERR_INVALID_ARG;
-    if (overlap(x, n * 4, partials, np * 4) || overlap(x, n * 4, out, 4) || overlap(partials, np * 4, out, 4))
+    if (overlap(x, n * 4, partials, np * 4) || overlap(x, n * 4, out, out ? 4 : 0) ||
+        overlap(partials, np * 4, out, out ? 4 : 0))
         return RED_ERR_INVALID_ARG;
     int dev;
     DeviceInfo info;
     const red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
-    hipError_t e = libred::launch_rung(rung, x, n, partials, np, stream);
+    const hipError_t e = libred::launch_rung(rung, x, n, partials, np, stream);
     if (e != hipSuccess) return fail(e, RED_ERR_HIP);
-    e = libred::launch_combine_partials_f32(partials, np, out, stream);
-    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
-    return RED_OK;
+    if (out == nullptr) return RED_OK;
+    // The partials are float32 values; their float64 sum, rounded once, is
+    // exactly what red_sum_f32 computes over them.
+    return red_sum_f32(partials, np, out, stream);
 }
 
 void red_default_flat_policy(size_t n, red_flat_policy* p) {
@@ -358,6 +359,19 @@ red_status red_probe_copy_f32(const float* x, float* y, size_t n, hipStream_t st
 red_status red_probe_read_f32(const float* x, size_t n, unsigned int* sink, hipStream_t stream) {
     return flat_call(reinterpret_cast<const uint32_t*>(x), n, reinterpret_cast<uint32_t*>(sink), nullptr,
                      stream, libred::launch_xor_u32);
+}
+
+red_status red_probe_lds_stride(int stride, int iters, unsigned int* sink, hipStream_t stream) {
+    if (stride < -1 || stride > 1 << 20 || iters < 0 || iters > 1 << 24 || sink == nullptr ||
+        !aligned(sink, 4))
+        return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    const hipError_t e = libred::launch_lds_stride(stride, iters, sink, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
 }
 
 red_status red_device_info(int* cu_count, char* arch, size_t arch_len) {

@@ -20,6 +20,31 @@ __global__ __launch_bounds__(kProbeBlock) void copy_f32_kernel(const float* __re
     if (blockIdx.x == 0 && threadIdx.x < n - 4 * nvec) y[4 * nvec + threadIdx.x] = x[4 * nvec + threadIdx.x];
 }
 
+// LDS bank probe (the reduction lesson's demo 1, for a 64-lane wave): LDS word
+// i holds i; lane l reads word (l * stride) mod kLdsProbeWords, or l / 2 for
+// stride -1, `iters` times. Each address also depends on the previous value
+// read through `zero` (0 at run time), so the loads cannot be hoisted out of
+// the loop. The lanes' totals are summed into *sink with one atomic per
+// lane. Reading SQ_LDS_BANK_CONFLICT against SQ_INSTS_LDS for each stride
+// gives the bank geometry.
+__global__ __launch_bounds__(64) void lds_stride_kernel(int stride, int iters, unsigned int zero,
+                                                        unsigned int* __restrict__ sink) {
+    __shared__ unsigned int lds[kLdsProbeWords];
+    for (int i = threadIdx.x; i < kLdsProbeWords; i += 64) lds[i] = (unsigned int)i;
+    __syncthreads();
+    const unsigned int lane = threadIdx.x;
+    const unsigned int base =
+        stride < 0 ? lane / 2 : (lane * (unsigned int)stride) % (unsigned int)kLdsProbeWords;
+    unsigned int acc = 0;
+    for (int k = 0; k < iters; ++k) acc += lds[base + (acc & zero)];
+    atomicAdd(sink, acc);
+}
+
+hipError_t launch_lds_stride(int stride, int iters, unsigned int* sink, hipStream_t stream) {
+    hipLaunchKernelGGL(lds_stride_kernel, dim3(1), dim3(64), 0, stream, stride, iters, 0u, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_copy_f32(const float* x, float* y, size_t n, int grid, hipStream_t stream) {
     hipLaunchKernelGGL(copy_f32_kernel, dim3(grid), dim3(kProbeBlock), 0, stream, x, y, n);
     return hipGetLastError();

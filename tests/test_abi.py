@@ -130,6 +130,7 @@ def test_ablate_argument_errors():
     assert L.red_ablate_sum_f32(1, _p(A), 0, _p(P), 4, _p(B), None) == INVALID
     assert L.red_ablate_sum_f32(2, _p(A), (1 << 31) + 1, _p(P), 1 << 24, _p(B), None) == INVALID
     assert L.red_ablate_sum_f32(3, _p(A), 1000, _p(A + 64), 4, _p(B), None) == INVALID  # overlap
+    assert L.red_ablate_sum_f32(6, _p(A), 1000, _p(P), 4, None, None) == INVALID     # rung 6 needs out
 
 
 def test_probe_argument_errors():
@@ -138,6 +139,9 @@ def test_probe_argument_errors():
     assert L.red_probe_copy_f32(_p(A), _p(A + 16), 8, None) == INVALID   # overlap
     assert L.red_probe_read_f32(_p(A), 8, None, None) == INVALID
     assert L.red_device_info(None, None, 0) == INVALID
+    assert L.red_probe_lds_stride(-2, 1, _p(A), None) == INVALID
+    assert L.red_probe_lds_stride(1, -1, _p(A), None) == INVALID
+    assert L.red_probe_lds_stride(1, 1, None, None) == INVALID
 
 
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,

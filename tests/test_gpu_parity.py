@@ -362,7 +362,34 @@ def test_ablation_rungs(rung):
         assert_sum_ok(out.item(), a)
 
 
+def test_ablation_partials_only():
+    n = (1 << 20) + 3
+    a = W.pattern_mod7(n)
+    x = device_view(a, 1)
+    for rung in range(1, 6):
+        say(f"rung {rung} partials only n={n}")
+        out, partials = rl.red_ablate_sum_f32(rung, x, partials_only=True)
+        torch.cuda.synchronize()
+        assert out is None
+        span = 512 if rung >= 4 else 256
+        assert np.array_equal(partials.cpu().numpy(), _block_sums_mod7(n, span))
+
+
 # ----------------------------------------------------------------- probes
+
+def test_lds_stride_probe():
+    words = 64 * 65
+    for stride in (1, 2, 32, 33, 0, -1, 4095):
+        for iters in (0, 1, 77):
+            say(f"lds probe stride={stride} iters={iters}")
+            sink = torch.zeros(1, dtype=torch.int32, device=DEV)
+            rl.red_probe_lds_stride(stride, iters, sink)
+            torch.cuda.synchronize()
+            base = [l // 2 if stride < 0 else (l * stride) % words for l in range(64)]
+            want = (iters * sum(base)) % (1 << 32)
+            assert int(sink.item()) & 0xFFFFFFFF == want, (stride, iters)
+
+
 
 def test_probes():
     n = (1 << 20) + 3
