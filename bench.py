@@ -306,6 +306,9 @@ def main():
 
     mout = torch.empty((), dtype=torch.float32, device=dev)
     measure("red_max_f32 sum_max_f32_2p28", lambda: rl.red_max_f32(x, out=mout), nbytes)
+    fout = torch.empty(3, dtype=torch.float32, device=dev)
+    measure("red_sum_max_f32 (fused sum, max, sum|x|) sum_max_f32_2p28",
+            lambda: rl.red_sum_max_f32(x, out=fout), 4 * n + 12)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     measure("probe read sum_max_f32_2p28", lambda: rl.red_probe_read_f32(x, sink=sink), 4 * n)
     y = torch.empty_like(x)

@@ -88,6 +88,20 @@ red_status red_sum_i32_i64(const int32_t *x, size_t n, int64_t *out, hipStream_t
 red_status red_max_f32(const float *x, size_t n, float *out, hipStream_t stream);
 
 /*
+ * Sum, max and sum of magnitudes of n float32 values in one pass over x:
+ * out3[0] = x[0] + ... + x[n-1] (as red_sum_f32), out3[1] = the maximum (as
+ * red_max_f32), out3[2] = |x[0]| + ... + |x[n-1]| (float64 inside, rounded
+ * once; NaN if any x is NaN, +inf if any is infinite). One read of the data
+ * yields all three, so sum and max together cost what one of them costs.
+ * out3 must hold 3 floats and must not overlap x. n == 0 stores 0, -inf, 0.
+ * This fuses the lesson's reduction with the simulator page's max rule; the
+ * sum of magnitudes is the scale against which a float sum's error is judged.
+ * Its default launch shape differs from red_sum_f32's on large arrays (more
+ * waves per CU for the extra arithmetic).
+ */
+red_status red_sum_max_f32(const float *x, size_t n, float *out3, hipStream_t stream);
+
+/*
  * Per-row sum of a rows x cols float32 matrix stored row-major and
  * contiguously (row r is x[r*cols .. r*cols + cols)):
  * out[r] = x[r*cols] + ... + x[r*cols + cols - 1], for r < rows.

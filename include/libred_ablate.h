@@ -68,7 +68,7 @@ typedef struct red_flat_policy {
 } red_flat_policy;
 
 /* Launch shape of the row kernels: `block` threads (64, 128, 256 or 512; one
- * row per wave at a time), `unroll` loads per lane per trip (1, 2, 4 or 8),
+ * row per wave at a time), `unroll` loads per lane per trip (1, 2, 4, 8, 16),
  * `nontemporal`, and `max_blocks` capping the grid. */
 typedef struct red_rows_policy {
     int block;
@@ -106,6 +106,8 @@ red_status red_sum_i32_i64_with(const int32_t *x, size_t n, int64_t *out,
                                 const red_flat_policy *p, hipStream_t stream);
 red_status red_max_f32_with(const float *x, size_t n, float *out, const red_flat_policy *p,
                             hipStream_t stream);
+red_status red_sum_max_f32_with(const float *x, size_t n, float *out3, const red_flat_policy *p,
+                                hipStream_t stream);
 red_status red_rows_sum_f32_with(const float *x, size_t rows, size_t cols, float *out,
                                  const red_rows_policy *p, hipStream_t stream);
 red_status red_rows_max_f32_with(const float *x, size_t rows, size_t cols, float *out,

@@ -39,6 +39,28 @@ red_status red_probe_read_f32(const float *x, size_t n, unsigned int *sink, hipS
  */
 red_status red_probe_lds_stride(int stride, int iters, unsigned int *sink, hipStream_t stream);
 
+/*
+ * The wave-level combine of the production kernels, alone: for each w <
+ * nwaves, out[w] = the reduction of in[64w .. 64w + 63] by one 64-lane wave
+ * with the library's DPP sequence (quad_perm [1,0,3,2] and [2,3,0,1],
+ * row_half_mirror, row_mirror, row_bcast:15 into rows 1 and 3, row_bcast:31
+ * into rows 2 and 3, then lane 63). op 0: in/out are double, summed; op 1:
+ * int64_t, summed; op 2: float, max (strictly-greater rule). The pairing
+ * order is fixed, so a float64 result is reproducible bit for bit. op outside
+ * 0..2, nwaves outside 1..2^20, NULL or misaligned pointers, or overlap is
+ * RED_ERR_INVALID_ARG.
+ */
+red_status red_probe_wave_reduce(int op, const void *in, size_t nwaves, void *out, hipStream_t stream);
+
+/*
+ * The register shuffle of ablation rung 5, alone, with the semantics of the
+ * simulator page "simt_lab.py" (section 4, Block.shfl_down): one 64-lane
+ * wave; out[l] = in[l + offset] when l + offset < 64, else in[l]. in and out
+ * hold 64 floats. offset outside 0..64 or NULL pointers is
+ * RED_ERR_INVALID_ARG.
+ */
+red_status red_probe_shfl_down_f32(const float *in, int offset, float *out, hipStream_t stream);
+
 /* Facts about the current device: compute-unit count and architecture name
  * (e.g. "gfx950:sramecc+:xnack-"), copied into arch[0..arch_len). */
 red_status red_device_info(int *cu_count, char *arch, size_t arch_len);

@@ -65,6 +65,8 @@ SIGNATURES = {
     "red_sum_f32": (_S, [_P, _Z, _P, _P]),
     "red_sum_i32_i64": (_S, [_P, _Z, _P, _P]),
     "red_max_f32": (_S, [_P, _Z, _P, _P]),
+    "red_sum_max_f32": (_S, [_P, _Z, _P, _P]),
+    "red_sum_max_f32_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
     "red_rows_sum_f32": (_S, [_P, _Z, _Z, _P, _P]),
     "red_rows_max_f32": (_S, [_P, _Z, _Z, _P, _P]),
     "red_status_string": (ctypes.c_char_p, [_S]),
@@ -85,6 +87,8 @@ SIGNATURES = {
     "red_probe_read_f32": (_S, [_P, _Z, _P, _P]),
     "red_device_info": (_S, [ctypes.POINTER(_I), ctypes.c_char_p, _Z]),
     "red_probe_lds_stride": (_S, [_I, _I, _P, _P]),
+    "red_probe_wave_reduce": (_S, [_I, _P, _Z, _P, _P]),
+    "red_probe_shfl_down_f32": (_S, [_P, _I, _P, _P]),
 }
 
 _lib = None
@@ -151,9 +155,9 @@ def _policy(cls, p, n=0):
     return base
 
 
-def _flat(name, cname, x, out, in_dtype, out_dtype, stream, policy=None):
+def _flat(name, cname, x, out, in_dtype, out_dtype, stream, policy=None, out_shape=()):
     _input(x, in_dtype, name)
-    out = _output(out, (), out_dtype, x.device, name)
+    out = _output(out, out_shape, out_dtype, x.device, name)
     with torch.cuda.device(x.device):
         s = _stream_handle(stream, x.device)
         if policy is None:
@@ -179,6 +183,12 @@ def red_sum_i32_i64(x, out=None, stream=None, policy=None):
 def red_max_f32(x, out=None, stream=None, policy=None):
     """Maximum of a float32 tensor (NaN never wins; empty gives -inf)."""
     return _flat("red_max_f32", "red_max_f32", x, out, torch.float32, torch.float32, stream, policy)
+
+
+def red_sum_max_f32(x, out=None, stream=None, policy=None):
+    """One pass: float32[3] = (sum, max, sum of |x|)."""
+    return _flat("red_sum_max_f32", "red_sum_max_f32", x, out, torch.float32, torch.float32, stream, policy,
+                 out_shape=(3,))
 
 
 def _rows(cname, x, out, stream, policy):
@@ -294,6 +304,36 @@ def red_probe_lds_stride(stride, iters, sink, stream=None):
         st = lib().red_probe_lds_stride(stride, iters, sink.data_ptr(), _stream_handle(stream, sink.device))
     _check("red_probe_lds_stride", st)
     return sink
+
+
+_WAVE_OPS = {"sum_f64": (0, torch.float64), "sum_i64": (1, torch.int64), "max_f32": (2, torch.float32)}
+
+
+def red_probe_wave_reduce(op, x, out=None, stream=None):
+    """One 64-lane DPP wave reduce per group of 64 elements of x (op is
+    'sum_f64', 'sum_i64' or 'max_f32'); returns a tensor of x.numel() / 64."""
+    code, dt = _WAVE_OPS[op]
+    _input(x, dt, "red_probe_wave_reduce")
+    if x.numel() % 64:
+        raise ValueError("red_probe_wave_reduce: x must hold a multiple of 64 elements")
+    out = _output(out, (x.numel() // 64,), dt, x.device, "red_probe_wave_reduce")
+    with torch.cuda.device(x.device):
+        st = lib().red_probe_wave_reduce(code, x.data_ptr(), x.numel() // 64, out.data_ptr(),
+                                         _stream_handle(stream, x.device))
+    _check("red_probe_wave_reduce", st)
+    return out
+
+
+def red_probe_shfl_down_f32(x, offset, out=None, stream=None):
+    """One 64-lane shuffle-down of the 64 floats in x."""
+    _input(x, torch.float32, "red_probe_shfl_down_f32")
+    if x.numel() != 64:
+        raise ValueError("red_probe_shfl_down_f32: x must hold 64 floats")
+    out = _output(out, (64,), torch.float32, x.device, "red_probe_shfl_down_f32")
+    with torch.cuda.device(x.device):
+        st = lib().red_probe_shfl_down_f32(x.data_ptr(), offset, out.data_ptr(), _stream_handle(stream, x.device))
+    _check("red_probe_shfl_down_f32", st)
+    return out
 
 
 def red_device_info():

@@ -59,6 +59,37 @@ struct MaxF32 {
     static __device__ __forceinline__ out_t finish(acc_t a) { return a; }
 };
 
+// Fused float32 sum, max and sum of magnitudes in one pass: a float64 sum
+// and a float64 sum of |x| (each rounded once at the end) and the max under
+// the strictly-greater rule. NaN and infinities follow IEEE arithmetic in the
+// two sums.
+struct SumMaxAbs {
+    double s;
+    double a;
+    float m;
+    float pad;
+};
+struct SumMaxAbsOut {
+    float s;
+    float m;
+    float a;
+};
+struct SumMaxAbsF32 {
+    using elem_t = float;
+    using vec_t = f32x4;
+    using acc_t = SumMaxAbs;
+    using out_t = SumMaxAbsOut;
+    static __device__ __forceinline__ acc_t identity() { return {0.0, 0.0, -__builtin_inff(), 0.0f}; }
+    static __device__ __forceinline__ acc_t lift(elem_t v) {
+        const double d = (double)v;
+        return {d, __builtin_fabs(d), v, 0.0f};
+    }
+    static __device__ __forceinline__ acc_t combine(acc_t x, acc_t y) {
+        return {x.s + y.s, x.a + y.a, (y.m > x.m) ? y.m : x.m, 0.0f};
+    }
+    static __device__ __forceinline__ out_t finish(acc_t x) { return {(float)x.s, x.m, (float)x.a}; }
+};
+
 // Read probe: xor of every 32-bit word. One cheap ALU op per element, so a
 // kernel built on it measures the load path alone.
 struct XorU32 {
@@ -105,11 +136,12 @@ __device__ __forceinline__ void accumulate4(typename Op::acc_t (&acc)[4], typena
 // fixed, so the result is deterministic. All 64 lanes must be active.
 // ---------------------------------------------------------------------------
 // Cross-lane moves act on 32-bit words: a 64-bit value is moved as its two
-// halves. (The compiler builtins convert a non-int argument or result by
-// value, which would truncate a double, so every value is bit-cast.)
+// halves, a struct word by word. (The compiler builtins convert a non-int
+// argument or result by value, which would truncate a double, so every value
+// is bit-cast.)
 template <class T>
 struct Words {
-    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "4- or 8-byte values only");
+    static_assert(sizeof(T) % 4 == 0, "values must be whole 32-bit words");
     static constexpr int n = sizeof(T) / 4;
     int w[n];
 };

@@ -170,22 +170,23 @@ __global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
     }
 
     // Step 5: publish the partial, then take a ticket. The release fence
-    // orders the partial before the counter update for every other block.
+    // orders the partial before the counter update for every other block; the
+    // block that draws the last ticket acquires before it reads any partial.
     if (threadIdx.x == 0) {
-        __hip_atomic_store(&partials[blockIdx.x], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        partials[blockIdx.x] = v;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const unsigned int prev =
             __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         is_last = (prev == gridDim.x - 1);
+        if (is_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!is_last) return;  // block-uniform: the whole block leaves together
 
-    // Step 6: the last block. The acquire fence makes every partial visible.
+    // Step 6: the last block combines the partials in index order.
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     acc_t w = Op::identity();
-    for (unsigned int j = threadIdx.x; j < gridDim.x; j += BLOCK)
-        w = Op::combine(w, __hip_atomic_load(&partials[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    for (unsigned int j = threadIdx.x; j < gridDim.x; j += BLOCK) w = Op::combine(w, partials[j]);
     w = block_reduce<Op, BLOCK>(w, lds);
     if (threadIdx.x == 0) {
         out[0] = Op::finish(w);
@@ -323,6 +324,11 @@ hipError_t launch_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, int grid
 hipError_t launch_max_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
                           const Workspace& ws, hipStream_t stream) {
     return launch_op<MaxF32>(x, n, out, grid, p, ws, stream);
+}
+
+hipError_t launch_sum_max_f32(const float* x, size_t n, float* out3, int grid, const FlatPolicy& p,
+                              const Workspace& ws, hipStream_t stream) {
+    return launch_op<SumMaxAbsF32>(x, n, reinterpret_cast<SumMaxAbsOut*>(out3), grid, p, ws, stream);
 }
 
 hipError_t launch_sum_f32_partials(const float* x, size_t n, double* partials, int grid,

@@ -39,7 +39,9 @@ struct RowsPolicy {
 };
 
 // Library-owned scratch of one (device, stream): a completion counter that
-// is zero between calls, and room for `max_partials` 8-byte block partials.
+// is zero between calls, and room for `max_partials` block partials of up to
+// kMaxPartialBytes each.
+constexpr size_t kMaxPartialBytes = 32;
 struct Workspace {
     unsigned int* ticket;
     void* partials;
@@ -56,6 +58,9 @@ hipError_t launch_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, int grid
                               const FlatPolicy& p, const Workspace& ws, hipStream_t stream);
 hipError_t launch_max_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
                           const Workspace& ws, hipStream_t stream);
+// Fused: out3[0] = sum, out3[1] = max, out3[2] = sum of |x|.
+hipError_t launch_sum_max_f32(const float* x, size_t n, float* out3, int grid, const FlatPolicy& p,
+                              const Workspace& ws, hipStream_t stream);
 
 // Steps 1-5 of the float32 sum only: one float64 partial per block into
 // partials[0..grid), whatever p.combine says.
@@ -82,6 +87,11 @@ hipError_t launch_rung(int rung, const float* x, size_t n, float* partials, size
 // (stride -1: lane / 2) `iters` times; *sink = the sum of all values read.
 constexpr int kLdsProbeWords = 64 * 65;
 hipError_t launch_lds_stride(int stride, int iters, unsigned int* sink, hipStream_t stream);
+
+// Cross-lane primitives alone: op 0 = float64 sum, 1 = int64 sum, 2 = f32
+// max over each group of 64 inputs; and one 64-lane shuffle-down.
+hipError_t launch_wave_reduce_probe(int op, const void* in, size_t nwaves, void* out, hipStream_t stream);
+hipError_t launch_shfl_down_probe(const float* in, int offset, float* out, hipStream_t stream);
 
 // Probes: a plain copy y = x with 16-byte accesses and a scalar tail, and
 // the single-value kernel with an xor fold (*out = xor of all words), which

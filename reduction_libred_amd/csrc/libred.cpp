@@ -32,11 +32,11 @@ struct DeviceInfo {
 };
 
 // Workspace layout: the completion counter alone in the first 256 bytes,
-// then room for kMaxPartials 8-byte partials. The grid never exceeds
-// kMaxPartials blocks.
+// then room for kMaxPartials partials of up to kMaxPartialBytes each. The
+// grid never exceeds kMaxPartials blocks.
 constexpr size_t kTicketBytes = 256;
 constexpr size_t kMaxPartials = 8192;
-constexpr size_t kWorkspaceBytes = kTicketBytes + kMaxPartials * 8;
+constexpr size_t kWorkspaceBytes = kTicketBytes + kMaxPartials * libred::kMaxPartialBytes;
 
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
@@ -53,11 +53,17 @@ constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
 constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
 constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024};
 
+// The fused sum/max/sum-of-magnitudes pass does ~6 VALU ops per element
+// instead of ~2, and prefers four waves per CU on large arrays.
+constexpr FlatPolicy kFusedLarge = {256, 1, 4, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
+
 FlatPolicy default_flat(size_t n) {
     if (n <= kSmallMax) return kFlatSmall;
     if (n <= kCachedMax) return kFlatCached;
     return kFlatLarge;
 }
+
+FlatPolicy default_fused(size_t n) { return n <= kCachedMax ? default_flat(n) : kFusedLarge; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -119,8 +125,8 @@ red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
     return RED_OK;
 }
 
-FlatPolicy to_flat(const red_flat_policy* p, size_t n) {
-    if (!p) return default_flat(n);
+FlatPolicy to_flat(const red_flat_policy* p, size_t n, bool fused = false) {
+    if (!p) return fused ? default_fused(n) : default_flat(n);
     FlatPolicy f = {p->block,  p->blocks_per_cu, p->unroll,  p->nontemporal,
                     p->layout, p->prefetch,      p->combine};
     return f;
@@ -145,11 +151,11 @@ size_t flat_grid_for(size_t n, const FlatPolicy& p, int cu_count) {
 
 template <class In, class Out, class Launch>
 red_status flat_call(const In* x, size_t n, Out* out, const red_flat_policy* pol, hipStream_t stream,
-                     Launch launch) {
+                     Launch launch, size_t out_count = 1, bool fused = false) {
     if (n > RED_MAX_N || (n > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
     if (!aligned(x, sizeof(In)) || !aligned(out, sizeof(Out))) return RED_ERR_INVALID_ARG;
-    if (overlap(x, n * sizeof(In), out, sizeof(Out))) return RED_ERR_INVALID_ARG;
-    const FlatPolicy p = to_flat(pol, n);
+    if (overlap(x, n * sizeof(In), out, out_count * sizeof(Out))) return RED_ERR_INVALID_ARG;
+    const FlatPolicy p = to_flat(pol, n, fused);
     if (!libred::flat_policy_supported(p)) return RED_ERR_INVALID_ARG;
     int dev;
     DeviceInfo info;
@@ -202,6 +208,10 @@ red_status red_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, hipStream_t
 
 red_status red_max_f32(const float* x, size_t n, float* out, hipStream_t stream) {
     return flat_call(x, n, out, nullptr, stream, libred::launch_max_f32);
+}
+
+red_status red_sum_max_f32(const float* x, size_t n, float* out3, hipStream_t stream) {
+    return flat_call(x, n, out3, nullptr, stream, libred::launch_sum_max_f32, 3, true);
 }
 
 red_status red_rows_sum_f32(const float* x, size_t rows, size_t cols, float* out, hipStream_t stream) {
@@ -319,6 +329,12 @@ red_status red_sum_i32_i64_with(const int32_t* x, size_t n, int64_t* out, const 
     return flat_call(x, n, out, p, stream, libred::launch_sum_i32_i64);
 }
 
+red_status red_sum_max_f32_with(const float* x, size_t n, float* out3, const red_flat_policy* p,
+                                hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    return flat_call(x, n, out3, p, stream, libred::launch_sum_max_f32, 3);
+}
+
 red_status red_max_f32_with(const float* x, size_t n, float* out, const red_flat_policy* p,
                             hipStream_t stream) {
     if (!p) return RED_ERR_INVALID_ARG;
@@ -370,6 +386,34 @@ red_status red_probe_lds_stride(int stride, int iters, unsigned int* sink, hipSt
     const red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
     const hipError_t e = libred::launch_lds_stride(stride, iters, sink, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+red_status red_probe_wave_reduce(int op, const void* in, size_t nwaves, void* out, hipStream_t stream) {
+    const size_t esize = op == 2 ? 4 : 8;
+    if (op < 0 || op > 2 || nwaves == 0 || nwaves > (1u << 20) || in == nullptr || out == nullptr)
+        return RED_ERR_INVALID_ARG;
+    if (!aligned(in, esize) || !aligned(out, esize) || overlap(in, nwaves * 64 * esize, out, nwaves * esize))
+        return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    const hipError_t e = libred::launch_wave_reduce_probe(op, in, nwaves, out, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+red_status red_probe_shfl_down_f32(const float* in, int offset, float* out, hipStream_t stream) {
+    if (in == nullptr || out == nullptr || offset < 0 || offset > 64 || !aligned(in, 4) || !aligned(out, 4) ||
+        overlap(in, 256, out, 256))
+        return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    const hipError_t e = libred::launch_shfl_down_probe(in, offset, out, stream);
     if (e != hipSuccess) return fail(e, RED_ERR_HIP);
     return RED_OK;
 }

@@ -45,6 +45,47 @@ hipError_t launch_lds_stride(int stride, int iters, unsigned int* sink, hipStrea
     return hipGetLastError();
 }
 
+// The production wave reduce on its own: wave w reduces in[64w .. 64w + 63]
+// with the DPP sequence of wave_reduce<Op> and lane 0 stores out[w].
+template <class Op>
+__global__ __launch_bounds__(64) void wave_reduce_probe_kernel(const typename Op::acc_t* __restrict__ in,
+                                                               typename Op::acc_t* __restrict__ out) {
+    const typename Op::acc_t v = wave_reduce<Op>(in[(size_t)blockIdx.x * 64 + threadIdx.x]);
+    if (threadIdx.x == 0) out[blockIdx.x] = v;
+}
+
+hipError_t launch_wave_reduce_probe(int op, const void* in, size_t nwaves, void* out, hipStream_t stream) {
+    const dim3 grid((unsigned)nwaves), block(64);
+    switch (op) {
+        case 0:
+            hipLaunchKernelGGL(wave_reduce_probe_kernel<SumF32>, grid, block, 0, stream,
+                               static_cast<const double*>(in), static_cast<double*>(out));
+            break;
+        case 1:
+            hipLaunchKernelGGL(wave_reduce_probe_kernel<SumI32>, grid, block, 0, stream,
+                               static_cast<const int64_t*>(in), static_cast<int64_t*>(out));
+            break;
+        case 2:
+            hipLaunchKernelGGL(wave_reduce_probe_kernel<MaxF32>, grid, block, 0, stream,
+                               static_cast<const float*>(in), static_cast<float*>(out));
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// The register shuffle rung 5 uses: out[l] = value of lane l + offset, or the
+// lane's own value when l + offset is past the wave.
+__global__ __launch_bounds__(64) void shfl_down_probe_kernel(const float* __restrict__ in, int offset,
+                                                             float* __restrict__ out) {
+    out[threadIdx.x] = __shfl_down(in[threadIdx.x], (unsigned)offset, kWave);
+}
+
+hipError_t launch_shfl_down_probe(const float* in, int offset, float* out, hipStream_t stream) {
+    hipLaunchKernelGGL(shfl_down_probe_kernel, dim3(1), dim3(64), 0, stream, in, offset, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_copy_f32(const float* x, float* y, size_t n, int grid, hipStream_t stream) {
     hipLaunchKernelGGL(copy_f32_kernel, dim3(grid), dim3(kProbeBlock), 0, stream, x, y, n);
     return hipGetLastError();

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(BLOCK) void rows_reduce_kernel(const typename Op::e
 
 bool rows_policy_supported(const RowsPolicy& p) {
     const bool b = p.block == 64 || p.block == 128 || p.block == 256 || p.block == 512;
-    const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8;
+    const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.max_blocks >= 1;
 }
 
@@ -77,6 +77,7 @@ static hipError_t rows_b(const typename Op::elem_t* x, size_t rows, size_t cols,
         case 2: return rows_bu<Op, BLOCK, 2>(x, rows, cols, out, grid, nt, stream);
         case 4: return rows_bu<Op, BLOCK, 4>(x, rows, cols, out, grid, nt, stream);
         case 8: return rows_bu<Op, BLOCK, 8>(x, rows, cols, out, grid, nt, stream);
+        case 16: return rows_bu<Op, BLOCK, 16>(x, rows, cols, out, grid, nt, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -142,6 +142,12 @@ def test_probe_argument_errors():
     assert L.red_probe_lds_stride(-2, 1, _p(A), None) == INVALID
     assert L.red_probe_lds_stride(1, -1, _p(A), None) == INVALID
     assert L.red_probe_lds_stride(1, 1, None, None) == INVALID
+    assert L.red_probe_wave_reduce(3, _p(A), 1, _p(B), None) == INVALID
+    assert L.red_probe_wave_reduce(0, _p(A), 0, _p(B), None) == INVALID
+    assert L.red_probe_wave_reduce(0, _p(A + 4), 1, _p(B), None) == INVALID
+    assert L.red_probe_wave_reduce(0, _p(A), 2, _p(A + 8), None) == INVALID   # overlap
+    assert L.red_probe_shfl_down_f32(_p(A), 65, _p(B), None) == INVALID
+    assert L.red_probe_shfl_down_f32(None, 1, _p(B), None) == INVALID
 
 
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,

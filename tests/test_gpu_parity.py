@@ -270,6 +270,54 @@ def test_sum_i32_all_policies():
         assert int(out.item()) == want, p
 
 
+# ----------------------------------------------------------------- fused sum, max, sum|x|
+
+def assert_fused_ok(got, a):
+    s, m, ab = (float(v) for v in got)
+    S, A = oracle.sum_f32(a)
+    assert oracle.sum_within_tolerance(s, S, A), ("sum", s, S)
+    assert oracle.max_equal(m, oracle.max_f32(a)), ("max", m)
+    SA, _ = oracle.sum_f32(np.abs(a))
+    assert oracle.sum_within_tolerance(ab, SA, SA if math.isfinite(SA) else 0.0), ("abs", ab, SA)
+
+
+@pytest.mark.parametrize("offset", [0, 1, 3])
+def test_sum_max_f32_ragged(offset):
+    rng = np.random.default_rng(600 + offset)
+    for n in RAGGED:
+        say(f"sum_max_f32 n={n} offset={offset}")
+        a = (rng.standard_normal(n) * 100).astype(np.float32)
+        got = rl.red_sum_max_f32(device_view(a, offset)).cpu().numpy()
+        assert_fused_ok(got, a)
+
+
+def test_sum_max_f32_special():
+    nan, inf = float("nan"), float("inf")
+    cases = [[1.0, nan, -2.0], [inf, -inf, 3.0], [-inf, -5.0], [-3.0, -1.0, -2.0], [nan, nan]]
+    for xs in cases:
+        for pad in (0, 3000):
+            a = np.concatenate([np.zeros(pad, np.float32), np.array(xs, np.float32)])
+            say(f"sum_max_f32 special {xs} pad={pad}")
+            got = rl.red_sum_max_f32(device_view(a, 1, guard=0.0)).cpu().numpy()
+            S, A = oracle.sum_f32(a)
+            SA, _ = oracle.sum_f32(np.abs(a))
+            assert oracle.sum_within_tolerance(got[0], S, A), (xs, got[0], S)
+            assert got[1] == oracle.max_f32(a)
+            assert oracle.sum_within_tolerance(got[2], SA, A), (xs, got[2], SA)
+    say("sum_max_f32 n=0")
+    got = rl.red_sum_max_f32(torch.empty(0, device=DEV)).cpu().numpy()
+    assert got[0] == 0.0 and got[1] == -np.inf and got[2] == 0.0
+
+
+def test_sum_max_f32_all_policies():
+    a = W.make("normal", (1 << 21) + 5, 81)
+    x = device_view(a, 2)
+    for p in all_flat_policies(bpcs=(2,)):
+        say(f"sum_max_f32 policy {p}")
+        got = rl.red_sum_max_f32(x, policy=p).cpu().numpy()
+        assert_fused_ok(got, a)
+
+
 # ----------------------------------------------------------------- rows
 
 ROW_SHAPES = [(1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
@@ -321,7 +369,7 @@ def test_rows_policies():
     M = oracle.rows_max_f32(a)
     x = device_view(a, 1)
     for block in (64, 128, 256, 512):
-        for unroll in (1, 2, 4, 8):
+        for unroll in (1, 2, 4, 8, 16):
             for nt in (0, 1):
                 for mb in (1, 7, 1 << 20):
                     say(f"rows policy block={block} unroll={unroll} nt={nt} max_blocks={mb}")
@@ -376,6 +424,73 @@ def test_ablation_partials_only():
 
 
 # ----------------------------------------------------------------- probes
+
+def test_wave_reduce_primitive_matches_lane_model():
+    # The DPP wave reduce against the lane-by-lane CPU model of the same
+    # pairing: bit-exact for float64 sums, exact for int64 sums and max.
+    from lane_models import add, dpp_reduce, max_rule
+    rng = np.random.default_rng(21)
+    waves = 64
+    f = (rng.standard_normal(waves * 64) * 10.0 ** rng.uniform(-6, 6, waves * 64)).astype(np.float64)
+    f[:64] = [1e16 if i % 16 == 0 else 1.0 for i in range(64)]      # order-sensitive wave
+    say("wave reduce f64")
+    got = rl.red_probe_wave_reduce("sum_f64", torch.from_numpy(f).to(DEV)).cpu().numpy()
+    want = [dpp_reduce(f[64 * w:64 * (w + 1)].tolist(), add, 0.0) for w in range(waves)]
+    assert got.tolist() == want
+    i = rng.integers(-(2 ** 62), 2 ** 62, waves * 64, dtype=np.int64)
+    say("wave reduce i64")
+    got = rl.red_probe_wave_reduce("sum_i64", torch.from_numpy(i).to(DEV)).cpu().numpy()
+    want = [(sum(i[64 * w:64 * (w + 1)].tolist()) + 2 ** 63) % 2 ** 64 - 2 ** 63 for w in range(waves)]
+    assert got.tolist() == want
+    m = rng.standard_normal(waves * 64).astype(np.float32)
+    m[5] = np.nan
+    say("wave reduce max")
+    got = rl.red_probe_wave_reduce("max_f32", torch.from_numpy(m).to(DEV)).cpu().numpy()
+    want = [dpp_reduce(m[64 * w:64 * (w + 1)].tolist(), max_rule, -math.inf) for w in range(waves)]
+    assert got.tolist() == [np.float32(v) for v in want]
+
+
+def test_shfl_down_primitive_matches_lane_model():
+    from lane_models import shfl_down
+    v = np.arange(64, dtype=np.float32) * 1.5 - 7
+    x = torch.from_numpy(v).to(DEV)
+    for off in (0, 1, 2, 4, 8, 16, 31, 32, 33, 63, 64):
+        say(f"shfl_down offset={off}")
+        got = rl.red_probe_shfl_down_f32(x, off).cpu().numpy()
+        assert got.tolist() == shfl_down(v.tolist(), off), off
+
+
+def test_graph_replay_matches_eager():
+    # Captured calls (after a first eager call per stream, so the workspace
+    # exists) replay correctly several times with eager work in between.
+    a = W.make("normal", (1 << 22) + 3, 31)
+    r = W.make("uniform01", 300 * 1001, 32).reshape(300, 1001)
+    x, xr = device_view(a, 1), device_view(r, 2)
+    outs = [torch.empty((), device=DEV), torch.empty((), device=DEV), torch.empty(300, device=DEV)]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        rl.red_sum_f32(x, out=outs[0])
+        rl.red_max_f32(x, out=outs[1])
+        rl.red_rows_sum_f32(xr, out=outs[2])
+        torch.cuda.synchronize()
+        eager = [o.clone() for o in outs]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            rl.red_sum_f32(x, out=outs[0])
+            rl.red_max_f32(x, out=outs[1])
+            rl.red_rows_sum_f32(xr, out=outs[2])
+    torch.cuda.synchronize()
+    for k in range(4):
+        say(f"graph replay {k}")
+        for o in outs:
+            o.zero_()
+        rl.red_sum_f32(x)                      # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e)
+
 
 def test_lds_stride_probe():
     words = 64 * 65
@@ -444,6 +559,15 @@ def test_full_sum_max_f32_2p28():
     m = rl.red_max_f32(x)
     torch.cuda.synchronize()
     assert m.item() == float(oracle.max_f32(a))
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_sum_max_f32_fused_2p28():
+    a, x = _load("sum_max_f32_2p28")
+    say("red_sum_max_f32 sum_max_f32_2p28")
+    got = rl.red_sum_max_f32(x).cpu().numpy()
+    assert_fused_ok(got, a)
     del x
     torch.cuda.empty_cache()
 
