@@ -107,8 +107,7 @@ red_status red_sum_max_f32(const float *x, size_t n, float *out3, hipStream_t st
  * out[r] = x[r*cols] + ... + x[r*cols + cols - 1], for r < rows.
  * One output per segment, as the lesson's block partials are one output
  * per block. Accumulated in float64, rounded once per row. rows == 0 does
- * nothing (out may be NULL); cols == 0 stores 0.0f in every out[r]. The
- * library workspace is not used.
+ * nothing (out may be NULL); cols == 0 stores 0.0f in every out[r].
  */
 red_status red_rows_sum_f32(const float *x, size_t rows, size_t cols, float *out,
                             hipStream_t stream);
@@ -119,6 +118,21 @@ red_status red_rows_sum_f32(const float *x, size_t rows, size_t cols, float *out
  */
 red_status red_rows_max_f32(const float *x, size_t rows, size_t cols, float *out,
                             hipStream_t stream);
+
+/*
+ * The same row reductions over rows that start `ld` elements apart
+ * (ld >= cols): row r is x[r*ld .. r*ld + cols). The elements between the
+ * end of one row and the start of the next are not read. ld < cols, or a
+ * span (rows - 1) * ld + cols above RED_MAX_N, is RED_ERR_INVALID_ARG. With
+ * ld == cols these are red_rows_sum_f32 / red_rows_max_f32. For fewer than
+ * 1024 rows of at least 8192 elements, each row is split across several
+ * blocks and the pieces are combined per row in a fixed order (this uses the
+ * library workspace of the stream).
+ */
+red_status red_rows_sum_f32_ld(const float *x, size_t rows, size_t cols, size_t ld, float *out,
+                               hipStream_t stream);
+red_status red_rows_max_f32_ld(const float *x, size_t rows, size_t cols, size_t ld, float *out,
+                               hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 const char *red_status_string(red_status status);

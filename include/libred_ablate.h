@@ -69,12 +69,16 @@ typedef struct red_flat_policy {
 
 /* Launch shape of the row kernels: `block` threads (64, 128, 256 or 512; one
  * row per wave at a time), `unroll` loads per lane per trip (1, 2, 4, 8, 16),
- * `nontemporal`, and `max_blocks` capping the grid. */
+ * `nontemporal`, `max_blocks` capping the grid, and `split`: 0 = split few
+ * long rows across single-wave blocks when that helps (the default rule),
+ * 1 = never, 2 = whenever a row holds at least two tiles of 64*unroll
+ * vectors. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
     int nontemporal;
     int max_blocks;
+    int split;
 } red_rows_policy;
 
 /* The shape red_sum_f32 / red_sum_i32_i64 / red_max_f32 use for n elements,
@@ -108,9 +112,9 @@ red_status red_max_f32_with(const float *x, size_t n, float *out, const red_flat
                             hipStream_t stream);
 red_status red_sum_max_f32_with(const float *x, size_t n, float *out3, const red_flat_policy *p,
                                 hipStream_t stream);
-red_status red_rows_sum_f32_with(const float *x, size_t rows, size_t cols, float *out,
+red_status red_rows_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_rows_policy *p, hipStream_t stream);
-red_status red_rows_max_f32_with(const float *x, size_t rows, size_t cols, float *out,
+red_status red_rows_max_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_rows_policy *p, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -49,7 +49,8 @@ class FlatPolicy(ctypes.Structure):
 
 class RowsPolicy(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int), ("unroll", ctypes.c_int),
-                ("nontemporal", ctypes.c_int), ("max_blocks", ctypes.c_int)]
+                ("nontemporal", ctypes.c_int), ("max_blocks", ctypes.c_int),
+                ("split", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -69,6 +70,8 @@ SIGNATURES = {
     "red_sum_max_f32_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
     "red_rows_sum_f32": (_S, [_P, _Z, _Z, _P, _P]),
     "red_rows_max_f32": (_S, [_P, _Z, _Z, _P, _P]),
+    "red_rows_sum_f32_ld": (_S, [_P, _Z, _Z, _Z, _P, _P]),
+    "red_rows_max_f32_ld": (_S, [_P, _Z, _Z, _Z, _P, _P]),
     "red_status_string": (ctypes.c_char_p, [_S]),
     "red_last_hip_error": (_I, []),
     "red_version": (ctypes.c_char_p, []),
@@ -81,8 +84,8 @@ SIGNATURES = {
     "red_sum_f32_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
     "red_sum_i32_i64_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
     "red_max_f32_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
-    "red_rows_sum_f32_with": (_S, [_P, _Z, _Z, _P, ctypes.POINTER(RowsPolicy), _P]),
-    "red_rows_max_f32_with": (_S, [_P, _Z, _Z, _P, ctypes.POINTER(RowsPolicy), _P]),
+    "red_rows_sum_f32_with": (_S, [_P, _Z, _Z, _Z, _P, ctypes.POINTER(RowsPolicy), _P]),
+    "red_rows_max_f32_with": (_S, [_P, _Z, _Z, _Z, _P, ctypes.POINTER(RowsPolicy), _P]),
     "red_probe_copy_f32": (_S, [_P, _P, _Z, _P]),
     "red_probe_read_f32": (_S, [_P, _Z, _P, _P]),
     "red_device_info": (_S, [ctypes.POINTER(_I), ctypes.c_char_p, _Z]),
@@ -192,25 +195,34 @@ def red_sum_max_f32(x, out=None, stream=None, policy=None):
 
 
 def _rows(cname, x, out, stream, policy):
-    _input(x, torch.float32, cname)
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.float32:
+        raise TypeError(f"{cname}: input must be a float32 tensor on a ROCm device")
     if x.dim() != 2:
         raise ValueError(f"{cname}: input must be 2-D (rows, cols)")
     rows, cols = x.shape
+    # Rows may be spaced apart (a column slice of a wider matrix): the row
+    # stride becomes the leading dimension; columns must be unit-stride.
+    if rows > 1 and cols > 1 and x.stride(1) != 1:
+        raise ValueError(f"{cname}: columns must be contiguous (stride 1)")
+    ld = x.stride(0) if (rows > 1 and cols > 0) else cols
+    if ld < cols:
+        raise ValueError(f"{cname}: rows overlap (row stride {ld} < cols {cols})")
     out = _output(out, (rows,), torch.float32, x.device, cname)
     with torch.cuda.device(x.device):
         s = _stream_handle(stream, x.device)
         if policy is None:
-            st = getattr(lib(), cname)(x.data_ptr(), rows, cols, out.data_ptr(), s)
+            st = getattr(lib(), cname + "_ld")(x.data_ptr(), rows, cols, ld, out.data_ptr(), s)
         else:
             p = _policy(RowsPolicy, policy)
-            st = getattr(lib(), cname + "_with")(x.data_ptr(), rows, cols, out.data_ptr(),
+            st = getattr(lib(), cname + "_with")(x.data_ptr(), rows, cols, ld, out.data_ptr(),
                                                  ctypes.byref(p), s)
     _check(cname, st)
     return out
 
 
 def red_rows_sum_f32(x, out=None, stream=None, policy=None):
-    """Per-row sum of a 2-D row-major float32 tensor -> float32[rows]."""
+    """Per-row sum of a 2-D float32 tensor with unit-stride columns (rows may
+    be spaced apart, e.g. a column slice) -> float32[rows]."""
     return _rows("red_rows_sum_f32", x, out, stream, policy)
 
 

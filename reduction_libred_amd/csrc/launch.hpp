@@ -30,13 +30,25 @@ struct FlatPolicy {
 
 // Launch shape of the row kernels: `block` threads (one row per 64-lane
 // wave at a time), `unroll` loads in flight per lane, `max_blocks` caps the
-// grid (rows beyond it are taken in a wave-uniform grid-stride loop).
+// grid (rows beyond it are taken in a wave-uniform grid-stride loop), `split`
+// 0 = split few long rows across blocks automatically, 1 = never, 2 = always.
 struct RowsPolicy {
     int block;
     int unroll;
     int nontemporal;
     int max_blocks;
+    int split;
 };
+
+// How one row call launches: `grid` blocks of the one-wave-per-row kernel,
+// or, when split_gx > 0, rows * split_gx single-wave blocks writing partials
+// (acc_t, at most kMaxSplitPartials of them) into `partials`.
+struct RowsLaunch {
+    int grid;
+    unsigned int split_gx;
+    void* partials;
+};
+constexpr size_t kMaxSplitPartials = 32768;
 
 // Library-owned scratch of one (device, stream): a completion counter that
 // is zero between calls, and room for `max_partials` block partials of up to
@@ -70,11 +82,11 @@ hipError_t launch_sum_f32_partials(const float* x, size_t n, double* partials, i
 // Zero `words` 32-bit words at p (used once, when a workspace is created).
 hipError_t launch_zero_words(unsigned int* p, size_t words, hipStream_t stream);
 
-// Row reductions (rows >= 1) with `grid` blocks.
-hipError_t launch_rows_sum_f32(const float* x, size_t rows, size_t cols, float* out, int grid,
-                               const RowsPolicy& p, hipStream_t stream);
-hipError_t launch_rows_max_f32(const float* x, size_t rows, size_t cols, float* out, int grid,
-                               const RowsPolicy& p, hipStream_t stream);
+// Row reductions (rows >= 1, rows starting ld >= cols elements apart).
+hipError_t launch_rows_sum_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                               const RowsLaunch& L, const RowsPolicy& p, hipStream_t stream);
+hipError_t launch_rows_max_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                               const RowsLaunch& L, const RowsPolicy& p, hipStream_t stream);
 
 // Ablation ladder: rung 1..5 writes one float partial per block of
 // kRungBlock threads into `partials`.

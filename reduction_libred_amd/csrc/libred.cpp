@@ -51,7 +51,13 @@ constexpr FlatPolicy kFlatCached = {1024, 1, 4, 1, libred::kWaveTiles, 1, libred
 constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
 constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
-constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024};
+constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0};
+// Split-row mode: used automatically for fewer than kSplitRowsBelow rows
+// whose rows hold at least kSplitMinCols elements; aims for about
+// kSplitTargetWaves waves in all.
+constexpr size_t kSplitRowsBelow = 1024;
+constexpr size_t kSplitMinCols = 8192;
+constexpr size_t kSplitTargetWaves = 1024;
 
 // The fused sum/max/sum-of-magnitudes pass does ~6 VALU ops per element
 // instead of ~2, and prefers four waves per CU on large arrays.
@@ -134,7 +140,7 @@ FlatPolicy to_flat(const red_flat_policy* p, size_t n, bool fused = false) {
 
 RowsPolicy to_rows(const red_rows_policy* p) {
     if (!p) return kDefaultRows;
-    RowsPolicy r = {p->block, p->unroll, p->nontemporal, p->max_blocks};
+    RowsPolicy r = {p->block, p->unroll, p->nontemporal, p->max_blocks, p->split};
     return r;
 }
 
@@ -171,25 +177,48 @@ red_status flat_call(const In* x, size_t n, Out* out, const red_flat_policy* pol
 }
 
 template <class Launch>
-red_status rows_call(const float* x, size_t rows, size_t cols, float* out, const red_rows_policy* pol,
-                     hipStream_t stream, Launch launch) {
-    if (cols != 0 && rows > SIZE_MAX / cols) return RED_ERR_INVALID_ARG;
-    const size_t total = rows * cols;
-    if (total > RED_MAX_N || rows > RED_MAX_N) return RED_ERR_INVALID_ARG;
+red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                     const red_rows_policy* pol, hipStream_t stream, Launch launch) {
+    if (ld < cols || rows > RED_MAX_N || cols > RED_MAX_N || ld > RED_MAX_N) return RED_ERR_INVALID_ARG;
+    // Elements spanned: (rows - 1) * ld + cols.
+    if (rows > 1 && ld != 0 && rows - 1 > (RED_MAX_N - cols) / ld) return RED_ERR_INVALID_ARG;
+    const size_t span = rows == 0 ? 0 : (rows - 1) * ld + cols;
+    if (span > RED_MAX_N) return RED_ERR_INVALID_ARG;
     const RowsPolicy p = to_rows(pol);
     if (!libred::rows_policy_supported(p)) return RED_ERR_INVALID_ARG;
     if (rows == 0) return RED_OK;
-    if ((total > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
+    if ((span > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
     if (!aligned(x, sizeof(float)) || !aligned(out, sizeof(float))) return RED_ERR_INVALID_ARG;
-    if (overlap(x, total * sizeof(float), out, rows * sizeof(float))) return RED_ERR_INVALID_ARG;
+    if (overlap(x, span * sizeof(float), out, rows * sizeof(float))) return RED_ERR_INVALID_ARG;
     int dev;
     DeviceInfo info;
-    const red_status st = current_device(&dev, &info);
+    red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
-    const size_t waves_per_block = (size_t)p.block / 64;
-    size_t grid = (rows + waves_per_block - 1) / waves_per_block;
-    if (grid > (size_t)p.max_blocks) grid = (size_t)p.max_blocks;
-    const hipError_t e = launch(x, rows, cols, out, (int)grid, p, stream);
+
+    libred::RowsLaunch L = {0, 0, nullptr};
+    const size_t tile_elems = (size_t)64 * (size_t)p.unroll * 4;
+    const size_t tiles_per_row = cols / tile_elems;
+    const bool want_split =
+        p.split == 2 || (p.split == 0 && rows < kSplitRowsBelow && cols >= kSplitMinCols);
+    if (want_split && tiles_per_row >= 2) {
+        size_t gx = (kSplitTargetWaves + rows - 1) / rows;
+        if (gx > tiles_per_row) gx = tiles_per_row;
+        if (gx > libred::kMaxSplitPartials / rows) gx = libred::kMaxSplitPartials / rows;
+        if (gx >= 2) {
+            Workspace ws;
+            st = get_workspace(dev, stream, &ws);
+            if (st != RED_OK) return st;
+            L.split_gx = (unsigned int)gx;
+            L.partials = ws.partials;
+        }
+    }
+    if (L.split_gx == 0) {
+        const size_t waves_per_block = (size_t)p.block / 64;
+        size_t grid = (rows + waves_per_block - 1) / waves_per_block;
+        if (grid > (size_t)p.max_blocks) grid = (size_t)p.max_blocks;
+        L.grid = (int)grid;
+    }
+    const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
     if (e != hipSuccess) return fail(e, RED_ERR_HIP);
     return RED_OK;
 }
@@ -215,11 +244,21 @@ red_status red_sum_max_f32(const float* x, size_t n, float* out3, hipStream_t st
 }
 
 red_status red_rows_sum_f32(const float* x, size_t rows, size_t cols, float* out, hipStream_t stream) {
-    return rows_call(x, rows, cols, out, nullptr, stream, libred::launch_rows_sum_f32);
+    return rows_call(x, rows, cols, cols, out, nullptr, stream, libred::launch_rows_sum_f32);
 }
 
 red_status red_rows_max_f32(const float* x, size_t rows, size_t cols, float* out, hipStream_t stream) {
-    return rows_call(x, rows, cols, out, nullptr, stream, libred::launch_rows_max_f32);
+    return rows_call(x, rows, cols, cols, out, nullptr, stream, libred::launch_rows_max_f32);
+}
+
+red_status red_rows_sum_f32_ld(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                               hipStream_t stream) {
+    return rows_call(x, rows, cols, ld, out, nullptr, stream, libred::launch_rows_sum_f32);
+}
+
+red_status red_rows_max_f32_ld(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                               hipStream_t stream) {
+    return rows_call(x, rows, cols, ld, out, nullptr, stream, libred::launch_rows_max_f32);
 }
 
 const char* red_status_string(red_status status) {
@@ -286,6 +325,7 @@ void red_default_rows_policy(red_rows_policy* p) {
     p->unroll = kDefaultRows.unroll;
     p->nontemporal = kDefaultRows.nontemporal;
     p->max_blocks = kDefaultRows.max_blocks;
+    p->split = kDefaultRows.split;
 }
 
 size_t red_flat_grid(size_t n, const red_flat_policy* pol) {
@@ -341,16 +381,16 @@ red_status red_max_f32_with(const float* x, size_t n, float* out, const red_flat
     return flat_call(x, n, out, p, stream, libred::launch_max_f32);
 }
 
-red_status red_rows_sum_f32_with(const float* x, size_t rows, size_t cols, float* out,
+red_status red_rows_sum_f32_with(const float* x, size_t rows, size_t cols, size_t ld, float* out,
                                  const red_rows_policy* p, hipStream_t stream) {
     if (!p) return RED_ERR_INVALID_ARG;
-    return rows_call(x, rows, cols, out, p, stream, libred::launch_rows_sum_f32);
+    return rows_call(x, rows, cols, ld, out, p, stream, libred::launch_rows_sum_f32);
 }
 
-red_status red_rows_max_f32_with(const float* x, size_t rows, size_t cols, float* out,
+red_status red_rows_max_f32_with(const float* x, size_t rows, size_t cols, size_t ld, float* out,
                                  const red_rows_policy* p, hipStream_t stream) {
     if (!p) return RED_ERR_INVALID_ARG;
-    return rows_call(x, rows, cols, out, p, stream, libred::launch_rows_max_f32);
+    return rows_call(x, rows, cols, ld, out, p, stream, libred::launch_rows_max_f32);
 }
 
 // ---------------------------------------------------------------- probes

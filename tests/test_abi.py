@@ -113,8 +113,15 @@ def test_rows_argument_errors():
         assert f(_p(A + 2), 2, 3, _p(B), None) == INVALID
         assert f(_p(A), 4, 4, _p(A + 16), None) == INVALID              # out inside x
         assert f(None, 0, 5, None, None) == rl.RED_OK                   # rows == 0: no-op
-    bad = rl.RowsPolicy(96, 4, 1, 16)
-    assert L.red_rows_sum_f32_with(_p(A), 2, 3, _p(B), ctypes.byref(bad), None) == INVALID
+    bad = rl.RowsPolicy(96, 4, 1, 16, 0)
+    assert L.red_rows_sum_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
+    bad = rl.RowsPolicy(64, 4, 1, 16, 3)
+    assert L.red_rows_sum_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
+    for f in (L.red_rows_sum_f32_ld, L.red_rows_max_f32_ld):
+        assert f(_p(A), 2, 5, 4, _p(B), None) == INVALID                   # ld < cols
+        assert f(_p(A), 1 << 20, 4, 1 << 21, _p(B), None) == INVALID        # span > RED_MAX_N
+        assert f(_p(A), 3, 4, 8, _p(A + 4 * 8), None) == INVALID            # out inside the span
+        assert f(None, 0, 4, 8, None, None) == rl.RED_OK
 
 
 def test_ablate_argument_errors():

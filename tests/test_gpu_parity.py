@@ -346,6 +346,46 @@ def test_rows_random(rows, cols):
         assert np.array_equal(out_m.cpu().numpy(), oracle.rows_max_f32(a)), (rows, cols)
 
 
+@pytest.mark.parametrize("rows,cols,ld", [(3, 5, 7), (10, 1000, 1003), (257, 4096, 4100), (64, 63, 64),
+                                          (1, 10, 10), (5, 0, 3), (1000, 129, 1024)])
+def test_rows_strided(rows, cols, ld):
+    # Rows spaced ld apart: the gap holds NaN, which must never be read.
+    rng = np.random.default_rng(rows + cols + ld)
+    full = np.full((rows, ld), np.nan, np.float32)
+    full[:, :cols] = rng.standard_normal((rows, cols)).astype(np.float32)
+    a = np.ascontiguousarray(full[:, :cols])
+    for offset in (0, 1):
+        say(f"rows strided {rows}x{cols} ld={ld} offset={offset}")
+        xf = device_view(full, offset)
+        x = xf[:, :cols]
+        s = rl.red_rows_sum_f32(x)
+        m = rl.red_rows_max_f32(x)
+        torch.cuda.synchronize()
+        S, A = oracle.rows_sum_f32(a)
+        assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
+        assert np.array_equal(m.cpu().numpy(), oracle.rows_max_f32(a))
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1_000_003), (2, 3_000_017), (7, 1 << 20), (100, 65537),
+                                        (1023, 8192), (3, 70_000)])
+def test_rows_split_long_rows(rows, cols):
+    # Few long rows take the split path (several blocks per row, partials
+    # combined per row in order); forced off it must agree too.
+    rng = np.random.default_rng(rows * 31 + cols)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    a[np.arange(rows), (np.arange(rows) * 7919) % cols] = 99.0 + np.arange(rows)
+    S, A = oracle.rows_sum_f32(a)
+    M = oracle.rows_max_f32(a)
+    x = device_view(a, 3)
+    for p in (None, dict(split=1), dict(split=2, unroll=4), dict(split=2, unroll=16, nontemporal=0)):
+        say(f"rows split {rows}x{cols} policy={p}")
+        s = rl.red_rows_sum_f32(x, policy=p)
+        m = rl.red_rows_max_f32(x, policy=p)
+        torch.cuda.synchronize()
+        assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
+        assert np.array_equal(m.cpu().numpy(), M), p
+
+
 def test_rows_mod7_exact():
     rows, cols = 1031, 4097
     say(f"rows mod7 {rows}x{cols}")
