@@ -324,6 +324,10 @@ def main():
         b4 = 4 * x4.numel() + 4 * x4.shape[0]
         measure(f"red_rows_sum_f32 {name4}", lambda: rl.red_rows_sum_f32(x4, out=r4), b4)
         measure(f"red_rows_max_f32 {name4}", lambda: rl.red_rows_max_f32(x4, out=r4), b4)
+        c4 = torch.empty(x4.shape[1], dtype=torch.float32, device=dev)
+        bc = 4 * x4.numel() + 4 * x4.shape[1]
+        measure(f"red_cols_sum_f32 {name4}", lambda: rl.red_cols_sum_f32(x4, out=c4), bc)
+        measure(f"red_cols_max_f32 {name4}", lambda: rl.red_cols_max_f32(x4, out=c4), bc)
         del x4
 
         # Small, cache-resident sizes, through HIP graphs so that host call

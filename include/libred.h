@@ -134,6 +134,22 @@ red_status red_rows_sum_f32_ld(const float *x, size_t rows, size_t cols, size_t 
 red_status red_rows_max_f32_ld(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                hipStream_t stream);
 
+/*
+ * Per-column sum and max of the same layouts: out[c] = reduction over
+ * r < rows of x[r*ld + c], for c < cols (ld >= cols; ld == cols for a dense
+ * matrix). out holds cols floats. Sums accumulate in float64 and round once
+ * per column; max follows red_max_f32's rule. cols == 0 does nothing (out
+ * may be NULL); rows == 0 stores 0.0f (sum) or -inf (max) in every out[c].
+ * When there are few columns, the rows are cut into chunks whose partials
+ * are added per column in a fixed order; those partials live in a scratch
+ * buffer of the stream that is grown on demand (growing it waits for the
+ * stream once). Errors as for the row entry points.
+ */
+red_status red_cols_sum_f32(const float *x, size_t rows, size_t cols, size_t ld, float *out,
+                            hipStream_t stream);
+red_status red_cols_max_f32(const float *x, size_t rows, size_t cols, size_t ld, float *out,
+                            hipStream_t stream);
+
 /* A static, human-readable name for a status code. */
 const char *red_status_string(red_status status);
 

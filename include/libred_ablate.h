@@ -81,6 +81,24 @@ typedef struct red_rows_policy {
     int split;
 } red_rows_policy;
 
+/* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,
+ * 4, 8 or 16), `nontemporal`, `target_waves` (the rows are cut into chunks
+ * until about this many single-wave blocks run), and `vec`: 0 = four
+ * adjacent columns per lane when x is 16-byte aligned and cols and ld are
+ * multiples of 4, else one; 1 = always one; 4 = same as 0. */
+typedef struct red_cols_policy {
+    int unroll;
+    int nontemporal;
+    int target_waves;
+    int vec;
+} red_cols_policy;
+
+void red_default_cols_policy(red_cols_policy *p);
+red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
+                                 const red_cols_policy *p, hipStream_t stream);
+red_status red_cols_max_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
+                                 const red_cols_policy *p, hipStream_t stream);
+
 /* The shape red_sum_f32 / red_sum_i32_i64 / red_max_f32 use for n elements,
  * and the shape of the row entry points. */
 void red_default_flat_policy(size_t n, red_flat_policy *p);

@@ -86,6 +86,15 @@ class Oracle:
         self.lib.oracle_rows_max_f32(a.ctypes.data, rows, cols, out.ctypes.data)
         return out
 
+    def cols_sum_f32(self, x):
+        """Per-column (S, A) of a 2-D float32 array: the row oracle applied to
+        the transposed array (sum along axis 0, by definition)."""
+        return self.rows_sum_f32(np.ascontiguousarray(np.asarray(x, np.float32).T))
+
+    def cols_max_f32(self, x):
+        """Per-column float32 maximum (the row oracle on the transpose)."""
+        return self.rows_max_f32(np.ascontiguousarray(np.asarray(x, np.float32).T))
+
 
 _default = None
 
@@ -118,6 +127,14 @@ def rows_sum_f32(x):
 
 def rows_max_f32(x):
     return default().rows_max_f32(x)
+
+
+def cols_sum_f32(x):
+    return default().cols_sum_f32(x)
+
+
+def cols_max_f32(x):
+    return default().cols_max_f32(x)
 
 
 def sum_within_tolerance(gpu, S, A):

@@ -56,6 +56,14 @@ class RowsPolicy(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class ColsPolicy(ctypes.Structure):
+    _fields_ = [("unroll", ctypes.c_int), ("nontemporal", ctypes.c_int),
+                ("target_waves", ctypes.c_int), ("vec", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 _P = ctypes.c_void_p
 _Z = ctypes.c_size_t
 _I = ctypes.c_int
@@ -71,6 +79,11 @@ SIGNATURES = {
     "red_rows_sum_f32": (_S, [_P, _Z, _Z, _P, _P]),
     "red_rows_max_f32": (_S, [_P, _Z, _Z, _P, _P]),
     "red_rows_sum_f32_ld": (_S, [_P, _Z, _Z, _Z, _P, _P]),
+    "red_cols_sum_f32": (_S, [_P, _Z, _Z, _Z, _P, _P]),
+    "red_cols_max_f32": (_S, [_P, _Z, _Z, _Z, _P, _P]),
+    "red_default_cols_policy": (None, [ctypes.POINTER(ColsPolicy)]),
+    "red_cols_sum_f32_with": (_S, [_P, _Z, _Z, _Z, _P, ctypes.POINTER(ColsPolicy), _P]),
+    "red_cols_max_f32_with": (_S, [_P, _Z, _Z, _Z, _P, ctypes.POINTER(ColsPolicy), _P]),
     "red_rows_max_f32_ld": (_S, [_P, _Z, _Z, _Z, _P, _P]),
     "red_status_string": (ctypes.c_char_p, [_S]),
     "red_last_hip_error": (_I, []),
@@ -150,7 +163,12 @@ def _policy(cls, p, n=0):
     given take the library default for n elements)."""
     if p is None or isinstance(p, cls):
         return p
-    base = red_default_flat_policy(n) if cls is FlatPolicy else red_default_rows_policy()
+    if cls is FlatPolicy:
+        base = red_default_flat_policy(n)
+    elif cls is ColsPolicy:
+        base = red_default_cols_policy()
+    else:
+        base = red_default_rows_policy()
     for k, v in p.items():
         if k not in base.as_dict():
             raise KeyError(f"unknown policy field {k!r}")
@@ -229,6 +247,46 @@ def red_rows_sum_f32(x, out=None, stream=None, policy=None):
 def red_rows_max_f32(x, out=None, stream=None, policy=None):
     """Per-row max of a 2-D row-major float32 tensor -> float32[rows]."""
     return _rows("red_rows_max_f32", x, out, stream, policy)
+
+
+def _cols(cname, x, out, stream, policy):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.float32:
+        raise TypeError(f"{cname}: input must be a float32 tensor on a ROCm device")
+    if x.dim() != 2:
+        raise ValueError(f"{cname}: input must be 2-D (rows, cols)")
+    rows, cols = x.shape
+    if rows > 1 and cols > 1 and x.stride(1) != 1:
+        raise ValueError(f"{cname}: columns must be contiguous (stride 1)")
+    ld = x.stride(0) if (rows > 1 and cols > 0) else cols
+    if ld < cols:
+        raise ValueError(f"{cname}: rows overlap (row stride {ld} < cols {cols})")
+    out = _output(out, (cols,), torch.float32, x.device, cname)
+    with torch.cuda.device(x.device):
+        s = _stream_handle(stream, x.device)
+        ptr = x.data_ptr() if rows * cols else 0
+        if policy is None:
+            st = getattr(lib(), cname)(ptr, rows, cols, ld, out.data_ptr(), s)
+        else:
+            p = _policy(ColsPolicy, policy)
+            st = getattr(lib(), cname + "_with")(ptr, rows, cols, ld, out.data_ptr(), ctypes.byref(p), s)
+    _check(cname, st)
+    return out
+
+
+def red_cols_sum_f32(x, out=None, stream=None, policy=None):
+    """Per-column sum of a 2-D float32 tensor with unit-stride columns -> float32[cols]."""
+    return _cols("red_cols_sum_f32", x, out, stream, policy)
+
+
+def red_cols_max_f32(x, out=None, stream=None, policy=None):
+    """Per-column max of a 2-D float32 tensor with unit-stride columns -> float32[cols]."""
+    return _cols("red_cols_max_f32", x, out, stream, policy)
+
+
+def red_default_cols_policy():
+    p = ColsPolicy()
+    lib().red_default_cols_policy(ctypes.byref(p))
+    return p
 
 
 def red_ablate_num_partials(rung, n):

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libred.so")
 
-SOURCES = ["libred.cpp", "flat_reduce.hip", "rows_reduce.hip", "ablate.hip", "probe.hip"]
+SOURCES = ["libred.cpp", "flat_reduce.hip", "rows_reduce.hip", "cols_reduce.hip", "ablate.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -60,7 +60,32 @@ struct Workspace {
     size_t max_partials;
 };
 
+// Launch shape of the column kernels: `unroll` rows in flight per lane,
+// `nontemporal`, `target_waves` (rows are cut into chunks until about this
+// many single-wave blocks run), `vec` 0 = four columns per lane when the
+// layout allows it (16-byte aligned, cols and ld multiples of 4), 1 = one,
+// 4 = four when allowed.
+struct ColsPolicy {
+    int unroll;
+    int nontemporal;
+    int target_waves;
+    int vec;
+};
+
+// How one column call launches: ncb column blocks of ngroups*vec columns
+// times nchunks row chunks (ngroups == 64, or a divisor of 64 for a narrow
+// matrix whose wave then covers 64 / ngroups rows per load); with
+// nchunks > 1, partials (nchunks * cols acc_t) live in `partials`.
+struct ColsLaunch {
+    size_t ncb;
+    size_t nchunks;
+    int vec;
+    unsigned int ngroups;
+    void* partials;
+};
+
 bool flat_policy_supported(const FlatPolicy& p);
+bool cols_policy_supported(const ColsPolicy& p);
 bool rows_policy_supported(const RowsPolicy& p);
 
 // Single-value reductions with `grid` blocks (1 <= grid <= ws.max_partials).
@@ -87,6 +112,12 @@ hipError_t launch_rows_sum_f32(const float* x, size_t rows, size_t cols, size_t 
                                const RowsLaunch& L, const RowsPolicy& p, hipStream_t stream);
 hipError_t launch_rows_max_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
                                const RowsLaunch& L, const RowsPolicy& p, hipStream_t stream);
+
+// Column reductions: out[c] over r < rows of x[r * ld + c], c < cols (>= 1).
+hipError_t launch_cols_sum_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                               const ColsLaunch& L, const ColsPolicy& p, hipStream_t stream);
+hipError_t launch_cols_max_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                               const ColsLaunch& L, const ColsPolicy& p, hipStream_t stream);
 
 // Ablation ladder: rung 1..5 writes one float partial per block of
 // kRungBlock threads into `partials`.

@@ -42,6 +42,16 @@ std::mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 
+// Per-(device, stream) scratch for column partials, grown on demand up to
+// kColsScratchMax bytes. Growing waits for the stream, then frees the old
+// buffer; it happens at most a few times per stream.
+struct Scratch {
+    void* ptr;
+    size_t bytes;
+};
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+constexpr size_t kColsScratchMax = (size_t)64 << 20;
+
 // Default launch shapes, chosen by measurement on MI355X (256 CUs, 8 TB/s):
 // single-wave blocks streaming 8 KiB tiles with the next tile in flight and
 // a second one-block launch for the combine. Arrays that fit in the 256 MB
@@ -129,6 +139,39 @@ red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
     g_workspaces.emplace(key, w);
     *ws = w;
     return RED_OK;
+}
+
+red_status get_scratch(int dev, hipStream_t stream, size_t bytes, void** out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    Scratch& sc = g_scratch[std::make_pair(dev, stream)];
+    if (sc.ptr != nullptr && sc.bytes >= bytes) {
+        *out = sc.ptr;
+        return RED_OK;
+    }
+    if (sc.ptr != nullptr) {
+        hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+        e = hipFree(sc.ptr);
+        sc.ptr = nullptr;
+        sc.bytes = 0;
+        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    }
+    size_t nb = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
+    void* p = nullptr;
+    const hipError_t e = hipMalloc(&p, nb);
+    if (e != hipSuccess || p == nullptr) return fail(e, RED_ERR_ALLOC);
+    sc.ptr = p;
+    sc.bytes = nb;
+    *out = p;
+    return RED_OK;
+}
+
+constexpr libred::ColsPolicy kDefaultCols = {8, 1, 1024, 0};
+
+libred::ColsPolicy to_cols(const red_cols_policy* p) {
+    if (!p) return kDefaultCols;
+    libred::ColsPolicy c = {p->unroll, p->nontemporal, p->target_waves, p->vec};
+    return c;
 }
 
 FlatPolicy to_flat(const red_flat_policy* p, size_t n, bool fused = false) {
@@ -223,6 +266,54 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     return RED_OK;
 }
 
+template <class Launch>
+red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                     const red_cols_policy* pol, hipStream_t stream, Launch launch) {
+    if (ld < cols || rows > RED_MAX_N || cols > RED_MAX_N || ld > RED_MAX_N) return RED_ERR_INVALID_ARG;
+    if (rows > 1 && ld != 0 && rows - 1 > (RED_MAX_N - cols) / ld) return RED_ERR_INVALID_ARG;
+    const size_t span = rows == 0 ? 0 : (rows - 1) * ld + cols;
+    const libred::ColsPolicy p = to_cols(pol);
+    if (!libred::cols_policy_supported(p)) return RED_ERR_INVALID_ARG;
+    if (cols == 0) return RED_OK;
+    if ((span > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
+    if (!aligned(x, sizeof(float)) || !aligned(out, sizeof(float))) return RED_ERR_INVALID_ARG;
+    if (overlap(x, span * sizeof(float), out, cols * sizeof(float))) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+
+    libred::ColsLaunch L;
+    const bool vec_ok = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
+    L.vec = (p.vec != 1 && vec_ok) ? 4 : 1;
+    // Narrow matrix: if the column groups divide a wave, pack several rows
+    // into each load.
+    const size_t groups = cols / (size_t)L.vec;
+    L.ngroups = 64;
+    if (groups < 64 && 64 % groups == 0) L.ngroups = (unsigned int)groups;
+    L.ncb = (cols + (size_t)L.ngroups * L.vec - 1) / ((size_t)L.ngroups * L.vec);
+    size_t nchunks = 1;
+    if (rows > 0) {
+        nchunks = ((size_t)p.target_waves + L.ncb - 1) / L.ncb;
+        const size_t by_rows = (rows + 8 * (64 / L.ngroups) - 1) / (8 * (64 / L.ngroups));  // >= 8 loads per lane
+        if (nchunks > by_rows) nchunks = by_rows;
+        const size_t by_scratch = kColsScratchMax / (cols * 8);
+        if (nchunks > by_scratch) nchunks = by_scratch;
+        if (nchunks < 1) nchunks = 1;
+        const size_t rchunk = (rows + nchunks - 1) / nchunks;
+        nchunks = (rows + rchunk - 1) / rchunk;  // no empty chunk
+    }
+    L.nchunks = nchunks;
+    L.partials = nullptr;
+    if (nchunks > 1) {
+        st = get_scratch(dev, stream, nchunks * cols * 8, &L.partials);
+        if (st != RED_OK) return st;
+    }
+    const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,6 +350,16 @@ red_status red_rows_sum_f32_ld(const float* x, size_t rows, size_t cols, size_t 
 red_status red_rows_max_f32_ld(const float* x, size_t rows, size_t cols, size_t ld, float* out,
                                hipStream_t stream) {
     return rows_call(x, rows, cols, ld, out, nullptr, stream, libred::launch_rows_max_f32);
+}
+
+red_status red_cols_sum_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                            hipStream_t stream) {
+    return cols_call(x, rows, cols, ld, out, nullptr, stream, libred::launch_cols_sum_f32);
+}
+
+red_status red_cols_max_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                            hipStream_t stream) {
+    return cols_call(x, rows, cols, ld, out, nullptr, stream, libred::launch_cols_max_f32);
 }
 
 const char* red_status_string(red_status status) {
@@ -391,6 +492,26 @@ red_status red_rows_max_f32_with(const float* x, size_t rows, size_t cols, size_
                                  const red_rows_policy* p, hipStream_t stream) {
     if (!p) return RED_ERR_INVALID_ARG;
     return rows_call(x, rows, cols, ld, out, p, stream, libred::launch_rows_max_f32);
+}
+
+void red_default_cols_policy(red_cols_policy* p) {
+    if (!p) return;
+    p->unroll = kDefaultCols.unroll;
+    p->nontemporal = kDefaultCols.nontemporal;
+    p->target_waves = kDefaultCols.target_waves;
+    p->vec = kDefaultCols.vec;
+}
+
+red_status red_cols_sum_f32_with(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                                 const red_cols_policy* p, hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    return cols_call(x, rows, cols, ld, out, p, stream, libred::launch_cols_sum_f32);
+}
+
+red_status red_cols_max_f32_with(const float* x, size_t rows, size_t cols, size_t ld, float* out,
+                                 const red_cols_policy* p, hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    return cols_call(x, rows, cols, ld, out, p, stream, libred::launch_cols_max_f32);
 }
 
 // ---------------------------------------------------------------- probes

@@ -244,5 +244,25 @@ def pin_rows_degenerate(o):
     assert S.size == 0 and A.size == 0
 
 
+def pin_cols_brute_force(o):
+    # Column reductions are the row reductions of the transpose; check them
+    # against fsum and max over each column directly.
+    rng = np.random.default_rng(12)
+    for rows, cols in ((1, 1), (5, 3), (64, 7), (129, 65), (3, 1000)):
+        x = rng.standard_normal((rows, cols)).astype(np.float32)
+        x[(np.arange(cols) * 5) % rows, np.arange(cols)] = 77.0 + np.arange(cols)
+        S, A = o.cols_sum_f32(x)
+        for c in range(cols):
+            col = x[:, c]
+            assert abs(S[c] - _fsum(col)) <= 2 * U * abs(_fsum(col)) + 1e-300, (rows, cols, c)
+            assert abs(A[c] - _fsum(np.abs(col))) <= rows * U * _fsum(np.abs(col))
+        assert np.array_equal(o.cols_max_f32(x), x.max(axis=0)), (rows, cols)
+    # (r + c) mod 7 is symmetric in r and c, so column sums follow the row
+    # closed form with rows and columns swapped.
+    x = ((np.arange(40)[:, None] + np.arange(9)[None, :]) % 7).astype(np.float32)
+    S, _ = o.cols_sum_f32(x)
+    assert np.array_equal(S, [_rows_mod7_closed(c, 40) for c in range(9)])
+
+
 PINS = [(name, fn) for name, fn in sorted(globals().items())
         if name.startswith("pin_") and callable(fn)]

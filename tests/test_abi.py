@@ -124,6 +124,22 @@ def test_rows_argument_errors():
         assert f(None, 0, 4, 8, None, None) == rl.RED_OK
 
 
+def test_cols_argument_errors():
+    L = rl.lib()
+    for f in (L.red_cols_sum_f32, L.red_cols_max_f32):
+        assert f(_p(A), 2, 5, 4, _p(B), None) == INVALID                 # ld < cols
+        assert f(None, 2, 3, 3, _p(B), None) == INVALID
+        assert f(_p(A), 2, 3, 3, None, None) == INVALID
+        assert f(_p(A + 2), 2, 3, 3, _p(B), None) == INVALID
+        assert f(_p(A), 4, 4, 4, _p(A + 16), None) == INVALID           # out inside x
+        assert f(_p(A), 1 << 30, 1 << 11, 1 << 11, _p(B), None) == INVALID   # span > RED_MAX_N
+        assert f(None, 5, 0, 0, None, None) == rl.RED_OK                 # cols == 0: no-op
+    bad = rl.ColsPolicy(3, 1, 1024, 0)
+    assert L.red_cols_sum_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
+    bad = rl.ColsPolicy(8, 1, 1024, 2)
+    assert L.red_cols_max_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
+
+
 def test_ablate_argument_errors():
     L = rl.lib()
     assert L.red_ablate_num_partials(1, 1000) == 4

@@ -386,6 +386,41 @@ def test_rows_split_long_rows(rows, cols):
         assert np.array_equal(m.cpu().numpy(), M), p
 
 
+COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260), (4099, 1024, 1024),
+              (33, 1000, 1001), (2, 4096, 4096), (0, 8, 8), (70_000, 12, 12), (5, 100_003, 100_003)]
+
+
+@pytest.mark.parametrize("rows,cols,ld", COL_SHAPES)
+def test_cols(rows, cols, ld):
+    rng = np.random.default_rng(rows * 13 + cols * 7 + ld)
+    full = np.full((rows, ld), np.nan, np.float32)
+    full[:, :cols] = rng.standard_normal((rows, cols)).astype(np.float32)
+    if rows and cols:
+        full[(np.arange(cols) * 7919) % rows, np.arange(cols)] = 50.0 + np.arange(cols) % 97
+    a = np.ascontiguousarray(full[:, :cols])
+    S, A = oracle.cols_sum_f32(a)
+    M = oracle.cols_max_f32(a)
+    for offset in (0, 1):
+        for p in (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=16, nontemporal=0)):
+            say(f"cols {rows}x{cols} ld={ld} offset={offset} policy={p}")
+            x = device_view(full, offset)[:, :cols]
+            s = rl.red_cols_sum_f32(x, policy=p)
+            m = rl.red_cols_max_f32(x, policy=p)
+            torch.cuda.synchronize()
+            assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
+            assert np.array_equal(m.cpu().numpy(), M), p
+
+
+def test_cols_mod7_exact():
+    rows, cols = 4097, 1031
+    say("cols mod7")
+    a = W.pattern_rows_mod7(rows, cols)
+    S, _ = oracle.cols_sum_f32(a)
+    out = rl.red_cols_sum_f32(device_view(a, 0))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.float64), S)
+
+
 def test_rows_mod7_exact():
     rows, cols = 1031, 4097
     say(f"rows mod7 {rows}x{cols}")
@@ -631,6 +666,19 @@ def test_full_rows_65536x4096():
     S, A = oracle.rows_sum_f32(a)
     assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
     assert np.array_equal(m.cpu().numpy(), oracle.rows_max_f32(a))
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_cols_65536x4096():
+    a, x = _load("rows_f32_65536x4096")
+    say("red_cols_sum_f32 / red_cols_max_f32 rows_f32_65536x4096")
+    s = rl.red_cols_sum_f32(x)
+    m = rl.red_cols_max_f32(x)
+    torch.cuda.synchronize()
+    S, A = oracle.cols_sum_f32(a)
+    assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
+    assert np.array_equal(m.cpu().numpy(), oracle.cols_max_f32(a))
     del x
     torch.cuda.empty_cache()
 
