@@ -44,6 +44,14 @@ class Oracle:
         lib.oracle_rows_sum_f32.restype = None
         lib.oracle_rows_max_f32.argtypes = [P, Z, Z, P]
         lib.oracle_rows_max_f32.restype = None
+        lib.oracle_min_f32.argtypes = [P, Z]
+        lib.oracle_min_f32.restype = ctypes.c_float
+        lib.oracle_argmax_f32.argtypes = [P, Z]
+        lib.oracle_argmax_f32.restype = ctypes.c_int64
+        lib.oracle_argmin_f32.argtypes = [P, Z]
+        lib.oracle_argmin_f32.restype = ctypes.c_int64
+        lib.oracle_sum_f64.argtypes = [P, Z, D, D]
+        lib.oracle_sum_f64.restype = None
         self.lib = lib
         self.path = libpath
 
@@ -86,6 +94,42 @@ class Oracle:
         self.lib.oracle_rows_max_f32(a.ctypes.data, rows, cols, out.ctypes.data)
         return out
 
+    def min_f32(self, x):
+        """float32 minimum (strictly-smaller rule from +inf; NaN never wins)."""
+        a = _as(x, np.float32).ravel()
+        return np.float32(self.lib.oracle_min_f32(a.ctypes.data, a.size))
+
+    def argmax_f32(self, x):
+        """Lowest index of the maximum among non-NaN elements, or -1."""
+        a = _as(x, np.float32).ravel()
+        return int(self.lib.oracle_argmax_f32(a.ctypes.data, a.size))
+
+    def argmin_f32(self, x):
+        """Lowest index of the minimum among non-NaN elements, or -1."""
+        a = _as(x, np.float32).ravel()
+        return int(self.lib.oracle_argmin_f32(a.ctypes.data, a.size))
+
+    def sum_f64(self, x):
+        """Return (S, A) for float64 x: compensated sum and sum|x|."""
+        a = _as(x, np.float64).ravel()
+        s = ctypes.c_double()
+        ab = ctypes.c_double()
+        self.lib.oracle_sum_f64(a.ctypes.data, a.size, ctypes.byref(s), ctypes.byref(ab))
+        return s.value, ab.value
+
+    def sum_bf16(self, bits):
+        """(S, A) of bfloat16 values given as uint16 bit patterns: each value
+        is the float32 whose upper 16 bits are the pattern (exact widening),
+        then summed like float32 input."""
+        b = np.ascontiguousarray(np.asarray(bits, np.uint16)).ravel()
+        return self.sum_f32((b.astype(np.uint32) << 16).view(np.float32))
+
+    def sum_f16(self, bits):
+        """(S, A) of IEEE half values given as uint16 bit patterns, widened
+        exactly to float32 (numpy's float16) and summed like float32 input."""
+        b = np.ascontiguousarray(np.asarray(bits, np.uint16)).ravel()
+        return self.sum_f32(b.view(np.float16).astype(np.float32))
+
     def cols_sum_f32(self, x):
         """Per-column (S, A) of a 2-D float32 array: the row oracle applied to
         the transposed array (sum along axis 0, by definition)."""
@@ -127,6 +171,30 @@ def rows_sum_f32(x):
 
 def rows_max_f32(x):
     return default().rows_max_f32(x)
+
+
+def min_f32(x):
+    return default().min_f32(x)
+
+
+def argmax_f32(x):
+    return default().argmax_f32(x)
+
+
+def argmin_f32(x):
+    return default().argmin_f32(x)
+
+
+def sum_f64(x):
+    return default().sum_f64(x)
+
+
+def sum_bf16(bits):
+    return default().sum_bf16(bits)
+
+
+def sum_f16(bits):
+    return default().sum_f16(bits)
 
 
 def cols_sum_f32(x):

@@ -47,33 +47,51 @@
  * *abs_sum receives sum |x_i| over the finite inputs in plain double
  * arithmetic (used only to scale a tolerance). n == 0 gives 0 and 0.
  */
+typedef struct {
+    double s, c, a;              /* running sum, correction, sum of |x| */
+    int saw_nan, saw_pinf, saw_ninf;
+} neumaier_t;
+
+static void nm_init(neumaier_t *st)
+{
+    st->s = st->c = st->a = 0.0;
+    st->saw_nan = st->saw_pinf = st->saw_ninf = 0;
+}
+
+static void nm_add(neumaier_t *st, double v)
+{
+    double t;
+    if (isnan(v)) { st->saw_nan = 1; return; }
+    if (isinf(v)) {
+        if (v > 0) st->saw_pinf = 1; else st->saw_ninf = 1;
+        return;
+    }
+    st->a += fabs(v);
+    t = st->s + v;
+    if (fabs(st->s) >= fabs(v))
+        st->c += (st->s - t) + v;   /* v's low bits were lost */
+    else
+        st->c += (v - t) + st->s;   /* s's low bits were lost */
+    st->s = t;
+}
+
+static void nm_result(const neumaier_t *st, double *sum, double *abs_sum)
+{
+    if (abs_sum) *abs_sum = st->a;
+    if (st->saw_nan || (st->saw_pinf && st->saw_ninf)) *sum = NAN;
+    else if (st->saw_pinf) *sum = INFINITY;
+    else if (st->saw_ninf) *sum = -INFINITY;
+    else *sum = st->s + st->c;
+}
+
 static void neumaier_f32(const float *x, size_t n, double *sum, double *abs_sum)
 {
-    double s = 0.0, c = 0.0, a = 0.0;
-    int saw_nan = 0, saw_pinf = 0, saw_ninf = 0;
+    neumaier_t st;
     size_t i;
-
-    for (i = 0; i < n; ++i) {
-        double v = (double)x[i];
-        double t;
-        if (isnan(v)) { saw_nan = 1; continue; }
-        if (isinf(v)) {
-            if (v > 0) saw_pinf = 1; else saw_ninf = 1;
-            continue;
-        }
-        a += fabs(v);
-        t = s + v;
-        if (fabs(s) >= fabs(v))
-            c += (s - t) + v;   /* v's low bits were lost */
-        else
-            c += (v - t) + s;   /* s's low bits were lost */
-        s = t;
-    }
-    if (abs_sum) *abs_sum = a;
-    if (saw_nan || (saw_pinf && saw_ninf)) *sum = NAN;
-    else if (saw_pinf) *sum = INFINITY;
-    else if (saw_ninf) *sum = -INFINITY;
-    else *sum = s + c;
+    nm_init(&st);
+    for (i = 0; i < n; ++i)
+        nm_add(&st, (double)x[i]);   /* float32 widens to double exactly */
+    nm_result(&st, sum, abs_sum);
 }
 
 void oracle_sum_f32(const float *x, size_t n, double *sum, double *abs_sum)
@@ -109,6 +127,59 @@ float oracle_max_f32(const float *x, size_t n)
     for (i = 0; i < n; ++i)
         if (x[i] > m) m = x[i];
     return m;
+}
+
+/*
+ * Minimum of n float32 values: the mirror of oracle_max_f32. The running
+ * value is replaced only by a strictly smaller one, starting from +inf; a NaN
+ * never wins; empty or all-NaN gives +inf.
+ */
+float oracle_min_f32(const float *x, size_t n)
+{
+    float m = INFINITY;
+    size_t i;
+    for (i = 0; i < n; ++i)
+        if (x[i] < m) m = x[i];
+    return m;
+}
+
+/*
+ * Index of the maximum (sign = +1) or minimum (sign = -1) of n float32
+ * values: the lowest index i whose x[i] is not NaN and is >= (resp. <=) every
+ * other non-NaN element. -1 when no element is a number (n == 0 included).
+ * Scanning upward and replacing only on a strictly better value keeps the
+ * first of equal extremes; -0 and +0 are equal.
+ */
+static int64_t arg_extreme(const float *x, size_t n, int sign)
+{
+    int64_t best = -1;
+    float m = 0.0f;
+    size_t i;
+    for (i = 0; i < n; ++i) {
+        if (isnan(x[i])) continue;
+        if (best < 0 || (sign > 0 ? x[i] > m : x[i] < m)) {
+            m = x[i];
+            best = (int64_t)i;
+        }
+    }
+    return best;
+}
+
+int64_t oracle_argmax_f32(const float *x, size_t n) { return arg_extreme(x, n, +1); }
+int64_t oracle_argmin_f32(const float *x, size_t n) { return arg_extreme(x, n, -1); }
+
+/*
+ * Sum of n float64 values with the same compensated summation and
+ * non-finite rules as oracle_sum_f32 (the inputs are already doubles).
+ */
+void oracle_sum_f64(const double *x, size_t n, double *sum, double *abs_sum)
+{
+    neumaier_t st;
+    size_t k;
+    nm_init(&st);
+    for (k = 0; k < n; ++k)
+        nm_add(&st, x[k]);
+    nm_result(&st, sum, abs_sum);
 }
 
 /*

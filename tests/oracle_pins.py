@@ -264,5 +264,70 @@ def pin_cols_brute_force(o):
     assert np.array_equal(S, [_rows_mod7_closed(c, 40) for c in range(9)])
 
 
+def pin_min_and_argext(o):
+    rng = np.random.default_rng(13)
+    nan, inf = np.float32("nan"), np.float32("inf")
+    for n in (1, 2, 3, 63, 64, 65, 257, 4097):
+        x = rng.uniform(1.0, 100.0, n).astype(np.float32)          # all positive
+        for where in {0, n - 1, n // 2}:
+            y = x.copy()
+            y[where] = 0.5
+            assert o.min_f32(y) == np.float32(0.5), (n, where)
+            assert o.argmin_f32(y) == where, (n, where)
+            z = -x
+            z[where] = -0.5
+            assert o.argmax_f32(z) == where, (n, where)
+        vals = x.tolist()
+        assert o.argmax_f32(x) == vals.index(max(vals))
+        assert o.argmin_f32(x) == vals.index(min(vals))
+    # Ties: the lowest index wins; -0 equals +0.
+    t = np.array([1.0, 3.0, 2.0, 3.0, 3.0], np.float32)
+    assert o.argmax_f32(t) == 1 and o.argmin_f32(t) == 0
+    assert o.argmax_f32(np.array([-0.0, 0.0], np.float32)) == 0
+    assert o.argmin_f32(np.array([0.0, -0.0], np.float32)) == 0
+    # NaN never wins; no number at all gives -1 (and +inf for min).
+    assert o.argmax_f32(np.array([nan, 2.0, nan, 5.0, nan], np.float32)) == 3
+    assert o.argmin_f32(np.array([nan, 2.0, nan, 5.0], np.float32)) == 1
+    assert o.argmax_f32(np.array([nan, nan], np.float32)) == -1
+    assert o.argmax_f32(np.zeros(0, np.float32)) == -1
+    assert o.min_f32(np.array([nan, nan], np.float32)) == inf
+    assert o.min_f32(np.zeros(0, np.float32)) == inf
+    # Infinities are numbers: all -inf has its argmax at index 0.
+    assert o.argmax_f32(np.array([-inf, -inf], np.float32)) == 0
+    assert o.argmin_f32(np.array([3.0, -inf, -inf], np.float32)) == 1
+
+
+def pin_sum_f64(o):
+    for n in LENGTHS:
+        S, A = o.sum_f64(np.arange(n, dtype=np.float64))
+        assert S == n * (n - 1) // 2 and A == S, n
+    cases = [([1e300, 1.0, -1e300], 1.0), ([1.0, 2.0 ** 60, 1.0, -(2.0 ** 60)], 2.0)]
+    for xs, want in cases:
+        assert o.sum_f64(np.array(xs))[0] == want
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal(100_000) * 10.0 ** rng.uniform(-10, 10, 100_000)
+    want = _fsum(x)
+    S, A = o.sum_f64(x)
+    assert abs(S - want) <= 2 * U * abs(want) + 4 * x.size * U * U * _fsum(np.abs(x))
+    assert np.isnan(o.sum_f64(np.array([1.0, np.nan]))[0])
+    assert o.sum_f64(np.array([np.inf, 1.0]))[0] == np.inf
+
+
+def pin_half_formats(o):
+    # bfloat16 keeps float32's upper 16 bits; small integers are exact in both
+    # 16-bit formats, so sums of them have closed forms.
+    ints = np.arange(256, dtype=np.float32)
+    bf = (ints.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal((bf.astype(np.uint32) << 16).view(np.float32), ints)
+    assert o.sum_bf16(bf)[0] == 255 * 256 // 2
+    hf = ints.astype(np.float16).view(np.uint16)
+    assert o.sum_f16(hf)[0] == 255 * 256 // 2
+    # Known bit patterns: bf16 0x3F80 = 1.0, 0xC000 = -2.0; f16 0x3C00 = 1.0,
+    # 0x7BFF = 65504 (largest half), 0x0001 = 2^-24 (smallest subnormal).
+    assert o.sum_bf16(np.array([0x3F80, 0xC000], np.uint16))[0] == -1.0
+    assert o.sum_f16(np.array([0x3C00, 0x7BFF], np.uint16))[0] == 65505.0
+    assert o.sum_f16(np.array([0x0001, 0x0001], np.uint16))[0] == 2.0 ** -23
+
+
 PINS = [(name, fn) for name, fn in sorted(globals().items())
         if name.startswith("pin_") and callable(fn)]

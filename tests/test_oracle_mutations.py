@@ -13,20 +13,24 @@ from oracle import build as obuild
 from oracle_pins import PINS
 
 MUTATIONS = {
-    "drop_compensation": ("else *sum = s + c;", "else *sum = s;"),
-    "kahan_branch": ("if (fabs(s) >= fabs(v))", "if (1)"),
-    "swapped_branches": ("c += (s - t) + v;   /* v's", "c += (v - t) + s;   /* v's"),
-    "wrong_sign": ("c += (s - t) + v;", "c += (t - s) + v;"),
-    "abs_without_fabs": ("a += fabs(v);", "a += v;"),
-    "inf_pair_not_nan": ("if (saw_nan || (saw_pinf && saw_ninf))", "if (saw_nan)"),
-    "inf_sign_lost": ("if (v > 0) saw_pinf = 1; else saw_ninf = 1;", "saw_pinf = 1;"),
-    "skip_last_element": ("for (i = 0; i < n; ++i) {\n        double v",
-                          "for (i = 0; i + 1 < n; ++i) {\n        double v"),
+    "drop_compensation": ("else *sum = st->s + st->c;", "else *sum = st->s;"),
+    "kahan_branch": ("if (fabs(st->s) >= fabs(v))", "if (1)"),
+    "swapped_branches": ("st->c += (st->s - t) + v;   /* v's", "st->c += (v - t) + st->s;   /* v's"),
+    "wrong_sign": ("st->c += (st->s - t) + v;", "st->c += (t - st->s) + v;"),
+    "abs_without_fabs": ("st->a += fabs(v);", "st->a += v;"),
+    "inf_pair_not_nan": ("if (st->saw_nan || (st->saw_pinf && st->saw_ninf))", "if (st->saw_nan)"),
+    "inf_sign_lost": ("if (v > 0) st->saw_pinf = 1; else st->saw_ninf = 1;", "st->saw_pinf = 1;"),
+    "skip_last_element": ("for (i = 0; i < n; ++i)\n        nm_add(&st, (double)x[i]);",
+                          "for (i = 0; i + 1 < n; ++i)\n        nm_add(&st, (double)x[i]);"),
+    "f64_skips_first": ("for (k = 0; k < n; ++k)", "for (k = 1; k < n; ++k)"),
     "int32_accumulator": ("uint64_t s = 0;", "uint32_t s = 0;"),
     "no_sign_extension": ("s += (uint64_t)(int64_t)x[i];", "s += (uint64_t)(uint32_t)x[i];"),
     "max_starts_at_zero": ("float m = -INFINITY;", "float m = 0.0f;"),
     "max_starts_at_x0": ("float m = -INFINITY;", "float m = n ? x[0] : -INFINITY;"),
     "max_nan_wins": ("if (x[i] > m) m = x[i];", "if (!(x[i] <= m)) m = x[i];"),
+    "min_starts_at_zero": ("float m = INFINITY;", "float m = 0.0f;"),
+    "argmax_last_of_ties": ("(sign > 0 ? x[i] > m : x[i] < m)", "(sign > 0 ? x[i] >= m : x[i] <= m)"),
+    "argext_nan_not_skipped": ("        if (isnan(x[i])) continue;\n", ""),
     "rows_wrong_stride": ("neumaier_f32(x + r * cols, cols,", "neumaier_f32(x + r, cols,"),
     "rows_max_drops_last_col": ("out[r] = oracle_max_f32(x + r * cols, cols);",
                                 "out[r] = oracle_max_f32(x + r * cols, cols - (cols > 0));"),
