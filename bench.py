@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "achieved HBM GB/s (% of MI355X peak) for f32 sum over 2^28 elements"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["reduction_libred_amd/csrc/flat_reduce.hip",
+KERNEL_SOURCES = ["reduction_libred_amd/csrc/flat_reduce.hpp",
+                  "reduction_libred_amd/csrc/flat_sum_f32.hip",
                   "reduction_libred_amd/csrc/device_common.hpp"]
 
 
@@ -309,6 +310,22 @@ def main():
     fout = torch.empty(3, dtype=torch.float32, device=dev)
     measure("red_sum_max_f32 (fused sum, max, sum|x|) sum_max_f32_2p28",
             lambda: rl.red_sum_max_f32(x, out=fout), 4 * n + 12)
+    measure("red_min_f32 sum_max_f32_2p28", lambda: rl.red_min_f32(x, out=mout), nbytes)
+    iout = torch.empty((), dtype=torch.int64, device=dev)
+    measure("red_argmax_f32 sum_max_f32_2p28", lambda: rl.red_argmax_f32(x, out=iout), 4 * n + 8)
+    if not args.quick:
+        # The same 2^28 values rounded to 16-bit formats (2^29 elements = 1 GiB
+        # after doubling the count) and a 1 GiB float64 array.
+        for tdt, fn, label in ((torch.bfloat16, rl.red_sum_bf16_f32, "red_sum_bf16_f32"),
+                               (torch.float16, rl.red_sum_f16_f32, "red_sum_f16_f32")):
+            xh = torch.cat([x, x]).to(tdt)
+            measure(f"{label} 2^29 elements (1 GiB, the 2^28 normal array twice)",
+                    lambda: fn(xh, out=mout), 2 * xh.numel() + 4)
+            del xh
+        xd = x[: n // 2].to(torch.float64)
+        dout = torch.empty((), dtype=torch.float64, device=dev)
+        measure("red_sum_f64 2^27 elements (1 GiB)", lambda: rl.red_sum_f64(xd, out=dout), 8 * xd.numel() + 8)
+        del xd
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     measure("probe read sum_max_f32_2p28", lambda: rl.red_probe_read_f32(x, sink=sink), 4 * n)
     y = torch.empty_like(x)

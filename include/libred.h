@@ -88,6 +88,42 @@ red_status red_sum_i32_i64(const int32_t *x, size_t n, int64_t *out, hipStream_t
 red_status red_max_f32(const float *x, size_t n, float *out, hipStream_t stream);
 
 /*
+ * Minimum of n float32 values: the mirror of red_max_f32 (replaced only by a
+ * strictly smaller value, from +inf; a NaN never wins; empty or all-NaN gives
+ * +inf).
+ */
+red_status red_min_f32(const float *x, size_t n, float *out, hipStream_t stream);
+
+/*
+ * Index of the maximum / minimum of n float32 values: *out = the lowest index
+ * i such that x[i] is not NaN and x[i] >= (resp. <=) every non-NaN element;
+ * -1 when no element is a number (n == 0 included). Ties go to the lowest
+ * index and -0 equals +0, so the answer is unique and independent of the
+ * order in which blocks finish. The candidate (value, index) pairs are
+ * combined on the device like the partials of red_max_f32.
+ */
+red_status red_argmax_f32(const float *x, size_t n, int64_t *out, hipStream_t stream);
+red_status red_argmin_f32(const float *x, size_t n, int64_t *out, hipStream_t stream);
+
+/*
+ * Sum of n 16-bit floats given as their bit patterns (2-byte aligned), into
+ * one float32: each element is widened exactly (bfloat16: the upper half of a
+ * float32; IEEE half: the binary16 value), accumulated in float64 and rounded
+ * once. Eight elements arrive per 16-byte load. NaN/inf and n == 0 as for
+ * red_sum_f32.
+ */
+red_status red_sum_bf16_f32(const uint16_t *x, size_t n, float *out, hipStream_t stream);
+red_status red_sum_f16_f32(const uint16_t *x, size_t n, float *out, hipStream_t stream);
+
+/*
+ * Sum of n float64 values (8-byte aligned), accumulated in float64 in a fixed
+ * order: the error is at most of the order of h * 2^-53 * sum|x_i| with h the
+ * longest chain of additions (a few hundred at most), and repeated calls
+ * return the same bits.
+ */
+red_status red_sum_f64(const double *x, size_t n, double *out, hipStream_t stream);
+
+/*
  * Sum, max and sum of magnitudes of n float32 values in one pass over x:
  * out3[0] = x[0] + ... + x[n-1] (as red_sum_f32), out3[1] = the maximum (as
  * red_max_f32), out3[2] = |x[0]| + ... + |x[n-1]| (float64 inside, rounded

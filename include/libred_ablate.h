@@ -119,6 +119,26 @@ size_t red_flat_grid(size_t n, const red_flat_policy *p);
 red_status red_sum_f32_partials(const float *x, size_t n, double *partials, size_t partials_cap,
                                 const red_flat_policy *p, size_t *count, hipStream_t stream);
 
+/* Operation codes for red_flat_with. */
+enum {
+    RED_OP_SUM_F32 = 0,     /* float in, float out (red_sum_f32) */
+    RED_OP_SUM_I32_I64 = 1, /* int32_t in, int64_t out */
+    RED_OP_MAX_F32 = 2,     /* float in, float out */
+    RED_OP_MIN_F32 = 3,     /* float in, float out */
+    RED_OP_ARGMAX_F32 = 4,  /* float in, int64_t out */
+    RED_OP_ARGMIN_F32 = 5,  /* float in, int64_t out */
+    RED_OP_SUM_BF16_F32 = 6,/* uint16_t (bfloat16 bits) in, float out */
+    RED_OP_SUM_F16_F32 = 7, /* uint16_t (IEEE half bits) in, float out */
+    RED_OP_SUM_F64 = 8,     /* double in, double out */
+    RED_OP_SUM_MAX_F32 = 9  /* float in, float[3] out (red_sum_max_f32) */
+};
+
+/* Any single-value operation with an explicit launch shape: x and out have
+ * the element types listed for `op`; contracts as for the plain entry
+ * point. An unknown op or an unsupported shape is RED_ERR_INVALID_ARG. */
+red_status red_flat_with(int op, const void *x, size_t n, void *out, const red_flat_policy *p,
+                         hipStream_t stream);
+
 /* The single-value and row entry points with an explicit launch shape.
  * An unsupported shape is RED_ERR_INVALID_ARG. Results obey the same
  * contracts as the default entry points. */

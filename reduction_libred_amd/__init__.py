@@ -75,6 +75,13 @@ SIGNATURES = {
     "red_sum_i32_i64": (_S, [_P, _Z, _P, _P]),
     "red_max_f32": (_S, [_P, _Z, _P, _P]),
     "red_sum_max_f32": (_S, [_P, _Z, _P, _P]),
+    "red_min_f32": (_S, [_P, _Z, _P, _P]),
+    "red_argmax_f32": (_S, [_P, _Z, _P, _P]),
+    "red_argmin_f32": (_S, [_P, _Z, _P, _P]),
+    "red_sum_bf16_f32": (_S, [_P, _Z, _P, _P]),
+    "red_sum_f16_f32": (_S, [_P, _Z, _P, _P]),
+    "red_sum_f64": (_S, [_P, _Z, _P, _P]),
+    "red_flat_with": (_S, [_I, _P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
     "red_sum_max_f32_with": (_S, [_P, _Z, _P, ctypes.POINTER(FlatPolicy), _P]),
     "red_rows_sum_f32": (_S, [_P, _Z, _Z, _P, _P]),
     "red_rows_max_f32": (_S, [_P, _Z, _Z, _P, _P]),
@@ -176,6 +183,12 @@ def _policy(cls, p, n=0):
     return base
 
 
+# Operation codes of red_flat_with (include/libred_ablate.h).
+OPS = {"red_sum_f32": 0, "red_sum_i32_i64": 1, "red_max_f32": 2, "red_min_f32": 3,
+       "red_argmax_f32": 4, "red_argmin_f32": 5, "red_sum_bf16_f32": 6, "red_sum_f16_f32": 7,
+       "red_sum_f64": 8, "red_sum_max_f32": 9}
+
+
 def _flat(name, cname, x, out, in_dtype, out_dtype, stream, policy=None, out_shape=()):
     _input(x, in_dtype, name)
     out = _output(out, out_shape, out_dtype, x.device, name)
@@ -185,8 +198,7 @@ def _flat(name, cname, x, out, in_dtype, out_dtype, stream, policy=None, out_sha
             st = getattr(lib(), cname)(x.data_ptr(), x.numel(), out.data_ptr(), s)
         else:
             p = _policy(FlatPolicy, policy, x.numel())
-            st = getattr(lib(), cname + "_with")(x.data_ptr(), x.numel(), out.data_ptr(),
-                                                 ctypes.byref(p), s)
+            st = lib().red_flat_with(OPS[cname], x.data_ptr(), x.numel(), out.data_ptr(), ctypes.byref(p), s)
     _check(cname, st)
     return out
 
@@ -204,6 +216,45 @@ def red_sum_i32_i64(x, out=None, stream=None, policy=None):
 def red_max_f32(x, out=None, stream=None, policy=None):
     """Maximum of a float32 tensor (NaN never wins; empty gives -inf)."""
     return _flat("red_max_f32", "red_max_f32", x, out, torch.float32, torch.float32, stream, policy)
+
+
+def red_min_f32(x, out=None, stream=None, policy=None):
+    """Minimum of a float32 tensor (NaN never wins; empty gives +inf)."""
+    return _flat("red_min_f32", "red_min_f32", x, out, torch.float32, torch.float32, stream, policy)
+
+
+def red_argmax_f32(x, out=None, stream=None, policy=None):
+    """Lowest index of the maximum of a float32 tensor (-1 if none) -> 0-d int64."""
+    return _flat("red_argmax_f32", "red_argmax_f32", x, out, torch.float32, torch.int64, stream, policy)
+
+
+def red_argmin_f32(x, out=None, stream=None, policy=None):
+    """Lowest index of the minimum of a float32 tensor (-1 if none) -> 0-d int64."""
+    return _flat("red_argmin_f32", "red_argmin_f32", x, out, torch.float32, torch.int64, stream, policy)
+
+
+def _bits16(x, dtype, name):
+    # A bfloat16 / float16 tensor is passed as its 16-bit patterns.
+    if not isinstance(x, torch.Tensor) or x.dtype != dtype:
+        raise TypeError(f"{name}: input must be a {dtype} tensor")
+    return x.view(torch.int16)
+
+
+def red_sum_bf16_f32(x, out=None, stream=None, policy=None):
+    """Sum of a bfloat16 tensor into a 0-d float32 tensor (float64 inside)."""
+    return _flat("red_sum_bf16_f32", "red_sum_bf16_f32", _bits16(x, torch.bfloat16, "red_sum_bf16_f32"), out,
+                 torch.int16, torch.float32, stream, policy)
+
+
+def red_sum_f16_f32(x, out=None, stream=None, policy=None):
+    """Sum of a float16 tensor into a 0-d float32 tensor (float64 inside)."""
+    return _flat("red_sum_f16_f32", "red_sum_f16_f32", _bits16(x, torch.float16, "red_sum_f16_f32"), out,
+                 torch.int16, torch.float32, stream, policy)
+
+
+def red_sum_f64(x, out=None, stream=None, policy=None):
+    """Sum of a float64 tensor into a 0-d float64 tensor."""
+    return _flat("red_sum_f64", "red_sum_f64", x, out, torch.float64, torch.float64, stream, policy)
 
 
 def red_sum_max_f32(x, out=None, stream=None, policy=None):

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libred.so")
 
-SOURCES = ["libred.cpp", "flat_reduce.hip", "rows_reduce.hip", "cols_reduce.hip", "ablate.hip", "probe.hip"]
+SOURCES = ["libred.cpp", "flat_sum_f32.hip", "flat_ops.hip", "flat_fused.hip", "flat_argmax.hip", "flat_argmin.hip",
+           "flat_wide.hip", "rows_reduce.hip", "cols_reduce.hip", "ablate.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -29,12 +29,12 @@ struct ColVec<4, Op> {
 template <class Op, int VEC>
 __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typename ColVec<VEC, Op>::type v) {
     if constexpr (VEC == 1) {
-        acc[0] = Op::combine(acc[0], Op::lift(v));
+        acc[0] = Op::combine(acc[0], Op::lift(v, 0));
     } else {
-        acc[0] = Op::combine(acc[0], Op::lift(v.x));
-        acc[1] = Op::combine(acc[1], Op::lift(v.y));
-        acc[2] = Op::combine(acc[2], Op::lift(v.z));
-        acc[3] = Op::combine(acc[3], Op::lift(v.w));
+        acc[0] = Op::combine(acc[0], Op::lift(v.x, 0));
+        acc[1] = Op::combine(acc[1], Op::lift(v.y, 0));
+        acc[2] = Op::combine(acc[2], Op::lift(v.z, 0));
+        acc[3] = Op::combine(acc[3], Op::lift(v.w, 0));
     }
 }
 

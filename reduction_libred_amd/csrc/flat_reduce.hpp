@@ -1,4 +1,6 @@
-// flat_reduce.hip -- single-value reductions (sum f32, sum i32->i64, max f32).
+// flat_reduce.hpp -- the single-value reduction kernel and its launch-shape
+// dispatch, as templates over the reduction operator; the flat_*.hip
+// translation units instantiate them for their operators.
 //
 // The steps follow the block-partial scheme of the reduction lesson
 // ("03_shared_memory_sync_reduction.py", demo 3), redesigned for wave64 and a
@@ -30,14 +32,19 @@
 //       vector per lane per load, so each wave streams contiguous memory.
 //       With `PREFETCH`, the next tile's loads are issued before the current
 //       tile is folded, keeping 2*UNROLL KiB in flight per wave.
+#pragma once
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace libred {
 
+// Element number of the first element of body vector i (after the head).
+#define LIBRED_ELEM(i) (head + (size_t)(i) * Op::kPerVec)
+
 template <class Op, int BLOCK, int UNROLL, bool NT>
 __device__ __forceinline__ void body_grid_stride(const typename Op::vec_t* __restrict__ xv, size_t nvec,
-                                                 typename Op::acc_t (&acc)[4]) {
+                                                 size_t head, typename Op::acc_t (&acc)[4]) {
     using vec_t = typename Op::vec_t;
     const size_t stride = (size_t)gridDim.x * BLOCK;
     size_t i = (size_t)blockIdx.x * BLOCK + threadIdx.x;
@@ -46,9 +53,9 @@ __device__ __forceinline__ void body_grid_stride(const typename Op::vec_t* __res
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(xv + i + (size_t)u * stride);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) accumulate4<Op>(acc, v[u]);
+        for (int u = 0; u < UNROLL; ++u) fold_vec<Op>(acc, v[u], LIBRED_ELEM(i + (size_t)u * stride));
     }
-    for (; i < nvec; i += stride) accumulate4<Op>(acc, load_vec<NT>(xv + i));
+    for (; i < nvec; i += stride) fold_vec<Op>(acc, load_vec<NT>(xv + i), LIBRED_ELEM(i));
 }
 
 // One tile of a wave: UNROLL loads, each of 64 lanes x 16 bytes = 1 KiB.
@@ -58,16 +65,23 @@ __device__ __forceinline__ void load_tile(V (&v)[UNROLL], const V* __restrict__ 
     for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
 }
 
+// Fold a tile loaded from body vector index v0 (lane's first vector).
+// An operator with its own tile fold gets the element number of vector 0's
+// first element (vector u starts 64 * kPerVec elements later per step).
 template <class Op, int UNROLL>
 __device__ __forceinline__ void fold_tile(typename Op::acc_t (&acc)[4],
-                                          const typename Op::vec_t (&v)[UNROLL]) {
+                                          const typename Op::vec_t (&v)[UNROLL], size_t v0, size_t head) {
+    if constexpr (HasTileFold<Op>::value) {
+        Op::template fold_tile<UNROLL>(acc, v, LIBRED_ELEM(v0));
+    } else {
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) accumulate4<Op>(acc, v[u]);
+        for (int u = 0; u < UNROLL; ++u) fold_vec<Op>(acc, v[u], LIBRED_ELEM(v0 + (size_t)u * kWave));
+    }
 }
 
 template <class Op, int BLOCK, int UNROLL, bool NT, bool PREFETCH>
 __device__ __forceinline__ void body_wave_tiles(const typename Op::vec_t* __restrict__ xv, size_t nvec,
-                                                typename Op::acc_t (&acc)[4]) {
+                                                size_t head, typename Op::acc_t (&acc)[4]) {
     using vec_t = typename Op::vec_t;
     constexpr int W = BLOCK / kWave;
     constexpr size_t TILE = (size_t)kWave * UNROLL;  // vectors per tile
@@ -83,8 +97,7 @@ __device__ __forceinline__ void body_wave_tiles(const typename Op::vec_t* __rest
             vec_t v[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) accumulate4<Op>(acc, v[u]);
+            fold_tile<Op>(acc, v, t * TILE + lane, head);
         }
     } else if (t < ntiles) {
         // Two register buffers, a and b, alternate: the loads of the next
@@ -94,25 +107,25 @@ __device__ __forceinline__ void body_wave_tiles(const typename Op::vec_t* __rest
         load_tile<NT>(a, xv + t * TILE + lane);
         while (true) {
             if (t + nwaves >= ntiles) {
-                fold_tile<Op>(acc, a);
+                fold_tile<Op>(acc, a, t * TILE + lane, head);
                 break;
             }
             load_tile<NT>(b, xv + (t + nwaves) * TILE + lane);
-            fold_tile<Op>(acc, a);
+            fold_tile<Op>(acc, a, t * TILE + lane, head);
             t += nwaves;
             if (t + nwaves >= ntiles) {
-                fold_tile<Op>(acc, b);
+                fold_tile<Op>(acc, b, t * TILE + lane, head);
                 break;
             }
             load_tile<NT>(a, xv + (t + nwaves) * TILE + lane);
-            fold_tile<Op>(acc, b);
+            fold_tile<Op>(acc, b, t * TILE + lane, head);
             t += nwaves;
         }
     }
     // Vectors after the last whole tile (fewer than one tile).
     const size_t w = (size_t)blockIdx.x * W + wave;
     for (size_t i = ntiles * TILE + w * kWave + lane; i < nvec; i += nwaves * kWave)
-        accumulate4<Op>(acc, load_vec<NT>(xv + i));
+        fold_vec<Op>(acc, load_vec<NT>(xv + i), LIBRED_ELEM(i));
 }
 
 // mode: kCombineTicket (the last block combines), kCombineTwoPass (each
@@ -134,22 +147,26 @@ __global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
 
     // Split x into head (scalar), 16-byte aligned body, tail (scalar).
     const size_t head = head_elems(x, sizeof(elem_t), n);
-    const size_t nvec = (n - head) / 4;
-    const size_t tail0 = head + 4 * nvec;
+    const size_t nvec = (n - head) / Op::kPerVec;
+    const size_t tail0 = head + (size_t)Op::kPerVec * nvec;
     const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x + head);
 
     acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
 
     // Step 1: the body.
     if constexpr (LAYOUT == kGridStride)
-        body_grid_stride<Op, BLOCK, UNROLL, NT>(xv, nvec, acc);
+        body_grid_stride<Op, BLOCK, UNROLL, NT>(xv, nvec, head, acc);
     else
-        body_wave_tiles<Op, BLOCK, UNROLL, NT, PREFETCH>(xv, nvec, acc);
+        body_wave_tiles<Op, BLOCK, UNROLL, NT, PREFETCH>(xv, nvec, head, acc);
+
+    // An operator that deferred part of its fold finishes it here.
+    if constexpr (HasTileFold<Op>::value) Op::template resolve<UNROLL, NT>(acc, x);
 
     // Step 2: head and tail.
     if (blockIdx.x == 0) {
-        if (threadIdx.x < head) acc[0] = Op::combine(acc[0], Op::lift(x[threadIdx.x]));
-        if (threadIdx.x < n - tail0) acc[1] = Op::combine(acc[1], Op::lift(x[tail0 + threadIdx.x]));
+        if (threadIdx.x < head) acc[0] = Op::combine(acc[0], Op::lift(x[threadIdx.x], threadIdx.x));
+        if (threadIdx.x < n - tail0)
+            acc[1] = Op::combine(acc[1], Op::lift(x[tail0 + threadIdx.x], tail0 + threadIdx.x));
     }
 
     // Steps 3-4: thread -> wave -> block.
@@ -208,41 +225,14 @@ __global__ __launch_bounds__(kCombineBlock) void combine_partials_kernel(
     if (threadIdx.x == 0) out[0] = Op::finish(w);
 }
 
-__global__ void zero_words_kernel(unsigned int* p, size_t words) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0u;
-}
-
-hipError_t launch_zero_words(unsigned int* p, size_t words, hipStream_t stream) {
-    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, stream, p, words);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
 // Policy dispatch: the (layout, block, unroll, nontemporal, prefetch) shapes
 // compiled in.
 //   grid-stride: block 256 / 512 / 1024, unroll 1 / 2 / 4 / 8 / 16
 //   wave tiles:  block 64 / 256 / 512 / 1024, unroll 4 / 8 / 16, prefetch 0 / 1
 // ---------------------------------------------------------------------------
-bool flat_policy_supported(const FlatPolicy& p) {
-    if (p.blocks_per_cu < 1 || (p.nontemporal != 0 && p.nontemporal != 1)) return false;
-    if (p.combine != (int)kCombineTicket && p.combine != (int)kCombineTwoPass) return false;
-    if (p.layout == kGridStride) {
-        const bool b = p.block == 256 || p.block == 512 || p.block == 1024;
-        const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
-        return b && u && p.prefetch == 0;
-    }
-    if (p.layout == kWaveTiles) {
-        const bool b = p.block == 64 || p.block == 256 || p.block == 512 || p.block == 1024;
-        const bool u = p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
-        return b && u && (p.prefetch == 0 || p.prefetch == 1);
-    }
-    return false;
-}
-
 template <class Op, int BLOCK, int UNROLL, int LAYOUT, bool PREFETCH>
-static hipError_t launch_shape(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+inline hipError_t launch_shape(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
                                int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
     auto* partials = static_cast<typename Op::acc_t*>(ws.partials);
     const int mode = out == nullptr ? (int)kPartialsOnly : p.combine;
@@ -260,7 +250,7 @@ static hipError_t launch_shape(const typename Op::elem_t* x, size_t n, typename 
 }
 
 template <class Op, int BLOCK>
-static hipError_t launch_grid_stride(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+inline hipError_t launch_grid_stride(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
                                      int grid, const FlatPolicy& p, const Workspace& ws,
                                      hipStream_t stream) {
     switch (p.unroll) {
@@ -274,7 +264,7 @@ static hipError_t launch_grid_stride(const typename Op::elem_t* x, size_t n, typ
 }
 
 template <class Op, int BLOCK, bool PREFETCH>
-static hipError_t launch_tiles_p(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+inline hipError_t launch_tiles_p(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
                                  int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
     switch (p.unroll) {
         case 4: return launch_shape<Op, BLOCK, 4, kWaveTiles, PREFETCH>(x, n, out, grid, p, ws, stream);
@@ -285,14 +275,14 @@ static hipError_t launch_tiles_p(const typename Op::elem_t* x, size_t n, typenam
 }
 
 template <class Op, int BLOCK>
-static hipError_t launch_tiles(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+inline hipError_t launch_tiles(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
                                int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
     if (p.prefetch) return launch_tiles_p<Op, BLOCK, true>(x, n, out, grid, p, ws, stream);
     return launch_tiles_p<Op, BLOCK, false>(x, n, out, grid, p, ws, stream);
 }
 
 template <class Op>
-static hipError_t launch_op(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
+inline hipError_t launch_op(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
                             int grid, const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
     if (p.layout == kGridStride) {
         switch (p.block) {
@@ -311,38 +301,6 @@ static hipError_t launch_op(const typename Op::elem_t* x, size_t n, typename Op:
     }
 }
 
-hipError_t launch_sum_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
-                          const Workspace& ws, hipStream_t stream) {
-    return launch_op<SumF32>(x, n, out, grid, p, ws, stream);
-}
-
-hipError_t launch_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, int grid,
-                              const FlatPolicy& p, const Workspace& ws, hipStream_t stream) {
-    return launch_op<SumI32>(x, n, out, grid, p, ws, stream);
-}
-
-hipError_t launch_max_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
-                          const Workspace& ws, hipStream_t stream) {
-    return launch_op<MaxF32>(x, n, out, grid, p, ws, stream);
-}
-
-hipError_t launch_sum_max_f32(const float* x, size_t n, float* out3, int grid, const FlatPolicy& p,
-                              const Workspace& ws, hipStream_t stream) {
-    return launch_op<SumMaxAbsF32>(x, n, reinterpret_cast<SumMaxAbsOut*>(out3), grid, p, ws, stream);
-}
-
-hipError_t launch_sum_f32_partials(const float* x, size_t n, double* partials, int grid,
-                                   const FlatPolicy& p, hipStream_t stream) {
-    Workspace ws;
-    ws.ticket = nullptr;
-    ws.partials = partials;
-    ws.max_partials = (size_t)grid;
-    return launch_op<SumF32>(x, n, nullptr, grid, p, ws, stream);
-}
-
-hipError_t launch_xor_u32(const uint32_t* x, size_t n, uint32_t* out, int grid, const FlatPolicy& p,
-                          const Workspace& ws, hipStream_t stream) {
-    return launch_op<XorU32>(x, n, out, grid, p, ws, stream);
-}
+#undef LIBRED_ELEM
 
 }  // namespace libred

@@ -95,6 +95,18 @@ hipError_t launch_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, int grid
                               const FlatPolicy& p, const Workspace& ws, hipStream_t stream);
 hipError_t launch_max_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
                           const Workspace& ws, hipStream_t stream);
+hipError_t launch_min_f32(const float* x, size_t n, float* out, int grid, const FlatPolicy& p,
+                          const Workspace& ws, hipStream_t stream);
+hipError_t launch_argmax_f32(const float* x, size_t n, int64_t* out, int grid, const FlatPolicy& p,
+                             const Workspace& ws, hipStream_t stream);
+hipError_t launch_argmin_f32(const float* x, size_t n, int64_t* out, int grid, const FlatPolicy& p,
+                             const Workspace& ws, hipStream_t stream);
+hipError_t launch_sum_bf16(const uint16_t* x, size_t n, float* out, int grid, const FlatPolicy& p,
+                           const Workspace& ws, hipStream_t stream);
+hipError_t launch_sum_f16(const uint16_t* x, size_t n, float* out, int grid, const FlatPolicy& p,
+                          const Workspace& ws, hipStream_t stream);
+hipError_t launch_sum_f64(const double* x, size_t n, double* out, int grid, const FlatPolicy& p,
+                          const Workspace& ws, hipStream_t stream);
 // Fused: out3[0] = sum, out3[1] = max, out3[2] = sum of |x|.
 hipError_t launch_sum_max_f32(const float* x, size_t n, float* out3, int grid, const FlatPolicy& p,
                               const Workspace& ws, hipStream_t stream);

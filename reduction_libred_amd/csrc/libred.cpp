@@ -334,6 +334,30 @@ red_status red_sum_max_f32(const float* x, size_t n, float* out3, hipStream_t st
     return flat_call(x, n, out3, nullptr, stream, libred::launch_sum_max_f32, 3, true);
 }
 
+red_status red_min_f32(const float* x, size_t n, float* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_min_f32);
+}
+
+red_status red_argmax_f32(const float* x, size_t n, int64_t* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_argmax_f32);
+}
+
+red_status red_argmin_f32(const float* x, size_t n, int64_t* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_argmin_f32);
+}
+
+red_status red_sum_bf16_f32(const uint16_t* x, size_t n, float* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_sum_bf16);
+}
+
+red_status red_sum_f16_f32(const uint16_t* x, size_t n, float* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_sum_f16);
+}
+
+red_status red_sum_f64(const double* x, size_t n, double* out, hipStream_t stream) {
+    return flat_call(x, n, out, nullptr, stream, libred::launch_sum_f64);
+}
+
 red_status red_rows_sum_f32(const float* x, size_t rows, size_t cols, float* out, hipStream_t stream) {
     return rows_call(x, rows, cols, cols, out, nullptr, stream, libred::launch_rows_sum_f32);
 }
@@ -468,6 +492,45 @@ red_status red_sum_i32_i64_with(const int32_t* x, size_t n, int64_t* out, const 
                                 hipStream_t stream) {
     if (!p) return RED_ERR_INVALID_ARG;
     return flat_call(x, n, out, p, stream, libred::launch_sum_i32_i64);
+}
+
+red_status red_flat_with(int op, const void* x, size_t n, void* out, const red_flat_policy* p,
+                         hipStream_t stream) {
+    if (!p) return RED_ERR_INVALID_ARG;
+    switch (op) {
+        case RED_OP_SUM_F32:
+            return flat_call(static_cast<const float*>(x), n, static_cast<float*>(out), p, stream,
+                             libred::launch_sum_f32);
+        case RED_OP_SUM_I32_I64:
+            return flat_call(static_cast<const int32_t*>(x), n, static_cast<int64_t*>(out), p, stream,
+                             libred::launch_sum_i32_i64);
+        case RED_OP_MAX_F32:
+            return flat_call(static_cast<const float*>(x), n, static_cast<float*>(out), p, stream,
+                             libred::launch_max_f32);
+        case RED_OP_MIN_F32:
+            return flat_call(static_cast<const float*>(x), n, static_cast<float*>(out), p, stream,
+                             libred::launch_min_f32);
+        case RED_OP_ARGMAX_F32:
+            return flat_call(static_cast<const float*>(x), n, static_cast<int64_t*>(out), p, stream,
+                             libred::launch_argmax_f32);
+        case RED_OP_ARGMIN_F32:
+            return flat_call(static_cast<const float*>(x), n, static_cast<int64_t*>(out), p, stream,
+                             libred::launch_argmin_f32);
+        case RED_OP_SUM_BF16_F32:
+            return flat_call(static_cast<const uint16_t*>(x), n, static_cast<float*>(out), p, stream,
+                             libred::launch_sum_bf16);
+        case RED_OP_SUM_F16_F32:
+            return flat_call(static_cast<const uint16_t*>(x), n, static_cast<float*>(out), p, stream,
+                             libred::launch_sum_f16);
+        case RED_OP_SUM_F64:
+            return flat_call(static_cast<const double*>(x), n, static_cast<double*>(out), p, stream,
+                             libred::launch_sum_f64);
+        case RED_OP_SUM_MAX_F32:
+            return flat_call(static_cast<const float*>(x), n, static_cast<float*>(out), p, stream,
+                             libred::launch_sum_max_f32, 3, true);
+        default:
+            return RED_ERR_INVALID_ARG;
+    }
 }
 
 red_status red_sum_max_f32_with(const float* x, size_t n, float* out3, const red_flat_policy* p,

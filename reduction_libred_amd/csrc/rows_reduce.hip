@@ -31,8 +31,8 @@ __device__ __forceinline__ void fold_row_span(const typename Op::elem_t* __restr
     constexpr size_t TILE = (size_t)kWave * UNROLL;
     const int lane = threadIdx.x % kWave;
     const size_t head = head_elems(row, sizeof(typename Op::elem_t), cols);
-    const size_t nvec = (cols - head) / 4;
-    const size_t tail0 = head + 4 * nvec;
+    const size_t nvec = (cols - head) / Op::kPerVec;
+    const size_t tail0 = head + (size_t)Op::kPerVec * nvec;
     const vec_t* __restrict__ rv = reinterpret_cast<const vec_t*>(row + head);
     const size_t ntiles = nvec / TILE;
     for (size_t t = first_tile; t < ntiles; t += tile_step) {
@@ -41,13 +41,15 @@ __device__ __forceinline__ void fold_row_span(const typename Op::elem_t* __restr
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) accumulate4<Op>(acc, v[u]);
+        for (int u = 0; u < UNROLL; ++u)
+            fold_vec<Op>(acc, v[u], head + (t * TILE + lane + (size_t)u * kWave) * Op::kPerVec);
     }
     for (size_t i = ntiles * TILE + first_tile * kWave + lane; i < nvec; i += tile_step * kWave)
-        accumulate4<Op>(acc, load_vec<NT>(rv + i));
+        fold_vec<Op>(acc, load_vec<NT>(rv + i), head + i * Op::kPerVec);
     if (edges) {
-        if ((size_t)lane < head) acc[0] = Op::combine(acc[0], Op::lift(row[lane]));
-        if ((size_t)lane < cols - tail0) acc[1] = Op::combine(acc[1], Op::lift(row[tail0 + lane]));
+        if ((size_t)lane < head) acc[0] = Op::combine(acc[0], Op::lift(row[lane], lane));
+        if ((size_t)lane < cols - tail0)
+            acc[1] = Op::combine(acc[1], Op::lift(row[tail0 + lane], tail0 + lane));
     }
 }
 

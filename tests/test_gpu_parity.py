@@ -318,6 +318,173 @@ def test_sum_max_f32_all_policies():
         assert_fused_ok(got, a)
 
 
+# ----------------------------------------------------------------- min, argmax, argmin
+
+@pytest.mark.parametrize("offset", [0, 1, 3])
+def test_min_argext_ragged(offset):
+    rng = np.random.default_rng(700 + offset)
+    for n in RAGGED:
+        say(f"min/argmax/argmin n={n} offset={offset}")
+        a = rng.standard_normal(n).astype(np.float32)
+        x = device_view(a, offset)
+        mn = rl.red_min_f32(x)
+        am = rl.red_argmax_f32(x)
+        ai = rl.red_argmin_f32(x)
+        torch.cuda.synchronize()
+        assert mn.item() == float(oracle.min_f32(a)), n
+        assert int(am.item()) == oracle.argmax_f32(a), n
+        assert int(ai.item()) == oracle.argmin_f32(a), n
+
+
+def test_argext_ties_nan_empty():
+    nan, inf = float("nan"), float("inf")
+    n = (1 << 20) + 5
+    cases = []
+    a = np.zeros(n, np.float32)
+    cases.append(a)                                         # all equal: index 0
+    b = np.zeros(n, np.float32)
+    b[[7, 5000, 70000, 900001, n - 1]] = 3.0               # equal maxima in many blocks
+    b[[9, 6000, 80000, 800001, n - 2]] = -3.0               # equal minima
+    cases.append(b)
+    c = np.full(n, nan, np.float32)
+    c[[12345, 777777]] = [-1.0, 2.0]                        # NaN everywhere else
+    cases.append(c)
+    d = np.full(n, -inf, np.float32)
+    d[0] = nan                                              # all -inf after a NaN: argmax 1
+    cases.append(d)
+    e = np.array([0.0, -0.0, 0.0, -0.0], np.float32)        # -0 == +0: index 0
+    cases.append(e)
+    for k, arr in enumerate(cases):
+        for offset in (0, 2):
+            say(f"argext case {k} offset={offset}")
+            x = device_view(arr, offset, guard=float("inf"))
+            am, ai = rl.red_argmax_f32(x), rl.red_argmin_f32(x)
+            torch.cuda.synchronize()
+            assert int(am.item()) == oracle.argmax_f32(arr), (k, offset)
+            assert int(ai.item()) == oracle.argmin_f32(arr), (k, offset)
+    for arr in (np.full(100, nan, np.float32), np.zeros(0, np.float32)):
+        say(f"argext no number n={arr.size}")
+        x = device_view(arr, 1) if arr.size else torch.empty(0, device=DEV)
+        assert int(rl.red_argmax_f32(x).item()) == -1
+        assert int(rl.red_argmin_f32(x).item()) == -1
+        assert rl.red_min_f32(x).item() == float("inf")
+
+
+def test_argext_tile_cases():
+    """Cases aimed at the streaming form of argmax/argmin: each thread keeps
+    only the best tile value while streaming and re-reads that tile to find
+    the first matching element, so ties inside and across tiles, extremes in
+    the last lane of a tile, denormal extremes, signaling NaNs beside the
+    extreme, and orders that replace the candidate on every tile all have to
+    give the oracle's index."""
+    rng = np.random.default_rng(4242)
+    n = (1 << 22) + 13
+    cases = {}
+    a = -rng.random(n, dtype=np.float32)
+    a[np.sort(rng.choice(n, 64, replace=False))] = 1.0          # 64 tied maxima
+    a[np.sort(rng.choice(n, 64, replace=False))] = -2.0         # 64 tied minima
+    cases["ties"] = a
+    cases["increasing"] = np.arange(n, dtype=np.float32)       # ties in the f32 rounding
+    cases["decreasing"] = -np.arange(n, dtype=np.float32)
+    d = (rng.random(n, dtype=np.float32) * 2.0 ** -130).astype(np.float32)   # denormals
+    d[[1_000_003, 3_000_001]] = np.float32(2.0 ** -127)
+    d[[2_000_002]] = np.float32(0.0)
+    cases["denormal"] = d
+    s = rng.standard_normal(n).astype(np.float32)
+    s.view(np.uint32)[::3] = 0x7F800001                      # signaling NaN bits
+    s[[777_777]] = 50.0
+    s[[777_778, 777_776]] = -50.0
+    cases["snan"] = s
+    z = -rng.random(n, dtype=np.float32) - 1.0
+    z[[5_000, 5_001, 4_000_000]] = [-0.0, 0.0, 0.0]             # first zero is -0
+    cases["signed_zero"] = z
+    e = rng.standard_normal(n).astype(np.float32)
+    e[[255, 256 * 64 - 1, n - 1]] = 30.0                         # last lanes, array end
+    e[[1023, n - 2]] = -30.0
+    cases["lane_edges"] = e
+    for name, arr in cases.items():
+        for offset in (0, 1):
+            say(f"argext tile case {name} offset={offset}")
+            x = device_view(arr, offset, guard=float("nan"))
+            am, ai = rl.red_argmax_f32(x), rl.red_argmin_f32(x)
+            torch.cuda.synchronize()
+            assert int(am.item()) == oracle.argmax_f32(arr), (name, offset)
+            assert int(ai.item()) == oracle.argmin_f32(arr), (name, offset)
+
+
+def test_min_argext_all_policies():
+    n = (1 << 21) + 7
+    a = W.make("normal", n, 83)
+    a[[3, 100_003, n - 2]] = 9.0          # tied maxima: head, middle, tail
+    a[[1, 200_003, n - 1]] = -9.0         # tied minima
+    x = device_view(a, 3, guard=float("nan"))
+    for p in all_flat_policies(bpcs=(2,)):
+        say(f"argext policy {p}")
+        am = rl.red_argmax_f32(x, policy=p)
+        ai = rl.red_argmin_f32(x, policy=p)
+        mn = rl.red_min_f32(x, policy=p)
+        torch.cuda.synchronize()
+        assert int(am.item()) == 3 and int(ai.item()) == 1 and mn.item() == -9.0, p
+
+
+# ----------------------------------------------------------------- bf16 / f16 / f64 sums
+
+def _half_bits(a32, dtype):
+    t = torch.from_numpy(a32).to(dtype)
+    return t.view(torch.int16).numpy().view(np.uint16), t
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_sum_half_ragged(dtype):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    fn = rl.red_sum_bf16_f32 if dtype == "bf16" else rl.red_sum_f16_f32
+    ofn = oracle.sum_bf16 if dtype == "bf16" else oracle.sum_f16
+    rng = np.random.default_rng(800)
+    for n in RAGGED + [8, 9, 15, 17, 1023 * 8 + 7]:
+        for offset in (0, 1, 3, 7):
+            say(f"sum {dtype} n={n} offset={offset}")
+            bits, t = _half_bits(rng.standard_normal(n).astype(np.float32) * 10, tdt)
+            buf = torch.full((n + offset + 16,), float("nan"), dtype=tdt, device=DEV)
+            buf[offset:offset + n] = t.to(DEV)
+            got = fn(buf[offset:offset + n])
+            torch.cuda.synchronize()
+            S, A = ofn(bits)
+            assert oracle.sum_within_tolerance(got.item(), S, A), (dtype, n, offset, got.item(), S)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_sum_half_exact_and_policies(dtype):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    fn = rl.red_sum_bf16_f32 if dtype == "bf16" else rl.red_sum_f16_f32
+    n = (1 << 22) + 13
+    ints = (np.arange(n) % 7).astype(np.float32)         # exact in both formats
+    t = torch.from_numpy(ints).to(tdt).to(DEV)
+    want = float(sum((i % 7) for i in range(7)) * (n // 7) + sum(range(n % 7)))
+    say(f"sum {dtype} mod7 exact")
+    assert fn(t).item() == want
+    for p in all_flat_policies(bpcs=(1,)):
+        if p["nontemporal"] == 0 or p["combine"] == 0:
+            continue
+        say(f"sum {dtype} policy {p}")
+        assert fn(t[1:], policy=p).item() == want - 0.0, p
+
+
+def test_sum_f64():
+    rng = np.random.default_rng(900)
+    for n in RAGGED:
+        for offset in (0, 1):
+            say(f"sum f64 n={n} offset={offset}")
+            a = rng.standard_normal(n) * 10.0 ** rng.uniform(-5, 5, n)
+            buf = torch.full((n + offset + 4,), float("nan"), dtype=torch.float64, device=DEV)
+            buf[offset:offset + n] = torch.from_numpy(a).to(DEV)
+            got = rl.red_sum_f64(buf[offset:offset + n]).item()
+            S, A = oracle.sum_f64(a)
+            assert abs(got - S) <= 1e-12 * A + 1e-300, (n, offset, got, S)
+    x = torch.arange(1 << 24, dtype=torch.float64, device=DEV)
+    say("sum f64 arange 2^24")
+    assert rl.red_sum_f64(x).item() == (1 << 24) * ((1 << 24) - 1) / 2
+
+
 # ----------------------------------------------------------------- rows
 
 ROW_SHAPES = [(1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
@@ -643,6 +810,18 @@ def test_full_sum_max_f32_fused_2p28():
     say("red_sum_max_f32 sum_max_f32_2p28")
     got = rl.red_sum_max_f32(x).cpu().numpy()
     assert_fused_ok(got, a)
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_min_argmax_2p28():
+    a, x = _load("sum_max_f32_2p28")
+    say("red_min_f32 / red_argmax_f32 / red_argmin_f32 sum_max_f32_2p28")
+    mn, am, ai = rl.red_min_f32(x), rl.red_argmax_f32(x), rl.red_argmin_f32(x)
+    torch.cuda.synchronize()
+    assert mn.item() == float(oracle.min_f32(a))
+    assert int(am.item()) == oracle.argmax_f32(a)
+    assert int(ai.item()) == oracle.argmin_f32(a)
     del x
     torch.cuda.empty_cache()
 
