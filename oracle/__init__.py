@@ -52,6 +52,8 @@ class Oracle:
         lib.oracle_argmin_f32.restype = ctypes.c_int64
         lib.oracle_sum_f64.argtypes = [P, Z, D, D]
         lib.oracle_sum_f64.restype = None
+        lib.oracle_sum_f32_mt.argtypes = [P, Z, ctypes.c_int, D, D]
+        lib.oracle_sum_f32_mt.restype = ctypes.c_int
         self.lib = lib
         self.path = libpath
 
@@ -61,6 +63,16 @@ class Oracle:
         s = ctypes.c_double()
         ab = ctypes.c_double()
         self.lib.oracle_sum_f32(a.ctypes.data, a.size, ctypes.byref(s), ctypes.byref(ab))
+        return s.value, ab.value
+
+    def sum_f32_mt(self, x, threads=None):
+        """(S, A) like sum_f32, computed in `threads` contiguous chunks on as
+        many host threads (default: all CPUs), chunk results added in order."""
+        a = _as(x, np.float32).ravel()
+        t = os.cpu_count() or 1 if threads is None else int(threads)
+        s = ctypes.c_double()
+        ab = ctypes.c_double()
+        self.lib.oracle_sum_f32_mt(a.ctypes.data, a.size, t, ctypes.byref(s), ctypes.byref(ab))
         return s.value, ab.value
 
     def sum_i32_i64(self, x):
@@ -155,6 +167,10 @@ def default():
 
 def sum_f32(x):
     return default().sum_f32(x)
+
+
+def sum_f32_mt(x, threads=None):
+    return default().sum_f32_mt(x, threads)
 
 
 def sum_i32_i64(x):

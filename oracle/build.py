@@ -12,13 +12,13 @@ SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
-          "-ffp-contract=off", "-Wall", "-Wextra", "-Werror"]
+          "-ffp-contract=off", "-pthread", "-Wall", "-Wextra", "-Werror"]
 
 
 def build(src=SRC, out=LIB, extra=()):
     """Compile `src` to the shared library `out`; return `out`."""
     tmp = out + ".tmp"
-    cmd = ["gcc", *CFLAGS, *extra, src, "-o", tmp, "-lm"]
+    cmd = ["gcc", *CFLAGS, *extra, src, "-o", tmp, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

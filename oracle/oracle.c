@@ -5,8 +5,10 @@
  * benchmark's CPU-baseline leg may load this code. The GPU library does not
  * include, link or call it, and it shares no source with the GPU library.
  *
- * It is plain, slow and single-threaded on purpose. Each function states the
- * definition it computes and the passage of the pages it follows:
+ * It is plain and slow on purpose (single-threaded, except for one
+ * chunked form of the float sum that splits the same computation over host
+ * threads). Each function states the definition it computes and the passage
+ * of the pages it follows:
  *
  *   [lesson] "03_shared_memory_sync_reduction.py -- shared memory, banks,
  *            synchronisation and parallel reduction" (CS349E prereq P2),
@@ -22,6 +24,7 @@
  * let the compiler delete the compensation term of the compensated sum).
  */
 #include <math.h>
+#include <pthread.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -58,21 +61,26 @@ static void nm_init(neumaier_t *st)
     st->saw_nan = st->saw_pinf = st->saw_ninf = 0;
 }
 
+/* One compensated addition of a finite v to (s, c). */
+static void nm_step(neumaier_t *st, double v)
+{
+    double t = st->s + v;
+    if (fabs(st->s) >= fabs(v))
+        st->c += (st->s - t) + v;   /* v's low bits were lost */
+    else
+        st->c += (v - t) + st->s;   /* s's low bits were lost */
+    st->s = t;
+}
+
 static void nm_add(neumaier_t *st, double v)
 {
-    double t;
     if (isnan(v)) { st->saw_nan = 1; return; }
     if (isinf(v)) {
         if (v > 0) st->saw_pinf = 1; else st->saw_ninf = 1;
         return;
     }
     st->a += fabs(v);
-    t = st->s + v;
-    if (fabs(st->s) >= fabs(v))
-        st->c += (st->s - t) + v;   /* v's low bits were lost */
-    else
-        st->c += (v - t) + st->s;   /* s's low bits were lost */
-    st->s = t;
+    nm_step(st, v);
 }
 
 static void nm_result(const neumaier_t *st, double *sum, double *abs_sum)
@@ -97,6 +105,63 @@ static void neumaier_f32(const float *x, size_t n, double *sum, double *abs_sum)
 void oracle_sum_f32(const float *x, size_t n, double *sum, double *abs_sum)
 {
     neumaier_f32(x, n, sum, abs_sum);
+}
+
+/*
+ * The same sum on several host threads. x is cut into `threads` contiguous
+ * chunks, chunk k being x[floor(k*n/T) .. floor((k+1)*n/T)); each thread runs
+ * the compensated summation above over its chunk, and the chunks' running
+ * sums and corrections are then added in chunk order with the same
+ * compensated step (sum|x| and the non-finite flags are simply combined).
+ * The result depends only on n and T, not on thread timing, and its error is
+ * of the same order as the single-threaded form's. threads < 1 means 1;
+ * more than 256 are capped at 256.
+ */
+typedef struct {
+    const float *x;
+    size_t n;
+    neumaier_t st;
+} nm_chunk_t;
+
+static void *nm_chunk_run(void *arg)
+{
+    nm_chunk_t *ch = (nm_chunk_t *)arg;
+    size_t i;
+    nm_init(&ch->st);
+    for (i = 0; i < ch->n; ++i)
+        nm_add(&ch->st, (double)ch->x[i]);
+    return NULL;
+}
+
+int oracle_sum_f32_mt(const float *x, size_t n, int threads, double *sum, double *abs_sum)
+{
+    nm_chunk_t ch[256];
+    pthread_t tid[256];
+    int started[256];
+    neumaier_t tot;
+    int T, k;
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    T = threads;
+    for (k = 0; k < T; ++k) {
+        size_t lo = (size_t)k * n / (size_t)T, hi = (size_t)(k + 1) * n / (size_t)T;
+        ch[k].x = x + lo;
+        ch[k].n = hi - lo;
+        started[k] = pthread_create(&tid[k], NULL, nm_chunk_run, &ch[k]) == 0;
+        if (!started[k]) nm_chunk_run(&ch[k]);   /* no thread: run it here */
+    }
+    nm_init(&tot);
+    for (k = 0; k < T; ++k) {
+        if (started[k]) pthread_join(tid[k], NULL);
+        tot.saw_nan |= ch[k].st.saw_nan;
+        tot.saw_pinf |= ch[k].st.saw_pinf;
+        tot.saw_ninf |= ch[k].st.saw_ninf;
+        tot.a += ch[k].st.a;
+        nm_step(&tot, ch[k].st.s);
+        nm_step(&tot, ch[k].st.c);
+    }
+    nm_result(&tot, sum, abs_sum);
+    return T;
 }
 
 /*

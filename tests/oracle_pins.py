@@ -125,6 +125,54 @@ def pin_sum_nonfinite(o):
     assert o.sum_f32(np.array([inf, -2.0, 3.0], np.float32))[1] == 5.0
 
 
+MT_THREADS = (1, 2, 3, 8, 64)
+
+
+def pin_sum_mt_closed_form(o):
+    # The chunked form on several thread counts, including more threads than
+    # elements (empty chunks): sum i = n(n-1)/2, exactly.
+    for T in MT_THREADS:
+        for n in LENGTHS:
+            S, A = o.sum_f32_mt(np.arange(n, dtype=np.float32), T)
+            assert S == n * (n - 1) // 2 and A == S, (T, n, S, A)
+
+
+def pin_sum_mt_matches_fsum(o):
+    # Each chunk keeps its (sum, correction) pair, accurate to second order,
+    # and the pairs are added with the same compensated step, so the bound of
+    # pin_sum_matches_fsum holds for every thread count; the single-threaded
+    # and chunked results then also agree within 1e-15 * sum|x|.
+    global _RANDOM_SETS
+    if _RANDOM_SETS is None:
+        _RANDOM_SETS = _random_sets()
+    for x in _RANDOM_SETS:
+        want = _fsum(x)
+        A_want = _fsum(np.abs(x))
+        S1, _ = o.sum_f32(x)
+        for T in MT_THREADS:
+            S, A = o.sum_f32_mt(x, T)
+            bound = 2 * U * abs(want) + 4 * x.size * U * U * A_want
+            assert abs(S - want) <= bound, (T, x.size, S, want, bound)
+            assert abs(A - A_want) <= x.size * U * A_want, (T, x.size, A, A_want)
+            assert abs(S - S1) <= 1e-15 * A_want, (T, x.size, S, S1)
+
+
+def pin_sum_mt_nonfinite(o):
+    nan, inf = float("nan"), float("inf")
+    n = 1000
+    for T in (2, 8):
+        x = np.ones(n, np.float32)
+        x[700] = nan                                   # in a late chunk
+        assert math.isnan(o.sum_f32_mt(x, T)[0])
+        x = np.ones(n, np.float32)
+        x[10], x[990] = inf, -inf                      # opposite signs, different chunks
+        assert math.isnan(o.sum_f32_mt(x, T)[0])
+        x = np.ones(n, np.float32)
+        x[990] = -inf
+        S, A = o.sum_f32_mt(x, T)
+        assert S == -inf and A == n - 1, (S, A)
+
+
 def pin_sum_empty(o):
     assert o.sum_f32(np.zeros(0, np.float32)) == (0.0, 0.0)
 

@@ -31,6 +31,10 @@ MUTATIONS = {
     "min_starts_at_zero": ("float m = INFINITY;", "float m = 0.0f;"),
     "argmax_last_of_ties": ("(sign > 0 ? x[i] > m : x[i] < m)", "(sign > 0 ? x[i] >= m : x[i] <= m)"),
     "argext_nan_not_skipped": ("        if (isnan(x[i])) continue;\n", ""),
+    "mt_chunk_skips_first": ("for (i = 0; i < ch->n; ++i)", "for (i = 1; i < ch->n; ++i)"),
+    "mt_drops_corrections": ("        nm_step(&tot, ch[k].st.c);\n", ""),
+    "mt_loses_nan": ("        tot.saw_nan |= ch[k].st.saw_nan;\n", ""),
+    "mt_loses_abs": ("        tot.a += ch[k].st.a;\n", "        tot.a = ch[k].st.a;\n"),
     "rows_wrong_stride": ("neumaier_f32(x + r * cols, cols,", "neumaier_f32(x + r, cols,"),
     "rows_max_drops_last_col": ("out[r] = oracle_max_f32(x + r * cols, cols);",
                                 "out[r] = oracle_max_f32(x + r * cols, cols - (cols > 0));"),
