@@ -26,9 +26,11 @@ sys.path.insert(0, ROOT)
 PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "achieved HBM GB/s (% of MI355X peak) for f32 sum over 2^28 elements"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CPU_THREADS_MAX = 16          # the host CPU share that goes with one GPU
 KERNEL_SOURCES = ["reduction_libred_amd/csrc/flat_reduce.hpp",
                   "reduction_libred_amd/csrc/flat_sum_f32.hip",
-                  "reduction_libred_amd/csrc/device_common.hpp"]
+                  "reduction_libred_amd/csrc/device_common.hpp",
+                  "reduction_libred_amd/csrc/launch.hpp"]
 
 
 def log(msg):
@@ -408,22 +410,34 @@ def main():
     if args.cpu_seconds > 0:
         import oracle
 
-        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        passes = 0
-        t0 = time.perf_counter()
-        while True:
-            oracle.sum_f32(a)
-            passes += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
+        def time_oracle(fn, budget):
+            passes, t0 = 0, time.perf_counter()
+            while True:
+                fn(a)
+                passes += 1
+                el = time.perf_counter() - t0
+                if el >= budget:
+                    return passes, el
+
+        threads = max(1, min(len(os.sched_getaffinity(0)), CPU_THREADS_MAX))
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s: {threads} threads, then 1)")
+        p_mt, el_mt = time_oracle(lambda v: oracle.sum_f32_mt(v, threads), args.cpu_seconds / 2)
+        p_st, el_st = time_oracle(oracle.sum_f32, args.cpu_seconds / 2)
         result["cpu_baseline"] = {
-            "value": round(gbps(nbytes * passes, el * 1e3), 3),
+            "value": round(gbps(nbytes * p_mt, el_mt * 1e3), 3),
             "unit": "GB/s",
-            "cores": 1,
+            "cores": threads,
             "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the single-threaded oracle (float64 Neumaier sum) "
-                      f"over the same 2^28-element host array, {el:.1f} s",
+            "sample": f"{p_mt} full pass(es) of the oracle's chunked float64 Neumaier sum on {threads} host "
+                      f"threads over the same 2^28-element host array, {el_mt:.1f} s",
+            "elements_per_s": round(n * p_mt / el_mt, 1),
+            "single_thread": {
+                "value": round(gbps(nbytes * p_st, el_st * 1e3), 3),
+                "unit": "GB/s",
+                "cores": 1,
+                "sample": f"{p_st} full pass(es) of the single-threaded oracle, {el_st:.1f} s",
+                "elements_per_s": round(n * p_st / el_st, 1),
+            },
             "host_cpu": _cpu_model(),
             "host_threads": os.cpu_count(),
         }

@@ -107,10 +107,14 @@ red_status red_argmin_f32(const float *x, size_t n, int64_t *out, hipStream_t st
 
 /*
  * Sum of n 16-bit floats given as their bit patterns (2-byte aligned), into
- * one float32: each element is widened exactly (bfloat16: the upper half of a
- * float32; IEEE half: the binary16 value), accumulated in float64 and rounded
- * once. Eight elements arrive per 16-byte load. NaN/inf and n == 0 as for
- * red_sum_f32.
+ * one float32. Each element is widened exactly (bfloat16: the upper half of a
+ * float32; IEEE half: the binary16 value); eight elements arrive per 16-byte
+ * load. bfloat16 values are accumulated in float64 one by one (their range is
+ * float32's, so a float32 partial could overflow). IEEE half values are first
+ * added eight at a time in float32 (at most three roundings on any path, each
+ * within 2^-24 of the magnitudes added; eight halves cannot overflow), then in
+ * float64. Both round once to float32 at the end, far inside
+ * |error| <= 1e-5 * sum|x|. NaN/inf and n == 0 as for red_sum_f32.
  */
 red_status red_sum_bf16_f32(const uint16_t *x, size_t n, float *out, hipStream_t stream);
 red_status red_sum_f16_f32(const uint16_t *x, size_t n, float *out, hipStream_t stream);

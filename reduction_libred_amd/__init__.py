@@ -247,7 +247,7 @@ def red_sum_bf16_f32(x, out=None, stream=None, policy=None):
 
 
 def red_sum_f16_f32(x, out=None, stream=None, policy=None):
-    """Sum of a float16 tensor into a 0-d float32 tensor (float64 inside)."""
+    """Sum of a float16 tensor into a 0-d float32 tensor (float32 per 16-byte load, then float64)."""
     return _flat("red_sum_f16_f32", "red_sum_f16_f32", _bits16(x, torch.float16, "red_sum_f16_f32"), out,
                  torch.int16, torch.float32, stream, policy)
 

@@ -1,6 +1,7 @@
 // flat_argmax.hip -- index of the max (lowest index of equal maxima; NaN
 // never wins).
 #include "flat_reduce.hpp"
+#include "ops_ext.hpp"
 
 namespace libred {
 

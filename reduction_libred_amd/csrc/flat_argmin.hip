@@ -1,6 +1,7 @@
 // flat_argmin.hip -- index of the min (lowest index of equal minima; NaN
 // never wins).
 #include "flat_reduce.hpp"
+#include "ops_ext.hpp"
 
 namespace libred {
 

@@ -1,6 +1,7 @@
 // flat_fused.hip -- the one-pass sum / max / sum-of-magnitudes, and the xor
 // read probe.
 #include "flat_reduce.hpp"
+#include "ops_ext.hpp"
 
 namespace libred {
 

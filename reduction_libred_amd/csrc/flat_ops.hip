@@ -1,5 +1,6 @@
 // flat_ops.hip -- the int32 -> int64 sum, the float32 max and min.
 #include "flat_reduce.hpp"
+#include "ops_ext.hpp"
 
 namespace libred {
 

@@ -160,7 +160,7 @@ __global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
         body_wave_tiles<Op, BLOCK, UNROLL, NT, PREFETCH>(xv, nvec, head, acc);
 
     // An operator that deferred part of its fold finishes it here.
-    if constexpr (HasTileFold<Op>::value) Op::template resolve<UNROLL, NT>(acc, x);
+    if constexpr (HasResolve<Op>::value) Op::template resolve<UNROLL, NT>(acc, x);
 
     // Step 2: head and tail.
     if (blockIdx.x == 0) {
@@ -211,18 +211,31 @@ __global__ __launch_bounds__(BLOCK) void flat_reduce_kernel(
     }
 }
 
-// Step 6 as a second launch: one block combines np partials in index order.
-constexpr int kCombineBlock = 256;
+// Step 6 as a second launch: one wave combines the np partials in a fixed
+// order. Lane l takes partials l, l + 64, l + 128, ... with eight loads in
+// flight at a time (one memory latency for up to 512 partials), then the wave
+// reduce combines the lanes. No LDS and no barrier.
+constexpr int kCombineBlock = kWave;
+constexpr int kCombineBatch = 8;
 
 template <class Op>
 __global__ __launch_bounds__(kCombineBlock) void combine_partials_kernel(
     const typename Op::acc_t* __restrict__ partials, unsigned int np, typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
-    __shared__ acc_t lds[kCombineBlock / kWave];
+    const unsigned int lane = threadIdx.x;
     acc_t w = Op::identity();
-    for (unsigned int j = threadIdx.x; j < np; j += kCombineBlock) w = Op::combine(w, partials[j]);
-    w = block_reduce<Op, kCombineBlock>(w, lds);
-    if (threadIdx.x == 0) out[0] = Op::finish(w);
+    for (unsigned int j0 = 0; j0 < np; j0 += kWave * kCombineBatch) {
+        acc_t v[kCombineBatch];
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) {
+            const unsigned int j = j0 + k * kWave + lane;
+            v[k] = j < np ? partials[j] : Op::identity();
+        }
+#pragma unroll
+        for (int k = 0; k < kCombineBatch; ++k) w = Op::combine(w, v[k]);
+    }
+    w = wave_reduce<Op>(w);
+    if (lane == 0) out[0] = Op::finish(w);
 }
 
 // ---------------------------------------------------------------------------

@@ -2,6 +2,7 @@
 // load, widened exactly, accumulated in float64, rounded once to float32) and
 // of float64 inputs (two per load).
 #include "flat_reduce.hpp"
+#include "ops_ext.hpp"
 
 namespace libred {
 

@@ -469,6 +469,39 @@ def test_sum_half_exact_and_policies(dtype):
         assert fn(t[1:], policy=p).item() == want - 0.0, p
 
 
+def test_sum_f16_vector_fold():
+    """IEEE half sums add each 16-byte load's eight values in float32 before
+    float64: denormal halves, the largest half beside tiny ones in one load,
+    cancellation inside a load, and infinities and NaN inside a load."""
+    rng = np.random.default_rng(810)
+    n = (1 << 20) + 5
+    cases = {}
+    cases["denormal"] = (rng.integers(1, 1024, n).astype(np.uint16))            # all subnormal halves
+    big = np.full(n, 0x0001, np.uint16)                                         # 2^-24 everywhere
+    big[::8] = 0x7BFF                                                           # 65504 once per load
+    cases["wide_range"] = big
+    c = rng.standard_normal(n).astype(np.float16)
+    c[1::2] = -c[0::2][: c[1::2].size]                                          # x, -x pairs
+    cases["cancel"] = c.view(np.uint16)
+    d = rng.standard_normal(n).astype(np.float16).view(np.uint16)
+    d[[17, 40_000]] = 0x7C00                                                    # +inf
+    cases["inf"] = d.copy()
+    d[[18]] = 0xFC00                                                            # and -inf: NaN
+    cases["inf_minus_inf"] = d.copy()
+    e = rng.standard_normal(n).astype(np.float16).view(np.uint16)
+    e[[99_999]] = 0x7E00                                                        # NaN
+    cases["nan"] = e
+    for name, bits in cases.items():
+        for offset in (0, 3):
+            say(f"sum f16 case {name} offset={offset}")
+            t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.float16)
+            buf = torch.zeros(n + offset + 8, dtype=torch.float16, device=DEV)
+            buf[offset:offset + n] = t.to(DEV)
+            got = rl.red_sum_f16_f32(buf[offset:offset + n]).item()
+            S, A = oracle.sum_f16(bits)
+            assert oracle.sum_within_tolerance(got, S, A), (name, offset, got, S, A)
+
+
 def test_sum_f64():
     rng = np.random.default_rng(900)
     for n in RAGGED:
