@@ -126,10 +126,12 @@ typedef struct {
 static void *nm_chunk_run(void *arg)
 {
     nm_chunk_t *ch = (nm_chunk_t *)arg;
+    neumaier_t st;   /* thread-local: the chunk records sit side by side */
     size_t i;
-    nm_init(&ch->st);
+    nm_init(&st);
     for (i = 0; i < ch->n; ++i)
-        nm_add(&ch->st, (double)ch->x[i]);
+        nm_add(&st, (double)ch->x[i]);
+    ch->st = st;
     return NULL;
 }
 
