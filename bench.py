@@ -27,36 +27,38 @@ PEAK_GBPS = 8000.0          # MI355X HBM3E peak, 8 TB/s
 METRIC = "achieved HBM GB/s (% of MI355X peak) for f32 sum over 2^28 elements"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CPU_THREADS_MAX = 16          # the host CPU share that goes with one GPU
-KERNEL_SOURCES = ["reduction_libred_amd/csrc/flat_reduce.hpp",
-                  "reduction_libred_amd/csrc/flat_sum_f32.hip",
-                  "reduction_libred_amd/csrc/device_common.hpp",
-                  "reduction_libred_amd/csrc/launch.hpp"]
+OBJECT_MANIFEST = os.path.join(ROOT, "reduction_libred_amd", "libred_objects.json")
+KERNEL_UNIT = "flat_sum_f32.hip"  # the translation unit of the f32 sum kernel
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(policy):
-    """Identity of the streaming kernel as launched: its device sources and
-    the launch shape."""
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as fh:
-            h.update(fh.read())
+def kernel_identity(policy):
+    """Identity of the streaming kernel as launched: the hash of its compiled
+    object (from the build's manifest) and the launch shape; None when the
+    manifest is missing."""
+    try:
+        with open(OBJECT_MANIFEST) as fh:
+            digest = json.load(fh)[KERNEL_UNIT]
+    except (OSError, ValueError, KeyError):
+        return None
+    h = hashlib.sha256(digest.encode())
     h.update(json.dumps(policy, sort_keys=True).encode())
     return h.hexdigest()
 
 
 def recorded_traffic(policy):
     """HBM bytes per launch of the sum kernel from the committed counter
-    runs, or None if the kernel or its launch shape changed since then."""
+    runs, or None if the kernel's code or its launch shape changed since."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_hash(policy):
+    ident = kernel_identity(policy)
+    if ident is None or rec.get("kernel_identity") != ident:
         return None
     return rec.get("flat_reduce_kernel_sum_f32_2p28_bytes_per_launch")
 

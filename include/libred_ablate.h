@@ -83,16 +83,25 @@ typedef struct red_rows_policy {
 
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,
  * 4, 8 or 16), `nontemporal`, `target_waves` (the rows are cut into chunks
- * until about this many single-wave blocks run), and `vec`: 0 = four
- * adjacent columns per lane when x is 16-byte aligned and cols and ld are
- * multiples of 4, else one; 1 = always one; 4 = same as 0. */
+ * until about this many single-wave blocks run), `vec`: 0 = four adjacent
+ * columns per lane when x is 16-byte aligned and cols and ld are multiples
+ * of 4, else one; 1 = always one; 4 = same as 0; and `width` (1, 2 or 4):
+ * with four columns per lane and at least 64 column groups, each row is read
+ * by `width` loads per lane, so a wave reads width KiB of a row at once
+ * (otherwise 1 is used); `prefetch` (0 or 1): issue the next group of
+ * `unroll` rows before adding the current one. */
 typedef struct red_cols_policy {
     int unroll;
     int nontemporal;
     int target_waves;
     int vec;
+    int width;
+    int prefetch;
 } red_cols_policy;
 
+/* The default column shape. A call without a policy uses it, except on
+ * short-wide matrices (four columns per lane and cols / 256 >= 1024), which
+ * use unroll 2, width 4, no prefetch and target_waves 1024. */
 void red_default_cols_policy(red_cols_policy *p);
 red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_cols_policy *p, hipStream_t stream);

@@ -7,6 +7,8 @@ FP32 instructions disabled, then linked into reduction_libred_amd/libred.so,
 which exports only the red_* symbols declared in include/*.h.
 """
 import concurrent.futures as cf
+import hashlib
+import json
 import os
 import shutil
 import subprocess
@@ -18,6 +20,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libred.so")
+# sha256 of each compiled object, written beside the library: it identifies
+# the machine code a measurement was taken on (the objects are reproducible,
+# and an edit that leaves a unit's code unchanged leaves its hash unchanged).
+MANIFEST = os.path.join(HERE, "libred_objects.json")
 
 SOURCES = ["libred.cpp", "flat_sum_f32.hip", "flat_ops.hip", "flat_fused.hip", "flat_argmax.hip", "flat_argmin.hip",
            "flat_wide.hip", "rows_reduce.hip", "cols_reduce.hip", "ablate.hip", "probe.hip"]
@@ -67,6 +73,12 @@ def build(verbose=True):
            f"-Wl,--version-script={os.path.join(CSRC, 'libred.map')}", "-Wl,-soname,libred.so"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    digests = {}
+    for src, obj in zip(SOURCES, objs):
+        with open(obj, "rb") as fh:
+            digests[src] = hashlib.sha256(fh.read()).hexdigest()
+    with open(MANIFEST, "w") as fh:
+        json.dump(digests, fh, indent=1, sort_keys=True)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)
     return LIB

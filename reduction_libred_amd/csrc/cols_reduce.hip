@@ -40,12 +40,16 @@ __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typenam
 
 // Block b: column block j = b % ncb, row chunk k = b / ncb. A wave covers
 // `ngroups` column groups of VEC columns per load: normally ngroups == 64
-// (one group per lane, 64*VEC columns per block); for narrow matrices
+// (one group per lane), and each row is read with CW loads that cover
+// CW * 64 * VEC adjacent columns (CW KiB when VEC == 4), lane l taking
+// columns l*VEC + w*64*VEC for w < CW. For narrow matrices (CW == 1 only)
 // ngroups divides 64 and the wave's lanes cover 64 / ngroups rows per load
-// (lane l: group l % ngroups, row offset l / ngroups), and lanes of one group
-// are added with shuffles at the end. With VEC == 4, cols and ld are
-// multiples of 4 and x is 16-byte aligned.
-template <class Op, int VEC, int UNROLL, bool NT>
+// (lane l: group l % ngroups, row offset l / ngroups); lanes of one group are
+// added with shuffles at the end. With VEC == 4, cols and ld are multiples of
+// 4 and x is 16-byte aligned. In the last column block a lane whose column
+// w lies past the end reads its column-0 vector again instead (so every load
+// stays in bounds and no load is predicated) and never stores that result.
+template <class Op, int VEC, int CW, int UNROLL, bool NT, bool PREFETCH>
 __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::elem_t* __restrict__ x,
                                                              size_t rows, size_t cols, size_t ld,
                                                              size_t rchunk, size_t ncb, unsigned int ngroups,
@@ -59,38 +63,89 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
     const unsigned int g = lane % ngroups;
     const size_t rpl = kWave / ngroups;  // rows per load
     const size_t q = lane / ngroups;
-    const size_t c0 = (j * ngroups + g) * VEC;
+    const size_t span = (size_t)ngroups * VEC;  // columns per load
+    const size_t c0 = j * span * CW + (size_t)g * VEC;
     const size_t r0 = k * rchunk;
     const size_t r1 = r0 + rchunk < rows ? r0 + rchunk : rows;
-    acc_t acc[VEC];
+    acc_t acc[CW][VEC];
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) acc[i] = Op::identity();
+    for (int w = 0; w < CW; ++w)
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[w][i] = Op::identity();
     if (c0 < cols) {
+        size_t off[CW];  // in V units from the lane's column-0 vector
+#pragma unroll
+        for (int w = 0; w < CW; ++w) off[w] = c0 + w * span < cols ? w * (size_t)ngroups : 0;
         const size_t step = ld / VEC * rpl;  // in V units, between a lane's rows
+        constexpr size_t U = UNROLL;
         size_t r = r0 + q;
         const V* __restrict__ p = reinterpret_cast<const V*>(x + r * ld + c0);
-        for (; r + (UNROLL - 1) * rpl < r1; r += UNROLL * rpl, p += UNROLL * step) {
-            V v[UNROLL];
+        // Groups of UNROLL rows. With PREFETCH, two register buffers
+        // alternate: the next group's loads are issued before the current
+        // group is folded, so a wave keeps two groups in flight.
+        auto load_group = [&](V (&v)[UNROLL][CW], const V* __restrict__ g) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * step);
+            for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) col_fold<Op, VEC>(acc, v[u]);
+                for (int w = 0; w < CW; ++w) v[u][w] = load_vec<NT>(g + u * step + off[w]);
+        };
+        auto fold_group = [&](const V (&v)[UNROLL][CW]) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+                for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], v[u][w]);
+        };
+        if (!PREFETCH) {
+            for (; r + (U - 1) * rpl < r1; r += U * rpl, p += U * step) {
+                V v[UNROLL][CW];
+                load_group(v, p);
+                fold_group(v);
+            }
+        } else if (r + (U - 1) * rpl < r1) {
+            V a[UNROLL][CW], b[UNROLL][CW];
+            load_group(a, p);
+            while (true) {
+                if (r + (2 * U - 1) * rpl >= r1) {
+                    fold_group(a);
+                    r += U * rpl, p += U * step;
+                    break;
+                }
+                load_group(b, p + U * step);
+                fold_group(a);
+                r += U * rpl, p += U * step;
+                if (r + (2 * U - 1) * rpl >= r1) {
+                    fold_group(b);
+                    r += U * rpl, p += U * step;
+                    break;
+                }
+                load_group(a, p + U * step);
+                fold_group(b);
+                r += U * rpl, p += U * step;
+            }
         }
-        for (; r < r1; r += rpl, p += step) col_fold<Op, VEC>(acc, load_vec<NT>(p));
-    }
-    // Packed rows: lane g collects lanes g + ngroups, g + 2*ngroups, ... in a
-    // fixed order (all lanes take part in the shuffles).
-    for (unsigned int off = kWave / 2; off >= ngroups; off >>= 1) {
+        for (; r < r1; r += rpl, p += step) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[i] = Op::combine(acc[i], __shfl_down(acc[i], off, kWave));
+            for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], load_vec<NT>(p + off[w]));
+        }
     }
-    if (q == 0 && c0 < cols) {
+    // Packed rows (CW == 1): lane g collects lanes g + ngroups, g + 2*ngroups,
+    // ... in a fixed order (all lanes take part in the shuffles).
+    for (unsigned int sh = kWave / 2; sh >= ngroups; sh >>= 1) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            if (out != nullptr)
-                out[c0 + i] = Op::finish(acc[i]);
-            else
-                partials[k * cols + c0 + i] = acc[i];
+        for (int i = 0; i < VEC; ++i) acc[0][i] = Op::combine(acc[0][i], __shfl_down(acc[0][i], sh, kWave));
+    }
+    if (q == 0) {
+#pragma unroll
+        for (int w = 0; w < CW; ++w) {
+            const size_t c = c0 + w * span;
+            if (c >= cols) continue;
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                if (out != nullptr)
+                    out[c + i] = Op::finish(acc[w][i]);
+                else
+                    partials[k * cols + c + i] = acc[w][i];
+            }
         }
     }
 }
@@ -115,23 +170,25 @@ __global__ __launch_bounds__(kColsCombineBlock) void cols_combine_kernel(
 
 bool cols_policy_supported(const ColsPolicy& p) {
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
-    return u && (p.nontemporal == 0 || p.nontemporal == 1) && p.target_waves >= 1 &&
+    const bool w = p.width == 1 || p.width == 2 || p.width == 4;
+    return u && w && (p.nontemporal == 0 || p.nontemporal == 1) && (p.prefetch == 0 || p.prefetch == 1) &&
+           p.target_waves >= 1 &&
            (p.vec == 0 || p.vec == 1 || p.vec == 4);
 }
 
-template <class Op, int VEC, int UNROLL>
-static hipError_t cols_vu(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
-                          typename Op::out_t* out, const ColsLaunch& L, bool nt, hipStream_t stream) {
+template <class Op, int VEC, int CW, int UNROLL, bool PF>
+static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+                            typename Op::out_t* out, const ColsLaunch& L, bool nt, hipStream_t stream) {
     auto* partials = static_cast<typename Op::acc_t*>(L.partials);
     const size_t rchunk = (rows + L.nchunks - 1) / L.nchunks;
     const dim3 grid((unsigned int)(L.ncb * L.nchunks));
     typename Op::out_t* direct = L.nchunks == 1 ? out : nullptr;
     if (nt)
-        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, UNROLL, true>), grid, dim3(kWave), 0, stream, x, rows,
-                           cols, ld, rchunk, L.ncb, L.ngroups, partials, direct);
+        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF>), grid, dim3(kWave), 0, stream, x,
+                           rows, cols, ld, rchunk, L.ncb, L.ngroups, partials, direct);
     else
-        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, UNROLL, false>), grid, dim3(kWave), 0, stream, x, rows,
-                           cols, ld, rchunk, L.ncb, L.ngroups, partials, direct);
+        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF>), grid, dim3(kWave), 0, stream, x,
+                           rows, cols, ld, rchunk, L.ncb, L.ngroups, partials, direct);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || L.nchunks == 1) return e;
     const size_t W = kColsCombineBlock / kWave;
@@ -140,16 +197,24 @@ static hipError_t cols_vu(const typename Op::elem_t* x, size_t rows, size_t cols
     return hipGetLastError();
 }
 
-template <class Op, int VEC>
-static hipError_t cols_v(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
-                         typename Op::out_t* out, const ColsLaunch& L, const ColsPolicy& p, hipStream_t stream) {
+template <class Op, int VEC, int CW, int UNROLL>
+static hipError_t cols_vwu(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+                           typename Op::out_t* out, const ColsLaunch& L, bool nt, bool pf, hipStream_t stream) {
+    if (pf) return cols_vwup<Op, VEC, CW, UNROLL, true>(x, rows, cols, ld, out, L, nt, stream);
+    return cols_vwup<Op, VEC, CW, UNROLL, false>(x, rows, cols, ld, out, L, nt, stream);
+}
+
+template <class Op, int VEC, int CW>
+static hipError_t cols_vw(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+                          typename Op::out_t* out, const ColsLaunch& L, const ColsPolicy& p, hipStream_t stream) {
     const bool nt = p.nontemporal != 0;
+    const bool pf = p.prefetch != 0;
     switch (p.unroll) {
-        case 1: return cols_vu<Op, VEC, 1>(x, rows, cols, ld, out, L, nt, stream);
-        case 2: return cols_vu<Op, VEC, 2>(x, rows, cols, ld, out, L, nt, stream);
-        case 4: return cols_vu<Op, VEC, 4>(x, rows, cols, ld, out, L, nt, stream);
-        case 8: return cols_vu<Op, VEC, 8>(x, rows, cols, ld, out, L, nt, stream);
-        case 16: return cols_vu<Op, VEC, 16>(x, rows, cols, ld, out, L, nt, stream);
+        case 1: return cols_vwu<Op, VEC, CW, 1>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 2: return cols_vwu<Op, VEC, CW, 2>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 4: return cols_vwu<Op, VEC, CW, 4>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 8: return cols_vwu<Op, VEC, CW, 8>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 16: return cols_vwu<Op, VEC, CW, 16>(x, rows, cols, ld, out, L, nt, pf, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -157,8 +222,13 @@ static hipError_t cols_v(const typename Op::elem_t* x, size_t rows, size_t cols,
 template <class Op>
 static hipError_t cols_op(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, const ColsLaunch& L, const ColsPolicy& p, hipStream_t stream) {
-    if (L.vec == 4) return cols_v<Op, 4>(x, rows, cols, ld, out, L, p, stream);
-    return cols_v<Op, 1>(x, rows, cols, ld, out, L, p, stream);
+    if (L.vec != 4) return cols_vw<Op, 1, 1>(x, rows, cols, ld, out, L, p, stream);
+    switch (L.width) {
+        case 1: return cols_vw<Op, 4, 1>(x, rows, cols, ld, out, L, p, stream);
+        case 2: return cols_vw<Op, 4, 2>(x, rows, cols, ld, out, L, p, stream);
+        case 4: return cols_vw<Op, 4, 4>(x, rows, cols, ld, out, L, p, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_cols_sum_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,

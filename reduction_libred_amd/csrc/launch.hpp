@@ -70,16 +70,19 @@ struct ColsPolicy {
     int nontemporal;
     int target_waves;
     int vec;
+    int width;
+    int prefetch;
 };
 
-// How one column call launches: ncb column blocks of ngroups*vec columns
-// times nchunks row chunks (ngroups == 64, or a divisor of 64 for a narrow
+// How one column call launches: ncb column blocks of ngroups*vec*width
+// columns times nchunks row chunks (ngroups == 64, or a divisor of 64 for a narrow
 // matrix whose wave then covers 64 / ngroups rows per load); with
 // nchunks > 1, partials (nchunks * cols acc_t) live in `partials`.
 struct ColsLaunch {
     size_t ncb;
     size_t nchunks;
     int vec;
+    int width;
     unsigned int ngroups;
     void* partials;
 };

@@ -587,7 +587,12 @@ def test_rows_split_long_rows(rows, cols):
 
 
 COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260), (4099, 1024, 1024),
-              (33, 1000, 1001), (2, 4096, 4096), (0, 8, 8), (70_000, 12, 12), (5, 100_003, 100_003)]
+              (33, 1000, 1001), (2, 4096, 4096), (0, 8, 8), (70_000, 12, 12), (5, 100_003, 100_003),
+              (301, 1028, 1032), (77, 2304, 2304)]
+COL_POLICIES = (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=16, nontemporal=0),
+                dict(width=2), dict(width=4, unroll=2), dict(width=4, unroll=16, nontemporal=0, target_waves=7),
+                dict(prefetch=1), dict(prefetch=1, unroll=1, target_waves=7), dict(width=4, unroll=2, prefetch=1),
+                dict(width=2, unroll=16, prefetch=1, nontemporal=0))
 
 
 @pytest.mark.parametrize("rows,cols,ld", COL_SHAPES)
@@ -601,7 +606,7 @@ def test_cols(rows, cols, ld):
     S, A = oracle.cols_sum_f32(a)
     M = oracle.cols_max_f32(a)
     for offset in (0, 1):
-        for p in (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=16, nontemporal=0)):
+        for p in COL_POLICIES:
             say(f"cols {rows}x{cols} ld={ld} offset={offset} policy={p}")
             x = device_view(full, offset)[:, :cols]
             s = rl.red_cols_sum_f32(x, policy=p)
