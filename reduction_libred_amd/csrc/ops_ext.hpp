@@ -120,20 +120,46 @@ struct ArgExtF32 {
 using ArgMaxF32 = ArgExtF32<true>;
 using ArgMinF32 = ArgExtF32<false>;
 
-// Sums of 16-bit floats given as bit patterns, widened exactly to float and
-// then to float64; eight elements per 16-byte vector.
+// Sums of 16-bit floats given as bit patterns, widened exactly to float;
+// eight elements per 16-byte vector.
 struct SumBF16 {
     using elem_t = uint16_t;
     using vec_t = u16x8;
     using acc_t = double;
     using out_t = float;
     static constexpr int kPerVec = 8;
-    static __device__ __forceinline__ acc_t identity() { return 0.0; }
-    static __device__ __forceinline__ acc_t lift(elem_t v, size_t) {
-        return (double)__builtin_bit_cast(float, (uint32_t)v << 16);  // bfloat16 = float's upper half
+    static __device__ __forceinline__ float widen(elem_t v) {
+        return __builtin_bit_cast(float, (uint32_t)v << 16);  // bfloat16 = float's upper half
     }
+    static __device__ __forceinline__ acc_t identity() { return 0.0; }
+    static __device__ __forceinline__ acc_t lift(elem_t v, size_t) { return (double)widen(v); }
     static __device__ __forceinline__ acc_t combine(acc_t a, acc_t b) { return a + b; }
     static __device__ __forceinline__ out_t finish(acc_t a) { return (float)a; }
+    // The eight values of a vector are added in float32 as a balanced tree,
+    // each first scaled by 1/8. The scaling is exact for every bfloat16 (its
+    // eight significant bits stay above float32's smallest subnormal, 2^-149,
+    // and float32 subnormals are kept), and it keeps the tree from
+    // overflowing: eight values of at most FLT_MAX / 8 cannot sum past
+    // FLT_MAX. Three roundings at most on any path, each within 2^-24 of the
+    // magnitudes added; the vector total is scaled back by 8 in float64
+    // (exactly). Infinities and NaN propagate as in IEEE arithmetic.
+    static __device__ __forceinline__ float tree8(vec_t v) {
+        constexpr float s = 0.125f;
+        const float s01 = __builtin_fmaf(widen(v[0]), s, widen(v[1]) * s);
+        const float s23 = __builtin_fmaf(widen(v[2]), s, widen(v[3]) * s);
+        const float s45 = __builtin_fmaf(widen(v[4]), s, widen(v[5]) * s);
+        const float s67 = __builtin_fmaf(widen(v[6]), s, widen(v[7]) * s);
+        return (s01 + s23) + (s45 + s67);
+    }
+    static __device__ __forceinline__ void fold(acc_t (&acc)[4], vec_t v, size_t) {
+        acc[0] = __builtin_fma(8.0, (double)tree8(v), acc[0]);
+    }
+    static constexpr bool kTileFold = true;
+    template <int UNROLL>
+    static __device__ __forceinline__ void fold_tile(acc_t (&acc)[4], const vec_t (&v)[UNROLL], size_t) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) acc[u & 3] = __builtin_fma(8.0, (double)tree8(v[u]), acc[u & 3]);
+    }
 };
 // IEEE half: the eight values of a vector are first added in float32 as a
 // balanced tree (three roundings on any path, each at most 2^-24 of the

@@ -502,6 +502,38 @@ def test_sum_f16_vector_fold():
             assert oracle.sum_within_tolerance(got, S, A), (name, offset, got, S, A)
 
 
+def test_sum_bf16_vector_fold():
+    """bfloat16 sums add each load's eight values in float32 and fall back to
+    float64 when that float32 result is not finite: values near the top of
+    the range that cancel (a float32 tree overflows, the exact sum is small),
+    a lone overflow in one load of a tile, infinities and NaN."""
+    rng = np.random.default_rng(820)
+    n = (1 << 20) + 3
+    cases = {}
+    big = np.resize(np.array([0x7F60, 0x7F60, 0xFF60, 0xFF60], np.uint16), n)  # +a +a -a -a, a = 2.97e38
+    cases["huge_cancel"] = big                                                  # exact sum: a (the tail)
+    one = rng.standard_normal(n).astype(np.float32)
+    b = (one.view(np.uint32) >> 16).astype(np.uint16)
+    b[[1000, 1001, 1002, 1003]] = [0x7F60, 0x7F60, 0xFF60, 0xFF60]             # overflow in one load only
+    cases["one_overflow"] = b.copy()
+    b[[5000]] = 0x7F80                                                          # +inf
+    cases["inf"] = b.copy()
+    b[[6000]] = 0xFF80                                                          # and -inf: NaN
+    cases["inf_minus_inf"] = b.copy()
+    c = (one.view(np.uint32) >> 16).astype(np.uint16)
+    c[[77_777]] = 0x7FC0                                                        # NaN
+    cases["nan"] = c
+    for name, bits in cases.items():
+        for offset in (0, 5):
+            say(f"sum bf16 case {name} offset={offset}")
+            t = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+            buf = torch.zeros(n + offset + 8, dtype=torch.bfloat16, device=DEV)
+            buf[offset:offset + n] = t.to(DEV)
+            got = rl.red_sum_bf16_f32(buf[offset:offset + n]).item()
+            S, A = oracle.sum_bf16(bits)
+            assert oracle.sum_within_tolerance(got, S, A), (name, offset, got, S, A)
+
+
 def test_sum_f64():
     rng = np.random.default_rng(900)
     for n in RAGGED:
@@ -742,24 +774,34 @@ def test_shfl_down_primitive_matches_lane_model():
 
 def test_graph_replay_matches_eager():
     # Captured calls (after a first eager call per stream, so the workspace
-    # exists) replay correctly several times with eager work in between.
+    # and the column scratch exist) replay correctly several times with eager
+    # work in between.
     a = W.make("normal", (1 << 22) + 3, 31)
     r = W.make("uniform01", 300 * 1001, 32).reshape(300, 1001)
     x, xr = device_view(a, 1), device_view(r, 2)
-    outs = [torch.empty((), device=DEV), torch.empty((), device=DEV), torch.empty(300, device=DEV)]
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(cap):
+    xh = torch.from_numpy(a).to(DEV).to(torch.float16)
+    outs = [torch.empty((), device=DEV), torch.empty((), device=DEV), torch.empty(300, device=DEV),
+            torch.empty((), dtype=torch.int64, device=DEV), torch.empty((), device=DEV),
+            torch.empty(3, device=DEV), torch.empty(1001, device=DEV)]
+
+    def calls():
         rl.red_sum_f32(x, out=outs[0])
         rl.red_max_f32(x, out=outs[1])
         rl.red_rows_sum_f32(xr, out=outs[2])
+        rl.red_argmax_f32(x, out=outs[3])
+        rl.red_sum_f16_f32(xh, out=outs[4])
+        rl.red_sum_max_f32(x, out=outs[5])
+        rl.red_cols_sum_f32(xr, out=outs[6])
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        calls()
         torch.cuda.synchronize()
         eager = [o.clone() for o in outs]
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            rl.red_sum_f32(x, out=outs[0])
-            rl.red_max_f32(x, out=outs[1])
-            rl.red_rows_sum_f32(xr, out=outs[2])
+            calls()
     torch.cuda.synchronize()
     for k in range(4):
         say(f"graph replay {k}")
