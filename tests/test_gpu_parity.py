@@ -503,10 +503,10 @@ def test_sum_f16_vector_fold():
 
 
 def test_sum_bf16_vector_fold():
-    """bfloat16 sums add each load's eight values in float32 and fall back to
-    float64 when that float32 result is not finite: values near the top of
-    the range that cancel (a float32 tree overflows, the exact sum is small),
-    a lone overflow in one load of a tile, infinities and NaN."""
+    """bfloat16 sums add each load's eight values in float32 after scaling
+    them by 1/8: values near the top of the range that cancel (an unscaled
+    float32 tree would overflow), such values in one load only, subnormal
+    values (the scaling must stay exact), infinities and NaN."""
     rng = np.random.default_rng(820)
     n = (1 << 20) + 3
     cases = {}
@@ -523,6 +523,7 @@ def test_sum_bf16_vector_fold():
     c = (one.view(np.uint32) >> 16).astype(np.uint16)
     c[[77_777]] = 0x7FC0                                                        # NaN
     cases["nan"] = c
+    cases["subnormal"] = rng.integers(1, 128, n).astype(np.uint16)              # all subnormal bfloat16
     for name, bits in cases.items():
         for offset in (0, 5):
             say(f"sum bf16 case {name} offset={offset}")
@@ -532,6 +533,8 @@ def test_sum_bf16_vector_fold():
             got = rl.red_sum_bf16_f32(buf[offset:offset + n]).item()
             S, A = oracle.sum_bf16(bits)
             assert oracle.sum_within_tolerance(got, S, A), (name, offset, got, S, A)
+            if name == "subnormal":   # the absolute 1e-6 would hide any error here
+                assert abs(got - S) <= 1e-5 * A, (offset, got, S, A)
 
 
 def test_sum_f64():
