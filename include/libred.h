@@ -29,6 +29,14 @@
  *    per (device, stream) and kept until the process exits. Calls on one
  *    stream are ordered, so they can share it; calls on different streams use
  *    different workspaces and may run concurrently.
+ *  - Graph capture: the calls can be captured into a HIP graph, provided the
+ *    stream already holds what the call needs. That is its workspace, made by
+ *    any earlier single-value call on the stream (row calls need it only
+ *    when they split long rows). For the column entry points it is also
+ *    scratch at least as large as the call needs, made by an earlier column
+ *    call of the same or a larger shape. Otherwise the
+ *    call returns RED_ERR_CAPTURE before it touches the stream, and the
+ *    capture stays intact.
  *  - Results are deterministic: for a given length and device the partials
  *    are combined in a fixed index order, so repeated calls return the same
  *    bits.
@@ -51,7 +59,9 @@ typedef enum red_status {
     RED_ERR_INVALID_ARG = 1, /* bad pointer, length, shape or alignment */
     RED_ERR_NO_DEVICE = 2,   /* no usable HIP device is current */
     RED_ERR_HIP = 3,         /* a HIP call or kernel launch failed; see red_last_hip_error */
-    RED_ERR_ALLOC = 4        /* the library workspace could not be allocated */
+    RED_ERR_ALLOC = 4,       /* the library workspace could not be allocated */
+    RED_ERR_CAPTURE = 5      /* the stream is being captured into a graph and the call
+                                would first have to allocate its workspace or scratch */
 } red_status;
 
 /* Largest element count accepted by one call (2^40 elements, 4 TiB of float). */

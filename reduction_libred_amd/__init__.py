@@ -24,6 +24,7 @@ RED_ERR_INVALID_ARG = 1
 RED_ERR_NO_DEVICE = 2
 RED_ERR_HIP = 3
 RED_ERR_ALLOC = 4
+RED_ERR_CAPTURE = 5
 RED_MAX_N = 1 << 40
 
 

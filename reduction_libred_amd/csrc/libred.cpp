@@ -114,6 +114,16 @@ red_status current_device(int* dev_out, DeviceInfo* info_out) {
     return RED_OK;
 }
 
+// Allocating while `stream` is being captured into a graph would break the
+// capture (or put a fill kernel into the graph), so a call that needs a new
+// or larger buffer then fails before touching the stream.
+red_status refuse_if_capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return cs == hipStreamCaptureStatusNone ? RED_OK : RED_ERR_CAPTURE;
+}
+
 red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
     std::lock_guard<std::mutex> lock(g_mu);
     const auto key = std::make_pair(dev, stream);
@@ -122,6 +132,8 @@ red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
         *ws = it->second;
         return RED_OK;
     }
+    const red_status cap = refuse_if_capturing(stream);
+    if (cap != RED_OK) return cap;
     void* p = nullptr;
     hipError_t e = hipMalloc(&p, kWorkspaceBytes);
     if (e != hipSuccess || p == nullptr) return fail(e, RED_ERR_ALLOC);
@@ -148,6 +160,8 @@ red_status get_scratch(int dev, hipStream_t stream, size_t bytes, void** out) {
         *out = sc.ptr;
         return RED_OK;
     }
+    const red_status cap = refuse_if_capturing(stream);
+    if (cap != RED_OK) return cap;
     if (sc.ptr != nullptr) {
         hipError_t e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return fail(e, RED_ERR_HIP);
@@ -402,6 +416,8 @@ const char* red_status_string(red_status status) {
         case RED_ERR_NO_DEVICE: return "RED_ERR_NO_DEVICE: no usable HIP device";
         case RED_ERR_HIP: return "RED_ERR_HIP: a HIP call or kernel launch failed";
         case RED_ERR_ALLOC: return "RED_ERR_ALLOC: workspace allocation failed";
+        case RED_ERR_CAPTURE:
+            return "RED_ERR_CAPTURE: the stream is being captured and its workspace is missing or too small";
     }
     return "unknown red_status";
 }

@@ -47,8 +47,8 @@ def test_exports_match_headers():
 
 def test_status_strings_and_version():
     L = rl.lib()
-    for code in range(5):
-        assert L.red_status_string(code)
+    for code in range(6):
+        assert L.red_status_string(code) != b"unknown red_status", code
     assert L.red_status_string(99) == b"unknown red_status"
     assert rl.red_version().startswith("libred")
 

@@ -817,6 +817,54 @@ def test_graph_replay_matches_eager():
             assert torch.equal(o, e)
 
 
+def test_capture_without_workspace_is_refused():
+    # A fresh stream has no workspace yet: a call captured on it must fail
+    # with RED_ERR_CAPTURE before touching the stream, leaving the capture
+    # usable; after one eager call the same capture works.
+    x = device_view(W.make("normal", 1 << 16, 41), 0)
+    out = torch.empty((), device=DEV)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    say("capture on a fresh stream")
+    with torch.cuda.stream(cap):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            with pytest.raises(rl.RedError) as ei:
+                rl.red_sum_f32(x, out=out)
+            out.fill_(1.0)
+        assert ei.value.status == rl.RED_ERR_CAPTURE
+    torch.cuda.synchronize()
+    out.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    assert out.item() == 1.0
+    say("capture after an eager call")
+    with torch.cuda.stream(cap):
+        want = rl.red_sum_f32(x).item()
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2, stream=cap):
+            rl.red_sum_f32(x, out=out)
+    torch.cuda.synchronize()
+    out.zero_()
+    g2.replay()
+    torch.cuda.synchronize()
+    assert out.item() == want
+    say("column call needing more scratch under capture")
+    small = device_view(W.make("normal", 64 * 256, 42).reshape(64, 256), 0)
+    big = device_view(W.make("normal", 4096 * 1024, 43).reshape(4096, 1024), 0)
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        rl.red_cols_sum_f32(small)                 # scratch sized for the small shape
+        torch.cuda.synchronize()
+        g3 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g3, stream=cs):
+            with pytest.raises(rl.RedError) as ei:
+                rl.red_cols_sum_f32(big, policy=dict(target_waves=4096, unroll=1))
+        assert ei.value.status == rl.RED_ERR_CAPTURE
+    torch.cuda.synchronize()
+
+
 def test_lds_stride_probe():
     words = 64 * 65
     for stride in (1, 2, 32, 33, 0, -1, 4095):
