@@ -6,10 +6,11 @@
 // VEC adjacent columns (one 16-byte load when VEC == 4), so a wave covers
 // 64*VEC columns of a row per load (or several short rows at once when the
 // matrix is narrow), and walks down its rows with UNROLL loads in flight. For
-// parallelism when there are few columns, the rows are cut into `nchunks`
-// chunks; pass 1 stores one partial per (chunk, column), and pass 2 adds each
-// column's partials with one wave per column in a fixed order
-// (deterministic). With a single chunk pass 1 stores the result directly.
+// parallelism when there are few columns, the rows are dealt round-robin to
+// `nchunks` row phases; pass 1 stores one partial per (phase, column), and
+// pass 2 adds each column's partials with one wave per column in a fixed
+// order (deterministic). With a single phase pass 1 stores the result
+// directly.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -38,7 +39,12 @@ __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typenam
     }
 }
 
-// Block b: column block j = b % ncb, row chunk k = b / ncb. A wave covers
+// Block b: column block j = b % ncb, row phase k = b / ncb of the
+// K = gridDim.x / ncb phases. Phase k takes rows k, k + K, k + 2K, ... (in
+// groups of 64 / ngroups rows, see below), so the waves of one column block
+// move down the matrix together and the whole grid sweeps it front to back,
+// as the single-value kernel sweeps its array; giving each wave a contiguous
+// chunk of rows instead ran 4-8% slower on 1 GiB matrices. A wave covers
 // `ngroups` column groups of VEC columns per load: normally ngroups == 64
 // (one group per lane), and each row is read with CW loads that cover
 // CW * 64 * VEC adjacent columns (CW KiB when VEC == 4), lane l taking
@@ -52,7 +58,7 @@ __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typenam
 template <class Op, int VEC, int CW, int UNROLL, bool NT, bool PREFETCH>
 __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::elem_t* __restrict__ x,
                                                              size_t rows, size_t cols, size_t ld,
-                                                             size_t rchunk, size_t ncb, unsigned int ngroups,
+                                                             size_t ncb, unsigned int ngroups,
                                                              typename Op::acc_t* __restrict__ partials,
                                                              typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
@@ -60,13 +66,15 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
     const unsigned int lane = threadIdx.x;
     const size_t j = blockIdx.x % ncb;
     const size_t k = blockIdx.x / ncb;
+    const size_t nphases = gridDim.x / ncb;
     const unsigned int g = lane % ngroups;
-    const size_t rpl = kWave / ngroups;  // rows per load
+    const size_t group = kWave / ngroups;  // rows per load
+    const size_t rpl = group * nphases;    // rows between a lane's consecutive loads
     const size_t q = lane / ngroups;
     const size_t span = (size_t)ngroups * VEC;  // columns per load
     const size_t c0 = j * span * CW + (size_t)g * VEC;
-    const size_t r0 = k * rchunk;
-    const size_t r1 = r0 + rchunk < rows ? r0 + rchunk : rows;
+    const size_t r0 = k * group;
+    const size_t r1 = rows;
     acc_t acc[CW][VEC];
 #pragma unroll
     for (int w = 0; w < CW; ++w)
@@ -76,18 +84,22 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
         size_t off[CW];  // in V units from the lane's column-0 vector
 #pragma unroll
         for (int w = 0; w < CW; ++w) off[w] = c0 + w * span < cols ? w * (size_t)ngroups : 0;
-        const size_t step = ld / VEC * rpl;  // in V units, between a lane's rows
+        const size_t step = ld / VEC * rpl;  // in V units, between a lane's consecutive rows
         constexpr size_t U = UNROLL;
         size_t r = r0 + q;
         const V* __restrict__ p = reinterpret_cast<const V*>(x + r * ld + c0);
         // Groups of UNROLL rows. With PREFETCH, two register buffers
         // alternate: the next group's loads are issued before the current
         // group is folded, so a wave keeps two groups in flight.
+        // The scheduling barrier keeps a group's loads issued back to back
+        // (left alone, the compiler sometimes interleaves them with waits
+        // for the previous group, halving the loads in flight).
         auto load_group = [&](V (&v)[UNROLL][CW], const V* __restrict__ g) {
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
                 for (int w = 0; w < CW; ++w) v[u][w] = load_vec<NT>(g + u * step + off[w]);
+            __builtin_amdgcn_sched_barrier(0);
         };
         auto fold_group = [&](const V (&v)[UNROLL][CW]) {
 #pragma unroll
@@ -180,15 +192,14 @@ template <class Op, int VEC, int CW, int UNROLL, bool PF>
 static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                             typename Op::out_t* out, const ColsLaunch& L, bool nt, hipStream_t stream) {
     auto* partials = static_cast<typename Op::acc_t*>(L.partials);
-    const size_t rchunk = (rows + L.nchunks - 1) / L.nchunks;
     const dim3 grid((unsigned int)(L.ncb * L.nchunks));
     typename Op::out_t* direct = L.nchunks == 1 ? out : nullptr;
     if (nt)
         hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF>), grid, dim3(kWave), 0, stream, x,
-                           rows, cols, ld, rchunk, L.ncb, L.ngroups, partials, direct);
+                           rows, cols, ld, L.ncb, L.ngroups, partials, direct);
     else
         hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF>), grid, dim3(kWave), 0, stream, x,
-                           rows, cols, ld, rchunk, L.ncb, L.ngroups, partials, direct);
+                           rows, cols, ld, L.ncb, L.ngroups, partials, direct);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || L.nchunks == 1) return e;
     const size_t W = kColsCombineBlock / kWave;

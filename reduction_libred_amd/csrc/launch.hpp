@@ -75,7 +75,8 @@ struct ColsPolicy {
 };
 
 // How one column call launches: ncb column blocks of ngroups*vec*width
-// columns times nchunks row chunks (ngroups == 64, or a divisor of 64 for a narrow
+// columns times nchunks row phases (phase k takes every nchunks-th group of
+// rows, starting at group k; ngroups == 64, or a divisor of 64 for a narrow
 // matrix whose wave then covers 64 / ngroups rows per load); with
 // nchunks > 1, partials (nchunks * cols acc_t) live in `partials`.
 struct ColsLaunch {

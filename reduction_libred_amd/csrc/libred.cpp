@@ -323,8 +323,6 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         const size_t by_scratch = kColsScratchMax / (cols * 8);
         if (nchunks > by_scratch) nchunks = by_scratch;
         if (nchunks < 1) nchunks = 1;
-        const size_t rchunk = (rows + nchunks - 1) / nchunks;
-        nchunks = (rows + rchunk - 1) / rchunk;  // no empty chunk
     }
     L.nchunks = nchunks;
     L.partials = nullptr;
