@@ -1014,3 +1014,45 @@ def test_full_sparse_ones_1e9p7():
     assert gpu_sum(x[3:]) == float(len(range(64, n, 64)))
     del x
     torch.cuda.empty_cache()
+
+
+def test_beyond_2p32_elements():
+    """More than 2^32 elements (16 GiB of float32), so every element index and
+    count needs 64 bits: sparse ones with one planted maximum past index 2^32,
+    read as float32, as int32 bit patterns, as a 65536 x 65536 matrix by rows
+    and by columns, and as two rows of 2^31 (the split-row path)."""
+    n = (1 << 32) + 7
+    p = (1 << 32) + 3                       # past 2^32, not a multiple of 64
+    say(f"n = 2^32 + 7 ({4 * n / 2**30:.1f} GiB)")
+    x = torch.zeros(n, device=DEV)
+    x[::64] = 1.0
+    x[p] = 5.0
+    ones = (n + 63) // 64
+    torch.cuda.synchronize()
+    say("sum / max / min / argmax / argmin beyond 2^32")
+    assert gpu_sum(x) == float(np.float32(ones + 5))
+    assert gpu_sum(x[1:]) == float(np.float32(ones - 1 + 5))
+    assert rl.red_max_f32(x).item() == 5.0
+    assert rl.red_min_f32(x).item() == 0.0
+    assert int(rl.red_argmax_f32(x).item()) == p
+    assert int(rl.red_argmin_f32(x).item()) == 1
+    assert int(rl.red_argmax_f32(x[5:]).item()) == p - 5
+    fused = rl.red_sum_max_f32(x).cpu().numpy()
+    assert fused[0] == np.float32(ones + 5) and fused[1] == 5.0 and fused[2] == np.float32(ones + 5)
+    say("int32 bit patterns beyond 2^32")
+    want = ones * 0x3F800000 + 0x40A00000            # bits of 1.0f and 5.0f
+    assert int(rl.red_sum_i32_i64(x.view(torch.int32)).item()) == want
+    say("rows and columns of a 65536 x 65536 view")
+    m = x[: 1 << 32].view(1 << 16, 1 << 16)
+    assert torch.all(rl.red_rows_sum_f32(m) == 1024.0)
+    assert torch.all(rl.red_rows_max_f32(m) == 1.0)
+    c = rl.red_cols_sum_f32(m)
+    want_c = torch.zeros(1 << 16, device=DEV)
+    want_c[::64] = float(1 << 16)
+    assert torch.equal(c, want_c)
+    assert torch.equal(rl.red_cols_max_f32(m), (want_c > 0).float())
+    say("two rows of 2^31 (split rows)")
+    r2 = x[: 1 << 32].view(2, 1 << 31)
+    assert torch.all(rl.red_rows_sum_f32(r2) == float(1 << 25))
+    del x, m, r2
+    torch.cuda.empty_cache()
