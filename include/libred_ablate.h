@@ -69,16 +69,23 @@ typedef struct red_flat_policy {
 
 /* Launch shape of the row kernels: `block` threads (64, 128, 256 or 512; one
  * row per wave at a time), `unroll` loads per lane per trip (1, 2, 4, 8, 16),
- * `nontemporal`, `max_blocks` capping the grid, and `split`: 0 = split few
+ * `nontemporal`, `max_blocks` capping the grid, `split`: 0 = split few
  * long rows across single-wave blocks when that helps (the default rule),
  * 1 = never, 2 = whenever a row holds at least two tiles of 64*unroll
- * vectors. */
+ * vectors; `prefetch` (0 or 1, one wave per row only): keep the next
+ * tile of 64*unroll vectors in flight while folding the current one, across
+ * row boundaries; and `short_rows`: 0 = rows of at most 1024 floats go to a
+ * kernel in which each single-wave block loads 16 / v rows at once (v = 1, 2
+ * or 4 vectors per lane per row; `block`, `unroll` and `prefetch` do not
+ * apply there, `max_blocks` caps its grid), 1 = never. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
     int nontemporal;
     int max_blocks;
     int split;
+    int prefetch;
+    int short_rows;
 } red_rows_policy;
 
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,
@@ -108,9 +115,12 @@ red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_
 red_status red_cols_max_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_cols_policy *p, hipStream_t stream);
 
-/* The shape red_sum_f32 / red_sum_i32_i64 / red_max_f32 use for n elements,
- * and the shape of the row entry points. */
+/* The shape red_sum_f32 / red_sum_i32_i64 / red_max_f32 use for n elements. */
 void red_default_flat_policy(size_t n, red_flat_policy *p);
+/* The default shape of the row entry points for rows of 2048 to 16383 floats. A
+ * call without a policy adapts it to the row length: 16 loads per lane and
+ * max_blocks 512 from 16384 floats up; below 2048 floats, at most 4 loads per
+ * lane (a tile no longer than the row) and max_blocks 2048. */
 void red_default_rows_policy(red_rows_policy *p);
 
 /* The number of blocks a single-value call of n elements launches with

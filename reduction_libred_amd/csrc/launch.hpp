@@ -38,6 +38,8 @@ struct RowsPolicy {
     int nontemporal;
     int max_blocks;
     int split;
+    int prefetch;
+    int short_rows;
 };
 
 // How one row call launches: `grid` blocks of the one-wave-per-row kernel,
@@ -47,6 +49,9 @@ struct RowsLaunch {
     int grid;
     unsigned int split_gx;
     void* partials;
+    int short_vpl;    // > 0: the short-row kernel with this many vectors per lane per row
+    int packed_log2l; // with packed_v > 0: the packed-row kernel, 2^packed_log2l lanes per row
+    int packed_v;     //   and up to packed_v vectors per lane per row
 };
 constexpr size_t kMaxSplitPartials = 32768;
 

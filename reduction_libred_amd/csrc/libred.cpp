@@ -61,7 +61,7 @@ constexpr FlatPolicy kFlatCached = {1024, 1, 4, 1, libred::kWaveTiles, 1, libred
 constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
 constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
-constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0};
+constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0};
 // Split-row mode: used automatically for fewer than kSplitRowsBelow rows
 // whose rows hold at least kSplitMinCols elements; aims for about
 // kSplitTargetWaves waves in all.
@@ -201,9 +201,29 @@ FlatPolicy to_flat(const red_flat_policy* p, size_t n, bool fused = false) {
     return f;
 }
 
-RowsPolicy to_rows(const red_rows_policy* p) {
-    if (!p) return kDefaultRows;
-    RowsPolicy r = {p->block, p->unroll, p->nontemporal, p->max_blocks, p->split};
+// The row defaults follow the row length (a sweep over 1 GiB matrices with
+// rows of 1024, 4096, 16384 and 65536 floats): rows of at least 16384 floats
+// take 16 loads per lane and 512 waves; rows under 2048 floats take a tile
+// no longer than the row (at most 4 loads per lane) and 2048 waves, so that
+// the per-row wave reduce is spread over more waves; the rest keep
+// kDefaultRows.
+RowsPolicy default_rows(size_t cols) {
+    RowsPolicy p = kDefaultRows;
+    const size_t nvec = cols / 4;
+    if (nvec >= 4096) {
+        p.unroll = 16;
+        p.max_blocks = 512;
+    } else if (nvec < 512) {
+        const size_t u = nvec / 64;
+        p.unroll = u >= 4 ? 4 : (u >= 2 ? 2 : 1);
+        p.max_blocks = 2048;
+    }
+    return p;
+}
+
+RowsPolicy to_rows(const red_rows_policy* p, size_t cols) {
+    if (!p) return default_rows(cols);
+    RowsPolicy r = {p->block, p->unroll, p->nontemporal, p->max_blocks, p->split, p->prefetch, p->short_rows};
     return r;
 }
 
@@ -247,7 +267,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (rows > 1 && ld != 0 && rows - 1 > (RED_MAX_N - cols) / ld) return RED_ERR_INVALID_ARG;
     const size_t span = rows == 0 ? 0 : (rows - 1) * ld + cols;
     if (span > RED_MAX_N) return RED_ERR_INVALID_ARG;
-    const RowsPolicy p = to_rows(pol);
+    const RowsPolicy p = to_rows(pol, cols);
     if (!libred::rows_policy_supported(p)) return RED_ERR_INVALID_ARG;
     if (rows == 0) return RED_OK;
     if ((span > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
@@ -258,7 +278,33 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
 
-    libred::RowsLaunch L = {0, 0, nullptr};
+    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0};
+    // Rows of at most 128 vectors (512 floats) go to a short-row kernel
+    // unless the policy turns that off: the packed one when every row starts
+    // 16-byte aligned and holds whole vectors, else one wave per row with
+    // 16 / v rows loaded at a time.
+    const size_t nv = cols / 4;
+    if (p.short_rows == 0 && cols > 0 && nv <= 128) {
+        size_t per_trip;
+        if (aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0) {
+            int lg = 0;
+            while ((1u << lg) < nv && lg < 4) ++lg;  // lanes per row: pow2ceil(nv), at most 16
+            const size_t lanes = (size_t)1 << lg;
+            const size_t per_lane = (nv + lanes - 1) / lanes;
+            L.packed_log2l = lg;
+            L.packed_v = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
+            const size_t rows_per_group = 64 / lanes;
+            const size_t groups = (rows + rows_per_group - 1) / rows_per_group;
+            per_trip = (groups + (16 / L.packed_v) - 1) / (16 / L.packed_v);
+        } else {
+            L.short_vpl = nv <= 64 ? 1 : 2;
+            per_trip = (rows + (16 / L.short_vpl) - 1) / (16 / L.short_vpl);
+        }
+        L.grid = (int)(per_trip < (size_t)p.max_blocks ? per_trip : (size_t)p.max_blocks);
+        const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
+        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+        return RED_OK;
+    }
     const size_t tile_elems = (size_t)64 * (size_t)p.unroll * 4;
     const size_t tiles_per_row = cols / tile_elems;
     const bool want_split =
@@ -474,6 +520,8 @@ void red_default_rows_policy(red_rows_policy* p) {
     p->nontemporal = kDefaultRows.nontemporal;
     p->max_blocks = kDefaultRows.max_blocks;
     p->split = kDefaultRows.split;
+    p->prefetch = kDefaultRows.prefetch;
+    p->short_rows = kDefaultRows.short_rows;
 }
 
 size_t red_flat_grid(size_t n, const red_flat_policy* pol) {

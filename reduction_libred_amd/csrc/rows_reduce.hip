@@ -20,6 +20,39 @@
 
 namespace libred {
 
+template <bool NT, class V, int UNROLL>
+__device__ __forceinline__ void load_tile_rows(V (&v)[UNROLL], const V* __restrict__ p) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
+}
+
+// Fold body vectors i = begin + lane, begin + lane + step, ... (< nvec) of a
+// row into acc, UNROLL loads at a time: a lane issues all of a batch's loads
+// before it folds any, so the vectors after a row's last whole tile cost one
+// memory latency, not one per vector. (The loads stay under a lane mask here:
+// loading a stand-in vector instead, as the short-row kernels do, made the
+// compiler wait for every outstanding memory operation at the top of each
+// row in the one-wave-per-row kernel, 11% slower on 65536 x 4096.)
+template <class Op, int UNROLL, bool NT>
+__device__ __forceinline__ void fold_remainder(typename Op::acc_t (&acc)[4], const typename Op::vec_t* __restrict__ rv,
+                                               size_t head, size_t begin, size_t nvec, size_t step) {
+    using vec_t = typename Op::vec_t;
+    const size_t lane = threadIdx.x % kWave;
+    for (size_t i0 = begin + lane; i0 < nvec; i0 += step * UNROLL) {
+        vec_t v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const size_t i = i0 + (size_t)u * step;
+            if (i < nvec) v[u] = load_vec<NT>(rv + i);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const size_t i = i0 + (size_t)u * step;
+            if (i < nvec) fold_vec<Op>(acc, v[u], head + i * Op::kPerVec);
+        }
+    }
+}
+
 // Fold row `row` (cols elements) into acc: vectors v0, v0 + vstep, ... of the
 // aligned body in loop trips of UNROLL loads spaced 64 vectors apart, with the
 // head and tail only when `edges` is set. Wave-uniform arguments.
@@ -44,8 +77,7 @@ __device__ __forceinline__ void fold_row_span(const typename Op::elem_t* __restr
         for (int u = 0; u < UNROLL; ++u)
             fold_vec<Op>(acc, v[u], head + (t * TILE + lane + (size_t)u * kWave) * Op::kPerVec);
     }
-    for (size_t i = ntiles * TILE + first_tile * kWave + lane; i < nvec; i += tile_step * kWave)
-        fold_vec<Op>(acc, load_vec<NT>(rv + i), head + i * Op::kPerVec);
+    fold_remainder<Op, UNROLL, NT>(acc, rv, head, ntiles * TILE + first_tile * kWave, nvec, tile_step * kWave);
     if (edges) {
         if ((size_t)lane < head) acc[0] = Op::combine(acc[0], Op::lift(row[lane], lane));
         if ((size_t)lane < cols - tail0)
@@ -69,6 +101,240 @@ __global__ __launch_bounds__(BLOCK) void rows_reduce_kernel(const typename Op::e
         acc_t v = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
         v = wave_reduce<Op>(v);
         if (lane == 0) out[r] = Op::finish(v);
+    }
+}
+
+// One wave per row with the next tile always in flight. A wave's work is a
+// sequence of (row, tile) positions: the whole tiles of row r, then those of
+// row r + stride, and so on. Two register buffers alternate: the loads of the
+// next position (which may be the first tile of the wave's next row) are
+// issued before the current tile is folded, and a row is finished (the
+// vectors after its last whole tile, its head and tail, the wave reduce and
+// the store) while the next row's first tile is on its way. Rows with no
+// whole tile are finished directly. Every load is of a tile that lies inside
+// its row.
+template <class Op>
+struct RowGeom {
+    const typename Op::vec_t* rv;  // first aligned vector of the row body
+    size_t head, nvec, ntiles;
+};
+
+template <class Op, int UNROLL>
+__device__ __forceinline__ RowGeom<Op> row_geom(const typename Op::elem_t* __restrict__ x, size_t r,
+                                                size_t cols, size_t ld) {
+    const typename Op::elem_t* row = x + r * ld;
+    RowGeom<Op> g;
+    g.head = head_elems(row, sizeof(typename Op::elem_t), cols);
+    g.nvec = (cols - g.head) / Op::kPerVec;
+    g.ntiles = g.nvec / ((size_t)kWave * UNROLL);
+    g.rv = reinterpret_cast<const typename Op::vec_t*>(row + g.head);
+    return g;
+}
+
+template <class Op, int BLOCK, int UNROLL, bool NT>
+__global__ __launch_bounds__(BLOCK) void rows_prefetch_kernel(const typename Op::elem_t* __restrict__ x,
+                                                              size_t rows, size_t cols, size_t ld,
+                                                              typename Op::out_t* __restrict__ out) {
+    using acc_t = typename Op::acc_t;
+    using vec_t = typename Op::vec_t;
+    constexpr int W = BLOCK / kWave;
+    constexpr size_t TILE = (size_t)kWave * UNROLL;
+    const int lane = threadIdx.x % kWave;
+    const size_t stride = (size_t)gridDim.x * W;
+    size_t r = (size_t)blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    if (r >= rows) return;  // wave-uniform
+    RowGeom<Op> g = row_geom<Op, UNROLL>(x, r, cols, ld);
+    size_t t = 0;
+    bool have = g.ntiles > 0;
+    acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
+    vec_t a[UNROLL], b[UNROLL];
+
+    // Everything of row r that is not a whole tile, then the row's result.
+    auto finish_row = [&]() {
+        const typename Op::elem_t* row = x + r * ld;
+        fold_remainder<Op, UNROLL, NT>(acc, g.rv, g.head, g.ntiles * TILE, g.nvec, kWave);
+        const size_t tail0 = g.head + (size_t)Op::kPerVec * g.nvec;
+        if ((size_t)lane < g.head) acc[0] = Op::combine(acc[0], Op::lift(row[lane], lane));
+        if ((size_t)lane < cols - tail0) acc[1] = Op::combine(acc[1], Op::lift(row[tail0 + lane], tail0 + lane));
+        acc_t v = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
+        v = wave_reduce<Op>(v);
+        if (lane == 0) out[r] = Op::finish(v);
+        acc[0] = acc[1] = acc[2] = acc[3] = Op::identity();
+    };
+    // Process the tile in `cur` (if any) and leave the next position's tile
+    // in `nxt`; false once the wave has no rows left.
+    auto step = [&](vec_t (&cur)[UNROLL], vec_t (&nxt)[UNROLL]) -> bool {
+        if (have) {
+            size_t rn = r, tn = t + 1;
+            RowGeom<Op> gn = g;
+            const bool row_done = tn >= g.ntiles;
+            if (row_done) {
+                rn = r + stride;
+                tn = 0;
+                if (rn < rows) gn = row_geom<Op, UNROLL>(x, rn, cols, ld);
+            }
+            const bool next_have = rn < rows && tn < gn.ntiles;
+            if (next_have) load_tile_rows<NT>(nxt, gn.rv + tn * TILE + lane);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                fold_vec<Op>(acc, cur[u], g.head + (t * TILE + lane + (size_t)u * kWave) * Op::kPerVec);
+            if (row_done) finish_row();
+            r = rn;
+            t = tn;
+            g = gn;
+            have = next_have;
+        } else {
+            finish_row();
+            r += stride;
+            if (r < rows) {
+                g = row_geom<Op, UNROLL>(x, r, cols, ld);
+                t = 0;
+                have = g.ntiles > 0;
+                if (have) load_tile_rows<NT>(nxt, g.rv + lane);
+            }
+        }
+        return r < rows;
+    };
+    if (have) load_tile_rows<NT>(a, g.rv + lane);
+    while (step(a, b) && step(b, a)) {
+    }
+}
+
+// Packed short rows: when every row starts on a 16-byte boundary and holds
+// whole vectors only (x 16-byte aligned, cols and ld multiples of 4), a row of
+// nvec <= 128 vectors gets a segment of L = 2^LOG2L <= 16 lanes, lane j taking
+// the row's vectors j, j + L, ..., up to V of them, so one load covers
+// P = 64 / L rows. Each lane folds its vectors, the L lanes of a segment are
+// combined with the first LOG2L steps of the DPP wave reduce (quad_perm,
+// row_half_mirror, row_mirror: after them every lane of the segment holds
+// the segment's total), and lane j == 0 stores the row. A wave takes groups
+// of P rows w, w + G, w + 2G, ... (G = grid size), U = 16 / V groups per trip
+// with all their loads issued first.
+template <class Op, int LOG2L>
+__device__ __forceinline__ typename Op::acc_t segment_reduce(typename Op::acc_t v) {
+    using T = typename Op::acc_t;
+    const T id = Op::identity();
+    if constexpr (LOG2L >= 1) v = Op::combine(v, dpp_move<0xB1, 0xF>(id, v));   // quad_perm:[1,0,3,2]
+    if constexpr (LOG2L >= 2) v = Op::combine(v, dpp_move<0x4E, 0xF>(id, v));   // quad_perm:[2,3,0,1]
+    if constexpr (LOG2L >= 3) v = Op::combine(v, dpp_move<0x141, 0xF>(id, v));  // row_half_mirror
+    if constexpr (LOG2L >= 4) v = Op::combine(v, dpp_move<0x140, 0xF>(id, v));  // row_mirror
+    return v;
+}
+
+template <class Op, int LOG2L, int V, bool NT>
+__global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::elem_t* __restrict__ x,
+                                                            size_t rows, size_t cols, size_t ld,
+                                                            typename Op::out_t* __restrict__ out) {
+    using acc_t = typename Op::acc_t;
+    using vec_t = typename Op::vec_t;
+    constexpr int L = 1 << LOG2L;
+    constexpr int P = kWave / L;
+    constexpr int U = V >= 16 ? 1 : 16 / V;
+    const int lane = threadIdx.x;
+    const size_t q = (size_t)(lane >> LOG2L);
+    const size_t j = (size_t)(lane & (L - 1));
+    const size_t nvec = cols / Op::kPerVec;
+    const size_t ldv = ld / Op::kPerVec;
+    const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x);
+    const size_t G = gridDim.x;
+    const size_t ngroups = (rows + P - 1) / P;
+    for (size_t g0 = blockIdx.x; g0 < ngroups; g0 += G * U) {  // wave-uniform
+        vec_t v[U][V];
+        // A lane with no vector to read (past the last row, or past its row's
+        // last vector) reads vector 0 of the matrix instead and folds nothing:
+        // no load sits under a lane mask.
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t r = (g0 + (size_t)u * G) * P + q;
+            const bool live = r < rows;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const size_t i = j + (size_t)k * L;
+                v[u][k] = load_vec<NT>(xv + (live && i < nvec ? r * ldv + i : 0));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t g = g0 + (size_t)u * G;
+            if (g >= ngroups) break;  // wave-uniform
+            const size_t r = g * P + q;
+            const bool live = r < rows;
+            acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const size_t i = j + (size_t)k * L;
+                if (live && i < nvec) fold_vec<Op>(acc, v[u][k], i * Op::kPerVec);
+            }
+            acc_t a = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
+            a = segment_reduce<Op, LOG2L>(a);
+            if (live && j == 0) out[r] = Op::finish(a);
+        }
+    }
+}
+
+// Short rows that the packed kernel cannot take (at most 64 * VPL vectors
+// each, VPL = 1 or 2, with heads and tails): one wave still reduces each
+// row, but it takes RB = 16 / VPL of its rows at a time and issues the loads
+// of all of them (VPL vectors per lane per row, and the scalar head and tail)
+// before it folds and reduces any, so 16 loads stay in flight per wave
+// instead of one row's. Single-wave blocks; wave w takes rows w, w + G,
+// w + 2G, ... (G = grid size), RB of them per trip. Rows past the end and
+// lanes past a row's end fold nothing.
+template <class Op, int VPL, bool NT>
+__global__ __launch_bounds__(kWave) void rows_short_kernel(const typename Op::elem_t* __restrict__ x,
+                                                           size_t rows, size_t cols, size_t ld,
+                                                           typename Op::out_t* __restrict__ out) {
+    using acc_t = typename Op::acc_t;
+    using vec_t = typename Op::vec_t;
+    using elem_t = typename Op::elem_t;
+    constexpr int RB = 16 / VPL;
+    const int lane = threadIdx.x;
+    const size_t G = gridDim.x;
+    for (size_t r0 = blockIdx.x; r0 < rows; r0 += G * RB) {  // wave-uniform
+        vec_t v[RB][VPL];
+        elem_t hv[RB], tv[RB];
+        size_t head[RB], nvec[RB], tail0[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const size_t r = r0 + (size_t)b * G;
+            const bool live = r < rows;
+            const elem_t* row = x + (live ? r : 0) * ld;
+            head[b] = live ? head_elems(row, sizeof(elem_t), cols) : 0;
+            nvec[b] = live ? (cols - head[b]) / Op::kPerVec : 0;
+            tail0[b] = head[b] + (size_t)Op::kPerVec * nvec[b];
+            const vec_t* rv = reinterpret_cast<const vec_t*>(row + head[b]);
+            // Loads are never under a lane mask (that would make the compiler
+            // wait for every earlier load first): a lane with nothing to read
+            // reads the row's vector 0, or element 0 (row 0 for a row past the
+            // end), and folds nothing. A row without a whole vector skips the
+            // vector loads (a wave-uniform branch).
+            if (nvec[b] > 0) {
+#pragma unroll
+                for (int k = 0; k < VPL; ++k) {
+                    const size_t i = (size_t)k * kWave + lane;
+                    v[b][k] = load_vec<NT>(rv + (i < nvec[b] ? i : 0));
+                }
+            }
+            hv[b] = row[(size_t)lane < head[b] ? (size_t)lane : 0];
+            tv[b] = row[(size_t)lane < cols - tail0[b] ? tail0[b] + lane : 0];
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const size_t r = r0 + (size_t)b * G;
+            if (r >= rows) break;  // wave-uniform
+            acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
+#pragma unroll
+            for (int k = 0; k < VPL; ++k) {
+                const size_t i = (size_t)k * kWave + lane;
+                if (i < nvec[b]) fold_vec<Op>(acc, v[b][k], head[b] + i * Op::kPerVec);
+            }
+            if ((size_t)lane < head[b]) acc[0] = Op::combine(acc[0], Op::lift(hv[b], lane));
+            if ((size_t)lane < cols - tail0[b])
+                acc[1] = Op::combine(acc[1], Op::lift(tv[b], tail0[b] + lane));
+            acc_t w = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
+            w = wave_reduce<Op>(w);
+            if (lane == 0) out[r] = Op::finish(w);
+        }
     }
 }
 
@@ -109,18 +375,26 @@ bool rows_policy_supported(const RowsPolicy& p) {
     const bool b = p.block == 64 || p.block == 128 || p.block == 256 || p.block == 512;
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.max_blocks >= 1 && p.split >= 0 &&
-           p.split <= 2;
+           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && (p.short_rows == 0 || p.short_rows == 1);
 }
 
 template <class Op, int BLOCK, int UNROLL>
 static hipError_t rows_bu(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
-                          typename Op::out_t* out, int grid, bool nt, hipStream_t stream) {
-    if (nt)
+                          typename Op::out_t* out, int grid, bool nt, bool pf, hipStream_t stream) {
+    if (pf) {
+        if (nt)
+            hipLaunchKernelGGL((rows_prefetch_kernel<Op, BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0,
+                               stream, x, rows, cols, ld, out);
+        else
+            hipLaunchKernelGGL((rows_prefetch_kernel<Op, BLOCK, UNROLL, false>), dim3(grid), dim3(BLOCK), 0,
+                               stream, x, rows, cols, ld, out);
+    } else if (nt) {
         hipLaunchKernelGGL((rows_reduce_kernel<Op, BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0,
                            stream, x, rows, cols, ld, out);
-    else
+    } else {
         hipLaunchKernelGGL((rows_reduce_kernel<Op, BLOCK, UNROLL, false>), dim3(grid), dim3(BLOCK), 0,
                            stream, x, rows, cols, ld, out);
+    }
     return hipGetLastError();
 }
 
@@ -128,12 +402,13 @@ template <class Op, int BLOCK>
 static hipError_t rows_b(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                          typename Op::out_t* out, int grid, const RowsPolicy& p, hipStream_t stream) {
     const bool nt = p.nontemporal != 0;
+    const bool pf = p.prefetch != 0;
     switch (p.unroll) {
-        case 1: return rows_bu<Op, BLOCK, 1>(x, rows, cols, ld, out, grid, nt, stream);
-        case 2: return rows_bu<Op, BLOCK, 2>(x, rows, cols, ld, out, grid, nt, stream);
-        case 4: return rows_bu<Op, BLOCK, 4>(x, rows, cols, ld, out, grid, nt, stream);
-        case 8: return rows_bu<Op, BLOCK, 8>(x, rows, cols, ld, out, grid, nt, stream);
-        case 16: return rows_bu<Op, BLOCK, 16>(x, rows, cols, ld, out, grid, nt, stream);
+        case 1: return rows_bu<Op, BLOCK, 1>(x, rows, cols, ld, out, grid, nt, pf, stream);
+        case 2: return rows_bu<Op, BLOCK, 2>(x, rows, cols, ld, out, grid, nt, pf, stream);
+        case 4: return rows_bu<Op, BLOCK, 4>(x, rows, cols, ld, out, grid, nt, pf, stream);
+        case 8: return rows_bu<Op, BLOCK, 8>(x, rows, cols, ld, out, grid, nt, pf, stream);
+        case 16: return rows_bu<Op, BLOCK, 16>(x, rows, cols, ld, out, grid, nt, pf, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -158,10 +433,64 @@ static hipError_t rows_split_u(const typename Op::elem_t* x, size_t rows, size_t
     return hipGetLastError();
 }
 
+template <class Op, int LOG2L, int V>
+static hipError_t rows_packed_lv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+                                 typename Op::out_t* out, int grid, bool nt, hipStream_t stream) {
+    if (nt)
+        hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, true>), dim3(grid), dim3(kWave), 0, stream, x, rows,
+                           cols, ld, out);
+    else
+        hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, false>), dim3(grid), dim3(kWave), 0, stream, x, rows,
+                           cols, ld, out);
+    return hipGetLastError();
+}
+
+template <class Op, int LOG2L>
+static hipError_t rows_packed_v(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+                                typename Op::out_t* out, const RowsLaunch& L, bool nt, hipStream_t stream) {
+    switch (L.packed_v) {
+        case 1: return rows_packed_lv<Op, LOG2L, 1>(x, rows, cols, ld, out, L.grid, nt, stream);
+        case 2: return rows_packed_lv<Op, LOG2L, 2>(x, rows, cols, ld, out, L.grid, nt, stream);
+        case 4: return rows_packed_lv<Op, LOG2L, 4>(x, rows, cols, ld, out, L.grid, nt, stream);
+        case 8: return rows_packed_lv<Op, LOG2L, 8>(x, rows, cols, ld, out, L.grid, nt, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class Op>
+static hipError_t rows_packed_l(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+                                typename Op::out_t* out, const RowsLaunch& L, bool nt, hipStream_t stream) {
+    switch (L.packed_log2l) {
+        case 0: return rows_packed_v<Op, 0>(x, rows, cols, ld, out, L, nt, stream);
+        case 1: return rows_packed_v<Op, 1>(x, rows, cols, ld, out, L, nt, stream);
+        case 2: return rows_packed_v<Op, 2>(x, rows, cols, ld, out, L, nt, stream);
+        case 3: return rows_packed_v<Op, 3>(x, rows, cols, ld, out, L, nt, stream);
+        case 4: return rows_packed_v<Op, 4>(x, rows, cols, ld, out, L, nt, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <class Op>
 static hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, const RowsLaunch& L, const RowsPolicy& p,
                           hipStream_t stream) {
+    if (L.packed_v > 0) return rows_packed_l<Op>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);
+    if (L.short_vpl > 0) {
+        const bool nt = p.nontemporal != 0;
+        const dim3 grid((unsigned int)L.grid);
+        switch (L.short_vpl) {
+            case 1:
+                if (nt) hipLaunchKernelGGL((rows_short_kernel<Op, 1, true>), grid, dim3(kWave), 0, stream, x, rows, cols, ld, out);
+                else hipLaunchKernelGGL((rows_short_kernel<Op, 1, false>), grid, dim3(kWave), 0, stream, x, rows, cols, ld, out);
+                break;
+            case 2:
+                if (nt) hipLaunchKernelGGL((rows_short_kernel<Op, 2, true>), grid, dim3(kWave), 0, stream, x, rows, cols, ld, out);
+                else hipLaunchKernelGGL((rows_short_kernel<Op, 2, false>), grid, dim3(kWave), 0, stream, x, rows, cols, ld, out);
+                break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     if (L.split_gx > 0) {
         const bool nt = p.nontemporal != 0;
         switch (p.unroll) {

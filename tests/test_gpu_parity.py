@@ -556,7 +556,11 @@ def test_sum_f64():
 # ----------------------------------------------------------------- rows
 
 ROW_SHAPES = [(1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
-              (5, 64), (6, 65), (257, 4096), (2, 100_003), (4097, 3)]
+              (5, 64), (6, 65), (257, 4096), (2, 100_003), (4097, 3), (333, 1024), (50, 513),
+              (1000, 4), (777, 16), (301, 32), (129, 128), (77, 200), (33, 8), (1025, 12), (70, 512)]
+ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1, max_blocks=3, short_rows=1),
+                dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
+                dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
@@ -565,40 +569,45 @@ def test_rows_random(rows, cols):
     a = rng.standard_normal((rows, cols)).astype(np.float32)
     if cols:
         a[np.arange(rows), np.arange(rows) % cols] = 50.0 + np.arange(rows)   # planted max
+    S, A = oracle.rows_sum_f32(a)
+    M = oracle.rows_max_f32(a)
     for offset in (0, 1):
-        say(f"rows {rows}x{cols} offset={offset}")
-        x = device_view(a, offset)
-        guard_out = torch.full((rows + 2,), 777.0, device=DEV)
-        out_s = guard_out[1:rows + 1]
-        rl.red_rows_sum_f32(x, out=out_s)
-        torch.cuda.synchronize()
-        assert guard_out[0].item() == 777.0 and guard_out[-1].item() == 777.0
-        S, A = oracle.rows_sum_f32(a)
-        got = out_s.cpu().numpy().astype(np.float64)
-        assert np.all(np.abs(got - S) <= 1e-5 * A + 1e-6), (rows, cols)
-        out_m = rl.red_rows_max_f32(x)
-        torch.cuda.synchronize()
-        assert np.array_equal(out_m.cpu().numpy(), oracle.rows_max_f32(a)), (rows, cols)
+        for p in ROW_POLICIES:
+            say(f"rows {rows}x{cols} offset={offset} policy={p}")
+            x = device_view(a, offset)
+            guard_out = torch.full((rows + 2,), 777.0, device=DEV)
+            out_s = guard_out[1:rows + 1]
+            rl.red_rows_sum_f32(x, out=out_s, policy=p)
+            torch.cuda.synchronize()
+            assert guard_out[0].item() == 777.0 and guard_out[-1].item() == 777.0
+            got = out_s.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(got - S) <= 1e-5 * A + 1e-6), (rows, cols, p)
+            out_m = rl.red_rows_max_f32(x, policy=p)
+            torch.cuda.synchronize()
+            assert np.array_equal(out_m.cpu().numpy(), M), (rows, cols, p)
 
 
 @pytest.mark.parametrize("rows,cols,ld", [(3, 5, 7), (10, 1000, 1003), (257, 4096, 4100), (64, 63, 64),
-                                          (1, 10, 10), (5, 0, 3), (1000, 129, 1024)])
+                                          (1, 10, 10), (5, 0, 3), (1000, 129, 1024), (300, 16, 20),
+                                          (100, 64, 68), (40, 128, 132), (65, 4, 8)])
 def test_rows_strided(rows, cols, ld):
     # Rows spaced ld apart: the gap holds NaN, which must never be read.
     rng = np.random.default_rng(rows + cols + ld)
     full = np.full((rows, ld), np.nan, np.float32)
     full[:, :cols] = rng.standard_normal((rows, cols)).astype(np.float32)
     a = np.ascontiguousarray(full[:, :cols])
+    S, A = oracle.rows_sum_f32(a)
+    M = oracle.rows_max_f32(a)
     for offset in (0, 1):
-        say(f"rows strided {rows}x{cols} ld={ld} offset={offset}")
-        xf = device_view(full, offset)
-        x = xf[:, :cols]
-        s = rl.red_rows_sum_f32(x)
-        m = rl.red_rows_max_f32(x)
-        torch.cuda.synchronize()
-        S, A = oracle.rows_sum_f32(a)
-        assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
-        assert np.array_equal(m.cpu().numpy(), oracle.rows_max_f32(a))
+        for p in ROW_POLICIES:
+            say(f"rows strided {rows}x{cols} ld={ld} offset={offset} policy={p}")
+            xf = device_view(full, offset)
+            x = xf[:, :cols]
+            s = rl.red_rows_sum_f32(x, policy=p)
+            m = rl.red_rows_max_f32(x, policy=p)
+            torch.cuda.synchronize()
+            assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
+            assert np.array_equal(m.cpu().numpy(), M), p
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 1_000_003), (2, 3_000_017), (7, 1 << 20), (100, 65537),
@@ -685,10 +694,10 @@ def test_rows_policies():
     x = device_view(a, 1)
     for block in (64, 128, 256, 512):
         for unroll in (1, 2, 4, 8, 16):
-            for nt in (0, 1):
+            for nt, pf in ((0, 0), (1, 0), (0, 1), (1, 1)):
                 for mb in (1, 7, 1 << 20):
-                    say(f"rows policy block={block} unroll={unroll} nt={nt} max_blocks={mb}")
-                    p = dict(block=block, unroll=unroll, nontemporal=nt, max_blocks=mb)
+                    say(f"rows policy block={block} unroll={unroll} nt={nt} pf={pf} max_blocks={mb}")
+                    p = dict(block=block, unroll=unroll, nontemporal=nt, max_blocks=mb, prefetch=pf)
                     s = rl.red_rows_sum_f32(x, policy=p)
                     m = rl.red_rows_max_f32(x, policy=p)
                     torch.cuda.synchronize()
