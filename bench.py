@@ -296,12 +296,12 @@ def main():
 
     # ---------------------------------------------------------- other entry points
     others = {}
-    reps = 50
+    reps = 50  # calls per timed region; each line is the median of three regions
 
     def measure(label, fn, nbytes_call, extra=None):
-        for _ in range(3):
+        for _ in range(10):
             fn()
-        t_ms = timer.region_ms(fn, reps)
+        t_ms = sorted(timer.region_ms(fn, reps) for _ in range(3))[1]
         rec = {"us": round(t_ms * 1e3, 3), "GB/s": round(gbps(nbytes_call, t_ms), 2),
                "pct_of_peak": round(100 * gbps(nbytes_call, t_ms) / PEAK_GBPS, 2)}
         if extra:
