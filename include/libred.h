@@ -146,6 +146,8 @@ red_status red_sum_f64(const double *x, size_t n, double *out, hipStream_t strea
  * out3 must hold 3 floats and must not overlap x. n == 0 stores 0, -inf, 0.
  * This fuses the lesson's reduction with the simulator page's max rule; the
  * sum of magnitudes is the scale against which a float sum's error is judged.
+ * Its default launch shape differs from red_sum_f32's on large arrays (more
+ * waves per CU for the extra arithmetic).
  */
 red_status red_sum_max_f32(const float *x, size_t n, float *out3, hipStream_t stream);
 
