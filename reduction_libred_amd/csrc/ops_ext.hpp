@@ -31,16 +31,17 @@ struct MinF32 {
 // Streaming. Each thread meets its elements in increasing index order, and a
 // later candidate replaces an earlier one only when it is strictly better, so
 // the first occurrence of a thread's extreme is what survives:
-//  - a whole tile of UNROLL vectors is reduced to its extreme value alone
-//    (fmaxf / fminf, which skip NaN), and acc[3] keeps the best tile value
-//    with the tile's first element index (fold_tile);
-//  - after the stream, resolve() reads that one tile again and finds its
+//  - a whole tile of UNROLL vectors is reduced to its extreme value and the
+//    first of its vectors that holds it (fmaxf / fminf, which skip NaN), and
+//    acc[3] keeps the best tile value with that vector's first element index
+//    (fold_tile);
+//  - after the stream, resolve() reads that one vector again and finds its
 //    first element equal to the kept value, making acc[3] exact;
 //  - vectors outside whole tiles find their exact index at once (fold, into
 //    acc[0]).
-// The streaming loop thus costs about two vector operations per element and
-// never selects a 64-bit index per element; the second read is one tile per
-// thread.
+// The streaming loop thus costs about two and a half vector operations per
+// element and never selects a 64-bit index per element; the second read is
+// one 16-byte vector per thread.
 struct ArgExt {
     float v;
     int32_t unused;
@@ -86,34 +87,37 @@ struct ArgExtF32 {
         acc[0].idx = take ? (int64_t)(i0 + pos) : acc[0].idx;
     }
 
-    // A tile: vector u starts at element i0 + u * 64 * kPerVec. Into acc[3].
+    // A tile: vector u starts at element i0 + u * 64 * kPerVec. Into acc[3],
+    // which keeps the first element number of the first vector of the tile
+    // that holds the tile's extreme.
     template <int UNROLL>
     static __device__ __forceinline__ void fold_tile(acc_t (&acc)[4], const vec_t (&v)[UNROLL], size_t i0) {
-        float e = ext4(v[0]);
+        float vm[UNROLL];
 #pragma unroll
-        for (int u = 1; u < UNROLL; ++u) e = ext(e, ext4(v[u]));
+        for (int u = 0; u < UNROLL; ++u) vm[u] = ext4(v[u]);
+        float e = vm[0];
+#pragma unroll
+        for (int u = 1; u < UNROLL; ++u) e = ext(e, vm[u]);
+        int first = UNROLL - 1;
+#pragma unroll
+        for (int u = UNROLL - 2; u >= 0; --u) first = vm[u] == e ? u : first;
         const bool take = replaces(e, acc[3].v);
         acc[3].v = take ? e : acc[3].v;
-        acc[3].idx = take ? (int64_t)i0 : acc[3].idx;
+        acc[3].idx = take ? (int64_t)(i0 + (size_t)first * kWave * kPerVec) : acc[3].idx;
     }
 
-    // Turn acc[3]'s tile into the index of its first element equal to the
-    // kept value, re-reading the tile from x (the start of the whole array).
-    // The value was produced by ext() from one of those elements, so the
-    // match compares ext(e, e), the form in which ext saw e.
+    // Turn acc[3]'s vector into the index of its first element equal to the
+    // kept value, re-reading that one vector from x (the start of the whole
+    // array). The value was produced by ext() from one of those elements, so
+    // the match compares ext(e, e), the form in which ext saw e.
     template <int UNROLL, bool NT>
     static __device__ __forceinline__ void resolve(acc_t (&acc)[4], const elem_t* __restrict__ x) {
         acc_t& a = acc[3];
         if (a.idx < 0) return;
-        const vec_t* __restrict__ p = reinterpret_cast<const vec_t*>(x + a.idx);
-        vec_t v[UNROLL];
+        const vec_t v = load_vec<NT>(reinterpret_cast<const vec_t*>(x + a.idx));
+        int pos = 3;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
-        int pos = 0;
-#pragma unroll
-        for (int u = UNROLL - 1; u >= 0; --u)
-#pragma unroll
-            for (int k = 3; k >= 0; --k) pos = ext(v[u][k], v[u][k]) == a.v ? u * kWave * kPerVec + k : pos;
+        for (int k = 2; k >= 0; --k) pos = ext(v[k], v[k]) == a.v ? k : pos;
         a.idx += pos;
     }
 };
