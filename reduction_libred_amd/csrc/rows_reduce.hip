@@ -209,7 +209,8 @@ __global__ __launch_bounds__(BLOCK) void rows_prefetch_kernel(const typename Op:
 // row_half_mirror, row_mirror: after them every lane of the segment holds
 // the segment's total), and lane j == 0 stores the row. A wave takes groups
 // of P rows w, w + G, w + 2G, ... (G = grid size), U = 16 / V groups per trip
-// with all their loads issued first.
+// with all their loads issued first, and the next trip's loads already in
+// flight.
 template <class Op, int LOG2L>
 __device__ __forceinline__ typename Op::acc_t segment_reduce(typename Op::acc_t v) {
     using T = typename Op::acc_t;
@@ -238,11 +239,10 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
     const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x);
     const size_t G = gridDim.x;
     const size_t ngroups = (rows + P - 1) / P;
-    for (size_t g0 = blockIdx.x; g0 < ngroups; g0 += G * U) {  // wave-uniform
-        vec_t v[U][V];
-        // A lane with no vector to read (past the last row, or past its row's
-        // last vector) reads vector 0 of the matrix instead and folds nothing:
-        // no load sits under a lane mask.
+    // A lane with no vector to read (past the last row, or past its row's
+    // last vector) reads vector 0 of the matrix instead and folds nothing:
+    // no load sits under a lane mask.
+    auto load_trip = [&](vec_t (&v)[U][V], size_t g0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t r = (g0 + (size_t)u * G) * P + q;
@@ -253,6 +253,8 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
                 v[u][k] = load_vec<NT>(xv + (live && i < nvec ? r * ldv + i : 0));
             }
         }
+    };
+    auto reduce_trip = [&](const vec_t (&v)[U][V], size_t g0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t g = g0 + (size_t)u * G;
@@ -269,6 +271,26 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
             a = segment_reduce<Op, LOG2L>(a);
             if (live && j == 0) out[r] = Op::finish(a);
         }
+    };
+    // Trips alternate between two register buffers: the next trip's loads
+    // are issued before the current trip is reduced and stored, so the loads
+    // stay in flight across trips (and, memory operations completing in
+    // order, waiting for them never waits for the stores that follow).
+    size_t g0 = blockIdx.x;  // wave-uniform
+    if (g0 >= ngroups) return;
+    vec_t a[U][V], b[U][V];
+    load_trip(a, g0);
+    while (true) {
+        size_t g1 = g0 + G * U;
+        if (g1 < ngroups) load_trip(b, g1);
+        reduce_trip(a, g0);
+        if (g1 >= ngroups) break;
+        g0 = g1;
+        g1 = g0 + G * U;
+        if (g1 < ngroups) load_trip(a, g1);
+        reduce_trip(b, g0);
+        if (g1 >= ngroups) break;
+        g0 = g1;
     }
 }
 
