@@ -74,10 +74,11 @@ typedef struct red_flat_policy {
  * 1 = never, 2 = whenever a row holds at least two tiles of 64*unroll
  * vectors; `prefetch` (0 or 1, one wave per row only): keep the next
  * tile of 64*unroll vectors in flight while folding the current one, across
- * row boundaries; and `short_rows`: 0 = rows of at most 1024 floats go to a
- * kernel in which each single-wave block loads 16 / v rows at once (v = 1, 2
- * or 4 vectors per lane per row; `block`, `unroll` and `prefetch` do not
- * apply there, `max_blocks` caps its grid), 1 = never. */
+ * row boundaries; and `short_rows`: 0 = rows of at most 512 floats go to a
+ * kernel that gives each row a segment of up to 16 (16-byte units, rows
+ * 16-byte aligned) or 64 lanes (single elements, any alignment), so that one
+ * load covers several rows (`block`, `unroll` and `prefetch` do not apply
+ * there, `max_blocks` caps its grid), 1 = never. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
@@ -93,10 +94,11 @@ typedef struct red_rows_policy {
  * until about this many single-wave blocks run), `vec`: 0 = four adjacent
  * columns per lane when x is 16-byte aligned and cols and ld are multiples
  * of 4, else one; 1 = always one; 4 = same as 0; and `width` (1, 2 or 4):
- * with four columns per lane and at least 64 column groups, each row is read
- * by `width` loads per lane, so a wave reads width KiB of a row at once
- * (otherwise 1 is used); `prefetch` (0 or 1): issue the next group of
- * `unroll` rows before adding the current one. */
+ * with at least 64 column groups, each row is read by `width` loads per lane,
+ * so a wave reads width x 1 KiB (four columns per lane) or width x 256 bytes
+ * (one column per lane) of a row at once (with fewer groups, 1 is used);
+ * `prefetch` (0 or 1): issue the next group of `unroll` rows before adding
+ * the current one. */
 typedef struct red_cols_policy {
     int unroll;
     int nontemporal;
@@ -108,7 +110,9 @@ typedef struct red_cols_policy {
 
 /* The default column shape. A call without a policy uses it, except on
  * short-wide matrices (four columns per lane and cols / 256 >= 1024), which
- * use unroll 2, width 4, no prefetch and target_waves 1024. */
+ * use unroll 2, width 4, no prefetch and target_waves 1024, and with one
+ * column per lane and at least 64 columns, which use unroll 8, width 2, no
+ * prefetch and target_waves 2048. */
 void red_default_cols_policy(red_cols_policy *p);
 red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_cols_policy *p, hipStream_t stream);

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
     for (int w = 0; w < CW; ++w)
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc[w][i] = Op::identity();
-    if (c0 < cols) {
+    if (c0 < cols && q < group) {  // lanes past the last whole row group of a load stay idle
         size_t off[CW];  // in V units from the lane's column-0 vector
 #pragma unroll
         for (int w = 0; w < CW; ++w) off[w] = c0 + w * span < cols ? w * (size_t)ngroups : 0;
@@ -141,10 +141,21 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
         }
     }
     // Packed rows (CW == 1): lane g collects lanes g + ngroups, g + 2*ngroups,
-    // ... in a fixed order (all lanes take part in the shuffles).
-    for (unsigned int sh = kWave / 2; sh >= ngroups; sh >>= 1) {
+    // ... in a fixed order (all lanes take part in the shuffles): a halving
+    // tree when ngroups divides 64, else one lane after another.
+    if ((kWave % ngroups) == 0) {
+        for (unsigned int sh = kWave / 2; sh >= ngroups; sh >>= 1) {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) acc[0][i] = Op::combine(acc[0][i], __shfl_down(acc[0][i], sh, kWave));
+            for (int i = 0; i < VEC; ++i) acc[0][i] = Op::combine(acc[0][i], __shfl_down(acc[0][i], sh, kWave));
+        }
+    } else {
+        for (size_t m = 1; m < group; ++m) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                const acc_t t = __shfl(acc[0][i], (int)(lane + m * ngroups) % kWave, kWave);
+                if (q == 0) acc[0][i] = Op::combine(acc[0][i], t);
+            }
+        }
     }
     if (q == 0) {
 #pragma unroll
@@ -233,7 +244,14 @@ static hipError_t cols_vw(const typename Op::elem_t* x, size_t rows, size_t cols
 template <class Op>
 static hipError_t cols_op(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, const ColsLaunch& L, const ColsPolicy& p, hipStream_t stream) {
-    if (L.vec != 4) return cols_vw<Op, 1, 1>(x, rows, cols, ld, out, L, p, stream);
+    if (L.vec != 4) {
+        switch (L.width) {
+            case 1: return cols_vw<Op, 1, 1>(x, rows, cols, ld, out, L, p, stream);
+            case 2: return cols_vw<Op, 1, 2>(x, rows, cols, ld, out, L, p, stream);
+            case 4: return cols_vw<Op, 1, 4>(x, rows, cols, ld, out, L, p, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (L.width) {
         case 1: return cols_vw<Op, 4, 1>(x, rows, cols, ld, out, L, p, stream);
         case 2: return cols_vw<Op, 4, 2>(x, rows, cols, ld, out, L, p, stream);

@@ -49,9 +49,9 @@ struct RowsLaunch {
     int grid;
     unsigned int split_gx;
     void* partials;
-    int short_vpl;    // > 0: the short-row kernel with this many vectors per lane per row
-    int packed_log2l; // with packed_v > 0: the packed-row kernel, 2^packed_log2l lanes per row
-    int packed_v;     //   and up to packed_v vectors per lane per row
+    int packed_log2l;   // with packed_v > 0: the packed-row kernel, 2^packed_log2l lanes per row,
+    int packed_v;       //   up to packed_v units per lane per row,
+    int packed_scalar;  //   units of one element (1) or of one 16-byte vector (0)
 };
 constexpr size_t kMaxSplitPartials = 32768;
 

@@ -188,6 +188,11 @@ red_status get_scratch(int dev, hipStream_t stream, size_t bytes, void** out) {
 // 2 rows at a time, without prefetch (256 x 1M: 5.9 -> 7.1 TB/s).
 constexpr libred::ColsPolicy kDefaultCols = {8, 1, 512, 0, 1, 1};
 constexpr libred::ColsPolicy kWideCols = {2, 1, 1024, 0, 4, 0};
+// Columns read one element per lane (rows not 16-byte aligned, or cols or ld
+// not a multiple of 4) with at least 64 of them: two loads per row per lane,
+// 2048 waves (a sweep over 4097, 1001, 257 and 65 columns: 2.3-2.8 ->
+// 3.4-5.3 TB/s against the vector default).
+constexpr libred::ColsPolicy kScalarCols = {8, 1, 2048, 0, 2, 0};
 
 libred::ColsPolicy to_cols(const red_cols_policy* p) {
     if (!p) return kDefaultCols;
@@ -282,28 +287,25 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (st != RED_OK) return st;
 
     libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0};
-    // Rows of at most 128 vectors (512 floats) go to a short-row kernel
-    // unless the policy turns that off: the packed one when every row starts
-    // 16-byte aligned and holds whole vectors, else one wave per row with
-    // 16 / v rows loaded at a time.
-    const size_t nv = cols / 4;
-    if (p.short_rows == 0 && cols > 0 && nv <= 128) {
-        size_t per_trip;
-        if (aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0) {
-            int lg = 0;
-            while ((1u << lg) < nv && lg < 4) ++lg;  // lanes per row: pow2ceil(nv), at most 16
-            const size_t lanes = (size_t)1 << lg;
-            const size_t per_lane = (nv + lanes - 1) / lanes;
-            L.packed_log2l = lg;
-            L.packed_v = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
-            const size_t rows_per_group = 64 / lanes;
-            const size_t groups = (rows + rows_per_group - 1) / rows_per_group;
-            per_trip = (groups + (16 / L.packed_v) - 1) / (16 / L.packed_v);
-        } else {
-            L.short_vpl = nv <= 64 ? 1 : 2;
-            per_trip = (rows + (16 / L.short_vpl) - 1) / (16 / L.short_vpl);
-        }
-        L.grid = (int)(per_trip < (size_t)p.max_blocks ? per_trip : (size_t)p.max_blocks);
+    // Rows of at most 512 floats go to the packed-row kernel unless the
+    // policy turns that off: 16-byte units when every row starts 16-byte
+    // aligned and holds whole vectors (segments of up to 16 lanes), else
+    // single elements (segments of up to 64 lanes).
+    if (p.short_rows == 0 && cols > 0 && cols <= 512) {
+        const bool vec = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
+        const size_t units = vec ? cols / 4 : cols;
+        const int max_lg = vec ? 4 : 6;
+        int lg = 0;
+        while ((1u << lg) < units && lg < max_lg) ++lg;  // lanes per row: pow2ceil(units), capped
+        const size_t lanes = (size_t)1 << lg;
+        const size_t per_lane = (units + lanes - 1) / lanes;
+        L.packed_log2l = lg;
+        L.packed_v = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : per_lane <= 4 ? 4 : 8;
+        L.packed_scalar = vec ? 0 : 1;
+        const size_t groups = (rows + (64 / lanes) - 1) / (64 / lanes);
+        const size_t per_trip_groups = (size_t)(vec ? 16 : 32) / (size_t)L.packed_v;
+        const size_t waves = (groups + per_trip_groups - 1) / per_trip_groups;
+        L.grid = (int)(waves < (size_t)p.max_blocks ? waves : (size_t)p.max_blocks);
         const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
         if (e != hipSuccess) return fail(e, RED_ERR_HIP);
         return RED_OK;
@@ -360,8 +362,9 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // into each load.
     const size_t groups = cols / (size_t)L.vec;
     L.ngroups = 64;
-    if (groups < 64 && 64 % groups == 0) L.ngroups = (unsigned int)groups;
-    L.width = (L.vec == 4 && L.ngroups == 64) ? p.width : 1;
+    if (groups < 64) L.ngroups = (unsigned int)groups;
+    if (pol == nullptr && L.vec == 1 && L.ngroups == 64) p = kScalarCols;
+    L.width = L.ngroups == 64 ? p.width : 1;
     const size_t per_block = (size_t)L.ngroups * L.vec * L.width;
     L.ncb = (cols + per_block - 1) / per_block;
     size_t nchunks = 1;

@@ -200,17 +200,25 @@ __global__ __launch_bounds__(BLOCK) void rows_prefetch_kernel(const typename Op:
     }
 }
 
-// Packed short rows: when every row starts on a 16-byte boundary and holds
-// whole vectors only (x 16-byte aligned, cols and ld multiples of 4), a row of
-// nvec <= 128 vectors gets a segment of L = 2^LOG2L <= 16 lanes, lane j taking
-// the row's vectors j, j + L, ..., up to V of them, so one load covers
-// P = 64 / L rows. Each lane folds its vectors, the L lanes of a segment are
-// combined with the first LOG2L steps of the DPP wave reduce (quad_perm,
-// row_half_mirror, row_mirror: after them every lane of the segment holds
-// the segment's total), and lane j == 0 stores the row. A wave takes groups
-// of P rows w, w + G, w + 2G, ... (G = grid size), U = 16 / V groups per trip
-// with all their loads issued first, and the next trip's loads already in
-// flight.
+// Packed short rows (at most 512 floats): a row gets a segment of
+// L = 2^LOG2L lanes, lane j taking the row's load units j, j + L, ..., up to
+// V of them, so one load instruction covers P = 64 / L rows. A unit is a
+// 16-byte vector when every row starts on a 16-byte boundary and holds whole
+// vectors (x 16-byte aligned, cols and ld multiples of 4; L <= 16), else one
+// element (L <= 64), which serves rows of any width and alignment. Each lane
+// folds its units, the L lanes of a segment are combined with the first
+// LOG2L steps of the DPP wave reduce, and the segment's leader stores the
+// row. A wave takes groups of P rows w, w + G, w + 2G, ... (G = grid size),
+// U groups per trip (16 vectors or 32 elements in flight per lane) with all
+// their loads issued first, and the next trip's loads issued before the
+// current trip is reduced and stored.
+//
+// After the first four steps (quad_perm x 2, row_half_mirror, row_mirror)
+// every lane of a 16-lane row holds the row's total; row_bcast:15 into rows 1
+// and 3 then leaves 32-lane totals in lanes 16-31 and 48-63, and
+// row_bcast:31 into rows 2 and 3 leaves the 64-lane total in lanes 48-63. So
+// the leader is lane 0 of a segment of up to 16 lanes and the last lane of a
+// 32- or 64-lane segment.
 template <class Op, int LOG2L>
 __device__ __forceinline__ typename Op::acc_t segment_reduce(typename Op::acc_t v) {
     using T = typename Op::acc_t;
@@ -219,30 +227,35 @@ __device__ __forceinline__ typename Op::acc_t segment_reduce(typename Op::acc_t 
     if constexpr (LOG2L >= 2) v = Op::combine(v, dpp_move<0x4E, 0xF>(id, v));   // quad_perm:[2,3,0,1]
     if constexpr (LOG2L >= 3) v = Op::combine(v, dpp_move<0x141, 0xF>(id, v));  // row_half_mirror
     if constexpr (LOG2L >= 4) v = Op::combine(v, dpp_move<0x140, 0xF>(id, v));  // row_mirror
+    if constexpr (LOG2L >= 5) v = Op::combine(v, dpp_move<0x142, 0xA>(id, v));  // row_bcast:15 -> rows 1, 3
+    if constexpr (LOG2L >= 6) v = Op::combine(v, dpp_move<0x143, 0xC>(id, v));  // row_bcast:31 -> rows 2, 3
     return v;
 }
 
-template <class Op, int LOG2L, int V, bool NT>
+template <class Op, int LOG2L, int V, bool SCALAR, bool NT>
 __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, size_t ld,
                                                             typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
-    using vec_t = typename Op::vec_t;
+    using unit_t = std::conditional_t<SCALAR, typename Op::elem_t, typename Op::vec_t>;
+    constexpr size_t E = SCALAR ? 1 : Op::kPerVec;  // elements per unit
     constexpr int L = 1 << LOG2L;
     constexpr int P = kWave / L;
-    constexpr int U = V >= 16 ? 1 : 16 / V;
+    constexpr int U = (SCALAR ? 32 : 16) / V;
     const int lane = threadIdx.x;
     const size_t q = (size_t)(lane >> LOG2L);
     const size_t j = (size_t)(lane & (L - 1));
-    const size_t nvec = cols / Op::kPerVec;
-    const size_t ldv = ld / Op::kPerVec;
-    const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x);
+    const bool leader = LOG2L <= 4 ? j == 0 : j == (size_t)L - 1;
+    const size_t nunits = cols / E;
+    const size_t ldu = ld / E;
+    const unit_t* __restrict__ xu = reinterpret_cast<const unit_t*>(x);
     const size_t G = gridDim.x;
     const size_t ngroups = (rows + P - 1) / P;
-    // A lane with no vector to read (past the last row, or past its row's
-    // last vector) reads vector 0 of the matrix instead and folds nothing:
-    // no load sits under a lane mask.
-    auto load_trip = [&](vec_t (&v)[U][V], size_t g0) {
+    // A lane with nothing to read (past the last row, or past its row's last
+    // unit) reads unit 0 of the matrix instead and folds nothing: no load
+    // sits under a lane mask (that would make the compiler wait for every
+    // earlier load first).
+    auto load_trip = [&](unit_t (&v)[U][V], size_t g0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t r = (g0 + (size_t)u * G) * P + q;
@@ -250,11 +263,11 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
 #pragma unroll
             for (int k = 0; k < V; ++k) {
                 const size_t i = j + (size_t)k * L;
-                v[u][k] = load_vec<NT>(xv + (live && i < nvec ? r * ldv + i : 0));
+                v[u][k] = load_vec<NT>(xu + (live && i < nunits ? r * ldu + i : 0));
             }
         }
     };
-    auto reduce_trip = [&](const vec_t (&v)[U][V], size_t g0) {
+    auto reduce_trip = [&](const unit_t (&v)[U][V], size_t g0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const size_t g = g0 + (size_t)u * G;
@@ -265,11 +278,16 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
 #pragma unroll
             for (int k = 0; k < V; ++k) {
                 const size_t i = j + (size_t)k * L;
-                if (live && i < nvec) fold_vec<Op>(acc, v[u][k], i * Op::kPerVec);
+                if (live && i < nunits) {
+                    if constexpr (SCALAR)
+                        acc[k & 3] = Op::combine(acc[k & 3], Op::lift(v[u][k], i));
+                    else
+                        fold_vec<Op>(acc, v[u][k], i * E);
+                }
             }
             acc_t a = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
             a = segment_reduce<Op, LOG2L>(a);
-            if (live && j == 0) out[r] = Op::finish(a);
+            if (live && leader) out[r] = Op::finish(a);
         }
     };
     // Trips alternate between two register buffers: the next trip's loads
@@ -278,7 +296,7 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
     // order, waiting for them never waits for the stores that follow).
     size_t g0 = blockIdx.x;  // wave-uniform
     if (g0 >= ngroups) return;
-    vec_t a[U][V], b[U][V];
+    unit_t a[U][V], b[U][V];
     load_trip(a, g0);
     while (true) {
         size_t g1 = g0 + G * U;
@@ -291,72 +309,6 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
         reduce_trip(b, g0);
         if (g1 >= ngroups) break;
         g0 = g1;
-    }
-}
-
-// Short rows that the packed kernel cannot take (at most 64 * VPL vectors
-// each, VPL = 1 or 2, with heads and tails): one wave still reduces each
-// row, but it takes RB = 16 / VPL of its rows at a time and issues the loads
-// of all of them (VPL vectors per lane per row, and the scalar head and tail)
-// before it folds and reduces any, so 16 loads stay in flight per wave
-// instead of one row's. Single-wave blocks; wave w takes rows w, w + G,
-// w + 2G, ... (G = grid size), RB of them per trip. Rows past the end and
-// lanes past a row's end fold nothing.
-template <class Op, int VPL, bool NT>
-__global__ __launch_bounds__(kWave) void rows_short_kernel(const typename Op::elem_t* __restrict__ x,
-                                                           size_t rows, size_t cols, size_t ld,
-                                                           typename Op::out_t* __restrict__ out) {
-    using acc_t = typename Op::acc_t;
-    using vec_t = typename Op::vec_t;
-    using elem_t = typename Op::elem_t;
-    constexpr int RB = 16 / VPL;
-    const int lane = threadIdx.x;
-    const size_t G = gridDim.x;
-    for (size_t r0 = blockIdx.x; r0 < rows; r0 += G * RB) {  // wave-uniform
-        vec_t v[RB][VPL];
-        elem_t hv[RB], tv[RB];
-        size_t head[RB], nvec[RB], tail0[RB];
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            const size_t r = r0 + (size_t)b * G;
-            const bool live = r < rows;
-            const elem_t* row = x + (live ? r : 0) * ld;
-            head[b] = live ? head_elems(row, sizeof(elem_t), cols) : 0;
-            nvec[b] = live ? (cols - head[b]) / Op::kPerVec : 0;
-            tail0[b] = head[b] + (size_t)Op::kPerVec * nvec[b];
-            const vec_t* rv = reinterpret_cast<const vec_t*>(row + head[b]);
-            // Loads are never under a lane mask (that would make the compiler
-            // wait for every earlier load first): a lane with nothing to read
-            // reads the row's vector 0, or element 0 (row 0 for a row past the
-            // end), and folds nothing. A row without a whole vector skips the
-            // vector loads (a wave-uniform branch).
-            if (nvec[b] > 0) {
-#pragma unroll
-                for (int k = 0; k < VPL; ++k) {
-                    const size_t i = (size_t)k * kWave + lane;
-                    v[b][k] = load_vec<NT>(rv + (i < nvec[b] ? i : 0));
-                }
-            }
-            hv[b] = row[(size_t)lane < head[b] ? (size_t)lane : 0];
-            tv[b] = row[(size_t)lane < cols - tail0[b] ? tail0[b] + lane : 0];
-        }
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-            const size_t r = r0 + (size_t)b * G;
-            if (r >= rows) break;  // wave-uniform
-            acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
-#pragma unroll
-            for (int k = 0; k < VPL; ++k) {
-                const size_t i = (size_t)k * kWave + lane;
-                if (i < nvec[b]) fold_vec<Op>(acc, v[b][k], head[b] + i * Op::kPerVec);
-            }
-            if ((size_t)lane < head[b]) acc[0] = Op::combine(acc[0], Op::lift(hv[b], lane));
-            if ((size_t)lane < cols - tail0[b])
-                acc[1] = Op::combine(acc[1], Op::lift(tv[b], tail0[b] + lane));
-            acc_t w = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
-            w = wave_reduce<Op>(w);
-            if (lane == 0) out[r] = Op::finish(w);
-        }
     }
 }
 
@@ -455,40 +407,52 @@ static hipError_t rows_split_u(const typename Op::elem_t* x, size_t rows, size_t
     return hipGetLastError();
 }
 
-template <class Op, int LOG2L, int V>
+template <class Op, int LOG2L, int V, bool SCALAR>
 static hipError_t rows_packed_lv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                                  typename Op::out_t* out, int grid, bool nt, hipStream_t stream) {
     if (nt)
-        hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, true>), dim3(grid), dim3(kWave), 0, stream, x, rows,
-                           cols, ld, out);
+        hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, SCALAR, true>), dim3(grid), dim3(kWave), 0, stream,
+                           x, rows, cols, ld, out);
     else
-        hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, false>), dim3(grid), dim3(kWave), 0, stream, x, rows,
-                           cols, ld, out);
+        hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, SCALAR, false>), dim3(grid), dim3(kWave), 0, stream,
+                           x, rows, cols, ld, out);
     return hipGetLastError();
 }
 
-template <class Op, int LOG2L>
+// Several units per lane only with the widest segment (16 lanes for vectors,
+// 64 for elements); narrower segments always take one.
+template <class Op, int LOG2L, bool SCALAR>
 static hipError_t rows_packed_v(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                                 typename Op::out_t* out, const RowsLaunch& L, bool nt, hipStream_t stream) {
-    switch (L.packed_v) {
-        case 1: return rows_packed_lv<Op, LOG2L, 1>(x, rows, cols, ld, out, L.grid, nt, stream);
-        case 2: return rows_packed_lv<Op, LOG2L, 2>(x, rows, cols, ld, out, L.grid, nt, stream);
-        case 4: return rows_packed_lv<Op, LOG2L, 4>(x, rows, cols, ld, out, L.grid, nt, stream);
-        case 8: return rows_packed_lv<Op, LOG2L, 8>(x, rows, cols, ld, out, L.grid, nt, stream);
-        default: return hipErrorInvalidValue;
+    if constexpr (LOG2L == (SCALAR ? 6 : 4)) {
+        switch (L.packed_v) {
+            case 1: return rows_packed_lv<Op, LOG2L, 1, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
+            case 2: return rows_packed_lv<Op, LOG2L, 2, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
+            case 4: return rows_packed_lv<Op, LOG2L, 4, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
+            case 8: return rows_packed_lv<Op, LOG2L, 8, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
+            default: return hipErrorInvalidValue;
+        }
+    } else {
+        if (L.packed_v != 1) return hipErrorInvalidValue;
+        return rows_packed_lv<Op, LOG2L, 1, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
     }
 }
 
-template <class Op>
-static hipError_t rows_packed_l(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+template <class Op, bool SCALAR>
+static hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                                 typename Op::out_t* out, const RowsLaunch& L, bool nt, hipStream_t stream) {
     switch (L.packed_log2l) {
-        case 0: return rows_packed_v<Op, 0>(x, rows, cols, ld, out, L, nt, stream);
-        case 1: return rows_packed_v<Op, 1>(x, rows, cols, ld, out, L, nt, stream);
-        case 2: return rows_packed_v<Op, 2>(x, rows, cols, ld, out, L, nt, stream);
-        case 3: return rows_packed_v<Op, 3>(x, rows, cols, ld, out, L, nt, stream);
-        case 4: return rows_packed_v<Op, 4>(x, rows, cols, ld, out, L, nt, stream);
-        default: return hipErrorInvalidValue;
+        case 0: return rows_packed_v<Op, 0, SCALAR>(x, rows, cols, ld, out, L, nt, stream);
+        case 1: return rows_packed_v<Op, 1, SCALAR>(x, rows, cols, ld, out, L, nt, stream);
+        case 2: return rows_packed_v<Op, 2, SCALAR>(x, rows, cols, ld, out, L, nt, stream);
+        case 3: return rows_packed_v<Op, 3, SCALAR>(x, rows, cols, ld, out, L, nt, stream);
+        case 4: return rows_packed_v<Op, 4, SCALAR>(x, rows, cols, ld, out, L, nt, stream);
+        default:
+            if constexpr (SCALAR) {
+                if (L.packed_log2l == 5) return rows_packed_v<Op, 5, SCALAR>(x, rows, cols, ld, out, L, nt, stream);
+                if (L.packed_log2l == 6) return rows_packed_v<Op, 6, SCALAR>(x, rows, cols, ld, out, L, nt, stream);
+            }
+            return hipErrorInvalidValue;
     }
 }
 
@@ -496,22 +460,9 @@ template <class Op>
 static hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, const RowsLaunch& L, const RowsPolicy& p,
                           hipStream_t stream) {
-    if (L.packed_v > 0) return rows_packed_l<Op>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);
-    if (L.short_vpl > 0) {
-        const bool nt = p.nontemporal != 0;
-        const dim3 grid((unsigned int)L.grid);
-        switch (L.short_vpl) {
-            case 1:
-                if (nt) hipLaunchKernelGGL((rows_short_kernel<Op, 1, true>), grid, dim3(kWave), 0, stream, x, rows, cols, ld, out);
-                else hipLaunchKernelGGL((rows_short_kernel<Op, 1, false>), grid, dim3(kWave), 0, stream, x, rows, cols, ld, out);
-                break;
-            case 2:
-                if (nt) hipLaunchKernelGGL((rows_short_kernel<Op, 2, true>), grid, dim3(kWave), 0, stream, x, rows, cols, ld, out);
-                else hipLaunchKernelGGL((rows_short_kernel<Op, 2, false>), grid, dim3(kWave), 0, stream, x, rows, cols, ld, out);
-                break;
-            default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
+    if (L.packed_v > 0) {
+        if (L.packed_scalar) return rows_packed_s<Op, true>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);
+        return rows_packed_s<Op, false>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);
     }
     if (L.split_gx > 0) {
         const bool nt = p.nontemporal != 0;
