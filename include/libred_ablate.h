@@ -74,11 +74,23 @@ typedef struct red_flat_policy {
  * 1 = never, 2 = whenever a row holds at least two tiles of 64*unroll
  * vectors; `prefetch` (0 or 1, one wave per row only): keep the next
  * tile of 64*unroll vectors in flight while folding the current one, across
- * row boundaries; and `short_rows`: 0 = rows of at most 512 floats go to a
- * kernel that gives each row a segment of up to 16 (16-byte units, rows
- * 16-byte aligned) or 64 lanes (single elements, any alignment), so that one
- * load covers several rows (`block`, `unroll` and `prefetch` do not apply
- * there, `max_blocks` caps its grid), 1 = never. */
+ * row boundaries; and `short_rows`, the kernels for short rows (`block`,
+ * `unroll` and `prefetch` do not apply to them, `max_blocks` caps their
+ * grid):
+ *   0  the library's choice: rows of fewer than 1024 floats of a contiguous
+ *      (ld == cols), 16-byte aligned matrix go to the LDS-staged kernel, which
+ *      loads tiles of whole rows as 16-byte vectors whatever the row length
+ *      and then reduces each row from LDS with a power of two of lanes;
+ *      other rows of at most 512 floats go to the packed kernel, which gives
+ *      each row a segment of up to 16 lanes (16-byte units, rows 16-byte
+ *      aligned) or 64 lanes (single elements), so that one load covers
+ *      several rows;
+ *   1  neither;
+ *   2  the packed kernel only (rows of at most 512 floats);
+ *   3-9  the LDS-staged kernel with 2^(short_rows - 3) lanes per row where it
+ *      applies (contiguous, 16-byte aligned, at least 4 elements, and 4 rows
+ *      of an odd width, 2 of a width of 2 mod 4, or 1 row, fit 4096 floats),
+ *      else as 2. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
@@ -93,7 +105,12 @@ typedef struct red_rows_policy {
  * 4, 8 or 16), `nontemporal`, `target_waves` (the rows are cut into chunks
  * until about this many single-wave blocks run), `vec`: 0 = four adjacent
  * columns per lane when x is 16-byte aligned and cols and ld are multiples
- * of 4, else one; 1 = always one; 4 = same as 0; and `width` (1, 2 or 4):
+ * of 4; a contiguous (ld == cols), 16-byte aligned matrix of another width
+ * is read as m consecutive rows at a time (m a multiple of 2 or 4 that makes
+ * the m-row spans start 16-byte aligned, chosen up to 16 to use the most
+ * lanes) with four columns per lane, and a second pass adds each column's
+ * m partial columns and the last rows % m rows; else one column per lane;
+ * 1 = always one; 4 = same as 0; and `width` (1, 2 or 4):
  * with at least 64 column groups, each row is read by `width` loads per lane,
  * so a wave reads width x 1 KiB (four columns per lane) or width x 256 bytes
  * (one column per lane) of a row at once (with fewer groups, 1 is used);

@@ -191,6 +191,40 @@ __global__ __launch_bounds__(kColsCombineBlock) void cols_combine_kernel(
     if (lane == 0) out[c] = Op::finish(v);
 }
 
+// Pass 2 of a folded launch (see ColsLaunch): one block per real column c.
+// Its items are j = k * m + r (chunk k, fold row r, partial of view column
+// r * cols + c), dealt to the threads in rounds of 4 * kColsCombineBlock (4
+// loads in flight per thread, each from a clamped index so no load is
+// predicated), then the tail rows, lane-strided; then the block reduce. The
+// order is fixed, so the result is deterministic.
+template <class Op>
+__global__ __launch_bounds__(kColsCombineBlock) void cols_fold_combine_kernel(
+    const typename Op::acc_t* __restrict__ partials, unsigned int nchunks, size_t vcols, size_t cols,
+    unsigned int m, const typename Op::elem_t* __restrict__ tail, unsigned int tail_rows,
+    typename Op::out_t* __restrict__ out) {
+    using acc_t = typename Op::acc_t;
+    __shared__ acc_t lds[kColsCombineBlock / kWave];
+    const size_t c = blockIdx.x;
+    const unsigned int total = nchunks * m;
+    acc_t v = Op::identity();
+    for (unsigned int j0 = 0; j0 < total; j0 += 4 * kColsCombineBlock) {
+        acc_t t[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const unsigned int j = j0 + u * kColsCombineBlock + threadIdx.x;
+            const unsigned int jj = j < total ? j : total - 1;
+            t[u] = partials[(size_t)(jj / m) * vcols + (size_t)(jj % m) * cols + c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (j0 + u * kColsCombineBlock + threadIdx.x < total) v = Op::combine(v, t[u]);
+    }
+    for (unsigned int t = threadIdx.x; t < tail_rows; t += kColsCombineBlock)
+        v = Op::combine(v, Op::lift(tail[(size_t)t * cols + c], 0));
+    v = block_reduce<Op, kColsCombineBlock>(v, lds);
+    if (threadIdx.x == 0) out[c] = Op::finish(v);
+}
+
 bool cols_policy_supported(const ColsPolicy& p) {
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     const bool w = p.width == 1 || p.width == 2 || p.width == 4;
@@ -204,7 +238,7 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
                             typename Op::out_t* out, const ColsLaunch& L, bool nt, hipStream_t stream) {
     auto* partials = static_cast<typename Op::acc_t*>(L.partials);
     const dim3 grid((unsigned int)(L.ncb * L.nchunks));
-    typename Op::out_t* direct = L.nchunks == 1 ? out : nullptr;
+    typename Op::out_t* direct = (L.nchunks == 1 && L.fold_m <= 1) ? out : nullptr;
     if (nt)
         hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF>), grid, dim3(kWave), 0, stream, x,
                            rows, cols, ld, L.ncb, L.ngroups, partials, direct);
@@ -212,8 +246,16 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
         hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF>), grid, dim3(kWave), 0, stream, x,
                            rows, cols, ld, L.ncb, L.ngroups, partials, direct);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || L.nchunks == 1) return e;
     const size_t W = kColsCombineBlock / kWave;
+    if (e != hipSuccess) return e;
+    if (L.fold_m > 1) {
+        hipLaunchKernelGGL((cols_fold_combine_kernel<Op>), dim3((unsigned int)L.real_cols), dim3(kColsCombineBlock),
+                           0, stream, partials, (unsigned int)L.nchunks, cols, L.real_cols,
+                           (unsigned int)L.fold_m, static_cast<const typename Op::elem_t*>(L.tail),
+                           (unsigned int)L.tail_rows, out);
+        return hipGetLastError();
+    }
+    if (L.nchunks == 1) return e;
     hipLaunchKernelGGL((cols_combine_kernel<Op>), dim3((unsigned int)((cols + W - 1) / W)),
                        dim3(kColsCombineBlock), 0, stream, partials, L.nchunks, cols, out);
     return hipGetLastError();

@@ -52,6 +52,9 @@ struct RowsLaunch {
     int packed_log2l;   // with packed_v > 0: the packed-row kernel, 2^packed_log2l lanes per row,
     int packed_v;       //   up to packed_v units per lane per row,
     int packed_scalar;  //   units of one element (1) or of one 16-byte vector (0)
+    int staged_u;       // > 0: the LDS-staged kernel, tiles of staged_rows rows (at most
+    unsigned int staged_rows;  //   256 * staged_u elements), 2^staged_log2s lanes per row
+    int staged_log2s;
 };
 constexpr size_t kMaxSplitPartials = 32768;
 
@@ -91,6 +94,15 @@ struct ColsLaunch {
     int width;
     unsigned int ngroups;
     void* partials;
+    // fold_m > 1: the launch runs on a contiguous matrix viewed with fold_m
+    // consecutive rows as one (rows / fold_m rows of fold_m * real_cols
+    // columns, so rows start 16-byte aligned); the partials of the fold_m
+    // view columns of each real column are then added, and the tail_rows
+    // (< fold_m) real rows after the view, starting at `tail`, last.
+    int fold_m;
+    size_t real_cols;
+    size_t tail_rows;
+    const void* tail;
 };
 
 bool flat_policy_supported(const FlatPolicy& p);

@@ -286,12 +286,40 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
 
-    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0};
+    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0};
+    // Rows of fewer than 1024 floats of a contiguous, 16-byte aligned matrix
+    // go to the LDS-staged kernel (short_rows 0), or do so with
+    // 2^(short_rows - 3) lanes per row (short_rows 3-9), as long as a tile
+    // of 16-byte aligned rows fits 4096 floats.
+    const bool contiguous = ld == cols || rows == 1;
+    const size_t fold = cols % 4 == 0 ? 1 : cols % 2 == 0 ? 2 : 4;  // rows per 16-byte aligned span
+    const bool staged_ok = contiguous && aligned(x, 16) && cols > 0 && rows * cols >= 4 && fold * cols <= 4096;
+    const bool staged_default = p.short_rows == 0 && cols < 1024;
+    if (staged_ok && (staged_default || p.short_rows >= 3)) {
+        L.staged_u = fold * cols <= 1024 ? 4 : fold * cols <= 2048 ? 8 : 16;
+        L.staged_rows = (unsigned int)((256 * (size_t)L.staged_u) / (fold * cols) * fold);
+        if (p.short_rows >= 3) {
+            L.staged_log2s = p.short_rows - 3;
+        } else {
+            // Lanes per row: the largest power of two up to cols / 8 (below
+            // 64 floats) or cols / 16 (up to 512), so a lane adds 8-16
+            // elements a row; longer rows take the whole wave.
+            const size_t per = cols < 64 ? 8 : 16;
+            int lg = 0;
+            while (lg < 6 && ((size_t)2 << lg) <= cols / per) ++lg;
+            L.staged_log2s = cols > 512 ? 6 : lg;
+        }
+        const size_t tiles = (rows + L.staged_rows - 1) / L.staged_rows;
+        L.grid = (int)(tiles < (size_t)p.max_blocks ? tiles : (size_t)p.max_blocks);
+        const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
+        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+        return RED_OK;
+    }
     // Rows of at most 512 floats go to the packed-row kernel unless the
-    // policy turns that off: 16-byte units when every row starts 16-byte
-    // aligned and holds whole vectors (segments of up to 16 lanes), else
-    // single elements (segments of up to 64 lanes).
-    if (p.short_rows == 0 && cols > 0 && cols <= 512) {
+    // policy turns that off (short_rows 1): 16-byte units when every row
+    // starts 16-byte aligned and holds whole vectors (segments of up to 16
+    // lanes), else single elements (segments of up to 64 lanes).
+    if (p.short_rows != 1 && cols > 0 && cols <= 512) {
         const bool vec = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
         const size_t units = vec ? cols / 4 : cols;
         const int max_lg = vec ? 4 : 6;
@@ -337,6 +365,30 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     return RED_OK;
 }
 
+// Fraction of a column kernel's lanes that read data when the (view) rows
+// hold `groups` 16-byte column groups: below 64 groups a wave packs
+// 64 / groups rows per load; from 64 up each block takes 64 groups, the last
+// block of a row only what is left.
+double cols_lane_use(size_t groups) {
+    if (groups < 64) return (double)(groups * (64 / groups)) / 64.0;
+    return (double)groups / (double)(64 * ((groups + 63) / 64));
+}
+
+// Rows per view row for a contiguous matrix whose width is not a multiple of
+// 4 (1 = no fold): among the multiples m of 4 / gcd(cols, 4) up to 16 (and
+// at most rows), the one whose view uses the most lanes, the smallest on a
+// tie. The second pass reads m partials per chunk, which caps m.
+size_t fold_rows(size_t rows, size_t cols) {
+    const size_t m0 = cols % 2 == 0 ? 2 : 4;
+    size_t best = 1;
+    double best_use = -1.0;
+    for (size_t m = m0; m <= 16 && m <= rows && cols * m <= RED_MAX_N; m += m0) {
+        const double use = cols_lane_use(m * cols / 4);
+        if (use > best_use + 1e-9) best_use = use, best = m;
+    }
+    return best;
+}
+
 template <class Launch>
 red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float* out,
                      const red_cols_policy* pol, hipStream_t stream, Launch launch) {
@@ -355,6 +407,27 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (st != RED_OK) return st;
 
     libred::ColsLaunch L;
+    L.fold_m = 1;
+    L.real_cols = cols;
+    L.tail_rows = 0;
+    L.tail = nullptr;
+    // A contiguous matrix whose width is not a multiple of 4 is viewed with
+    // m = 2 or 4 consecutive rows as one row of m * cols columns, so that
+    // every view row starts 16-byte aligned and four columns go per lane;
+    // pass 2 adds each real column's m view columns, then the last
+    // rows % m rows.
+    const size_t rows_real = rows, cols_real = cols;
+    if (p.vec != 1 && cols % 4 != 0 && ld == cols && aligned(x, 16)) {
+        const size_t m = fold_rows(rows, cols);
+        if (m > 1) {
+            L.fold_m = (int)m;
+            rows = rows_real / m;
+            cols = cols_real * m;
+            ld = cols;
+            L.tail_rows = rows_real - rows * m;
+            L.tail = x + rows * m * cols_real;
+        }
+    }
     const bool vec_ok = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
     L.vec = (p.vec != 1 && vec_ok) ? 4 : 1;
     if (pol == nullptr && L.vec == 4 && cols / 256 >= (size_t)kWideCols.target_waves) p = kWideCols;
@@ -378,7 +451,7 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     }
     L.nchunks = nchunks;
     L.partials = nullptr;
-    if (nchunks > 1) {
+    if (nchunks > 1 || L.fold_m > 1) {
         st = get_scratch(dev, stream, nchunks * cols * 8, &L.partials);
         if (st != RED_OK) return st;
     }

@@ -312,6 +312,101 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
     }
 }
 
+// Short rows of a contiguous matrix (ld == cols, x 16-byte aligned, at
+// least 4 elements in all), staged through LDS. The matrix is one flat
+// array; a tile is R consecutive rows, R a multiple of 4 / gcd(cols, 4) so
+// that every tile starts 16-byte aligned, and R * cols <= 256 * U elements.
+// A wave loads a tile as U 16-byte vectors per lane (coalesced whatever the
+// row length; the 1-3 elements of a last vector that runs past the end are
+// read one by one), stores it to LDS, and then reduces its rows 64 / S at a
+// time with S = 2^LOG2S lanes per row: lane s of a row adds elements s,
+// s + S, ... in order, then the segment reduce. Tiles are dealt round-robin
+// to the waves, and the next tile's loads are issued before the current tile
+// is reduced. A lane with no whole vector to read in a tile reads vector 0 of
+// the matrix instead (no load sits under a lane mask).
+template <class Op, int LOG2S, int U, bool NT>
+__global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::elem_t* __restrict__ x,
+                                                            size_t rows, size_t cols, unsigned int R,
+                                                            typename Op::out_t* __restrict__ out) {
+    using acc_t = typename Op::acc_t;
+    using elem_t = typename Op::elem_t;
+    using vec_t = typename Op::vec_t;
+    constexpr int S = 1 << LOG2S;
+    constexpr int P = kWave / S;
+    constexpr size_t E = Op::kPerVec;
+    __shared__ vec_t stage[kWave * U];
+    elem_t* lds = reinterpret_cast<elem_t*>(stage);
+    const unsigned int lane = threadIdx.x;
+    const unsigned int s = lane & (S - 1);
+    const bool leader = LOG2S <= 4 ? s == 0 : s == (unsigned int)S - 1;
+    const size_t total = rows * cols;
+    const size_t tile_elems = (size_t)R * cols;
+    const size_t ntiles = (rows + R - 1) / R;
+    const size_t G = gridDim.x;
+    const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x);
+    auto rows_in = [&](size_t t) -> unsigned int {  // rows of tile t (0 past the last tile)
+        return t + 1 < ntiles ? R : t + 1 == ntiles ? (unsigned int)(rows - t * R) : 0u;
+    };
+    auto count = [&](size_t t) -> size_t { return (size_t)rows_in(t) * cols; };
+    auto load_tile = [&](vec_t (&v)[U], size_t t) {
+        const size_t base = t * tile_elems / E;
+        const size_t nv = count(t) / E;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t i = lane + (size_t)u * kWave;
+            v[u] = load_vec<NT>(xv + (i < nv ? base + i : 0));
+        }
+    };
+    auto reduce_tile = [&](const vec_t (&v)[U], size_t t) {
+        const size_t cnt = count(t);
+#pragma unroll
+        for (int u = 0; u < U; ++u) stage[lane + u * kWave] = v[u];
+        const size_t whole = cnt / E * E;
+        if (whole < cnt && lane < cnt - whole) lds[whole + lane] = x[t * tile_elems + whole + lane];
+        __syncthreads();
+        const unsigned int rows_t = rows_in(t);
+        const unsigned int C = (unsigned int)cols;
+        for (unsigned int r0 = 0; r0 < rows_t; r0 += P) {
+            const unsigned int r = r0 + (lane >> LOG2S);
+            acc_t a = Op::identity();
+            if (r < rows_t) {
+                const elem_t* row = lds + r * C;
+                unsigned int j = s;
+                for (; j + 3 * S < C; j += 4 * S) {  // four LDS reads in flight
+                    const elem_t e0 = row[j], e1 = row[j + S], e2 = row[j + 2 * S], e3 = row[j + 3 * S];
+                    a = Op::combine(a, Op::lift(e0, j));
+                    a = Op::combine(a, Op::lift(e1, j + S));
+                    a = Op::combine(a, Op::lift(e2, j + 2 * S));
+                    a = Op::combine(a, Op::lift(e3, j + 3 * S));
+                }
+                for (; j < C; j += S) a = Op::combine(a, Op::lift(row[j], j));
+            }
+            a = segment_reduce<Op, LOG2S>(a);
+            if (r < rows_t && leader) out[t * R + r] = Op::finish(a);
+        }
+        __syncthreads();
+    };
+    // The next tile's loads are issued unconditionally (past the last tile
+    // every lane reads vector 0): loads under a branch would make the
+    // compiler wait for all of them before the stores to LDS.
+    size_t t0 = blockIdx.x;  // wave-uniform
+    if (t0 >= ntiles) return;
+    vec_t a[U], b[U];
+    load_tile(a, t0);
+    while (true) {
+        size_t t1 = t0 + G;
+        load_tile(b, t1);
+        reduce_tile(a, t0);
+        if (t1 >= ntiles) break;
+        t0 = t1;
+        t1 = t0 + G;
+        load_tile(a, t1);
+        reduce_tile(b, t0);
+        if (t1 >= ntiles) break;
+        t0 = t1;
+    }
+}
+
 // Split rows: block b is split s = b % gx of row r = b / gx.
 template <class Op, int UNROLL, bool NT>
 __global__ __launch_bounds__(kWave) void rows_split_kernel(const typename Op::elem_t* __restrict__ x,
@@ -349,7 +444,7 @@ bool rows_policy_supported(const RowsPolicy& p) {
     const bool b = p.block == 64 || p.block == 128 || p.block == 256 || p.block == 512;
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.max_blocks >= 1 && p.split >= 0 &&
-           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && (p.short_rows == 0 || p.short_rows == 1);
+           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.short_rows >= 0 && p.short_rows <= 9;
 }
 
 template <class Op, int BLOCK, int UNROLL>
@@ -456,10 +551,49 @@ static hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_
     }
 }
 
+template <class Op, int LOG2S, int U>
+static hipError_t rows_staged_su(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
+                                 const RowsLaunch& L, bool nt, hipStream_t stream) {
+    if (nt)
+        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true>), dim3(L.grid), dim3(kWave), 0, stream, x, rows,
+                           cols, L.staged_rows, out);
+    else
+        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false>), dim3(L.grid), dim3(kWave), 0, stream, x,
+                           rows, cols, L.staged_rows, out);
+    return hipGetLastError();
+}
+
+template <class Op, int LOG2S>
+static hipError_t rows_staged_s(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
+                                const RowsLaunch& L, bool nt, hipStream_t stream) {
+    switch (L.staged_u) {
+        case 4: return rows_staged_su<Op, LOG2S, 4>(x, rows, cols, out, L, nt, stream);
+        case 8: return rows_staged_su<Op, LOG2S, 8>(x, rows, cols, out, L, nt, stream);
+        case 16: return rows_staged_su<Op, LOG2S, 16>(x, rows, cols, out, L, nt, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <class Op>
+static hipError_t rows_staged(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
+                              const RowsLaunch& L, bool nt, hipStream_t stream) {
+    switch (L.staged_log2s) {
+        case 0: return rows_staged_s<Op, 0>(x, rows, cols, out, L, nt, stream);
+        case 1: return rows_staged_s<Op, 1>(x, rows, cols, out, L, nt, stream);
+        case 2: return rows_staged_s<Op, 2>(x, rows, cols, out, L, nt, stream);
+        case 3: return rows_staged_s<Op, 3>(x, rows, cols, out, L, nt, stream);
+        case 4: return rows_staged_s<Op, 4>(x, rows, cols, out, L, nt, stream);
+        case 5: return rows_staged_s<Op, 5>(x, rows, cols, out, L, nt, stream);
+        case 6: return rows_staged_s<Op, 6>(x, rows, cols, out, L, nt, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <class Op>
 static hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, const RowsLaunch& L, const RowsPolicy& p,
                           hipStream_t stream) {
+    if (L.staged_u > 0) return rows_staged<Op>(x, rows, cols, out, L, p.nontemporal != 0, stream);
     if (L.packed_v > 0) {
         if (L.packed_scalar) return rows_packed_s<Op, true>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);
         return rows_packed_s<Op, false>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);

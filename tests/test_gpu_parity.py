@@ -558,10 +558,13 @@ def test_sum_f64():
 ROW_SHAPES = [(1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
               (5, 64), (6, 65), (257, 4096), (2, 100_003), (4097, 3), (333, 1024), (50, 513),
               (1000, 4), (777, 16), (301, 32), (129, 128), (77, 200), (33, 8), (1025, 12), (70, 512),
-              (200, 33), (100, 511), (1000, 100), (3000, 2)]
+              (200, 33), (100, 511), (1000, 100), (3000, 2), (1, 3), (2, 2), (5, 6), (1001, 6),
+              (1, 2048), (2, 1023), (3, 1025), (300, 7), (9, 510), (20_001, 5), (5, 1021), (40, 700), (3, 1023)]
 ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1, max_blocks=3, short_rows=1),
                 dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
-                dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0))
+                dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0),
+                dict(short_rows=2), dict(short_rows=3), dict(short_rows=6, max_blocks=3),
+                dict(short_rows=9, nontemporal=0), dict(short_rows=5, max_blocks=1))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
@@ -634,7 +637,8 @@ def test_rows_split_long_rows(rows, cols):
 COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260), (4099, 1024, 1024),
               (33, 1000, 1001), (2, 4096, 4096), (0, 8, 8), (70_000, 12, 12), (5, 100_003, 100_003),
               (301, 1028, 1032), (77, 2304, 2304), (1000, 3, 3), (777, 33, 33), (500, 65, 65), (3000, 17, 17),
-              (200, 257, 257), (99, 1, 1), (4000, 20, 24), (64, 100, 100)]
+              (200, 257, 257), (99, 1, 1), (4000, 20, 24), (64, 100, 100),
+              (1001, 6, 6), (4001, 10, 10), (37, 2, 2), (20_003, 7, 7), (9, 4097, 4097), (5, 3, 3)]
 COL_POLICIES = (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=16, nontemporal=0),
                 dict(width=2), dict(width=4, unroll=2), dict(width=4, unroll=16, nontemporal=0, target_waves=7),
                 dict(prefetch=1), dict(prefetch=1, unroll=1, target_waves=7), dict(width=4, unroll=2, prefetch=1),
