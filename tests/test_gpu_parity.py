@@ -666,6 +666,70 @@ def test_cols(rows, cols, ld):
             assert np.array_equal(m.cpu().numpy(), M), p
 
 
+def _nonfinite_matrix(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    flat = a.reshape(-1)
+    k = max(1, flat.size // 97)
+    flat[rng.integers(0, flat.size, k)] = np.nan
+    flat[rng.integers(0, flat.size, k)] = np.inf
+    flat[rng.integers(0, flat.size, k)] = -np.inf
+    if rows > 2 and cols > 0:
+        a[1, :] = np.nan        # a row of NaN only: its max is -inf
+        a[2, :] = -np.inf
+    if rows > 0 and cols > 2:
+        a[:, 1] = np.nan        # a column of NaN only
+        a[:, 2] = np.inf
+    return a
+
+
+def _check_sums(got, S, A, what):
+    for i, (g, s_, a_) in enumerate(zip(got, S, A)):
+        assert oracle.sum_within_tolerance(g, s_, a_), (what, i, g, s_)
+
+
+@pytest.mark.parametrize("rows,cols,ld", [(300, 3, 3), (300, 16, 16), (50, 700, 700), (20, 4096, 4096),
+                                          (100, 7, 9), (100, 16, 20), (77, 33, 33), (5, 1021, 1021)])
+def test_rows_nonfinite(rows, cols, ld):
+    """NaN and infinities through every row kernel (LDS-staged, packed with
+    16-byte and element units, one wave per row): a sum is NaN or the
+    infinity exactly when the oracle's is; a max skips NaN (a NaN-only row
+    gives -inf)."""
+    a = _nonfinite_matrix(rows, cols, rows * 3 + cols)
+    full = np.full((rows, ld), 1e30, np.float32)
+    full[:, :cols] = a
+    S, A = oracle.rows_sum_f32(a)
+    M = oracle.rows_max_f32(a)
+    for p in (None, dict(short_rows=1), dict(short_rows=2)):
+        say(f"rows nonfinite {rows}x{cols} ld={ld} policy={p}")
+        x = device_view(full, 0)[:, :cols]
+        s_ = rl.red_rows_sum_f32(x, policy=p)
+        m_ = rl.red_rows_max_f32(x, policy=p)
+        torch.cuda.synchronize()
+        _check_sums(s_.cpu().numpy().astype(np.float64), S, A, p)
+        assert np.array_equal(m_.cpu().numpy(), M), p
+
+
+@pytest.mark.parametrize("rows,cols,ld", [(1000, 3, 3), (1000, 64, 64), (999, 7, 9), (97, 1031, 1031),
+                                          (4001, 10, 10), (500, 12, 12)])
+def test_cols_nonfinite(rows, cols, ld):
+    """NaN and infinities through every column path (four columns per lane,
+    folded m-row views, one column per lane, packed narrow matrices)."""
+    a = _nonfinite_matrix(rows, cols, rows * 5 + cols)
+    full = np.full((rows, ld), 1e30, np.float32)
+    full[:, :cols] = a
+    S, A = oracle.cols_sum_f32(a)
+    M = oracle.cols_max_f32(a)
+    for p in (None, dict(vec=1), dict(target_waves=7, unroll=1)):
+        say(f"cols nonfinite {rows}x{cols} ld={ld} policy={p}")
+        x = device_view(full, 0)[:, :cols]
+        s_ = rl.red_cols_sum_f32(x, policy=p)
+        m_ = rl.red_cols_max_f32(x, policy=p)
+        torch.cuda.synchronize()
+        _check_sums(s_.cpu().numpy().astype(np.float64), S, A, p)
+        assert np.array_equal(m_.cpu().numpy(), M), p
+
+
 def test_cols_mod7_exact():
     rows, cols = 4097, 1031
     say("cols mod7")
