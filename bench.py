@@ -10,6 +10,7 @@ combine launch. The line also carries the roofline of the streaming kernel
 host, and the other entry points at their own workloads.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+    python bench.py --ablation | --widths     (other measurements, one JSON line each)
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -74,6 +75,10 @@ def parse_args():
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the headline: time the five-rung ladder and the production "
                          "path on the 2^28 array, and the LDS bank probe; print one JSON line")
+    ap.add_argument("--widths", action="store_true",
+                    help="instead of the headline: time the row and column entry points on 1 GiB "
+                         "of f32 viewed as (2^28 // cols) x cols for a range of widths; print one "
+                         "JSON line")
     return ap.parse_args()
 
 
@@ -142,6 +147,44 @@ def run_ablation(args, torch, rl, W, timer, dev):
           flush=True)
 
 
+# Row lengths covering each row and column path: one float, odd widths (the
+# LDS-staged rows, folded column views), multiples of 4 (packed and staged
+# rows, four columns per lane), and long rows (one wave per row).
+WIDTHS = [1, 3, 4, 7, 16, 17, 33, 64, 65, 100, 256, 512, 1000, 1023, 4096, 4097]
+
+
+def run_widths(args, torch, rl, W, timer, dev):
+    name = "rows_f32_65536x4096"
+    log(f"generate {name}")
+    flat = torch.from_numpy(W.workload(name)).to(dev).view(-1)
+    total = flat.numel()
+    shapes = []
+    for cols in WIDTHS:
+        rows = total // cols
+        m = flat[: rows * cols].view(rows, cols)
+        ro = torch.empty(rows, device=dev)
+        co = torch.empty(cols, device=dev)
+        entry = {"rows": rows, "cols": cols}
+        calls = (("rows_sum", lambda: rl.red_rows_sum_f32(m, out=ro), rows),
+                 ("rows_max", lambda: rl.red_rows_max_f32(m, out=ro), rows),
+                 ("cols_sum", lambda: rl.red_cols_sum_f32(m, out=co), cols),
+                 ("cols_max", lambda: rl.red_cols_max_f32(m, out=co), cols))
+        for label, fn, nout in calls:
+            for _ in range(args.warmup):
+                fn()
+            ms = timer.region_ms(fn, args.steps)
+            nin = 4 * rows * cols
+            entry[label] = {"us": round(ms * 1e3, 2), "GB/s": round(gbps(nin, ms), 1),
+                            "GB/s_with_output": round(gbps(nin + 4 * nout, ms), 1),
+                            "pct_of_peak": round(100 * gbps(nin, ms) / PEAK_GBPS, 2)}
+        log(f"{rows}x{cols}: " + ", ".join(f"{k} {entry[k]['GB/s']}" for k in ("rows_sum", "rows_max",
+                                                                                 "cols_sum", "cols_max")))
+        shapes.append(entry)
+    print(json.dumps({"mode": "widths", "workload": f"{name} viewed as (2^28 // cols) x cols, contiguous",
+                      "steps": args.steps, "warmup": args.warmup, "unit": "GB/s of input",
+                      "shapes": shapes}), flush=True)
+
+
 class Timer:
     """HIP events on one stream around a region of `reps` enqueued calls."""
 
@@ -205,6 +248,9 @@ def main():
     log(f"device: {torch.cuda.get_device_name(dev)} {arch}, {cu} CUs; {rl.red_version()}")
     if args.ablation:
         run_ablation(args, torch, rl, W, timer, dev)
+        return
+    if args.widths:
+        run_widths(args, torch, rl, W, timer, dev)
         return
 
     # ---------------------------------------------------------- headline

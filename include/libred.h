@@ -36,7 +36,9 @@
  *    scratch at least as large as the call needs, made by an earlier column
  *    call of the same or a larger shape. Otherwise the
  *    call returns RED_ERR_CAPTURE before it touches the stream, and the
- *    capture stays intact.
+ *    capture stays intact. Workspace and scratch are never freed while the
+ *    process runs (outgrown scratch included), so a captured graph stays
+ *    valid after later calls on its stream.
  *  - Results are deterministic: for a given length and device the partials
  *    are combined in a fixed index order, so repeated calls return the same
  *    bits.

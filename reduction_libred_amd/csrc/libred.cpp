@@ -7,6 +7,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "launch.hpp"
 #include "libred.h"
@@ -43,13 +44,15 @@ std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 
 // Per-(device, stream) scratch for column partials, grown on demand up to
-// kColsScratchMax bytes. Growing waits for the stream, then frees the old
-// buffer; it happens at most a few times per stream.
+// kColsScratchMax bytes (starting at 1 MiB and at least doubling each time,
+// so growth is rare). A buffer that is outgrown is kept, not freed, until the
+// process exits: a graph captured earlier may still write to it.
 struct Scratch {
     void* ptr;
     size_t bytes;
 };
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+std::vector<void*> g_retired_scratch;
 constexpr size_t kColsScratchMax = (size_t)64 << 20;
 
 // Default launch shapes, chosen by measurement on MI355X (256 CUs, 8 TB/s):
@@ -163,18 +166,13 @@ red_status get_scratch(int dev, hipStream_t stream, size_t bytes, void** out) {
     }
     const red_status cap = refuse_if_capturing(stream);
     if (cap != RED_OK) return cap;
-    if (sc.ptr != nullptr) {
-        hipError_t e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
-        e = hipFree(sc.ptr);
-        sc.ptr = nullptr;
-        sc.bytes = 0;
-        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
-    }
     size_t nb = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
+    if (sc.ptr != nullptr && nb < 2 * sc.bytes) nb = 2 * sc.bytes;
+    if (nb > kColsScratchMax && bytes <= kColsScratchMax) nb = kColsScratchMax;
     void* p = nullptr;
     const hipError_t e = hipMalloc(&p, nb);
     if (e != hipSuccess || p == nullptr) return fail(e, RED_ERR_ALLOC);
+    if (sc.ptr != nullptr) g_retired_scratch.push_back(sc.ptr);
     sc.ptr = p;
     sc.bytes = nb;
     *out = p;

@@ -896,6 +896,33 @@ def test_graph_replay_matches_eager():
             assert torch.equal(o, e)
 
 
+def test_graph_survives_scratch_growth():
+    # A graph holds the column scratch pointer it was captured with; a later
+    # eager call on the same stream that needs more scratch must not free it,
+    # so the graph replays correctly afterwards.
+    small = device_view(W.make("normal", 64 * 256, 44).reshape(64, 256), 0)
+    big = device_view(W.make("normal", 4096 * 1024, 45).reshape(4096, 1024), 0)
+    out = torch.empty(256, device=DEV)
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    say("graph over column scratch, then scratch growth")
+    with torch.cuda.stream(cs):
+        want = rl.red_cols_sum_f32(small).clone()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            rl.red_cols_sum_f32(small, out=out)
+        big_sum = rl.red_cols_sum_f32(big, policy=dict(target_waves=4096, unroll=1))  # grows the scratch
+    torch.cuda.synchronize()
+    S, A = oracle.cols_sum_f32(big.cpu().numpy())
+    assert np.all(np.abs(big_sum.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
+    for k in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), k
+
+
 def test_capture_without_workspace_is_refused():
     # A fresh stream has no workspace yet: a call captured on it must fail
     # with RED_ERR_CAPTURE before touching the stream, leaving the capture
