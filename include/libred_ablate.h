@@ -69,12 +69,20 @@ typedef struct red_flat_policy {
 
 /* Launch shape of the row kernels: `block` threads (64, 128, 256 or 512; one
  * row per wave at a time), `unroll` loads per lane per trip (1, 2, 4, 8, 16),
- * `nontemporal`, `max_blocks` capping the grid, `split`: 0 = split few
- * long rows across single-wave blocks when that helps (the default rule),
- * 1 = never, 2 = whenever a row holds at least two tiles of 64*unroll
- * vectors; `prefetch` (0 or 1, one wave per row only): keep the next
- * tile of 64*unroll vectors in flight while folding the current one, across
- * row boundaries; and `short_rows`, the kernels for short rows (`block`,
+ * `nontemporal`, `max_blocks` capping the grid (the one-wave-per-row grid is
+ * then trimmed so that every wave gets the same number of rows, give or take
+ * one), `split`: 0 = split few long rows across single-wave blocks when that
+ * helps (the default rule), 1 = never, 2 = whenever a row holds at least two
+ * tiles of 64*unroll vectors; `cover` (one wave per row): 0 = rows that do
+ * not all start 16-byte aligned are read as the aligned 16-byte vectors
+ * that cover each row, with every load unconditional and the elements
+ * outside the row masked when folded (rows of at least 16 elements), and
+ * aligned rows directly; 1 = never (each row peels its unaligned head and
+ * tail element by element); 2 = always; `prefetch` (0 or 1, one wave per
+ * row, rows of at least 16 elements): a single-wave streaming kernel that
+ * reads rows through their covers and keeps the next tile of 64*unroll
+ * vectors in flight while folding the current one, across row boundaries;
+ * and `short_rows`, the kernels for short rows (`block`,
  * `unroll` and `prefetch` do not apply to them, `max_blocks` caps their
  * grid):
  *   0  the library's choice: rows of fewer than 1024 floats of a contiguous
@@ -99,6 +107,7 @@ typedef struct red_rows_policy {
     int split;
     int prefetch;
     int short_rows;
+    int cover;
 } red_rows_policy;
 
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,
@@ -138,10 +147,13 @@ red_status red_cols_max_f32_with(const float *x, size_t rows, size_t cols, size_
 
 /* The shape red_sum_f32 / red_sum_i32_i64 / red_max_f32 use for n elements. */
 void red_default_flat_policy(size_t n, red_flat_policy *p);
-/* The default shape of the row entry points for rows of 2048 to 16383 floats. A
- * call without a policy adapts it to the row length: 16 loads per lane and
- * max_blocks 512 from 16384 floats up; below 2048 floats, at most 4 loads per
- * lane (a tile no longer than the row) and max_blocks 2048. */
+/* The default shape of the row entry points for aligned rows of 2048 to 16383
+ * floats. A call without a policy adapts it to the row length: 16 loads per
+ * lane and max_blocks 512 from 16384 floats up; below 2048 floats, at most 4
+ * loads per lane (a tile no longer than the row) and max_blocks 2048. Rows
+ * read through their covers take 8 loads per lane and max_blocks 4096 below
+ * 1280 floats, 8 and 2048 below 2048, 4 and 2048 below 16384, and 8 and 1024
+ * from there. */
 void red_default_rows_policy(red_rows_policy *p);
 
 /* The number of blocks a single-value call of n elements launches with

@@ -40,6 +40,7 @@ struct RowsPolicy {
     int split;
     int prefetch;
     int short_rows;
+    int cover;
 };
 
 // How one row call launches: `grid` blocks of the one-wave-per-row kernel,
@@ -55,6 +56,7 @@ struct RowsLaunch {
     int staged_u;       // > 0: the LDS-staged kernel, tiles of staged_rows rows (at most
     unsigned int staged_rows;  //   256 * staged_u elements), 2^staged_log2s lanes per row
     int staged_log2s;
+    int cover;          // one wave per row: read each row through its aligned cover
 };
 constexpr size_t kMaxSplitPartials = 32768;
 

@@ -64,7 +64,7 @@ constexpr FlatPolicy kFlatCached = {1024, 1, 4, 1, libred::kWaveTiles, 1, libred
 constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
 constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
-constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0};
+constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0, 0};
 // Split-row mode: used automatically for fewer than kSplitRowsBelow rows
 // whose rows hold at least kSplitMinCols elements; aims for about
 // kSplitTargetWaves waves in all.
@@ -229,7 +229,8 @@ RowsPolicy default_rows(size_t cols) {
 
 RowsPolicy to_rows(const red_rows_policy* p, size_t cols) {
     if (!p) return default_rows(cols);
-    RowsPolicy r = {p->block, p->unroll, p->nontemporal, p->max_blocks, p->split, p->prefetch, p->short_rows};
+    RowsPolicy r = {p->block, p->unroll,     p->nontemporal, p->max_blocks,
+                    p->split, p->prefetch, p->short_rows,  p->cover};
     return r;
 }
 
@@ -273,8 +274,9 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (rows > 1 && ld != 0 && rows - 1 > (RED_MAX_N - cols) / ld) return RED_ERR_INVALID_ARG;
     const size_t span = rows == 0 ? 0 : (rows - 1) * ld + cols;
     if (span > RED_MAX_N) return RED_ERR_INVALID_ARG;
-    const RowsPolicy p = to_rows(pol, cols);
+    RowsPolicy p = to_rows(pol, cols);
     if (!libred::rows_policy_supported(p)) return RED_ERR_INVALID_ARG;
+    if (cols < 16) p.prefetch = 0;  // the streaming kernel takes rows of at least 16 elements
     if (rows == 0) return RED_OK;
     if ((span > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
     if (!aligned(x, sizeof(float)) || !aligned(out, sizeof(float))) return RED_ERR_INVALID_ARG;
@@ -284,7 +286,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
 
-    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0};
+    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0};
     // Rows of fewer than 1024 floats of a contiguous, 16-byte aligned matrix
     // go to the LDS-staged kernel (short_rows 0), or do so with
     // 2^(short_rows - 3) lanes per row (short_rows 3-9), as long as a tile
@@ -353,10 +355,29 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         }
     }
     if (L.split_gx == 0) {
-        const size_t waves_per_block = (size_t)p.block / 64;
-        size_t grid = (rows + waves_per_block - 1) / waves_per_block;
-        if (grid > (size_t)p.max_blocks) grid = (size_t)p.max_blocks;
-        L.grid = (int)grid;
+        // One wave per row. Rows that do not all start 16-byte aligned are
+        // read through their aligned covers (cover 0), or always (cover 2),
+        // or never (cover 1); the covered kernel takes rows of at least 16
+        // elements. Its defaults by row length come from a sweep over
+        // unaligned rows of 1025 to 50257 floats.
+        const bool misaligned = !aligned(x, 16) || (rows > 1 && ld % 4 != 0);
+        L.cover = cols >= 16 && (p.cover == 2 || (p.cover == 0 && misaligned)) ? 1 : 0;
+        if (L.cover && pol == nullptr) {
+            p.unroll = cols < 2048 ? 8 : cols < 16384 ? 4 : 8;
+            p.max_blocks = cols < 1280 ? 4096 : cols < 16384 ? 2048 : 1024;
+        }
+        // Every wave gets the same number of rows, give or take one: with
+        // per = ceil(rows / (max_blocks waves)), ceil(rows / per) waves, so
+        // no few waves are left with an extra round of rows. (Filling the
+        // cap exactly, or going past it to even out the rounds, measured
+        // slower: 8388 x 32001 and 5341 x 50257 ran 6-7% slower with the
+        // larger grids.)
+        const size_t W = (size_t)p.block / 64;
+        size_t target = (size_t)p.max_blocks * W;
+        if (target > rows) target = rows;
+        const size_t per = (rows + target - 1) / target;  // rows per wave
+        const size_t waves = (rows + per - 1) / per;
+        L.grid = (int)((waves + W - 1) / W);
     }
     const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
     if (e != hipSuccess) return fail(e, RED_ERR_HIP);
@@ -599,6 +620,7 @@ void red_default_rows_policy(red_rows_policy* p) {
     p->split = kDefaultRows.split;
     p->prefetch = kDefaultRows.prefetch;
     p->short_rows = kDefaultRows.short_rows;
+    p->cover = kDefaultRows.cover;
 }
 
 size_t red_flat_grid(size_t n, const red_flat_policy* pol) {

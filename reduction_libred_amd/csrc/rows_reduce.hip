@@ -12,9 +12,13 @@
 //       blocks that stream tiles of 64*UNROLL vectors dealt round-robin, each
 //       storing one partial; a second launch combines each row's partials in
 //       index order with one wave per row.
-// A row's start may be misaligned when ld is not a multiple of 4, so every
-// row peels its own head and tail. Sums accumulate in float64 and round once
-// per row.
+// A row's start may be misaligned (x not 16-byte aligned, or ld not a
+// multiple of 4). Then a row is read as the aligned 16-byte vectors that
+// cover it, with the elements outside the row masked when folded (the cover
+// kernels below); aligned rows, and the split kernel, peel a head and tail
+// element by element (none when aligned). Short rows have kernels of their
+// own (LDS-staged and packed, below). Sums accumulate in float64 and round
+// once per row.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -104,98 +108,221 @@ __global__ __launch_bounds__(BLOCK) void rows_reduce_kernel(const typename Op::e
     }
 }
 
-// One wave per row with the next tile always in flight. A wave's work is a
-// sequence of (row, tile) positions: the whole tiles of row r, then those of
-// row r + stride, and so on. Two register buffers alternate: the loads of the
-// next position (which may be the first tile of the wave's next row) are
-// issued before the current tile is folded, and a row is finished (the
-// vectors after its last whole tile, its head and tail, the wave reduce and
-// the store) while the next row's first tile is on its way. Rows with no
-// whole tile are finished directly. Every load is of a tile that lies inside
-// its row.
+// One wave per row, streaming. A row is read as the aligned 16-byte vectors
+// that cover it: vector 0 holds the row's first element at position s (0-3),
+// and the cover has nv = ceil((s + cols) / 4) vectors, cut into tiles of
+// 64 * UNROLL. A wave's work is the sequence of (row, tile) items of rows
+// r, r + G, r + 2G, ... (G waves in all); the loads of the next item (which may
+// be the first tile of the wave's next row) are issued before the current
+// item is folded, and every load is unconditional: an index past the row's
+// last vector is clamped to it, and elements outside the row are replaced by
+// the identity when folded, never masked at the load. Only the first and last
+// tiles of a row need that masking. A cover vector that would reach outside
+// the array (before x when x is not 16-byte aligned, or past the end of the
+// last row) is not loaded as a vector; its elements of the row are read one
+// by one when the row is finished. Rows hold at least 16 elements.
 template <class Op>
-struct RowGeom {
-    const typename Op::vec_t* rv;  // first aligned vector of the row body
-    size_t head, nvec, ntiles;
+struct CoverGeom {
+    const typename Op::vec_t* vb;  // the aligned vector holding the row's first element
+    size_t nv;                     // vectors of the cover
+    size_t ntiles;                 // tiles of 64 * UNROLL vectors
+    size_t vlo, vhi;               // vectors [vlo, vhi) are loaded as vectors
+    unsigned int s;                // position of the row's first element in vector 0
 };
 
 template <class Op, int UNROLL>
-__device__ __forceinline__ RowGeom<Op> row_geom(const typename Op::elem_t* __restrict__ x, size_t r,
-                                                size_t cols, size_t ld) {
-    const typename Op::elem_t* row = x + r * ld;
-    RowGeom<Op> g;
-    g.head = head_elems(row, sizeof(typename Op::elem_t), cols);
-    g.nvec = (cols - g.head) / Op::kPerVec;
-    g.ntiles = g.nvec / ((size_t)kWave * UNROLL);
-    g.rv = reinterpret_cast<const typename Op::vec_t*>(row + g.head);
+__device__ __forceinline__ CoverGeom<Op> cover_geom(const typename Op::elem_t* __restrict__ x, size_t r,
+                                                    size_t cols, size_t ld, uintptr_t end) {
+    using elem_t = typename Op::elem_t;
+    constexpr size_t E = Op::kPerVec;
+    const elem_t* row = x + r * ld;
+    CoverGeom<Op> g;
+    g.s = (unsigned int)(((uintptr_t)row & 15u) / sizeof(elem_t));
+    // Pointer arithmetic from x (not an integer cast) keeps the loads global.
+    g.vb = reinterpret_cast<const typename Op::vec_t*>(row - g.s);
+    g.nv = (g.s + cols + E - 1) / E;
+    g.ntiles = (g.nv + (size_t)kWave * UNROLL - 1) / ((size_t)kWave * UNROLL);
+    g.vlo = (uintptr_t)g.vb < (uintptr_t)x ? 1 : 0;
+    g.vhi = (uintptr_t)(g.vb + g.nv) > end ? g.nv - 1 : g.nv;
     return g;
 }
 
+// The element that leaves a row reduction unchanged: 0 for the sum, -inf for
+// the max (which skips NaN and keeps its incumbent on ties).
+template <class Op>
+struct RowNeutral;
+template <>
+struct RowNeutral<SumF32> {
+    static __device__ __forceinline__ float value() { return 0.0f; }
+};
+template <>
+struct RowNeutral<MaxF32> {
+    static __device__ __forceinline__ float value() { return -__builtin_inff(); }
+};
+
+// Fold row r through its cover (see above), one tile at a time: the tile's
+// loads are unconditional (indices clamped into [vlo, vhi)), load slots of
+// the last tile that hold no vector of the row are skipped (a wave-uniform
+// test), and the first and last tiles are folded with the elements outside
+// the row replaced by the identity. Then the edge elements of a cover vector
+// that was not loaded as a vector.
+template <class Op, int UNROLL, bool NT>
+__device__ __forceinline__ void fold_row_cover(const typename Op::elem_t* __restrict__ x, size_t r, size_t cols,
+                                               size_t ld, uintptr_t end, typename Op::acc_t (&acc)[4]) {
+    using vec_t = typename Op::vec_t;
+    constexpr size_t E = Op::kPerVec;
+    constexpr size_t TILE = (size_t)kWave * UNROLL;
+    const unsigned int lane = threadIdx.x % kWave;
+    const CoverGeom<Op> g = cover_geom<Op, UNROLL>(x, r, cols, ld, end);
+    // Only cover vector 0 (elements before position s) and the last cover
+    // vector (elements from position s + cols on) can hold elements outside
+    // the row; a vector outside [vlo, vhi) holds none of the row. Those
+    // elements become the operator's neutral element.
+    const unsigned int k_end = (unsigned int)(g.s + cols - (g.nv - 1) * E);  // 1..E
+    for (size_t t = 0; t < g.ntiles; ++t) {
+        vec_t v[UNROLL];
+        if (t != 0 && t + 1 != g.ntiles) {  // wave-uniform: a tile inside the row, read as is
+            const vec_t* __restrict__ p = g.vb + t * TILE + lane;
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                fold_vec<Op>(acc, v[u], (t * TILE + (size_t)u * kWave + lane) * E - g.s);
+        } else {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                size_t i = t * TILE + (size_t)u * kWave + lane;
+                i = i < g.vlo ? g.vlo : i;
+                i = i >= g.vhi ? g.vhi - 1 : i;
+                v[u] = load_vec<NT>(g.vb + i);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const size_t i = t * TILE + (size_t)u * kWave + lane;
+                unsigned int lo = i == 0 ? g.s : 0u;
+                unsigned int hi = i + 1 == g.nv ? k_end : (unsigned int)E;
+                if (i < g.vlo || i >= g.vhi) hi = 0;
+                vec_t w = v[u];
+#pragma unroll
+                for (int k = 0; k < (int)E; ++k)
+                    w[k] = ((unsigned int)k >= lo && (unsigned int)k < hi) ? w[k] : RowNeutral<Op>::value();
+                fold_vec<Op>(acc, w, i * E - g.s);
+            }
+        }
+    }
+    const typename Op::elem_t* row = x + r * ld;
+    if (g.vlo != 0) {
+        const size_t nfirst = E - g.s;
+        if (lane < nfirst) acc[0] = Op::combine(acc[0], Op::lift(row[lane], lane));
+    }
+    if (g.vhi != g.nv) {
+        const size_t e0 = (g.nv - 1) * E - g.s;
+        if (lane < cols - e0) acc[1] = Op::combine(acc[1], Op::lift(row[e0 + lane], e0 + lane));
+    }
+}
+
 template <class Op, int BLOCK, int UNROLL, bool NT>
-__global__ __launch_bounds__(BLOCK) void rows_prefetch_kernel(const typename Op::elem_t* __restrict__ x,
-                                                              size_t rows, size_t cols, size_t ld,
-                                                              typename Op::out_t* __restrict__ out) {
+__global__ __launch_bounds__(BLOCK) void rows_cover_kernel(const typename Op::elem_t* __restrict__ x,
+                                                           size_t rows, size_t cols, size_t ld,
+                                                           typename Op::out_t* __restrict__ out) {
+    using acc_t = typename Op::acc_t;
+    constexpr int W = BLOCK / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uintptr_t end = (uintptr_t)(x + (rows - 1) * ld + cols);
+    for (size_t r = (size_t)blockIdx.x * W + wave; r < rows; r += (size_t)gridDim.x * W) {
+        acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
+        fold_row_cover<Op, UNROLL, NT>(x, r, cols, ld, end, acc);
+        acc_t v = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
+        v = wave_reduce<Op>(v);
+        if (lane == 0) out[r] = Op::finish(v);
+    }
+}
+
+template <class Op, int UNROLL, bool NT>
+__global__ __launch_bounds__(kWave) void rows_stream_kernel(const typename Op::elem_t* __restrict__ x,
+                                                            size_t rows, size_t cols, size_t ld,
+                                                            typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
     using vec_t = typename Op::vec_t;
-    constexpr int W = BLOCK / kWave;
+    using elem_t = typename Op::elem_t;
+    constexpr size_t E = Op::kPerVec;
     constexpr size_t TILE = (size_t)kWave * UNROLL;
-    const int lane = threadIdx.x % kWave;
-    const size_t stride = (size_t)gridDim.x * W;
-    size_t r = (size_t)blockIdx.x * W + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
-    if (r >= rows) return;  // wave-uniform
-    RowGeom<Op> g = row_geom<Op, UNROLL>(x, r, cols, ld);
+    const unsigned int lane = threadIdx.x;
+    const size_t G = gridDim.x;
+    const uintptr_t end = (uintptr_t)(x + (rows - 1) * ld + cols);
+    size_t r = blockIdx.x;  // wave-uniform
+    if (r >= rows) return;
+    CoverGeom<Op> g = cover_geom<Op, UNROLL>(x, r, cols, ld, end);
     size_t t = 0;
-    bool have = g.ntiles > 0;
     acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
-    vec_t a[UNROLL], b[UNROLL];
 
-    // Everything of row r that is not a whole tile, then the row's result.
+    auto load_item = [&](vec_t (&v)[UNROLL], const CoverGeom<Op>& h, size_t tt) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            size_t i = tt * TILE + (size_t)u * kWave + lane;
+            i = i < h.vlo ? h.vlo : i;
+            i = i >= h.vhi ? h.vhi - 1 : i;
+            v[u] = load_vec<NT>(h.vb + i);
+        }
+    };
+    auto fold_item = [&](const vec_t (&v)[UNROLL]) {
+        if (t != 0 && t + 1 != g.ntiles) {  // wave-uniform: a tile inside the row
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                fold_vec<Op>(acc, v[u], (t * TILE + (size_t)u * kWave + lane) * E - g.s);
+        } else {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const size_t i = t * TILE + (size_t)u * kWave + lane;
+                const bool live = i >= g.vlo && i < g.vhi;
+#pragma unroll
+                for (int k = 0; k < (int)E; ++k) {
+                    const size_t e = i * E + k;  // position in the cover; the row is [s, s + cols)
+                    const bool in = live && e >= g.s && e < g.s + cols;
+                    acc[k & 3] = Op::combine(acc[k & 3], in ? Op::lift(v[u][k], e - g.s) : Op::identity());
+                }
+            }
+        }
+    };
     auto finish_row = [&]() {
-        const typename Op::elem_t* row = x + r * ld;
-        fold_remainder<Op, UNROLL, NT>(acc, g.rv, g.head, g.ntiles * TILE, g.nvec, kWave);
-        const size_t tail0 = g.head + (size_t)Op::kPerVec * g.nvec;
-        if ((size_t)lane < g.head) acc[0] = Op::combine(acc[0], Op::lift(row[lane], lane));
-        if ((size_t)lane < cols - tail0) acc[1] = Op::combine(acc[1], Op::lift(row[tail0 + lane], tail0 + lane));
+        const elem_t* row = x + r * ld;
+        if (g.vlo != 0) {  // the row's elements in cover vector 0, read one by one
+            const size_t nfirst = E - g.s;
+            if (lane < nfirst) acc[0] = Op::combine(acc[0], Op::lift(row[lane], lane));
+        }
+        if (g.vhi != g.nv) {  // and those in the last cover vector
+            const size_t e0 = (g.nv - 1) * E - g.s;
+            if (lane < cols - e0) acc[1] = Op::combine(acc[1], Op::lift(row[e0 + lane], e0 + lane));
+        }
         acc_t v = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
         v = wave_reduce<Op>(v);
         if (lane == 0) out[r] = Op::finish(v);
         acc[0] = acc[1] = acc[2] = acc[3] = Op::identity();
     };
-    // Process the tile in `cur` (if any) and leave the next position's tile
-    // in `nxt`; false once the wave has no rows left.
-    auto step = [&](vec_t (&cur)[UNROLL], vec_t (&nxt)[UNROLL]) -> bool {
-        if (have) {
-            size_t rn = r, tn = t + 1;
-            RowGeom<Op> gn = g;
-            const bool row_done = tn >= g.ntiles;
-            if (row_done) {
-                rn = r + stride;
-                tn = 0;
-                if (rn < rows) gn = row_geom<Op, UNROLL>(x, rn, cols, ld);
-            }
-            const bool next_have = rn < rows && tn < gn.ntiles;
-            if (next_have) load_tile_rows<NT>(nxt, gn.rv + tn * TILE + lane);
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-                fold_vec<Op>(acc, cur[u], g.head + (t * TILE + lane + (size_t)u * kWave) * Op::kPerVec);
-            if (row_done) finish_row();
-            r = rn;
-            t = tn;
-            g = gn;
-            have = next_have;
-        } else {
-            finish_row();
-            r += stride;
-            if (r < rows) {
-                g = row_geom<Op, UNROLL>(x, r, cols, ld);
-                t = 0;
-                have = g.ntiles > 0;
-                if (have) load_tile_rows<NT>(nxt, g.rv + lane);
-            }
+    // One item: load the next one, fold this one, finish the row after its
+    // last tile. Returns false when the wave has no item left (its final
+    // loads then re-read the current tile, which stays in bounds).
+    auto step = [&](const vec_t (&cur)[UNROLL], vec_t (&nxt)[UNROLL]) -> bool {
+        size_t rn = r, tn = t + 1;
+        CoverGeom<Op> gn = g;
+        const bool row_done = tn >= g.ntiles;
+        if (row_done) {
+            rn = r + G;
+            tn = 0;
+            if (rn < rows) gn = cover_geom<Op, UNROLL>(x, rn, cols, ld, end);
         }
-        return r < rows;
+        const bool more = rn < rows;
+        load_item(nxt, more ? gn : g, more ? tn : t);
+        fold_item(cur);
+        if (row_done) finish_row();
+        r = rn;
+        t = tn;
+        g = gn;
+        return more;
     };
-    if (have) load_tile_rows<NT>(a, g.rv + lane);
+    vec_t a[UNROLL], b[UNROLL];
+    load_item(a, g, 0);
     while (step(a, b) && step(b, a)) {
     }
 }
@@ -444,18 +571,31 @@ bool rows_policy_supported(const RowsPolicy& p) {
     const bool b = p.block == 64 || p.block == 128 || p.block == 256 || p.block == 512;
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.max_blocks >= 1 && p.split >= 0 &&
-           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.short_rows >= 0 && p.short_rows <= 9;
+           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.cover >= 0 && p.cover <= 2 && p.short_rows >= 0 && p.short_rows <= 9;
 }
 
 template <class Op, int BLOCK, int UNROLL>
 static hipError_t rows_bu(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
-                          typename Op::out_t* out, int grid, bool nt, bool pf, hipStream_t stream) {
-    if (pf) {
+                          typename Op::out_t* out, int grid, bool nt, bool pf, bool cover, hipStream_t stream) {
+    if (cover && !pf) {
         if (nt)
-            hipLaunchKernelGGL((rows_prefetch_kernel<Op, BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0,
+            hipLaunchKernelGGL((rows_cover_kernel<Op, BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0, stream, x,
+                               rows, cols, ld, out);
+        else
+            hipLaunchKernelGGL((rows_cover_kernel<Op, BLOCK, UNROLL, false>), dim3(grid), dim3(BLOCK), 0, stream,
+                               x, rows, cols, ld, out);
+        return hipGetLastError();
+    }
+    if (pf) {
+        // The streaming kernel runs single-wave blocks: as many waves as the
+        // BLOCK-thread grid holds, at most one per row.
+        size_t waves = (size_t)grid * (BLOCK / kWave);
+        if (waves > rows) waves = rows;
+        if (nt)
+            hipLaunchKernelGGL((rows_stream_kernel<Op, UNROLL, true>), dim3((unsigned int)waves), dim3(kWave), 0,
                                stream, x, rows, cols, ld, out);
         else
-            hipLaunchKernelGGL((rows_prefetch_kernel<Op, BLOCK, UNROLL, false>), dim3(grid), dim3(BLOCK), 0,
+            hipLaunchKernelGGL((rows_stream_kernel<Op, UNROLL, false>), dim3((unsigned int)waves), dim3(kWave), 0,
                                stream, x, rows, cols, ld, out);
     } else if (nt) {
         hipLaunchKernelGGL((rows_reduce_kernel<Op, BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0,
@@ -469,15 +609,15 @@ static hipError_t rows_bu(const typename Op::elem_t* x, size_t rows, size_t cols
 
 template <class Op, int BLOCK>
 static hipError_t rows_b(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
-                         typename Op::out_t* out, int grid, const RowsPolicy& p, hipStream_t stream) {
+                         typename Op::out_t* out, int grid, bool cover, const RowsPolicy& p, hipStream_t stream) {
     const bool nt = p.nontemporal != 0;
     const bool pf = p.prefetch != 0;
     switch (p.unroll) {
-        case 1: return rows_bu<Op, BLOCK, 1>(x, rows, cols, ld, out, grid, nt, pf, stream);
-        case 2: return rows_bu<Op, BLOCK, 2>(x, rows, cols, ld, out, grid, nt, pf, stream);
-        case 4: return rows_bu<Op, BLOCK, 4>(x, rows, cols, ld, out, grid, nt, pf, stream);
-        case 8: return rows_bu<Op, BLOCK, 8>(x, rows, cols, ld, out, grid, nt, pf, stream);
-        case 16: return rows_bu<Op, BLOCK, 16>(x, rows, cols, ld, out, grid, nt, pf, stream);
+        case 1: return rows_bu<Op, BLOCK, 1>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
+        case 2: return rows_bu<Op, BLOCK, 2>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
+        case 4: return rows_bu<Op, BLOCK, 4>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
+        case 8: return rows_bu<Op, BLOCK, 8>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
+        case 16: return rows_bu<Op, BLOCK, 16>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -610,10 +750,10 @@ static hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols
         }
     }
     switch (p.block) {
-        case 64: return rows_b<Op, 64>(x, rows, cols, ld, out, L.grid, p, stream);
-        case 128: return rows_b<Op, 128>(x, rows, cols, ld, out, L.grid, p, stream);
-        case 256: return rows_b<Op, 256>(x, rows, cols, ld, out, L.grid, p, stream);
-        case 512: return rows_b<Op, 512>(x, rows, cols, ld, out, L.grid, p, stream);
+        case 64: return rows_b<Op, 64>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
+        case 128: return rows_b<Op, 128>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
+        case 256: return rows_b<Op, 256>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
+        case 512: return rows_b<Op, 512>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -564,7 +564,9 @@ ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1,
                 dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
                 dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0),
                 dict(short_rows=2), dict(short_rows=3), dict(short_rows=6, max_blocks=3),
-                dict(short_rows=9, nontemporal=0), dict(short_rows=5, max_blocks=1))
+                dict(short_rows=9, nontemporal=0), dict(short_rows=5, max_blocks=1),
+                dict(cover=2, short_rows=1), dict(cover=2, unroll=16, max_blocks=3, short_rows=1),
+                dict(cover=2, block=256, unroll=2, short_rows=1), dict(cover=1, short_rows=1, max_blocks=5))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
@@ -625,7 +627,8 @@ def test_rows_split_long_rows(rows, cols):
     S, A = oracle.rows_sum_f32(a)
     M = oracle.rows_max_f32(a)
     x = device_view(a, 3)
-    for p in (None, dict(split=1), dict(split=2, unroll=4), dict(split=2, unroll=16, nontemporal=0)):
+    for p in (None, dict(split=1), dict(split=2, unroll=4), dict(split=2, unroll=16, nontemporal=0),
+              dict(split=1, cover=1), dict(split=1, cover=2, unroll=16), dict(split=1, prefetch=1)):
         say(f"rows split {rows}x{cols} policy={p}")
         s = rl.red_rows_sum_f32(x, policy=p)
         m = rl.red_rows_max_f32(x, policy=p)
