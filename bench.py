@@ -149,8 +149,10 @@ def run_ablation(args, torch, rl, W, timer, dev):
 
 # Row lengths covering each row and column path: one float, odd widths (the
 # LDS-staged rows, folded column views), multiples of 4 (packed and staged
-# rows, four columns per lane), and long rows (one wave per row).
-WIDTHS = [1, 3, 4, 7, 16, 17, 33, 64, 65, 100, 256, 512, 1000, 1023, 4096, 4097]
+# rows, four columns per lane), and long rows (one wave per row; odd lengths
+# read through their aligned covers).
+WIDTHS = [1, 3, 4, 7, 16, 17, 33, 64, 65, 100, 256, 260, 512, 1000, 1020, 1023, 1025, 2049, 4096, 4097,
+          6000, 16385, 50257]
 
 
 def run_widths(args, torch, rl, W, timer, dev):

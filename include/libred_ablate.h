@@ -114,12 +114,17 @@ typedef struct red_rows_policy {
  * 4, 8 or 16), `nontemporal`, `target_waves` (the rows are cut into chunks
  * until about this many single-wave blocks run), `vec`: 0 = four adjacent
  * columns per lane when x is 16-byte aligned and cols and ld are multiples
- * of 4; a contiguous (ld == cols), 16-byte aligned matrix of another width
- * is read as m consecutive rows at a time (m a multiple of 2 or 4 that makes
- * the m-row spans start 16-byte aligned, chosen up to 16 to use the most
- * lanes) with four columns per lane, and a second pass adds each column's
- * m partial columns and the last rows % m rows; else one column per lane;
- * 1 = always one; 4 = same as 0; and `width` (1, 2 or 4):
+ * of 4, or through an m-row view (see `fold`); else one column per lane;
+ * 1 = always one; 4 = same as 0; `fold` (with vec 0 or 4, for a contiguous
+ * (ld == cols), 16-byte aligned matrix): the matrix is read as rows / m rows
+ * of m * cols columns, m consecutive rows as one, with four columns per
+ * lane, and a second pass adds each column's m partial columns and then the
+ * last rows % m rows. m must make every m-row span start 16-byte aligned (a
+ * multiple of 4 / gcd(cols, 4)). 0 = the library's choice (16 for widths of
+ * at least 256 that are not a multiple of 4; otherwise the m up to 16 that
+ * leaves the fewest lanes idle, multiples of 4 folded only for 5% more
+ * lanes), 1 = never, 2-16 = that m, rounded up to a valid multiple and
+ * down to the rows; and `width` (1, 2 or 4):
  * with at least 64 column groups, each row is read by `width` loads per lane,
  * so a wave reads width x 1 KiB (four columns per lane) or width x 256 bytes
  * (one column per lane) of a row at once (with fewer groups, 1 is used);
@@ -132,12 +137,15 @@ typedef struct red_cols_policy {
     int vec;
     int width;
     int prefetch;
+    int fold;
 } red_cols_policy;
 
 /* The default column shape. A call without a policy uses it, except on
- * short-wide matrices (four columns per lane and cols / 256 >= 1024), which
- * use unroll 2, width 4, no prefetch and target_waves 1024, and with one
- * column per lane and at least 64 columns, which use unroll 8, width 2, no
+ * short-wide matrices (four columns per lane and cols / 256 > 1024, cols of
+ * the m-row view when folded), and on unfolded matrices of at least 256
+ * columns whose rows are not a whole number of 128-byte lines, which use
+ * unroll 2, width 4, no prefetch and target_waves 1024; and with one column
+ * per lane and at least 64 columns, which use unroll 8, width 2, no
  * prefetch and target_waves 2048. */
 void red_default_cols_policy(red_cols_policy *p);
 red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,

@@ -191,33 +191,31 @@ __global__ __launch_bounds__(kColsCombineBlock) void cols_combine_kernel(
     if (lane == 0) out[c] = Op::finish(v);
 }
 
-// Pass 2 of a folded launch (see ColsLaunch): one block per real column c.
-// Its items are j = k * m + r (chunk k, fold row r, partial of view column
-// r * cols + c), dealt to the threads in rounds of 4 * kColsCombineBlock (4
-// loads in flight per thread, each from a clamped index so no load is
-// predicated), then the tail rows, lane-strided; then the block reduce. The
-// order is fixed, so the result is deterministic.
+// Pass 2 of a folded launch (see ColsLaunch): the partials of real column c
+// are items j * cols + c for j < nchunks * m (chunk j / m, view column
+// (j % m) * cols + c), then the tail rows. One block per real column: items
+// dealt to the threads in rounds of 4 * kColsCombineBlock (4 loads in flight
+// per thread, each from a clamped index so no load is predicated), then the
+// tail rows, lane-strided, then the block reduce. The order is fixed, so the
+// result is deterministic.
 template <class Op>
 __global__ __launch_bounds__(kColsCombineBlock) void cols_fold_combine_kernel(
-    const typename Op::acc_t* __restrict__ partials, unsigned int nchunks, size_t vcols, size_t cols,
-    unsigned int m, const typename Op::elem_t* __restrict__ tail, unsigned int tail_rows,
-    typename Op::out_t* __restrict__ out) {
+    const typename Op::acc_t* __restrict__ partials, unsigned int items, size_t cols,
+    const typename Op::elem_t* __restrict__ tail, unsigned int tail_rows, typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
     __shared__ acc_t lds[kColsCombineBlock / kWave];
     const size_t c = blockIdx.x;
-    const unsigned int total = nchunks * m;
     acc_t v = Op::identity();
-    for (unsigned int j0 = 0; j0 < total; j0 += 4 * kColsCombineBlock) {
+    for (unsigned int j0 = 0; j0 < items; j0 += 4 * kColsCombineBlock) {
         acc_t t[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const unsigned int j = j0 + u * kColsCombineBlock + threadIdx.x;
-            const unsigned int jj = j < total ? j : total - 1;
-            t[u] = partials[(size_t)(jj / m) * vcols + (size_t)(jj % m) * cols + c];
+            t[u] = partials[(size_t)(j < items ? j : items - 1) * cols + c];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-            if (j0 + u * kColsCombineBlock + threadIdx.x < total) v = Op::combine(v, t[u]);
+            if (j0 + u * kColsCombineBlock + threadIdx.x < items) v = Op::combine(v, t[u]);
     }
     for (unsigned int t = threadIdx.x; t < tail_rows; t += kColsCombineBlock)
         v = Op::combine(v, Op::lift(tail[(size_t)t * cols + c], 0));
@@ -225,12 +223,39 @@ __global__ __launch_bounds__(kColsCombineBlock) void cols_fold_combine_kernel(
     if (threadIdx.x == 0) out[c] = Op::finish(v);
 }
 
+// Pass 2 when there are many columns and few partials each: one thread per
+// column adds items j * cols + c for j < items in order (consecutive threads
+// read consecutive partials, so the reads coalesce), 8 loads in flight, then
+// the tail rows in order. Serves folded and plain launches alike (m = 1, no
+// tail).
+template <class Op>
+__global__ __launch_bounds__(kColsCombineBlock) void cols_combine_wide_kernel(
+    const typename Op::acc_t* __restrict__ partials, unsigned int items, size_t cols,
+    const typename Op::elem_t* __restrict__ tail, unsigned int tail_rows, typename Op::out_t* __restrict__ out) {
+    using acc_t = typename Op::acc_t;
+    const size_t c = (size_t)blockIdx.x * kColsCombineBlock + threadIdx.x;
+    if (c >= cols) return;
+    acc_t v = Op::identity();
+    for (unsigned int j0 = 0; j0 < items; j0 += 8) {
+        acc_t t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const unsigned int j = j0 + u < items ? j0 + u : items - 1;  // uniform
+            t[u] = partials[(size_t)j * cols + c];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u < items) v = Op::combine(v, t[u]);
+    }
+    for (unsigned int t = 0; t < tail_rows; ++t) v = Op::combine(v, Op::lift(tail[(size_t)t * cols + c], 0));
+    out[c] = Op::finish(v);
+}
+
 bool cols_policy_supported(const ColsPolicy& p) {
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     const bool w = p.width == 1 || p.width == 2 || p.width == 4;
     return u && w && (p.nontemporal == 0 || p.nontemporal == 1) && (p.prefetch == 0 || p.prefetch == 1) &&
-           p.target_waves >= 1 &&
-           (p.vec == 0 || p.vec == 1 || p.vec == 4);
+           p.target_waves >= 1 && (p.vec == 0 || p.vec == 1 || p.vec == 4) && p.fold >= 0 && p.fold <= 16;
 }
 
 template <class Op, int VEC, int CW, int UNROLL, bool PF>
@@ -248,14 +273,23 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
     hipError_t e = hipGetLastError();
     const size_t W = kColsCombineBlock / kWave;
     if (e != hipSuccess) return e;
-    if (L.fold_m > 1) {
-        hipLaunchKernelGGL((cols_fold_combine_kernel<Op>), dim3((unsigned int)L.real_cols), dim3(kColsCombineBlock),
-                           0, stream, partials, (unsigned int)L.nchunks, cols, L.real_cols,
-                           (unsigned int)L.fold_m, static_cast<const typename Op::elem_t*>(L.tail),
-                           (unsigned int)L.tail_rows, out);
+    if (L.nchunks == 1 && L.fold_m <= 1) return e;
+    // Items per real column; with at least 64 columns per item, one thread
+    // per column (coalesced), else one block or wave per column.
+    const size_t items = L.nchunks * (size_t)(L.fold_m > 1 ? L.fold_m : 1);
+    const auto* tail = static_cast<const typename Op::elem_t*>(L.tail);
+    if (items * 64 <= L.real_cols) {
+        const size_t nb = (L.real_cols + kColsCombineBlock - 1) / kColsCombineBlock;
+        hipLaunchKernelGGL((cols_combine_wide_kernel<Op>), dim3((unsigned int)nb), dim3(kColsCombineBlock), 0, stream,
+                           partials, (unsigned int)items, L.real_cols, tail, (unsigned int)L.tail_rows, out);
         return hipGetLastError();
     }
-    if (L.nchunks == 1) return e;
+    if (L.fold_m > 1) {
+        hipLaunchKernelGGL((cols_fold_combine_kernel<Op>), dim3((unsigned int)L.real_cols), dim3(kColsCombineBlock),
+                           0, stream, partials, (unsigned int)items, L.real_cols, tail, (unsigned int)L.tail_rows,
+                           out);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((cols_combine_kernel<Op>), dim3((unsigned int)((cols + W - 1) / W)),
                        dim3(kColsCombineBlock), 0, stream, partials, L.nchunks, cols, out);
     return hipGetLastError();

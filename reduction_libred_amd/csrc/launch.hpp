@@ -82,6 +82,7 @@ struct ColsPolicy {
     int vec;
     int width;
     int prefetch;
+    int fold;
 };
 
 // How one column call launches: ncb column blocks of ngroups*vec*width

@@ -181,20 +181,20 @@ red_status get_scratch(int dev, hipStream_t stream, size_t bytes, void** out) {
 
 // Column defaults, from a sweep over five 1 GiB shapes (65536 x 4096,
 // 16K x 16K, 1M x 256, 256K x 1024, 256 x 1M): 512 waves with two groups of
-// 8 rows in flight each are best on average. Short-wide matrices (at least
+// 8 rows in flight each are best on average. Short-wide matrices (more than
 // 1024 blocks of 256 columns) instead read 4 KiB of a row per wave and
 // 2 rows at a time, without prefetch (256 x 1M: 5.9 -> 7.1 TB/s).
-constexpr libred::ColsPolicy kDefaultCols = {8, 1, 512, 0, 1, 1};
-constexpr libred::ColsPolicy kWideCols = {2, 1, 1024, 0, 4, 0};
+constexpr libred::ColsPolicy kDefaultCols = {8, 1, 512, 0, 1, 1, 0};
+constexpr libred::ColsPolicy kWideCols = {2, 1, 1024, 0, 4, 0, 0};
 // Columns read one element per lane (rows not 16-byte aligned, or cols or ld
 // not a multiple of 4) with at least 64 of them: two loads per row per lane,
 // 2048 waves (a sweep over 4097, 1001, 257 and 65 columns: 2.3-2.8 ->
 // 3.4-5.3 TB/s against the vector default).
-constexpr libred::ColsPolicy kScalarCols = {8, 1, 2048, 0, 2, 0};
+constexpr libred::ColsPolicy kScalarCols = {8, 1, 2048, 0, 2, 0, 0};
 
 libred::ColsPolicy to_cols(const red_cols_policy* p) {
     if (!p) return kDefaultCols;
-    libred::ColsPolicy c = {p->unroll, p->nontemporal, p->target_waves, p->vec, p->width, p->prefetch};
+    libred::ColsPolicy c = {p->unroll, p->nontemporal, p->target_waves, p->vec, p->width, p->prefetch, p->fold};
     return c;
 }
 
@@ -393,18 +393,29 @@ double cols_lane_use(size_t groups) {
     return (double)groups / (double)(64 * ((groups + 63) / 64));
 }
 
-// Rows per view row for a contiguous matrix whose width is not a multiple of
-// 4 (1 = no fold): among the multiples m of 4 / gcd(cols, 4) up to 16 (and
-// at most rows), the one whose view uses the most lanes, the smallest on a
-// tie. The second pass reads m partials per chunk, which caps m.
+// Rows per view row for a contiguous matrix (1 = no fold): among the
+// multiples m of 4 / gcd(cols, 4) up to 16 (and at most rows), the one whose
+// view uses the most lanes; a larger m is taken only for 1% more of them,
+// since the second pass reads m partials per chunk. A width that is a multiple of 4 is
+// folded only when that uses at least 5% more of the lanes (65 groups of
+// four columns, say, leave a second block per row with one group).
 size_t fold_rows(size_t rows, size_t cols) {
-    const size_t m0 = cols % 2 == 0 ? 2 : 4;
+    const size_t m0 = cols % 4 == 0 ? 1 : cols % 2 == 0 ? 2 : 4;
+    if (m0 > 1 && cols >= 256) {
+        // Widths of at least 256 that are not a multiple of 4 take 16 rows
+        // (fewer if the matrix has fewer): over 1023 to 65537 columns that
+        // ran 3-24% faster than 4 rows, which already use 98% of the lanes.
+        size_t m = 16;
+        while (m > rows || cols * m > RED_MAX_N) m -= m0;
+        return m < m0 ? 1 : m;
+    }
     size_t best = 1;
     double best_use = -1.0;
     for (size_t m = m0; m <= 16 && m <= rows && cols * m <= RED_MAX_N; m += m0) {
         const double use = cols_lane_use(m * cols / 4);
-        if (use > best_use + 1e-9) best_use = use, best = m;
+        if (use > best_use + 0.01) best_use = use, best = m;  // a larger m must gain 1% of the lanes
     }
+    if (m0 == 1 && best_use < cols_lane_use(cols / 4) + 0.05) return 1;
     return best;
 }
 
@@ -430,14 +441,21 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     L.real_cols = cols;
     L.tail_rows = 0;
     L.tail = nullptr;
-    // A contiguous matrix whose width is not a multiple of 4 is viewed with
-    // m = 2 or 4 consecutive rows as one row of m * cols columns, so that
-    // every view row starts 16-byte aligned and four columns go per lane;
-    // pass 2 adds each real column's m view columns, then the last
-    // rows % m rows.
+    // A contiguous matrix may be viewed with m consecutive rows as one row
+    // of m * cols columns (see fold_rows): for a width that is not a
+    // multiple of 4 this makes every view row start 16-byte aligned, so four
+    // columns go per lane; for any width it can leave fewer lanes idle.
+    // Pass 2 adds each real column's m view columns, then the last rows % m
+    // rows.
     const size_t rows_real = rows, cols_real = cols;
-    if (p.vec != 1 && cols % 4 != 0 && ld == cols && aligned(x, 16)) {
-        const size_t m = fold_rows(rows, cols);
+    if (p.vec != 1 && p.fold != 1 && ld == cols && aligned(x, 16)) {
+        size_t m = fold_rows(rows, cols);
+        if (p.fold > 1) {  // the policy's m, made a multiple of 4 / gcd(cols, 4) that fits the rows
+            const size_t m0 = cols % 4 == 0 ? 1 : cols % 2 == 0 ? 2 : 4;
+            m = ((size_t)p.fold + m0 - 1) / m0 * m0;
+            while (m > rows || cols * m > RED_MAX_N) m -= m0;
+            if (m < m0) m = 1;
+        }
         if (m > 1) {
             L.fold_m = (int)m;
             rows = rows_real / m;
@@ -449,7 +467,11 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     }
     const bool vec_ok = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
     L.vec = (p.vec != 1 && vec_ok) ? 4 : 1;
-    if (pol == nullptr && L.vec == 4 && cols / 256 >= (size_t)kWideCols.target_waves) p = kWideCols;
+    if (pol == nullptr && L.vec == 4 && cols / 256 > (size_t)kWideCols.target_waves) p = kWideCols;
+    // Rows that are not a whole number of 128-byte lines (and not a folded
+    // view) also read best 4 KiB at a time, 2 rows in flight: 1020, 1500,
+    // 3000 and 6000 columns ran 8-12% faster than with the default shape.
+    if (pol == nullptr && L.vec == 4 && L.fold_m == 1 && cols % 32 != 0 && cols >= 256) p = kWideCols;
     // Narrow matrix: if the column groups divide a wave, pack several rows
     // into each load.
     const size_t groups = cols / (size_t)L.vec;
@@ -735,6 +757,7 @@ void red_default_cols_policy(red_cols_policy* p) {
     p->vec = kDefaultCols.vec;
     p->width = kDefaultCols.width;
     p->prefetch = kDefaultCols.prefetch;
+    p->fold = kDefaultCols.fold;
 }
 
 red_status red_cols_sum_f32_with(const float* x, size_t rows, size_t cols, size_t ld, float* out,

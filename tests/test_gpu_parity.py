@@ -641,11 +641,13 @@ COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260)
               (33, 1000, 1001), (2, 4096, 4096), (0, 8, 8), (70_000, 12, 12), (5, 100_003, 100_003),
               (301, 1028, 1032), (77, 2304, 2304), (1000, 3, 3), (777, 33, 33), (500, 65, 65), (3000, 17, 17),
               (200, 257, 257), (99, 1, 1), (4000, 20, 24), (64, 100, 100),
-              (1001, 6, 6), (4001, 10, 10), (37, 2, 2), (20_003, 7, 7), (9, 4097, 4097), (5, 3, 3)]
+              (1001, 6, 6), (4001, 10, 10), (37, 2, 2), (20_003, 7, 7), (9, 4097, 4097), (5, 3, 3),
+              (1000, 260, 260), (333, 516, 516), (41, 300, 300)]
 COL_POLICIES = (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=16, nontemporal=0),
                 dict(width=2), dict(width=4, unroll=2), dict(width=4, unroll=16, nontemporal=0, target_waves=7),
                 dict(prefetch=1), dict(prefetch=1, unroll=1, target_waves=7), dict(width=4, unroll=2, prefetch=1),
-                dict(width=2, unroll=16, prefetch=1, nontemporal=0))
+                dict(width=2, unroll=16, prefetch=1, nontemporal=0), dict(fold=1), dict(fold=16),
+                dict(fold=3, unroll=1, target_waves=7), dict(fold=8, width=4, unroll=2, prefetch=0))
 
 
 @pytest.mark.parametrize("rows,cols,ld", COL_SHAPES)
