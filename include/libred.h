@@ -121,11 +121,13 @@ red_status red_argmin_f32(const float *x, size_t n, int64_t *out, hipStream_t st
  * Sum of n 16-bit floats given as their bit patterns (2-byte aligned), into
  * one float32. Each element is widened exactly (bfloat16: the upper half of a
  * float32; IEEE half: the binary16 value); eight elements arrive per 16-byte
- * load. bfloat16 values are accumulated in float64 one by one (their range is
- * float32's, so a float32 partial could overflow). IEEE half values are first
- * added eight at a time in float32 (at most three roundings on any path, each
- * within 2^-24 of the magnitudes added; eight halves cannot overflow), then in
- * float64. Both round once to float32 at the end, far inside
+ * load. The eight values of a load are first added in float32 as a balanced
+ * tree (at most three roundings on any path, each within 2^-24 of the
+ * magnitudes added), and each load's total then enters float64 accumulators.
+ * bfloat16 values (float32's range) are scaled by 1/8 before the tree, which
+ * is exact for every bfloat16 and keeps eight values from overflowing, and
+ * the total is scaled back by 8 in float64; eight IEEE halves cannot
+ * overflow. Both round once to float32 at the end, far inside
  * |error| <= 1e-5 * sum|x|. NaN/inf and n == 0 as for red_sum_f32.
  */
 red_status red_sum_bf16_f32(const uint16_t *x, size_t n, float *out, hipStream_t stream);
