@@ -195,9 +195,11 @@ red_status red_rows_max_f32_ld(const float *x, size_t rows, size_t cols, size_t 
  * per column; max follows red_max_f32's rule. cols == 0 does nothing (out
  * may be NULL); rows == 0 stores 0.0f (sum) or -inf (max) in every out[c].
  * When there are few columns, the rows are cut into chunks whose partials
- * are added per column in a fixed order; those partials live in a scratch
- * buffer of the stream that is grown on demand (growing it waits for the
- * stream once). Errors as for the row entry points.
+ * are added per column in a fixed order; a contiguous matrix may also be
+ * read m rows at a time (one row of m * cols columns), and each column's m
+ * partial columns are added the same way. Those partials live in a scratch
+ * buffer of the stream that is grown on demand; an outgrown buffer is kept
+ * until the process exits. Errors as for the row entry points.
  */
 red_status red_cols_sum_f32(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                             hipStream_t stream);
