@@ -297,6 +297,16 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     const bool staged_default = p.short_rows == 0 && cols < 1024;
     if (staged_ok && (staged_default || p.short_rows >= 3)) {
         L.staged_u = fold * cols <= 1024 ? 4 : fold * cols <= 2048 ? 8 : 16;
+        size_t max_blocks = (size_t)p.max_blocks;
+        if (pol == nullptr && fold * cols >= 128 && cols <= 512) {
+            // Rows whose aligned span is 128 to 2048 floats stream best in
+            // 4096-float tiles on 1024 waves (65-512 floats: 5.1-6.4 ->
+            // 5.6-6.9 TB/s against 1024-float tiles on 2048 waves).
+            L.staged_u = 16;
+            max_blocks = 1024;
+        }
+        // An explicit policy may ask for larger tiles (unroll 8 or 16).
+        if (pol != nullptr && p.unroll > L.staged_u) L.staged_u = p.unroll >= 16 ? 16 : 8;
         L.staged_rows = (unsigned int)((256 * (size_t)L.staged_u) / (fold * cols) * fold);
         if (p.short_rows >= 3) {
             L.staged_log2s = p.short_rows - 3;
@@ -310,7 +320,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             L.staged_log2s = cols > 512 ? 6 : lg;
         }
         const size_t tiles = (rows + L.staged_rows - 1) / L.staged_rows;
-        L.grid = (int)(tiles < (size_t)p.max_blocks ? tiles : (size_t)p.max_blocks);
+        L.grid = (int)(tiles < max_blocks ? tiles : max_blocks);
         const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
         if (e != hipSuccess) return fail(e, RED_ERR_HIP);
         return RED_OK;
