@@ -82,9 +82,10 @@ typedef struct red_flat_policy {
  * row, rows of at least 16 elements): a single-wave streaming kernel that
  * reads rows through their covers and keeps the next tile of 64*unroll
  * vectors in flight while folding the current one, across row boundaries;
- * and `short_rows`, the kernels for short rows (`block`,
- * `unroll` and `prefetch` do not apply to them, `max_blocks` caps their
- * grid):
+ * and `short_rows`, the kernels for short rows (`block` and `prefetch` do
+ * not apply to them, `max_blocks` caps their grid, and an `unroll` of 8 or
+ * 16 gives the LDS-staged kernel tiles of that many 16-byte vectors per lane
+ * when that is more than the rows need):
  *   0  the library's choice: rows of fewer than 1024 floats of a contiguous
  *      (ld == cols), 16-byte aligned matrix go to the LDS-staged kernel, which
  *      loads tiles of whole rows as 16-byte vectors whatever the row length
