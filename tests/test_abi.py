@@ -117,6 +117,17 @@ def test_rows_argument_errors():
     assert L.red_rows_sum_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
     bad = rl.RowsPolicy(64, 4, 1, 16, 3)
     assert L.red_rows_sum_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
+    # The fields added for cover reading and the streaming kernel are checked
+    # before anything else (rows == 0 then makes a valid call a no-op).
+    base = rl.red_default_rows_policy()
+    assert base.cover == 0 and base.prefetch == 0 and base.short_rows == 0
+    for field, value, ok in (("cover", 3, False), ("cover", -1, False), ("cover", 2, True),
+                             ("prefetch", 2, False), ("prefetch", 1, True), ("short_rows", 10, False),
+                             ("short_rows", 9, True), ("split", 3, False)):
+        pol = rl.red_default_rows_policy()
+        setattr(pol, field, value)
+        want = rl.RED_OK if ok else INVALID
+        assert L.red_rows_sum_f32_with(None, 0, 3, 3, None, ctypes.byref(pol), None) == want, (field, value)
     for f in (L.red_rows_sum_f32_ld, L.red_rows_max_f32_ld):
         assert f(_p(A), 2, 5, 4, _p(B), None) == INVALID                   # ld < cols
         assert f(_p(A), 1 << 20, 4, 1 << 21, _p(B), None) == INVALID        # span > RED_MAX_N
@@ -138,6 +149,14 @@ def test_cols_argument_errors():
     assert L.red_cols_sum_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
     bad = rl.ColsPolicy(8, 1, 1024, 2)
     assert L.red_cols_max_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
+    base = rl.red_default_cols_policy()
+    assert base.fold == 0 and base.vec == 0
+    for field, value, ok in (("fold", 17, False), ("fold", -1, False), ("fold", 16, True), ("fold", 1, True),
+                             ("width", 3, False), ("target_waves", 0, False)):
+        pol = rl.red_default_cols_policy()
+        setattr(pol, field, value)
+        want = rl.RED_OK if ok else INVALID
+        assert L.red_cols_sum_f32_with(None, 5, 0, 0, None, ctypes.byref(pol), None) == want, (field, value)
 
 
 def test_ablate_argument_errors():
