@@ -1167,3 +1167,47 @@ def test_beyond_2p32_elements():
     assert torch.all(rl.red_rows_sum_f32(r2) == float(1 << 25))
     del x, m, r2
     torch.cuda.empty_cache()
+
+
+def test_concurrent_streams_from_host_threads():
+    # Calls from several host threads, each on its own stream, run at once
+    # (ctypes releases the interpreter lock during each call): every stream
+    # gets its own workspace and scratch, created under the library's lock,
+    # and every result equals the one computed alone.
+    import threading
+    arrays = [device_view(W.make("normal", (1 << 20) + 7 * k, 60 + k), k % 4) for k in range(4)]
+    mats = [device_view(W.make("uniform01", 700 * (300 + k), 70 + k).reshape(700, 300 + k), 0) for k in range(4)]
+    want = []
+    for a, m in zip(arrays, mats):
+        want.append((rl.red_sum_f32(a).clone(), rl.red_max_f32(a).clone(), rl.red_rows_sum_f32(m).clone(),
+                     rl.red_cols_sum_f32(m).clone(), rl.red_argmax_f32(a).clone()))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    got = [None] * 4
+    errors = []
+
+    def work(k):
+        try:
+            with torch.cuda.stream(streams[k]):
+                res = None
+                for _ in range(20):
+                    res = (rl.red_sum_f32(arrays[k]), rl.red_max_f32(arrays[k]), rl.red_rows_sum_f32(mats[k]),
+                           rl.red_cols_sum_f32(mats[k]), rl.red_argmax_f32(arrays[k]))
+                streams[k].synchronize()
+                got[k] = res
+        except Exception as e:  # reported below, in the test's thread
+            errors.append(e)
+
+    say("four host threads, four streams")
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k in range(4):
+        for g, w in zip(got[k], want[k]):
+            assert torch.equal(g, w), k
