@@ -176,7 +176,11 @@ red_status red_rows_max_f32(const float *x, size_t rows, size_t cols, float *out
 /*
  * The same row reductions over rows that start `ld` elements apart
  * (ld >= cols): row r is x[r*ld .. r*ld + cols). The elements between the
- * end of one row and the start of the next are not read. ld < cols, or a
+ * end of one row and the start of the next never enter a result (rows that
+ * do not start 16-byte aligned are read as the aligned 16-byte vectors that
+ * cover them, which may load up to 3 of those elements on either side of a
+ * row, always inside the span x[0 .. (rows - 1) * ld + cols); nothing
+ * outside the span is read). ld < cols, or a
  * span (rows - 1) * ld + cols above RED_MAX_N, is RED_ERR_INVALID_ARG. With
  * ld == cols these are red_rows_sum_f32 / red_rows_max_f32. For fewer than
  * 1024 rows of at least 8192 elements, each row is split across several

@@ -597,7 +597,7 @@ def test_rows_random(rows, cols):
                                           (1, 10, 10), (5, 0, 3), (1000, 129, 1024), (300, 16, 20),
                                           (100, 64, 68), (40, 128, 132), (65, 4, 8)])
 def test_rows_strided(rows, cols, ld):
-    # Rows spaced ld apart: the gap holds NaN, which must never be read.
+    # Rows spaced ld apart: the gap holds NaN, which must never enter a result.
     rng = np.random.default_rng(rows + cols + ld)
     full = np.full((rows, ld), np.nan, np.float32)
     full[:, :cols] = rng.standard_normal((rows, cols)).astype(np.float32)
