@@ -403,18 +403,19 @@ double cols_lane_use(size_t groups) {
     return (double)groups / (double)(64 * ((groups + 63) / 64));
 }
 
-// Rows per view row for a contiguous matrix (1 = no fold): among the
-// multiples m of 4 / gcd(cols, 4) up to 16 (and at most rows), the one whose
-// view uses the most lanes; a larger m is taken only for 1% more of them,
-// since the second pass reads m partials per chunk. A width that is a multiple of 4 is
-// folded only when that uses at least 5% more of the lanes (65 groups of
-// four columns, say, leave a second block per row with one group).
+// Rows per view row for a contiguous matrix (1 = no fold). m is a multiple
+// of m0 = 4 / gcd(cols, 4), at most 16 and at most rows:
+// - a width of at least 256 that is not a multiple of 4 takes the largest;
+// - otherwise the m whose view uses the most lanes, a larger m only for 1%
+//   more of them (the second pass reads m partials per chunk);
+// - a width that is a multiple of 4 is folded only when that uses at least
+//   5% more lanes than the matrix itself (65 groups of four columns, say,
+//   leave a second block per row phase with one group).
 size_t fold_rows(size_t rows, size_t cols) {
     const size_t m0 = cols % 4 == 0 ? 1 : cols % 2 == 0 ? 2 : 4;
     if (m0 > 1 && cols >= 256) {
-        // Widths of at least 256 that are not a multiple of 4 take 16 rows
-        // (fewer if the matrix has fewer): over 1023 to 65537 columns that
-        // ran 3-24% faster than 4 rows, which already use 98% of the lanes.
+        // Over 1023 to 65537 columns, 16 rows ran 3-24% faster than 4 rows,
+        // which already use 98% of the lanes.
         size_t m = 16;
         while (m > rows || cols * m > RED_MAX_N) m -= m0;
         return m < m0 ? 1 : m;
