@@ -99,7 +99,10 @@ typedef struct red_flat_policy {
  *   3-9  the LDS-staged kernel with 2^(short_rows - 3) lanes per row where it
  *      applies (contiguous, 16-byte aligned, at least 4 elements, and 4 rows
  *      of an odd width, 2 of a width of 2 mod 4, or 1 row, fit 4096 floats),
- *      else as 2. */
+ *      else as 2;
+ *   10-16  the same with 2^(short_rows - 10) lanes per row, which read
+ *      16-byte vectors from LDS when the rows hold whole vectors (cols a
+ *      multiple of 4; the default for such rows of at most 64 floats). */
 typedef struct red_rows_policy {
     int block;
     int unroll;

@@ -57,6 +57,7 @@ struct RowsLaunch {
     unsigned int staged_rows;  //   256 * staged_u elements), 2^staged_log2s lanes per row
     int staged_log2s;
     int cover;          // one wave per row: read each row through its aligned cover
+    int staged_vread;   // the LDS-staged kernel reads 16-byte vectors (rows of whole vectors)
 };
 constexpr size_t kMaxSplitPartials = 32768;
 

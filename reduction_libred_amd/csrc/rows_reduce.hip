@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
 // to the waves, and the next tile's loads are issued before the current tile
 // is reduced. A lane with no whole vector to read in a tile reads vector 0 of
 // the matrix instead (no load sits under a lane mask).
-template <class Op, int LOG2S, int U, bool NT>
+template <class Op, int LOG2S, int U, bool NT, bool VREAD>
 __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, unsigned int R,
                                                             typename Op::out_t* __restrict__ out) {
@@ -496,7 +496,23 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
         for (unsigned int r0 = 0; r0 < rows_t; r0 += P) {
             const unsigned int r = r0 + (lane >> LOG2S);
             acc_t a = Op::identity();
-            if (r < rows_t) {
+            if constexpr (VREAD) {
+                // Rows of whole 16-byte vectors, read a vector at a time:
+                // lane s takes vectors s, s + S, ... of its row. With S no
+                // smaller than the row's vectors, the lanes of a pass read one
+                // contiguous run of LDS (no bank conflicts); element reads at
+                // a stride of cols words put rows on the same banks whenever
+                // cols is a multiple of 16.
+                if (r < rows_t) {
+                    const unsigned int V = C / (unsigned int)E;
+                    const vec_t* rowv = stage + r * V;
+                    for (unsigned int j = s; j < V; j += S) {
+                        const vec_t v = rowv[j];
+#pragma unroll
+                        for (int k = 0; k < (int)E; ++k) a = Op::combine(a, Op::lift(v[k], j * E + k));
+                    }
+                }
+            } else if (r < rows_t) {
                 const elem_t* row = lds + r * C;
                 unsigned int j = s;
                 for (; j + 3 * S < C; j += 4 * S) {  // four LDS reads in flight
@@ -571,7 +587,7 @@ bool rows_policy_supported(const RowsPolicy& p) {
     const bool b = p.block == 64 || p.block == 128 || p.block == 256 || p.block == 512;
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.max_blocks >= 1 && p.split >= 0 &&
-           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.cover >= 0 && p.cover <= 2 && p.short_rows >= 0 && p.short_rows <= 9;
+           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.cover >= 0 && p.cover <= 2 && p.short_rows >= 0 && p.short_rows <= 16;
 }
 
 template <class Op, int BLOCK, int UNROLL>
@@ -691,16 +707,23 @@ static hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_
     }
 }
 
+template <class Op, int LOG2S, int U, bool VREAD>
+static hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
+                                  const RowsLaunch& L, bool nt, hipStream_t stream) {
+    if (nt)
+        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD>), dim3(L.grid), dim3(kWave), 0, stream,
+                           x, rows, cols, L.staged_rows, out);
+    else
+        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD>), dim3(L.grid), dim3(kWave), 0, stream,
+                           x, rows, cols, L.staged_rows, out);
+    return hipGetLastError();
+}
+
 template <class Op, int LOG2S, int U>
 static hipError_t rows_staged_su(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
                                  const RowsLaunch& L, bool nt, hipStream_t stream) {
-    if (nt)
-        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true>), dim3(L.grid), dim3(kWave), 0, stream, x, rows,
-                           cols, L.staged_rows, out);
-    else
-        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false>), dim3(L.grid), dim3(kWave), 0, stream, x,
-                           rows, cols, L.staged_rows, out);
-    return hipGetLastError();
+    if (L.staged_vread) return rows_staged_suv<Op, LOG2S, U, true>(x, rows, cols, out, L, nt, stream);
+    return rows_staged_suv<Op, LOG2S, U, false>(x, rows, cols, out, L, nt, stream);
 }
 
 template <class Op, int LOG2S>

@@ -122,8 +122,9 @@ def test_rows_argument_errors():
     base = rl.red_default_rows_policy()
     assert base.cover == 0 and base.prefetch == 0 and base.short_rows == 0
     for field, value, ok in (("cover", 3, False), ("cover", -1, False), ("cover", 2, True),
-                             ("prefetch", 2, False), ("prefetch", 1, True), ("short_rows", 10, False),
-                             ("short_rows", 9, True), ("split", 3, False)):
+                             ("prefetch", 2, False), ("prefetch", 1, True), ("short_rows", 10, True),
+                             ("short_rows", 9, True), ("short_rows", 16, True), ("short_rows", 17, False),
+                             ("split", 3, False)):
         pol = rl.red_default_rows_policy()
         setattr(pol, field, value)
         want = rl.RED_OK if ok else INVALID

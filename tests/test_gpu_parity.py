@@ -566,7 +566,8 @@ ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1,
                 dict(short_rows=2), dict(short_rows=3), dict(short_rows=6, max_blocks=3),
                 dict(short_rows=9, nontemporal=0), dict(short_rows=5, max_blocks=1),
                 dict(cover=2, short_rows=1), dict(cover=2, unroll=16, max_blocks=3, short_rows=1),
-                dict(cover=2, block=256, unroll=2, short_rows=1), dict(cover=1, short_rows=1, max_blocks=5))
+                dict(cover=2, block=256, unroll=2, short_rows=1), dict(cover=1, short_rows=1, max_blocks=5),
+                dict(short_rows=11), dict(short_rows=14, unroll=16, max_blocks=3), dict(short_rows=16))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
