@@ -4,21 +4,27 @@
 //
 // The lesson's reduction gives one output per block segment
 // ("03_shared_memory_sync_reduction.py", demo 3). Here the segment is a row,
-// and two layouts cover the shapes:
-//   one wave per row (many rows): a 64-lane wave owns one row at a time, with
-//       no LDS, no barrier and no cross-block combine; a 4096-float row is
-//       16 KiB, i.e. 16 aligned 16-byte loads per lane;
-//   split rows (few long rows): each row is cut across `gx` single-wave
-//       blocks that stream tiles of 64*UNROLL vectors dealt round-robin, each
-//       storing one partial; a second launch combines each row's partials in
-//       index order with one wave per row.
-// A row's start may be misaligned (x not 16-byte aligned, or ld not a
-// multiple of 4). Then a row is read as the aligned 16-byte vectors that
-// cover it, with the elements outside the row masked when folded (the cover
-// kernels below); aligned rows, and the split kernel, peel a head and tail
-// element by element (none when aligned). Short rows have kernels of their
-// own (LDS-staged and packed, below). Sums accumulate in float64 and round
-// once per row.
+// and the kernels, in the order of this file, cover the shapes:
+//   rows_reduce_kernel, one wave per row (many long rows): a 64-lane wave
+//       owns one row at a time, with no LDS, no barrier and no cross-block
+//       combine; a 4096-float row is 16 KiB, i.e. 16 aligned 16-byte loads
+//       per lane;
+//   rows_cover_kernel, the same for rows that do not start 16-byte aligned
+//       (x unaligned, or ld not a multiple of 4): a row is read as the
+//       aligned 16-byte vectors that cover it, elements outside the row
+//       masked when folded; rows_stream_kernel reads rows the same way with
+//       the next tile always in flight across rows (a policy option);
+//   rows_packed_kernel, short strided or unaligned rows: several rows per
+//       load, a segment of lanes per row;
+//   rows_staged_kernel, short rows of a contiguous matrix: tiles of whole
+//       rows loaded as 16-byte vectors into LDS and reduced from there;
+//   rows_split_kernel + rows_combine_kernel, few long rows: each row is cut
+//       across `gx` single-wave blocks that stream tiles of 64*UNROLL
+//       vectors, each storing one partial; a second launch combines each
+//       row's partials in index order with one wave per row.
+// rows_reduce_kernel and the split kernel peel an unaligned row's head and
+// tail element by element (none when aligned). Sums accumulate in float64
+// and round once per row.
 #include "device_common.hpp"
 #include "launch.hpp"
 
