@@ -8,9 +8,14 @@
 // matrix is narrow), and walks down its rows with UNROLL loads in flight. For
 // parallelism when there are few columns, the rows are dealt round-robin to
 // `nchunks` row phases; pass 1 stores one partial per (phase, column), and
-// pass 2 adds each column's partials with one wave per column in a fixed
-// order (deterministic). With a single phase pass 1 stores the result
-// directly.
+// pass 2 adds each column's partials in a fixed order (deterministic): one
+// wave per column (cols_combine_kernel), or one thread per column when there
+// are many columns and few partials each (cols_combine_wide_kernel). With a
+// single phase pass 1 stores the result directly. A contiguous matrix may be
+// read as rows / m rows of m * cols columns (the host picks m; the kernels
+// see an ordinary matrix): then pass 2 also adds the m partial columns of
+// each column and the last rows % m rows (cols_fold_combine_kernel, or the
+// wide kernel).
 #include "device_common.hpp"
 #include "launch.hpp"
 
