@@ -298,10 +298,11 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (staged_ok && (staged_default || p.short_rows >= 3)) {
         L.staged_u = fold * cols <= 1024 ? 4 : fold * cols <= 2048 ? 8 : 16;
         size_t max_blocks = (size_t)p.max_blocks;
-        if (pol == nullptr && fold * cols >= 128 && cols <= 512) {
-            // Rows whose aligned span is 128 to 2048 floats stream best in
-            // 4096-float tiles on 1024 waves (65-512 floats: 5.1-6.4 ->
-            // 5.6-6.9 TB/s against 1024-float tiles on 2048 waves).
+        const bool vread_default = cols % 4 == 0 && cols <= 64;
+        if (pol == nullptr && cols >= 32 && cols <= 512 && !(vread_default && cols < 128)) {
+            // Rows of 32 to 512 floats read element by element stream best in
+            // 4096-float tiles on 1024 waves (33-512 floats: 4.5-6.4 ->
+            // 5.5-6.9 TB/s against 1024-float tiles on 2048 waves).
             L.staged_u = 16;
             max_blocks = 1024;
         }
@@ -313,7 +314,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             L.staged_vread = cols % 4 == 0 ? 1 : 0;
         } else if (p.short_rows >= 3) {
             L.staged_log2s = p.short_rows - 3;
-        } else if (cols % 4 == 0 && cols <= 64) {
+        } else if (vread_default) {
             // Rows of up to 16 whole vectors: 16-byte reads from LDS, one lane
             // per 2 vectors of the row (per 4 from 16 vectors). Element reads
             // at a stride of cols words put the rows of a pass on the same
@@ -324,10 +325,11 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             L.staged_log2s = lg;
             L.staged_vread = 1;
         } else {
-            // Lanes per row: the largest power of two up to cols / 8 (below
-            // 64 floats) or cols / 16 (up to 512), so a lane adds 8-16
-            // elements a row; longer rows take the whole wave.
-            const size_t per = cols < 64 ? 8 : 16;
+            // Lanes per row: the largest power of two up to cols / 8 below
+            // 32 floats (1024-float tiles), cols / 24 from there, or cols / 16
+            // for rows of whole vectors from 128 floats (4096-float tiles);
+            // longer rows take the whole wave.
+            const size_t per = cols < 32 ? 8 : (cols % 4 == 0 && cols >= 128) ? 16 : 24;
             int lg = 0;
             while (lg < 6 && ((size_t)2 << lg) <= cols / per) ++lg;
             L.staged_log2s = cols > 512 ? 6 : lg;
