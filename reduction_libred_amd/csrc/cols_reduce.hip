@@ -260,7 +260,7 @@ bool cols_policy_supported(const ColsPolicy& p) {
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     const bool w = p.width == 1 || p.width == 2 || p.width == 4;
     return u && w && (p.nontemporal == 0 || p.nontemporal == 1) && (p.prefetch == 0 || p.prefetch == 1) &&
-           p.target_waves >= 1 && (p.vec == 0 || p.vec == 1 || p.vec == 4) && p.fold >= 0 && p.fold <= 16;
+           p.target_waves >= 1 && (p.vec == 0 || p.vec == 1 || p.vec == 4) && p.fold >= 0 && p.fold <= 64;
 }
 
 template <class Op, int VEC, int CW, int UNROLL, bool PF>

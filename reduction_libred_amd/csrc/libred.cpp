@@ -419,10 +419,11 @@ double cols_lane_use(size_t groups) {
 }
 
 // Rows per view row for a contiguous matrix (1 = no fold). m is a multiple
-// of m0 = 4 / gcd(cols, 4), at most 16 and at most rows:
-// - a width of at least 256 that is not a multiple of 4 takes the largest;
-// - otherwise the m whose view uses the most lanes, a larger m only for 1%
-//   more of them (the second pass reads m partials per chunk);
+// of m0 = 4 / gcd(cols, 4) and at most rows:
+// - a width of at least 256 that is not a multiple of 4 takes the largest
+//   up to 16, an odd width of 33 to 255 the largest up to 64;
+// - otherwise the m up to 16 whose view uses the most lanes, a larger m
+//   only for 1% more of them (the second pass reads m partials per chunk);
 // - a width that is a multiple of 4 is folded only when that uses at least
 //   5% more lanes than the matrix itself (65 groups of four columns, say,
 //   leave a second block per row phase with one group).
@@ -432,6 +433,15 @@ size_t fold_rows(size_t rows, size_t cols) {
         // Over 1023 to 65537 columns, 16 rows ran 3-24% faster than 4 rows,
         // which already use 98% of the lanes.
         size_t m = 16;
+        while (m > rows || cols * m > RED_MAX_N) m -= m0;
+        return m < m0 ? 1 : m;
+    }
+    if (m0 == 4 && cols >= 32) {
+        // Odd widths of 33 to 255 take 64 rows (fewer if the matrix has
+        // fewer): over 33 to 113 columns that ran from as fast (57) to 20%
+        // faster (33: 5.6 -> 6.7 TB/s; 65: 5.5 -> 6.4) than the choice by
+        // lane use below, whose 4-16 rows already keep most lanes busy.
+        size_t m = 64;
         while (m > rows || cols * m > RED_MAX_N) m -= m0;
         return m < m0 ? 1 : m;
     }

@@ -643,7 +643,7 @@ COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260)
               (301, 1028, 1032), (77, 2304, 2304), (1000, 3, 3), (777, 33, 33), (500, 65, 65), (3000, 17, 17),
               (200, 257, 257), (99, 1, 1), (4000, 20, 24), (64, 100, 100),
               (1001, 6, 6), (4001, 10, 10), (37, 2, 2), (20_003, 7, 7), (9, 4097, 4097), (5, 3, 3),
-              (1000, 260, 260), (333, 516, 516), (41, 300, 300)]
+              (1000, 260, 260), (333, 516, 516), (41, 300, 300), (3001, 33, 33), (70, 65, 65), (63, 97, 97)]
 COL_POLICIES = (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=16, nontemporal=0),
                 dict(width=2), dict(width=4, unroll=2), dict(width=4, unroll=16, nontemporal=0, target_waves=7),
                 dict(prefetch=1), dict(prefetch=1, unroll=1, target_waves=7), dict(width=4, unroll=2, prefetch=1),
