@@ -152,7 +152,7 @@ def test_cols_argument_errors():
     assert L.red_cols_max_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
     base = rl.red_default_cols_policy()
     assert base.fold == 0 and base.vec == 0
-    for field, value, ok in (("fold", 17, False), ("fold", -1, False), ("fold", 16, True), ("fold", 1, True),
+    for field, value, ok in (("fold", 65, False), ("fold", -1, False), ("fold", 64, True), ("fold", 17, True), ("fold", 1, True),
                              ("width", 3, False), ("target_waves", 0, False)):
         pol = rl.red_default_cols_policy()
         setattr(pol, field, value)
