@@ -421,9 +421,12 @@ double cols_lane_use(size_t groups) {
 // Rows per view row for a contiguous matrix (1 = no fold). m is a multiple
 // of m0 = 4 / gcd(cols, 4) and at most rows:
 // - a width of at least 256 that is not a multiple of 4 takes the largest
-//   up to 16, an odd width of 33 to 255 the largest up to 64;
-// - otherwise the m up to 16 whose view uses the most lanes, a larger m
-//   only for 1% more of them (the second pass reads m partials per chunk);
+//   up to 16;
+// - a width of 32 to 255 (a multiple of 4 only if its own rows leave 5% of
+//   the lanes idle) takes the smallest m with 512 groups of four columns in
+//   a view row, at most 64;
+// - otherwise the m up to 16 whose view uses the most lanes, the smallest
+//   on a tie;
 // - a width that is a multiple of 4 is folded only when that uses at least
 //   5% more lanes than the matrix itself (65 groups of four columns, say,
 //   leave a second block per row phase with one group).
@@ -436,12 +439,16 @@ size_t fold_rows(size_t rows, size_t cols) {
         while (m > rows || cols * m > RED_MAX_N) m -= m0;
         return m < m0 ? 1 : m;
     }
-    if (m0 == 4 && cols >= 32) {
-        // Odd widths of 33 to 255 take 64 rows (fewer if the matrix has
-        // fewer): over 33 to 113 columns that ran from as fast (57) to 20%
-        // faster (33: 5.6 -> 6.7 TB/s; 65: 5.5 -> 6.4) than the choice by
-        // lane use below, whose 4-16 rows already keep most lanes busy.
-        size_t m = 64;
+    if (cols >= 32 && cols < 256 && (m0 > 1 || cols_lane_use(cols / 4) < 0.95)) {
+        // Widths of 32 to 255 (multiples of 4 only when their own rows leave
+        // lanes idle) take the smallest m whose view rows hold 512 groups of
+        // four columns (8 KiB), at most 64: over 33 to 132 columns that
+        // matched the best measured m within 1-4% (33: 5.6 -> 6.7 TB/s, 65:
+        // 5.5 -> 6.8, 68: 6.0 -> 6.7 against the choice by lane use below,
+        // whose 4-16 rows already keep most lanes busy).
+        size_t m = (2048 + cols - 1) / cols;
+        m = (m + m0 - 1) / m0 * m0;
+        if (m > 64) m = 64;
         while (m > rows || cols * m > RED_MAX_N) m -= m0;
         return m < m0 ? 1 : m;
     }
@@ -449,7 +456,7 @@ size_t fold_rows(size_t rows, size_t cols) {
     double best_use = -1.0;
     for (size_t m = m0; m <= 16 && m <= rows && cols * m <= RED_MAX_N; m += m0) {
         const double use = cols_lane_use(m * cols / 4);
-        if (use > best_use + 0.01) best_use = use, best = m;  // a larger m must gain 1% of the lanes
+        if (use > best_use + 1e-9) best_use = use, best = m;  // the smallest m on a tie
     }
     if (m0 == 1 && best_use < cols_lane_use(cols / 4) + 0.05) return 1;
     return best;
