@@ -559,7 +559,8 @@ ROW_SHAPES = [(1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1
               (5, 64), (6, 65), (257, 4096), (2, 100_003), (4097, 3), (333, 1024), (50, 513),
               (1000, 4), (777, 16), (301, 32), (129, 128), (77, 200), (33, 8), (1025, 12), (70, 512),
               (200, 33), (100, 511), (1000, 100), (3000, 2), (1, 3), (2, 2), (5, 6), (1001, 6),
-              (1, 2048), (2, 1023), (3, 1025), (300, 7), (9, 510), (20_001, 5), (5, 1021), (40, 700), (3, 1023)]
+              (1, 2048), (2, 1023), (3, 1025), (300, 7), (9, 510), (20_001, 5), (5, 1021), (40, 700), (3, 1023),
+              (1, 5000), (2, 1030), (7, 1031), (1, 16), (17, 16)]
 ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1, max_blocks=3, short_rows=1),
                 dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
                 dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0),
