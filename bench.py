@@ -365,6 +365,10 @@ def main():
     measure("red_min_f32 sum_max_f32_2p28", lambda: rl.red_min_f32(x, out=mout), nbytes)
     iout = torch.empty((), dtype=torch.int64, device=dev)
     measure("red_argmax_f32 sum_max_f32_2p28", lambda: rl.red_argmax_f32(x, out=iout), 4 * n + 8)
+    # The int32 sum over 1 GiB: the same 2^28 words read as int32 (their bit
+    # patterns; every value is exact in the int64 accumulator).
+    measure("red_sum_i32_i64 2^28 int32 (1 GiB, the bits of the normal array)",
+            lambda: rl.red_sum_i32_i64(x.view(torch.int32), out=iout), 4 * n + 8)
     if not args.quick:
         # The same 2^28 values rounded to 16-bit formats (2^29 elements = 1 GiB
         # after doubling the count) and a 1 GiB float64 array.

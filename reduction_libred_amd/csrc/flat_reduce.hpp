@@ -59,10 +59,21 @@ __device__ __forceinline__ void body_grid_stride(const typename Op::vec_t* __res
 }
 
 // One tile of a wave: UNROLL loads, each of 64 lanes x 16 bytes = 1 KiB.
-template <bool NT, class V, int UNROLL>
+// With GROUP the loads are held together by a scheduling barrier: for the
+// int32 sum the compiler otherwise split the next tile's loads around the
+// fold of the current one, leaving half of them in flight during its waits
+// (1 GiB: 6.6 -> 7.3 TB/s with the barrier). The other operators keep the
+// compiler's own order.
+template <class Op>
+struct GroupLoads : std::false_type {};
+template <>
+struct GroupLoads<SumI32> : std::true_type {};
+
+template <bool NT, bool GROUP = false, class V, int UNROLL>
 __device__ __forceinline__ void load_tile(V (&v)[UNROLL], const V* __restrict__ p) {
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
+    if constexpr (GROUP) __builtin_amdgcn_sched_barrier(0);
 }
 
 // Fold a tile loaded from body vector index v0 (lane's first vector).
@@ -103,21 +114,22 @@ __device__ __forceinline__ void body_wave_tiles(const typename Op::vec_t* __rest
         // Two register buffers, a and b, alternate: the loads of the next
         // tile go into one while the other is folded, so the wait before a
         // fold leaves the next tile's loads in flight.
+        constexpr bool G = GroupLoads<Op>::value;
         vec_t a[UNROLL], b[UNROLL];
-        load_tile<NT>(a, xv + t * TILE + lane);
+        load_tile<NT, G>(a, xv + t * TILE + lane);
         while (true) {
             if (t + nwaves >= ntiles) {
                 fold_tile<Op>(acc, a, t * TILE + lane, head);
                 break;
             }
-            load_tile<NT>(b, xv + (t + nwaves) * TILE + lane);
+            load_tile<NT, G>(b, xv + (t + nwaves) * TILE + lane);
             fold_tile<Op>(acc, a, t * TILE + lane, head);
             t += nwaves;
             if (t + nwaves >= ntiles) {
                 fold_tile<Op>(acc, b, t * TILE + lane, head);
                 break;
             }
-            load_tile<NT>(a, xv + (t + nwaves) * TILE + lane);
+            load_tile<NT, G>(a, xv + (t + nwaves) * TILE + lane);
             fold_tile<Op>(acc, b, t * TILE + lane, head);
             t += nwaves;
         }

@@ -1049,6 +1049,19 @@ def test_full_sum_max_f32_2p28():
     torch.cuda.empty_cache()
 
 
+def test_full_sum_i32_bits_2p28():
+    # The int32 sum at the 1 GiB size the bench times: the 2^28 words of the
+    # normal array read as int32 (large values of both signs), bit-exact
+    # against the oracle's int64 sum.
+    a, x = _load("sum_max_f32_2p28")
+    say("red_sum_i32_i64 over the bits of sum_max_f32_2p28")
+    out = rl.red_sum_i32_i64(x.view(torch.int32))
+    torch.cuda.synchronize()
+    assert int(out.item()) == oracle.sum_i32_i64(a.view(np.int32))
+    del x
+    torch.cuda.empty_cache()
+
+
 def test_full_sum_max_f32_fused_2p28():
     a, x = _load("sum_max_f32_2p28")
     say("red_sum_max_f32 sum_max_f32_2p28")
