@@ -102,7 +102,13 @@ typedef struct red_flat_policy {
  *      else as 2;
  *   10-16  the same with 2^(short_rows - 10) lanes per row, which read
  *      16-byte vectors from LDS when the rows hold whole vectors (cols a
- *      multiple of 4; the default for such rows of at most 64 floats). */
+ *      multiple of 4; the default for such rows of at most 64 floats);
+ * and `defer` (the LDS-staged kernel): 0 = a wave keeps its row results in
+ * LDS and stores them after its last tile when they fit beside its staging
+ * tile in its share of the CU's LDS (the CU's LDS over the waves the grid
+ * puts on each CU, and at most one block's limit), else stores each tile's
+ * results as the tile is reduced; 1 = always as each tile is reduced. The
+ * results are the same either way. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
@@ -112,6 +118,7 @@ typedef struct red_rows_policy {
     int prefetch;
     int short_rows;
     int cover;
+    int defer;
 } red_rows_policy;
 
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,

@@ -52,7 +52,8 @@ class RowsPolicy(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int), ("unroll", ctypes.c_int),
                 ("nontemporal", ctypes.c_int), ("max_blocks", ctypes.c_int),
                 ("split", ctypes.c_int), ("prefetch", ctypes.c_int), ("short_rows", ctypes.c_int),
-                ("cover", ctypes.c_int)]
+                ("cover", ctypes.c_int),
+                ("defer", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

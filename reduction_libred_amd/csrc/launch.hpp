@@ -41,6 +41,7 @@ struct RowsPolicy {
     int prefetch;
     int short_rows;
     int cover;
+    int defer;
 };
 
 // How one row call launches: `grid` blocks of the one-wave-per-row kernel,
@@ -58,6 +59,8 @@ struct RowsLaunch {
     int staged_log2s;
     int cover;          // one wave per row: read each row through its aligned cover
     int staged_vread;   // the LDS-staged kernel reads 16-byte vectors (rows of whole vectors)
+    unsigned int staged_hold;  // > 0: the LDS-staged kernel holds this many results per wave in
+                               //   dynamic LDS and stores them after the wave's last tile
 };
 constexpr size_t kMaxSplitPartials = 32768;
 

@@ -29,6 +29,8 @@ red_status fail(hipError_t e, red_status code) {
 
 struct DeviceInfo {
     int cu_count;
+    size_t lds_per_cu;     // bytes of LDS per compute unit
+    size_t lds_per_block;  // bytes of LDS one block may use
     char arch[64];
 };
 
@@ -64,7 +66,7 @@ constexpr FlatPolicy kFlatCached = {1024, 1, 4, 1, libred::kWaveTiles, 1, libred
 constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
 constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
-constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0, 0};
+constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0, 0, 0};
 // Split-row mode: used automatically for fewer than kSplitRowsBelow rows
 // whose rows hold at least kSplitMinCols elements; aims for about
 // kSplitTargetWaves waves in all.
@@ -110,6 +112,8 @@ red_status current_device(int* dev_out, DeviceInfo* info_out) {
         e = hipGetDeviceProperties(&prop, dev);
         if (e != hipSuccess) return fail(e, RED_ERR_HIP);
         strncpy(di.arch, prop.gcnArchName, sizeof(di.arch) - 1);
+        di.lds_per_cu = prop.maxSharedMemoryPerMultiProcessor;
+        di.lds_per_block = prop.sharedMemPerBlock;
         if (di.cu_count <= 0) return fail(hipErrorInvalidDevice, RED_ERR_NO_DEVICE);
         it = g_devices.emplace(dev, di).first;
     }
@@ -229,8 +233,8 @@ RowsPolicy default_rows(size_t cols) {
 
 RowsPolicy to_rows(const red_rows_policy* p, size_t cols) {
     if (!p) return default_rows(cols);
-    RowsPolicy r = {p->block, p->unroll,     p->nontemporal, p->max_blocks,
-                    p->split, p->prefetch, p->short_rows,  p->cover};
+    RowsPolicy r = {p->block,    p->unroll,     p->nontemporal, p->max_blocks, p->split,
+                    p->prefetch, p->short_rows, p->cover,       p->defer};
     return r;
 }
 
@@ -286,7 +290,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
 
-    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
+    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     // Rows of fewer than 1024 floats of a contiguous, 16-byte aligned matrix
     // go to the LDS-staged kernel (short_rows 0), or do so with
     // 2^(short_rows - 3) lanes per row (short_rows 3-9), as long as a tile
@@ -296,19 +300,10 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     const bool staged_ok = contiguous && aligned(x, 16) && cols > 0 && rows * cols >= 4 && fold * cols <= 4096;
     const bool staged_default = p.short_rows == 0 && cols < 1024;
     if (staged_ok && (staged_default || p.short_rows >= 3)) {
-        L.staged_u = fold * cols <= 1024 ? 4 : fold * cols <= 2048 ? 8 : 16;
+        const size_t base_u = fold * cols <= 1024 ? 4 : fold * cols <= 2048 ? 8 : 16;
         size_t max_blocks = (size_t)p.max_blocks;
         const bool vread_default = cols % 4 == 0 && cols <= 64;
-        if (pol == nullptr && cols >= 32 && cols <= 512 && !(vread_default && cols < 128)) {
-            // Rows of 32 to 512 floats read element by element stream best in
-            // 4096-float tiles on 1024 waves (33-512 floats: 4.5-6.4 ->
-            // 5.5-6.9 TB/s against 1024-float tiles on 2048 waves).
-            L.staged_u = 16;
-            max_blocks = 1024;
-        }
-        // An explicit policy may ask for larger tiles (unroll 8 or 16).
-        if (pol != nullptr && p.unroll > L.staged_u) L.staged_u = p.unroll >= 16 ? 16 : 8;
-        L.staged_rows = (unsigned int)((256 * (size_t)L.staged_u) / (fold * cols) * fold);
+        // Lanes per row first: the tile size below depends on them.
         if (p.short_rows >= 10) {  // vector reads (rows of whole vectors), 2^(short_rows - 10) lanes
             L.staged_log2s = p.short_rows - 10;
             L.staged_vread = cols % 4 == 0 ? 1 : 0;
@@ -334,8 +329,57 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             while (lg < 6 && ((size_t)2 << lg) <= cols / per) ++lg;
             L.staged_log2s = cols > 512 ? 6 : lg;
         }
+        // Tile size: 16-byte vectors per lane (4, 8 or 16, at least base_u
+        // so that a tile holds one aligned span of rows).
+        const size_t pass = (size_t)64 >> L.staged_log2s;  // rows reduced at a time
+        auto tile_rows = [&](size_t u) { return (256 * u) / (fold * cols) * fold; };
+        auto pass_use = [&](size_t u) {  // share of the passes' row slots that hold a row
+            const size_t r = tile_rows(u);
+            return r == 0 ? 0.0 : (double)r / (double)(pass * ((r + pass - 1) / pass));
+        };
+        size_t u = base_u;
+        if (pol == nullptr && vread_default && cols >= 44) {
+            // Rows of 11-16 whole vectors (measured on 1 GiB, sums): 4096-float
+            // tiles on 1024 waves for 44-60 floats (48: 5.9 -> 6.3, 60: 5.4 ->
+            // 6.4 TB/s), 2048-float tiles on 1024 waves for 64 floats (6.5 ->
+            // 6.8 TB/s); narrower rows keep 1024-float tiles on 2048 waves.
+            u = cols == 64 ? 8 : 16;
+            max_blocks = 1024;
+        } else if (pol == nullptr && !vread_default && cols >= 32 && cols <= 512) {
+            // Rows of 33 to 512 floats read element by element: the largest
+            // tile whose passes are within 2% as full as the fullest, on 1024
+            // waves for 4096-float tiles and 2048 below (over 54 widths of
+            // 33-512 floats on 1 GiB, 97.3% of the best of four shapes on
+            // geometric mean, against 95.8% for 4096-float tiles throughout).
+            double best = 0.0;
+            for (size_t c : {(size_t)16, (size_t)8, (size_t)4})
+                if (c >= base_u && pass_use(c) > best + 0.02) {
+                    best = pass_use(c);
+                    u = c;
+                }
+            max_blocks = u == 16 ? 1024 : 2048;
+        }
+        L.staged_u = (int)u;
+        // An explicit policy may ask for larger tiles (unroll 8 or 16).
+        if (pol != nullptr && p.unroll > L.staged_u) L.staged_u = p.unroll >= 16 ? 16 : 8;
+        L.staged_rows = (unsigned int)tile_rows((size_t)L.staged_u);
         const size_t tiles = (rows + L.staged_rows - 1) / L.staged_rows;
         L.grid = (int)(tiles < max_blocks ? tiles : max_blocks);
+        // A wave's results are held in LDS and stored after its last tile
+        // (defer 0) when they fit beside its staging tile in one wave's share
+        // of a CU's LDS (the grid's waves spread evenly over the CUs) and in
+        // one block's limit.
+        // Rows of 960 floats and more are left out: with a row or two per
+        // tile, holding measured 1-10% slower there (and 5-20% faster on
+        // narrower rows).
+        if (p.defer == 0 && cols < 960) {
+            const size_t results = (tiles + L.grid - 1) / L.grid * L.staged_rows;
+            const size_t waves_per_cu = ((size_t)L.grid + info.cu_count - 1) / info.cu_count;
+            const size_t stage = (size_t)64 * L.staged_u * 16;  // 64 lanes x staged_u 16-byte vectors
+            const size_t need = stage + results * sizeof(float);
+            if (need <= info.lds_per_cu / waves_per_cu && need <= info.lds_per_block)
+                L.staged_hold = (unsigned int)results;
+        }
         const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
         if (e != hipSuccess) return fail(e, RED_ERR_HIP);
         return RED_OK;
@@ -686,6 +730,7 @@ void red_default_rows_policy(red_rows_policy* p) {
     p->prefetch = kDefaultRows.prefetch;
     p->short_rows = kDefaultRows.short_rows;
     p->cover = kDefaultRows.cover;
+    p->defer = kDefaultRows.defer;
 }
 
 size_t red_flat_grid(size_t n, const red_flat_policy* pol) {

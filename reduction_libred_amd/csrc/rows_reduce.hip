@@ -426,22 +426,30 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
     // Trips alternate between two register buffers: the next trip's loads
     // are issued before the current trip is reduced and stored, so the loads
     // stay in flight across trips (and, memory operations completing in
-    // order, waiting for them never waits for the stores that follow).
+    // order, waiting for them never waits for the stores that follow). The
+    // wave's n trips run two per loop pass with the odd or last two after
+    // the loop, which then has a single exit: with an exit after each half,
+    // the compiler joins the exits in a block that also leads back to the
+    // loop head, and on that path the other buffer's loads are still in
+    // flight, so the head waited for them before issuing the next loads.
     size_t g0 = blockIdx.x;  // wave-uniform
     if (g0 >= ngroups) return;
+    const size_t step = G * U;
+    size_t n = (ngroups - g0 + step - 1) / step;
     unit_t a[U][V], b[U][V];
     load_trip(a, g0);
-    while (true) {
-        size_t g1 = g0 + G * U;
-        if (g1 < ngroups) load_trip(b, g1);
+    for (; n > 2; n -= 2, g0 += 2 * step) {
+        load_trip(b, g0 + step);
         reduce_trip(a, g0);
-        if (g1 >= ngroups) break;
-        g0 = g1;
-        g1 = g0 + G * U;
-        if (g1 < ngroups) load_trip(a, g1);
-        reduce_trip(b, g0);
-        if (g1 >= ngroups) break;
-        g0 = g1;
+        load_trip(a, g0 + 2 * step);
+        reduce_trip(b, g0 + step);
+    }
+    if (n == 2) {
+        load_trip(b, g0 + step);
+        reduce_trip(a, g0);
+        reduce_trip(b, g0 + step);
+    } else {
+        reduce_trip(a, g0);
     }
 }
 
@@ -457,7 +465,17 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
 // to the waves, and the next tile's loads are issued before the current tile
 // is reduced. A lane with no whole vector to read in a tile reads vector 0 of
 // the matrix instead (no load sits under a lane mask).
-template <class Op, int LOG2S, int U, bool NT, bool VREAD>
+//
+// With HOLD, a wave keeps its row results in LDS (dynamic shared memory, at
+// least R times the wave's tile count) and stores them all after its last
+// tile. (A template parameter: with a run-time choice the compiler merges the
+// LDS store and the global store into one flat store, which counts against
+// both the LDS and the memory counters, so every LDS wait became a wait for
+// all loads in flight.) Small stores spread through the read stream cost
+// far more HBM time than their bytes: on 1 GiB of 64-float rows, 16 MiB of
+// results stored as each tile was reduced took about 20 us more than no
+// stores at all, against about 2 us when they all went out at the end.
+template <class Op, int LOG2S, int U, bool NT, bool VREAD, bool HOLD>
 __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, unsigned int R,
                                                             typename Op::out_t* __restrict__ out) {
@@ -468,6 +486,8 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
     constexpr int P = kWave / S;
     constexpr size_t E = Op::kPerVec;
     __shared__ vec_t stage[kWave * U];
+    extern __shared__ __align__(16) unsigned char rows_staged_held[];
+    typename Op::out_t* held = reinterpret_cast<typename Op::out_t*>(rows_staged_held);
     elem_t* lds = reinterpret_cast<elem_t*>(stage);
     const unsigned int lane = threadIdx.x;
     const unsigned int s = lane & (S - 1);
@@ -490,7 +510,7 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
             v[u] = load_vec<NT>(xv + (i < nv ? base + i : 0));
         }
     };
-    auto reduce_tile = [&](const vec_t (&v)[U], size_t t) {
+    auto reduce_tile = [&](const vec_t (&v)[U], size_t t, size_t k) {  // k: the wave's tile number
         const size_t cnt = count(t);
 #pragma unroll
         for (int u = 0; u < U; ++u) stage[lane + u * kWave] = v[u];
@@ -531,28 +551,45 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
                 for (; j < C; j += S) a = Op::combine(a, Op::lift(row[j], j));
             }
             a = segment_reduce<Op, LOG2S>(a);
-            if (r < rows_t && leader) out[t * R + r] = Op::finish(a);
+            if (r < rows_t && leader) {
+                if constexpr (HOLD)
+                    held[k * R + r] = Op::finish(a);
+                else
+                    out[t * R + r] = Op::finish(a);
+            }
         }
         __syncthreads();
     };
-    // The next tile's loads are issued unconditionally (past the last tile
-    // every lane reads vector 0): loads under a branch would make the
-    // compiler wait for all of them before the stores to LDS.
-    size_t t0 = blockIdx.x;  // wave-uniform
-    if (t0 >= ntiles) return;
+    // The wave's n tiles t0, t0 + G, ... run two per loop pass, one register
+    // buffer each, with the odd or last two after the loop (a loop with one
+    // exit, as in rows_packed_kernel, so that its head never waits for loads).
+    const size_t first = blockIdx.x;  // wave-uniform
+    if (first >= ntiles) return;
+    const size_t mine = (ntiles - first + G - 1) / G;
+    size_t n = mine, k = 0, t0 = first;
     vec_t a[U], b[U];
     load_tile(a, t0);
-    while (true) {
-        size_t t1 = t0 + G;
-        load_tile(b, t1);
-        reduce_tile(a, t0);
-        if (t1 >= ntiles) break;
-        t0 = t1;
-        t1 = t0 + G;
-        load_tile(a, t1);
-        reduce_tile(b, t0);
-        if (t1 >= ntiles) break;
-        t0 = t1;
+    for (; n > 2; n -= 2, k += 2, t0 += 2 * G) {
+        load_tile(b, t0 + G);
+        reduce_tile(a, t0, k);
+        load_tile(a, t0 + 2 * G);
+        reduce_tile(b, t0 + G, k + 1);
+    }
+    if (n == 2) {
+        load_tile(b, t0 + G);
+        reduce_tile(a, t0, k);
+        reduce_tile(b, t0 + G, k + 1);
+    } else {
+        reduce_tile(a, t0, k);
+    }
+    if constexpr (HOLD) {
+        // Held result i is row i % R of the wave's tile i / R.
+        const unsigned int total = (unsigned int)(mine * R);
+        for (unsigned int i = lane; i < total; i += kWave) {
+            const unsigned int q = i / R, r = i - q * R;
+            const size_t t = first + (size_t)q * G;
+            if (r < rows_in(t)) out[t * R + r] = held[i];
+        }
     }
 }
 
@@ -593,7 +630,8 @@ bool rows_policy_supported(const RowsPolicy& p) {
     const bool b = p.block == 64 || p.block == 128 || p.block == 256 || p.block == 512;
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.max_blocks >= 1 && p.split >= 0 &&
-           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.cover >= 0 && p.cover <= 2 && p.short_rows >= 0 && p.short_rows <= 16;
+           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.cover >= 0 && p.cover <= 2 && p.short_rows >= 0 && p.short_rows <= 16 &&
+           (p.defer == 0 || p.defer == 1);
 }
 
 template <class Op, int BLOCK, int UNROLL>
@@ -716,12 +754,22 @@ static hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_
 template <class Op, int LOG2S, int U, bool VREAD>
 static hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
                                   const RowsLaunch& L, bool nt, hipStream_t stream) {
-    if (nt)
-        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD>), dim3(L.grid), dim3(kWave), 0, stream,
-                           x, rows, cols, L.staged_rows, out);
-    else
-        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD>), dim3(L.grid), dim3(kWave), 0, stream,
-                           x, rows, cols, L.staged_rows, out);
+    const size_t held_bytes = (size_t)L.staged_hold * sizeof(typename Op::out_t);
+    if (L.staged_hold > 0) {
+        if (nt)
+            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true>), dim3(L.grid), dim3(kWave),
+                               held_bytes, stream, x, rows, cols, L.staged_rows, out);
+        else
+            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, true>), dim3(L.grid), dim3(kWave),
+                               held_bytes, stream, x, rows, cols, L.staged_rows, out);
+    } else {
+        if (nt)
+            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, false>), dim3(L.grid), dim3(kWave), 0,
+                               stream, x, rows, cols, L.staged_rows, out);
+        else
+            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, false>), dim3(L.grid), dim3(kWave), 0,
+                               stream, x, rows, cols, L.staged_rows, out);
+    }
     return hipGetLastError();
 }
 

@@ -117,11 +117,13 @@ def test_rows_argument_errors():
     assert L.red_rows_sum_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
     bad = rl.RowsPolicy(64, 4, 1, 16, 3)
     assert L.red_rows_sum_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
-    # The fields added for cover reading and the streaming kernel are checked
-    # before anything else (rows == 0 then makes a valid call a no-op).
+    # The fields added for cover reading, the streaming kernel and held results
+    # are checked before anything else (rows == 0 then makes a valid call a
+    # no-op).
     base = rl.red_default_rows_policy()
-    assert base.cover == 0 and base.prefetch == 0 and base.short_rows == 0
+    assert base.cover == 0 and base.prefetch == 0 and base.short_rows == 0 and base.defer == 0
     for field, value, ok in (("cover", 3, False), ("cover", -1, False), ("cover", 2, True),
+                             ("defer", 1, True), ("defer", 2, False), ("defer", -1, False),
                              ("prefetch", 2, False), ("prefetch", 1, True), ("short_rows", 10, True),
                              ("short_rows", 9, True), ("short_rows", 16, True), ("short_rows", 17, False),
                              ("split", 3, False)):

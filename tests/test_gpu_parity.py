@@ -568,7 +568,8 @@ ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1,
                 dict(short_rows=9, nontemporal=0), dict(short_rows=5, max_blocks=1),
                 dict(cover=2, short_rows=1), dict(cover=2, unroll=16, max_blocks=3, short_rows=1),
                 dict(cover=2, block=256, unroll=2, short_rows=1), dict(cover=1, short_rows=1, max_blocks=5),
-                dict(short_rows=11), dict(short_rows=14, unroll=16, max_blocks=3), dict(short_rows=16))
+                dict(short_rows=11), dict(short_rows=14, unroll=16, max_blocks=3), dict(short_rows=16),
+                dict(defer=1), dict(defer=1, short_rows=12, max_blocks=2))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
@@ -1102,6 +1103,35 @@ def test_full_rows_65536x4096():
     S, A = oracle.rows_sum_f32(a)
     assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
     assert np.array_equal(m.cpu().numpy(), oracle.rows_max_f32(a))
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_rows_short_1gib():
+    # The 1 GiB rows workload viewed as (2^28 // cols) x cols rows, the shapes
+    # the widths benchmark times. By default the LDS-staged kernel holds each
+    # wave's row results until its last tile; defer=1 stores them tile by
+    # tile. Each row is reduced the same way in both, so the floats must be
+    # identical, and sampled rows (the first and last 1000 and 2000 drawn at
+    # random) must match the oracle.
+    a, x = _load("rows_f32_65536x4096")
+    flat = a.reshape(-1)
+    rng = np.random.default_rng(64)
+    for cols in (16, 64, 100, 256, 1000):
+        rows = flat.size // cols
+        say(f"red_rows_sum_f32 / red_rows_max_f32 rows_f32_65536x4096 as {rows}x{cols}, held and tile by tile")
+        v = x.view(-1)[: rows * cols].view(rows, cols)
+        s0, m0 = rl.red_rows_sum_f32(v), rl.red_rows_max_f32(v)
+        s1, m1 = rl.red_rows_sum_f32(v, policy=dict(defer=1)), rl.red_rows_max_f32(v, policy=dict(defer=1))
+        torch.cuda.synchronize()
+        assert torch.equal(s0, s1) and torch.equal(m0, m1), cols
+        idx = np.unique(np.concatenate([np.arange(1000), np.arange(rows - 1000, rows),
+                                        rng.integers(0, rows, 2000)]))
+        sub = flat[: rows * cols].reshape(rows, cols)[idx]
+        S, A = oracle.rows_sum_f32(sub)
+        got = s0.cpu().numpy()[idx].astype(np.float64)
+        assert np.all(np.abs(got - S) <= 1e-5 * A + 1e-6), cols
+        assert np.array_equal(m0.cpu().numpy()[idx], oracle.rows_max_f32(sub)), cols
     del x
     torch.cuda.empty_cache()
 
