@@ -131,14 +131,17 @@ typedef struct red_rows_policy {
  * of m * cols columns, m consecutive rows as one, with four columns per
  * lane, and a second pass adds each column's m partial columns and then the
  * last rows % m rows. m must make every m-row span start 16-byte aligned (a
- * multiple of 4 / gcd(cols, 4)). 0 = the library's choice (16 for widths of
- * at least 256 that are not a multiple of 4; for widths of 32 to 255, the
- * smallest m whose view rows hold 512 groups of four columns, at most 64,
- * unless the width is a multiple of 4 whose own rows keep 95% of the lanes
- * busy; otherwise the m up to 16 that leaves the fewest lanes idle,
- * multiples of 4 folded only for 5% more lanes), 1 = never, 2-64 = that m,
- * rounded up to a valid multiple and down to the rows; and `width` (1, 2 or
- * 4):
+ * multiple of 4 / gcd(cols, 4)). 0 = the library's choice (for widths of
+ * at least 256 that are not a multiple of 32, with at least 32768 rows: 32,
+ * so that each view row spans whole 128-byte lines, except for widths of
+ * 2 mod 4, which take 16; 16 for the other widths of at least 256 that are
+ * not a multiple of 4; for widths of 32 to 255, the smallest m that is a
+ * multiple of 32 / gcd(cols, 32) and whose view rows hold 512 groups of
+ * four columns, at most 64, unless the width is a multiple of 4 whose own
+ * rows keep 95% of the lanes busy; otherwise the m up to 16 that leaves the
+ * fewest lanes idle, multiples of 4 folded only for 5% more lanes), 1 =
+ * never, 2-64 = that m, rounded up to a valid multiple and down to the
+ * rows; and `width` (1, 2 or 4):
  * with at least 64 column groups, each row is read by `width` loads per lane,
  * so a wave reads width x 1 KiB (four columns per lane) or width x 256 bytes
  * (one column per lane) of a row at once (with fewer groups, 1 is used);

@@ -6,6 +6,7 @@
 
 #include <map>
 #include <mutex>
+#include <numeric>
 #include <utility>
 #include <vector>
 
@@ -476,6 +477,20 @@ double cols_lane_use(size_t groups) {
 //   leave a second block per row phase with one group).
 size_t fold_rows(size_t rows, size_t cols) {
     const size_t m0 = cols % 4 == 0 ? 1 : cols % 2 == 0 ? 2 : 4;
+    // m_line rows span whole 128-byte lines. A wave reads 1 KiB of a row per
+    // load; when rows do not start on a line, the line at each boundary is
+    // fetched by the two waves (on different XCDs) that read either side of
+    // it: 6.3% more HBM bytes with 16-row views of odd widths, 11-14% at 3,
+    // 7, 17 and 100 columns (FETCH_SIZE).
+    const size_t m_line = 32 / std::gcd(cols, (size_t)32);
+    if (cols >= 256 && cols % 32 != 0 && m_line != 16 && rows / 32 >= 1024 && cols * 32 <= RED_MAX_N) {
+        // 32 rows per view row (a multiple of m_line): odd widths of 257 to
+        // 4097 ran 7-17% faster than with 16 rows (1025: 5.8 -> 6.3, 2049:
+        // 5.9 -> 6.9 TB/s), multiples of 4 from 300 to 6000 0-15% faster
+        // than unfolded. Widths of 2 mod 4 keep 16 rows, which already
+        // span whole lines (32 measured up to 8% slower there).
+        return 32;
+    }
     if (m0 > 1 && cols >= 256) {
         // Over 1023 to 65537 columns, 16 rows ran 3-24% faster than 4 rows,
         // which already use 98% of the lanes.
@@ -486,12 +501,13 @@ size_t fold_rows(size_t rows, size_t cols) {
     if (cols >= 32 && cols < 256 && (m0 > 1 || cols_lane_use(cols / 4) < 0.95)) {
         // Widths of 32 to 255 (multiples of 4 only when their own rows leave
         // lanes idle) take the smallest m whose view rows hold 512 groups of
-        // four columns (8 KiB), at most 64: over 33 to 132 columns that
-        // matched the best measured m within 1-4% (33: 5.6 -> 6.7 TB/s, 65:
-        // 5.5 -> 6.8, 68: 6.0 -> 6.7 against the choice by lane use below,
-        // whose 4-16 rows already keep most lanes busy).
+        // four columns (8 KiB) and span whole lines, at most 64: over 33 to
+        // 132 columns 512 groups matched the best measured m within 1-4%
+        // (33: 5.6 -> 6.7 TB/s, 65: 5.5 -> 6.8, 68: 6.0 -> 6.7 against the
+        // choice by lane use below, whose 4-16 rows already keep most lanes
+        // busy).
         size_t m = (2048 + cols - 1) / cols;
-        m = (m + m0 - 1) / m0 * m0;
+        m = (m + m_line - 1) / m_line * m_line;
         if (m > 64) m = 64;
         while (m > rows || cols * m > RED_MAX_N) m -= m0;
         return m < m0 ? 1 : m;

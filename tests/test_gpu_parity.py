@@ -650,7 +650,8 @@ COL_POLICIES = (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=1
                 dict(width=2), dict(width=4, unroll=2), dict(width=4, unroll=16, nontemporal=0, target_waves=7),
                 dict(prefetch=1), dict(prefetch=1, unroll=1, target_waves=7), dict(width=4, unroll=2, prefetch=1),
                 dict(width=2, unroll=16, prefetch=1, nontemporal=0), dict(fold=1), dict(fold=16),
-                dict(fold=3, unroll=1, target_waves=7), dict(fold=8, width=4, unroll=2, prefetch=0))
+                dict(fold=3, unroll=1, target_waves=7), dict(fold=8, width=4, unroll=2, prefetch=0),
+                dict(fold=32), dict(fold=64, unroll=2))
 
 
 @pytest.mark.parametrize("rows,cols,ld", COL_SHAPES)
@@ -672,6 +673,29 @@ def test_cols(rows, cols, ld):
             torch.cuda.synchronize()
             assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
             assert np.array_equal(m.cpu().numpy(), M), p
+
+
+@pytest.mark.parametrize("rows,cols", [(40_001, 257), (33_000, 1000), (32_810, 1025), (32_768, 300),
+                                       (40_000, 1026), (32_800, 2049)])
+def test_cols_line_views(rows, cols):
+    # Widths of at least 256 that are not a multiple of 32, with enough rows
+    # for the default to read the matrix through 32-row views (16 at 1026
+    # columns), each view row whole 128-byte lines; the rows past the last
+    # whole view (1-31 of them here, or none) are added in the second pass.
+    rng = np.random.default_rng(rows + 3 * cols)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    a[(np.arange(cols) * 7919) % rows, np.arange(cols)] = 50.0 + np.arange(cols) % 89
+    a[-1, ::5] = 80.0                                      # maxima in the last (tail) row
+    S, A = oracle.cols_sum_f32(a)
+    M = oracle.cols_max_f32(a)
+    x = torch.from_numpy(a).to(DEV)
+    for p in (None, dict(fold=1)):
+        say(f"cols line views {rows}x{cols} policy={p}")
+        s = rl.red_cols_sum_f32(x, policy=p)
+        m = rl.red_cols_max_f32(x, policy=p)
+        torch.cuda.synchronize()
+        assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
+        assert np.array_equal(m.cpu().numpy(), M), p
 
 
 def _nonfinite_matrix(rows, cols, seed):
