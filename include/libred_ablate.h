@@ -176,9 +176,8 @@ void red_default_flat_policy(size_t n, red_flat_policy *p);
  * floats. A call without a policy adapts it to the row length: 16 loads per
  * lane and max_blocks 512 from 16384 floats up; below 2048 floats, at most 4
  * loads per lane (a tile no longer than the row) and max_blocks 2048. Rows
- * read through their covers take 8 loads per lane and max_blocks 4096 below
- * 1280 floats, 8 and 2048 below 2048, 4 and 2048 below 16384, and 8 and 1024
- * from there. */
+ * read through their covers take 8 loads per lane and max_blocks 32768 below
+ * 16384 floats, and 8 and 1024 from there. */
 void red_default_rows_policy(red_rows_policy *p);
 
 /* The number of blocks a single-value call of n elements launches with

@@ -433,8 +433,14 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         const bool misaligned = !aligned(x, 16) || (rows > 1 && ld % 4 != 0);
         L.cover = cols >= 16 && (p.cover == 2 || (p.cover == 0 && misaligned)) ? 1 : 0;
         if (L.cover && pol == nullptr) {
-            p.unroll = cols < 2048 ? 8 : cols < 16384 ? 4 : 8;
-            p.max_blocks = cols < 1280 ? 4096 : cols < 16384 ? 2048 : 1024;
+            // A wave folds its rows one after another, so below 16384 floats
+            // more waves hide more of each row's memory latency: 8 loads per
+            // lane on up to 32768 waves ran 4-21% faster over 1025-8193
+            // floats than 4096 or 2048 waves (2049: 5.8 -> 6.8, 2500: 5.5 ->
+            // 6.6 TB/s) and within 2% at 1700, 3001 and 6001; longer rows
+            // keep 1024 waves (50257 floats: 6% slower with more).
+            p.unroll = 8;
+            p.max_blocks = cols < 16384 ? 32768 : 1024;
         }
         // Every wave gets the same number of rows, give or take one: with
         // per = ceil(rows / (max_blocks waves)), ceil(rows / per) waves, so
@@ -465,11 +471,13 @@ double cols_lane_use(size_t groups) {
 
 // Rows per view row for a contiguous matrix (1 = no fold). m is a multiple
 // of m0 = 4 / gcd(cols, 4) and at most rows:
-// - a width of at least 256 that is not a multiple of 4 takes the largest
-//   up to 16;
+// - a width of at least 256 that is not a multiple of 32 (nor 2 mod 4) takes
+//   32 when that leaves at least 1024 view rows;
+// - another width of at least 256 that is not a multiple of 4 takes the
+//   largest up to 16;
 // - a width of 32 to 255 (a multiple of 4 only if its own rows leave 5% of
-//   the lanes idle) takes the smallest m with 512 groups of four columns in
-//   a view row, at most 64;
+//   the lanes idle) takes the smallest multiple of 32 / gcd(cols, 32) with
+//   512 groups of four columns in a view row, at most 64;
 // - otherwise the m up to 16 whose view uses the most lanes, the smallest
 //   on a tie;
 // - a width that is a multiple of 4 is folded only when that uses at least
