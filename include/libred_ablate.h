@@ -174,7 +174,9 @@ red_status red_cols_max_f32_with(const float *x, size_t rows, size_t cols, size_
 void red_default_flat_policy(size_t n, red_flat_policy *p);
 /* The default shape of the row entry points for aligned rows of 2048 to 16383
  * floats. A call without a policy adapts it to the row length: 16 loads per
- * lane and max_blocks 512 from 16384 floats up; below 2048 floats, at most 4
+ * lane and max_blocks 512 from 16384 floats up; 4 loads per lane and
+ * max_blocks 2048 for rows of 2049 to 4095 floats whose last 2048-float tile
+ * is at most 75% full; below 2048 floats, at most 4
  * loads per lane (a tile no longer than the row) and max_blocks 2048. Rows
  * read through their covers take 8 loads per lane and max_blocks 32768 below
  * 16384 floats, and 8 and 1024 from there. */

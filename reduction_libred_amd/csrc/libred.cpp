@@ -228,6 +228,13 @@ RowsPolicy default_rows(size_t cols) {
         const size_t u = nvec / 64;
         p.unroll = u >= 4 ? 4 : (u >= 2 ? 2 : 1);
         p.max_blocks = 2048;
+    } else if (nvec < 1024 && nvec % 512 != 0 && nvec % 512 <= 384) {
+        // Rows of 1-1.75 tiles of 8 loads per lane: the partial tile costs a
+        // round trip of its own, better hidden by 4-load tiles on 2048 waves
+        // (2052: 4.9 -> 6.4, 2560: 5.6 -> 7.1, 3072: 6.2 -> 6.9, 3584: 6.7 ->
+        // 7.0 TB/s; at 4000 floats, a 95% full second tile, 3% slower).
+        p.unroll = 4;
+        p.max_blocks = 2048;
     }
     return p;
 }
