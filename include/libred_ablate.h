@@ -138,8 +138,11 @@ typedef struct red_rows_policy {
  * not a multiple of 4; for widths of 32 to 255, the smallest m that is a
  * multiple of 32 / gcd(cols, 32) and whose view rows hold 512 groups of
  * four columns, at most 64, unless the width is a multiple of 4 whose own
- * rows keep 95% of the lanes busy; otherwise the m up to 16 that leaves the
- * fewest lanes idle, multiples of 4 folded only for 5% more lanes), 1 =
+ * rows keep 95% of the lanes busy; below 32 columns, the smallest multiple
+ * of 32 / gcd(cols, 32) up to 32 (16 for multiples of 4) that keeps 84% of
+ * the lanes busy, when the choice below keeps fewer than 99%; otherwise the
+ * m up to 16 that leaves the fewest lanes idle, multiples of 4 folded only
+ * for 5% more lanes), 1 =
  * never, 2-64 = that m, rounded up to a valid multiple and down to the
  * rows; and `width` (1, 2 or 4):
  * with at least 64 column groups, each row is read by `width` loads per lane,
