@@ -173,7 +173,9 @@ red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_
 red_status red_cols_max_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_cols_policy *p, hipStream_t stream);
 
-/* The shape red_sum_f32 / red_sum_i32_i64 / red_max_f32 use for n elements. */
+/* The shape red_sum_f32 / red_sum_i32_i64 / red_max_f32 use for n elements
+ * (up to 2^15 elements, one block of 1024 threads that stores the result
+ * itself). */
 void red_default_flat_policy(size_t n, red_flat_policy *p);
 /* The default shape of the row entry points for aligned rows of 2048 to 16383
  * floats. A call without a policy adapts it to the row length: 16 loads per
