@@ -225,8 +225,8 @@ def gbps(nbytes, ms):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the multi-GPU sharding is a design note, not code).", file=sys.stderr, flush=True)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the library "
+              "reduces on one GPU, and sharding across GPUs is not implemented.", file=sys.stderr, flush=True)
         sys.exit(2)
 
     import numpy as np
