@@ -86,23 +86,28 @@ typedef struct red_flat_policy {
  * not apply to them, `max_blocks` caps their grid, and an `unroll` of 8 or
  * 16 gives the LDS-staged kernel tiles of that many 16-byte vectors per lane
  * when that is more than the rows need):
- *   0  the library's choice: rows of fewer than 1024 floats of a contiguous
- *      (ld == cols), 16-byte aligned matrix go to the LDS-staged kernel, which
- *      loads tiles of whole rows as 16-byte vectors whatever the row length
- *      and then reduces each row from LDS with a power of two of lanes;
- *      other rows of at most 512 floats go to the packed kernel, which gives
+ *   0  the library's choice: rows of fewer than 1024 floats go to the
+ *      LDS-staged kernel when they are contiguous or their gaps (ld - cols)
+ *      hold at most a quarter of a row, and the matrix spans at least 8
+ *      elements (any alignment of x: the first and last vectors of the
+ *      matrix are read element by element when they reach outside it); it
+ *      loads tiles of rows, gaps included, as 16-byte vectors whatever the
+ *      row length and then reduces each row from LDS with a power of two of
+ *      lanes; other rows of at most 512 floats go to the packed kernel, which gives
  *      each row a segment of up to 16 lanes (16-byte units, rows 16-byte
  *      aligned) or 64 lanes (single elements), so that one load covers
  *      several rows;
  *   1  neither;
  *   2  the packed kernel only (rows of at most 512 floats);
  *   3-9  the LDS-staged kernel with 2^(short_rows - 3) lanes per row where it
- *      applies (contiguous, 16-byte aligned, at least 4 elements, and 4 rows
- *      of an odd width, 2 of a width of 2 mod 4, or 1 row, fit 4096 floats),
- *      else as 2;
+ *      applies (as for 0, at any row length whose tile fits 4096 floats:
+ *      for a contiguous, 16-byte aligned matrix, 4 rows of an odd width, 2
+ *      of a width of 2 mod 4, or 1 row; otherwise one row plus 3), else as
+ *      2;
  *   10-16  the same with 2^(short_rows - 10) lanes per row, which read
- *      16-byte vectors from LDS when the rows hold whole vectors (cols a
- *      multiple of 4; the default for such rows of at most 64 floats);
+ *      16-byte vectors from LDS when the rows hold whole vectors that start
+ *      16-byte aligned (cols and ld multiples of 4, x 16-byte aligned; the
+ *      default for such rows of at most 64 floats);
  * and `defer` (the LDS-staged kernel): 0 = a wave keeps its row results in
  * LDS and stores them after its last tile when they fit beside its staging
  * tile in its share of the CU's LDS (the CU's LDS over the waves the grid

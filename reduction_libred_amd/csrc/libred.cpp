@@ -307,22 +307,38 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (st != RED_OK) return st;
 
     libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    // Rows of fewer than 1024 floats of a contiguous, 16-byte aligned matrix
-    // go to the LDS-staged kernel (short_rows 0), or do so with
-    // 2^(short_rows - 3) lanes per row (short_rows 3-9), as long as a tile
-    // of 16-byte aligned rows fits 4096 floats.
-    const bool contiguous = ld == cols || rows == 1;
+    // Rows of fewer than 1024 floats go to the LDS-staged kernel (short_rows
+    // 0), or do so with 2^(short_rows - 3) lanes per row (short_rows 3-9),
+    // when the rows are contiguous or their gaps hold at most a quarter of a
+    // row's elements (the tiles read the gaps along), the matrix spans at
+    // least 8 elements, and a tile fits 4096 floats. A contiguous, 16-byte
+    // aligned matrix ("dense") is tiled in 16-byte aligned spans of rows;
+    // other matrices in spans that start anywhere.
+    const size_t step = rows == 1 ? cols : ld;  // elements from one row to the next
+    const bool dense = step == cols && aligned(x, 16);
     const size_t fold = cols % 4 == 0 ? 1 : cols % 2 == 0 ? 2 : 4;  // rows per 16-byte aligned span
-    const bool staged_ok = contiguous && aligned(x, 16) && cols > 0 && rows * cols >= 4 && fold * cols <= 4096;
+    const size_t span_all = (rows - 1) * step + cols;
+    // (Strided rows of 512 floats and more stay with the packed or
+    // one-wave-per-row kernels: 512 floats at a stride of 516 ran 6% slower
+    // staged.)
+    const bool staged_ok = cols > 0 && (dense ? rows * cols >= 4 && fold * cols <= 4096
+                                              : span_all >= 8 && (step - cols) * 4 <= cols && cols + 3 <= 4096 &&
+                                                    (step == cols || cols < 512));
     const bool staged_default = p.short_rows == 0 && cols < 1024;
     if (staged_ok && (staged_default || p.short_rows >= 3)) {
-        const size_t base_u = fold * cols <= 1024 ? 4 : fold * cols <= 2048 ? 8 : 16;
+        const size_t base_u = dense ? (fold * cols <= 1024 ? 4 : fold * cols <= 2048 ? 8 : 16)
+                                    : (cols + 3 <= 1024 ? 4 : cols + 3 <= 2048 ? 8 : 16);
+        // x's offset in elements from the 16-byte boundary before it.
+        const size_t sh = ((uintptr_t)x % 16) / sizeof(float);
+        // Rows of whole vectors that start 16-byte aligned, the condition for
+        // reading them from LDS a vector at a time.
+        const bool vec_rows = cols % 4 == 0 && sh == 0 && step % 4 == 0;
         size_t max_blocks = (size_t)p.max_blocks;
-        const bool vread_default = cols % 4 == 0 && cols <= 64;
+        const bool vread_default = vec_rows && cols <= 64;
         // Lanes per row first: the tile size below depends on them.
         if (p.short_rows >= 10) {  // vector reads (rows of whole vectors), 2^(short_rows - 10) lanes
             L.staged_log2s = p.short_rows - 10;
-            L.staged_vread = cols % 4 == 0 ? 1 : 0;
+            L.staged_vread = vec_rows ? 1 : 0;
         } else if (p.short_rows >= 3) {
             L.staged_log2s = p.short_rows - 3;
         } else if (vread_default) {
@@ -348,7 +364,12 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         // Tile size: 16-byte vectors per lane (4, 8 or 16, at least base_u
         // so that a tile holds one aligned span of rows).
         const size_t pass = (size_t)64 >> L.staged_log2s;  // rows reduced at a time
-        auto tile_rows = [&](size_t u) { return (256 * u) / (fold * cols) * fold; };
+        // Rows per tile: dense, a whole number of aligned spans in 256 * u
+        // elements; otherwise as many rows as fit with room for a span that
+        // starts 3 elements into its first vector.
+        auto tile_rows = [&](size_t u) {
+            return dense ? (256 * u) / (fold * cols) * fold : (256 * u - 3 - cols) / step + 1;
+        };
         auto pass_use = [&](size_t u) {  // share of the passes' row slots that hold a row
             const size_t r = tile_rows(u);
             return r == 0 ? 0.0 : (double)r / (double)(pass * ((r + pass - 1) / pass));

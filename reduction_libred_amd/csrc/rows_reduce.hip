@@ -453,18 +453,27 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
     }
 }
 
-// Short rows of a contiguous matrix (ld == cols, x 16-byte aligned, at
-// least 4 elements in all), staged through LDS. The matrix is one flat
-// array; a tile is R consecutive rows, R a multiple of 4 / gcd(cols, 4) so
-// that every tile starts 16-byte aligned, and R * cols <= 256 * U elements.
-// A wave loads a tile as U 16-byte vectors per lane (coalesced whatever the
-// row length; the 1-3 elements of a last vector that runs past the end are
-// read one by one), stores it to LDS, and then reduces its rows 64 / S at a
-// time with S = 2^LOG2S lanes per row: lane s of a row adds elements s,
-// s + S, ... in order, then the segment reduce. Tiles are dealt round-robin
-// to the waves, and the next tile's loads are issued before the current tile
-// is reduced. A lane with no whole vector to read in a tile reads vector 0 of
-// the matrix instead (no load sits under a lane mask).
+// Short rows, staged through LDS: rows starting ld >= cols elements apart,
+// x at any element. A tile is R consecutive rows; its span, from its first
+// row's first element to its last row's last, is loaded as the aligned
+// 16-byte vectors that cover it (coalesced whatever the row length or
+// stride), at most U per lane, and stored to LDS, where the tile's first
+// element lands at `off` (0-3, the span's offset within its first vector)
+// and row r at off + r * ld. The vectors a tile loads beyond its own span
+// hold elements of its neighbours or of the gaps between rows, all inside
+// the matrix, and are never read. Two vectors may reach outside the matrix:
+// the first, when x is not 16-byte aligned (it starts sh elements before
+// x), and the last, when the matrix ends inside it; neither is loaded as a
+// vector, and their elements of the matrix are read one by one. (For a
+// contiguous, 16-byte aligned matrix, R is a multiple of 4 / gcd(cols, 4),
+// so every tile starts 16-byte aligned and off is 0.) The wave then reduces
+// the tile's rows 64 / S at a time with S = 2^LOG2S lanes per row: lane s of
+// a row adds elements s, s + S, ... in order, then the segment reduce; with
+// VREAD (rows of whole vectors, off always 0 and ld a multiple of 4) lane s
+// reads vectors s, s + S, ... of its row. Tiles are dealt round-robin to the
+// waves, and the next tile's loads are issued before the current tile is
+// reduced. A load slot with no vector of the tile reads the first whole
+// vector of the matrix instead (no load sits under a lane mask).
 //
 // With HOLD, a wave keeps its row results in LDS (dynamic shared memory, at
 // least R times the wave's tile count) and stores them all after its last
@@ -475,9 +484,13 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
 // far more HBM time than their bytes: on 1 GiB of 64-float rows, 16 MiB of
 // results stored as each tile was reduced took about 20 us more than no
 // stores at all, against about 2 us when they all went out at the end.
+//
+// The host ensures that a tile's span plus 3 fits 256 * U elements, that the
+// matrix spans at least 8 elements, and that R * ld >= 4.
 template <class Op, int LOG2S, int U, bool NT, bool VREAD, bool HOLD>
 __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::elem_t* __restrict__ x,
-                                                            size_t rows, size_t cols, unsigned int R,
+                                                            size_t rows, size_t cols, size_t ld,
+                                                            unsigned int sh, unsigned int R,
                                                             typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
     using elem_t = typename Op::elem_t;
@@ -492,33 +505,52 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
     const unsigned int lane = threadIdx.x;
     const unsigned int s = lane & (S - 1);
     const bool leader = LOG2S <= 4 ? s == 0 : s == (unsigned int)S - 1;
-    const size_t total = rows * cols;
-    const size_t tile_elems = (size_t)R * cols;
     const size_t ntiles = (rows + R - 1) / R;
     const size_t G = gridDim.x;
-    const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x);
+    // Vectors of the aligned cover, counted from x - sh.
+    const vec_t* __restrict__ xv = reinterpret_cast<const vec_t*>(x - sh);
+    const size_t end = (size_t)sh + (rows - 1) * ld + cols;  // one past the matrix, from x - sh
+    const size_t vlast = (end - 1) / E;                       // the cover's last vector
+    const bool cut_last = end % E != 0;                       // ... reaches past the matrix
+    const size_t safe = sh > 0 ? 1 : 0;                       // a vector wholly inside
     auto rows_in = [&](size_t t) -> unsigned int {  // rows of tile t (0 past the last tile)
         return t + 1 < ntiles ? R : t + 1 == ntiles ? (unsigned int)(rows - t * R) : 0u;
     };
-    auto count = [&](size_t t) -> size_t { return (size_t)rows_in(t) * cols; };
+    auto first_vec = [&](size_t t) -> size_t { return ((size_t)sh + t * R * ld) / E; };
+    auto end_vec = [&](size_t t) -> size_t {  // one past the tile's last cover vector
+        return ((size_t)sh + (t * R + rows_in(t) - 1) * ld + cols + E - 1) / E;
+    };
     auto load_tile = [&](vec_t (&v)[U], size_t t) {
-        const size_t base = t * tile_elems / E;
-        const size_t nv = count(t) / E;
+        // Slots [lo, hi) load the tile's cover vectors vb + slot (wave-uniform
+        // bounds); the matrix's first vector (when x is not 16-byte aligned)
+        // and its last (when the matrix ends inside it) are left out.
+        const size_t vb = first_vec(t), ve = end_vec(t);
+        const unsigned int lo = vb == 0 && sh > 0 ? 1u : 0u;
+        const unsigned int hi = (unsigned int)(ve - vb) - (cut_last && ve - 1 == vlast ? 1u : 0u);
+        const vec_t* __restrict__ tv = xv + vb;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const size_t i = lane + (size_t)u * kWave;
-            v[u] = load_vec<NT>(xv + (i < nv ? base + i : 0));
+            const unsigned int slot = lane + (unsigned int)(u * kWave);
+            v[u] = load_vec<NT>(slot >= lo && slot < hi ? tv + slot : xv + safe);
         }
     };
     auto reduce_tile = [&](const vec_t (&v)[U], size_t t, size_t k) {  // k: the wave's tile number
-        const size_t cnt = count(t);
+        const size_t vb = first_vec(t);
+        const unsigned int off = (unsigned int)((size_t)sh + t * R * ld - vb * E);
 #pragma unroll
         for (int u = 0; u < U; ++u) stage[lane + u * kWave] = v[u];
-        const size_t whole = cnt / E * E;
-        if (whole < cnt && lane < cnt - whole) lds[whole + lane] = x[t * tile_elems + whole + lane];
+        // The vectors left out: their elements of the matrix, one by one
+        // (LDS position = cover position - vb * E). The last one may belong
+        // to the covers of the last two tiles.
+        if (vb == 0 && sh > 0 && lane < E - sh) lds[sh + lane] = x[lane];
+        if (cut_last && end_vec(t) - 1 == vlast) {
+            const size_t c0 = vlast * E;  // cover position of the last vector
+            if (lane < end - c0) lds[c0 - vb * E + lane] = x[c0 + lane - sh];
+        }
         __syncthreads();
         const unsigned int rows_t = rows_in(t);
         const unsigned int C = (unsigned int)cols;
+        const unsigned int L = (unsigned int)ld;
         for (unsigned int r0 = 0; r0 < rows_t; r0 += P) {
             const unsigned int r = r0 + (lane >> LOG2S);
             acc_t a = Op::identity();
@@ -531,7 +563,7 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
                 // cols is a multiple of 16.
                 if (r < rows_t) {
                     const unsigned int V = C / (unsigned int)E;
-                    const vec_t* rowv = stage + r * V;
+                    const vec_t* rowv = stage + r * (L / (unsigned int)E);
                     for (unsigned int j = s; j < V; j += S) {
                         const vec_t v = rowv[j];
 #pragma unroll
@@ -539,7 +571,7 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
                     }
                 }
             } else if (r < rows_t) {
-                const elem_t* row = lds + r * C;
+                const elem_t* row = lds + off + r * L;
                 unsigned int j = s;
                 for (; j + 3 * S < C; j += 4 * S) {  // four LDS reads in flight
                     const elem_t e0 = row[j], e1 = row[j + S], e2 = row[j + 2 * S], e3 = row[j + 3 * S];
@@ -752,56 +784,58 @@ static hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_
 }
 
 template <class Op, int LOG2S, int U, bool VREAD>
-static hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
+static hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                                   const RowsLaunch& L, bool nt, hipStream_t stream) {
     const size_t held_bytes = (size_t)L.staged_hold * sizeof(typename Op::out_t);
+    // x's offset, in elements, from the 16-byte boundary before it.
+    const unsigned int sh = (unsigned int)(((uintptr_t)x % 16) / sizeof(typename Op::elem_t));
     if (L.staged_hold > 0) {
         if (nt)
             hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true>), dim3(L.grid), dim3(kWave),
-                               held_bytes, stream, x, rows, cols, L.staged_rows, out);
+                               held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
         else
             hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, true>), dim3(L.grid), dim3(kWave),
-                               held_bytes, stream, x, rows, cols, L.staged_rows, out);
+                               held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
     } else {
         if (nt)
             hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, false>), dim3(L.grid), dim3(kWave), 0,
-                               stream, x, rows, cols, L.staged_rows, out);
+                               stream, x, rows, cols, ld, sh, L.staged_rows, out);
         else
             hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, false>), dim3(L.grid), dim3(kWave), 0,
-                               stream, x, rows, cols, L.staged_rows, out);
+                               stream, x, rows, cols, ld, sh, L.staged_rows, out);
     }
     return hipGetLastError();
 }
 
 template <class Op, int LOG2S, int U>
-static hipError_t rows_staged_su(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
+static hipError_t rows_staged_su(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                                  const RowsLaunch& L, bool nt, hipStream_t stream) {
-    if (L.staged_vread) return rows_staged_suv<Op, LOG2S, U, true>(x, rows, cols, out, L, nt, stream);
-    return rows_staged_suv<Op, LOG2S, U, false>(x, rows, cols, out, L, nt, stream);
+    if (L.staged_vread) return rows_staged_suv<Op, LOG2S, U, true>(x, rows, cols, ld, out, L, nt, stream);
+    return rows_staged_suv<Op, LOG2S, U, false>(x, rows, cols, ld, out, L, nt, stream);
 }
 
 template <class Op, int LOG2S>
-static hipError_t rows_staged_s(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
+static hipError_t rows_staged_s(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                                 const RowsLaunch& L, bool nt, hipStream_t stream) {
     switch (L.staged_u) {
-        case 4: return rows_staged_su<Op, LOG2S, 4>(x, rows, cols, out, L, nt, stream);
-        case 8: return rows_staged_su<Op, LOG2S, 8>(x, rows, cols, out, L, nt, stream);
-        case 16: return rows_staged_su<Op, LOG2S, 16>(x, rows, cols, out, L, nt, stream);
+        case 4: return rows_staged_su<Op, LOG2S, 4>(x, rows, cols, ld, out, L, nt, stream);
+        case 8: return rows_staged_su<Op, LOG2S, 8>(x, rows, cols, ld, out, L, nt, stream);
+        case 16: return rows_staged_su<Op, LOG2S, 16>(x, rows, cols, ld, out, L, nt, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <class Op>
-static hipError_t rows_staged(const typename Op::elem_t* x, size_t rows, size_t cols, typename Op::out_t* out,
+static hipError_t rows_staged(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                               const RowsLaunch& L, bool nt, hipStream_t stream) {
     switch (L.staged_log2s) {
-        case 0: return rows_staged_s<Op, 0>(x, rows, cols, out, L, nt, stream);
-        case 1: return rows_staged_s<Op, 1>(x, rows, cols, out, L, nt, stream);
-        case 2: return rows_staged_s<Op, 2>(x, rows, cols, out, L, nt, stream);
-        case 3: return rows_staged_s<Op, 3>(x, rows, cols, out, L, nt, stream);
-        case 4: return rows_staged_s<Op, 4>(x, rows, cols, out, L, nt, stream);
-        case 5: return rows_staged_s<Op, 5>(x, rows, cols, out, L, nt, stream);
-        case 6: return rows_staged_s<Op, 6>(x, rows, cols, out, L, nt, stream);
+        case 0: return rows_staged_s<Op, 0>(x, rows, cols, ld, out, L, nt, stream);
+        case 1: return rows_staged_s<Op, 1>(x, rows, cols, ld, out, L, nt, stream);
+        case 2: return rows_staged_s<Op, 2>(x, rows, cols, ld, out, L, nt, stream);
+        case 3: return rows_staged_s<Op, 3>(x, rows, cols, ld, out, L, nt, stream);
+        case 4: return rows_staged_s<Op, 4>(x, rows, cols, ld, out, L, nt, stream);
+        case 5: return rows_staged_s<Op, 5>(x, rows, cols, ld, out, L, nt, stream);
+        case 6: return rows_staged_s<Op, 6>(x, rows, cols, ld, out, L, nt, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -810,7 +844,7 @@ template <class Op>
 static hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, const RowsLaunch& L, const RowsPolicy& p,
                           hipStream_t stream) {
-    if (L.staged_u > 0) return rows_staged<Op>(x, rows, cols, out, L, p.nontemporal != 0, stream);
+    if (L.staged_u > 0) return rows_staged<Op>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);
     if (L.packed_v > 0) {
         if (L.packed_scalar) return rows_packed_s<Op, true>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);
         return rows_packed_s<Op, false>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);

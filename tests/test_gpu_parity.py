@@ -596,6 +596,39 @@ def test_rows_random(rows, cols):
             assert np.array_equal(out_m.cpu().numpy(), M), (rows, cols, p)
 
 
+@pytest.mark.parametrize("rows,cols,gap", [(1, 8, 0), (2, 4, 0), (3, 3, 0), (100, 1, 0), (9, 1, 0), (7, 1023, 0),
+                                           (5, 1021, 3), (1000, 7, 1), (640, 33, 3), (333, 100, 4), (2, 5, 1),
+                                           (1, 1000, 0), (4000, 16, 4), (300, 64, 4), (257, 256, 4), (65, 65, 2),
+                                           (2048, 2, 0), (77, 511, 1),
+                                           # a last tile of one short row whose elements share the
+                                           # matrix's last vector with the tile before (unaligned x)
+                                           (1022, 1, 0), (2043, 1, 0), (511, 2, 0), (341, 3, 0), (1023, 1, 1)])
+def test_rows_staged_any_offset(rows, cols, gap):
+    # The LDS-staged kernel at every 16-byte offset of x and with short gaps
+    # between rows: each tile's span is loaded through its aligned cover, and
+    # the matrix's first and last vectors are read element by element when
+    # they reach outside it. NaN fills the gaps and the memory on both sides
+    # of the matrix, so any element read from outside a row shows in a
+    # result.
+    ld = cols + gap
+    rng = np.random.default_rng(rows * 31 + cols * 7 + gap)
+    full = np.full((rows, ld), np.nan, np.float32)
+    full[:, :cols] = rng.standard_normal((rows, cols)).astype(np.float32)
+    a = np.ascontiguousarray(full[:, :cols])
+    S, A = oracle.rows_sum_f32(a)
+    M = oracle.rows_max_f32(a)
+    for offset in (0, 1, 2, 3):
+        for p in (None, dict(defer=1), dict(short_rows=12), dict(short_rows=4, max_blocks=3),
+                  dict(short_rows=9, unroll=16)):
+            say(f"rows staged {rows}x{cols} ld={ld} offset={offset} policy={p}")
+            x = device_view(full, offset)[:, :cols]
+            s = rl.red_rows_sum_f32(x, policy=p)
+            m = rl.red_rows_max_f32(x, policy=p)
+            torch.cuda.synchronize()
+            assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), (offset, p)
+            assert np.array_equal(m.cpu().numpy(), M), (offset, p)
+
+
 @pytest.mark.parametrize("rows,cols,ld", [(3, 5, 7), (10, 1000, 1003), (257, 4096, 4100), (64, 63, 64),
                                           (1, 10, 10), (5, 0, 3), (1000, 129, 1024), (300, 16, 20),
                                           (100, 64, 68), (40, 128, 132), (65, 4, 8)])
