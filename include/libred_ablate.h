@@ -132,10 +132,12 @@ typedef struct red_rows_policy {
  * columns per lane when x is 16-byte aligned and cols and ld are multiples
  * of 4, or through an m-row view (see `fold`); else one column per lane;
  * 1 = always one; 4 = same as 0; `fold` (with vec 0 or 4, for a contiguous
- * (ld == cols), 16-byte aligned matrix): the matrix is read as rows / m rows
- * of m * cols columns, m consecutive rows as one, with four columns per
- * lane, and a second pass adds each column's m partial columns and then the
- * last rows % m rows. m must make every m-row span start 16-byte aligned (a
+ * (ld == cols) matrix): the matrix is read as view rows of m * cols columns,
+ * m consecutive rows as one, with four columns per lane, starting at x or,
+ * when x is not 16-byte aligned, at the next 128-byte boundary (so that such
+ * a matrix is read four columns per lane too, even with m = 1), and a
+ * second pass adds each column's m partial columns and then its elements
+ * after the last whole view row and before the view. m must make every m-row span start 16-byte aligned (a
  * multiple of 4 / gcd(cols, 4)). 0 = the library's choice (for widths of
  * at least 256 that are not a multiple of 32, with at least 32768 rows: 32,
  * so that each view row spans whole 128-byte lines, except for widths of

@@ -196,63 +196,75 @@ __global__ __launch_bounds__(kColsCombineBlock) void cols_combine_kernel(
     if (lane == 0) out[c] = Op::finish(v);
 }
 
-// Pass 2 of a folded launch (see ColsLaunch): the partials of real column c
-// are items j * cols + c for j < nchunks * m (chunk j / m, view column
-// (j % m) * cols + c), then the tail rows. One block per real column: items
-// dealt to the threads in rounds of 4 * kColsCombineBlock (4 loads in flight
-// per thread, each from a clamped index so no load is predicated), then the
-// tail rows, lane-strided, then the block reduce. The order is fixed, so the
-// result is deterministic.
+// Pass 2 of a launch on a view (see ColsLaunch): the partials of real column
+// c are items j * cols + rc for j < nchunks * m (chunk j / m, view column
+// (j % m) * cols + rc), rc = (c - rot) mod cols its place in a run of cols
+// view columns; then its elements after the view (tail elements rc,
+// rc + cols, ...) and before it (head elements c, c + cols, ... < rot). One
+// block per real column: items dealt to the threads in rounds of
+// 4 * kColsCombineBlock (4 loads in flight per thread, each from a clamped
+// index so no load is predicated), then the tail and head elements,
+// thread-strided, then the block reduce. The order is fixed, so the result
+// is deterministic.
 template <class Op>
 __global__ __launch_bounds__(kColsCombineBlock) void cols_fold_combine_kernel(
     const typename Op::acc_t* __restrict__ partials, unsigned int items, size_t cols,
-    const typename Op::elem_t* __restrict__ tail, unsigned int tail_rows, typename Op::out_t* __restrict__ out) {
+    const typename Op::elem_t* __restrict__ tail, size_t tail_elems, unsigned int rot,
+    const typename Op::elem_t* __restrict__ head, typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
     __shared__ acc_t lds[kColsCombineBlock / kWave];
     const size_t c = blockIdx.x;
+    const size_t rc = (c + cols - rot % cols) % cols;
     acc_t v = Op::identity();
     for (unsigned int j0 = 0; j0 < items; j0 += 4 * kColsCombineBlock) {
         acc_t t[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const unsigned int j = j0 + u * kColsCombineBlock + threadIdx.x;
-            t[u] = partials[(size_t)(j < items ? j : items - 1) * cols + c];
+            t[u] = partials[(size_t)(j < items ? j : items - 1) * cols + rc];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             if (j0 + u * kColsCombineBlock + threadIdx.x < items) v = Op::combine(v, t[u]);
     }
-    for (unsigned int t = threadIdx.x; t < tail_rows; t += kColsCombineBlock)
-        v = Op::combine(v, Op::lift(tail[(size_t)t * cols + c], 0));
+    for (size_t i = rc + (size_t)threadIdx.x * cols; i < tail_elems; i += (size_t)kColsCombineBlock * cols)
+        v = Op::combine(v, Op::lift(tail[i], 0));
+    for (size_t f = c + (size_t)threadIdx.x * cols; f < rot; f += (size_t)kColsCombineBlock * cols)
+        v = Op::combine(v, Op::lift(head[f], 0));
     v = block_reduce<Op, kColsCombineBlock>(v, lds);
     if (threadIdx.x == 0) out[c] = Op::finish(v);
 }
 
 // Pass 2 when there are many columns and few partials each: one thread per
-// column adds items j * cols + c for j < items in order (consecutive threads
+// column adds items j * cols + rc for j < items in order (consecutive threads
 // read consecutive partials, so the reads coalesce), 8 loads in flight, then
-// the tail rows in order. Serves folded and plain launches alike (m = 1, no
-// tail).
+// its tail and head elements in order (as in cols_fold_combine_kernel).
+// Serves views and plain launches alike (m = 1, rot = 0, no tail).
 template <class Op>
 __global__ __launch_bounds__(kColsCombineBlock) void cols_combine_wide_kernel(
     const typename Op::acc_t* __restrict__ partials, unsigned int items, size_t cols,
-    const typename Op::elem_t* __restrict__ tail, unsigned int tail_rows, typename Op::out_t* __restrict__ out) {
+    const typename Op::elem_t* __restrict__ tail, size_t tail_elems, unsigned int rot,
+    const typename Op::elem_t* __restrict__ head, typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
-    const size_t c = (size_t)blockIdx.x * kColsCombineBlock + threadIdx.x;
-    if (c >= cols) return;
+    const size_t c0 = (size_t)blockIdx.x * kColsCombineBlock + threadIdx.x;
+    if (c0 >= cols) return;
+    // Thread c0 takes the partials of run position c0, those of real column
+    // c = (c0 + rot) mod cols.
+    const size_t c = (c0 + rot) % cols;
     acc_t v = Op::identity();
     for (unsigned int j0 = 0; j0 < items; j0 += 8) {
         acc_t t[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const unsigned int j = j0 + u < items ? j0 + u : items - 1;  // uniform
-            t[u] = partials[(size_t)j * cols + c];
+            t[u] = partials[(size_t)j * cols + c0];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
             if (j0 + u < items) v = Op::combine(v, t[u]);
     }
-    for (unsigned int t = 0; t < tail_rows; ++t) v = Op::combine(v, Op::lift(tail[(size_t)t * cols + c], 0));
+    for (size_t i = c0; i < tail_elems; i += cols) v = Op::combine(v, Op::lift(tail[i], 0));
+    for (size_t f = c; f < rot; f += cols) v = Op::combine(v, Op::lift(head[f], 0));
     out[c] = Op::finish(v);
 }
 
@@ -268,7 +280,7 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
                             typename Op::out_t* out, const ColsLaunch& L, bool nt, hipStream_t stream) {
     auto* partials = static_cast<typename Op::acc_t*>(L.partials);
     const dim3 grid((unsigned int)(L.ncb * L.nchunks));
-    typename Op::out_t* direct = (L.nchunks == 1 && L.fold_m <= 1) ? out : nullptr;
+    typename Op::out_t* direct = (L.nchunks == 1 && L.fold_m <= 1 && L.rot == 0) ? out : nullptr;
     if (nt)
         hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF>), grid, dim3(kWave), 0, stream, x,
                            rows, cols, ld, L.ncb, L.ngroups, partials, direct);
@@ -278,20 +290,21 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
     hipError_t e = hipGetLastError();
     const size_t W = kColsCombineBlock / kWave;
     if (e != hipSuccess) return e;
-    if (L.nchunks == 1 && L.fold_m <= 1) return e;
+    if (direct != nullptr) return e;
     // Items per real column; with at least 64 columns per item, one thread
     // per column (coalesced), else one block or wave per column.
     const size_t items = L.nchunks * (size_t)(L.fold_m > 1 ? L.fold_m : 1);
     const auto* tail = static_cast<const typename Op::elem_t*>(L.tail);
+    const auto* head = static_cast<const typename Op::elem_t*>(L.head);
     if (items * 64 <= L.real_cols) {
         const size_t nb = (L.real_cols + kColsCombineBlock - 1) / kColsCombineBlock;
         hipLaunchKernelGGL((cols_combine_wide_kernel<Op>), dim3((unsigned int)nb), dim3(kColsCombineBlock), 0, stream,
-                           partials, (unsigned int)items, L.real_cols, tail, (unsigned int)L.tail_rows, out);
+                           partials, (unsigned int)items, L.real_cols, tail, L.tail_elems, L.rot, head, out);
         return hipGetLastError();
     }
-    if (L.fold_m > 1) {
+    if (L.fold_m > 1 || L.rot > 0) {
         hipLaunchKernelGGL((cols_fold_combine_kernel<Op>), dim3((unsigned int)L.real_cols), dim3(kColsCombineBlock),
-                           0, stream, partials, (unsigned int)items, L.real_cols, tail, (unsigned int)L.tail_rows,
+                           0, stream, partials, (unsigned int)items, L.real_cols, tail, L.tail_elems, L.rot, head,
                            out);
         return hipGetLastError();
     }

@@ -101,15 +101,19 @@ struct ColsLaunch {
     int width;
     unsigned int ngroups;
     void* partials;
-    // fold_m > 1: the launch runs on a contiguous matrix viewed with fold_m
-    // consecutive rows as one (rows / fold_m rows of fold_m * real_cols
-    // columns, so rows start 16-byte aligned); the partials of the fold_m
-    // view columns of each real column are then added, and the tail_rows
-    // (< fold_m) real rows after the view, starting at `tail`, last.
+    // fold_m > 1 or rot > 0: the launch runs on a view of a contiguous
+    // matrix, fold_m consecutive rows as one view row of fold_m * real_cols
+    // columns starting rot (0-31) elements into the matrix, so that view rows
+    // start 16-byte aligned. View column c' holds real column
+    // (c' + rot) % real_cols. Pass 2 adds, per real column, the partials of
+    // its fold_m view columns, then its elements among the tail_elems after
+    // the view (from `tail`) and among the rot before it (from `head`).
     int fold_m;
     size_t real_cols;
-    size_t tail_rows;
+    size_t tail_elems;
     const void* tail;
+    unsigned int rot;
+    const void* head;
 };
 
 bool flat_policy_supported(const FlatPolicy& p);

@@ -600,16 +600,24 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     libred::ColsLaunch L;
     L.fold_m = 1;
     L.real_cols = cols;
-    L.tail_rows = 0;
+    L.tail_elems = 0;
     L.tail = nullptr;
+    L.rot = 0;
+    L.head = nullptr;
     // A contiguous matrix may be viewed with m consecutive rows as one row
     // of m * cols columns (see fold_rows): for a width that is not a
     // multiple of 4 this makes every view row start 16-byte aligned, so four
     // columns go per lane; for any width it can leave fewer lanes idle.
-    // Pass 2 adds each real column's m view columns, then the last rows % m
-    // rows.
-    const size_t rows_real = rows, cols_real = cols;
-    if (p.vec != 1 && p.fold != 1 && ld == cols && aligned(x, 16)) {
+    // When x is not 16-byte aligned the view starts rot = 1-31 elements into
+    // the matrix, at the next 128-byte boundary (m * cols is a multiple of 4,
+    // so every view row starts 16-byte aligned, and on a line when m * cols
+    // is a multiple of 32: 4096 columns at x + 4 bytes ran at 6.3 TB/s from
+    // the next 16-byte boundary). Column membership depends only on
+    // an element's position mod cols, so view column c' holds real column
+    // (c' + rot) mod cols. Pass 2 adds each real column's m view columns,
+    // then its elements after the last whole view row and before the view.
+    const size_t cols_real = cols;
+    if (p.vec != 1 && p.fold != 1 && (ld == cols || rows == 1) && rows > 0) {
         size_t m = fold_rows(rows, cols);
         if (p.fold > 1) {  // the policy's m, made a multiple of 4 / gcd(cols, 4) that fits the rows
             const size_t m0 = cols % 4 == 0 ? 1 : cols % 2 == 0 ? 2 : 4;
@@ -617,13 +625,20 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             while (m > rows || cols * m > RED_MAX_N) m -= m0;
             if (m < m0) m = 1;
         }
-        if (m > 1) {
+        const size_t rot = (uintptr_t)x % 16 == 0 ? 0 : (128 - (uintptr_t)x % 128) % 128 / sizeof(float);
+        const size_t W = cols_real * m;  // view columns
+        const size_t total = rows * cols_real;
+        const size_t vrows = total >= rot ? (total - rot) / W : 0;
+        if ((m > 1 || rot > 0) && W % 4 == 0 && vrows >= 1) {
             L.fold_m = (int)m;
-            rows = rows_real / m;
-            cols = cols_real * m;
-            ld = cols;
-            L.tail_rows = rows_real - rows * m;
-            L.tail = x + rows * m * cols_real;
+            L.rot = (unsigned int)rot;
+            L.head = x;
+            x += rot;
+            rows = vrows;
+            cols = W;
+            ld = W;
+            L.tail = x + vrows * W;
+            L.tail_elems = total - rot - vrows * W;
         }
     }
     const bool vec_ok = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
@@ -653,7 +668,7 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     }
     L.nchunks = nchunks;
     L.partials = nullptr;
-    if (nchunks > 1 || L.fold_m > 1) {
+    if (nchunks > 1 || L.fold_m > 1 || L.rot > 0) {
         st = get_scratch(dev, stream, nchunks * cols * 8, &L.partials);
         if (st != RED_OK) return st;
     }

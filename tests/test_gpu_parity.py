@@ -731,6 +731,33 @@ def test_cols_line_views(rows, cols):
         assert np.array_equal(m.cpu().numpy(), M), p
 
 
+@pytest.mark.parametrize("rows,cols", [(1, 8), (3, 5), (100, 7), (7, 3), (1000, 64), (33, 1000), (2, 4096),
+                                       (3001, 33), (500, 65), (41, 300), (1000, 1), (999, 2), (5, 1021),
+                                       (40_001, 257), (2, 2), (1, 5)])
+def test_cols_unaligned_views(rows, cols):
+    # A contiguous matrix whose x is 1-3 floats past a 16-byte boundary is
+    # read through a view that starts at the next boundary, so view column c'
+    # holds real column (c' + rot) mod cols; the elements before the view and
+    # after its last whole row are added in the second pass. NaN on both
+    # sides of the matrix shows any element read from outside it.
+    rng = np.random.default_rng(rows * 5 + cols)
+    a = rng.standard_normal((rows, cols)).astype(np.float32)
+    a[(np.arange(cols) * 7919) % rows, np.arange(cols)] = 40.0 + np.arange(cols) % 83
+    a[0, :] = np.where(np.arange(cols) % 3 == 0, 90.0, a[0, :])      # maxima before the view
+    a[-1, ::2] = 95.0                                                  # and after it
+    S, A = oracle.cols_sum_f32(a)
+    M = oracle.cols_max_f32(a)
+    for offset in (1, 2, 3):
+        for p in (None, dict(fold=16), dict(fold=4, unroll=2), dict(width=4, unroll=2), dict(vec=1)):
+            say(f"cols unaligned {rows}x{cols} offset={offset} policy={p}")
+            x = device_view(a, offset)
+            s = rl.red_cols_sum_f32(x, policy=p)
+            m = rl.red_cols_max_f32(x, policy=p)
+            torch.cuda.synchronize()
+            assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), (offset, p)
+            assert np.array_equal(m.cpu().numpy(), M), (offset, p)
+
+
 def _nonfinite_matrix(rows, cols, seed):
     rng = np.random.default_rng(seed)
     a = rng.standard_normal((rows, cols)).astype(np.float32)
