@@ -395,6 +395,23 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
                     u = c;
                 }
             max_blocks = u == 16 ? 1024 : 2048;
+            // Rows of 33-39 floats: when 4096-float tiles leave no room to
+            // hold the results in LDS but 2048-float tiles on 1024 waves do,
+            // and their passes are within 5% as full, take those (1 GiB: sums
+            // 5.5 -> 5.5-6.4, maxima 5.5-5.6 -> 5.7-6.0 TB/s; at 41-43 floats
+            // the maxima ran 8% slower).
+            auto holds = [&](size_t c, size_t mb) {
+                const size_t r = tile_rows(c), tl = (rows + r - 1) / r;
+                const size_t g = tl < mb ? tl : mb;
+                const size_t need = 64 * c * 16 + (tl + g - 1) / g * r * sizeof(float);
+                return need <= info.lds_per_cu / ((g + info.cu_count - 1) / info.cu_count) &&
+                       need <= info.lds_per_block;
+            };
+            if (u == 16 && p.defer == 0 && cols < 40 && base_u <= 8 && !holds(16, 1024) && holds(8, 1024) &&
+                pass_use(8) >= pass_use(16) - 0.05) {
+                u = 8;
+                max_blocks = 1024;
+            }
         }
         L.staged_u = (int)u;
         // An explicit policy may ask for larger tiles (unroll 8 or 16).
