@@ -61,6 +61,8 @@ struct RowsLaunch {
     int staged_vread;   // the LDS-staged kernel reads 16-byte vectors (rows of whole vectors)
     unsigned int staged_hold;  // > 0: the LDS-staged kernel holds this many results per wave in
                                //   dynamic LDS and stores them after the wave's last tile
+    int staged_spread;  // the LDS-staged kernel's element reads start at a different element
+                        //   in each row of a pass (rows at a stride of a multiple of 16)
 };
 constexpr size_t kMaxSplitPartials = 32768;
 

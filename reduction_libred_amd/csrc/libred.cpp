@@ -306,7 +306,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
 
-    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     // Rows of fewer than 1024 floats go to the LDS-staged kernel (short_rows
     // 0), or do so with 2^(short_rows - 3) lanes per row (short_rows 3-9),
     // when the rows are contiguous or their gaps hold at most a quarter of a
@@ -417,6 +417,15 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         // An explicit policy may ask for larger tiles (unroll 8 or 16).
         if (pol != nullptr && p.unroll > L.staged_u) L.staged_u = p.unroll >= 16 ? 16 : 8;
         L.staged_rows = (unsigned int)tile_rows((size_t)L.staged_u);
+        // Element reads: LDS serves each 32-lane half of a wave from 32
+        // banks of 4 bytes. When 16 or more rows of a half start on the same
+        // bank ((pass / 2) * gcd(step, 32) / 32 of them), their lanes read
+        // the same banks at every step; then each row's lanes start at a
+        // different element (32 floats at an unaligned x 2.3 -> 5.7, 64
+        // floats 4.0 -> 5.6 TB/s; at 8 such rows and fewer, the wrapping
+        // index cost 7-30%).
+        const size_t low = step & (~step + 1), bank_gcd = low < 32 ? low : 32;
+        L.staged_spread = !L.staged_vread && (pass / 2) * bank_gcd >= 16 * 32 ? 1 : 0;
         const size_t tiles = (rows + L.staged_rows - 1) / L.staged_rows;
         L.grid = (int)(tiles < max_blocks ? tiles : max_blocks);
         // A wave's results are held in LDS and stored after its last tile

@@ -468,7 +468,8 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
 // contiguous, 16-byte aligned matrix, R is a multiple of 4 / gcd(cols, 4),
 // so every tile starts 16-byte aligned and off is 0.) The wave then reduces
 // the tile's rows 64 / S at a time with S = 2^LOG2S lanes per row: lane s of
-// a row adds elements s, s + S, ... in order, then the segment reduce; with
+// a row adds elements s, s + S, ... in order (with SPREAD, from a starting
+// element that differs between the rows of a pass), then the segment reduce; with
 // VREAD (rows of whole vectors, off always 0 and ld a multiple of 4) lane s
 // reads vectors s, s + S, ... of its row. Tiles are dealt round-robin to the
 // waves, and the next tile's loads are issued before the current tile is
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
 //
 // The host ensures that a tile's span plus 3 fits 256 * U elements, that the
 // matrix spans at least 8 elements, and that R * ld >= 4.
-template <class Op, int LOG2S, int U, bool NT, bool VREAD, bool HOLD>
+template <class Op, int LOG2S, int U, bool NT, bool VREAD, bool HOLD, bool SPREAD>
 __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, size_t ld,
                                                             unsigned int sh, unsigned int R,
@@ -513,6 +514,14 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
     const size_t vlast = (end - 1) / E;                       // the cover's last vector
     const bool cut_last = end % E != 0;                       // ... reaches past the matrix
     const size_t safe = sh > 0 ? 1 : 0;                       // a vector wholly inside
+    // With SPREAD (element reads), lane s of a pass's row q reads its m
+    // elements s, s + S, ... starting from number q mod m and wrapping round:
+    // rows at a stride of a multiple of 16 or 32 words would otherwise put
+    // many rows of a pass on the same LDS banks at every step.
+    const unsigned int Cw = (unsigned int)cols;
+    const unsigned int m_lane = s < Cw ? ((Cw - 1 - s) >> LOG2S) + 1 : 0u;
+    const unsigned int wrap_back = m_lane << LOG2S;
+    const unsigned int j_first = m_lane > 0 ? s + (((lane >> LOG2S) % m_lane) << LOG2S) : s;
     auto rows_in = [&](size_t t) -> unsigned int {  // rows of tile t (0 past the last tile)
         return t + 1 < ntiles ? R : t + 1 == ntiles ? (unsigned int)(rows - t * R) : 0u;
     };
@@ -568,6 +577,25 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
                         const vec_t v = rowv[j];
 #pragma unroll
                         for (int k = 0; k < (int)E; ++k) a = Op::combine(a, Op::lift(v[k], j * E + k));
+                    }
+                }
+            } else if constexpr (SPREAD) {
+                if (r < rows_t) {
+                    const elem_t* row = lds + off + r * L;
+                    auto next = [&](unsigned int j) { return j + S >= C ? j + S - wrap_back : j + S; };
+                    unsigned int j = j_first, i = 0;
+                    for (; i + 4 <= m_lane; i += 4) {
+                        const unsigned int j1 = next(j), j2 = next(j1), j3 = next(j2);
+                        const elem_t e0 = row[j], e1 = row[j1], e2 = row[j2], e3 = row[j3];
+                        a = Op::combine(a, Op::lift(e0, j));
+                        a = Op::combine(a, Op::lift(e1, j1));
+                        a = Op::combine(a, Op::lift(e2, j2));
+                        a = Op::combine(a, Op::lift(e3, j3));
+                        j = next(j3);
+                    }
+                    for (; i < m_lane; ++i) {
+                        a = Op::combine(a, Op::lift(row[j], j));
+                        j = next(j);
                     }
                 }
             } else if (r < rows_t) {
@@ -783,28 +811,41 @@ static hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_
     }
 }
 
-template <class Op, int LOG2S, int U, bool VREAD>
-static hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
-                                  const RowsLaunch& L, bool nt, hipStream_t stream) {
+template <class Op, int LOG2S, int U, bool VREAD, bool SPREAD>
+static hipError_t rows_staged_go(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
+                                 const RowsLaunch& L, bool nt, hipStream_t stream) {
     const size_t held_bytes = (size_t)L.staged_hold * sizeof(typename Op::out_t);
     // x's offset, in elements, from the 16-byte boundary before it.
     const unsigned int sh = (unsigned int)(((uintptr_t)x % 16) / sizeof(typename Op::elem_t));
     if (L.staged_hold > 0) {
         if (nt)
-            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true>), dim3(L.grid), dim3(kWave),
-                               held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
+            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true, SPREAD>), dim3(L.grid),
+                               dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
         else
-            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, true>), dim3(L.grid), dim3(kWave),
-                               held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
+            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, true, SPREAD>), dim3(L.grid),
+                               dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
     } else {
         if (nt)
-            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, false>), dim3(L.grid), dim3(kWave), 0,
-                               stream, x, rows, cols, ld, sh, L.staged_rows, out);
+            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, false, SPREAD>), dim3(L.grid),
+                               dim3(kWave), 0, stream, x, rows, cols, ld, sh, L.staged_rows, out);
         else
-            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, false>), dim3(L.grid), dim3(kWave), 0,
-                               stream, x, rows, cols, ld, sh, L.staged_rows, out);
+            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, false, SPREAD>), dim3(L.grid),
+                               dim3(kWave), 0, stream, x, rows, cols, ld, sh, L.staged_rows, out);
     }
     return hipGetLastError();
+}
+
+// Spread element reads are built only where the host asks for them: one or
+// two lanes per row (32 or more rows per pass).
+template <class Op, int LOG2S, int U, bool VREAD>
+static hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
+                                  const RowsLaunch& L, bool nt, hipStream_t stream) {
+    if constexpr (!VREAD && LOG2S <= 1) {
+        if (L.staged_spread) return rows_staged_go<Op, LOG2S, U, false, true>(x, rows, cols, ld, out, L, nt, stream);
+    } else {
+        if (L.staged_spread) return hipErrorInvalidValue;
+    }
+    return rows_staged_go<Op, LOG2S, U, VREAD, false>(x, rows, cols, ld, out, L, nt, stream);
 }
 
 template <class Op, int LOG2S, int U>

@@ -602,7 +602,12 @@ def test_rows_random(rows, cols):
                                            (2048, 2, 0), (77, 511, 1),
                                            # a last tile of one short row whose elements share the
                                            # matrix's last vector with the tile before (unaligned x)
-                                           (1022, 1, 0), (2043, 1, 0), (511, 2, 0), (341, 3, 0), (1023, 1, 1)])
+                                           (1022, 1, 0), (2043, 1, 0), (511, 2, 0), (341, 3, 0), (1023, 1, 1),
+                                           # rows at a stride of a multiple of 16 floats: element reads
+                                           # start at a different element in each row of a pass
+                                           (300, 64, 0), (130, 128, 0), (65, 512, 0), (500, 16, 0),
+                                           (3000, 32, 0), (40, 960, 0), (200, 48, 16), (100, 60, 4),
+                                           (300, 14, 2), (90, 250, 6), (500, 30, 2), (300, 62, 2)])
 def test_rows_staged_any_offset(rows, cols, gap):
     # The LDS-staged kernel at every 16-byte offset of x and with short gaps
     # between rows: each tile's span is loaded through its aligned cover, and
