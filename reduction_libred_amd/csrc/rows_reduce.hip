@@ -499,6 +499,12 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
     constexpr int S = 1 << LOG2S;
     constexpr int P = kWave / S;
     constexpr size_t E = Op::kPerVec;
+    // Element reads keep eight LDS reads in flight where the combine is a
+    // cheap 32-bit one and a row has 4 or more lanes: such a loop has too
+    // little arithmetic to cover four reads' latency (1 GiB, maxima of 100,
+    // 256 and 384 floats: 6.1-6.5 -> 6.6-6.9 TB/s). Float64 sums, and maxima
+    // with one or two lanes per row, measured as fast or faster with four.
+    constexpr bool kEightReads = sizeof(acc_t) == 4 && LOG2S >= 2;
     __shared__ vec_t stage[kWave * U];
     extern __shared__ __align__(16) unsigned char rows_staged_held[];
     typename Op::out_t* held = reinterpret_cast<typename Op::out_t*>(rows_staged_held);
@@ -601,6 +607,15 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
             } else if (r < rows_t) {
                 const elem_t* row = lds + off + r * L;
                 unsigned int j = s;
+                if constexpr (kEightReads) {
+                    for (; j + 7 * S < C; j += 8 * S) {  // eight LDS reads in flight
+                        elem_t e[8];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) e[k] = row[j + k * S];
+#pragma unroll
+                        for (int k = 0; k < 8; ++k) a = Op::combine(a, Op::lift(e[k], j + k * S));
+                    }
+                }
                 for (; j + 3 * S < C; j += 4 * S) {  // four LDS reads in flight
                     const elem_t e0 = row[j], e1 = row[j + S], e2 = row[j + 2 * S], e3 = row[j + 3 * S];
                     a = Op::combine(a, Op::lift(e0, j));
