@@ -21,8 +21,12 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libred.so")
 # sha256 of each compiled object, written beside the library: it identifies
-# the machine code a measurement was taken on (the objects are reproducible,
-# and an edit that leaves a unit's code unchanged leaves its hash unchanged).
+# the machine code a measurement was taken on. hipcc would otherwise stamp a
+# random compilation-unit id (__hip_cuid_*) into every object; -cuid=<name>
+# fixes it per unit (unique, so the units still link together), so two
+# builds of the same sources give byte-identical objects (checked in
+# tests/test_build_repro.py), and an edit that leaves a unit's code unchanged
+# leaves its hash unchanged.
 MANIFEST = os.path.join(HERE, "libred_objects.json")
 
 SOURCES = ["libred.cpp", "flat_sum_f32.hip", "flat_ops.hip", "flat_fused.hip", "flat_argmax.hip", "flat_argmin.hip",
@@ -49,9 +53,12 @@ COMMON = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def compile_unit(src, obj):
+    """Compile csrc/<src> with the library's flags into object file `obj`."""
+    # A fixed compilation-unit id per unit instead of a random one: the
+    # objects are reproducible.
+    cuid = "libred_" + os.path.splitext(src)[0]
+    cmd = [hipcc(), *COMMON, f"-cuid={cuid}", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so.
     noise = "'-packed-fp32-ops' is not a recognized feature"
@@ -61,6 +68,10 @@ def _compile(src):
     if err.strip():
         print(err, file=sys.stderr)
     return obj
+
+
+def _compile(src):
+    return compile_unit(src, os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o"))
 
 
 def build(verbose=True):
