@@ -62,8 +62,10 @@ typedef enum red_status {
     RED_ERR_NO_DEVICE = 2,   /* no usable HIP device is current */
     RED_ERR_HIP = 3,         /* a HIP call or kernel launch failed; see red_last_hip_error */
     RED_ERR_ALLOC = 4,       /* the library workspace could not be allocated */
-    RED_ERR_CAPTURE = 5      /* the stream is being captured into a graph and the call
+    RED_ERR_CAPTURE = 5,     /* the stream is being captured into a graph and the call
                                 would first have to allocate its workspace or scratch */
+    RED_ERR_SCRATCH = 6      /* red_sum_f32_noalloc: the launch needs more block partials
+                                than its fixed device array holds */
 } red_status;
 
 /* Largest element count accepted by one call (2^40 elements, 4 TiB of float). */
@@ -81,6 +83,24 @@ typedef enum red_status {
  * then be NULL).
  */
 red_status red_sum_f32(const float *x, size_t n, float *out, hipStream_t stream);
+
+/*
+ * red_sum_f32 for callers that cannot allocate device memory: code being
+ * captured into a HIP graph on a stream that holds no workspace yet, serving
+ * loops that must not allocate, harnesses that forbid hipMalloc. Same
+ * arguments, kernels, launch shapes and result bits as red_sum_f32 (n, x,
+ * out, stream; errors as there). It calls no hipMalloc, hipFree or other
+ * allocating routine: the block partials go to a fixed array of 4096
+ * float64 values (32 KiB) in device memory, one per device, held until the
+ * process exits. A launch that would need more partials than that returns
+ * RED_ERR_SCRATCH before anything is enqueued (on MI355X the default shapes
+ * launch at most 2 blocks per compute unit, 512 in all). Every call on one
+ * device shares that device's array, and each call overwrites the partials
+ * it reads before reading them, so nothing in it needs clearing; but calls
+ * that overlap in time on one device (on different streams, or graphs
+ * replayed concurrently) race on it and may return wrong sums: order them.
+ */
+red_status red_sum_f32_noalloc(const float *x, size_t n, float *out, hipStream_t stream);
 
 /*
  * Sum of n int32 values into one int64: *out = x[0] + ... + x[n-1], exact

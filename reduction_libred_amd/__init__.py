@@ -25,6 +25,7 @@ RED_ERR_NO_DEVICE = 2
 RED_ERR_HIP = 3
 RED_ERR_ALLOC = 4
 RED_ERR_CAPTURE = 5
+RED_ERR_SCRATCH = 6
 RED_MAX_N = 1 << 40
 
 
@@ -77,6 +78,7 @@ _S = ctypes.c_int  # red_status
 SIGNATURES = {
     "red_sum_f32": (_S, [_P, _Z, _P, _P]),
     "red_sum_i32_i64": (_S, [_P, _Z, _P, _P]),
+    "red_sum_f32_noalloc": (_S, [_P, _Z, _P, _P]),
     "red_max_f32": (_S, [_P, _Z, _P, _P]),
     "red_sum_max_f32": (_S, [_P, _Z, _P, _P]),
     "red_min_f32": (_S, [_P, _Z, _P, _P]),
@@ -210,6 +212,12 @@ def _flat(name, cname, x, out, in_dtype, out_dtype, stream, policy=None, out_sha
 def red_sum_f32(x, out=None, stream=None, policy=None):
     """Sum of a float32 tensor into a 0-d float32 tensor (float64 inside)."""
     return _flat("red_sum_f32", "red_sum_f32", x, out, torch.float32, torch.float32, stream, policy)
+
+
+def red_sum_f32_noalloc(x, out=None, stream=None):
+    """red_sum_f32 with its block partials in a fixed device array: no
+    device allocation. Calls that overlap in time on one device race."""
+    return _flat("red_sum_f32_noalloc", "red_sum_f32_noalloc", x, out, torch.float32, torch.float32, stream)
 
 
 def red_sum_i32_i64(x, out=None, stream=None, policy=None):

@@ -1,6 +1,7 @@
 // libred.cpp -- the C ABI of libred: argument checks, device facts, the
 // per-(device, stream) workspace, launch shapes, and the calls into the
-// kernel translation units. Host code only.
+// kernel translation units. Host code, apart from the one device array of
+// the allocation-free sum below.
 #include <stdint.h>
 #include <string.h>
 
@@ -18,6 +19,15 @@
 using libred::FlatPolicy;
 using libred::RowsPolicy;
 using libred::Workspace;
+
+// The block partials of red_sum_f32_noalloc, which allocates nothing: a
+// fixed device array instead of a workspace. Every device the library runs
+// on holds its own copy until the process ends. In host code `scratch`
+// names only a host-side stand-in, never device memory; host code uses the
+// device address that hipGetSymbolAddress gives for the current device
+// (noalloc_scratch below), and passes that to the kernels.
+constexpr size_t kNoAllocMaxPartials = 4096;  // float64 partials: 32 KiB
+static __device__ __align__(256) double scratch[kNoAllocMaxPartials];
 
 namespace {
 
@@ -45,6 +55,7 @@ constexpr size_t kWorkspaceBytes = kTicketBytes + kMaxPartials * libred::kMaxPar
 std::mutex g_mu;
 std::map<int, DeviceInfo> g_devices;
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
+std::map<int, double*> g_noalloc_scratch;  // device -> its copy of `scratch`
 
 // Per-(device, stream) scratch for column partials, grown on demand up to
 // kColsScratchMax bytes (starting at 1 MiB and at least doubling each time,
@@ -88,6 +99,13 @@ constexpr size_t kSplitTargetWaves = 1024;
 // 165 us within a few dozen back-to-back calls, while this shape held
 // 146 us.
 constexpr FlatPolicy kFusedLarge = {256, 1, 4, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
+
+// The allocation-free sum reads only partials its own first launch wrote,
+// which holds for the two-launch combine of every default shape (the
+// counter of the single-launch combine would have to start at zero).
+static_assert(kFlatTiny.combine == libred::kCombineTwoPass && kFlatSmall.combine == libred::kCombineTwoPass &&
+                  kFlatCached.combine == libred::kCombineTwoPass && kFlatLarge.combine == libred::kCombineTwoPass,
+              "red_sum_f32_noalloc relies on the two-launch combine");
 
 FlatPolicy default_flat(size_t n) {
     if (n <= kTinyMax) return kFlatTiny;
@@ -167,6 +185,21 @@ red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
     w.max_partials = kMaxPartials;
     g_workspaces.emplace(key, w);
     *ws = w;
+    return RED_OK;
+}
+
+// Device address of `scratch` on device `dev`, which must be current: looked
+// up once per device, then cached. No allocation.
+red_status noalloc_scratch(int dev, double** out) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_noalloc_scratch.find(dev);
+    if (it == g_noalloc_scratch.end()) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) return fail(e == hipSuccess ? hipErrorInvalidSymbol : e, RED_ERR_HIP);
+        it = g_noalloc_scratch.emplace(dev, static_cast<double*>(ptr)).first;
+    }
+    *out = it->second;
     return RED_OK;
 }
 
@@ -715,6 +748,29 @@ red_status red_sum_i32_i64(const int32_t* x, size_t n, int64_t* out, hipStream_t
     return flat_call(x, n, out, nullptr, stream, libred::launch_sum_i32_i64);
 }
 
+red_status red_sum_f32_noalloc(const float* x, size_t n, float* out, hipStream_t stream) {
+    if (n > RED_MAX_N || (n > 0 && x == nullptr) || out == nullptr) return RED_ERR_INVALID_ARG;
+    if (!aligned(x, sizeof(float)) || !aligned(out, sizeof(float))) return RED_ERR_INVALID_ARG;
+    if (overlap(x, n * sizeof(float), out, sizeof(float))) return RED_ERR_INVALID_ARG;
+    const FlatPolicy p = default_flat(n);
+    int dev;
+    DeviceInfo info;
+    red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    const size_t grid = flat_grid_for(n, p, info.cu_count);
+    if (grid > kNoAllocMaxPartials) return RED_ERR_SCRATCH;
+    double* ptr = nullptr;
+    st = noalloc_scratch(dev, &ptr);
+    if (st != RED_OK) return st;
+    Workspace ws;
+    ws.ticket = nullptr;  // the two-launch combine never touches a counter
+    ws.partials = ptr;
+    ws.max_partials = kNoAllocMaxPartials;
+    const hipError_t e = libred::launch_sum_f32(x, n, out, (int)grid, p, ws, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
 red_status red_max_f32(const float* x, size_t n, float* out, hipStream_t stream) {
     return flat_call(x, n, out, nullptr, stream, libred::launch_max_f32);
 }
@@ -784,6 +840,8 @@ const char* red_status_string(red_status status) {
         case RED_ERR_ALLOC: return "RED_ERR_ALLOC: workspace allocation failed";
         case RED_ERR_CAPTURE:
             return "RED_ERR_CAPTURE: the stream is being captured and its workspace is missing or too small";
+        case RED_ERR_SCRATCH:
+            return "RED_ERR_SCRATCH: the call needs more block partials than the fixed scratch array holds";
     }
     return "unknown red_status";
 }

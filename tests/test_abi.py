@@ -47,7 +47,7 @@ def test_exports_match_headers():
 
 def test_status_strings_and_version():
     L = rl.lib()
-    for code in range(6):
+    for code in range(7):
         assert L.red_status_string(code) != b"unknown red_status", code
     assert L.red_status_string(99) == b"unknown red_status"
     assert rl.red_version().startswith("libred")
@@ -62,7 +62,7 @@ A, B = 0x10000, 0x20000            # aligned fake addresses, never dereferenced
 
 def test_flat_argument_errors():
     L = rl.lib()
-    for f in (L.red_sum_f32, L.red_max_f32, L.red_sum_i32_i64):
+    for f in (L.red_sum_f32, L.red_sum_f32_noalloc, L.red_max_f32, L.red_sum_i32_i64):
         assert f(None, 4, _p(B), None) == INVALID                 # null x, n > 0
         assert f(_p(A), 4, None, None) == INVALID                 # null out
         assert f(_p(A + 1), 4, _p(B), None) == INVALID            # misaligned x
