@@ -10,7 +10,8 @@ combine launch. The line also carries the roofline of the streaming kernel
 host, and the other entry points at their own workloads.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
-    python bench.py --ablation | --widths     (other measurements, one JSON line each)
+    python bench.py --ablation | --widths | --probe-sweep
+                                              (other measurements, one JSON line each)
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -75,6 +76,9 @@ def parse_args():
     ap.add_argument("--ablation", action="store_true",
                     help="instead of the headline: time the five-rung ladder and the production "
                          "path on the 2^28 array, and the LDS bank probe; print one JSON line")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="instead of the headline: time the load-only read probe at every launch shape "
+                         "on the 2^28-float array and print one JSON line, fastest first")
     ap.add_argument("--widths", action="store_true",
                     help="instead of the headline: time the row and column entry points on 1 GiB "
                          "of f32 viewed as (2^28 // cols) x cols for a range of widths; print one "
@@ -187,6 +191,60 @@ def run_widths(args, torch, rl, W, timer, dev):
                       "shapes": shapes}), flush=True)
 
 
+def read_shapes():
+    """Every launch shape of the read probe: block 64 / 256 / 1024, 1-16 waves
+    per CU, 4-32 loads in flight per lane, non-temporal or not, three layouts
+    (the shapes that fit in registers without spilling)."""
+    for block in (64, 256, 1024):
+        per_block = block // 64
+        for waves in (1, 2, 4, 8, 16):
+            if waves < per_block or waves % per_block:
+                continue
+            for unroll in (4, 8, 16, 32):
+                for layout in (0, 1, 2):
+                    if block == 1024 and (unroll > 16 or (layout == 2 and unroll > 8)):
+                        continue
+                    for nt in (0, 1):
+                        yield dict(block=block, blocks_per_cu=waves // per_block, unroll=unroll, nontemporal=nt,
+                                   layout=layout)
+
+
+def run_probe_sweep(args, torch, rl, W, timer, dev):
+    name = "sum_max_f32_2p28"
+    log(f"generate {name}")
+    x = torch.from_numpy(W.workload(name)).to(dev)
+    nbytes = 4 * x.numel()
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    results = []
+    reps = max(5, min(args.steps, 30))
+    for shape in read_shapes():
+        fn = lambda: rl.red_probe_read_ceiling(x, sink=sink, shape=shape)
+        for _ in range(3):
+            fn()
+        ms = timer.region_ms(fn, reps)
+        results.append(dict(shape, **{"us": round(ms * 1e3, 2), "GB/s": round(gbps(nbytes, ms), 1)}))
+        log(f"{shape}: {results[-1]['GB/s']} GB/s")
+    results.sort(key=lambda r: -r["GB/s"])
+    # The five fastest again, alternating, to separate them from noise.
+    top = results[:5]
+    again = {i: [] for i in range(len(top))}
+    for _ in range(3):
+        for i, r in enumerate(top):
+            shape = {k: r[k] for k in ("block", "blocks_per_cu", "unroll", "nontemporal", "layout")}
+            ms = timer.region_ms(lambda: rl.red_probe_read_ceiling(x, sink=sink, shape=shape), reps)
+            again[i].append(gbps(nbytes, ms))
+    for i, r in enumerate(top):
+        r["GB/s_rerun_median"] = round(sorted(again[i])[1], 1)
+    # The reduction kernel in the same process, for comparison.
+    parts = torch.empty(rl.red_flat_grid(x.numel()), dtype=torch.float64, device=dev)
+    for _ in range(3):
+        rl.red_sum_f32_partials(x, partials=parts)
+    ms = timer.region_ms(lambda: rl.red_sum_f32_partials(x, partials=parts), reps)
+    print(json.dumps({"mode": "probe_sweep", "workload": name, "bytes": nbytes, "reps": reps,
+                      "default_shape": rl.red_default_read_shape().as_dict(),
+                      "sum_kernel_GB/s": round(gbps(nbytes + 4, ms), 1), "shapes": results}), flush=True)
+
+
 class Timer:
     """HIP events on one stream around a region of `reps` enqueued calls."""
 
@@ -254,6 +312,9 @@ def main():
     if args.widths:
         run_widths(args, torch, rl, W, timer, dev)
         return
+    if args.probe_sweep:
+        run_probe_sweep(args, torch, rl, W, timer, dev)
+        return
 
     # ---------------------------------------------------------- headline
     name = "sum_max_f32_2p28"
@@ -281,6 +342,8 @@ def main():
         raise RuntimeError("red_sum_f32 is not reproducible run to run")
     value = gbps(nbytes, ms)
     log(f"red_sum_f32: {ms * 1e3:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of peak)")
+    # Each step bracketed by its own events: median and min.
+    step_med, step_min = timer.per_launch_ms(step, max(20, min(args.steps, 200)))
 
     # The dominant kernel alone: steps 1-5 (the streaming pass) without the
     # one-block combine launch, via red_sum_f32_partials, same launch shape.
@@ -296,6 +359,16 @@ def main():
     achieved = gbps(nbytes, k_ms)
     log(f"flat_reduce_kernel alone: {k_ms * 1e3:.1f} us/launch, {achieved:.1f} GB/s; "
         f"per-launch median {med_ms * 1e3:.1f} us")
+    # The achievable read ceiling: the load-only probe at its default (the
+    # fastest swept) shape over the same resident array.
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    probe = lambda: rl.red_probe_read_ceiling(x, sink=sink)
+    for _ in range(args.warmup):
+        probe()
+    p_ms = timer.region_ms(probe, args.steps)
+    p_med, p_min = timer.per_launch_ms(probe, max(20, min(args.steps, 200)))
+    probe_gbps = gbps(4 * n, p_ms)
+    log(f"read probe: {p_ms * 1e3:.1f} us/launch, {probe_gbps:.1f} GB/s")
     kname = (f"flat_reduce_kernel<SumF32, {policy['block']}, {policy['unroll']}, "
              f"{'true' if policy['nontemporal'] else 'false'}, {policy['layout']}, "
              f"{'true' if policy['prefetch'] else 'false'}>")
@@ -325,7 +398,16 @@ def main():
             "cus": cu,
         },
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "pct_of_probe": round(100 * value / probe_gbps, 2),
         "elements_per_s": round(n / (ms * 1e-3), 1),
+        "step_us": {"mean": round(ms * 1e3, 3), "median": round(step_med * 1e3, 3),
+                    "min": round(step_min * 1e3, 3), "median_GB/s": round(gbps(nbytes, step_med), 2),
+                    "max_GB/s": round(gbps(nbytes, step_min), 2)},
+        "read_ceiling": {"kernel": "read_probe_kernel (load-only, xor of every word)",
+                         "shape": rl.red_default_read_shape().as_dict(), "us": round(p_ms * 1e3, 3),
+                         "median_us": round(p_med * 1e3, 3), "min_us": round(p_min * 1e3, 3),
+                         "GB/s": round(probe_gbps, 2), "pct_of_peak": round(100 * probe_gbps / PEAK_GBPS, 2),
+                         "kernel_pct_of_probe": None},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -341,6 +423,8 @@ def main():
             "step_us_with_combine_launch": round(ms * 1e3, 3),
         },
     }
+
+    result["read_ceiling"]["kernel_pct_of_probe"] = round(100 * achieved / probe_gbps, 2)
 
     # ---------------------------------------------------------- other entry points
     others = {}

@@ -27,8 +27,12 @@
  *  - The single-value entry points use a small workspace owned by the library
  *    (block partials plus a completion counter), allocated on the first call
  *    per (device, stream) and kept until the process exits. Calls on one
- *    stream are ordered, so they can share it; calls on different streams use
- *    different workspaces and may run concurrently.
+ *    stream are ordered, so they can share it; eager calls on different
+ *    streams use different workspaces and may run concurrently. The column
+ *    entry points keep their partials in a per-stream scratch buffer under
+ *    the same rule. The library allocates with the calling thread in relaxed
+ *    capture mode, so a first call on a stream that is not being captured
+ *    does not disturb a capture under way on another stream.
  *  - Graph capture: the calls can be captured into a HIP graph, provided the
  *    stream already holds what the call needs. That is its workspace, made by
  *    any earlier single-value call on the stream (row calls need it only
@@ -39,6 +43,12 @@
  *    capture stays intact. Workspace and scratch are never freed while the
  *    process runs (outgrown scratch included), so a captured graph stays
  *    valid after later calls on its stream.
+ *  - A captured graph keeps the workspace and scratch of its capture stream.
+ *    It must therefore not run at the same time as other work on that
+ *    stream's buffers: eager calls still enqueued on the capture stream, or
+ *    another graph captured on the same stream with the same buffers. To
+ *    replay graphs concurrently, give each capture buffers of its own with
+ *    red_stream_new_workspace between the captures.
  *  - Results are deterministic: for a given length and device the partials
  *    are combined in a fixed index order, so repeated calls return the same
  *    bits.
@@ -104,9 +114,15 @@ red_status red_sum_f32_noalloc(const float *x, size_t n, float *out, hipStream_t
 
 /*
  * Sum of n int32 values into one int64: *out = x[0] + ... + x[n-1], exact
- * (each element is sign-extended to 64 bits before it is added). The sum
- * wraps modulo 2^64 only if it leaves the int64 range, which needs n > 2^32.
- * n == 0 stores 0.
+ * (each element is sign-extended to 64 bits before it is added). This is the
+ * reduction of the lesson's demo 3 (block partials, then their sum) over
+ * integers: the lesson's own inputs are small integers (i mod 7), summed
+ * exactly. Integer addition is associative, so the result is the same
+ * whatever the block order, which the simulator page "simt_lab.py" (section
+ * 5, launch) asks of every kernel; its shared memory holds only 4-byte words,
+ * so the 64-bit accumulator is this library's choice (exact for every int32
+ * input). The sum wraps modulo 2^64 only if it leaves the int64 range, which
+ * needs n > 2^32. n == 0 stores 0.
  */
 red_status red_sum_i32_i64(const int32_t *x, size_t n, int64_t *out, hipStream_t stream);
 
@@ -229,6 +245,18 @@ red_status red_cols_sum_f32(const float *x, size_t rows, size_t cols, size_t ld,
                             hipStream_t stream);
 red_status red_cols_max_f32(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                             hipStream_t stream);
+
+/*
+ * A fresh workspace for (current device, stream): allocates a new workspace
+ * (zeroed on `stream`), which later calls on the stream and graphs captured
+ * on it from now on use, and drops the stream's column scratch, which the
+ * next column call on it allocates anew. The replaced buffers stay allocated
+ * until the process exits, so graphs captured earlier keep working and may
+ * run concurrently with graphs captured afterwards. Returns RED_ERR_CAPTURE
+ * (allocating nothing) while the stream is being captured, RED_ERR_ALLOC if
+ * the allocation fails.
+ */
+red_status red_stream_new_workspace(hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 const char *red_status_string(red_status status);

@@ -21,6 +21,53 @@ extern "C" {
  * overlap. */
 red_status red_probe_copy_f32(const float *x, float *y, size_t n, hipStream_t stream);
 
+/*
+ * Launch shape of the load-only read probe: `block` threads per block (64,
+ * 256 or 1024), `blocks_per_cu` blocks per compute unit (1..32), `unroll`
+ * 16-byte loads in flight per lane (4, 8, 16 or 32; with 1024-thread blocks
+ * at most 16, and at most 8 with layout 2), `nontemporal` (0 or 1: the
+ * streaming hint on the loads), `layout` (0 grid-stride, 1 wave tiles of
+ * 64 * unroll vectors, 2 wave tiles with the next tile's loads in flight
+ * while the current one is folded).
+ */
+typedef struct red_read_shape {
+    int block;
+    int blocks_per_cu;
+    int unroll;
+    int nontemporal;
+    int layout;
+} red_read_shape;
+
+/* The read probe's default shape: the fastest found by its launch-shape
+ * sweep on a 1 GiB buffer of this device. */
+void red_default_read_shape(red_read_shape *shape);
+
+/*
+ * Load-only read probe: reads each 16-byte vector of x[0 .. bytes) once with
+ * the given launch shape (NULL = the default) and xors every 32-bit word
+ * into *sink (which the caller sets first; xor is order-free, so the result
+ * is exact whatever the shape). Its time gives how fast this device can
+ * stream a buffer, the measured counterpart of the memory bound of the
+ * simulator page ("simt_lab.py", section 6, estimate_time). x must be
+ * 16-byte aligned and bytes a multiple of 16; an unsupported shape, a NULL
+ * or misaligned pointer, or overlap is RED_ERR_INVALID_ARG.
+ */
+red_status red_probe_read_ceiling(const void *x, size_t bytes, const red_read_shape *shape,
+                                  unsigned int *sink, hipStream_t stream);
+
+/*
+ * Test probe for the poison check of the simulator page ("simt.py", section
+ * 3, shared memory filled with NaN so that unwritten values show): sets every
+ * block-partial slot of the workspace of (current device, stream) -- creating
+ * the workspace first if the stream has none -- and every word of the
+ * stream's column scratch, if it has any, to the 32-bit `word`, with an
+ * ordinary store kernel on `stream`. The completion counter is left alone.
+ * A later call on the stream must overwrite every partial it reads, so its
+ * result does not change. Returns RED_ERR_CAPTURE, enqueuing nothing, while
+ * the stream is being captured.
+ */
+red_status red_probe_fill_workspace(unsigned int word, hipStream_t stream);
+
 /* Reads every 32-bit word of x[0..n) once, with the launch shape and kernel
  * structure of red_sum_f32, and stores their xor at *sink: the reduction's
  * load path with one integer op per element instead of the float64 adds.

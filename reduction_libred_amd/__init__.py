@@ -69,6 +69,14 @@ class ColsPolicy(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class ReadShape(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int), ("blocks_per_cu", ctypes.c_int), ("unroll", ctypes.c_int),
+                ("nontemporal", ctypes.c_int), ("layout", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 _P = ctypes.c_void_p
 _Z = ctypes.c_size_t
 _I = ctypes.c_int
@@ -114,6 +122,10 @@ SIGNATURES = {
     "red_rows_max_f32_with": (_S, [_P, _Z, _Z, _Z, _P, ctypes.POINTER(RowsPolicy), _P]),
     "red_probe_copy_f32": (_S, [_P, _P, _Z, _P]),
     "red_probe_read_f32": (_S, [_P, _Z, _P, _P]),
+    "red_default_read_shape": (None, [ctypes.POINTER(ReadShape)]),
+    "red_probe_read_ceiling": (_S, [_P, _Z, ctypes.POINTER(ReadShape), _P, _P]),
+    "red_probe_fill_workspace": (_S, [ctypes.c_uint, _P]),
+    "red_stream_new_workspace": (_S, [_P]),
     "red_device_info": (_S, [ctypes.POINTER(_I), ctypes.c_char_p, _Z]),
     "red_probe_lds_stride": (_S, [_I, _I, _P, _P]),
     "red_probe_wave_reduce": (_S, [_I, _P, _Z, _P, _P]),
@@ -428,6 +440,54 @@ def red_probe_read_f32(x, sink=None, stream=None):
         st = lib().red_probe_read_f32(x.data_ptr(), x.numel(), sink.data_ptr(), _stream_handle(stream, x.device))
     _check("red_probe_read_f32", st)
     return sink
+
+
+def red_default_read_shape():
+    """The read probe's default launch shape."""
+    p = ReadShape()
+    lib().red_default_read_shape(ctypes.byref(p))
+    return p
+
+
+def red_probe_read_ceiling(x, sink=None, shape=None, stream=None):
+    """Load-only read of a contiguous tensor (16-byte aligned, a multiple of
+    16 bytes) with the given launch shape (a ReadShape, a dict of its fields,
+    or None for the default); sink[0] ^= the xor of all its 32-bit words."""
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or not x.is_contiguous():
+        raise TypeError("red_probe_read_ceiling: x must be a contiguous tensor on a ROCm device")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=x.device)
+    if isinstance(shape, dict):
+        base = red_default_read_shape()
+        for k, v in shape.items():
+            if k not in base.as_dict():
+                raise KeyError(f"unknown read shape field {k!r}")
+            setattr(base, k, int(v))
+        shape = base
+    with torch.cuda.device(x.device):
+        st = lib().red_probe_read_ceiling(x.data_ptr(), x.numel() * x.element_size(),
+                                          ctypes.byref(shape) if shape is not None else None, sink.data_ptr(),
+                                          _stream_handle(stream, x.device))
+    _check("red_probe_read_ceiling", st)
+    return sink
+
+
+def red_probe_fill_workspace(word, stream=None, device=None):
+    """Set every partial slot of the stream's workspace, and its column
+    scratch, to the 32-bit `word` (a test of the poison rule)."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    with torch.cuda.device(device):
+        st = lib().red_probe_fill_workspace(word & 0xFFFFFFFF, _stream_handle(stream, device))
+    _check("red_probe_fill_workspace", st)
+
+
+def red_stream_new_workspace(stream=None, device=None):
+    """Give the stream a fresh workspace (and column scratch), so that graphs
+    captured on it from now on do not share buffers with earlier ones."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    with torch.cuda.device(device):
+        st = lib().red_stream_new_workspace(_stream_handle(stream, device))
+    _check("red_stream_new_workspace", st)
 
 
 def red_probe_lds_stride(stride, iters, sink, stream=None):

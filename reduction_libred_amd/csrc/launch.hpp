@@ -152,6 +152,8 @@ hipError_t launch_sum_f32_partials(const float* x, size_t n, double* partials, i
 
 // Zero `words` 32-bit words at p (used once, when a workspace is created).
 hipError_t launch_zero_words(unsigned int* p, size_t words, hipStream_t stream);
+// Set `words` 32-bit words at p to `value` (test probe: poisons scratch).
+hipError_t launch_fill_words(unsigned int* p, size_t words, unsigned int value, hipStream_t stream);
 
 // Row reductions (rows >= 1, rows starting ld >= cols elements apart).
 hipError_t launch_rows_sum_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
@@ -181,6 +183,21 @@ hipError_t launch_lds_stride(int stride, int iters, unsigned int* sink, hipStrea
 // max over each group of 64 inputs; and one 64-lane shuffle-down.
 hipError_t launch_wave_reduce_probe(int op, const void* in, size_t nwaves, void* out, hipStream_t stream);
 hipError_t launch_shfl_down_probe(const float* in, int offset, float* out, hipStream_t stream);
+
+// Load-only read probe: `block` threads, `blocks_per_cu` blocks per compute
+// unit, `unroll` 16-byte loads in flight per lane, `nontemporal`, `layout`
+// 0 = grid-stride, 1 = wave tiles, 2 = wave tiles with the next tile in
+// flight. *sink ^= the xor of every 32-bit word of x[0 .. 16 * nvec).
+struct ReadShape {
+    int block;
+    int blocks_per_cu;
+    int unroll;
+    int nontemporal;
+    int layout;
+};
+bool read_shape_supported(const ReadShape& s);
+hipError_t launch_read_probe(const void* x, size_t nvec, unsigned int* sink, int grid, const ReadShape& s,
+                             hipStream_t stream);
 
 // Probes: a plain copy y = x with 16-byte accesses and a scalar tail, and
 // the single-value kernel with an xor fold (*out = xor of all words), which

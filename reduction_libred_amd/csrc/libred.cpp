@@ -67,6 +67,9 @@ struct Scratch {
 };
 std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
 std::vector<void*> g_retired_scratch;
+// Workspaces replaced by red_stream_new_workspace: kept, like outgrown
+// scratch, because graphs captured earlier may still use them.
+std::vector<Workspace> g_retired_workspaces;
 constexpr size_t kColsScratchMax = (size_t)64 << 20;
 
 // Default launch shapes, chosen by measurement on MI355X (256 CUs, 8 TB/s):
@@ -159,6 +162,39 @@ red_status refuse_if_capturing(hipStream_t stream) {
     return cs == hipStreamCaptureStatusNone ? RED_OK : RED_ERR_CAPTURE;
 }
 
+// hipMalloc with this thread in relaxed capture mode. Another stream may be
+// being captured in global mode (PyTorch's default) while this call runs on a
+// stream that is not; an allocation is then harmless to that capture, but in
+// global mode the runtime would refuse it and could invalidate the capture.
+// The caller has already checked that its own stream is not capturing.
+hipError_t malloc_outside_capture(void** p, size_t bytes) {
+    hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+    hipError_t e = hipThreadExchangeStreamCaptureMode(&mode);
+    if (e != hipSuccess) return e;
+    e = hipMalloc(p, bytes);
+    hipStreamCaptureMode back = mode;
+    const hipError_t e2 = hipThreadExchangeStreamCaptureMode(&back);
+    return e != hipSuccess ? e : e2;
+}
+
+// A new workspace for (dev, stream), zeroed on the stream; not yet recorded.
+red_status new_workspace(hipStream_t stream, Workspace* ws) {
+    void* p = nullptr;
+    hipError_t e = malloc_outside_capture(&p, kWorkspaceBytes);
+    if (e != hipSuccess || p == nullptr) return fail(e, RED_ERR_ALLOC);
+    // Zeroed by a kernel on the caller's stream, so the counter is 0 before
+    // the first reduction on this stream runs.
+    e = libred::launch_zero_words(static_cast<unsigned int*>(p), kWorkspaceBytes / 4, stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return fail(e, RED_ERR_HIP);
+    }
+    ws->ticket = static_cast<unsigned int*>(p);
+    ws->partials = static_cast<char*>(p) + kTicketBytes;
+    ws->max_partials = kMaxPartials;
+    return RED_OK;
+}
+
 red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
     std::lock_guard<std::mutex> lock(g_mu);
     const auto key = std::make_pair(dev, stream);
@@ -169,20 +205,9 @@ red_status get_workspace(int dev, hipStream_t stream, Workspace* ws) {
     }
     const red_status cap = refuse_if_capturing(stream);
     if (cap != RED_OK) return cap;
-    void* p = nullptr;
-    hipError_t e = hipMalloc(&p, kWorkspaceBytes);
-    if (e != hipSuccess || p == nullptr) return fail(e, RED_ERR_ALLOC);
-    // Zeroed by a kernel on the caller's stream, so the counter is 0 before
-    // the first reduction on this stream runs.
-    e = libred::launch_zero_words(static_cast<unsigned int*>(p), kWorkspaceBytes / 4, stream);
-    if (e != hipSuccess) {
-        (void)hipFree(p);
-        return fail(e, RED_ERR_HIP);
-    }
     Workspace w;
-    w.ticket = static_cast<unsigned int*>(p);
-    w.partials = static_cast<char*>(p) + kTicketBytes;
-    w.max_partials = kMaxPartials;
+    const red_status st = new_workspace(stream, &w);
+    if (st != RED_OK) return st;
     g_workspaces.emplace(key, w);
     *ws = w;
     return RED_OK;
@@ -216,7 +241,7 @@ red_status get_scratch(int dev, hipStream_t stream, size_t bytes, void** out) {
     if (sc.ptr != nullptr && nb < 2 * sc.bytes) nb = 2 * sc.bytes;
     if (nb > kColsScratchMax && bytes <= kColsScratchMax) nb = kColsScratchMax;
     void* p = nullptr;
-    const hipError_t e = hipMalloc(&p, nb);
+    const hipError_t e = malloc_outside_capture(&p, nb);
     if (e != hipSuccess || p == nullptr) return fail(e, RED_ERR_ALLOC);
     if (sc.ptr != nullptr) g_retired_scratch.push_back(sc.ptr);
     sc.ptr = p;
@@ -231,6 +256,9 @@ red_status get_scratch(int dev, hipStream_t stream, size_t bytes, void** out) {
 // 1024 blocks of 256 columns) instead read 4 KiB of a row per wave and
 // 2 rows at a time, without prefetch (256 x 1M: 5.9 -> 7.1 TB/s).
 constexpr libred::ColsPolicy kDefaultCols = {8, 1, 512, 0, 1, 1, 0};
+
+// The read probe's default shape: the fastest of its sweep on a 1 GiB buffer.
+constexpr red_read_shape kDefaultReadShape = {64, 2, 8, 1, 2};
 constexpr libred::ColsPolicy kWideCols = {2, 1, 1024, 0, 4, 0, 0};
 // Columns read one element per lane (rows not 16-byte aligned, or cols or ld
 // not a multiple of 4) with at least 64 of them: two loads per row per lane,
@@ -831,6 +859,35 @@ red_status red_cols_max_f32(const float* x, size_t rows, size_t cols, size_t ld,
     return cols_call(x, rows, cols, ld, out, nullptr, stream, libred::launch_cols_max_f32);
 }
 
+red_status red_stream_new_workspace(hipStream_t stream) {
+    int dev;
+    DeviceInfo info;
+    red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    std::lock_guard<std::mutex> lock(g_mu);
+    st = refuse_if_capturing(stream);
+    if (st != RED_OK) return st;
+    Workspace w;
+    st = new_workspace(stream, &w);
+    if (st != RED_OK) return st;
+    const auto key = std::make_pair(dev, stream);
+    auto it = g_workspaces.find(key);
+    if (it != g_workspaces.end()) {
+        g_retired_workspaces.push_back(it->second);
+        it->second = w;
+    } else {
+        g_workspaces.emplace(key, w);
+    }
+    // The column scratch starts over too: the next column call on the stream
+    // allocates its own (a capture on the stream must warm it up first).
+    auto sc = g_scratch.find(key);
+    if (sc != g_scratch.end()) {
+        if (sc->second.ptr != nullptr) g_retired_scratch.push_back(sc->second.ptr);
+        g_scratch.erase(sc);
+    }
+    return RED_OK;
+}
+
 const char* red_status_string(red_status status) {
     switch (status) {
         case RED_OK: return "RED_OK";
@@ -1055,6 +1112,54 @@ red_status red_probe_copy_f32(const float* x, float* y, size_t n, hipStream_t st
 red_status red_probe_read_f32(const float* x, size_t n, unsigned int* sink, hipStream_t stream) {
     return flat_call(reinterpret_cast<const uint32_t*>(x), n, reinterpret_cast<uint32_t*>(sink), nullptr,
                      stream, libred::launch_xor_u32);
+}
+
+void red_default_read_shape(red_read_shape* s) {
+    if (!s) return;
+    *s = kDefaultReadShape;
+}
+
+red_status red_probe_read_ceiling(const void* x, size_t bytes, const red_read_shape* shape, unsigned int* sink,
+                                  hipStream_t stream) {
+    if (bytes > RED_MAX_N * 4 || bytes % 16 != 0 || (bytes > 0 && x == nullptr) || sink == nullptr)
+        return RED_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(sink, 4) || overlap(x, bytes, sink, 4)) return RED_ERR_INVALID_ARG;
+    const red_read_shape& r = shape ? *shape : kDefaultReadShape;
+    const libred::ReadShape rs = {r.block, r.blocks_per_cu, r.unroll, r.nontemporal, r.layout};
+    if (!libred::read_shape_supported(rs)) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    if (bytes == 0) return RED_OK;
+    const int grid = rs.blocks_per_cu * info.cu_count;
+    const hipError_t e = libred::launch_read_probe(x, bytes / 16, sink, grid, rs, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+red_status red_probe_fill_workspace(unsigned int word, hipStream_t stream) {
+    int dev;
+    DeviceInfo info;
+    red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    Workspace ws;
+    st = get_workspace(dev, stream, &ws);
+    if (st != RED_OK) return st;
+    std::lock_guard<std::mutex> lock(g_mu);
+    st = refuse_if_capturing(stream);
+    if (st != RED_OK) return st;
+    // The partial slots only: the counter line stays zero.
+    hipError_t e = libred::launch_fill_words(static_cast<unsigned int*>(ws.partials),
+                                             kMaxPartials * libred::kMaxPartialBytes / 4, word, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    auto sc = g_scratch.find(std::make_pair(dev, stream));
+    if (sc != g_scratch.end() && sc->second.ptr != nullptr) {
+        e = libred::launch_fill_words(static_cast<unsigned int*>(sc->second.ptr), sc->second.bytes / 4, word,
+                                      stream);
+        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    }
+    return RED_OK;
 }
 
 red_status red_probe_lds_stride(int stride, int iters, unsigned int* sink, hipStream_t stream) {

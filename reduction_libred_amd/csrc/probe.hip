@@ -1,7 +1,8 @@
 // probe.hip -- a plain device copy: the known-size reference that hardware
-// byte counters are scaled by. It takes 16-byte aligned pointers; the caller
-// checks that. (The read-only probe is the single-value kernel with an xor
-// fold; see flat_reduce.hip.)
+// byte counters are scaled by (it takes 16-byte aligned pointers; the caller
+// checks that); the LDS bank probe; the cross-lane primitives alone; and a
+// fill of library scratch with a poison word. (The load-only read probe is
+// in read_probe.hip.)
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -83,6 +84,17 @@ __global__ __launch_bounds__(64) void shfl_down_probe_kernel(const float* __rest
 
 hipError_t launch_shfl_down_probe(const float* in, int offset, float* out, hipStream_t stream) {
     hipLaunchKernelGGL(shfl_down_probe_kernel, dim3(1), dim3(64), 0, stream, in, offset, out);
+    return hipGetLastError();
+}
+
+// p[i] = value for i < words, with ordinary vector stores.
+__global__ void fill_words_kernel(unsigned int* __restrict__ p, size_t words, unsigned int value) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = value;
+}
+
+hipError_t launch_fill_words(unsigned int* p, size_t words, unsigned int value, hipStream_t stream) {
+    hipLaunchKernelGGL(fill_words_kernel, dim3(256), dim3(256), 0, stream, p, words, value);
     return hipGetLastError();
 }
 

@@ -1,0 +1,169 @@
+// read_probe.hip -- a load-only streaming kernel that measures how fast this
+// device reads HBM, the achievable counterpart of the simulator page's memory
+// bound ("simt_lab.py", section 6, estimate_time: time = bytes / bandwidth).
+//
+// Each lane issues 16-byte loads and folds every 32-bit word into one xor
+// (one VALU op per word, far below what the loads take), so the result is
+// checkable and no load can be dropped. The launch shape is free: block
+// size, blocks per compute unit, loads in flight per lane, the non-temporal
+// hint, and the access layout, so that a sweep can find the fastest way this
+// device streams a buffer. Section 7 of the same page (latency_hiding)
+// sizes the bytes in flight that need: bandwidth per CU times latency.
+//
+// Layouts:
+//   0 grid-stride: thread i of the grid reads vectors i, i + G*T, ...
+//     (UNROLL per loop trip), a wave-wide load covering 1 KiB;
+//   1 wave tiles: the buffer is cut into tiles of 64 * UNROLL vectors; wave
+//     w reads tiles w, w + nwaves, ... whole;
+//   2 wave tiles with the next tile's loads issued before the current tile
+//     is folded (two register buffers).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace libred {
+
+namespace {
+
+__device__ __forceinline__ uint32_t xor4(u32x4 v) { return (v.x ^ v.y) ^ (v.z ^ v.w); }
+
+template <int UNROLL, bool NT>
+__device__ __forceinline__ void read_tile(u32x4 (&v)[UNROLL], const u32x4* __restrict__ p) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(p + u * kWave);
+}
+
+template <int UNROLL>
+__device__ __forceinline__ uint32_t fold_tile_xor(const u32x4 (&v)[UNROLL]) {
+    uint32_t a = 0;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) a ^= xor4(v[u]);
+    return a;
+}
+
+template <int BLOCK, int UNROLL, bool NT, int LAYOUT>
+__global__ __launch_bounds__(BLOCK) void read_probe_kernel(const u32x4* __restrict__ xv, size_t nvec,
+                                                           unsigned int* __restrict__ sink) {
+    uint32_t acc = 0;
+    const int lane = threadIdx.x % kWave;
+    if constexpr (LAYOUT == 0) {
+        const size_t stride = (size_t)gridDim.x * BLOCK;
+        size_t i = (size_t)blockIdx.x * BLOCK + threadIdx.x;
+        for (; i + (size_t)(UNROLL - 1) * stride < nvec; i += (size_t)UNROLL * stride) {
+            u32x4 v[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) v[u] = load_vec<NT>(xv + i + (size_t)u * stride);
+            acc ^= fold_tile_xor<UNROLL>(v);
+        }
+        for (; i < nvec; i += stride) acc ^= xor4(load_vec<NT>(xv + i));
+    } else {
+        constexpr int W = BLOCK / kWave;
+        constexpr size_t TILE = (size_t)kWave * UNROLL;
+        const size_t wave = (size_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+        const size_t nwaves = (size_t)gridDim.x * W;
+        const size_t ntiles = nvec / TILE;
+        size_t t = (size_t)blockIdx.x * W + wave;
+        if constexpr (LAYOUT == 1) {
+            for (; t < ntiles; t += nwaves) {
+                u32x4 v[UNROLL];
+                read_tile<UNROLL, NT>(v, xv + t * TILE + lane);
+                acc ^= fold_tile_xor<UNROLL>(v);
+            }
+        } else if (t < ntiles) {
+            u32x4 a[UNROLL], b[UNROLL];
+            read_tile<UNROLL, NT>(a, xv + t * TILE + lane);
+            while (true) {
+                if (t + nwaves >= ntiles) {
+                    acc ^= fold_tile_xor<UNROLL>(a);
+                    break;
+                }
+                read_tile<UNROLL, NT>(b, xv + (t + nwaves) * TILE + lane);
+                acc ^= fold_tile_xor<UNROLL>(a);
+                t += nwaves;
+                if (t + nwaves >= ntiles) {
+                    acc ^= fold_tile_xor<UNROLL>(b);
+                    break;
+                }
+                read_tile<UNROLL, NT>(a, xv + (t + nwaves) * TILE + lane);
+                acc ^= fold_tile_xor<UNROLL>(b);
+                t += nwaves;
+            }
+        }
+        // Vectors after the last whole tile.
+        const size_t w = (size_t)blockIdx.x * W + wave;
+        for (size_t i = ntiles * TILE + w * kWave + lane; i < nvec; i += nwaves * kWave)
+            acc ^= xor4(load_vec<NT>(xv + i));
+    }
+    // Xor across the wave, then one atomic per wave (xor is order-free).
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, off, kWave);
+    if (lane == 0) atomicXor(sink, acc);
+}
+
+// Shapes whose registers fit without spilling: 1024-thread blocks (four
+// waves per SIMD, 128 VGPRs each) take at most 16 loads per lane, 8 with the
+// second register buffer.
+template <int BLOCK, int UNROLL, int LAYOUT>
+constexpr bool rp_fits() {
+    return BLOCK < 1024 || (LAYOUT == 2 ? UNROLL <= 8 : UNROLL <= 16);
+}
+
+template <int BLOCK, int UNROLL, int LAYOUT>
+hipError_t launch_rp(const u32x4* xv, size_t nvec, unsigned int* sink, int grid, bool nt, hipStream_t stream) {
+    if constexpr (!rp_fits<BLOCK, UNROLL, LAYOUT>()) {
+        return hipErrorInvalidValue;
+    } else {
+        if (nt)
+            hipLaunchKernelGGL((read_probe_kernel<BLOCK, UNROLL, true, LAYOUT>), dim3(grid), dim3(BLOCK), 0,
+                               stream, xv, nvec, sink);
+        else
+            hipLaunchKernelGGL((read_probe_kernel<BLOCK, UNROLL, false, LAYOUT>), dim3(grid), dim3(BLOCK), 0,
+                               stream, xv, nvec, sink);
+        return hipGetLastError();
+    }
+}
+
+template <int BLOCK, int LAYOUT>
+hipError_t launch_rp_u(const u32x4* xv, size_t nvec, unsigned int* sink, int grid, const ReadShape& s,
+                       hipStream_t stream) {
+    switch (s.unroll) {
+        case 4: return launch_rp<BLOCK, 4, LAYOUT>(xv, nvec, sink, grid, s.nontemporal != 0, stream);
+        case 8: return launch_rp<BLOCK, 8, LAYOUT>(xv, nvec, sink, grid, s.nontemporal != 0, stream);
+        case 16: return launch_rp<BLOCK, 16, LAYOUT>(xv, nvec, sink, grid, s.nontemporal != 0, stream);
+        case 32: return launch_rp<BLOCK, 32, LAYOUT>(xv, nvec, sink, grid, s.nontemporal != 0, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int BLOCK>
+hipError_t launch_rp_b(const u32x4* xv, size_t nvec, unsigned int* sink, int grid, const ReadShape& s,
+                       hipStream_t stream) {
+    switch (s.layout) {
+        case 0: return launch_rp_u<BLOCK, 0>(xv, nvec, sink, grid, s, stream);
+        case 1: return launch_rp_u<BLOCK, 1>(xv, nvec, sink, grid, s, stream);
+        case 2: return launch_rp_u<BLOCK, 2>(xv, nvec, sink, grid, s, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool read_shape_supported(const ReadShape& s) {
+    const bool block = s.block == 64 || s.block == 256 || s.block == 1024;
+    const bool unroll = s.unroll == 4 || s.unroll == 8 || s.unroll == 16 || s.unroll == 32;
+    const bool fits = s.block < 1024 || (s.layout == 2 ? s.unroll <= 8 : s.unroll <= 16);
+    return block && unroll && fits && s.layout >= 0 && s.layout <= 2 && s.blocks_per_cu >= 1 &&
+           s.blocks_per_cu <= 32 && (s.nontemporal == 0 || s.nontemporal == 1);
+}
+
+hipError_t launch_read_probe(const void* x, size_t nvec, unsigned int* sink, int grid, const ReadShape& s,
+                             hipStream_t stream) {
+    const u32x4* xv = static_cast<const u32x4*>(x);
+    switch (s.block) {
+        case 64: return launch_rp_b<64>(xv, nvec, sink, grid, s, stream);
+        case 256: return launch_rp_b<256>(xv, nvec, sink, grid, s, stream);
+        case 1024: return launch_rp_b<1024>(xv, nvec, sink, grid, s, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace libred

@@ -193,6 +193,26 @@ def test_probe_argument_errors():
     assert L.red_probe_wave_reduce(0, _p(A), 2, _p(A + 8), None) == INVALID   # overlap
     assert L.red_probe_shfl_down_f32(_p(A), 65, _p(B), None) == INVALID
     assert L.red_probe_shfl_down_f32(None, 1, _p(B), None) == INVALID
+    # The load-only read probe: 16-byte aligned, whole vectors, a shape it compiles.
+    sh = rl.red_default_read_shape()
+    assert L.red_probe_read_ceiling(_p(A + 4), 64, ctypes.byref(sh), _p(B), None) == INVALID
+    assert L.red_probe_read_ceiling(_p(A), 60, ctypes.byref(sh), _p(B), None) == INVALID
+    assert L.red_probe_read_ceiling(_p(A), 64, ctypes.byref(sh), None, None) == INVALID
+    assert L.red_probe_read_ceiling(_p(A), 64, None, _p(A + 8), None) == INVALID      # sink inside x
+    for field, value in (("block", 128), ("unroll", 12), ("layout", 3), ("blocks_per_cu", 0),
+                         ("nontemporal", 2)):
+        bad = rl.red_default_read_shape()
+        setattr(bad, field, value)
+        assert L.red_probe_read_ceiling(_p(A), 64, ctypes.byref(bad), _p(B), None) == INVALID, field
+    bad = rl.ReadShape(1024, 1, 32, 1, 0)        # would spill: not compiled
+    assert L.red_probe_read_ceiling(_p(A), 64, ctypes.byref(bad), _p(B), None) == INVALID
+    bad = rl.ReadShape(1024, 1, 16, 1, 2)
+    assert L.red_probe_read_ceiling(_p(A), 64, ctypes.byref(bad), _p(B), None) == INVALID
+
+
+def test_read_shapes_default_is_supported():
+    d = rl.red_default_read_shape().as_dict()
+    assert d["block"] in (64, 256, 1024) and d["unroll"] in (4, 8, 16, 32) and 0 <= d["layout"] <= 2
 
 
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
@@ -204,3 +224,7 @@ def test_no_device():
     assert L.red_rows_max_f32(_p(A), 2, 2, _p(B), None) == NO_DEVICE
     cu = ctypes.c_int()
     assert L.red_device_info(ctypes.byref(cu), None, 0) == NO_DEVICE
+    assert L.red_sum_f32_noalloc(_p(A), 4, _p(B), None) == NO_DEVICE
+    assert L.red_stream_new_workspace(None) == NO_DEVICE
+    assert L.red_probe_fill_workspace(0x7FC00000, None) == NO_DEVICE
+    assert L.red_probe_read_ceiling(_p(A), 64, None, _p(B), None) == NO_DEVICE

@@ -2,7 +2,12 @@
 
 Float sums must lie within |gpu - S| <= 1e-5 * sum|x| + 1e-6 of the oracle's
 float64 compensated sum (per row for the row sums); integer sums and every
-max must match exactly. Inputs are the seeded workloads of workloads.py and
+max must match exactly. The sums the headers promise to accumulate in
+float64 and round once to float32 are also held to that promise:
+|gpu - S| <= 2^-24 * |S| + 1e-12 * sum|x| (one float32 rounding of the
+result, plus float64 rounding along chains of at most a few thousand
+additions: h * 2^-53 < 1e-12 for h < 9000). A float32 accumulator anywhere
+on such a path would break it. Inputs are the seeded workloads of workloads.py and
 deterministic patterns. Views into larger buffers give misaligned heads and
 ragged tails, and the elements just outside each view hold NaN (or +inf for
 max), so reading one element too many changes the answer.
@@ -53,9 +58,31 @@ def gpu_sum(x, **kw):
     return float(out.item())
 
 
+U32 = 2.0 ** -24          # unit roundoff of float32
+F64_CHAIN = 1e-12         # float64 accumulation error per unit of sum|x|
+
+
+def f64_contract_ok(got, S, A):
+    """|got - S| <= 2^-24 |S| + 1e-12 A elementwise (finite S), plus the
+    size of a float32 subnormal step."""
+    got = np.asarray(got, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    return bool(np.all(np.abs(got - S) <= U32 * np.abs(S) + F64_CHAIN * A + 2.0 ** -149))
+
+
+def sums_ok(got, S, A):
+    """Both bars for finite sums accumulated in float64: the 1e-5 acceptance
+    bound and the one-rounding contract."""
+    g = np.asarray(got, dtype=np.float64)
+    return bool(np.all(np.abs(g - S) <= 1e-5 * A + 1e-6)) and f64_contract_ok(g, S, A)
+
+
 def assert_sum_ok(got, a):
     S, A = oracle.sum_f32(a)
     assert oracle.sum_within_tolerance(got, S, A), (got, S, A, a.size)
+    if math.isfinite(S):
+        assert f64_contract_ok(got, S, A), ("float64 contract", got, S, A, a.size)
 
 
 # ----------------------------------------------------------------- f32 sum
@@ -147,6 +174,7 @@ def test_sum_f32_all_policies_agree():
             say(f"sum_f32 n={n} policy {p}")
             got = gpu_sum(x, policy=p)
             assert oracle.sum_within_tolerance(got, S, A), (p, got, S)
+            assert f64_contract_ok(got, S, A), ("float64 contract", p, got, S)
 
 
 def test_sum_f32_partials():
@@ -279,6 +307,11 @@ def assert_fused_ok(got, a):
     assert oracle.max_equal(m, oracle.max_f32(a)), ("max", m)
     SA, _ = oracle.sum_f32(np.abs(a))
     assert oracle.sum_within_tolerance(ab, SA, SA if math.isfinite(SA) else 0.0), ("abs", ab, SA)
+    # Both sums accumulate in float64 and round once.
+    if math.isfinite(S):
+        assert f64_contract_ok(s, S, A), ("sum, float64 contract", s, S, A)
+    if math.isfinite(SA):
+        assert f64_contract_ok(ab, SA, SA), ("sum|x|, float64 contract", ab, SA)
 
 
 @pytest.mark.parametrize("offset", [0, 1, 3])
@@ -429,6 +462,16 @@ def test_min_argext_all_policies():
 
 # ----------------------------------------------------------------- bf16 / f16 / f64 sums
 
+def half_contract_ok(got, S, A, n):
+    """16-bit sums: each 16-byte load's eight values are added in float32 as a
+    balanced tree (three roundings on any path, each within 2^-24 of the
+    magnitudes added; bfloat16 values are scaled by 1/8 first, exactly), the
+    load totals in float64, then one rounding to float32:
+    |got - S| <= 2^-24 |S| + 3 * 2^-24 * A + 1e-12 * A, with a float32
+    subnormal step per load for sums that rounding absolutely."""
+    return abs(float(got) - S) <= U32 * abs(S) + 3.01 * U32 * A + F64_CHAIN * A + (n / 8 + 1) * 2.0 ** -146
+
+
 def _half_bits(a32, dtype):
     t = torch.from_numpy(a32).to(dtype)
     return t.view(torch.int16).numpy().view(np.uint16), t
@@ -450,6 +493,7 @@ def test_sum_half_ragged(dtype):
             torch.cuda.synchronize()
             S, A = ofn(bits)
             assert oracle.sum_within_tolerance(got.item(), S, A), (dtype, n, offset, got.item(), S)
+            assert half_contract_ok(got.item(), S, A, n), ("16-bit contract", dtype, n, offset, got.item(), S)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -500,6 +544,8 @@ def test_sum_f16_vector_fold():
             got = rl.red_sum_f16_f32(buf[offset:offset + n]).item()
             S, A = oracle.sum_f16(bits)
             assert oracle.sum_within_tolerance(got, S, A), (name, offset, got, S, A)
+            if math.isfinite(S):
+                assert half_contract_ok(got, S, A, n), ("16-bit contract", name, offset, got, S, A)
 
 
 def test_sum_bf16_vector_fold():
@@ -533,6 +579,8 @@ def test_sum_bf16_vector_fold():
             got = rl.red_sum_bf16_f32(buf[offset:offset + n]).item()
             S, A = oracle.sum_bf16(bits)
             assert oracle.sum_within_tolerance(got, S, A), (name, offset, got, S, A)
+            if math.isfinite(S):
+                assert half_contract_ok(got, S, A, n), ("16-bit contract", name, offset, got, S, A)
             if name == "subnormal":   # the absolute 1e-6 would hide any error here
                 assert abs(got - S) <= 1e-5 * A, (offset, got, S, A)
 
@@ -590,7 +638,7 @@ def test_rows_random(rows, cols):
             torch.cuda.synchronize()
             assert guard_out[0].item() == 777.0 and guard_out[-1].item() == 777.0
             got = out_s.cpu().numpy().astype(np.float64)
-            assert np.all(np.abs(got - S) <= 1e-5 * A + 1e-6), (rows, cols, p)
+            assert sums_ok(got, S, A), (rows, cols, p)
             out_m = rl.red_rows_max_f32(x, policy=p)
             torch.cuda.synchronize()
             assert np.array_equal(out_m.cpu().numpy(), M), (rows, cols, p)
@@ -630,7 +678,7 @@ def test_rows_staged_any_offset(rows, cols, gap):
             s = rl.red_rows_sum_f32(x, policy=p)
             m = rl.red_rows_max_f32(x, policy=p)
             torch.cuda.synchronize()
-            assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), (offset, p)
+            assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), (offset, p)
             assert np.array_equal(m.cpu().numpy(), M), (offset, p)
 
 
@@ -653,7 +701,7 @@ def test_rows_strided(rows, cols, ld):
             s = rl.red_rows_sum_f32(x, policy=p)
             m = rl.red_rows_max_f32(x, policy=p)
             torch.cuda.synchronize()
-            assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
+            assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), p
             assert np.array_equal(m.cpu().numpy(), M), p
 
 
@@ -674,7 +722,7 @@ def test_rows_split_long_rows(rows, cols):
         s = rl.red_rows_sum_f32(x, policy=p)
         m = rl.red_rows_max_f32(x, policy=p)
         torch.cuda.synchronize()
-        assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
+        assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), p
         assert np.array_equal(m.cpu().numpy(), M), p
 
 
@@ -709,7 +757,7 @@ def test_cols(rows, cols, ld):
             s = rl.red_cols_sum_f32(x, policy=p)
             m = rl.red_cols_max_f32(x, policy=p)
             torch.cuda.synchronize()
-            assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
+            assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), p
             assert np.array_equal(m.cpu().numpy(), M), p
 
 
@@ -732,7 +780,7 @@ def test_cols_line_views(rows, cols):
         s = rl.red_cols_sum_f32(x, policy=p)
         m = rl.red_cols_max_f32(x, policy=p)
         torch.cuda.synchronize()
-        assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), p
+        assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), p
         assert np.array_equal(m.cpu().numpy(), M), p
 
 
@@ -759,7 +807,7 @@ def test_cols_unaligned_views(rows, cols):
             s = rl.red_cols_sum_f32(x, policy=p)
             m = rl.red_cols_max_f32(x, policy=p)
             torch.cuda.synchronize()
-            assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6), (offset, p)
+            assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), (offset, p)
             assert np.array_equal(m.cpu().numpy(), M), (offset, p)
 
 
@@ -868,7 +916,7 @@ def test_rows_policies():
                     s = rl.red_rows_sum_f32(x, policy=p)
                     m = rl.red_rows_max_f32(x, policy=p)
                     torch.cuda.synchronize()
-                    assert np.all(np.abs(s.cpu().numpy() - S) <= 1e-5 * A + 1e-6)
+                    assert sums_ok(s.cpu().numpy(), S, A)
                     assert np.array_equal(m.cpu().numpy(), M)
 
 
@@ -898,7 +946,13 @@ def test_ablation_rungs(rung):
         a = W.make("normal", n, 400 + n % 97)
         out, _ = rl.red_ablate_sum_f32(rung, device_view(a, 1))
         torch.cuda.synchronize()
-        assert_sum_ok(out.item(), a)
+        if rung == 6:
+            assert_sum_ok(out.item(), a)
+        else:
+            # Rungs 1-5 are the lesson's versions: float32 block trees (at most
+            # 9 additions deep), so only the 1e-5 acceptance bound applies.
+            S, A = oracle.sum_f32(a)
+            assert oracle.sum_within_tolerance(out.item(), S, A), (rung, n, out.item(), S)
 
 
 def test_ablation_partials_only():
@@ -1012,7 +1066,7 @@ def test_graph_survives_scratch_growth():
         big_sum = rl.red_cols_sum_f32(big, policy=dict(target_waves=4096, unroll=1))  # grows the scratch
     torch.cuda.synchronize()
     S, A = oracle.cols_sum_f32(big.cpu().numpy())
-    assert np.all(np.abs(big_sum.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
+    assert sums_ok(big_sum.cpu().numpy().astype(np.float64), S, A)
     for k in range(3):
         out.zero_()
         g.replay()
@@ -1190,7 +1244,7 @@ def test_full_rows_65536x4096():
     m = rl.red_rows_max_f32(x)
     torch.cuda.synchronize()
     S, A = oracle.rows_sum_f32(a)
-    assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
+    assert sums_ok(s.cpu().numpy().astype(np.float64), S, A)
     assert np.array_equal(m.cpu().numpy(), oracle.rows_max_f32(a))
     del x
     torch.cuda.empty_cache()
@@ -1198,15 +1252,13 @@ def test_full_rows_65536x4096():
 
 def test_full_rows_short_1gib():
     # The 1 GiB rows workload viewed as (2^28 // cols) x cols rows, the shapes
-    # the widths benchmark times. By default the LDS-staged kernel holds each
-    # wave's row results until its last tile; defer=1 stores them tile by
-    # tile. Each row is reduced the same way in both, so the floats must be
-    # identical, and sampled rows (the first and last 1000 and 2000 drawn at
-    # random) must match the oracle.
+    # the widths benchmark times. Every row of every view is compared with
+    # the oracle. By default the LDS-staged kernel holds each wave's row
+    # results until its last tile; defer=1 stores them tile by tile. Each row
+    # is reduced the same way in both, so the floats must also be identical.
     a, x = _load("rows_f32_65536x4096")
     flat = a.reshape(-1)
-    rng = np.random.default_rng(64)
-    for cols in (16, 64, 100, 256, 1000):
+    for cols in (1, 3, 4, 7, 16, 17, 64, 100, 256, 1000):
         rows = flat.size // cols
         say(f"red_rows_sum_f32 / red_rows_max_f32 rows_f32_65536x4096 as {rows}x{cols}, held and tile by tile")
         v = x.view(-1)[: rows * cols].view(rows, cols)
@@ -1214,13 +1266,11 @@ def test_full_rows_short_1gib():
         s1, m1 = rl.red_rows_sum_f32(v, policy=dict(defer=1)), rl.red_rows_max_f32(v, policy=dict(defer=1))
         torch.cuda.synchronize()
         assert torch.equal(s0, s1) and torch.equal(m0, m1), cols
-        idx = np.unique(np.concatenate([np.arange(1000), np.arange(rows - 1000, rows),
-                                        rng.integers(0, rows, 2000)]))
-        sub = flat[: rows * cols].reshape(rows, cols)[idx]
-        S, A = oracle.rows_sum_f32(sub)
-        got = s0.cpu().numpy()[idx].astype(np.float64)
-        assert np.all(np.abs(got - S) <= 1e-5 * A + 1e-6), cols
-        assert np.array_equal(m0.cpu().numpy()[idx], oracle.rows_max_f32(sub)), cols
+        mat = flat[: rows * cols].reshape(rows, cols)
+        say(f"oracle rows {rows}x{cols}")
+        S, A = oracle.rows_sum_f32(mat)
+        assert sums_ok(s0.cpu().numpy(), S, A), cols
+        assert np.array_equal(m0.cpu().numpy(), oracle.rows_max_f32(mat)), cols
     del x
     torch.cuda.empty_cache()
 
@@ -1232,7 +1282,7 @@ def test_full_cols_65536x4096():
     m = rl.red_cols_max_f32(x)
     torch.cuda.synchronize()
     S, A = oracle.cols_sum_f32(a)
-    assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - S) <= 1e-5 * A + 1e-6)
+    assert sums_ok(s.cpu().numpy().astype(np.float64), S, A)
     assert np.array_equal(m.cpu().numpy(), oracle.cols_max_f32(a))
     del x
     torch.cuda.empty_cache()
