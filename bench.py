@@ -5,7 +5,9 @@ Headline: achieved HBM GB/s of red_sum_f32 over 2^28 float32 elements
 (1 GiB, normal(0,1), seed 2), as a fraction of the 8 TB/s HBM3E peak. One
 step is one red_sum_f32 call over the resident array: the streaming kernel
 (load, peel, wave reduce, LDS combine, block partial) and the one-block
-combine launch. The line also carries the roofline of the streaming kernel
+combine launch. The K timed steps are captured in one HIP graph and
+replayed once between two events; the same calls launched eagerly are timed
+too. The line also carries the roofline of the streaming kernel
 (timed alone through red_sum_f32_partials), the CPU oracle timed on the
 host, and the other entry points at their own workloads.
 
@@ -79,6 +81,10 @@ def parse_args():
     ap.add_argument("--probe-sweep", action="store_true",
                     help="instead of the headline: time the load-only read probe at every launch shape "
                          "on the 2^28-float array and print one JSON line, fastest first")
+    ap.add_argument("--combine-sweep", action="store_true",
+                    help="instead of the headline: time red_sum_f32 with the second-launch and the "
+                         "single-launch (ticket) combine over launch shapes at 2^20, 2^24 and 2^28 elements, "
+                         "eager and inside HIP graphs, against the streaming kernel alone; one JSON line")
     ap.add_argument("--widths", action="store_true",
                     help="instead of the headline: time the row and column entry points on 1 GiB "
                          "of f32 viewed as (2^28 // cols) x cols for a range of widths; print one "
@@ -245,6 +251,56 @@ def run_probe_sweep(args, torch, rl, W, timer, dev):
                       "sum_kernel_GB/s": round(gbps(nbytes + 4, ms), 1), "shapes": results}), flush=True)
 
 
+COMBINE_SHAPES = [(64, 2, 8), (64, 1, 8), (256, 1, 8), (256, 1, 4), (512, 1, 4), (1024, 1, 4), (1024, 1, 8)]
+
+
+def run_combine_sweep(args, torch, rl, W, timer, dev):
+    """Both forms of the final combine: a one-wave second launch (combine 1)
+    and the ticket, where the last block to finish combines (combine 0),
+    which needs an agent-scope release by every block before its counter
+    update."""
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    for n in (1 << 20, 1 << 24, 1 << 28):
+        log(f"generate normal n={n}")
+        x = torch.from_numpy(W.make("normal", n, 2)).to(dev)
+        out = torch.empty((), device=dev)
+        reps = 50 if n >= 1 << 28 else 200
+        for (b, bpc, u) in COMBINE_SHAPES:
+            for comb in (1, 0):
+                pol = dict(block=b, blocks_per_cu=bpc, unroll=u, layout=1, prefetch=1, nontemporal=1, combine=comb)
+                fn = lambda: rl.red_sum_f32(x, out=out, policy=pol)
+                for _ in range(5):
+                    fn()
+                eager = timer.region_ms(fn, reps)
+                cap = torch.cuda.Stream()
+                cap.wait_stream(stream)
+                with torch.cuda.stream(cap):
+                    fn()
+                    torch.cuda.synchronize()
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=cap):
+                        for _ in range(50):
+                            rl.red_sum_f32(x, out=out, policy=pol)
+                torch.cuda.synchronize()
+                g.replay()
+                graph = timer.region_ms(g.replay, 10) / 50
+                parts = rl.red_sum_f32_partials(x, policy=pol)
+                kfn = lambda: rl.red_sum_f32_partials(x, partials=parts, policy=pol)
+                for _ in range(5):
+                    kfn()
+                kern = timer.region_ms(kfn, reps)
+                rows.append(dict(n=n, block=b, blocks_per_cu=bpc, unroll=u, combine=comb,
+                                 grid=rl.red_flat_grid(n, pol), eager_us=round(eager * 1e3, 3),
+                                 graph_us=round(graph * 1e3, 3), kernel_alone_us=round(kern * 1e3, 3)))
+                log(json.dumps(rows[-1]))
+                del g
+        del x
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "combine_sweep", "workload": "normal(0,1) float32, seed 2", "rows": rows}),
+          flush=True)
+
+
 class Timer:
     """HIP events on one stream around a region of `reps` enqueued calls."""
 
@@ -315,6 +371,9 @@ def main():
     if args.probe_sweep:
         run_probe_sweep(args, torch, rl, W, timer, dev)
         return
+    if args.combine_sweep:
+        run_combine_sweep(args, torch, rl, W, timer, dev)
+        return
 
     # ---------------------------------------------------------- headline
     name = "sum_max_f32_2p28"
@@ -336,14 +395,41 @@ def main():
         step()
     torch.cuda.synchronize()
     eager = out.item()
-    log(f"timed {args.steps} steps")
-    ms = timer.region_ms(step, args.steps)
+    log(f"timed {args.steps} eager steps")
+    ms_eager = timer.region_ms(step, args.steps)
     if out.item() != eager:
         raise RuntimeError("red_sum_f32 is not reproducible run to run")
+    log(f"red_sum_f32 eager: {ms_eager * 1e3:.1f} us/step, {gbps(nbytes, ms_eager):.1f} GB/s")
+    # Each eager step bracketed by its own events: median and min.
+    step_med, step_min = timer.per_launch_ms(step, max(20, min(args.steps, 200)))
+
+    # The timed steps: the same K calls captured in one HIP graph (launch
+    # overhead out of the way, as a serving loop would run them), replayed
+    # once between two events. The capture stream gets its workspace from an
+    # eager call first; the replay must give the eager bits.
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(args.steps):
+                step()
+    torch.cuda.synchronize()
+    out.zero_()
+    graph.replay()                              # warm
+    torch.cuda.synchronize()
+    if out.item() != eager:
+        raise RuntimeError("graph replay of red_sum_f32 differs from the eager result")
+    log(f"timed {args.steps} steps in one graph replay")
+    ms = timer.region_ms(graph.replay, 1) / args.steps
+    if out.item() != eager:
+        raise RuntimeError("graph replay of red_sum_f32 differs from the eager result")
     value = gbps(nbytes, ms)
     log(f"red_sum_f32: {ms * 1e3:.1f} us/step, {value:.1f} GB/s ({100 * value / PEAK_GBPS:.1f}% of peak)")
-    # Each step bracketed by its own events: median and min.
-    step_med, step_min = timer.per_launch_ms(step, max(20, min(args.steps, 200)))
+    replays = sorted(timer.region_ms(graph.replay, 1) / args.steps for _ in range(5))
+    del graph
 
     # The dominant kernel alone: steps 1-5 (the streaming pass) without the
     # one-block combine launch, via red_sum_f32_partials, same launch shape.
@@ -400,9 +486,14 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "pct_of_probe": round(100 * value / probe_gbps, 2),
         "elements_per_s": round(n / (ms * 1e-3), 1),
-        "step_us": {"mean": round(ms * 1e3, 3), "median": round(step_med * 1e3, 3),
-                    "min": round(step_min * 1e3, 3), "median_GB/s": round(gbps(nbytes, step_med), 2),
-                    "max_GB/s": round(gbps(nbytes, step_min), 2)},
+        "timing": f"{args.steps} red_sum_f32 calls captured in one HIP graph, one replay between two HIP "
+                  "events on the stream; eager = the same calls launched one by one",
+        "step_us": {"graph_mean": round(ms * 1e3, 3),
+                    "graph_median_of_5_replays": round(replays[2] * 1e3, 3),
+                    "graph_min_of_5_replays": round(replays[0] * 1e3, 3),
+                    "eager_mean": round(ms_eager * 1e3, 3), "eager_median": round(step_med * 1e3, 3),
+                    "eager_min": round(step_min * 1e3, 3), "eager_GB/s": round(gbps(nbytes, ms_eager), 2),
+                    "eager_median_GB/s": round(gbps(nbytes, step_med), 2)},
         "read_ceiling": {"kernel": "read_probe_kernel (load-only, xor of every word)",
                          "shape": rl.red_default_read_shape().as_dict(), "us": round(p_ms * 1e3, 3),
                          "median_us": round(p_med * 1e3, 3), "min_us": round(p_min * 1e3, 3),
@@ -421,6 +512,7 @@ def main():
             "median_launch_us_events": round(med_ms * 1e3, 3),
             "min_launch_us_events": round(min_ms * 1e3, 3),
             "step_us_with_combine_launch": round(ms * 1e3, 3),
+            "step_over_kernel": round(ms / k_ms, 4),
         },
     }
 

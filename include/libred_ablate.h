@@ -86,7 +86,9 @@ typedef struct red_flat_policy {
  * not apply to them, `max_blocks` caps their grid, and an `unroll` of 8 or
  * 16 gives the LDS-staged kernel tiles of that many 16-byte vectors per lane
  * when that is more than the rows need):
- *   0  the library's choice: rows of fewer than 1024 floats go to the
+ *   0  the library's choice: rows of 2 or 4 floats of a contiguous,
+ *      16-byte aligned matrix go to the register kernel (17); other rows of
+ *      fewer than 1024 floats go to the
  *      LDS-staged kernel when they are contiguous or their gaps (ld - cols)
  *      hold at most a quarter of a row, and the matrix spans at least 8
  *      elements (any alignment of x: the first and last vectors of the
@@ -108,12 +110,20 @@ typedef struct red_flat_policy {
  *      16-byte vectors from LDS when the rows hold whole vectors that start
  *      16-byte aligned (cols and ld multiples of 4, x 16-byte aligned; the
  *      default for such rows of at most 64 floats);
+ *   17  the register kernel for rows of 1, 2 or 4 floats of a contiguous,
+ *      16-byte aligned matrix (each lane folds the whole rows of its own
+ *      16-byte vectors; tiles of 8 coalesced loads per lane; the library's
+ *      choice for 2 and 4 floats), else as 0;
  * and `defer` (the LDS-staged kernel): 0 = a wave keeps its row results in
  * LDS and stores them after its last tile when they fit beside its staging
  * tile in its share of the CU's LDS (the CU's LDS over the waves the grid
  * puts on each CU, and at most one block's limit), else stores each tile's
  * results as the tile is reduced; 1 = always as each tile is reduced. The
- * results are the same either way. */
+ * results are the same either way; and `lines` (the LDS-staged kernel, a
+ * contiguous, 16-byte aligned matrix): 0 = the library's choice (1 for rows
+ * of fewer than 32 floats), 1 = tiles of a multiple of 32 rows (whole
+ * 128-byte lines of input and of output when x and out are 128-byte
+ * aligned), 2 = as many rows as fit. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
@@ -124,6 +134,7 @@ typedef struct red_rows_policy {
     int short_rows;
     int cover;
     int defer;
+    int lines;
 } red_rows_policy;
 
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,

@@ -42,6 +42,7 @@ struct RowsPolicy {
     int short_rows;
     int cover;
     int defer;
+    int lines;
 };
 
 // How one row call launches: `grid` blocks of the one-wave-per-row kernel,
@@ -63,7 +64,17 @@ struct RowsLaunch {
                                //   dynamic LDS and stores them after the wave's last tile
     int staged_spread;  // the LDS-staged kernel's element reads start at a different element
                         //   in each row of a pass (rows at a stride of a multiple of 16)
+    int narrow;         // the register kernel for narrow rows (rows_narrow.hip), `grid` waves
 };
+
+// Narrow rows: a contiguous, 16-byte aligned matrix of rows of 1, 2 or 4
+// floats, reduced in registers (op 0 = sum, 1 = max) by `grid` single-wave
+// blocks, tiles of kNarrowTileLoads 16-byte loads per lane.
+// rows_narrow_tile_rows(cols) rows make one tile (0 for another width).
+constexpr int kNarrowTileLoads = 8;
+size_t rows_narrow_tile_rows(size_t cols);
+hipError_t launch_rows_narrow(int op, const float* x, size_t rows, size_t cols, float* out, int grid, bool nt,
+                              hipStream_t stream);
 constexpr size_t kMaxSplitPartials = 32768;
 
 // Library-owned scratch of one (device, stream): a completion counter that

@@ -88,7 +88,7 @@ constexpr FlatPolicy kFlatCached = {1024, 1, 4, 1, libred::kWaveTiles, 1, libred
 constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
 constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
-constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0, 0, 0};
+constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0, 0, 0, 0};
 // Split-row mode: used automatically for fewer than kSplitRowsBelow rows
 // whose rows hold at least kSplitMinCols elements; aims for about
 // kSplitTargetWaves waves in all.
@@ -310,8 +310,8 @@ RowsPolicy default_rows(size_t cols) {
 
 RowsPolicy to_rows(const red_rows_policy* p, size_t cols) {
     if (!p) return default_rows(cols);
-    RowsPolicy r = {p->block,    p->unroll,     p->nontemporal, p->max_blocks, p->split,
-                    p->prefetch, p->short_rows, p->cover,       p->defer};
+    RowsPolicy r = {p->block,      p->unroll, p->nontemporal, p->max_blocks, p->split,
+                    p->prefetch,   p->short_rows, p->cover,   p->defer,      p->lines};
     return r;
 }
 
@@ -367,7 +367,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
 
-    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     // Rows of fewer than 1024 floats go to the LDS-staged kernel (short_rows
     // 0), or do so with 2^(short_rows - 3) lanes per row (short_rows 3-9),
     // when the rows are contiguous or their gaps hold at most a quarter of a
@@ -382,6 +382,23 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // (Strided rows of 512 floats and more stay with the packed or
     // one-wave-per-row kernels: 512 floats at a stride of 516 ran 6% slower
     // staged.)
+    // Rows of 1, 2 or 4 floats of a contiguous, 16-byte aligned matrix: the
+    // register kernel, each lane reducing the whole rows of its 16-byte
+    // vectors and storing its results side by side (short_rows 17).
+    // By default for rows of 2 and 4 floats, on 1024 waves (1 GiB: 2 floats
+    // 5.45 -> 5.77 TB/s of input and output, 4 floats level with the staged
+    // kernel; 1 float, a copy, level or slower).
+    const bool narrow_default = p.short_rows == 0 && (cols == 2 || cols == 4);
+    if (dense && libred::rows_narrow_tile_rows(cols) > 0 && (p.short_rows == 17 || narrow_default)) {
+        const size_t steps = rows / libred::rows_narrow_tile_rows(cols);
+        const size_t cap = pol == nullptr ? (size_t)1024 : (size_t)p.max_blocks;
+        L.narrow = 1;
+        L.grid = (int)(steps == 0 ? 1 : steps < cap ? steps : cap);
+        const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
+        if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+        return RED_OK;
+    }
+    if (p.short_rows == 17) p.short_rows = 0;  // where the register kernel does not apply: the default
     const bool staged_ok = cols > 0 && (dense ? rows * cols >= 4 && fold * cols <= 4096
                                               : span_all >= 8 && (step - cols) * 4 <= cols && cols + 3 <= 4096 &&
                                                     (step == cols || cols < 512));
@@ -428,15 +445,35 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         // Rows per tile: dense, a whole number of aligned spans in 256 * u
         // elements; otherwise as many rows as fit with room for a span that
         // starts 3 elements into its first vector.
+        // Whole-line tiles (lines 1): for a contiguous, 16-byte aligned
+        // matrix, R a multiple of 32, so that a tile's rows span whole 128-byte
+        // lines of input (R * cols floats) and of output (R floats) when x and
+        // out are 128-byte aligned; a line shared by two tiles is otherwise
+        // read, or written in part, by two waves.
+        // By default (lines 0) for contiguous, aligned rows of fewer than 32
+        // floats, whose results are too many to hold to the end of the wave:
+        // 1 GiB, 3 floats 4.7 -> 5.4, 5-15 and 17 floats 5.0-5.4 -> 5.7-5.9,
+        // 24 floats 5.3 -> 5.8 TB/s of input and output (widths 4, 8, 16 and
+        // 32 had whole-line tiles already).
+        const bool whole_lines = dense && (p.lines == 1 || (p.lines == 0 && cols < 32));
         auto tile_rows = [&](size_t u) {
-            return dense ? (256 * u) / (fold * cols) * fold : (256 * u - 3 - cols) / step + 1;
+            if (!dense) return (256 * u - 3 - cols) / step + 1;
+            if (whole_lines && (256 * u) / (32 * cols) >= 1) return (256 * u) / (32 * cols) * 32;
+            return (256 * u) / (fold * cols) * fold;
         };
         auto pass_use = [&](size_t u) {  // share of the passes' row slots that hold a row
             const size_t r = tile_rows(u);
             return r == 0 ? 0.0 : (double)r / (double)(pass * ((r + pass - 1) / pass));
         };
         size_t u = base_u;
-        if (pol == nullptr && vread_default && cols >= 44) {
+        if (pol == nullptr && whole_lines && cols >= 5 && cols < 32 && (cols & (cols - 1)) != 0 &&
+            base_u <= 8) {
+            // Whole-line tiles of rows of 5-31 floats that are not a power of
+            // two: 8 loads per lane on 2048 waves came within 3% of the best
+            // of nine shapes at each width measured (5-15, 17, 24 floats);
+            // 3 floats and the powers of two ran 1-3% faster with 4.
+            u = 8;
+        } else if (pol == nullptr && vread_default && cols >= 44) {
             // Rows of 11-16 whole vectors (measured on 1 GiB, sums): 4096-float
             // tiles on 1024 waves for 44-60 floats (48: 5.9 -> 6.3, 60: 5.4 ->
             // 6.4 TB/s), 2048-float tiles on 1024 waves for 64 floats (6.5 ->
@@ -961,6 +998,7 @@ void red_default_rows_policy(red_rows_policy* p) {
     p->short_rows = kDefaultRows.short_rows;
     p->cover = kDefaultRows.cover;
     p->defer = kDefaultRows.defer;
+    p->lines = kDefaultRows.lines;
 }
 
 size_t red_flat_grid(size_t n, const red_flat_policy* pol) {

@@ -125,7 +125,7 @@ def test_rows_argument_errors():
     for field, value, ok in (("cover", 3, False), ("cover", -1, False), ("cover", 2, True),
                              ("defer", 1, True), ("defer", 2, False), ("defer", -1, False),
                              ("prefetch", 2, False), ("prefetch", 1, True), ("short_rows", 10, True),
-                             ("short_rows", 9, True), ("short_rows", 16, True), ("short_rows", 17, False),
+                             ("short_rows", 9, True), ("short_rows", 16, True), ("short_rows", 17, True), ("short_rows", 18, False),
                              ("split", 3, False)):
         pol = rl.red_default_rows_policy()
         setattr(pol, field, value)

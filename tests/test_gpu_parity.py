@@ -603,7 +603,7 @@ def test_sum_f64():
 
 # ----------------------------------------------------------------- rows
 
-ROW_SHAPES = [(1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
+ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023, 2), (511, 4), (1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
               (5, 64), (6, 65), (257, 4096), (2, 100_003), (4097, 3), (333, 1024), (50, 513),
               (1000, 4), (777, 16), (301, 32), (129, 128), (77, 200), (33, 8), (1025, 12), (70, 512),
               (200, 33), (100, 511), (1000, 100), (3000, 2), (1, 3), (2, 2), (5, 6), (1001, 6),
@@ -617,7 +617,9 @@ ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1,
                 dict(cover=2, short_rows=1), dict(cover=2, unroll=16, max_blocks=3, short_rows=1),
                 dict(cover=2, block=256, unroll=2, short_rows=1), dict(cover=1, short_rows=1, max_blocks=5),
                 dict(short_rows=11), dict(short_rows=14, unroll=16, max_blocks=3), dict(short_rows=16),
-                dict(defer=1), dict(defer=1, short_rows=12, max_blocks=2))
+                dict(defer=1), dict(defer=1, short_rows=12, max_blocks=2),
+                dict(short_rows=17), dict(short_rows=17, max_blocks=3, nontemporal=0),
+                dict(lines=1), dict(lines=1, unroll=16, max_blocks=3), dict(lines=2, unroll=8))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
