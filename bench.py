@@ -251,7 +251,7 @@ def run_probe_sweep(args, torch, rl, W, timer, dev):
                       "sum_kernel_GB/s": round(gbps(nbytes + 4, ms), 1), "shapes": results}), flush=True)
 
 
-COMBINE_SHAPES = [(64, 2, 8), (64, 1, 8), (256, 1, 8), (256, 1, 4), (512, 1, 4), (1024, 1, 4), (1024, 1, 8)]
+COMBINE_SHAPES = [(64, 2, 8), (64, 1, 8), (256, 1, 8), (256, 1, 4), (1024, 1, 4), (1024, 1, 8)]
 
 
 def run_combine_sweep(args, torch, rl, W, timer, dev):

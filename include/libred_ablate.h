@@ -54,8 +54,10 @@ size_t red_ablate_num_partials(int rung, size_t n);
  *                  the current tile
  *   combine        0: the last block to finish combines the partials in the
  *                  same launch; 1: a second one-block launch combines them
- * Compiled shapes: layout 0 with block 256/512/1024 and unroll 1/2/4/8/16
- * (prefetch 0); layout 1 with block 64/256/512/1024 and unroll 4/8/16.
+ * Compiled shapes: layout 0 with block 256/1024 and unroll 1/4/8
+ * (prefetch 0); layout 1 with block 64/256/1024 and unroll 4/8/16 (every
+ * default shape, and a small set around them). Others are
+ * RED_ERR_INVALID_ARG.
  */
 typedef struct red_flat_policy {
     int block;
@@ -83,9 +85,10 @@ typedef struct red_flat_policy {
  * reads rows through their covers and keeps the next tile of 64*unroll
  * vectors in flight while folding the current one, across row boundaries;
  * and `short_rows`, the kernels for short rows (`block` and `prefetch` do
- * not apply to them, `max_blocks` caps their grid, and an `unroll` of 8 or
- * 16 gives the LDS-staged kernel tiles of that many 16-byte vectors per lane
- * when that is more than the rows need):
+ * not apply to them, `max_blocks` caps their grid, an `unroll` of 8 or 16
+ * gives the LDS-staged kernel tiles of that many 16-byte vectors per lane
+ * when that is more than the rows need, and the LDS-staged kernel always
+ * loads non-temporally, whatever `nontemporal` says):
  *   0  the library's choice: rows of 2 or 4 floats of a contiguous,
  *      16-byte aligned matrix go to the register kernel (17); other rows of
  *      fewer than 1024 floats go to the

@@ -30,7 +30,7 @@ LIB = os.path.join(HERE, "libred.so")
 MANIFEST = os.path.join(HERE, "libred_objects.json")
 
 SOURCES = ["libred.cpp", "flat_sum_f32.hip", "flat_ops.hip", "flat_fused.hip", "flat_argmax.hip", "flat_argmin.hip",
-           "flat_wide.hip", "rows_reduce.hip", "cols_reduce.hip", "ablate.hip", "probe.hip", "read_probe.hip", "rows_narrow.hip"]
+           "flat_wide.hip", "rows_sum.hip", "rows_max.hip", "cols_reduce.hip", "ablate.hip", "probe.hip", "read_probe.hip", "rows_narrow.hip"]
 ARCH = "gfx950"
 
 

@@ -252,9 +252,10 @@ __global__ __launch_bounds__(kCombineBlock) void combine_partials_kernel(
 
 // ---------------------------------------------------------------------------
 // Policy dispatch: the (layout, block, unroll, nontemporal, prefetch) shapes
-// compiled in.
-//   grid-stride: block 256 / 512 / 1024, unroll 1 / 2 / 4 / 8 / 16
-//   wave tiles:  block 64 / 256 / 512 / 1024, unroll 4 / 8 / 16, prefetch 0 / 1
+// compiled in: the default shapes and a small set around them for the
+// launch-shape comparisons.
+//   grid-stride: block 256 / 1024, unroll 1 / 4 / 8
+//   wave tiles:  block 64 / 256 / 1024, unroll 4 / 8 / 16, prefetch 0 / 1
 // ---------------------------------------------------------------------------
 template <class Op, int BLOCK, int UNROLL, int LAYOUT, bool PREFETCH>
 inline hipError_t launch_shape(const typename Op::elem_t* x, size_t n, typename Op::out_t* out,
@@ -280,10 +281,8 @@ inline hipError_t launch_grid_stride(const typename Op::elem_t* x, size_t n, typ
                                      hipStream_t stream) {
     switch (p.unroll) {
         case 1: return launch_shape<Op, BLOCK, 1, kGridStride, false>(x, n, out, grid, p, ws, stream);
-        case 2: return launch_shape<Op, BLOCK, 2, kGridStride, false>(x, n, out, grid, p, ws, stream);
         case 4: return launch_shape<Op, BLOCK, 4, kGridStride, false>(x, n, out, grid, p, ws, stream);
         case 8: return launch_shape<Op, BLOCK, 8, kGridStride, false>(x, n, out, grid, p, ws, stream);
-        case 16: return launch_shape<Op, BLOCK, 16, kGridStride, false>(x, n, out, grid, p, ws, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -312,7 +311,6 @@ inline hipError_t launch_op(const typename Op::elem_t* x, size_t n, typename Op:
     if (p.layout == kGridStride) {
         switch (p.block) {
             case 256: return launch_grid_stride<Op, 256>(x, n, out, grid, p, ws, stream);
-            case 512: return launch_grid_stride<Op, 512>(x, n, out, grid, p, ws, stream);
             case 1024: return launch_grid_stride<Op, 1024>(x, n, out, grid, p, ws, stream);
             default: return hipErrorInvalidValue;
         }
@@ -320,7 +318,6 @@ inline hipError_t launch_op(const typename Op::elem_t* x, size_t n, typename Op:
     switch (p.block) {
         case 64: return launch_tiles<Op, 64>(x, n, out, grid, p, ws, stream);
         case 256: return launch_tiles<Op, 256>(x, n, out, grid, p, ws, stream);
-        case 512: return launch_tiles<Op, 512>(x, n, out, grid, p, ws, stream);
         case 1024: return launch_tiles<Op, 1024>(x, n, out, grid, p, ws, stream);
         default: return hipErrorInvalidValue;
     }

@@ -20,12 +20,12 @@ bool flat_policy_supported(const FlatPolicy& p) {
     if (p.blocks_per_cu < 1 || (p.nontemporal != 0 && p.nontemporal != 1)) return false;
     if (p.combine != (int)kCombineTicket && p.combine != (int)kCombineTwoPass) return false;
     if (p.layout == kGridStride) {
-        const bool b = p.block == 256 || p.block == 512 || p.block == 1024;
-        const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
+        const bool b = p.block == 256 || p.block == 1024;
+        const bool u = p.unroll == 1 || p.unroll == 4 || p.unroll == 8;
         return b && u && p.prefetch == 0;
     }
     if (p.layout == kWaveTiles) {
-        const bool b = p.block == 64 || p.block == 256 || p.block == 512 || p.block == 1024;
+        const bool b = p.block == 64 || p.block == 256 || p.block == 1024;
         const bool u = p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
         return b && u && (p.prefetch == 0 || p.prefetch == 1);
     }

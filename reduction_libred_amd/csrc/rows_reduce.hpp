@@ -1,6 +1,7 @@
-// rows_reduce.hip -- per-row (segmented) sum and max of a row-major matrix
+// rows_reduce.hpp -- per-row (segmented) sum and max of a row-major matrix
 // whose rows start `ld` elements apart (ld >= cols; ld == cols is the dense
-// case).
+// case), as templates over the operator; rows_sum.hip and rows_max.hip
+// instantiate them for the sum and the max, so the two compile in parallel.
 //
 // The lesson's reduction gives one output per block segment
 // ("03_shared_memory_sync_reduction.py", demo 3). Here the segment is a row,
@@ -25,6 +26,8 @@
 // rows_reduce_kernel and the split kernel peel an unaligned row's head and
 // tail element by element (none when aligned). Sums accumulate in float64
 // and round once per row.
+#pragma once
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -716,16 +719,8 @@ __global__ __launch_bounds__(kRowsCombineBlock) void rows_combine_kernel(
     if (lane == 0) out[r] = Op::finish(v);
 }
 
-bool rows_policy_supported(const RowsPolicy& p) {
-    const bool b = p.block == 64 || p.block == 128 || p.block == 256 || p.block == 512;
-    const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
-    return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.max_blocks >= 1 && p.split >= 0 &&
-           p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.cover >= 0 && p.cover <= 2 && p.short_rows >= 0 && p.short_rows <= 17 &&
-           (p.defer == 0 || p.defer == 1) && p.lines >= 0 && p.lines <= 2;
-}
-
 template <class Op, int BLOCK, int UNROLL>
-static hipError_t rows_bu(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+inline hipError_t rows_bu(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, int grid, bool nt, bool pf, bool cover, hipStream_t stream) {
     if (cover && !pf) {
         if (nt)
@@ -758,7 +753,7 @@ static hipError_t rows_bu(const typename Op::elem_t* x, size_t rows, size_t cols
 }
 
 template <class Op, int BLOCK>
-static hipError_t rows_b(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+inline hipError_t rows_b(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                          typename Op::out_t* out, int grid, bool cover, const RowsPolicy& p, hipStream_t stream) {
     const bool nt = p.nontemporal != 0;
     const bool pf = p.prefetch != 0;
@@ -773,7 +768,7 @@ static hipError_t rows_b(const typename Op::elem_t* x, size_t rows, size_t cols,
 }
 
 template <class Op, int UNROLL>
-static hipError_t rows_split_u(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+inline hipError_t rows_split_u(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                                typename Op::out_t* out, unsigned int gx, bool nt, void* ws_partials,
                                hipStream_t stream) {
     auto* partials = static_cast<typename Op::acc_t*>(ws_partials);
@@ -793,7 +788,7 @@ static hipError_t rows_split_u(const typename Op::elem_t* x, size_t rows, size_t
 }
 
 template <class Op, int LOG2L, int V, bool SCALAR>
-static hipError_t rows_packed_lv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+inline hipError_t rows_packed_lv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                                  typename Op::out_t* out, int grid, bool nt, hipStream_t stream) {
     if (nt)
         hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, SCALAR, true>), dim3(grid), dim3(kWave), 0, stream,
@@ -807,7 +802,7 @@ static hipError_t rows_packed_lv(const typename Op::elem_t* x, size_t rows, size
 // Several units per lane only with the widest segment (16 lanes for vectors,
 // 64 for elements); narrower segments always take one.
 template <class Op, int LOG2L, bool SCALAR>
-static hipError_t rows_packed_v(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+inline hipError_t rows_packed_v(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                                 typename Op::out_t* out, const RowsLaunch& L, bool nt, hipStream_t stream) {
     if constexpr (LOG2L == (SCALAR ? 6 : 4)) {
         switch (L.packed_v) {
@@ -824,7 +819,7 @@ static hipError_t rows_packed_v(const typename Op::elem_t* x, size_t rows, size_
 }
 
 template <class Op, bool SCALAR>
-static hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+inline hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                                 typename Op::out_t* out, const RowsLaunch& L, bool nt, hipStream_t stream) {
     switch (L.packed_log2l) {
         case 0: return rows_packed_v<Op, 0, SCALAR>(x, rows, cols, ld, out, L, nt, stream);
@@ -842,33 +837,27 @@ static hipError_t rows_packed_s(const typename Op::elem_t* x, size_t rows, size_
 }
 
 template <class Op, int LOG2S, int U, bool VREAD, bool SPREAD>
-static hipError_t rows_staged_go(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
+inline hipError_t rows_staged_go(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                                  const RowsLaunch& L, bool nt, hipStream_t stream) {
     const size_t held_bytes = (size_t)L.staged_hold * sizeof(typename Op::out_t);
     // x's offset, in elements, from the 16-byte boundary before it.
     const unsigned int sh = (unsigned int)(((uintptr_t)x % 16) / sizeof(typename Op::elem_t));
-    if (L.staged_hold > 0) {
-        if (nt)
-            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true, SPREAD>), dim3(L.grid),
-                               dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
-        else
-            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, true, SPREAD>), dim3(L.grid),
-                               dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
-    } else {
-        if (nt)
-            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, false, SPREAD>), dim3(L.grid),
-                               dim3(kWave), 0, stream, x, rows, cols, ld, sh, L.staged_rows, out);
-        else
-            hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, false, VREAD, false, SPREAD>), dim3(L.grid),
-                               dim3(kWave), 0, stream, x, rows, cols, ld, sh, L.staged_rows, out);
-    }
+    // The staged tiles are always loaded non-temporally (the default of every
+    // row shape): built only that way, which halves this kernel's variants.
+    (void)nt;
+    if (L.staged_hold > 0)
+        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true, SPREAD>), dim3(L.grid),
+                           dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
+    else
+        hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, false, SPREAD>), dim3(L.grid),
+                           dim3(kWave), 0, stream, x, rows, cols, ld, sh, L.staged_rows, out);
     return hipGetLastError();
 }
 
 // Spread element reads are built only where the host asks for them: one or
 // two lanes per row (32 or more rows per pass).
 template <class Op, int LOG2S, int U, bool VREAD>
-static hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
+inline hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                                   const RowsLaunch& L, bool nt, hipStream_t stream) {
     if constexpr (!VREAD && LOG2S <= 1) {
         if (L.staged_spread) return rows_staged_go<Op, LOG2S, U, false, true>(x, rows, cols, ld, out, L, nt, stream);
@@ -879,14 +868,14 @@ static hipError_t rows_staged_suv(const typename Op::elem_t* x, size_t rows, siz
 }
 
 template <class Op, int LOG2S, int U>
-static hipError_t rows_staged_su(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
+inline hipError_t rows_staged_su(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                                  const RowsLaunch& L, bool nt, hipStream_t stream) {
     if (L.staged_vread) return rows_staged_suv<Op, LOG2S, U, true>(x, rows, cols, ld, out, L, nt, stream);
     return rows_staged_suv<Op, LOG2S, U, false>(x, rows, cols, ld, out, L, nt, stream);
 }
 
 template <class Op, int LOG2S>
-static hipError_t rows_staged_s(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
+inline hipError_t rows_staged_s(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                                 const RowsLaunch& L, bool nt, hipStream_t stream) {
     switch (L.staged_u) {
         case 4: return rows_staged_su<Op, LOG2S, 4>(x, rows, cols, ld, out, L, nt, stream);
@@ -897,7 +886,7 @@ static hipError_t rows_staged_s(const typename Op::elem_t* x, size_t rows, size_
 }
 
 template <class Op>
-static hipError_t rows_staged(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
+inline hipError_t rows_staged(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld, typename Op::out_t* out,
                               const RowsLaunch& L, bool nt, hipStream_t stream) {
     switch (L.staged_log2s) {
         case 0: return rows_staged_s<Op, 0>(x, rows, cols, ld, out, L, nt, stream);
@@ -912,7 +901,7 @@ static hipError_t rows_staged(const typename Op::elem_t* x, size_t rows, size_t 
 }
 
 template <class Op>
-static hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
+inline hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, const RowsLaunch& L, const RowsPolicy& p,
                           hipStream_t stream) {
     if (L.staged_u > 0) return rows_staged<Op>(x, rows, cols, ld, out, L, p.nontemporal != 0, stream);
@@ -938,18 +927,6 @@ static hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols
         case 512: return rows_b<Op, 512>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
         default: return hipErrorInvalidValue;
     }
-}
-
-hipError_t launch_rows_sum_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
-                               const RowsLaunch& L, const RowsPolicy& p, hipStream_t stream) {
-    if (L.narrow) return launch_rows_narrow(0, x, rows, cols, out, L.grid, p.nontemporal != 0, stream);
-    return rows_op<SumF32>(x, rows, cols, ld, out, L, p, stream);
-}
-
-hipError_t launch_rows_max_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
-                               const RowsLaunch& L, const RowsPolicy& p, hipStream_t stream) {
-    if (L.narrow) return launch_rows_narrow(1, x, rows, cols, out, L.grid, p.nontemporal != 0, stream);
-    return rows_op<MaxF32>(x, rows, cols, ld, out, L, p, stream);
 }
 
 }  // namespace libred

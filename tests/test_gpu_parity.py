@@ -152,11 +152,11 @@ def all_flat_policies(bpcs=(1, 4)):
     for bpc in bpcs:
         for nt in (0, 1):
             for combine in (0, 1):
-                for block in (256, 512, 1024):
-                    for unroll in (1, 2, 4, 8, 16):
+                for block in (256, 1024):
+                    for unroll in (1, 4, 8):
                         shapes.append(dict(block=block, blocks_per_cu=bpc, unroll=unroll, nontemporal=nt,
                                            layout=0, prefetch=0, combine=combine))
-                for block in (64, 256, 512, 1024):
+                for block in (64, 256, 1024):
                     for unroll in (4, 8, 16):
                         for pf in (0, 1):
                             shapes.append(dict(block=block, blocks_per_cu=bpc, unroll=unroll,

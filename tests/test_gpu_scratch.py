@@ -52,7 +52,7 @@ def _sum_ok(got, S, A):
 
 
 FLAT_SHAPES = (None, dict(combine=0), dict(block=256, blocks_per_cu=4, unroll=4, combine=1),
-               dict(layout=0, block=1024, blocks_per_cu=1, unroll=2, prefetch=0, combine=0))
+               dict(layout=0, block=1024, blocks_per_cu=1, unroll=4, prefetch=0, combine=0))
 
 
 def test_poisoned_workspace_single_value_calls():
