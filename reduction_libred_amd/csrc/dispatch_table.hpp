@@ -1,0 +1,156 @@
+// dispatch_table.hpp -- every width-keyed threshold that the row and column
+// entry points choose kernels, tiles and grids by, in one table, each with
+// the measurement that chose it (the default launch-shape structs stay next
+// to the code in libred.cpp). Host code only (included by libred.cpp).
+//
+// Unless an entry says otherwise, a figure is from one MI355X on 1 GiB of
+// float32 (the 65536 x 4096 uniform[0,1) workload viewed as a contiguous
+// (2^28 / cols) x cols matrix), in TB/s of input bytes, with HIP events over
+// 20-50 calls; "widths" means `bench.py --widths` (the kernels and per-width
+// times of profiles/rows_cols_widths_1gib.md), and "sweep" a launch-shape
+// sweep over the named widths run with the `_with` entry points. A change to
+// an entry is a change of measured behaviour and should come with a new
+// measurement.
+#pragma once
+
+#include <stddef.h>
+
+namespace libred {
+namespace table {
+
+// ------------------------------------------------------------ rows: choice
+// Rows of 1024 floats and more go to a one-wave-per-row kernel; shorter ones
+// to the LDS-staged kernel (widths: 1000 floats staged 6.5, one wave per row
+// 4.8 TB/s).
+constexpr size_t kStagedBelowCols = 1024;
+// A staged tile holds at most this many floats (16 loads of 16 bytes per
+// lane); contiguous rows whose aligned span does not fit go elsewhere.
+constexpr size_t kStagedMaxTileFloats = 4096;
+// Strided rows stay staged only under this width (512 floats at a stride of
+// 516 ran 6% slower staged than with the packed kernel).
+constexpr size_t kStagedStridedBelowCols = 512;
+// Strided or unaligned rows up to this width go to the packed kernel (a
+// segment of lanes per row) when the staged kernel does not apply.
+constexpr size_t kPackedMaxCols = 512;
+
+// ------------------------------------------------------------ rows: register kernel
+// Rows of 2 and 4 floats of a contiguous, 16-byte aligned matrix take the
+// register kernel on 1024 waves (2 floats 5.45 -> 5.77 TB/s of input plus
+// output, 4 floats level; 1 float, a copy, level or slower: kept staged).
+constexpr int kNarrowWaves = 1024;
+
+// ------------------------------------------------------------ rows: staged tile
+// Tile sizes by the floats a tile's rows span: up to 1024 -> 4 loads per
+// lane, up to 2048 -> 8, else 16 (a tile must hold at least one aligned
+// span of rows).
+constexpr size_t kTileFloats4 = 1024;
+constexpr size_t kTileFloats8 = 2048;
+// Whole-line tiles (R a multiple of 32 rows) by default under this width:
+// 3 floats 4.7 -> 5.4, 5-15 and 17 floats 5.0-5.4 -> 5.7-5.9, 24 floats
+// 5.3 -> 5.8 TB/s of input plus output (rows sweep, lines 1 against 2).
+constexpr size_t kWholeLinesBelowCols = 32;
+// ... and non-power-of-two widths from this one up take 8 loads per lane:
+// within 3% of the best of nine shapes at 5-15, 17 and 24 floats; 3 floats
+// and the powers of two ran 1-3% faster with 4.
+constexpr size_t kWholeLinesWideTileFromCols = 5;
+// Rows of whole vectors up to this width read 16-byte vectors from LDS
+// (bank conflicts with element reads: 18.7 against 2.0-5.2 cycles per LDS
+// instruction at 16 and 64 floats, profiles/rows_staged_lds_counters.md).
+constexpr size_t kVectorReadMaxCols = 64;
+// Vector-read rows from this width take 4096-float tiles on 1024 waves, and
+// 64 floats 2048-float tiles (48: 5.9 -> 6.3, 60: 5.4 -> 6.4, 64: 6.5 -> 6.8).
+constexpr size_t kVectorReadBigTileFromCols = 44;
+// Element-read rows from 32 to 512 floats take the largest tile whose passes
+// are within this share as full as the fullest tile's (over 54 widths of
+// 33-512 floats: 97.3% of the best of four shapes on geometric mean).
+constexpr size_t kElementTileRuleMinCols = 32;
+constexpr size_t kElementTileRuleMaxCols = 512;
+constexpr double kPassUseSlack = 0.02;
+// Rows of 33-39 floats: 2048-float tiles on 1024 waves when 4096-float tiles
+// leave no room to hold the results and their passes are within this share
+// as full (sums 5.5 -> 5.5-6.4, maxima 5.5-5.6 -> 5.7-6.0; at 41-43 floats
+// the maxima ran 8% slower, so the rule stops below 40).
+constexpr size_t kHoldSmallTileBelowCols = 40;
+constexpr double kHoldSmallTileSlack = 0.05;
+// Waves of the staged kernel: 1024 with 4096-float tiles, else 2048.
+constexpr int kStagedBigTileWaves = 1024;
+constexpr int kStagedWaves = 2048;
+// Lanes per row, element reads: the largest power of two up to cols / 8
+// below 32 floats, cols / 16 for whole-vector rows from 128 floats, else
+// cols / 24 (a sweep of lanes per row: 8-16 elements per lane best); rows
+// over 512 floats take the whole wave.
+constexpr size_t kLanesDivNarrow = 8;
+constexpr size_t kLanesDivWholeVec = 16;
+constexpr size_t kLanesDivOther = 24;
+constexpr size_t kLanesNarrowBelowCols = 32;
+constexpr size_t kLanesWholeVecFromCols = 128;
+constexpr size_t kWholeWaveAboveCols = 512;
+// Results held in LDS to the end of the wave under this width (with one or
+// two rows per tile, at 960-1020 floats, holding measured 1-10% slower).
+constexpr size_t kHoldBelowCols = 960;
+
+// ------------------------------------------------------------ rows: one wave per row
+// Rows of at least this many floats take 16 loads per lane on 512 waves
+// (sweep over 1024, 4096, 16384 and 65536 floats).
+constexpr size_t kRowsLongFromCols = 16384;
+constexpr int kRowsLongUnroll = 16;
+constexpr int kRowsLongWaves = 512;
+// Rows under this width take a tile no longer than the row on 2048 waves.
+constexpr size_t kRowsShortBelowCols = 2048;
+constexpr int kRowsShortWaves = 2048;
+// Rows of 1 to 1.75 tiles of 8 loads per lane (a second tile at most this
+// many vectors full) take 4-load tiles on 2048 waves (2052: 4.9 -> 6.4,
+// 2560: 5.6 -> 7.1, 3072: 6.2 -> 6.9 TB/s; a 95% full second tile: 3%
+// slower).
+constexpr size_t kPartialTileMaxVectors = 384;
+// Rows read through their aligned covers: 8 loads per lane on up to 32768
+// waves below 16384 floats (2049: 5.8 -> 6.8, 2500: 5.5 -> 6.6 TB/s),
+// 1024 waves from there (50257 floats: 6% slower on more).
+constexpr int kCoverUnroll = 8;
+constexpr int kCoverWavesBelowLong = 32768;
+constexpr int kCoverWavesLong = 1024;
+
+// ------------------------------------------------------------ rows: split
+// Fewer than kSplitRowsBelow rows of at least kSplitMinCols floats are cut
+// across blocks, about kSplitTargetWaves waves in all (2 x 2^27: one wave
+// per row 27 GB/s, split 7.0 TB/s).
+constexpr size_t kSplitRowsBelow = 1024;
+constexpr size_t kSplitMinCols = 8192;
+constexpr size_t kSplitTargetWaves = 1024;
+
+// ------------------------------------------------------------ columns: folded views
+// A width of at least this many columns that is not a multiple of 32 reads
+// through views of 32 rows (whole 128-byte lines) when that leaves at least
+// kFold32MinViewRows view rows (odd widths 257-4097: 7-17% faster than 16
+// rows; 1025: 5.8 -> 6.4, 2049: 5.9 -> 6.9 TB/s).
+constexpr size_t kFoldWideFromCols = 256;
+constexpr size_t kFold32MinViewRows = 1024;
+// Other widths of at least kFoldWideFromCols that are not a multiple of 4:
+// 16-row views (1023-65537 columns: 3-24% faster than 4 rows).
+constexpr size_t kFold16Rows = 16;
+// Widths from 32 to 255: view rows of about kFoldViewFloats floats (512
+// groups of four columns), at most kFoldMaxRows rows (33: 5.6 -> 6.7, 65:
+// 5.5 -> 6.8 TB/s), unless a multiple of 4 already uses this share of the
+// lanes.
+constexpr size_t kFoldMidFromCols = 32;
+constexpr size_t kFoldViewFloats = 2048;
+constexpr size_t kFoldMaxRows = 64;
+constexpr double kFoldMidLaneUse = 0.95;
+// Under 32 columns: the smallest line-spanning view keeping this share of
+// the lanes busy (23: 5.7 -> 6.3, 28: 6.1 -> 6.5, 31: 6.1 -> 6.8 TB/s),
+// unless the best view up to 16 rows already keeps kFoldNarrowEnough.
+constexpr double kFoldNarrowLaneUse = 0.84;
+constexpr double kFoldNarrowEnough = 0.99;
+// A multiple of 4 is folded only when that uses this much more of the lanes
+// (260 columns: 4.0 -> 6.4 TB/s folded 16 rows).
+constexpr double kFoldGain = 0.05;
+
+// ------------------------------------------------------------ columns: shapes
+// Short-wide matrices (more than this many blocks of 256 columns), and rows
+// of at least kFoldWideFromCols columns that are not whole lines (unfolded),
+// take the wide shape (256 x 1M: 5.9 -> 7.1 TB/s; 1020, 1500, 3000, 6000
+// columns 8-12% faster).
+constexpr size_t kWideColBlocks = 1024;
+
+}  // namespace table
+}  // namespace libred

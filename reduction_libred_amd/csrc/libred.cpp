@@ -11,6 +11,7 @@
 #include <utility>
 #include <vector>
 
+#include "dispatch_table.hpp"
 #include "launch.hpp"
 #include "libred.h"
 #include "libred_ablate.h"
@@ -89,12 +90,9 @@ constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::k
 constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
 constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
 constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0, 0, 0, 0};
-// Split-row mode: used automatically for fewer than kSplitRowsBelow rows
-// whose rows hold at least kSplitMinCols elements; aims for about
-// kSplitTargetWaves waves in all.
-constexpr size_t kSplitRowsBelow = 1024;
-constexpr size_t kSplitMinCols = 8192;
-constexpr size_t kSplitTargetWaves = 1024;
+using libred::table::kSplitMinCols;
+using libred::table::kSplitRowsBelow;
+using libred::table::kSplitTargetWaves;
 
 // The fused sum/max/sum-of-magnitudes pass folds three accumulators per
 // element (two of them float64) and keeps four waves per CU on large arrays:
@@ -290,20 +288,21 @@ FlatPolicy to_flat(const red_flat_policy* p, size_t n, bool fused = false) {
 RowsPolicy default_rows(size_t cols) {
     RowsPolicy p = kDefaultRows;
     const size_t nvec = cols / 4;
-    if (nvec >= 4096) {
-        p.unroll = 16;
-        p.max_blocks = 512;
-    } else if (nvec < 512) {
+    namespace T = libred::table;
+    if (cols >= T::kRowsLongFromCols) {
+        p.unroll = T::kRowsLongUnroll;
+        p.max_blocks = T::kRowsLongWaves;
+    } else if (cols < T::kRowsShortBelowCols) {
         const size_t u = nvec / 64;
         p.unroll = u >= 4 ? 4 : (u >= 2 ? 2 : 1);
-        p.max_blocks = 2048;
-    } else if (nvec < 1024 && nvec % 512 != 0 && nvec % 512 <= 384) {
+        p.max_blocks = T::kRowsShortWaves;
+    } else if (nvec < 1024 && nvec % 512 != 0 && nvec % 512 <= T::kPartialTileMaxVectors) {
         // Rows of 1-1.75 tiles of 8 loads per lane: the partial tile costs a
         // round trip of its own, better hidden by 4-load tiles on 2048 waves
         // (2052: 4.9 -> 6.4, 2560: 5.6 -> 7.1, 3072: 6.2 -> 6.9, 3584: 6.7 ->
         // 7.0 TB/s; at 4000 floats, a 95% full second tile, 3% slower).
         p.unroll = 4;
-        p.max_blocks = 2048;
+        p.max_blocks = T::kRowsShortWaves;
     }
     return p;
 }
@@ -366,6 +365,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     DeviceInfo info;
     red_status st = current_device(&dev, &info);
     if (st != RED_OK) return st;
+    namespace T = libred::table;
 
     libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     // Rows of fewer than 1024 floats go to the LDS-staged kernel (short_rows
@@ -391,7 +391,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     const bool narrow_default = p.short_rows == 0 && (cols == 2 || cols == 4);
     if (dense && libred::rows_narrow_tile_rows(cols) > 0 && (p.short_rows == 17 || narrow_default)) {
         const size_t steps = rows / libred::rows_narrow_tile_rows(cols);
-        const size_t cap = pol == nullptr ? (size_t)1024 : (size_t)p.max_blocks;
+        const size_t cap = pol == nullptr ? (size_t)T::kNarrowWaves : (size_t)p.max_blocks;
         L.narrow = 1;
         L.grid = (int)(steps == 0 ? 1 : steps < cap ? steps : cap);
         const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
@@ -399,20 +399,21 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         return RED_OK;
     }
     if (p.short_rows == 17) p.short_rows = 0;  // where the register kernel does not apply: the default
-    const bool staged_ok = cols > 0 && (dense ? rows * cols >= 4 && fold * cols <= 4096
-                                              : span_all >= 8 && (step - cols) * 4 <= cols && cols + 3 <= 4096 &&
-                                                    (step == cols || cols < 512));
-    const bool staged_default = p.short_rows == 0 && cols < 1024;
+    const bool staged_ok =
+        cols > 0 && (dense ? rows * cols >= 4 && fold * cols <= T::kStagedMaxTileFloats
+                           : span_all >= 8 && (step - cols) * 4 <= cols && cols + 3 <= T::kStagedMaxTileFloats &&
+                                 (step == cols || cols < T::kStagedStridedBelowCols));
+    const bool staged_default = p.short_rows == 0 && cols < T::kStagedBelowCols;
     if (staged_ok && (staged_default || p.short_rows >= 3)) {
-        const size_t base_u = dense ? (fold * cols <= 1024 ? 4 : fold * cols <= 2048 ? 8 : 16)
-                                    : (cols + 3 <= 1024 ? 4 : cols + 3 <= 2048 ? 8 : 16);
+        const size_t span_floats = dense ? fold * cols : cols + 3;  // one aligned span of rows
+        const size_t base_u = span_floats <= T::kTileFloats4 ? 4 : span_floats <= T::kTileFloats8 ? 8 : 16;
         // x's offset in elements from the 16-byte boundary before it.
         const size_t sh = ((uintptr_t)x % 16) / sizeof(float);
         // Rows of whole vectors that start 16-byte aligned, the condition for
         // reading them from LDS a vector at a time.
         const bool vec_rows = cols % 4 == 0 && sh == 0 && step % 4 == 0;
         size_t max_blocks = (size_t)p.max_blocks;
-        const bool vread_default = vec_rows && cols <= 64;
+        const bool vread_default = vec_rows && cols <= T::kVectorReadMaxCols;
         // Lanes per row first: the tile size below depends on them.
         if (p.short_rows >= 10) {  // vector reads (rows of whole vectors), 2^(short_rows - 10) lanes
             L.staged_log2s = p.short_rows - 10;
@@ -434,10 +435,12 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             // 32 floats (1024-float tiles), cols / 24 from there, or cols / 16
             // for rows of whole vectors from 128 floats (4096-float tiles);
             // longer rows take the whole wave.
-            const size_t per = cols < 32 ? 8 : (cols % 4 == 0 && cols >= 128) ? 16 : 24;
+            const size_t per = cols < T::kLanesNarrowBelowCols ? T::kLanesDivNarrow
+                               : (cols % 4 == 0 && cols >= T::kLanesWholeVecFromCols) ? T::kLanesDivWholeVec
+                                                                                        : T::kLanesDivOther;
             int lg = 0;
             while (lg < 6 && ((size_t)2 << lg) <= cols / per) ++lg;
-            L.staged_log2s = cols > 512 ? 6 : lg;
+            L.staged_log2s = cols > T::kWholeWaveAboveCols ? 6 : lg;
         }
         // Tile size: 16-byte vectors per lane (4, 8 or 16, at least base_u
         // so that a tile holds one aligned span of rows).
@@ -455,7 +458,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         // 1 GiB, 3 floats 4.7 -> 5.4, 5-15 and 17 floats 5.0-5.4 -> 5.7-5.9,
         // 24 floats 5.3 -> 5.8 TB/s of input and output (widths 4, 8, 16 and
         // 32 had whole-line tiles already).
-        const bool whole_lines = dense && (p.lines == 1 || (p.lines == 0 && cols < 32));
+        const bool whole_lines = dense && (p.lines == 1 || (p.lines == 0 && cols < T::kWholeLinesBelowCols));
         auto tile_rows = [&](size_t u) {
             if (!dense) return (256 * u - 3 - cols) / step + 1;
             if (whole_lines && (256 * u) / (32 * cols) >= 1) return (256 * u) / (32 * cols) * 32;
@@ -466,21 +469,22 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             return r == 0 ? 0.0 : (double)r / (double)(pass * ((r + pass - 1) / pass));
         };
         size_t u = base_u;
-        if (pol == nullptr && whole_lines && cols >= 5 && cols < 32 && (cols & (cols - 1)) != 0 &&
-            base_u <= 8) {
+        if (pol == nullptr && whole_lines && cols >= T::kWholeLinesWideTileFromCols &&
+            cols < T::kWholeLinesBelowCols && (cols & (cols - 1)) != 0 && base_u <= 8) {
             // Whole-line tiles of rows of 5-31 floats that are not a power of
             // two: 8 loads per lane on 2048 waves came within 3% of the best
             // of nine shapes at each width measured (5-15, 17, 24 floats);
             // 3 floats and the powers of two ran 1-3% faster with 4.
             u = 8;
-        } else if (pol == nullptr && vread_default && cols >= 44) {
+        } else if (pol == nullptr && vread_default && cols >= T::kVectorReadBigTileFromCols) {
             // Rows of 11-16 whole vectors (measured on 1 GiB, sums): 4096-float
             // tiles on 1024 waves for 44-60 floats (48: 5.9 -> 6.3, 60: 5.4 ->
             // 6.4 TB/s), 2048-float tiles on 1024 waves for 64 floats (6.5 ->
             // 6.8 TB/s); narrower rows keep 1024-float tiles on 2048 waves.
             u = cols == 64 ? 8 : 16;
-            max_blocks = 1024;
-        } else if (pol == nullptr && !vread_default && cols >= 32 && cols <= 512) {
+            max_blocks = T::kStagedBigTileWaves;
+        } else if (pol == nullptr && !vread_default && cols >= T::kElementTileRuleMinCols &&
+                   cols <= T::kElementTileRuleMaxCols) {
             // Rows of 33 to 512 floats read element by element: the largest
             // tile whose passes are within 2% as full as the fullest, on 1024
             // waves for 4096-float tiles and 2048 below (over 54 widths of
@@ -488,11 +492,11 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             // geometric mean, against 95.8% for 4096-float tiles throughout).
             double best = 0.0;
             for (size_t c : {(size_t)16, (size_t)8, (size_t)4})
-                if (c >= base_u && pass_use(c) > best + 0.02) {
+                if (c >= base_u && pass_use(c) > best + T::kPassUseSlack) {
                     best = pass_use(c);
                     u = c;
                 }
-            max_blocks = u == 16 ? 1024 : 2048;
+            max_blocks = u == 16 ? T::kStagedBigTileWaves : T::kStagedWaves;
             // Rows of 33-39 floats: when 4096-float tiles leave no room to
             // hold the results in LDS but 2048-float tiles on 1024 waves do,
             // and their passes are within 5% as full, take those (1 GiB: sums
@@ -505,10 +509,11 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
                 return need <= info.lds_per_cu / ((g + info.cu_count - 1) / info.cu_count) &&
                        need <= info.lds_per_block;
             };
-            if (u == 16 && p.defer == 0 && cols < 40 && base_u <= 8 && !holds(16, 1024) && holds(8, 1024) &&
-                pass_use(8) >= pass_use(16) - 0.05) {
+            if (u == 16 && p.defer == 0 && cols < T::kHoldSmallTileBelowCols && base_u <= 8 &&
+                !holds(16, T::kStagedBigTileWaves) && holds(8, T::kStagedBigTileWaves) &&
+                pass_use(8) >= pass_use(16) - T::kHoldSmallTileSlack) {
                 u = 8;
-                max_blocks = 1024;
+                max_blocks = T::kStagedBigTileWaves;
             }
         }
         L.staged_u = (int)u;
@@ -533,7 +538,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         // Rows of 960 floats and more are left out: with a row or two per
         // tile, holding measured 1-10% slower there (and 5-20% faster on
         // narrower rows).
-        if (p.defer == 0 && cols < 960) {
+        if (p.defer == 0 && cols < T::kHoldBelowCols) {
             const size_t results = (tiles + L.grid - 1) / L.grid * L.staged_rows;
             const size_t waves_per_cu = ((size_t)L.grid + info.cu_count - 1) / info.cu_count;
             const size_t stage = (size_t)64 * L.staged_u * 16;  // 64 lanes x staged_u 16-byte vectors
@@ -549,7 +554,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // policy turns that off (short_rows 1): 16-byte units when every row
     // starts 16-byte aligned and holds whole vectors (segments of up to 16
     // lanes), else single elements (segments of up to 64 lanes).
-    if (p.short_rows != 1 && cols > 0 && cols <= 512) {
+    if (p.short_rows != 1 && cols > 0 && cols <= T::kPackedMaxCols) {
         const bool vec = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
         const size_t units = vec ? cols / 4 : cols;
         const int max_lg = vec ? 4 : 6;
@@ -599,8 +604,8 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             // floats than 4096 or 2048 waves (2049: 5.8 -> 6.8, 2500: 5.5 ->
             // 6.6 TB/s) and within 2% at 1700, 3001 and 6001; longer rows
             // keep 1024 waves (50257 floats: 6% slower with more).
-            p.unroll = 8;
-            p.max_blocks = cols < 16384 ? 32768 : 1024;
+            p.unroll = T::kCoverUnroll;
+            p.max_blocks = cols < T::kRowsLongFromCols ? T::kCoverWavesBelowLong : T::kCoverWavesLong;
         }
         // Every wave gets the same number of rows, give or take one: with
         // per = ceil(rows / (max_blocks waves)), ceil(rows / per) waves, so
@@ -647,6 +652,7 @@ double cols_lane_use(size_t groups) {
 //   5% more lanes than the matrix itself (65 groups of four columns, say,
 //   leave a second block per row phase with one group).
 size_t fold_rows(size_t rows, size_t cols) {
+    namespace T = libred::table;
     const size_t m0 = cols % 4 == 0 ? 1 : cols % 2 == 0 ? 2 : 4;
     // m_line rows span whole 128-byte lines. A wave reads 1 KiB of a row per
     // load; when rows do not start on a line, the line at each boundary is
@@ -654,7 +660,8 @@ size_t fold_rows(size_t rows, size_t cols) {
     // it: 6.3% more HBM bytes with 16-row views of odd widths, 11-14% at 3,
     // 7, 17 and 100 columns (FETCH_SIZE).
     const size_t m_line = 32 / std::gcd(cols, (size_t)32);
-    if (cols >= 256 && cols % 32 != 0 && m_line != 16 && rows / 32 >= 1024 && cols * 32 <= RED_MAX_N) {
+    if (cols >= T::kFoldWideFromCols && cols % 32 != 0 && m_line != 16 && rows / 32 >= T::kFold32MinViewRows &&
+        cols * 32 <= RED_MAX_N) {
         // 32 rows per view row (a multiple of m_line): odd widths of 257 to
         // 4097 ran 7-17% faster than with 16 rows (1025: 5.8 -> 6.3, 2049:
         // 5.9 -> 6.9 TB/s), multiples of 4 from 300 to 6000 0-15% faster
@@ -662,14 +669,15 @@ size_t fold_rows(size_t rows, size_t cols) {
         // span whole lines (32 measured up to 8% slower there).
         return 32;
     }
-    if (m0 > 1 && cols >= 256) {
+    if (m0 > 1 && cols >= T::kFoldWideFromCols) {
         // Over 1023 to 65537 columns, 16 rows ran 3-24% faster than 4 rows,
         // which already use 98% of the lanes.
-        size_t m = 16;
+        size_t m = T::kFold16Rows;
         while (m > rows || cols * m > RED_MAX_N) m -= m0;
         return m < m0 ? 1 : m;
     }
-    if (cols >= 32 && cols < 256 && (m0 > 1 || cols_lane_use(cols / 4) < 0.95)) {
+    if (cols >= T::kFoldMidFromCols && cols < T::kFoldWideFromCols &&
+        (m0 > 1 || cols_lane_use(cols / 4) < T::kFoldMidLaneUse)) {
         // Widths of 32 to 255 (multiples of 4 only when their own rows leave
         // lanes idle) take the smallest m whose view rows hold 512 groups of
         // four columns (8 KiB) and span whole lines, at most 64: over 33 to
@@ -677,9 +685,9 @@ size_t fold_rows(size_t rows, size_t cols) {
         // (33: 5.6 -> 6.7 TB/s, 65: 5.5 -> 6.8, 68: 6.0 -> 6.7 against the
         // choice by lane use below, whose 4-16 rows already keep most lanes
         // busy).
-        size_t m = (2048 + cols - 1) / cols;
+        size_t m = (T::kFoldViewFloats + cols - 1) / cols;
         m = (m + m_line - 1) / m_line * m_line;
-        if (m > 64) m = 64;
+        if (m > T::kFoldMaxRows) m = T::kFoldMaxRows;
         while (m > rows || cols * m > RED_MAX_N) m -= m0;
         return m < m0 ? 1 : m;
     }
@@ -689,7 +697,7 @@ size_t fold_rows(size_t rows, size_t cols) {
         const double use = cols_lane_use(m * cols / 4);
         if (use > best_use + 1e-9) best_use = use, best = m;  // the smallest m on a tie
     }
-    if (cols < 32 && best_use < 0.99) {
+    if (cols < T::kFoldMidFromCols && best_use < T::kFoldNarrowEnough) {
         // Below 32 columns, a view whose rows span whole lines wins when it
         // keeps 84% of the lanes busy (23: 5.7 -> 6.3, 28: 6.1 -> 6.5, 31:
         // 6.1 -> 6.8 TB/s; 7, 14, 21, 27, 29 3-5% faster); with fewer lanes
@@ -698,9 +706,9 @@ size_t fold_rows(size_t rows, size_t cols) {
         // own rows best).
         const size_t top = m0 == 1 ? 16 : 32;
         for (size_t m = m_line; m <= top && m <= rows && cols * m <= RED_MAX_N; m += m_line)
-            if (cols_lane_use(m * cols / 4) >= 0.84) return m;
+            if (cols_lane_use(m * cols / 4) >= T::kFoldNarrowLaneUse) return m;
     }
-    if (m0 == 1 && best_use < cols_lane_use(cols / 4) + 0.05) return 1;
+    if (m0 == 1 && best_use < cols_lane_use(cols / 4) + T::kFoldGain) return 1;
     return best;
 }
 
@@ -767,11 +775,12 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     }
     const bool vec_ok = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
     L.vec = (p.vec != 1 && vec_ok) ? 4 : 1;
-    if (pol == nullptr && L.vec == 4 && cols / 256 > (size_t)kWideCols.target_waves) p = kWideCols;
+    if (pol == nullptr && L.vec == 4 && cols / 256 > libred::table::kWideColBlocks) p = kWideCols;
     // Rows that are not a whole number of 128-byte lines (and not a folded
     // view) also read best 4 KiB at a time, 2 rows in flight: 1020, 1500,
     // 3000 and 6000 columns ran 8-12% faster than with the default shape.
-    if (pol == nullptr && L.vec == 4 && L.fold_m == 1 && cols % 32 != 0 && cols >= 256) p = kWideCols;
+    if (pol == nullptr && L.vec == 4 && L.fold_m == 1 && cols % 32 != 0 && cols >= libred::table::kFoldWideFromCols)
+        p = kWideCols;
     // Narrow matrix: if the column groups divide a wave, pack several rows
     // into each load.
     const size_t groups = cols / (size_t)L.vec;
