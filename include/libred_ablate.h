@@ -89,8 +89,8 @@ typedef struct red_flat_policy {
  * gives the LDS-staged kernel tiles of that many 16-byte vectors per lane
  * when that is more than the rows need, and the LDS-staged kernel always
  * loads non-temporally, whatever `nontemporal` says):
- *   0  the library's choice: rows of 2 or 4 floats of a contiguous,
- *      16-byte aligned matrix go to the register kernel (17); other rows of
+ *   0  the library's choice: rows of 1 to 16 floats of a contiguous,
+ *      16-byte aligned matrix go to the narrow kernel (17); other rows of
  *      fewer than 1024 floats go to the
  *      LDS-staged kernel when they are contiguous or their gaps (ld - cols)
  *      hold at most a quarter of a row, and the matrix spans at least 8
@@ -113,10 +113,11 @@ typedef struct red_flat_policy {
  *      16-byte vectors from LDS when the rows hold whole vectors that start
  *      16-byte aligned (cols and ld multiples of 4, x 16-byte aligned; the
  *      default for such rows of at most 64 floats);
- *   17  the register kernel for rows of 1, 2 or 4 floats of a contiguous,
+ *   17  the narrow kernel for rows of 1 to 16 floats of a contiguous,
  *      16-byte aligned matrix (each lane folds the whole rows of its own
- *      16-byte vectors; tiles of 8 coalesced loads per lane; the library's
- *      choice for 2 and 4 floats), else as 0;
+ *      16-byte vectors, read through LDS when they span several; tiles of
+ *      at least 8 coalesced loads per lane; the library's choice), else as
+ *      0;
  * and `defer` (the LDS-staged kernel): 0 = a wave keeps its row results in
  * LDS and stores them after its last tile when they fit beside its staging
  * tile in its share of the CU's LDS (the CU's LDS over the waves the grid

@@ -33,11 +33,18 @@ constexpr size_t kStagedStridedBelowCols = 512;
 // segment of lanes per row) when the staged kernel does not apply.
 constexpr size_t kPackedMaxCols = 512;
 
-// ------------------------------------------------------------ rows: register kernel
-// Rows of 2 and 4 floats of a contiguous, 16-byte aligned matrix take the
-// register kernel on 1024 waves (2 floats 5.45 -> 5.77 TB/s of input plus
-// output, 4 floats level; 1 float, a copy, level or slower: kept staged).
+// ------------------------------------------------------------ rows: narrow kernel
+// Rows of up to 16 floats of a contiguous, 16-byte aligned matrix take the
+// narrow kernel (each lane folds whole rows) on 1024 waves: against the
+// staged kernel with whole-line tiles, TB/s of input plus output, 3 floats
+// 5.3-5.4 -> 5.5, 5 floats 5.9 -> 6.1, 7 floats 5.8 -> 6.1, 9-11 floats
+// 5.7-5.8 -> 6.0-6.1, 12-15 floats +1-4%, 2, 4, 8 and 16 floats level or
+// better (narrow sweep, widths 1-16). Rows of one float (a copy) on 512
+// waves: 5.5 -> 5.9 and 5.0 -> 5.1 TB/s in two runs; 512 waves at the other
+// widths was erratic (up to 15% slower).
+constexpr size_t kNarrowDefaultMaxCols = 16;
 constexpr int kNarrowWaves = 1024;
+constexpr int kNarrowCopyWaves = 512;
 
 // ------------------------------------------------------------ rows: staged tile
 // Tile sizes by the floats a tile's rows span: up to 1024 -> 4 loads per

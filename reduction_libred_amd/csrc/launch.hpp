@@ -67,11 +67,13 @@ struct RowsLaunch {
     int narrow;         // the register kernel for narrow rows (rows_narrow.hip), `grid` waves
 };
 
-// Narrow rows: a contiguous, 16-byte aligned matrix of rows of 1, 2 or 4
-// floats, reduced in registers (op 0 = sum, 1 = max) by `grid` single-wave
-// blocks, tiles of kNarrowTileLoads 16-byte loads per lane.
-// rows_narrow_tile_rows(cols) rows make one tile (0 for another width).
+// Narrow rows: a contiguous, 16-byte aligned matrix of rows of 1 to
+// kNarrowMaxCols floats, each lane folding whole rows (op 0 = sum, 1 = max),
+// `grid` single-wave blocks, tiles of at least kNarrowTileLoads 16-byte loads
+// per lane. rows_narrow_tile_rows(cols) rows make one tile (0 for another
+// width).
 constexpr int kNarrowTileLoads = 8;
+constexpr size_t kNarrowMaxCols = 16;
 size_t rows_narrow_tile_rows(size_t cols);
 hipError_t launch_rows_narrow(int op, const float* x, size_t rows, size_t cols, float* out, int grid, bool nt,
                               hipStream_t stream);

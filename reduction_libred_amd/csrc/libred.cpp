@@ -382,16 +382,18 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // (Strided rows of 512 floats and more stay with the packed or
     // one-wave-per-row kernels: 512 floats at a stride of 516 ran 6% slower
     // staged.)
-    // Rows of 1, 2 or 4 floats of a contiguous, 16-byte aligned matrix: the
-    // register kernel, each lane reducing the whole rows of its 16-byte
-    // vectors and storing its results side by side (short_rows 17).
-    // By default for rows of 2 and 4 floats, on 1024 waves (1 GiB: 2 floats
-    // 5.45 -> 5.77 TB/s of input and output, 4 floats level with the staged
-    // kernel; 1 float, a copy, level or slower).
-    const bool narrow_default = p.short_rows == 0 && (cols == 2 || cols == 4);
+    // Rows of 1 to 16 floats of a contiguous, 16-byte aligned matrix: the
+    // narrow kernel, each lane reducing the whole rows of its own 16-byte
+    // vectors (through LDS when they span several) and storing its results
+    // side by side (short_rows 17).
+    // The default for rows of up to 16 floats (see the table for the
+    // measurements), on 1024 waves (512 for rows of one float, a copy).
+    const bool narrow_default = p.short_rows == 0 && cols <= T::kNarrowDefaultMaxCols;
     if (dense && libred::rows_narrow_tile_rows(cols) > 0 && (p.short_rows == 17 || narrow_default)) {
         const size_t steps = rows / libred::rows_narrow_tile_rows(cols);
-        const size_t cap = pol == nullptr ? (size_t)T::kNarrowWaves : (size_t)p.max_blocks;
+        const size_t cap = pol != nullptr ? (size_t)p.max_blocks
+                           : cols == 1    ? (size_t)T::kNarrowCopyWaves
+                                          : (size_t)T::kNarrowWaves;
         L.narrow = 1;
         L.grid = (int)(steps == 0 ? 1 : steps < cap ? steps : cap);
         const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);

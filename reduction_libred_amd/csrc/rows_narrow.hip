@@ -1,16 +1,27 @@
-// rows_narrow.hip -- per-row sum and max of rows of 1, 2 or 4 floats of a
-// contiguous, 16-byte aligned row-major matrix, in registers only.
+// rows_narrow.hip -- per-row sum and max of narrow rows (1 to 16 floats) of
+// a contiguous, 16-byte aligned row-major matrix, each lane folding whole
+// rows.
 //
 // One output per segment, as the lesson's block partials are one output per
 // block ("03_shared_memory_sync_reduction.py", demo 3); here a segment is a
-// row of C floats, a quarter of a 16-byte vector or less. Each lane's vector
-// holds M = 4 / C whole rows: the lane folds them in order (float64 for the
-// sum, the strictly-greater rule for the max) and stores its M results side
-// by side. The matrix is cut into tiles of U * 64 vectors; a wave reads a
-// tile with U loads per lane, each a coalesced 1 KiB, and writes its
-// U * 64 * M results with U stores of 256 * M contiguous bytes, whole
-// 128-byte lines when out is 128-byte aligned. Nothing goes through LDS and
-// no lane talks to another.
+// row of C floats, far shorter than a wave. Each lane owns M = 4 / gcd(C, 4)
+// consecutive rows, whose M * C floats are V = M * C / 4 whole 16-byte
+// vectors (C = 1: four rows in one vector; C = 3: four rows in three; C = 16:
+// one row in four). A wave step covers 64 * M consecutive rows; a tile is U
+// steps, U = ceil(8 / V), so that about eight 16-byte loads per lane are in
+// flight. The lane folds each of its rows in order (float64 for the sum, the
+// strictly-greater rule for the max) and stores its M results side by side:
+// a store instruction writes 256 * M contiguous bytes, whole 128-byte lines
+// when out is 128-byte aligned.
+//
+// A tile is read with coalesced loads (lane l takes vectors l, l + 64, ...,
+// 1 KiB per instruction). With V = 1 each lane's vector already holds its
+// rows. With V > 1 the tile goes through LDS as it arrived and each lane
+// reads back its own V consecutive vectors with 16-byte LDS reads (lanes
+// 16 * V bytes apart: for odd V, which covers every width but the multiples
+// of 8, no two lanes of a 16-lane pass share a bank). Reading each lane's
+// vectors straight from memory instead, 16 * V bytes apart, touched many
+// lines per load instruction for little data and ran 2.5 times slower.
 //
 // Tiles are dealt to the waves round-robin, and the next tile's loads are
 // issued before the current tile is folded and stored. The rows after the
@@ -23,25 +34,48 @@ namespace libred {
 
 namespace {
 
-template <class Op, int C, int U, bool NT>
+template <int C>
+struct NarrowShape {
+    static constexpr int M = C % 4 == 0 ? 1 : (C % 2 == 0 ? 2 : 4);  // rows per lane per step
+    static constexpr int V = C * M / 4;                               // 16-byte vectors per lane per step
+    static constexpr int U = (kNarrowTileLoads + V - 1) / V;          // steps per tile
+    static constexpr int L = U * V;                                   // loads per lane per tile
+};
+
+template <class Op, int C, bool NT>
 __global__ __launch_bounds__(kWave) void rows_narrow_kernel(const float* __restrict__ x, size_t rows,
                                                             float* __restrict__ out) {
-    static_assert(C == 1 || C == 2 || C == 4, "one vector must hold whole rows");
     using acc_t = typename Op::acc_t;
-    constexpr int M = 4 / C;                                 // rows per vector
+    using S = NarrowShape<C>;
+    constexpr int M = S::M, V = S::V, U = S::U, L = S::L;
     constexpr size_t kTileRows = (size_t)U * kWave * M;
+    __shared__ f32x4 stage[V > 1 ? kWave * L : 1];
     const unsigned int lane = threadIdx.x;
     const f32x4* __restrict__ xv = reinterpret_cast<const f32x4*>(x);
     const size_t ntiles = rows / kTileRows;
     const size_t G = gridDim.x;
     const bool out16 = ((uintptr_t)out & 15) == 0;
 
-    auto load = [&](f32x4 (&v)[U], size_t t) {
-        const f32x4* __restrict__ p = xv + t * U * kWave + lane;
+    auto load = [&](f32x4 (&v)[L], size_t t) {
+        const f32x4* __restrict__ p = xv + t * L * kWave + lane;
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = load_vec<NT>(p + u * kWave);
+        for (int i = 0; i < L; ++i) v[i] = load_vec<NT>(p + i * kWave);
     };
-    auto fold_store = [&](const f32x4 (&v)[U], size_t t) {
+    auto fold_store = [&](const f32x4 (&v)[L], size_t t) {
+        f32x4 w[L];  // the lane's own vectors: step u's are w[u * V .. u * V + V)
+        if constexpr (V == 1) {
+#pragma unroll
+            for (int i = 0; i < L; ++i) w[i] = v[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < L; ++i) stage[i * kWave + lane] = v[i];
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int j = 0; j < V; ++j) w[u * V + j] = stage[u * kWave * V + lane * V + j];
+            __syncthreads();
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             float res[M];
@@ -49,14 +83,17 @@ __global__ __launch_bounds__(kWave) void rows_narrow_kernel(const float* __restr
             for (int r = 0; r < M; ++r) {
                 acc_t a = Op::identity();
 #pragma unroll
-                for (int c = 0; c < C; ++c) a = Op::combine(a, Op::lift(v[u][r * C + c], (size_t)c));
+                for (int c = 0; c < C; ++c) {
+                    const int e = r * C + c;
+                    a = Op::combine(a, Op::lift(w[u * V + e / 4][e % 4], (size_t)c));
+                }
                 res[r] = Op::finish(a);
             }
             float* __restrict__ o = out + ((t * U + u) * kWave + lane) * M;
             if constexpr (M == 4) {
                 if (out16) {
-                    f32x4 w = {res[0], res[1], res[2], res[3]};
-                    *reinterpret_cast<f32x4*>(o) = w;
+                    f32x4 q = {res[0], res[1], res[2], res[3]};
+                    *reinterpret_cast<f32x4*>(o) = q;
                     continue;
                 }
             }
@@ -70,7 +107,7 @@ __global__ __launch_bounds__(kWave) void rows_narrow_kernel(const float* __restr
     size_t t0 = blockIdx.x;  // wave-uniform
     if (t0 < ntiles) {
         size_t n = (ntiles - t0 + G - 1) / G;
-        f32x4 a[U], b[U];
+        f32x4 a[L], b[L];
         load(a, t0);
         for (; n > 2; n -= 2, t0 += 2 * G) {
             load(b, t0 + G);
@@ -99,12 +136,10 @@ __global__ __launch_bounds__(kWave) void rows_narrow_kernel(const float* __restr
 
 template <class Op, int C>
 hipError_t launch_c(const float* x, size_t rows, float* out, int grid, bool nt, hipStream_t stream) {
-    constexpr int U = kNarrowTileLoads;
     if (nt)
-        hipLaunchKernelGGL((rows_narrow_kernel<Op, C, U, true>), dim3(grid), dim3(kWave), 0, stream, x, rows, out);
+        hipLaunchKernelGGL((rows_narrow_kernel<Op, C, true>), dim3(grid), dim3(kWave), 0, stream, x, rows, out);
     else
-        hipLaunchKernelGGL((rows_narrow_kernel<Op, C, U, false>), dim3(grid), dim3(kWave), 0, stream, x, rows,
-                           out);
+        hipLaunchKernelGGL((rows_narrow_kernel<Op, C, false>), dim3(grid), dim3(kWave), 0, stream, x, rows, out);
     return hipGetLastError();
 }
 
@@ -113,7 +148,20 @@ hipError_t launch_op(const float* x, size_t rows, size_t cols, float* out, int g
     switch (cols) {
         case 1: return launch_c<Op, 1>(x, rows, out, grid, nt, stream);
         case 2: return launch_c<Op, 2>(x, rows, out, grid, nt, stream);
+        case 3: return launch_c<Op, 3>(x, rows, out, grid, nt, stream);
         case 4: return launch_c<Op, 4>(x, rows, out, grid, nt, stream);
+        case 5: return launch_c<Op, 5>(x, rows, out, grid, nt, stream);
+        case 6: return launch_c<Op, 6>(x, rows, out, grid, nt, stream);
+        case 7: return launch_c<Op, 7>(x, rows, out, grid, nt, stream);
+        case 8: return launch_c<Op, 8>(x, rows, out, grid, nt, stream);
+        case 9: return launch_c<Op, 9>(x, rows, out, grid, nt, stream);
+        case 10: return launch_c<Op, 10>(x, rows, out, grid, nt, stream);
+        case 11: return launch_c<Op, 11>(x, rows, out, grid, nt, stream);
+        case 12: return launch_c<Op, 12>(x, rows, out, grid, nt, stream);
+        case 13: return launch_c<Op, 13>(x, rows, out, grid, nt, stream);
+        case 14: return launch_c<Op, 14>(x, rows, out, grid, nt, stream);
+        case 15: return launch_c<Op, 15>(x, rows, out, grid, nt, stream);
+        case 16: return launch_c<Op, 16>(x, rows, out, grid, nt, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -121,8 +169,11 @@ hipError_t launch_op(const float* x, size_t rows, size_t cols, float* out, int g
 }  // namespace
 
 size_t rows_narrow_tile_rows(size_t cols) {
-    if (cols != 1 && cols != 2 && cols != 4) return 0;
-    return (size_t)kNarrowTileLoads * kWave * (4 / cols);
+    if (cols < 1 || cols > kNarrowMaxCols) return 0;
+    const size_t m = cols % 4 == 0 ? 1 : (cols % 2 == 0 ? 2 : 4);
+    const size_t v = cols * m / 4;
+    const size_t u = (kNarrowTileLoads + v - 1) / v;
+    return u * kWave * m;
 }
 
 hipError_t launch_rows_narrow(int op, const float* x, size_t rows, size_t cols, float* out, int grid, bool nt,

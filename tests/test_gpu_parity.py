@@ -603,7 +603,9 @@ def test_sum_f64():
 
 # ----------------------------------------------------------------- rows
 
-ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023, 2), (511, 4), (1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
+ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023, 2), (511, 4),
+              (5000, 7), (3001, 9), (3000, 10), (2999, 11), (2000, 12), (3003, 13), (3000, 14), (3002, 15),
+              (3000, 16), (10_001, 8), (768, 3), (767, 3), (4000, 6), (1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
               (5, 64), (6, 65), (257, 4096), (2, 100_003), (4097, 3), (333, 1024), (50, 513),
               (1000, 4), (777, 16), (301, 32), (129, 128), (77, 200), (33, 8), (1025, 12), (70, 512),
               (200, 33), (100, 511), (1000, 100), (3000, 2), (1, 3), (2, 2), (5, 6), (1001, 6),
@@ -619,7 +621,9 @@ ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1,
                 dict(short_rows=11), dict(short_rows=14, unroll=16, max_blocks=3), dict(short_rows=16),
                 dict(defer=1), dict(defer=1, short_rows=12, max_blocks=2),
                 dict(short_rows=17), dict(short_rows=17, max_blocks=3, nontemporal=0),
-                dict(lines=1), dict(lines=1, unroll=16, max_blocks=3), dict(lines=2, unroll=8))
+                dict(lines=1), dict(lines=1, unroll=16, max_blocks=3), dict(lines=2, unroll=8),
+                dict(short_rows=3, lines=1), dict(short_rows=11, lines=1, unroll=8),
+                dict(short_rows=17, max_blocks=1))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
