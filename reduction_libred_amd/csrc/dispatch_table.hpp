@@ -39,12 +39,16 @@ constexpr size_t kPackedMaxCols = 512;
 // staged kernel with whole-line tiles, TB/s of input plus output, 3 floats
 // 5.3-5.4 -> 5.5, 5 floats 5.9 -> 6.1, 7 floats 5.8 -> 6.1, 9-11 floats
 // 5.7-5.8 -> 6.0-6.1, 12-15 floats +1-4%, 2, 4, 8 and 16 floats level or
-// better (narrow sweep, widths 1-16). Rows of one float (a copy) on 512
-// waves: 5.5 -> 5.9 and 5.0 -> 5.1 TB/s in two runs; 512 waves at the other
-// widths was erratic (up to 15% slower).
+// better (narrow sweep, widths 1-16).
 constexpr size_t kNarrowDefaultMaxCols = 16;
-constexpr int kNarrowWaves = 1024;
-constexpr int kNarrowCopyWaves = 512;
+// Waves by width: the fastest of 256-1536 waves, medians of three
+// alternating rounds of sum and max (TB/s of input plus output, 512 against
+// 1024 waves): 1 float 5.9 / 5.5, 3 floats 5.8-5.9 / 5.5, 5 floats
+// 6.2-6.3 / 6.2, 7 floats 6.3 / 6.1, 13 floats 6.1-6.2 / 6.0; 2, 4, 6, 9,
+// 12 and 16 floats ran as fast or faster on 768-1024 waves (4 floats 6.0-5.3
+// on 512). Widths 8, 10, 11, 14 and 15 were not swept and take 1024.
+constexpr int kNarrowWaves[kNarrowDefaultMaxCols + 1] = {1024, 512,  1024, 512,  1024, 512,  1024, 512, 1024,
+                                                          1024, 1024, 1024, 1024, 512,  1024, 1024, 1024};
 
 // ------------------------------------------------------------ rows: staged tile
 // Tile sizes by the floats a tile's rows span: up to 1024 -> 4 loads per

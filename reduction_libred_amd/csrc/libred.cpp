@@ -386,14 +386,12 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // narrow kernel, each lane reducing the whole rows of its own 16-byte
     // vectors (through LDS when they span several) and storing its results
     // side by side (short_rows 17).
-    // The default for rows of up to 16 floats (see the table for the
-    // measurements), on 1024 waves (512 for rows of one float, a copy).
+    // The default for rows of up to 16 floats, on the measured number of
+    // waves for the width (the table).
     const bool narrow_default = p.short_rows == 0 && cols <= T::kNarrowDefaultMaxCols;
     if (dense && libred::rows_narrow_tile_rows(cols) > 0 && (p.short_rows == 17 || narrow_default)) {
         const size_t steps = rows / libred::rows_narrow_tile_rows(cols);
-        const size_t cap = pol != nullptr ? (size_t)p.max_blocks
-                           : cols == 1    ? (size_t)T::kNarrowCopyWaves
-                                          : (size_t)T::kNarrowWaves;
+        const size_t cap = pol != nullptr ? (size_t)p.max_blocks : (size_t)T::kNarrowWaves[cols];
         L.narrow = 1;
         L.grid = (int)(steps == 0 ? 1 : steps < cap ? steps : cap);
         const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
