@@ -241,6 +241,22 @@ def run_probe_sweep(args, torch, rl, W, timer, dev):
             again[i].append(gbps(nbytes, ms))
     for i, r in enumerate(top):
         r["GB/s_rerun_median"] = round(sorted(again[i])[1], 1)
+    # The copy probe (reads and writes) at its shapes: the ceiling for a
+    # reduction whose output is as large as its input.
+    y = torch.empty_like(x)
+    copies = []
+    for bpc in (1, 2, 4, 8):
+        for unroll in (4, 8, 16):
+            for nt in (0, 1):
+                shape = dict(block=64, blocks_per_cu=bpc, unroll=unroll, nontemporal=nt, layout=2)
+                fn = lambda: rl.red_probe_copy_ceiling(x, y, shape=shape)
+                for _ in range(3):
+                    fn()
+                ms = timer.region_ms(fn, reps)
+                copies.append(dict(shape, **{"us": round(ms * 1e3, 2), "GB/s_read_plus_write": round(gbps(2 * nbytes, ms), 1)}))
+                log(f"copy {shape}: {copies[-1]['GB/s_read_plus_write']} GB/s")
+    copies.sort(key=lambda r: -r["GB/s_read_plus_write"])
+    del y
     # The reduction kernel in the same process, for comparison.
     parts = torch.empty(rl.red_flat_grid(x.numel()), dtype=torch.float64, device=dev)
     for _ in range(3):
@@ -248,7 +264,8 @@ def run_probe_sweep(args, torch, rl, W, timer, dev):
     ms = timer.region_ms(lambda: rl.red_sum_f32_partials(x, partials=parts), reps)
     print(json.dumps({"mode": "probe_sweep", "workload": name, "bytes": nbytes, "reps": reps,
                       "default_shape": rl.red_default_read_shape().as_dict(),
-                      "sum_kernel_GB/s": round(gbps(nbytes + 4, ms), 1), "shapes": results}), flush=True)
+                      "sum_kernel_GB/s": round(gbps(nbytes + 4, ms), 1), "shapes": results,
+                      "copy_default_shape": rl.red_default_copy_shape().as_dict(), "copy_shapes": copies}), flush=True)
 
 
 COMBINE_SHAPES = [(64, 2, 8), (64, 1, 8), (256, 1, 8), (256, 1, 4), (1024, 1, 4), (1024, 1, 8)]
@@ -562,6 +579,8 @@ def main():
     measure("probe read sum_max_f32_2p28", lambda: rl.red_probe_read_f32(x, sink=sink), 4 * n)
     y = torch.empty_like(x)
     measure("probe copy sum_max_f32_2p28", lambda: rl.red_probe_copy_f32(x, y), 8 * n)
+    measure("probe copy ceiling (default shape) sum_max_f32_2p28, read plus write bytes",
+            lambda: rl.red_probe_copy_ceiling(x, y), 8 * n)
     del y
 
     if not args.quick:

@@ -55,6 +55,23 @@ void red_default_read_shape(red_read_shape *shape);
 red_status red_probe_read_ceiling(const void *x, size_t bytes, const red_read_shape *shape,
                                   unsigned int *sink, hipStream_t stream);
 
+/* The copy probe's default shape (see red_probe_copy_ceiling). */
+void red_default_copy_shape(red_read_shape *shape);
+
+/*
+ * Copy ceiling: y = x over `bytes` (a multiple of 16; x and y 16-byte
+ * aligned and not overlapping), read and written as 16-byte vectors by
+ * single-wave blocks streaming wave tiles with the next tile's loads in
+ * flight, the load-only probe's fastest layout. A shape (NULL = the
+ * default) must have block 64 and layout 2; it chooses blocks per compute
+ * unit (1..32), loads per lane per tile (4, 8 or 16) and whether loads and
+ * stores are non-temporal. Its time bounds what a reduction whose output is
+ * as large as its input (rows of one float) can reach. Errors as for
+ * red_probe_read_ceiling.
+ */
+red_status red_probe_copy_ceiling(const void *x, void *y, size_t bytes, const red_read_shape *shape,
+                                  hipStream_t stream);
+
 /*
  * Test probe for the poison check of the simulator page ("simt.py", section
  * 3, shared memory filled with NaN so that unwritten values show): sets every

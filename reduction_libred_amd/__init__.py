@@ -125,6 +125,8 @@ SIGNATURES = {
     "red_default_read_shape": (None, [ctypes.POINTER(ReadShape)]),
     "red_probe_read_ceiling": (_S, [_P, _Z, ctypes.POINTER(ReadShape), _P, _P]),
     "red_probe_fill_workspace": (_S, [ctypes.c_uint, _P]),
+    "red_default_copy_shape": (None, [ctypes.POINTER(ReadShape)]),
+    "red_probe_copy_ceiling": (_S, [_P, _P, _Z, ctypes.POINTER(ReadShape), _P]),
     "red_stream_new_workspace": (_S, [_P]),
     "red_device_info": (_S, [ctypes.POINTER(_I), ctypes.c_char_p, _Z]),
     "red_probe_lds_stride": (_S, [_I, _I, _P, _P]),
@@ -470,6 +472,38 @@ def red_probe_read_ceiling(x, sink=None, shape=None, stream=None):
                                           _stream_handle(stream, x.device))
     _check("red_probe_read_ceiling", st)
     return sink
+
+
+def red_default_copy_shape():
+    """The copy probe's default launch shape."""
+    p = ReadShape()
+    lib().red_default_copy_shape(ctypes.byref(p))
+    return p
+
+
+def red_probe_copy_ceiling(x, y, shape=None, stream=None):
+    """y = x (contiguous, 16-byte aligned, a multiple of 16 bytes, same size)
+    with the copy probe's launch shape (a ReadShape, a dict of its fields, or
+    None for the default)."""
+    for t in (x, y):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise TypeError("red_probe_copy_ceiling: x and y must be contiguous tensors on a ROCm device")
+    nbytes = x.numel() * x.element_size()
+    if y.numel() * y.element_size() != nbytes:
+        raise ValueError("red_probe_copy_ceiling: x and y differ in size")
+    if isinstance(shape, dict):
+        base = red_default_copy_shape()
+        for k, v in shape.items():
+            if k not in base.as_dict():
+                raise KeyError(f"unknown copy shape field {k!r}")
+            setattr(base, k, int(v))
+        shape = base
+    with torch.cuda.device(x.device):
+        st = lib().red_probe_copy_ceiling(x.data_ptr(), y.data_ptr(), nbytes,
+                                          ctypes.byref(shape) if shape is not None else None,
+                                          _stream_handle(stream, x.device))
+    _check("red_probe_copy_ceiling", st)
+    return y
 
 
 def red_probe_fill_workspace(word, stream=None, device=None):

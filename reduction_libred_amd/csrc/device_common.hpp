@@ -28,6 +28,14 @@ __device__ __forceinline__ V load_vec(const V* p) {
         return *p;
 }
 
+template <bool NT, class V>
+__device__ __forceinline__ void store_vec(V* p, V v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);  // streaming hint: do not keep in cache
+    else
+        *p = v;
+}
+
 // ---------------------------------------------------------------------------
 // Reduction operators. Each names its element type, the 16-byte vector and
 // how many elements it holds (kPerVec), the accumulator type, the output type,

@@ -35,20 +35,24 @@ constexpr size_t kPackedMaxCols = 512;
 
 // ------------------------------------------------------------ rows: narrow kernel
 // Rows of up to 16 floats of a contiguous, 16-byte aligned matrix take the
-// narrow kernel (each lane folds whole rows) on 1024 waves: against the
+// narrow kernel (each lane folds whole rows): on 1024 waves, against the
 // staged kernel with whole-line tiles, TB/s of input plus output, 3 floats
 // 5.3-5.4 -> 5.5, 5 floats 5.9 -> 6.1, 7 floats 5.8 -> 6.1, 9-11 floats
 // 5.7-5.8 -> 6.0-6.1, 12-15 floats +1-4%, 2, 4, 8 and 16 floats level or
-// better (narrow sweep, widths 1-16).
+// better (narrow sweep, widths 1-16); the waves by width below add more.
 constexpr size_t kNarrowDefaultMaxCols = 16;
-// Waves by width: the fastest of 256-1536 waves, medians of three
-// alternating rounds of sum and max (TB/s of input plus output, 512 against
-// 1024 waves): 1 float 5.9 / 5.5, 3 floats 5.8-5.9 / 5.5, 5 floats
-// 6.2-6.3 / 6.2, 7 floats 6.3 / 6.1, 13 floats 6.1-6.2 / 6.0; 2, 4, 6, 9,
-// 12 and 16 floats ran as fast or faster on 768-1024 waves (4 floats 6.0-5.3
-// on 512). Widths 8, 10, 11, 14 and 15 were not swept and take 1024.
-constexpr int kNarrowWaves[kNarrowDefaultMaxCols + 1] = {1024, 512,  1024, 512,  1024, 512,  1024, 512, 1024,
-                                                          1024, 1024, 1024, 1024, 512,  1024, 1024, 1024};
+// Waves by width, from medians of three alternating rounds of sum and max
+// (the narrow grid sweep: 256-1536 waves, then 512 against 1024 for every
+// width once the result stores were non-temporal). 512 waves, TB/s of input
+// plus output against 1024: 1 float 6.1 / 5.9, 3 floats 6.5 / 5.9, 5 floats
+// 6.3 / 5.9, 7 floats 6.0-6.2 / 5.9, 9 floats 6.2-6.4 / 5.9, 10 floats
+// 6.0-6.1 / 5.9-6.0, 11 floats 6.4 / 6.0, 13 floats 6.1-6.4 / 6.0, 14 floats
+// 6.1 / 5.8, 15 floats 6.1-6.3 / 6.0. 1024 waves: 2, 4, 6, 8, 12 and 16
+// floats, where 512 ran slower for one operator or both (4 floats 5.5-6.2
+// against 6.0-6.2, 8 floats' max 5.6 against 6.2, 16 floats' max 5.2
+// against 6.2).
+constexpr int kNarrowWaves[kNarrowDefaultMaxCols + 1] = {1024, 512, 1024, 512, 1024, 512, 1024, 512, 1024,
+                                                          512,  512, 512,  1024, 512,  512,  512,  1024};
 
 // ------------------------------------------------------------ rows: staged tile
 // Tile sizes by the floats a tile's rows span: up to 1024 -> 4 loads per

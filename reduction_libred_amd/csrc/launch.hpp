@@ -211,6 +211,10 @@ struct ReadShape {
 bool read_shape_supported(const ReadShape& s);
 hipError_t launch_read_probe(const void* x, size_t nvec, unsigned int* sink, int grid, const ReadShape& s,
                              hipStream_t stream);
+// Copy ceiling: y[0 .. nvec) = x[0 .. nvec) in 16-byte vectors, wave tiles
+// with the next tile in flight (block 64, layout 2, unroll 4 / 8 / 16).
+bool copy_shape_supported(const ReadShape& s);
+hipError_t launch_copy_probe(const void* x, void* y, size_t nvec, int grid, const ReadShape& s, hipStream_t stream);
 
 // Probes: a plain copy y = x with 16-byte accesses and a scalar tail, and
 // the single-value kernel with an xor fold (*out = xor of all words), which

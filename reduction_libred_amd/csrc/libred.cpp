@@ -257,6 +257,8 @@ constexpr libred::ColsPolicy kDefaultCols = {8, 1, 512, 0, 1, 1, 0};
 
 // The read probe's default shape: the fastest of its sweep on a 1 GiB buffer.
 constexpr red_read_shape kDefaultReadShape = {64, 2, 8, 1, 2};
+// The copy probe's default shape (single-wave blocks, next tile in flight).
+constexpr red_read_shape kDefaultCopyShape = {64, 2, 8, 1, 2};
 constexpr libred::ColsPolicy kWideCols = {2, 1, 1024, 0, 4, 0, 0};
 // Columns read one element per lane (rows not 16-byte aligned, or cols or ld
 // not a multiple of 4) with at least 64 of them: two loads per row per lane,
@@ -1181,6 +1183,29 @@ red_status red_probe_read_ceiling(const void* x, size_t bytes, const red_read_sh
     if (bytes == 0) return RED_OK;
     const int grid = rs.blocks_per_cu * info.cu_count;
     const hipError_t e = libred::launch_read_probe(x, bytes / 16, sink, grid, rs, stream);
+    if (e != hipSuccess) return fail(e, RED_ERR_HIP);
+    return RED_OK;
+}
+
+void red_default_copy_shape(red_read_shape* s) {
+    if (!s) return;
+    *s = kDefaultCopyShape;
+}
+
+red_status red_probe_copy_ceiling(const void* x, void* y, size_t bytes, const red_read_shape* shape,
+                                  hipStream_t stream) {
+    if (bytes > RED_MAX_N * 4 || bytes % 16 != 0 || (bytes > 0 && (x == nullptr || y == nullptr)))
+        return RED_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(y, 16) || overlap(x, bytes, y, bytes)) return RED_ERR_INVALID_ARG;
+    const red_read_shape& r = shape ? *shape : kDefaultCopyShape;
+    const libred::ReadShape rs = {r.block, r.blocks_per_cu, r.unroll, r.nontemporal, r.layout};
+    if (!libred::copy_shape_supported(rs)) return RED_ERR_INVALID_ARG;
+    int dev;
+    DeviceInfo info;
+    const red_status st = current_device(&dev, &info);
+    if (st != RED_OK) return st;
+    if (bytes == 0) return RED_OK;
+    const hipError_t e = libred::launch_copy_probe(x, y, bytes / 16, rs.blocks_per_cu * info.cu_count, rs, stream);
     if (e != hipSuccess) return fail(e, RED_ERR_HIP);
     return RED_OK;
 }

@@ -1,6 +1,8 @@
 // read_probe.hip -- a load-only streaming kernel that measures how fast this
 // device reads HBM, the achievable counterpart of the simulator page's memory
-// bound ("simt_lab.py", section 6, estimate_time: time = bytes / bandwidth).
+// bound ("simt_lab.py", section 6, estimate_time: time = bytes / bandwidth),
+// and a copy kernel of the same layout that measures reads and writes
+// together.
 //
 // Each lane issues 16-byte loads and folds every 32-bit word into one xor
 // (one VALU op per word, far below what the loads take), so the result is
@@ -145,7 +147,78 @@ hipError_t launch_rp_b(const u32x4* xv, size_t nvec, unsigned int* sink, int gri
     }
 }
 
+// Copy ceiling: y = x with the read probe's fastest layout (single-wave
+// blocks, wave tiles of UNROLL 16-byte loads per lane, the next tile's loads
+// in flight while the current one is stored). NT marks both the loads and
+// the stores non-temporal.
+template <int UNROLL, bool NT>
+__global__ __launch_bounds__(kWave) void copy_probe_kernel(const u32x4* __restrict__ xv, u32x4* __restrict__ yv,
+                                                           size_t nvec) {
+    constexpr size_t TILE = (size_t)kWave * UNROLL;
+    const int lane = threadIdx.x;
+    const size_t G = gridDim.x;
+    const size_t ntiles = nvec / TILE;
+    auto load = [&](u32x4 (&v)[UNROLL], size_t t) { read_tile<UNROLL, NT>(v, xv + t * TILE + lane); };
+    auto store = [&](const u32x4 (&v)[UNROLL], size_t t) {
+        u32x4* __restrict__ p = yv + t * TILE + lane;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if constexpr (NT)
+                __builtin_nontemporal_store(v[u], p + u * kWave);
+            else
+                p[u * kWave] = v[u];
+        }
+    };
+    size_t t = blockIdx.x;
+    if (t < ntiles) {
+        size_t n = (ntiles - t + G - 1) / G;
+        u32x4 a[UNROLL], b[UNROLL];
+        load(a, t);
+        for (; n > 2; n -= 2, t += 2 * G) {
+            load(b, t + G);
+            store(a, t);
+            load(a, t + 2 * G);
+            store(b, t + G);
+        }
+        if (n == 2) {
+            load(b, t + G);
+            store(a, t);
+            store(b, t + G);
+        } else {
+            store(a, t);
+        }
+    }
+    // Vectors after the last whole tile.
+    for (size_t i = ntiles * TILE + (size_t)blockIdx.x * kWave + lane; i < nvec; i += G * kWave) yv[i] = xv[i];
+}
+
+template <int UNROLL>
+hipError_t launch_cp(const u32x4* xv, u32x4* yv, size_t nvec, int grid, bool nt, hipStream_t stream) {
+    if (nt)
+        hipLaunchKernelGGL((copy_probe_kernel<UNROLL, true>), dim3(grid), dim3(kWave), 0, stream, xv, yv, nvec);
+    else
+        hipLaunchKernelGGL((copy_probe_kernel<UNROLL, false>), dim3(grid), dim3(kWave), 0, stream, xv, yv, nvec);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool copy_shape_supported(const ReadShape& s) {
+    return s.block == 64 && s.layout == 2 && (s.unroll == 4 || s.unroll == 8 || s.unroll == 16) &&
+           s.blocks_per_cu >= 1 && s.blocks_per_cu <= 32 && (s.nontemporal == 0 || s.nontemporal == 1);
+}
+
+hipError_t launch_copy_probe(const void* x, void* y, size_t nvec, int grid, const ReadShape& s, hipStream_t stream) {
+    const u32x4* xv = static_cast<const u32x4*>(x);
+    u32x4* yv = static_cast<u32x4*>(y);
+    const bool nt = s.nontemporal != 0;
+    switch (s.unroll) {
+        case 4: return launch_cp<4>(xv, yv, nvec, grid, nt, stream);
+        case 8: return launch_cp<8>(xv, yv, nvec, grid, nt, stream);
+        case 16: return launch_cp<16>(xv, yv, nvec, grid, nt, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
 
 bool read_shape_supported(const ReadShape& s) {
     const bool block = s.block == 64 || s.block == 256 || s.block == 1024;

@@ -298,3 +298,24 @@ def test_read_ceiling_probe_every_shape():
         rl.red_probe_read_ceiling(x[1:5])          # not 16-byte aligned
     with pytest.raises(rl.RedError):
         rl.red_probe_read_ceiling(x, shape=dict(block=1024, unroll=32))
+
+
+def test_copy_ceiling_probe_every_shape():
+    # Whole tiles, a partial tile and leftover vectors, every compiled shape:
+    # the copy must be exact, and nothing past the end may be written.
+    rng = np.random.default_rng(1207)
+    nvec = 64 * 16 * 23 + 64 * 3 + 11
+    w = rng.integers(0, 2 ** 32, 4 * nvec, dtype=np.uint64).astype(np.uint32).view(np.int32)
+    x = torch.from_numpy(w).to(DEV)
+    for bpc in (1, 3):
+        for unroll in (4, 8, 16):
+            for nt in (0, 1):
+                shape = dict(block=64, blocks_per_cu=bpc, unroll=unroll, nontemporal=nt, layout=2)
+                say(f"copy probe {shape}")
+                y = torch.full((4 * nvec + 8,), -7, dtype=torch.int32, device=DEV)
+                rl.red_probe_copy_ceiling(x, y[: 4 * nvec], shape=shape)
+                torch.cuda.synchronize()
+                assert torch.equal(y[: 4 * nvec], x), shape
+                assert torch.all(y[4 * nvec:] == -7), shape
+    with pytest.raises(rl.RedError):
+        rl.red_probe_copy_ceiling(x, torch.empty_like(x), shape=dict(layout=1))
