@@ -89,7 +89,7 @@ typedef struct red_flat_policy {
  * gives the LDS-staged kernel tiles of that many 16-byte vectors per lane
  * when that is more than the rows need, and the LDS-staged kernel always
  * loads non-temporally, whatever `nontemporal` says):
- *   0  the library's choice: rows of 1 to 16 floats of a contiguous,
+ *   0  the library's choice: rows of 1 to 31 floats of a contiguous,
  *      16-byte aligned matrix go to the narrow kernel (17); other rows of
  *      fewer than 1024 floats go to the
  *      LDS-staged kernel when they are contiguous or their gaps (ld - cols)
@@ -113,7 +113,7 @@ typedef struct red_flat_policy {
  *      16-byte vectors from LDS when the rows hold whole vectors that start
  *      16-byte aligned (cols and ld multiples of 4, x 16-byte aligned; the
  *      default for such rows of at most 64 floats);
- *   17  the narrow kernel for rows of 1 to 16 floats of a contiguous,
+ *   17  the narrow kernel for rows of 1 to 32 floats of a contiguous,
  *      16-byte aligned matrix (each lane folds the whole rows of its own
  *      16-byte vectors, read through LDS when they span several; tiles of
  *      at least 8 coalesced loads per lane; the library's choice), else as

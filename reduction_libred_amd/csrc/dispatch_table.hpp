@@ -34,13 +34,17 @@ constexpr size_t kStagedStridedBelowCols = 512;
 constexpr size_t kPackedMaxCols = 512;
 
 // ------------------------------------------------------------ rows: narrow kernel
-// Rows of up to 16 floats of a contiguous, 16-byte aligned matrix take the
+// Rows of up to 31 floats of a contiguous, 16-byte aligned matrix take the
 // narrow kernel (each lane folds whole rows): on 1024 waves, against the
 // staged kernel with whole-line tiles, TB/s of input plus output, 3 floats
 // 5.3-5.4 -> 5.5, 5 floats 5.9 -> 6.1, 7 floats 5.8 -> 6.1, 9-11 floats
 // 5.7-5.8 -> 6.0-6.1, 12-15 floats +1-4%, 2, 4, 8 and 16 floats level or
 // better (narrow sweep, widths 1-16); the waves by width below add more.
-constexpr size_t kNarrowDefaultMaxCols = 16;
+// Widths 17-31 on 1024 waves, medians of three alternating rounds, against
+// the staged kernel: odd widths 5.7-5.8 -> 6.0-6.3 TB/s (17: 5.8 -> 6.0-6.1,
+// 31: 5.8 -> 6.3), widths 18-30 level to 6% faster; 32 floats stay staged
+// (vector reads from LDS: 6.4 against 5.9-6.0).
+constexpr size_t kNarrowDefaultMaxCols = 31;
 // Waves by width, from medians of three alternating rounds of sum and max
 // (the narrow grid sweep: 256-1536 waves, then 512 against 1024 for every
 // width once the result stores were non-temporal). 512 waves, TB/s of input
@@ -51,8 +55,9 @@ constexpr size_t kNarrowDefaultMaxCols = 16;
 // floats, where 512 ran slower for one operator or both (4 floats 5.5-6.2
 // against 6.0-6.2, 8 floats' max 5.6 against 6.2, 16 floats' max 5.2
 // against 6.2).
-constexpr int kNarrowWaves[kNarrowDefaultMaxCols + 1] = {1024, 512, 1024, 512, 1024, 512, 1024, 512, 1024,
-                                                          512,  512, 512,  1024, 512,  512,  512,  1024};
+constexpr int kNarrowWaves[kNarrowDefaultMaxCols + 1] = {
+    1024, 512,  1024, 512,  1024, 512,  1024, 512,  1024, 512,  512,  512,  1024, 512,  512,  512,
+    1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
 
 // ------------------------------------------------------------ rows: staged tile
 // Tile sizes by the floats a tile's rows span: up to 1024 -> 4 loads per

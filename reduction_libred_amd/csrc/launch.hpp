@@ -73,7 +73,7 @@ struct RowsLaunch {
 // per lane. rows_narrow_tile_rows(cols) rows make one tile (0 for another
 // width).
 constexpr int kNarrowTileLoads = 8;
-constexpr size_t kNarrowMaxCols = 16;
+constexpr size_t kNarrowMaxCols = 32;
 size_t rows_narrow_tile_rows(size_t cols);
 hipError_t launch_rows_narrow(int op, const float* x, size_t rows, size_t cols, float* out, int grid, bool nt,
                               hipStream_t stream);

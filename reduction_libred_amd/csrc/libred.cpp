@@ -384,11 +384,11 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // (Strided rows of 512 floats and more stay with the packed or
     // one-wave-per-row kernels: 512 floats at a stride of 516 ran 6% slower
     // staged.)
-    // Rows of 1 to 16 floats of a contiguous, 16-byte aligned matrix: the
+    // Rows of 1 to 32 floats of a contiguous, 16-byte aligned matrix: the
     // narrow kernel, each lane reducing the whole rows of its own 16-byte
     // vectors (through LDS when they span several) and storing its results
     // side by side (short_rows 17).
-    // The default for rows of up to 16 floats, on the measured number of
+    // The default for rows of up to 31 floats, on the measured number of
     // waves for the width (the table).
     const bool narrow_default = p.short_rows == 0 && cols <= T::kNarrowDefaultMaxCols;
     if (dense && libred::rows_narrow_tile_rows(cols) > 0 && (p.short_rows == 17 || narrow_default)) {

@@ -1,4 +1,4 @@
-// rows_narrow.hip -- per-row sum and max of narrow rows (1 to 16 floats) of
+// rows_narrow.hip -- per-row sum and max of narrow rows (1 to 32 floats) of
 // a contiguous, 16-byte aligned row-major matrix, each lane folding whole
 // rows.
 //
@@ -110,8 +110,16 @@ __global__ __launch_bounds__(kWave) void rows_narrow_kernel(const float* __restr
 
     // The wave's tiles t0, t0 + G, ... two per loop pass, one register
     // buffer each, the next tile's loads in flight while one is folded.
+    // Tiles of more than 16 loads per lane (odd widths from 21 floats) take
+    // one buffer: two would not fit in registers.
     size_t t0 = blockIdx.x;  // wave-uniform
-    if (t0 < ntiles) {
+    if constexpr (L > 16) {
+        for (; t0 < ntiles; t0 += G) {
+            f32x4 a[L];
+            load(a, t0);
+            fold_store(a, t0);
+        }
+    } else if (t0 < ntiles) {
         size_t n = (ntiles - t0 + G - 1) / G;
         f32x4 a[L], b[L];
         load(a, t0);
@@ -168,6 +176,22 @@ hipError_t launch_op(const float* x, size_t rows, size_t cols, float* out, int g
         case 14: return launch_c<Op, 14>(x, rows, out, grid, nt, stream);
         case 15: return launch_c<Op, 15>(x, rows, out, grid, nt, stream);
         case 16: return launch_c<Op, 16>(x, rows, out, grid, nt, stream);
+        case 17: return launch_c<Op, 17>(x, rows, out, grid, nt, stream);
+        case 18: return launch_c<Op, 18>(x, rows, out, grid, nt, stream);
+        case 19: return launch_c<Op, 19>(x, rows, out, grid, nt, stream);
+        case 20: return launch_c<Op, 20>(x, rows, out, grid, nt, stream);
+        case 21: return launch_c<Op, 21>(x, rows, out, grid, nt, stream);
+        case 22: return launch_c<Op, 22>(x, rows, out, grid, nt, stream);
+        case 23: return launch_c<Op, 23>(x, rows, out, grid, nt, stream);
+        case 24: return launch_c<Op, 24>(x, rows, out, grid, nt, stream);
+        case 25: return launch_c<Op, 25>(x, rows, out, grid, nt, stream);
+        case 26: return launch_c<Op, 26>(x, rows, out, grid, nt, stream);
+        case 27: return launch_c<Op, 27>(x, rows, out, grid, nt, stream);
+        case 28: return launch_c<Op, 28>(x, rows, out, grid, nt, stream);
+        case 29: return launch_c<Op, 29>(x, rows, out, grid, nt, stream);
+        case 30: return launch_c<Op, 30>(x, rows, out, grid, nt, stream);
+        case 31: return launch_c<Op, 31>(x, rows, out, grid, nt, stream);
+        case 32: return launch_c<Op, 32>(x, rows, out, grid, nt, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -605,7 +605,8 @@ def test_sum_f64():
 
 ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023, 2), (511, 4),
               (5000, 7), (3001, 9), (3000, 10), (2999, 11), (2000, 12), (3003, 13), (3000, 14), (3002, 15),
-              (3000, 16), (10_001, 8), (768, 3), (767, 3), (4000, 6), (1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
+              (3000, 16), (10_001, 8), (768, 3), (767, 3), (4000, 6), (2000, 17), (1500, 21), (1000, 24),
+              (999, 31), (1500, 32), (1400, 26), (1, 1), (3, 5), (7, 1000), (65, 257), (4, 0), (1000, 4099), (13, 1), (9, 63),
               (5, 64), (6, 65), (257, 4096), (2, 100_003), (4097, 3), (333, 1024), (50, 513),
               (1000, 4), (777, 16), (301, 32), (129, 128), (77, 200), (33, 8), (1025, 12), (70, 512),
               (200, 33), (100, 511), (1000, 100), (3000, 2), (1, 3), (2, 2), (5, 6), (1001, 6),
