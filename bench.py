@@ -89,6 +89,10 @@ def parse_args():
                     help="instead of the headline: time the row and column entry points on 1 GiB "
                          "of f32 viewed as (2^28 // cols) x cols for a range of widths; print one "
                          "JSON line")
+    ap.add_argument("--col-orders", action="store_true",
+                    help="instead of the headline: time the column entry points on 1 GiB of f32 viewed as "
+                         "(2^28 // cols) x cols at widths around the row pitches that alias on the memory "
+                         "channels, with each row order and the default; print one JSON line")
     return ap.parse_args()
 
 
@@ -195,6 +199,38 @@ def run_widths(args, torch, rl, W, timer, dev):
     print(json.dumps({"mode": "widths", "workload": f"{name} viewed as (2^28 // cols) x cols, contiguous",
                       "steps": args.steps, "warmup": args.warmup, "unit": "GB/s of input",
                       "shapes": shapes}), flush=True)
+
+
+# Widths whose rows (or 32-row views) have a pitch that is a multiple of 255
+# or 257 floats, and neighbours that are not.
+ORDER_WIDTHS = [1016, 1020, 1024, 1028, 2040, 2044, 3060, 4080, 5100, 8160, 765, 4096]
+COL_ORDERS = (("band", dict(order=1)), ("rotated", dict(order=2)), ("chunks", dict(order=3)), ("default", None))
+
+
+def run_col_orders(args, torch, rl, W, timer, dev):
+    name = "rows_f32_65536x4096"
+    log(f"generate {name}")
+    flat = torch.from_numpy(W.workload(name)).to(dev).view(-1)
+    total = flat.numel()
+    shapes = []
+    for cols in ORDER_WIDTHS:
+        rows = total // cols
+        m = flat[: rows * cols].view(rows, cols)
+        co = torch.empty(cols, device=dev)
+        entry = {"rows": rows, "cols": cols}
+        for op_name, op in (("sum", rl.red_cols_sum_f32), ("max", rl.red_cols_max_f32)):
+            for label, pol in COL_ORDERS:
+                def fn():
+                    op(m, out=co, policy=pol)
+                for _ in range(args.warmup):
+                    fn()
+                ms = timer.region_ms(fn, args.steps)
+                entry[f"{op_name}_{label}"] = round(gbps(4 * rows * cols, ms), 1)
+        log(f"{rows}x{cols}: " + ", ".join(f"{k} {v}" for k, v in entry.items() if k not in ("rows", "cols")))
+        shapes.append(entry)
+    print(json.dumps({"mode": "col_orders", "workload": f"{name} viewed as (2^28 // cols) x cols, contiguous",
+                      "steps": args.steps, "warmup": args.warmup, "unit": "GB/s of input",
+                      "orders": [k for k, _ in COL_ORDERS], "shapes": shapes}), flush=True)
 
 
 def read_shapes():
@@ -387,6 +423,9 @@ def main():
         return
     if args.probe_sweep:
         run_probe_sweep(args, torch, rl, W, timer, dev)
+        return
+    if args.col_orders:
+        run_col_orders(args, torch, rl, W, timer, dev)
         return
     if args.combine_sweep:
         run_combine_sweep(args, torch, rl, W, timer, dev)

@@ -171,7 +171,16 @@ typedef struct red_rows_policy {
  * so a wave reads width x 1 KiB (four columns per lane) or width x 256 bytes
  * (one column per lane) of a row at once (with fewer groups, 1 is used);
  * `prefetch` (0 or 1): issue the next group of `unroll` rows before adding
- * the current one. */
+ * the current one; `order`, which rows each of the n row phases takes and
+ * in what order: 1 = every n-th group of rows, each phase from the top, so
+ * a launch reads one band of the matrix at a time; 2 = the same rows, but
+ * block b starts at its (b mod m)-th of m groups and wraps around to the
+ * first, so the waves read rows spread over the matrix; 3 = one run of
+ * consecutive rows per phase (about rows / n); 0 = the library's choice
+ * (2 when the row pitch as read, ld or the view's, is a multiple of 255 or
+ * 257 floats, pitches whose band reads fill a few memory channels' queues,
+ * else 1). The order changes the order in which a column's elements are
+ * added, never the fact that the result is fixed by the shape. */
 typedef struct red_cols_policy {
     int unroll;
     int nontemporal;
@@ -180,6 +189,7 @@ typedef struct red_cols_policy {
     int width;
     int prefetch;
     int fold;
+    int order;
 } red_cols_policy;
 
 /* The default column shape. A call without a policy uses it, except on

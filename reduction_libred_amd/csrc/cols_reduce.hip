@@ -63,7 +63,7 @@ __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typenam
 template <class Op, int VEC, int CW, int UNROLL, bool NT, bool PREFETCH>
 __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::elem_t* __restrict__ x,
                                                              size_t rows, size_t cols, size_t ld,
-                                                             size_t ncb, unsigned int ngroups,
+                                                             size_t ncb, unsigned int ngroups, int order,
                                                              typename Op::acc_t* __restrict__ partials,
                                                              typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
@@ -74,75 +74,101 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
     const size_t nphases = gridDim.x / ncb;
     const unsigned int g = lane % ngroups;
     const size_t group = kWave / ngroups;  // rows per load
-    const size_t rpl = group * nphases;    // rows between a lane's consecutive loads
     const size_t q = lane / ngroups;
     const size_t span = (size_t)ngroups * VEC;  // columns per load
     const size_t c0 = j * span * CW + (size_t)g * VEC;
-    const size_t r0 = k * group;
-    const size_t r1 = rows;
+    // The phase's rows r0 + q, r0 + q + rpl, ... below r1: every nphases-th
+    // group of rows (orders 0 and 1), or one run of consecutive rows (order
+    // 2: phase k takes rows [k * per, (k + 1) * per), per a multiple of the
+    // group).
+    size_t r0, r1, rpl;
+    if (order == 2) {
+        const size_t per = (rows + nphases * group - 1) / (nphases * group) * group;
+        r0 = k * per;
+        r1 = r0 + per < rows ? r0 + per : rows;
+        rpl = group;
+    } else {
+        r0 = k * group;
+        r1 = rows;
+        rpl = group * nphases;
+    }
     acc_t acc[CW][VEC];
 #pragma unroll
     for (int w = 0; w < CW; ++w)
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc[w][i] = Op::identity();
-    if (c0 < cols && q < group) {  // lanes past the last whole row group of a load stay idle
+    if (c0 < cols && q < group && r0 < r1) {  // lanes past the last whole row group of a load stay idle
         size_t off[CW];  // in V units from the lane's column-0 vector
 #pragma unroll
         for (int w = 0; w < CW; ++w) off[w] = c0 + w * span < cols ? w * (size_t)ngroups : 0;
         const size_t step = ld / VEC * rpl;  // in V units, between a lane's consecutive rows
         constexpr size_t U = UNROLL;
-        size_t r = r0 + q;
-        const V* __restrict__ p = reinterpret_cast<const V*>(x + r * ld + c0);
-        // Groups of UNROLL rows. With PREFETCH, two register buffers
-        // alternate: the next group's loads are issued before the current
-        // group is folded, so a wave keeps two groups in flight.
-        // The scheduling barrier keeps a group's loads issued back to back
-        // (left alone, the compiler sometimes interleaves them with waits
-        // for the previous group, halving the loads in flight).
-        auto load_group = [&](V (&v)[UNROLL][CW], const V* __restrict__ g) {
+        // Fold rows r, r + rpl, ... below rend. Groups of UNROLL rows; with
+        // PREFETCH, two register buffers alternate: the next group's loads
+        // are issued before the current group is folded, so a wave keeps two
+        // groups in flight. The scheduling barrier keeps a group's loads
+        // issued back to back (left alone, the compiler sometimes interleaves
+        // them with waits for the previous group, halving the loads in
+        // flight).
+        auto sweep = [&](size_t r, size_t rend) {
+            const V* __restrict__ p = reinterpret_cast<const V*>(x + r * ld + c0);
+            auto load_group = [&](V (&v)[UNROLL][CW], const V* __restrict__ g) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
+                for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-                for (int w = 0; w < CW; ++w) v[u][w] = load_vec<NT>(g + u * step + off[w]);
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        auto fold_group = [&](const V (&v)[UNROLL][CW]) {
+                    for (int w = 0; w < CW; ++w) v[u][w] = load_vec<NT>(g + u * step + off[w]);
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            auto fold_group = [&](const V (&v)[UNROLL][CW]) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
+                for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-                for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], v[u][w]);
-        };
-        if (!PREFETCH) {
-            for (; r + (U - 1) * rpl < r1; r += U * rpl, p += U * step) {
-                V v[UNROLL][CW];
-                load_group(v, p);
-                fold_group(v);
-            }
-        } else if (r + (U - 1) * rpl < r1) {
-            V a[UNROLL][CW], b[UNROLL][CW];
-            load_group(a, p);
-            while (true) {
-                if (r + (2 * U - 1) * rpl >= r1) {
+                    for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], v[u][w]);
+            };
+            if (!PREFETCH) {
+                for (; r + (U - 1) * rpl < rend; r += U * rpl, p += U * step) {
+                    V v[UNROLL][CW];
+                    load_group(v, p);
+                    fold_group(v);
+                }
+            } else if (r + (U - 1) * rpl < rend) {
+                V a[UNROLL][CW], b[UNROLL][CW];
+                load_group(a, p);
+                while (true) {
+                    if (r + (2 * U - 1) * rpl >= rend) {
+                        fold_group(a);
+                        r += U * rpl, p += U * step;
+                        break;
+                    }
+                    load_group(b, p + U * step);
                     fold_group(a);
                     r += U * rpl, p += U * step;
-                    break;
-                }
-                load_group(b, p + U * step);
-                fold_group(a);
-                r += U * rpl, p += U * step;
-                if (r + (2 * U - 1) * rpl >= r1) {
+                    if (r + (2 * U - 1) * rpl >= rend) {
+                        fold_group(b);
+                        r += U * rpl, p += U * step;
+                        break;
+                    }
+                    load_group(a, p + U * step);
                     fold_group(b);
                     r += U * rpl, p += U * step;
-                    break;
                 }
-                load_group(a, p + U * step);
-                fold_group(b);
-                r += U * rpl, p += U * step;
             }
-        }
-        for (; r < r1; r += rpl, p += step) {
+            for (; r < rend; r += rpl, p += step) {
 #pragma unroll
-            for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], load_vec<NT>(p + off[w]));
+                for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], load_vec<NT>(p + off[w]));
+            }
+        };
+        // The wave visits its rows in nvis rounds (round i: rows r0 + i * rpl
+        // + q). In order 1, block b starts at round b mod nvis and wraps
+        // around to round 0, so that the waves of a launch read rows spread
+        // over the matrix rather than one band of it.
+        const size_t nvis = (r1 - r0 + rpl - 1) / rpl;  // r0 < r1 here
+        const size_t split = r0 + (order == 1 ? (size_t)blockIdx.x % nvis : 0) * rpl;
+#pragma unroll 1
+        for (int part = 0; part < 2; ++part) {  // rounds from the split on, then those before it
+            const size_t rb = part == 0 ? split + q : r0 + q;
+            const size_t re = part == 0 ? r1 : (split + q < r1 ? split + q : r1);
+            sweep(rb, re);
         }
     }
     // Packed rows (CW == 1): lane g collects lanes g + ngroups, g + 2*ngroups,
@@ -272,7 +298,8 @@ bool cols_policy_supported(const ColsPolicy& p) {
     const bool u = p.unroll == 1 || p.unroll == 2 || p.unroll == 4 || p.unroll == 8 || p.unroll == 16;
     const bool w = p.width == 1 || p.width == 2 || p.width == 4;
     return u && w && (p.nontemporal == 0 || p.nontemporal == 1) && (p.prefetch == 0 || p.prefetch == 1) &&
-           p.target_waves >= 1 && (p.vec == 0 || p.vec == 1 || p.vec == 4) && p.fold >= 0 && p.fold <= 64;
+           p.target_waves >= 1 && (p.vec == 0 || p.vec == 1 || p.vec == 4) && p.fold >= 0 && p.fold <= 64 &&
+           p.order >= 0 && p.order <= 3;
 }
 
 template <class Op, int VEC, int CW, int UNROLL, bool PF>
@@ -283,10 +310,10 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
     typename Op::out_t* direct = (L.nchunks == 1 && L.fold_m <= 1 && L.rot == 0) ? out : nullptr;
     if (nt)
         hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF>), grid, dim3(kWave), 0, stream, x,
-                           rows, cols, ld, L.ncb, L.ngroups, partials, direct);
+                           rows, cols, ld, L.ncb, L.ngroups, L.order, partials, direct);
     else
         hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF>), grid, dim3(kWave), 0, stream, x,
-                           rows, cols, ld, L.ncb, L.ngroups, partials, direct);
+                           rows, cols, ld, L.ncb, L.ngroups, L.order, partials, direct);
     hipError_t e = hipGetLastError();
     const size_t W = kColsCombineBlock / kWave;
     if (e != hipSuccess) return e;

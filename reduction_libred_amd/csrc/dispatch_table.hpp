@@ -165,6 +165,23 @@ constexpr double kFoldNarrowEnough = 0.99;
 // (260 columns: 4.0 -> 6.4 TB/s folded 16 rows).
 constexpr double kFoldGain = 0.05;
 
+// ------------------------------------------------------------ columns: row order
+// Rows read at a pitch (the matrix's leading dimension, or the view's) that
+// is a multiple of one of these many floats start each block's sweep at a
+// different row group (rotated order) instead of sweeping one band of the
+// matrix: with the band, every one of these pitches read at 5.0-5.7 TB/s
+// against 6.1-7.1 for the neighbouring widths (1012-1036, 2032-2052,
+// 3052-3068, 4080-4084, 5096-5104, 6120-6124, 8160-8164 columns and
+// 508-516, 765-766, 1530-1534), and the DRAM credit stalls per read request
+// rose from 0.02-0.03 to 0.19-0.49 (TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum at
+// 1020, 1028 and 2040 columns). Rotated, sums of 1020, 2040, 3060, 4080,
+// 5100, 6120, 7140 and 8160 columns read at 5.9-6.3 TB/s (+0.5-0.9), 510,
+// 765 and 1530 columns (32640- and 97920-byte view rows) at 6.0-6.2 (+0.5),
+// 1028, 2056, 3084 and 4112 at 5.4-5.6 (+0.1-0.4); at the other widths of
+// that scan the rotated order ran up to 3% slower, so it stays off there.
+constexpr size_t kRotateRowsPitchFactorA = 255;
+constexpr size_t kRotateRowsPitchFactorB = 257;
+
 // ------------------------------------------------------------ columns: shapes
 // Short-wide matrices (more than this many blocks of 256 columns), and rows
 // of at least kFoldWideFromCols columns that are not whole lines (unfolded),

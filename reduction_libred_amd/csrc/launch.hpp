@@ -102,6 +102,7 @@ struct ColsPolicy {
     int width;
     int prefetch;
     int fold;
+    int order;
 };
 
 // How one column call launches: ncb column blocks of ngroups*vec*width
@@ -129,6 +130,11 @@ struct ColsLaunch {
     const void* tail;
     unsigned int rot;
     const void* head;
+    // Rows of a phase: 0 = every nchunks-th group from group k (a launch
+    // reads one band of the matrix at a time); 1 = the same rows, block b
+    // starting at its (b mod n)-th of n groups and wrapping around to the
+    // first; 2 = one run of consecutive rows per phase.
+    int order;
 };
 
 bool flat_policy_supported(const FlatPolicy& p);

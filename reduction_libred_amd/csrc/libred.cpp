@@ -253,22 +253,23 @@ red_status get_scratch(int dev, hipStream_t stream, size_t bytes, void** out) {
 // 8 rows in flight each are best on average. Short-wide matrices (more than
 // 1024 blocks of 256 columns) instead read 4 KiB of a row per wave and
 // 2 rows at a time, without prefetch (256 x 1M: 5.9 -> 7.1 TB/s).
-constexpr libred::ColsPolicy kDefaultCols = {8, 1, 512, 0, 1, 1, 0};
+constexpr libred::ColsPolicy kDefaultCols = {8, 1, 512, 0, 1, 1, 0, 0};
 
 // The read probe's default shape: the fastest of its sweep on a 1 GiB buffer.
 constexpr red_read_shape kDefaultReadShape = {64, 2, 8, 1, 2};
 // The copy probe's default shape (single-wave blocks, next tile in flight).
 constexpr red_read_shape kDefaultCopyShape = {64, 2, 8, 1, 2};
-constexpr libred::ColsPolicy kWideCols = {2, 1, 1024, 0, 4, 0, 0};
+constexpr libred::ColsPolicy kWideCols = {2, 1, 1024, 0, 4, 0, 0, 0};
 // Columns read one element per lane (rows not 16-byte aligned, or cols or ld
 // not a multiple of 4) with at least 64 of them: two loads per row per lane,
 // 2048 waves (a sweep over 4097, 1001, 257 and 65 columns: 2.3-2.8 ->
 // 3.4-5.3 TB/s against the vector default).
-constexpr libred::ColsPolicy kScalarCols = {8, 1, 2048, 0, 2, 0, 0};
+constexpr libred::ColsPolicy kScalarCols = {8, 1, 2048, 0, 2, 0, 0, 0};
 
 libred::ColsPolicy to_cols(const red_cols_policy* p) {
     if (!p) return kDefaultCols;
-    libred::ColsPolicy c = {p->unroll, p->nontemporal, p->target_waves, p->vec, p->width, p->prefetch, p->fold};
+    libred::ColsPolicy c = {p->unroll, p->nontemporal, p->target_waves, p->vec, p->width, p->prefetch, p->fold,
+                            p->order};
     return c;
 }
 
@@ -738,6 +739,7 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     L.tail = nullptr;
     L.rot = 0;
     L.head = nullptr;
+    L.order = 0;
     // A contiguous matrix may be viewed with m consecutive rows as one row
     // of m * cols columns (see fold_rows): for a width that is not a
     // multiple of 4 this makes every view row start 16-byte aligned, so four
@@ -802,6 +804,15 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         if (nchunks < 1) nchunks = 1;
     }
     L.nchunks = nchunks;
+    // Row order: rotated starts at pitches the memory channels alias on
+    // (see kRotateRowsPitchFactorA), else one band at a time.
+    if (p.order > 0)
+        L.order = p.order - 1;
+    else
+        L.order = rows > 1 && (ld % libred::table::kRotateRowsPitchFactorA == 0 ||
+                               ld % libred::table::kRotateRowsPitchFactorB == 0)
+                      ? 1
+                      : 0;
     L.partials = nullptr;
     if (nchunks > 1 || L.fold_m > 1 || L.rot > 0) {
         st = get_scratch(dev, stream, nchunks * cols * 8, &L.partials);
@@ -1125,6 +1136,7 @@ void red_default_cols_policy(red_cols_policy* p) {
     p->width = kDefaultCols.width;
     p->prefetch = kDefaultCols.prefetch;
     p->fold = kDefaultCols.fold;
+    p->order = kDefaultCols.order;
 }
 
 red_status red_cols_sum_f32_with(const float* x, size_t rows, size_t cols, size_t ld, float* out,

@@ -738,13 +738,17 @@ COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260)
               (301, 1028, 1032), (77, 2304, 2304), (1000, 3, 3), (777, 33, 33), (500, 65, 65), (3000, 17, 17),
               (200, 257, 257), (99, 1, 1), (4000, 20, 24), (64, 100, 100),
               (1001, 6, 6), (4001, 10, 10), (37, 2, 2), (20_003, 7, 7), (9, 4097, 4097), (5, 3, 3),
-              (1000, 260, 260), (333, 516, 516), (41, 300, 300), (3001, 33, 33), (70, 65, 65), (63, 97, 97)]
+              (1000, 260, 260), (333, 516, 516), (41, 300, 300), (3001, 33, 33), (70, 65, 65), (63, 97, 97),
+              (300, 1020, 1020), (129, 2040, 2040), (500, 1000, 1020), (77, 765, 765), (45, 1028, 1028),
+              (1203, 255, 255), (31, 510, 514)]
 COL_POLICIES = (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=16, nontemporal=0),
                 dict(width=2), dict(width=4, unroll=2), dict(width=4, unroll=16, nontemporal=0, target_waves=7),
                 dict(prefetch=1), dict(prefetch=1, unroll=1, target_waves=7), dict(width=4, unroll=2, prefetch=1),
                 dict(width=2, unroll=16, prefetch=1, nontemporal=0), dict(fold=1), dict(fold=16),
                 dict(fold=3, unroll=1, target_waves=7), dict(fold=8, width=4, unroll=2, prefetch=0),
-                dict(fold=32), dict(fold=64, unroll=2))
+                dict(fold=32), dict(fold=64, unroll=2), dict(order=1), dict(order=2),
+                dict(order=2, unroll=1, target_waves=7, prefetch=1), dict(order=3),
+                dict(order=3, width=4, unroll=2, target_waves=7), dict(order=3, fold=16, prefetch=0))
 
 
 @pytest.mark.parametrize("rows,cols,ld", COL_SHAPES)
@@ -769,12 +773,14 @@ def test_cols(rows, cols, ld):
 
 
 @pytest.mark.parametrize("rows,cols", [(40_001, 257), (33_000, 1000), (32_810, 1025), (32_768, 300),
-                                       (40_000, 1026), (32_800, 2049)])
+                                       (40_000, 1026), (32_800, 2049), (32_790, 1020), (32_801, 1028)])
 def test_cols_line_views(rows, cols):
     # Widths of at least 256 that are not a multiple of 32, with enough rows
     # for the default to read the matrix through 32-row views (16 at 1026
     # columns), each view row whole 128-byte lines; the rows past the last
     # whole view (1-31 of them here, or none) are added in the second pass.
+    # At 1020 and 1028 columns the view pitch is a multiple of 255 or 257
+    # floats, so the default sweeps the view rows in rotated order.
     rng = np.random.default_rng(rows + 3 * cols)
     a = rng.standard_normal((rows, cols)).astype(np.float32)
     a[(np.arange(cols) * 7919) % rows, np.arange(cols)] = 50.0 + np.arange(cols) % 89
