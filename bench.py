@@ -235,7 +235,7 @@ def run_col_orders(args, torch, rl, W, timer, dev):
 
 def read_shapes():
     """Every launch shape of the read probe: block 64 / 256 / 1024, 1-16 waves
-    per CU, 4-32 loads in flight per lane, non-temporal or not, three layouts
+    per CU, 4-32 loads in flight per lane, non-temporal or not, four layouts
     (the shapes that fit in registers without spilling)."""
     for block in (64, 256, 1024):
         per_block = block // 64
@@ -243,8 +243,8 @@ def read_shapes():
             if waves < per_block or waves % per_block:
                 continue
             for unroll in (4, 8, 16, 32):
-                for layout in (0, 1, 2):
-                    if block == 1024 and (unroll > 16 or (layout == 2 and unroll > 8)):
+                for layout in (0, 1, 2, 3):
+                    if block == 1024 and (unroll > 16 or (layout >= 2 and unroll > 8)):
                         continue
                     for nt in (0, 1):
                         yield dict(block=block, blocks_per_cu=waves // per_block, unroll=unroll, nontemporal=nt,

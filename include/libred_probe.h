@@ -25,10 +25,11 @@ red_status red_probe_copy_f32(const float *x, float *y, size_t n, hipStream_t st
  * Launch shape of the load-only read probe: `block` threads per block (64,
  * 256 or 1024), `blocks_per_cu` blocks per compute unit (1..32), `unroll`
  * 16-byte loads in flight per lane (4, 8, 16 or 32; with 1024-thread blocks
- * at most 16, and at most 8 with layout 2), `nontemporal` (0 or 1: the
- * streaming hint on the loads), `layout` (0 grid-stride, 1 wave tiles of
+ * at most 16, and at most 8 with layouts 2 and 3), `nontemporal` (0 or 1:
+ * the streaming hint on the loads), `layout` (0 grid-stride, 1 wave tiles of
  * 64 * unroll vectors, 2 wave tiles with the next tile's loads in flight
- * while the current one is folded).
+ * while the current one is folded, 3 as 2 with each XCD's blocks (block b
+ * runs on XCD b mod 8) reading one contiguous eighth of the tiles).
  */
 typedef struct red_read_shape {
     int block;

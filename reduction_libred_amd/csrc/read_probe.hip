@@ -18,7 +18,11 @@
 //   1 wave tiles: the buffer is cut into tiles of 64 * UNROLL vectors; wave
 //     w reads tiles w, w + nwaves, ... whole;
 //   2 wave tiles with the next tile's loads issued before the current tile
-//     is folded (two register buffers).
+//     is folded (two register buffers);
+//   3 as 2, but each XCD reads one contiguous eighth of the tiles: blocks
+//     are dispatched to the eight XCDs round robin (block b on XCD b mod 8),
+//     so the blocks b = x mod 8 take tiles [x T / 8, (x + 1) T / 8) of the T
+//     tiles, their waves round robin.
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -64,30 +68,39 @@ __global__ __launch_bounds__(BLOCK) void read_probe_kernel(const u32x4* __restri
         const size_t nwaves = (size_t)gridDim.x * W;
         const size_t ntiles = nvec / TILE;
         size_t t = (size_t)blockIdx.x * W + wave;
+        // Tiles t, t + step, ... below t1.
+        size_t t1 = ntiles, step = nwaves;
+        if constexpr (LAYOUT == 3) {
+            const size_t G = gridDim.x, xcd = blockIdx.x % 8;
+            const size_t xblocks = (G + 7 - xcd) / 8;  // blocks on this XCD
+            t = xcd * ntiles / 8 + (blockIdx.x / 8) * W + wave;
+            t1 = (xcd + 1) * ntiles / 8;
+            step = xblocks * W;
+        }
         if constexpr (LAYOUT == 1) {
-            for (; t < ntiles; t += nwaves) {
+            for (; t < t1; t += step) {
                 u32x4 v[UNROLL];
                 read_tile<UNROLL, NT>(v, xv + t * TILE + lane);
                 acc ^= fold_tile_xor<UNROLL>(v);
             }
-        } else if (t < ntiles) {
+        } else if (t < t1) {
             u32x4 a[UNROLL], b[UNROLL];
             read_tile<UNROLL, NT>(a, xv + t * TILE + lane);
             while (true) {
-                if (t + nwaves >= ntiles) {
+                if (t + step >= t1) {
                     acc ^= fold_tile_xor<UNROLL>(a);
                     break;
                 }
-                read_tile<UNROLL, NT>(b, xv + (t + nwaves) * TILE + lane);
+                read_tile<UNROLL, NT>(b, xv + (t + step) * TILE + lane);
                 acc ^= fold_tile_xor<UNROLL>(a);
-                t += nwaves;
-                if (t + nwaves >= ntiles) {
+                t += step;
+                if (t + step >= t1) {
                     acc ^= fold_tile_xor<UNROLL>(b);
                     break;
                 }
-                read_tile<UNROLL, NT>(a, xv + (t + nwaves) * TILE + lane);
+                read_tile<UNROLL, NT>(a, xv + (t + step) * TILE + lane);
                 acc ^= fold_tile_xor<UNROLL>(b);
-                t += nwaves;
+                t += step;
             }
         }
         // Vectors after the last whole tile.
@@ -106,7 +119,7 @@ __global__ __launch_bounds__(BLOCK) void read_probe_kernel(const u32x4* __restri
 // second register buffer.
 template <int BLOCK, int UNROLL, int LAYOUT>
 constexpr bool rp_fits() {
-    return BLOCK < 1024 || (LAYOUT == 2 ? UNROLL <= 8 : UNROLL <= 16);
+    return BLOCK < 1024 || (LAYOUT >= 2 ? UNROLL <= 8 : UNROLL <= 16);
 }
 
 template <int BLOCK, int UNROLL, int LAYOUT>
@@ -143,6 +156,7 @@ hipError_t launch_rp_b(const u32x4* xv, size_t nvec, unsigned int* sink, int gri
         case 0: return launch_rp_u<BLOCK, 0>(xv, nvec, sink, grid, s, stream);
         case 1: return launch_rp_u<BLOCK, 1>(xv, nvec, sink, grid, s, stream);
         case 2: return launch_rp_u<BLOCK, 2>(xv, nvec, sink, grid, s, stream);
+        case 3: return launch_rp_u<BLOCK, 3>(xv, nvec, sink, grid, s, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -223,8 +237,8 @@ hipError_t launch_copy_probe(const void* x, void* y, size_t nvec, int grid, cons
 bool read_shape_supported(const ReadShape& s) {
     const bool block = s.block == 64 || s.block == 256 || s.block == 1024;
     const bool unroll = s.unroll == 4 || s.unroll == 8 || s.unroll == 16 || s.unroll == 32;
-    const bool fits = s.block < 1024 || (s.layout == 2 ? s.unroll <= 8 : s.unroll <= 16);
-    return block && unroll && fits && s.layout >= 0 && s.layout <= 2 && s.blocks_per_cu >= 1 &&
+    const bool fits = s.block < 1024 || (s.layout >= 2 ? s.unroll <= 8 : s.unroll <= 16);
+    return block && unroll && fits && s.layout >= 0 && s.layout <= 3 && s.blocks_per_cu >= 1 &&
            s.blocks_per_cu <= 32 && (s.nontemporal == 0 || s.nontemporal == 1);
 }
 

@@ -200,7 +200,7 @@ def test_probe_argument_errors():
     assert L.red_probe_read_ceiling(_p(A), 60, ctypes.byref(sh), _p(B), None) == INVALID
     assert L.red_probe_read_ceiling(_p(A), 64, ctypes.byref(sh), None, None) == INVALID
     assert L.red_probe_read_ceiling(_p(A), 64, None, _p(A + 8), None) == INVALID      # sink inside x
-    for field, value in (("block", 128), ("unroll", 12), ("layout", 3), ("blocks_per_cu", 0),
+    for field, value in (("block", 128), ("unroll", 12), ("layout", 4), ("blocks_per_cu", 0),
                          ("nontemporal", 2)):
         bad = rl.red_default_read_shape()
         setattr(bad, field, value)
@@ -209,11 +209,13 @@ def test_probe_argument_errors():
     assert L.red_probe_read_ceiling(_p(A), 64, ctypes.byref(bad), _p(B), None) == INVALID
     bad = rl.ReadShape(1024, 1, 16, 1, 2)
     assert L.red_probe_read_ceiling(_p(A), 64, ctypes.byref(bad), _p(B), None) == INVALID
+    bad = rl.ReadShape(1024, 1, 16, 1, 3)
+    assert L.red_probe_read_ceiling(_p(A), 64, ctypes.byref(bad), _p(B), None) == INVALID
 
 
 def test_read_shapes_default_is_supported():
     d = rl.red_default_read_shape().as_dict()
-    assert d["block"] in (64, 256, 1024) and d["unroll"] in (4, 8, 16, 32) and 0 <= d["layout"] <= 2
+    assert d["block"] in (64, 256, 1024) and d["unroll"] in (4, 8, 16, 32) and 0 <= d["layout"] <= 3
 
 
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,

@@ -266,8 +266,8 @@ def test_first_call_on_a_fresh_stream_during_another_capture():
 def _read_shapes():
     for block in (64, 256, 1024):
         for unroll in (4, 8, 16, 32):
-            for layout in (0, 1, 2):
-                if block == 1024 and (unroll > 16 or (layout == 2 and unroll > 8)):
+            for layout in (0, 1, 2, 3):
+                if block == 1024 and (unroll > 16 or (layout >= 2 and unroll > 8)):
                     continue
                 for nt in (0, 1):
                     yield dict(block=block, blocks_per_cu=1 if block == 1024 else 3, unroll=unroll,
