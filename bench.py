@@ -165,8 +165,8 @@ def run_ablation(args, torch, rl, W, timer, dev):
 # LDS-staged rows, folded column views), multiples of 4 (packed and staged
 # rows, four columns per lane), and long rows (one wave per row; odd lengths
 # read through their aligned covers).
-WIDTHS = [1, 3, 4, 7, 16, 17, 33, 64, 65, 100, 256, 260, 512, 1000, 1020, 1023, 1025, 2049, 4096, 4097,
-          6000, 16385, 50257]
+WIDTHS = [1, 3, 4, 7, 12, 16, 17, 24, 32, 33, 64, 65, 100, 256, 260, 512, 1000, 1020, 1023, 1025, 2049, 4096,
+          4097, 6000, 16385, 50257]
 
 
 def run_widths(args, torch, rl, W, timer, dev):

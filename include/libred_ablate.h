@@ -89,7 +89,7 @@ typedef struct red_flat_policy {
  * gives the LDS-staged kernel tiles of that many 16-byte vectors per lane
  * when that is more than the rows need, and the LDS-staged kernel always
  * loads non-temporally, whatever `nontemporal` says):
- *   0  the library's choice: rows of 1 to 31 floats of a contiguous,
+ *   0  the library's choice: rows of 1 to 32 floats of a contiguous,
  *      16-byte aligned matrix go to the narrow kernel (17); other rows of
  *      fewer than 1024 floats go to the
  *      LDS-staged kernel when they are contiguous or their gaps (ld - cols)
@@ -118,11 +118,15 @@ typedef struct red_flat_policy {
  *      16-byte vectors, read through LDS when they span several; tiles of
  *      at least 8 coalesced loads per lane; the library's choice), else as
  *      0;
- * and `defer` (the LDS-staged kernel): 0 = a wave keeps its row results in
- * LDS and stores them after its last tile when they fit beside its staging
- * tile in its share of the CU's LDS (the CU's LDS over the waves the grid
- * puts on each CU, and at most one block's limit), else stores each tile's
- * results as the tile is reduced; 1 = always as each tile is reduced. The
+ * and `defer`: for the LDS-staged kernel, 0 or 2 = a wave keeps its row
+ * results in LDS and stores them after its last tile when they fit beside
+ * its staging tile in its share of the CU's LDS (the CU's LDS over the waves
+ * the grid puts on each CU, and at most one block's limit), else stores
+ * each tile's results as the tile is reduced; 1 = always as each tile is
+ * reduced; for the narrow kernel, 0 = a wave holds the results of several
+ * tiles (up to 48 KiB) in LDS and stores them in one burst, for rows of 6
+ * and of 8 to 32 floats, and stores each tile's results as the tile is
+ * reduced otherwise; 1 = always as each tile is reduced; 2 = always held. The
  * results are the same either way; and `lines` (the LDS-staged kernel, a
  * contiguous, 16-byte aligned matrix): 0 = the library's choice (1 for rows
  * of fewer than 32 floats), 1 = tiles of a multiple of 32 rows (whole

@@ -42,9 +42,9 @@ constexpr size_t kPackedMaxCols = 512;
 // better (narrow sweep, widths 1-16); the waves by width below add more.
 // Widths 17-31 on 1024 waves, medians of three alternating rounds, against
 // the staged kernel: odd widths 5.7-5.8 -> 6.0-6.3 TB/s (17: 5.8 -> 6.0-6.1,
-// 31: 5.8 -> 6.3), widths 18-30 level to 6% faster; 32 floats stay staged
-// (vector reads from LDS: 6.4 against 5.9-6.0).
-constexpr size_t kNarrowDefaultMaxCols = 31;
+// 31: 5.8 -> 6.3), widths 18-30 level to 6% faster. 32 floats, with the
+// results held (below): 7.2 / 6.8 TB/s (sum / max) against 6.3-6.4 staged.
+constexpr size_t kNarrowDefaultMaxCols = 32;
 // Waves by width, from medians of three alternating rounds of sum and max
 // (the narrow grid sweep: 256-1536 waves, then 512 against 1024 for every
 // width once the result stores were non-temporal). 512 waves, TB/s of input
@@ -57,7 +57,24 @@ constexpr size_t kNarrowDefaultMaxCols = 31;
 // against 6.2).
 constexpr int kNarrowWaves[kNarrowDefaultMaxCols + 1] = {
     1024, 512,  1024, 512,  1024, 512,  1024, 512,  1024, 512,  512,  512,  1024, 512,  512,  512,
-    1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
+    1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024, 1024};
+// Widths whose waves hold their results in LDS and store them in bursts,
+// on kNarrowHoldWaves waves. TB/s of input plus output, medians of three
+// alternating rounds, storing each tile's results (the waves above) against
+// holding them on 512 waves, sum / max: 6 floats 5.9-6.0 / 6.2 -> 6.3-6.4 /
+// 6.4-6.5 (two machines), 8: 6.1 / 6.1 -> 6.7 / 6.7, 12: 6.0 / 5.9 -> 6.8 /
+// 6.9, 16: 6.0 / 6.0 -> 7.0 / 7.0, 21: 6.1 / 6.1 -> 7.1 / 6.5, 25: 6.2 /
+// 6.1 -> 6.9 / 6.8, 31: 6.2 / 6.2 -> 6.8 / 6.5; every width from 8 to 32
+// gains for both operators (9-15 on a second machine too: +3-10%). Not
+// held: 7 floats (+2% on one machine, -5% on another), and below 6 floats,
+// whose results are a fifth of the traffic or more (1 float: 6.1 -> 5.5, 3:
+// 6.5 -> 6.0, 5: 6.3 -> 5.9 on one machine, level on another). Holding on
+// 1024 waves (four per CU where the LDS allows it) ran 2-16% slower than on
+// 512, and 768 waves slower still.
+constexpr bool kNarrowHold[kNarrowDefaultMaxCols + 1] = {
+    false, false, false, false, false, false, true, false, true, true, true, true, true, true, true, true, true,
+    true,  true,  true,  true,  true,  true,  true, true,  true, true, true, true, true, true, true, true};
+constexpr int kNarrowHoldWaves = 512;
 
 // ------------------------------------------------------------ rows: staged tile
 // Tile sizes by the floats a tile's rows span: up to 1024 -> 4 loads per

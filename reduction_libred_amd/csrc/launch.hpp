@@ -64,7 +64,9 @@ struct RowsLaunch {
                                //   dynamic LDS and stores them after the wave's last tile
     int staged_spread;  // the LDS-staged kernel's element reads start at a different element
                         //   in each row of a pass (rows at a stride of a multiple of 16)
-    int narrow;         // the register kernel for narrow rows (rows_narrow.hip), `grid` waves
+    int narrow;         // the register kernel for narrow rows (rows_narrow.hip), `grid` waves:
+                        //   1 = results stored as each tile is folded, 2 = held in LDS and
+                        //   stored in bursts
 };
 
 // Narrow rows: a contiguous, 16-byte aligned matrix of rows of 1 to
@@ -75,8 +77,11 @@ struct RowsLaunch {
 constexpr int kNarrowTileLoads = 8;
 constexpr size_t kNarrowMaxCols = 32;
 size_t rows_narrow_tile_rows(size_t cols);
+// Static LDS bytes of one narrow block (0 for another width); with hold,
+// the block keeps its results in LDS and stores them in bursts.
+size_t rows_narrow_lds_bytes(size_t cols, bool hold);
 hipError_t launch_rows_narrow(int op, const float* x, size_t rows, size_t cols, float* out, int grid, bool nt,
-                              hipStream_t stream);
+                              bool hold, hipStream_t stream);
 constexpr size_t kMaxSplitPartials = 32768;
 
 // Library-owned scratch of one (device, stream): a completion counter that

@@ -391,11 +391,24 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // side by side (short_rows 17).
     // The default for rows of up to 31 floats, on the measured number of
     // waves for the width (the table).
+    // Each wave holds its results in LDS and stores them in bursts where
+    // the table says so (defer 0), always (defer 2) or never (defer 1); by
+    // default on the table's waves for the width, no more than the CUs hold
+    // at once with that LDS.
     const bool narrow_default = p.short_rows == 0 && cols <= T::kNarrowDefaultMaxCols;
     if (dense && libred::rows_narrow_tile_rows(cols) > 0 && (p.short_rows == 17 || narrow_default)) {
         const size_t steps = rows / libred::rows_narrow_tile_rows(cols);
-        const size_t cap = pol != nullptr ? (size_t)p.max_blocks : (size_t)T::kNarrowWaves[cols];
-        L.narrow = 1;
+        const bool hold = (p.defer == 2 || (p.defer == 0 && T::kNarrowHold[cols])) &&
+                          libred::rows_narrow_lds_bytes(cols, true) <= info.lds_per_block;
+        size_t cap = pol != nullptr ? (size_t)p.max_blocks
+                     : hold         ? (size_t)T::kNarrowHoldWaves
+                                    : (size_t)T::kNarrowWaves[cols];
+        if (pol == nullptr && hold) {
+            const size_t lds = libred::rows_narrow_lds_bytes(cols, true);
+            const size_t resident = (size_t)info.cu_count * (info.lds_per_cu / lds);
+            if (cap > resident && resident > 0) cap = resident;
+        }
+        L.narrow = hold ? 2 : 1;
         L.grid = (int)(steps == 0 ? 1 : steps < cap ? steps : cap);
         const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
         if (e != hipSuccess) return fail(e, RED_ERR_HIP);
@@ -512,7 +525,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
                 return need <= info.lds_per_cu / ((g + info.cu_count - 1) / info.cu_count) &&
                        need <= info.lds_per_block;
             };
-            if (u == 16 && p.defer == 0 && cols < T::kHoldSmallTileBelowCols && base_u <= 8 &&
+            if (u == 16 && p.defer != 1 && cols < T::kHoldSmallTileBelowCols && base_u <= 8 &&
                 !holds(16, T::kStagedBigTileWaves) && holds(8, T::kStagedBigTileWaves) &&
                 pass_use(8) >= pass_use(16) - T::kHoldSmallTileSlack) {
                 u = 8;
@@ -541,7 +554,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         // Rows of 960 floats and more are left out: with a row or two per
         // tile, holding measured 1-10% slower there (and 5-20% faster on
         // narrower rows).
-        if (p.defer == 0 && cols < T::kHoldBelowCols) {
+        if (p.defer != 1 && cols < T::kHoldBelowCols) {
             const size_t results = (tiles + L.grid - 1) / L.grid * L.staged_rows;
             const size_t waves_per_cu = ((size_t)L.grid + info.cu_count - 1) / info.cu_count;
             const size_t stage = (size_t)64 * L.staged_u * 16;  // 64 lanes x staged_u 16-byte vectors

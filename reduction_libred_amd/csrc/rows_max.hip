@@ -7,7 +7,8 @@ namespace libred {
 
 hipError_t launch_rows_max_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,
                                const RowsLaunch& L, const RowsPolicy& p, hipStream_t stream) {
-    if (L.narrow) return launch_rows_narrow(1, x, rows, cols, out, L.grid, p.nontemporal != 0, stream);
+    if (L.narrow)
+        return launch_rows_narrow(1, x, rows, cols, out, L.grid, p.nontemporal != 0, L.narrow == 2, stream);
     return rows_op<MaxF32>(x, rows, cols, ld, out, L, p, stream);
 }
 

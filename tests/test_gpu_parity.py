@@ -611,7 +611,8 @@ ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023
               (1000, 4), (777, 16), (301, 32), (129, 128), (77, 200), (33, 8), (1025, 12), (70, 512),
               (200, 33), (100, 511), (1000, 100), (3000, 2), (1, 3), (2, 2), (5, 6), (1001, 6),
               (1, 2048), (2, 1023), (3, 1025), (300, 7), (9, 510), (20_001, 5), (5, 1021), (40, 700), (3, 1023),
-              (1, 5000), (2, 1030), (7, 1031), (1, 16), (17, 16)]
+              (1, 5000), (2, 1030), (7, 1031), (1, 16), (17, 16), (100_003, 16), (60_001, 7), (50_000, 6),
+              (40_001, 25), (30_007, 12)]
 ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1, max_blocks=3, short_rows=1),
                 dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
                 dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0),
@@ -624,7 +625,9 @@ ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1,
                 dict(short_rows=17), dict(short_rows=17, max_blocks=3, nontemporal=0),
                 dict(lines=1), dict(lines=1, unroll=16, max_blocks=3), dict(lines=2, unroll=8),
                 dict(short_rows=3, lines=1), dict(short_rows=11, lines=1, unroll=8),
-                dict(short_rows=17, max_blocks=1))
+                dict(short_rows=17, max_blocks=1), dict(short_rows=17, defer=2),
+                dict(short_rows=17, defer=2, max_blocks=3), dict(short_rows=17, defer=1), dict(defer=2),
+                dict(short_rows=17, defer=2, max_blocks=5, nontemporal=0))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
@@ -847,7 +850,9 @@ def _check_sums(got, S, A, what):
 
 
 @pytest.mark.parametrize("rows,cols,ld", [(300, 3, 3), (300, 16, 16), (50, 700, 700), (20, 4096, 4096),
-                                          (100, 7, 9), (100, 16, 20), (77, 33, 33), (5, 1021, 1021)])
+                                          (100, 7, 9), (100, 16, 20), (77, 33, 33), (5, 1021, 1021),
+                                          (3000, 17, 17), (2000, 32, 32), (1500, 21, 21), (1200, 19, 19),
+                                          (900, 23, 23), (800, 31, 31), (1000, 24, 24), (5000, 7, 7)])
 def test_rows_nonfinite(rows, cols, ld):
     """NaN and infinities through every row kernel (LDS-staged, packed with
     16-byte and element units, one wave per row): a sum is NaN or the
@@ -858,7 +863,8 @@ def test_rows_nonfinite(rows, cols, ld):
     full[:, :cols] = a
     S, A = oracle.rows_sum_f32(a)
     M = oracle.rows_max_f32(a)
-    for p in (None, dict(short_rows=1), dict(short_rows=2)):
+    for p in (None, dict(short_rows=1), dict(short_rows=2), dict(short_rows=17, defer=1),
+              dict(short_rows=17, defer=2, max_blocks=3)):
         say(f"rows nonfinite {rows}x{cols} ld={ld} policy={p}")
         x = device_view(full, 0)[:, :cols]
         s_ = rl.red_rows_sum_f32(x, policy=p)
@@ -866,6 +872,36 @@ def test_rows_nonfinite(rows, cols, ld):
         torch.cuda.synchronize()
         _check_sums(s_.cpu().numpy().astype(np.float64), S, A, p)
         assert np.array_equal(m_.cpu().numpy(), M), p
+
+
+def test_rows_signalling_nan():
+    # Signalling NaNs (quiet bit clear, either sign) never win a row's max,
+    # whichever way the kernel folds the row (compare-and-select, or a
+    # maximum instruction that quiets its inputs first), and make the sum
+    # NaN like any other NaN.
+    rng = np.random.default_rng(4242)
+    snans = np.array([0x7F800001, 0x7FA00000, 0xFF800123, 0x7FBFFFFF], np.uint32)
+    for cols in list(range(1, 34)) + [64]:
+        rows = 1500 if cols > 8 else 6000
+        a = rng.standard_normal((rows, cols)).astype(np.float32)
+        bits = a.view(np.uint32)
+        k = max(1, a.size // 50)
+        idx = rng.integers(0, a.size, k)
+        bits.reshape(-1)[idx] = snans[np.arange(k) % snans.size]
+        bits[3, :] = snans[np.arange(cols) % snans.size]          # a row of signalling NaNs only
+        a[5, :] = -np.inf
+        a[7, cols - 1] = np.inf
+        S, A = oracle.rows_sum_f32(a)
+        M = oracle.rows_max_f32(a)
+        assert M[3] == -np.inf and not np.isnan(M).any()
+        x = torch.from_numpy(a).to(DEV)
+        for p in (None, dict(short_rows=17, defer=1), dict(short_rows=17, defer=2), dict(short_rows=1)):
+            say(f"rows signalling NaN {rows}x{cols} policy={p}")
+            s_ = rl.red_rows_sum_f32(x, policy=p)
+            m_ = rl.red_rows_max_f32(x, policy=p)
+            torch.cuda.synchronize()
+            _check_sums(s_.cpu().numpy().astype(np.float64), S, A, (cols, p))
+            assert np.array_equal(m_.cpu().numpy(), M), (cols, p)
 
 
 @pytest.mark.parametrize("rows,cols,ld", [(1000, 3, 3), (1000, 64, 64), (999, 7, 9), (97, 1031, 1031),
@@ -1267,11 +1303,13 @@ def test_full_rows_short_1gib():
     # The 1 GiB rows workload viewed as (2^28 // cols) x cols rows, the shapes
     # the widths benchmark times. Every row of every view is compared with
     # the oracle. By default the LDS-staged kernel holds each wave's row
-    # results until its last tile; defer=1 stores them tile by tile. Each row
-    # is reduced the same way in both, so the floats must also be identical.
+    # results until its last tile, and the narrow kernel (from 6 floats)
+    # holds them for a burst of tiles; defer=1 stores them tile by tile. Each
+    # row is reduced the same way in both, so the floats must also be
+    # identical.
     a, x = _load("rows_f32_65536x4096")
     flat = a.reshape(-1)
-    for cols in (1, 3, 4, 7, 16, 17, 64, 100, 256, 1000):
+    for cols in (1, 3, 4, 7, 12, 16, 17, 21, 32, 64, 100, 256, 1000):
         rows = flat.size // cols
         say(f"red_rows_sum_f32 / red_rows_max_f32 rows_f32_65536x4096 as {rows}x{cols}, held and tile by tile")
         v = x.view(-1)[: rows * cols].view(rows, cols)
