@@ -202,8 +202,9 @@ def run_widths(args, torch, rl, W, timer, dev):
 
 
 # Widths whose rows (or 32-row views) have a pitch that is a multiple of 255
-# or 257 floats, and neighbours that are not.
-ORDER_WIDTHS = [1016, 1020, 1024, 1028, 2040, 2044, 3060, 4080, 5100, 8160, 765, 4096]
+# or 257 floats, and neighbours that are not; then narrow matrices whose wave
+# loads cover several rows, with and without whole 128-byte lines per load.
+ORDER_WIDTHS = [1016, 1020, 1024, 1028, 2040, 2044, 3060, 4080, 5100, 8160, 765, 4096, 3, 4, 12, 16, 17, 24]
 COL_ORDERS = (("band", dict(order=1)), ("rotated", dict(order=2)), ("chunks", dict(order=3)), ("default", None))
 
 

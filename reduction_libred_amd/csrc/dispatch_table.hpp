@@ -198,6 +198,19 @@ constexpr double kFoldGain = 0.05;
 // that scan the rotated order ran up to 3% slower, so it stays off there.
 constexpr size_t kRotateRowsPitchFactorA = 255;
 constexpr size_t kRotateRowsPitchFactorB = 257;
+// A narrow matrix (or view) whose wave loads each cover several rows
+// (ngroups < 64) takes one run of consecutive rows per phase when such a
+// load's rows do not span whole lines of this many bytes: in the band order
+// the line at each boundary between two loads' rows is read by two waves of
+// different phases (on different XCDs) and fetched twice (1.07-1.14 times
+// the input at 3, 12, 17 and 24 columns); in a run the next load is the same
+// wave's. Sums, TB/s of input, band against runs: 3 columns 6.1 -> 6.9, 5:
+// 6.5 -> 7.0, 6: 6.1 -> 6.9, 9: 6.1 -> 6.9, 11: 6.1 -> 6.9, 12: 6.0 -> 6.8,
+// 13: 6.3 -> 6.8, 17: 6.0 -> 6.6, 18: 6.1 -> 7.0, 20: 6.5 -> 6.9, 24: 6.5 ->
+// 6.9, 25: 6.1 -> 6.5 (maxima alike); where the loads span whole lines (1,
+// 2, 4, 8, 16 and 32 columns, and the line-spanning views of 7, 15, 21-23
+// and 27-31 columns) runs read 1-4% slower, so the band stays there.
+constexpr size_t kLineBytes = 128;
 
 // ------------------------------------------------------------ columns: shapes
 // Short-wide matrices (more than this many blocks of 256 columns), and rows

@@ -818,14 +818,18 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     }
     L.nchunks = nchunks;
     // Row order: rotated starts at pitches the memory channels alias on
-    // (see kRotateRowsPitchFactorA), else one band at a time.
+    // (see kRotateRowsPitchFactorA); runs of rows where a load covers rows
+    // that do not span whole lines (see kLineBytes); else one band at a time.
+    const size_t load_rows = 64 / L.ngroups;  // rows per wave load
     if (p.order > 0)
         L.order = p.order - 1;
+    else if (rows > 1 && (ld % libred::table::kRotateRowsPitchFactorA == 0 ||
+                          ld % libred::table::kRotateRowsPitchFactorB == 0))
+        L.order = 1;
+    else if (rows > 1 && L.ngroups < 64 && load_rows * ld * sizeof(float) % libred::table::kLineBytes != 0)
+        L.order = 2;
     else
-        L.order = rows > 1 && (ld % libred::table::kRotateRowsPitchFactorA == 0 ||
-                               ld % libred::table::kRotateRowsPitchFactorB == 0)
-                      ? 1
-                      : 0;
+        L.order = 0;
     L.partials = nullptr;
     if (nchunks > 1 || L.fold_m > 1 || L.rot > 0) {
         st = get_scratch(dev, stream, nchunks * cols * 8, &L.partials);
