@@ -146,6 +146,15 @@ constexpr size_t kPartialTileMaxVectors = 384;
 constexpr int kCoverUnroll = 8;
 constexpr int kCoverWavesBelowLong = 32768;
 constexpr int kCoverWavesLong = 1024;
+// Aligned rows under kRowsLongFromCols floats whose last round of loads, in
+// the tiles their shape above gives them, is at most this share of a tile
+// full are read as covers too, one unconditional tile of 8 loads where the
+// row fits, on up to 32768 waves (aligned rows just over 1024 floats paid a
+// nearly empty second round per row: 1028: 4.9 -> 6.3, 1060: 5.1 -> 6.4,
+// 1200: 5.6 -> 6.5, 1500: 6.3 -> 6.6, 2052: 6.4 -> 6.7, 4100: 6.3 -> 6.8
+// TB/s; with a last round 76-100% full (1800, 2048, 6000 floats) the
+// covers ran 2-9% slower; 2500 floats, 44%: 1% slower).
+constexpr double kCoverLastRoundMax = 0.5;
 
 // ------------------------------------------------------------ rows: split
 // Fewer than kSplitRowsBelow rows of at least kSplitMinCols floats are cut

@@ -612,7 +612,12 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         // elements. Its defaults by row length come from a sweep over
         // unaligned rows of 1025 to 50257 floats.
         const bool misaligned = !aligned(x, 16) || (rows > 1 && ld % 4 != 0);
-        L.cover = cols >= 16 && (p.cover == 2 || (p.cover == 0 && misaligned)) ? 1 : 0;
+        // Aligned rows whose last round of loads would be at most half a
+        // tile take the covered kernel's shape too (see kCoverLastRoundMax).
+        const size_t nvec = cols / 4, tile_vecs = (size_t)64 * p.unroll;
+        const bool thin_last = pol == nullptr && cols < T::kRowsLongFromCols && nvec % tile_vecs != 0 &&
+                               (double)(nvec % tile_vecs) <= T::kCoverLastRoundMax * (double)tile_vecs;
+        L.cover = cols >= 16 && (p.cover == 2 || (p.cover == 0 && (misaligned || thin_last))) ? 1 : 0;
         if (L.cover && pol == nullptr) {
             // A wave folds its rows one after another, so below 16384 floats
             // more waves hide more of each row's memory latency: 8 loads per
