@@ -34,7 +34,7 @@ constexpr size_t kStagedStridedBelowCols = 512;
 constexpr size_t kPackedMaxCols = 512;
 
 // ------------------------------------------------------------ rows: narrow kernel
-// Rows of up to 31 floats of a contiguous, 16-byte aligned matrix take the
+// Rows of up to 32 floats of a contiguous, 16-byte aligned matrix take the
 // narrow kernel (each lane folds whole rows): on 1024 waves, against the
 // staged kernel with whole-line tiles, TB/s of input plus output, 3 floats
 // 5.3-5.4 -> 5.5, 5 floats 5.9 -> 6.1, 7 floats 5.8 -> 6.1, 9-11 floats

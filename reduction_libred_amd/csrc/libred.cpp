@@ -389,7 +389,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // narrow kernel, each lane reducing the whole rows of its own 16-byte
     // vectors (through LDS when they span several) and storing its results
     // side by side (short_rows 17).
-    // The default for rows of up to 31 floats, on the measured number of
+    // The default for rows of up to 32 floats, on the measured number of
     // waves for the width (the table).
     // Each wave holds its results in LDS and stores them in bursts where
     // the table says so (defer 0), always (defer 2) or never (defer 1); by
