@@ -75,8 +75,8 @@ constexpr size_t kColsScratchMax = (size_t)64 << 20;
 
 // Default launch shapes, chosen by measurement on MI355X (256 CUs, 8 TB/s):
 // single-wave blocks streaming 8 KiB tiles with the next tile in flight and
-// a second one-block launch for the combine. Arrays that fit in the 256 MB
-// Infinity Cache prefer fewer, larger blocks; tiny arrays fewer blocks.
+// a second one-block launch for the combine. Arrays of 2^22 to 2^24
+// elements prefer fewer, larger blocks; tiny arrays fewer blocks.
 // Up to kTinyMax elements one 1024-thread block reads everything and stores
 // the result itself, with no second launch: in a graph of calls on a
 // cache-resident array, 2^12 / 2^14 / 2^15 floats took 2.0 / 2.2 / 2.6 us
@@ -88,7 +88,12 @@ constexpr FlatPolicy kFlatSmall = {64, 1, 8, 1, libred::kWaveTiles, 1, libred::k
 constexpr FlatPolicy kFlatCached = {1024, 1, 4, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
-constexpr size_t kCachedMax = (size_t)1 << 26;  // elements (256 MiB of 4-byte data)
+// Up to 2^24 elements the cached shape; above, the large one. In graphs of
+// calls (one array, or rotating copies that evict each other), int32 and
+// float32 sums: 2^24 cached 11.2-11.5 / 13.6-13.9 us against 11.8-12.7 /
+// 13.0-14.0 large; 2^25 22.1-22.7 / 24.1-24.6 against 20.6-21.6 / 22.4-23.0;
+// 2^26 41.2-43.1 / 44.8-45.4 against 38.6-39.7 / 41.3-42.2.
+constexpr size_t kCachedMax = (size_t)1 << 24;  // elements
 constexpr RowsPolicy kDefaultRows = {64, 8, 1, 1024, 0, 0, 0, 0, 0, 0};
 using libred::table::kSplitMinCols;
 using libred::table::kSplitRowsBelow;
