@@ -75,7 +75,7 @@ constexpr size_t kColsScratchMax = (size_t)64 << 20;
 
 // Default launch shapes, chosen by measurement on MI355X (256 CUs, 8 TB/s):
 // single-wave blocks streaming 8 KiB tiles with the next tile in flight and
-// a second one-block launch for the combine. Arrays of 2^22 to 2^24
+// a second one-block launch for the combine. Arrays of 2^20 to 2^24
 // elements prefer fewer, larger blocks; tiny arrays fewer blocks.
 // Up to kTinyMax elements one 1024-thread block reads everything and stores
 // the result itself, with no second launch: in a graph of calls on a
@@ -85,9 +85,17 @@ constexpr size_t kColsScratchMax = (size_t)64 << 20;
 constexpr FlatPolicy kFlatTiny = {1024, 1, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr size_t kTinyMax = (size_t)1 << 15;  // elements: one block of 1024 x 8 loads of 4
 constexpr FlatPolicy kFlatSmall = {64, 1, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
+constexpr FlatPolicy kFlatMid = {256, 1, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr FlatPolicy kFlatCached = {1024, 1, 4, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
 constexpr FlatPolicy kFlatLarge = {64, 2, 8, 1, libred::kWaveTiles, 1, libred::kCombineTwoPass};
-constexpr size_t kSmallMax = (size_t)1 << 22;   // elements
+// Up to 2^20 elements the small shape, then 256-thread blocks up to 2^23. In
+// graphs of calls on one array / on rotating copies, medians of three rounds,
+// int32 sums: 2^20 small 3.7 / 4.6 us against 4.1 / 4.6 for 256 x 8 loads;
+// 2^21 4.6 / 5.6 against 4.2 / 5.1; 3 x 2^20 5.9 / 6.5 against 5.2 / 5.9;
+// 2^22 7.0 / 7.4 against 5.6 / 6.2; 6 x 2^20 8.9 / 9.3 against 6.4 / 7.6
+// (float32 alike); at 2^23 the cached shape ties it (7.1-7.3 / 8.4-8.6).
+constexpr size_t kSmallMax = (size_t)1 << 20;   // elements
+constexpr size_t kMidMax = (size_t)1 << 23;     // elements
 // Up to 2^24 elements the cached shape; above, the large one. In graphs of
 // calls (one array, or rotating copies that evict each other), int32 and
 // float32 sums: 2^24 cached 11.2-11.5 / 13.6-13.9 us against 11.8-12.7 /
@@ -110,12 +118,14 @@ constexpr FlatPolicy kFusedLarge = {256, 1, 4, 1, libred::kWaveTiles, 1, libred:
 // which holds for the two-launch combine of every default shape (the
 // counter of the single-launch combine would have to start at zero).
 static_assert(kFlatTiny.combine == libred::kCombineTwoPass && kFlatSmall.combine == libred::kCombineTwoPass &&
-                  kFlatCached.combine == libred::kCombineTwoPass && kFlatLarge.combine == libred::kCombineTwoPass,
+                  kFlatMid.combine == libred::kCombineTwoPass && kFlatCached.combine == libred::kCombineTwoPass &&
+                  kFlatLarge.combine == libred::kCombineTwoPass,
               "red_sum_f32_noalloc relies on the two-launch combine");
 
 FlatPolicy default_flat(size_t n) {
     if (n <= kTinyMax) return kFlatTiny;
     if (n <= kSmallMax) return kFlatSmall;
+    if (n <= kMidMax) return kFlatMid;
     if (n <= kCachedMax) return kFlatCached;
     return kFlatLarge;
 }
