@@ -93,6 +93,11 @@ def parse_args():
                     help="instead of the headline: time the column entry points on 1 GiB of f32 viewed as "
                          "(2^28 // cols) x cols at widths around the row pitches that alias on the memory "
                          "channels, with each row order and the default; print one JSON line")
+    ap.add_argument("--col-strides", action="store_true",
+                    help="instead of the headline: time the column entry points on 1 GiB of f32 read as "
+                         "rows of ld floats of which the first cols are the matrix, with the default, the "
+                         "same launch shape with blocks dealt in launch order instead of grouped per XCD, "
+                         "and one column per lane; print one JSON line")
     return ap.parse_args()
 
 
@@ -232,6 +237,56 @@ def run_col_orders(args, torch, rl, W, timer, dev):
     print(json.dumps({"mode": "col_orders", "workload": f"{name} viewed as (2^28 // cols) x cols, contiguous",
                       "steps": args.steps, "warmup": args.warmup, "unit": "GB/s of input",
                       "orders": [k for k, _ in COL_ORDERS], "shapes": shapes}), flush=True)
+
+
+# Strided matrices: rows that start 4-byte but not 16-byte aligned (odd ld),
+# and two 16-byte aligned pitches that are not whole lines (4100, 1028).
+STRIDE_SHAPES = [(4096, 4097), (4096, 4100), (8192, 8193), (3000, 3001), (2000, 2001), (1020, 1021), (1024, 1028),
+                 (500, 503), (300, 301), (256, 257), (200, 201), (128, 129), (100, 101), (64, 65), (33, 35),
+                 (17, 19), (12, 13), (5, 7)]
+
+
+def stride_variants(cols, ld):
+    """The library's default for a (cols, ld) matrix at an aligned x, the
+    same launch shape with blocks dealt in launch order (xcd 1), and the
+    one-column-per-lane shape that was the default for such rows before the
+    shifted-vector form."""
+    if ld % 4 == 0 and cols % 4 == 0:
+        same = dict(xcd=1)
+    elif (cols + 3) // 4 + (cols % 4 != 1) >= 64:  # a spare group makes 64 lanes a row
+        same = dict(unroll=4, width=2, target_waves=1024, prefetch=1, xcd=1)
+    else:
+        same = dict(unroll=8, width=1, target_waves=2048, prefetch=1, xcd=1)
+    return (("default", None), ("launch_order", same),
+            ("one_per_lane", dict(vec=1, unroll=8, width=2, target_waves=2048, prefetch=0, xcd=1)))
+
+
+def run_col_strides(args, torch, rl, W, timer, dev):
+    name = "rows_f32_65536x4096"
+    log(f"generate {name}")
+    flat = torch.from_numpy(W.workload(name)).to(dev).view(-1)
+    total = flat.numel()
+    shapes = []
+    for cols, ld in STRIDE_SHAPES:
+        rows = total // ld
+        m = flat[: rows * ld].view(rows, ld)[:, :cols]
+        co = torch.empty(cols, device=dev)
+        entry = {"rows": rows, "cols": cols, "ld": ld}
+        for op_name, op in (("sum", rl.red_cols_sum_f32), ("max", rl.red_cols_max_f32)):
+            for label, pol in stride_variants(cols, ld):
+                def fn():
+                    op(m, out=co, policy=pol)
+                for _ in range(args.warmup):
+                    fn()
+                ms = timer.region_ms(fn, args.steps)
+                entry[f"{op_name}_{label}"] = round(gbps(4 * rows * cols, ms), 1)
+        log(f"{rows}x{cols} ld {ld}: " + ", ".join(f"{k} {v}" for k, v in entry.items()
+                                                  if k not in ("rows", "cols", "ld")))
+        shapes.append(entry)
+    print(json.dumps({"mode": "col_strides", "workload": f"{name} read as (2^28 // ld) rows of ld floats, "
+                      "the first cols of each the matrix", "steps": args.steps, "warmup": args.warmup,
+                      "unit": "GB/s of matrix bytes (4 * rows * cols)",
+                      "variants": [k for k, _ in stride_variants(1, 1)], "shapes": shapes}), flush=True)
 
 
 def read_shapes():
@@ -427,6 +482,9 @@ def main():
         return
     if args.col_orders:
         run_col_orders(args, torch, rl, W, timer, dev)
+        return
+    if args.col_strides:
+        run_col_strides(args, torch, rl, W, timer, dev)
         return
     if args.combine_sweep:
         run_combine_sweep(args, torch, rl, W, timer, dev)

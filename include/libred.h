@@ -239,7 +239,12 @@ red_status red_rows_max_f32_ld(const float *x, size_t rows, size_t cols, size_t 
  * read m rows at a time (one row of m * cols columns), and each column's m
  * partial columns are added the same way. Those partials live in a scratch
  * buffer of the stream that is grown on demand; an outgrown buffer is kept
- * until the process exits. Errors as for the row entry points.
+ * until the process exits. Rows that do not start 16-byte aligned (of at
+ * least 4 columns) are read as the aligned 16-byte vectors that cover them:
+ * such a load may cover up to 3 elements before x[0] or after
+ * x[(rows - 1) * ld + cols - 1], never outside the aligned vectors holding
+ * those two; they, and the elements between rows, never enter a result.
+ * Errors as for the row entry points.
  */
 red_status red_cols_sum_f32(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                             hipStream_t stream);

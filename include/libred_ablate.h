@@ -148,9 +148,15 @@ typedef struct red_rows_policy {
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,
  * 4, 8 or 16), `nontemporal`, `target_waves` (the rows are cut into chunks
  * until about this many single-wave blocks run), `vec`: 0 = four adjacent
- * columns per lane when x is 16-byte aligned and cols and ld are multiples
- * of 4, or through an m-row view (see `fold`); else one column per lane;
- * 1 = always one; 4 = same as 0; `fold` (with vec 0 or 4, for a contiguous
+ * columns per lane: from one aligned 16-byte load per row when x is 16-byte
+ * aligned and cols and ld are multiples of 4, or through an m-row view (see
+ * `fold`); else, with at least 4 columns, from the aligned vector each
+ * lane's first column lies in and the next one, which the lane takes from
+ * the lane that loaded it (lane l + 1), so that each block's last group of
+ * four columns, or a packed row's, only lends its vector (no lane reads
+ * past the vector that holds its row's last column); under 4 columns of
+ * such rows, one column per lane; 1 = always one; 4 = same as 0; `fold`
+ * (with vec 0 or 4, for a contiguous
  * (ld == cols) matrix): the matrix is read as view rows of m * cols columns,
  * m consecutive rows as one, with four columns per lane, starting at x or,
  * when x is not 16-byte aligned, at the next 128-byte boundary (so that such
@@ -186,7 +192,14 @@ typedef struct red_rows_policy {
  * 3 when a wave's load covers several rows (fewer than 64 column groups)
  * whose bytes are not a whole number of 128-byte lines, so that the line two
  * loads share is read by one wave; else 1). The order changes the order in which a column's elements are
- * added, never the fact that the result is fixed by the shape. */
+ * added, never the fact that the result is fixed by the shape. `xcd`: which
+ * blocks run on which of the 8 XCDs (the launch deals block b to XCD
+ * b mod 8): 1 = block b takes column block b mod n of phase b / n (n column
+ * blocks); 2 = the blocks of each XCD take every column block of a run of
+ * consecutive phases (the phases rounded down to a multiple of 8), so that
+ * the 128-byte line two column blocks, or two adjacent rows, share is
+ * fetched into one XCD's L2; 0 = the library's choice (2 with at least 8
+ * phases unless the row pitch as read is a power of two bytes, else 1). */
 typedef struct red_cols_policy {
     int unroll;
     int nontemporal;
@@ -196,15 +209,19 @@ typedef struct red_cols_policy {
     int prefetch;
     int fold;
     int order;
+    int xcd;
 } red_cols_policy;
 
 /* The default column shape. A call without a policy uses it, except on
  * short-wide matrices (four columns per lane and cols / 256 > 1024, cols of
  * the m-row view when folded), and on unfolded matrices of at least 256
  * columns whose rows are not a whole number of 128-byte lines, which use
- * unroll 2, width 4, no prefetch and target_waves 1024; and with one column
+ * unroll 2, width 4, no prefetch and target_waves 1024; with one column
  * per lane and at least 64 columns, which use unroll 8, width 2, no
- * prefetch and target_waves 2048. */
+ * prefetch and target_waves 2048; and on rows that do not start 16-byte
+ * aligned (four columns per lane from shifted vectors), which use unroll 4,
+ * width 2, prefetch and target_waves 1024 with at least 63 groups of four
+ * columns, else unroll 8, prefetch and target_waves 2048. */
 void red_default_cols_policy(red_cols_policy *p);
 red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_cols_policy *p, hipStream_t stream);

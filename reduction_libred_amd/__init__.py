@@ -63,7 +63,8 @@ class RowsPolicy(ctypes.Structure):
 class ColsPolicy(ctypes.Structure):
     _fields_ = [("unroll", ctypes.c_int), ("nontemporal", ctypes.c_int),
                 ("target_waves", ctypes.c_int), ("vec", ctypes.c_int), ("width", ctypes.c_int),
-                ("prefetch", ctypes.c_int), ("fold", ctypes.c_int), ("order", ctypes.c_int)]
+                ("prefetch", ctypes.c_int), ("fold", ctypes.c_int), ("order", ctypes.c_int),
+                ("xcd", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -44,6 +44,47 @@ __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typenam
     }
 }
 
+// The four columns a lane owns in a row whose first of them sits at position
+// s (0-3) of aligned vector v0: elements s..3 of v0, then 0..s-1 of v1 (the
+// next aligned vector).
+// The choice is made with bit masks (bitfield inserts), not branches: as a
+// chain of conditionals on s the compiler branched on every element. The
+// vectors are reinterpreted whole (a bit cast of one vector component, as
+// in __builtin_bit_cast(uint32_t, v.y), compiled to a read of component 0).
+template <class Op>
+__device__ __forceinline__ void col_fold_shift(typename Op::acc_t (&acc)[4], typename Op::vec_t v0,
+                                               typename Op::vec_t v1, unsigned int s) {
+    using elem_t = typename Op::elem_t;
+    static_assert(sizeof(typename Op::vec_t) == sizeof(u32x4), "four four-byte elements");
+    const u32x4 w0 = __builtin_bit_cast(u32x4, v0), w1 = __builtin_bit_cast(u32x4, v1);
+    const uint32_t e[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const uint32_t m1 = 0u - (s & 1u), m2 = 0u - ((s >> 1) & 1u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (e[i + 1] & m1) | (e[i] & ~m1);      // element i + (s & 1)
+        const uint32_t hi = (e[i + 3] & m1) | (e[i + 2] & ~m1);  // element i + 2 + (s & 1)
+        const elem_t t = __builtin_bit_cast(elem_t, (hi & m2) | (lo & ~m2));
+        acc[i] = Op::combine(acc[i], Op::lift(t, 0));
+    }
+}
+
+// Lane l + 1's vector v (a DPP rotate of the wave by one lane, wave_rol:1);
+// lane 63 gets lane 0's vector `after` instead. A lane whose source lane is
+// inactive gets 0.
+template <class V>
+__device__ __forceinline__ V next_lane_vec(V v, V after, unsigned int lane) {
+    static_assert(sizeof(V) == sizeof(u32x4), "four four-byte elements");
+    constexpr int kWaveRol1 = 0x134;
+    const u32x4 a = __builtin_bit_cast(u32x4, v), b = __builtin_bit_cast(u32x4, after);
+    const bool first = lane == 0;  // lane 0 lends `after` to lane 63
+    u32x4 r;
+    r.x = __builtin_amdgcn_update_dpp(0u, first ? b.x : a.x, kWaveRol1, 0xf, 0xf, false);
+    r.y = __builtin_amdgcn_update_dpp(0u, first ? b.y : a.y, kWaveRol1, 0xf, 0xf, false);
+    r.z = __builtin_amdgcn_update_dpp(0u, first ? b.z : a.z, kWaveRol1, 0xf, 0xf, false);
+    r.w = __builtin_amdgcn_update_dpp(0u, first ? b.w : a.w, kWaveRol1, 0xf, 0xf, false);
+    return __builtin_bit_cast(V, r);
+}
+
 // Block b: column block j = b % ncb, row phase k = b / ncb of the
 // K = gridDim.x / ncb phases. Phase k takes rows k, k + K, k + 2K, ... (in
 // groups of 64 / ngroups rows, see below), so the waves of one column block
@@ -60,23 +101,42 @@ __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typenam
 // 4 and x is 16-byte aligned. In the last column block a lane whose column
 // w lies past the end reads its column-0 vector again instead (so every load
 // stays in bounds and no load is predicated) and never stores that result.
-template <class Op, int VEC, int CW, int UNROLL, bool NT, bool PREFETCH>
+// With SHIFT (VEC == 4, any x, cols and ld) a row's four columns of a lane
+// start at any position s of an aligned 16-byte vector: the lane loads that
+// vector, takes the next one from the lane holding it (lane l + 1; lane 63
+// takes lane 0's vector of its next column group), and picks its columns
+// from the two. So each block owns cspan columns, one group fewer than its
+// lanes cover: the last group of a packed row, or lane 63's last group, is
+// a spare that only lends its vector. Every lane of a row group loads, also
+// past cols (for its neighbour), with the vector index clamped to the one
+// holding the row's last column, so no load reaches past the matrix; the
+// first vector can begin before x, but only within the aligned vector
+// holding x[0]. Columns past cols, and spare groups, are never stored.
+template <class Op, int VEC, int CW, int UNROLL, bool NT, bool PREFETCH, bool SHIFT = false>
 __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::elem_t* __restrict__ x,
                                                              size_t rows, size_t cols, size_t ld,
-                                                             size_t ncb, unsigned int ngroups, int order,
+                                                             size_t ncb, unsigned int ngroups, size_t cspan,
+                                                             int order, int xmap,
                                                              typename Op::acc_t* __restrict__ partials,
                                                              typename Op::out_t* __restrict__ out) {
     using acc_t = typename Op::acc_t;
     using V = typename ColVec<VEC, Op>::type;
     const unsigned int lane = threadIdx.x;
-    const size_t j = blockIdx.x % ncb;
-    const size_t k = blockIdx.x / ncb;
     const size_t nphases = gridDim.x / ncb;
+    // xmap: the blocks of one XCD (blocks are dealt to the kXcds XCDs in
+    // turn, block b to XCD b mod kXcds) take every column block of a run of
+    // nphases / kXcds consecutive phases, so that a line two column blocks,
+    // or two adjacent rows, share is fetched into one XCD's L2 (nphases is
+    // then a multiple of kXcds).
+    const size_t xi = xmap ? blockIdx.x / kXcds : blockIdx.x;
+    const size_t j = xi % ncb;
+    const size_t k = xmap ? blockIdx.x % kXcds * (nphases / kXcds) + xi / ncb : xi / ncb;
     const unsigned int g = lane % ngroups;
     const size_t group = kWave / ngroups;  // rows per load
     const size_t q = lane / ngroups;
     const size_t span = (size_t)ngroups * VEC;  // columns per load
-    const size_t c0 = j * span * CW + (size_t)g * VEC;
+    const size_t cstart = j * (SHIFT ? cspan : span * CW);
+    const size_t c0 = cstart + (size_t)g * VEC;
     // The phase's rows r0 + q, r0 + q + rpl, ... below r1: every nphases-th
     // group of rows (orders 0 and 1), or one run of consecutive rows (order
     // 2: phase k takes rows [k * per, (k + 1) * per), per a multiple of the
@@ -97,12 +157,44 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
     for (int w = 0; w < CW; ++w)
 #pragma unroll
         for (int i = 0; i < VEC; ++i) acc[w][i] = Op::identity();
-    if (c0 < cols && q < group && r0 < r1) {  // lanes past the last whole row group of a load stay idle
+    // Lanes past the last whole row group of a load stay idle, and so (but
+    // for SHIFT) do lanes past the last column.
+    if ((SHIFT || c0 < cols) && q < group && r0 < r1) {
         size_t off[CW];  // in V units from the lane's column-0 vector
 #pragma unroll
-        for (int w = 0; w < CW; ++w) off[w] = c0 + w * span < cols ? w * (size_t)ngroups : 0;
+        for (int w = 0; w < CW; ++w) off[w] = (SHIFT || c0 + w * span < cols) ? w * (size_t)ngroups : 0;
         const size_t step = ld / VEC * rpl;  // in V units, between a lane's consecutive rows
         constexpr size_t U = UNROLL;
+        // SHIFT: positions are elements from the aligned vector at or before
+        // x (xv), a row's columns of this lane at xoff + r * ld + c0.
+        const size_t xoff = SHIFT ? ((uintptr_t)x & 15) / sizeof(typename Op::elem_t) : 0;
+        const V* __restrict__ xv = reinterpret_cast<const V*>(x - xoff);
+        const size_t estep = ld * rpl;  // elements between a lane's consecutive rows
+        struct Buf {
+            V v[UNROLL][CW];
+            unsigned int s[SHIFT ? UNROLL : 1];
+        };
+        // A lane's row at position e: one vector per column group, clamped
+        // to the vector holding the row's last column (a vector past it
+        // holds none of the row's columns, so no lane needs it; the clamp
+        // keeps every load in the row's own lines).
+        auto load_shift = [&](V (&v0)[CW], unsigned int& sh, size_t e) {
+            sh = (unsigned int)(e % VEC);
+            const size_t alast = (e - c0 + cols - 1) / VEC;
+#pragma unroll
+            for (int w = 0; w < CW; ++w) {
+                const size_t a = e / VEC + off[w];
+                v0[w] = load_vec<NT>(xv + (a < alast ? a : alast));
+            }
+        };
+        // Fold a row's groups, each with the vector after it from the next lane.
+        auto fold_shift = [&](const V (&v0)[CW], unsigned int sh) {
+            if constexpr (SHIFT) {
+#pragma unroll
+                for (int w = 0; w < CW; ++w)
+                    col_fold_shift<Op>(acc[w], v0[w], next_lane_vec(v0[w], v0[w + 1 < CW ? w + 1 : w], lane), sh);
+            }
+        };
         // Fold rows r, r + rpl, ... below rend. Groups of UNROLL rows; with
         // PREFETCH, two register buffers alternate: the next group's loads
         // are issued before the current group is folded, so a wave keeps two
@@ -111,51 +203,71 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
         // them with waits for the previous group, halving the loads in
         // flight).
         auto sweep = [&](size_t r, size_t rend) {
-            const V* __restrict__ p = reinterpret_cast<const V*>(x + r * ld + c0);
-            auto load_group = [&](V (&v)[UNROLL][CW], const V* __restrict__ g) {
+            // The cursor: row r's column-0 vector (p), or its position (e).
+            const V* __restrict__ p = reinterpret_cast<const V*>(x + (SHIFT ? 0 : r * ld + c0));
+            size_t e = xoff + r * ld + c0;
+            auto load_group = [&](Buf& b, const V* __restrict__ g, size_t ge) {
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u)
+                for (int u = 0; u < UNROLL; ++u) {
+                    if constexpr (SHIFT) {
+                        load_shift(b.v[u], b.s[u], ge + u * estep);
+                    } else {
 #pragma unroll
-                    for (int w = 0; w < CW; ++w) v[u][w] = load_vec<NT>(g + u * step + off[w]);
+                        for (int w = 0; w < CW; ++w) b.v[u][w] = load_vec<NT>(g + u * step + off[w]);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             };
-            auto fold_group = [&](const V (&v)[UNROLL][CW]) {
+            auto fold_group = [&](const Buf& b) {
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u)
+                for (int u = 0; u < UNROLL; ++u) {
+                    if constexpr (SHIFT) {
+                        fold_shift(b.v[u], b.s[u]);
+                    } else {
 #pragma unroll
-                    for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], v[u][w]);
+                        for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], b.v[u][w]);
+                    }
+                }
             };
+            auto advance = [&]() { r += U * rpl, p += U * step, e += U * estep; };
             if (!PREFETCH) {
-                for (; r + (U - 1) * rpl < rend; r += U * rpl, p += U * step) {
-                    V v[UNROLL][CW];
-                    load_group(v, p);
+                for (; r + (U - 1) * rpl < rend; advance()) {
+                    Buf v;
+                    load_group(v, p, e);
                     fold_group(v);
                 }
             } else if (r + (U - 1) * rpl < rend) {
-                V a[UNROLL][CW], b[UNROLL][CW];
-                load_group(a, p);
+                Buf a, b;
+                load_group(a, p, e);
                 while (true) {
                     if (r + (2 * U - 1) * rpl >= rend) {
                         fold_group(a);
-                        r += U * rpl, p += U * step;
+                        advance();
                         break;
                     }
-                    load_group(b, p + U * step);
+                    load_group(b, p + U * step, e + U * estep);
                     fold_group(a);
-                    r += U * rpl, p += U * step;
+                    advance();
                     if (r + (2 * U - 1) * rpl >= rend) {
                         fold_group(b);
-                        r += U * rpl, p += U * step;
+                        advance();
                         break;
                     }
-                    load_group(a, p + U * step);
+                    load_group(a, p + U * step, e + U * estep);
                     fold_group(b);
-                    r += U * rpl, p += U * step;
+                    advance();
                 }
             }
-            for (; r < rend; r += rpl, p += step) {
+            for (; r < rend; r += rpl, p += step, e += estep) {
+                if constexpr (SHIFT) {
+                    V v0[CW];
+                    unsigned int sh;
+                    load_shift(v0, sh, e);
+                    fold_shift(v0, sh);
+                } else {
 #pragma unroll
-                for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], load_vec<NT>(p + off[w]));
+                    for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], load_vec<NT>(p + off[w]));
+                }
             }
         };
         // The wave visits its rows in nvis rounds (round i: rows r0 + i * rpl
@@ -192,9 +304,10 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
 #pragma unroll
         for (int w = 0; w < CW; ++w) {
             const size_t c = c0 + w * span;
-            if (c >= cols) continue;
+            if (c >= cols || (SHIFT && c - cstart >= cspan)) continue;
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
+                if (SHIFT && c + i >= cols) continue;
                 if (out != nullptr)
                     out[c + i] = Op::finish(acc[w][i]);
                 else
@@ -299,21 +412,21 @@ bool cols_policy_supported(const ColsPolicy& p) {
     const bool w = p.width == 1 || p.width == 2 || p.width == 4;
     return u && w && (p.nontemporal == 0 || p.nontemporal == 1) && (p.prefetch == 0 || p.prefetch == 1) &&
            p.target_waves >= 1 && (p.vec == 0 || p.vec == 1 || p.vec == 4) && p.fold >= 0 && p.fold <= 64 &&
-           p.order >= 0 && p.order <= 3;
+           p.order >= 0 && p.order <= 3 && p.xcd >= 0 && p.xcd <= 2;
 }
 
-template <class Op, int VEC, int CW, int UNROLL, bool PF>
+template <class Op, int VEC, int CW, int UNROLL, bool PF, bool SH>
 static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                             typename Op::out_t* out, const ColsLaunch& L, bool nt, hipStream_t stream) {
     auto* partials = static_cast<typename Op::acc_t*>(L.partials);
     const dim3 grid((unsigned int)(L.ncb * L.nchunks));
     typename Op::out_t* direct = (L.nchunks == 1 && L.fold_m <= 1 && L.rot == 0) ? out : nullptr;
     if (nt)
-        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF>), grid, dim3(kWave), 0, stream, x,
-                           rows, cols, ld, L.ncb, L.ngroups, L.order, partials, direct);
+        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF, SH>), grid, dim3(kWave), 0, stream,
+                           x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials, direct);
     else
-        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF>), grid, dim3(kWave), 0, stream, x,
-                           rows, cols, ld, L.ncb, L.ngroups, L.order, partials, direct);
+        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF, SH>), grid, dim3(kWave), 0, stream,
+                           x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials, direct);
     hipError_t e = hipGetLastError();
     const size_t W = kColsCombineBlock / kWave;
     if (e != hipSuccess) return e;
@@ -340,24 +453,24 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
     return hipGetLastError();
 }
 
-template <class Op, int VEC, int CW, int UNROLL>
+template <class Op, int VEC, int CW, int UNROLL, bool SH>
 static hipError_t cols_vwu(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                            typename Op::out_t* out, const ColsLaunch& L, bool nt, bool pf, hipStream_t stream) {
-    if (pf) return cols_vwup<Op, VEC, CW, UNROLL, true>(x, rows, cols, ld, out, L, nt, stream);
-    return cols_vwup<Op, VEC, CW, UNROLL, false>(x, rows, cols, ld, out, L, nt, stream);
+    if (pf) return cols_vwup<Op, VEC, CW, UNROLL, true, SH>(x, rows, cols, ld, out, L, nt, stream);
+    return cols_vwup<Op, VEC, CW, UNROLL, false, SH>(x, rows, cols, ld, out, L, nt, stream);
 }
 
-template <class Op, int VEC, int CW>
+template <class Op, int VEC, int CW, bool SH>
 static hipError_t cols_vw(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
                           typename Op::out_t* out, const ColsLaunch& L, const ColsPolicy& p, hipStream_t stream) {
     const bool nt = p.nontemporal != 0;
     const bool pf = p.prefetch != 0;
     switch (p.unroll) {
-        case 1: return cols_vwu<Op, VEC, CW, 1>(x, rows, cols, ld, out, L, nt, pf, stream);
-        case 2: return cols_vwu<Op, VEC, CW, 2>(x, rows, cols, ld, out, L, nt, pf, stream);
-        case 4: return cols_vwu<Op, VEC, CW, 4>(x, rows, cols, ld, out, L, nt, pf, stream);
-        case 8: return cols_vwu<Op, VEC, CW, 8>(x, rows, cols, ld, out, L, nt, pf, stream);
-        case 16: return cols_vwu<Op, VEC, CW, 16>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 1: return cols_vwu<Op, VEC, CW, 1, SH>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 2: return cols_vwu<Op, VEC, CW, 2, SH>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 4: return cols_vwu<Op, VEC, CW, 4, SH>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 8: return cols_vwu<Op, VEC, CW, 8, SH>(x, rows, cols, ld, out, L, nt, pf, stream);
+        case 16: return cols_vwu<Op, VEC, CW, 16, SH>(x, rows, cols, ld, out, L, nt, pf, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -367,16 +480,24 @@ static hipError_t cols_op(const typename Op::elem_t* x, size_t rows, size_t cols
                           typename Op::out_t* out, const ColsLaunch& L, const ColsPolicy& p, hipStream_t stream) {
     if (L.vec != 4) {
         switch (L.width) {
-            case 1: return cols_vw<Op, 1, 1>(x, rows, cols, ld, out, L, p, stream);
-            case 2: return cols_vw<Op, 1, 2>(x, rows, cols, ld, out, L, p, stream);
-            case 4: return cols_vw<Op, 1, 4>(x, rows, cols, ld, out, L, p, stream);
+            case 1: return cols_vw<Op, 1, 1, false>(x, rows, cols, ld, out, L, p, stream);
+            case 2: return cols_vw<Op, 1, 2, false>(x, rows, cols, ld, out, L, p, stream);
+            case 4: return cols_vw<Op, 1, 4, false>(x, rows, cols, ld, out, L, p, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (L.shift) {
+        switch (L.width) {
+            case 1: return cols_vw<Op, 4, 1, true>(x, rows, cols, ld, out, L, p, stream);
+            case 2: return cols_vw<Op, 4, 2, true>(x, rows, cols, ld, out, L, p, stream);
+            case 4: return cols_vw<Op, 4, 4, true>(x, rows, cols, ld, out, L, p, stream);
             default: return hipErrorInvalidValue;
         }
     }
     switch (L.width) {
-        case 1: return cols_vw<Op, 4, 1>(x, rows, cols, ld, out, L, p, stream);
-        case 2: return cols_vw<Op, 4, 2>(x, rows, cols, ld, out, L, p, stream);
-        case 4: return cols_vw<Op, 4, 4>(x, rows, cols, ld, out, L, p, stream);
+        case 1: return cols_vw<Op, 4, 1, false>(x, rows, cols, ld, out, L, p, stream);
+        case 2: return cols_vw<Op, 4, 2, false>(x, rows, cols, ld, out, L, p, stream);
+        case 4: return cols_vw<Op, 4, 4, false>(x, rows, cols, ld, out, L, p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -221,6 +221,22 @@ constexpr size_t kRotateRowsPitchFactorB = 257;
 // and 27-31 columns) runs read 1-4% slower, so the band stays there.
 constexpr size_t kLineBytes = 128;
 
+// ------------------------------------------------------------ columns: XCD grouping
+// A launch of at least this many row phases deals each XCD the column
+// blocks of a run of consecutive phases (the phases rounded down to a
+// multiple of 8), unless the row pitch as read (ld or the view's) is a
+// power of two bytes. Where rows, or a block's share of a row, do not end on
+// a 128-byte line, two blocks read the line between them, and it is fetched
+// twice when they run on different XCDs: sums over 1 GiB matrices read
+// 1.06-1.11 times their input dealt block by block, 1.04-1.05 grouped; 4096
+// columns at ld 4097: 5.3 -> 6.3 TB/s, 3000 at 3001: 5.4 -> 6.6, 1020 at
+// 1021: 4.7 -> 6.4, 8192 at 8193: 5.1 -> 6.3, 4096 at 4100: 6.2 -> 6.6, 1024
+// at 1028: 5.2 -> 6.2, 256 at 257: 5.3 -> 5.5; contiguous 100 and 260
+// columns +12% and +5%, the other contiguous widths from 1 to 2^20 within 1%.
+// At power-of-two pitches (contiguous 1, 4, 16, 32, 64, 256, 512, 1024, 4096
+// and 16384 columns, 1000 columns at ld 1024) grouping ran 5-7% slower.
+constexpr size_t kXcdGroupMinPhases = 8;
+
 // ------------------------------------------------------------ columns: shapes
 // Short-wide matrices (more than this many blocks of 256 columns), and rows
 // of at least kFoldWideFromCols columns that are not whole lines (unfolded),

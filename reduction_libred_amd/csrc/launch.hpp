@@ -9,6 +9,10 @@
 
 namespace libred {
 
+// MI355X: 8 XCDs of 32 CUs, each with its own L2; the workgroups of a launch
+// are dealt to them in turn (workgroup b to XCD b mod 8).
+constexpr int kXcds = 8;
+
 // Launch shape of the single-value kernels: `block` threads per block, at
 // most `blocks_per_cu` blocks per compute unit, `unroll` independent 16-byte
 // loads in flight per lane per loop trip, `nontemporal` marks the streaming
@@ -108,6 +112,7 @@ struct ColsPolicy {
     int prefetch;
     int fold;
     int order;
+    int xcd;
 };
 
 // How one column call launches: ncb column blocks of ngroups*vec*width
@@ -135,11 +140,23 @@ struct ColsLaunch {
     const void* tail;
     unsigned int rot;
     const void* head;
+    // With vec 4: the rows need not start 16-byte aligned (cols, ld and x
+    // arbitrary); each lane loads the aligned vector its four columns start
+    // in and takes the next one from the next lane. A block then owns cspan
+    // columns: 4 * (64 * width - 1) with one column group per lane, or
+    // 4 * (ngroups - 1) for packed rows whose last group is a spare that only
+    // lends its vector (4 * ngroups when no row's last group reaches past its
+    // vector).
+    int shift;
+    size_t cspan;
     // Rows of a phase: 0 = every nchunks-th group from group k (a launch
     // reads one band of the matrix at a time); 1 = the same rows, block b
     // starting at its (b mod n)-th of n groups and wrapping around to the
     // first; 2 = one run of consecutive rows per phase.
     int order;
+    // 1: the blocks on each XCD take all column blocks of consecutive phases
+    // (nchunks a multiple of kXcds); 0: column block b mod ncb, phase b / ncb.
+    int xmap;
 };
 
 bool flat_policy_supported(const FlatPolicy& p);

@@ -280,11 +280,22 @@ constexpr libred::ColsPolicy kWideCols = {2, 1, 1024, 0, 4, 0, 0, 0};
 // 2048 waves (a sweep over 4097, 1001, 257 and 65 columns: 2.3-2.8 ->
 // 3.4-5.3 TB/s against the vector default).
 constexpr libred::ColsPolicy kScalarCols = {8, 1, 2048, 0, 2, 0, 0, 0};
+// Columns read four per lane from rows that do not start 16-byte aligned
+// (the shifted form), the best of a sweep of launch shapes over 1 GiB
+// matrices at odd ld. Rows that take 64 lanes: 4 rows in flight twice over,
+// 2 KiB of a row per wave, 1024 waves (9 shapes over 255-16000 columns).
+// Packed rows: 8 rows in flight twice over, 2048 waves (6 shapes over 5-200
+// columns). Against one column per lane (kScalarCols): 256-8192 columns
+// 5.1-5.6 -> 5.4-6.5 TB/s with the XCD grouping, 5-200 columns 3.2-4.9 ->
+// 4.5-6.3.
+static_assert(libred::table::kXcdGroupMinPhases >= (size_t)libred::kXcds, "a whole number of phases per XCD");
+constexpr libred::ColsPolicy kShiftWideCols = {4, 1, 1024, 0, 2, 1, 0, 0};
+constexpr libred::ColsPolicy kShiftNarrowCols = {8, 1, 2048, 0, 1, 1, 0, 0};
 
 libred::ColsPolicy to_cols(const red_cols_policy* p) {
     if (!p) return kDefaultCols;
     libred::ColsPolicy c = {p->unroll, p->nontemporal, p->target_waves, p->vec, p->width, p->prefetch, p->fold,
-                            p->order};
+                            p->order,  p->xcd};
     return c;
 }
 
@@ -773,6 +784,8 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     L.rot = 0;
     L.head = nullptr;
     L.order = 0;
+    L.shift = 0;
+    L.xmap = 0;
     // A contiguous matrix may be viewed with m consecutive rows as one row
     // of m * cols columns (see fold_rows): for a width that is not a
     // multiple of 4 this makes every view row start 16-byte aligned, so four
@@ -812,6 +825,14 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     }
     const bool vec_ok = aligned(x, 16) && cols % 4 == 0 && ld % 4 == 0;
     L.vec = (p.vec != 1 && vec_ok) ? 4 : 1;
+    // Rows that do not start 16-byte aligned (or widths that are not a
+    // multiple of 4) still read four columns per lane: a lane loads the
+    // aligned vector its columns start in and takes the next from the next
+    // lane.
+    if (p.vec != 1 && !vec_ok && cols >= 4) {
+        L.vec = 4;
+        L.shift = 1;
+    }
     if (pol == nullptr && L.vec == 4 && cols / 256 > libred::table::kWideColBlocks) p = kWideCols;
     // Rows that are not a whole number of 128-byte lines (and not a folded
     // view) also read best 4 KiB at a time, 2 rows in flight: 1020, 1500,
@@ -820,13 +841,30 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         p = kWideCols;
     // Narrow matrix: if the column groups divide a wave, pack several rows
     // into each load.
-    const size_t groups = cols / (size_t)L.vec;
+    // With shift, a packed row's last group reaches into the vector after
+    // its own when its first column can sit at position s of its vector
+    // with s + (its columns) > 4; then one more lane per row (a spare) loads
+    // that vector. The position is fixed by x when ld is a multiple of 4,
+    // else it runs through 0-3.
+    const size_t groups = L.shift ? (cols + 3) / 4 : cols / (size_t)L.vec;
+    size_t spare = 0;
+    if (L.shift) {
+        const size_t last = cols - 4 * (groups - 1);  // columns of the last group, 1-4
+        const size_t smax = ld % 4 == 0 ? (uintptr_t)x % 16 / sizeof(float) : 3;
+        spare = last + smax > 4 ? 1 : 0;
+    }
     L.ngroups = 64;
-    if (groups < 64) L.ngroups = (unsigned int)groups;
+    if (groups + spare < 64) L.ngroups = (unsigned int)(groups + spare);
     if (pol == nullptr && L.vec == 1 && L.ngroups == 64) p = kScalarCols;
+    if (pol == nullptr && L.shift) p = L.ngroups == 64 ? kShiftWideCols : kShiftNarrowCols;
     L.width = L.ngroups == 64 ? p.width : 1;
-    const size_t per_block = (size_t)L.ngroups * L.vec * L.width;
-    L.ncb = (cols + per_block - 1) / per_block;
+    if (!L.shift)
+        L.cspan = (size_t)L.ngroups * L.vec * L.width;
+    else if (L.ngroups == 64)
+        L.cspan = 4 * (64 * (size_t)L.width - 1);
+    else
+        L.cspan = 4 * (L.ngroups - spare);
+    L.ncb = (cols + L.cspan - 1) / L.cspan;
     size_t nchunks = 1;
     if (rows > 0) {
         nchunks = ((size_t)p.target_waves + L.ncb - 1) / L.ncb;
@@ -835,6 +873,14 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         const size_t by_scratch = kColsScratchMax / (cols * 8);
         if (nchunks > by_scratch) nchunks = by_scratch;
         if (nchunks < 1) nchunks = 1;
+    }
+    // Blocks grouped per XCD (see ColsLaunch::xmap and
+    // kXcdGroupMinPhases): a whole number of phases per XCD.
+    const size_t pitch = ld * sizeof(float);
+    const bool pow2_pitch = pitch != 0 && (pitch & (pitch - 1)) == 0;
+    if ((p.xcd == 2 || (p.xcd == 0 && !pow2_pitch)) && nchunks >= libred::table::kXcdGroupMinPhases) {
+        nchunks = nchunks / libred::kXcds * libred::kXcds;
+        L.xmap = 1;
     }
     L.nchunks = nchunks;
     // Row order: rotated starts at pitches the memory channels alias on
@@ -1174,6 +1220,7 @@ void red_default_cols_policy(red_cols_policy* p) {
     p->prefetch = kDefaultCols.prefetch;
     p->fold = kDefaultCols.fold;
     p->order = kDefaultCols.order;
+    p->xcd = kDefaultCols.xcd;
 }
 
 red_status red_cols_sum_f32_with(const float* x, size_t rows, size_t cols, size_t ld, float* out,

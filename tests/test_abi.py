@@ -153,10 +153,11 @@ def test_cols_argument_errors():
     bad = rl.ColsPolicy(8, 1, 1024, 2)
     assert L.red_cols_max_f32_with(_p(A), 2, 3, 3, _p(B), ctypes.byref(bad), None) == INVALID
     base = rl.red_default_cols_policy()
-    assert base.fold == 0 and base.vec == 0 and base.order == 0
+    assert base.fold == 0 and base.vec == 0 and base.order == 0 and base.xcd == 0
     for field, value, ok in (("fold", 65, False), ("fold", -1, False), ("fold", 64, True), ("fold", 17, True), ("fold", 1, True),
                              ("width", 3, False), ("target_waves", 0, False), ("order", 4, False),
-                             ("order", -1, False), ("order", 3, True), ("order", 0, True)):
+                             ("order", -1, False), ("order", 3, True), ("order", 0, True),
+                             ("xcd", 3, False), ("xcd", -1, False), ("xcd", 2, True), ("xcd", 1, True)):
         pol = rl.red_default_cols_policy()
         setattr(pol, field, value)
         want = rl.RED_OK if ok else INVALID

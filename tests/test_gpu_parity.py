@@ -743,7 +743,14 @@ COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260)
               (1001, 6, 6), (4001, 10, 10), (37, 2, 2), (20_003, 7, 7), (9, 4097, 4097), (5, 3, 3),
               (1000, 260, 260), (333, 516, 516), (41, 300, 300), (3001, 33, 33), (70, 65, 65), (63, 97, 97),
               (300, 1020, 1020), (129, 2040, 2040), (500, 1000, 1020), (77, 765, 765), (45, 1028, 1028),
-              (1203, 255, 255), (31, 510, 514)]
+              (1203, 255, 255), (31, 510, 514),
+              # rows not 16-byte aligned: four columns per lane from shifted
+              # vectors, with and without a spare group per packed row, the
+              # wide form's last block past a width of 252 columns per block
+              # (and 508 and 1020 at widths 2 and 4), ld a multiple of 4
+              # (with the offset 1 runs), and 64 lanes in a row of 252.
+              (300, 252, 253), (300, 253, 255), (300, 250, 251), (1000, 509, 511), (100, 1017, 1019),
+              (2000, 16, 17), (3000, 5, 7), (1500, 4096, 4097), (400, 125, 128), (123, 2000, 2001)]
 COL_POLICIES = (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=16, nontemporal=0),
                 dict(width=2), dict(width=4, unroll=2), dict(width=4, unroll=16, nontemporal=0, target_waves=7),
                 dict(prefetch=1), dict(prefetch=1, unroll=1, target_waves=7), dict(width=4, unroll=2, prefetch=1),
@@ -751,7 +758,9 @@ COL_POLICIES = (None, dict(vec=1), dict(unroll=1, target_waves=7), dict(unroll=1
                 dict(fold=3, unroll=1, target_waves=7), dict(fold=8, width=4, unroll=2, prefetch=0),
                 dict(fold=32), dict(fold=64, unroll=2), dict(order=1), dict(order=2),
                 dict(order=2, unroll=1, target_waves=7, prefetch=1), dict(order=3),
-                dict(order=3, width=4, unroll=2, target_waves=7), dict(order=3, fold=16, prefetch=0))
+                dict(order=3, width=4, unroll=2, target_waves=7), dict(order=3, fold=16, prefetch=0),
+                dict(xcd=1), dict(xcd=2), dict(xcd=2, width=4, unroll=2, target_waves=64),
+                dict(xcd=2, order=3, target_waves=64), dict(xcd=2, order=2, width=2, unroll=1, target_waves=100))
 
 
 @pytest.mark.parametrize("rows,cols,ld", COL_SHAPES)
@@ -905,10 +914,13 @@ def test_rows_signalling_nan():
 
 
 @pytest.mark.parametrize("rows,cols,ld", [(1000, 3, 3), (1000, 64, 64), (999, 7, 9), (97, 1031, 1031),
-                                          (4001, 10, 10), (500, 12, 12)])
+                                          (4001, 10, 10), (500, 12, 12), (999, 64, 65), (300, 1000, 1003),
+                                          (2001, 17, 19)])
 def test_cols_nonfinite(rows, cols, ld):
     """NaN and infinities through every column path (four columns per lane,
-    folded m-row views, one column per lane, packed narrow matrices)."""
+    folded m-row views, one column per lane, packed narrow matrices, shifted
+    vectors; the padding between rows is 1e30, which a shifted load reads
+    but no column may take)."""
     a = _nonfinite_matrix(rows, cols, rows * 5 + cols)
     full = np.full((rows, ld), 1e30, np.float32)
     full[:, :cols] = a
@@ -1335,6 +1347,31 @@ def test_full_cols_65536x4096():
     S, A = oracle.cols_sum_f32(a)
     assert sums_ok(s.cpu().numpy().astype(np.float64), S, A)
     assert np.array_equal(m.cpu().numpy(), oracle.cols_max_f32(a))
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_cols_strided_1gib():
+    # The 1 GiB rows workload viewed as rows of ld floats of which the first
+    # cols are the matrix, the strided shapes the column-stride benchmark
+    # times (default launch shapes: shifted vectors where rows do not start
+    # 16-byte aligned, XCD-grouped blocks where the pitch is not a power of
+    # two). Every column is compared with the oracle.
+    a, x = _load("rows_f32_65536x4096")
+    flat = a.reshape(-1)
+    for cols, ld in ((4096, 4097), (4096, 4100), (1020, 1021), (256, 257), (64, 65), (17, 19), (5, 7)):
+        rows = flat.size // ld
+        say(f"red_cols_sum_f32 / red_cols_max_f32 rows_f32_65536x4096 as {rows}x{cols}, ld {ld}")
+        v = x.view(-1)[: rows * ld].view(rows, ld)[:, :cols]
+        s = rl.red_cols_sum_f32(v)
+        m = rl.red_cols_max_f32(v)
+        torch.cuda.synchronize()
+        mat = np.ascontiguousarray(flat[: rows * ld].reshape(rows, ld)[:, :cols])
+        say(f"oracle cols {rows}x{cols}")
+        S, A = oracle.cols_sum_f32(mat)
+        assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), (cols, ld)
+        assert np.array_equal(m.cpu().numpy(), oracle.cols_max_f32(mat)), (cols, ld)
+        del mat
     del x
     torch.cuda.empty_cache()
 
