@@ -131,7 +131,16 @@ typedef struct red_flat_policy {
  * contiguous, 16-byte aligned matrix): 0 = the library's choice (1 for rows
  * of fewer than 32 floats), 1 = tiles of a multiple of 32 rows (whole
  * 128-byte lines of input and of output when x and out are 128-byte
- * aligned), 2 = as many rows as fit. */
+ * aligned), 2 = as many rows as fit; and `xcd`, which blocks of the
+ * one-wave-per-row, streaming, packed and LDS-staged kernels run on which
+ * of the 8 XCDs (the launch deals block b to XCD b mod 8): 1 = block b takes
+ * the rows (or tiles) of index b; n = 2-4096: the indices are dealt to the
+ * XCDs in runs of n consecutive ones, the grid rounded up to a multiple of
+ * 8n when it has at least 8n blocks (else as 1), so that a row and the next,
+ * which share the 128-byte line where one ends, are mostly read on one XCD;
+ * 0 = the library's choice (runs of 64 for rows of 768 to 4095 floats that
+ * do not all start on a 128-byte line, else 1). The results are the same
+ * either way. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
@@ -143,6 +152,7 @@ typedef struct red_rows_policy {
     int cover;
     int defer;
     int lines;
+    int xcd;
 } red_rows_policy;
 
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,

@@ -164,6 +164,26 @@ constexpr size_t kSplitRowsBelow = 1024;
 constexpr size_t kSplitMinCols = 8192;
 constexpr size_t kSplitTargetWaves = 1024;
 
+// ------------------------------------------------------------ rows: XCD grouping
+// Rows of kGroupRowsMinCols to kGroupRowsMaxCols - 1 floats that do not all
+// start on kRowLineBytes lines are read by grid-stride kernels whose block
+// indices are dealt to the XCDs in runs of kGroupRowsChunk consecutive ones
+// (grid rounded up to a multiple of 8 runs): a row and the next share the
+// line where one ends, and dealt block by block the two waves that read it
+// sit on different XCDs and fetch it twice. Sums over 1 GiB, TB/s, launch
+// order against runs of 64: contiguous 1000 floats 6.48 -> 6.77, 1020: 6.12
+// -> 6.66, 1023: 5.97 -> 6.43, 1025: 6.49 -> 6.97, 1500: 6.54 -> 7.00, 2049:
+// 6.86 -> 6.91, 3001: 6.71 -> 7.01; 1000 at ld 1003: 6.37 -> 6.91, 2000 at
+// 2001: 6.63 -> 6.99, 1025 at 1028: 5.19 -> 5.34 (+6.4% on average; runs of
+// 16 and 256: +6.0% and +6.2%). Elsewhere grouping was neutral or lost: 4097 and 6000
+// floats 2% slower, 48 floats 4-7%, whole-line rows (64, 1024, 2048, 4096
+// floats) up to 4%; grouping a launch's blocks in 8 contiguous bands (one per
+// XCD) lost 6% at 4097 floats, whose bands then lie 64 MiB + 16 KiB apart.
+constexpr size_t kGroupRowsMinCols = 768;
+constexpr size_t kGroupRowsMaxCols = 4096;
+constexpr int kGroupRowsChunk = 64;
+constexpr size_t kRowLineBytes = 128;
+
 // ------------------------------------------------------------ columns: folded views
 // A width of at least this many columns that is not a multiple of 32 reads
 // through views of 32 rows (whole 128-byte lines) when that leaves at least

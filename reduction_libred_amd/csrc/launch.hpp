@@ -47,6 +47,7 @@ struct RowsPolicy {
     int cover;
     int defer;
     int lines;
+    int xcd;
 };
 
 // How one row call launches: `grid` blocks of the one-wave-per-row kernel,
@@ -71,6 +72,8 @@ struct RowsLaunch {
     int narrow;         // the register kernel for narrow rows (rows_narrow.hip), `grid` waves:
                         //   1 = results stored as each tile is folded, 2 = held in LDS and
                         //   stored in bursts
+    int xmap;           // grid-stride row kernels: the blocks of each XCD take consecutive
+                        //   block indices (used when the grid is a multiple of kXcds)
 };
 
 // Narrow rows: a contiguous, 16-byte aligned matrix of rows of 1 to

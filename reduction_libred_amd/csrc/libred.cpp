@@ -339,7 +339,7 @@ RowsPolicy default_rows(size_t cols) {
 RowsPolicy to_rows(const red_rows_policy* p, size_t cols) {
     if (!p) return default_rows(cols);
     RowsPolicy r = {p->block,      p->unroll, p->nontemporal, p->max_blocks, p->split,
-                    p->prefetch,   p->short_rows, p->cover,   p->defer,      p->lines};
+                    p->prefetch,   p->short_rows, p->cover,   p->defer,      p->lines, p->xcd};
     return r;
 }
 
@@ -396,7 +396,20 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (st != RED_OK) return st;
     namespace T = libred::table;
 
-    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    // Grid-stride kernels with the blocks of each XCD on consecutive rows
+    // (RowsLaunch::xmap): the grid rounded up to a multiple of kXcds, so a
+    // wave keeps its number of rows or gets one fewer.
+    const bool whole_lines = aligned(x, T::kRowLineBytes) && (rows == 1 || ld * sizeof(float) % T::kRowLineBytes == 0);
+    const bool group_default = !whole_lines && cols >= T::kGroupRowsMinCols && cols < T::kGroupRowsMaxCols;
+    const int chunk = p.xcd >= 2 ? p.xcd : (p.xcd == 0 && group_default) ? T::kGroupRowsChunk : 0;
+    auto group = [&]() {
+        if (chunk <= 0) return;
+        const size_t per = (size_t)libred::kXcds * (size_t)chunk;
+        if ((size_t)L.grid < per) return;
+        L.grid = (int)(((size_t)L.grid + per - 1) / per * per);
+        L.xmap = chunk;
+    };
     // Rows of fewer than 1024 floats go to the LDS-staged kernel (short_rows
     // 0), or do so with 2^(short_rows - 3) lanes per row (short_rows 3-9),
     // when the rows are contiguous or their gaps hold at most a quarter of a
@@ -573,6 +586,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         L.staged_spread = !L.staged_vread && (pass / 2) * bank_gcd >= 16 * 32 ? 1 : 0;
         const size_t tiles = (rows + L.staged_rows - 1) / L.staged_rows;
         L.grid = (int)(tiles < max_blocks ? tiles : max_blocks);
+        group();
         // A wave's results are held in LDS and stored after its last tile
         // (defer 0) when they fit beside its staging tile in one wave's share
         // of a CU's LDS (the grid's waves spread evenly over the CUs) and in
@@ -611,6 +625,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         const size_t per_trip_groups = (size_t)(vec ? 16 : 32) / (size_t)L.packed_v;
         const size_t waves = (groups + per_trip_groups - 1) / per_trip_groups;
         L.grid = (int)(waves < (size_t)p.max_blocks ? waves : (size_t)p.max_blocks);
+        group();
         const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
         if (e != hipSuccess) return fail(e, RED_ERR_HIP);
         return RED_OK;
@@ -666,6 +681,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         const size_t per = (rows + target - 1) / target;  // rows per wave
         const size_t waves = (rows + per - 1) / per;
         L.grid = (int)((waves + W - 1) / W);
+        group();
     }
     const hipError_t e = launch(x, rows, cols, ld, out, L, p, stream);
     if (e != hipSuccess) return fail(e, RED_ERR_HIP);
@@ -1104,6 +1120,7 @@ void red_default_rows_policy(red_rows_policy* p) {
     p->cover = kDefaultRows.cover;
     p->defer = kDefaultRows.defer;
     p->lines = kDefaultRows.lines;
+    p->xcd = kDefaultRows.xcd;
 }
 
 size_t red_flat_grid(size_t n, const red_flat_policy* pol) {

@@ -33,6 +33,19 @@
 
 namespace libred {
 
+// The block index a grid-stride row kernel works as. With chunk C > 0, the
+// indices are dealt to the XCDs (the launch deals block b to XCD b mod
+// kXcds) in runs of C consecutive ones, the runs in turn, gridDim.x a
+// multiple of kXcds * C: neighbouring rows (or tiles), which share the
+// 128-byte line where one ends and the next begins, are then read into one
+// XCD's L2 but at the end of a run, while the blocks running at any time
+// still hold one band of consecutive indices.
+__device__ __forceinline__ size_t work_block(int chunk) {
+    if (chunk <= 0) return blockIdx.x;
+    const size_t c = (size_t)chunk, i = blockIdx.x / kXcds;
+    return i / c * (kXcds * c) + (blockIdx.x % kXcds) * c + i % c;
+}
+
 template <bool NT, class V, int UNROLL>
 __device__ __forceinline__ void load_tile_rows(V (&v)[UNROLL], const V* __restrict__ p) {
 #pragma unroll
@@ -101,14 +114,14 @@ __device__ __forceinline__ void fold_row_span(const typename Op::elem_t* __restr
 template <class Op, int BLOCK, int UNROLL, bool NT>
 __global__ __launch_bounds__(BLOCK) void rows_reduce_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, size_t ld,
-                                                            typename Op::out_t* __restrict__ out) {
+                                                            typename Op::out_t* __restrict__ out, int xmap) {
     using acc_t = typename Op::acc_t;
     constexpr int W = BLOCK / kWave;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
     // Wave-uniform loop over rows: all 64 lanes stay active at the wave reduce.
-    for (size_t r = (size_t)blockIdx.x * W + wave; r < rows; r += (size_t)gridDim.x * W) {
+    for (size_t r = work_block(xmap) * W + wave; r < rows; r += (size_t)gridDim.x * W) {
         acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
         fold_row_span<Op, UNROLL, NT>(x + r * ld, cols, 0, 1, true, acc);
         acc_t v = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
@@ -233,13 +246,13 @@ __device__ __forceinline__ void fold_row_cover(const typename Op::elem_t* __rest
 template <class Op, int BLOCK, int UNROLL, bool NT>
 __global__ __launch_bounds__(BLOCK) void rows_cover_kernel(const typename Op::elem_t* __restrict__ x,
                                                            size_t rows, size_t cols, size_t ld,
-                                                           typename Op::out_t* __restrict__ out) {
+                                                           typename Op::out_t* __restrict__ out, int xmap) {
     using acc_t = typename Op::acc_t;
     constexpr int W = BLOCK / kWave;
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uintptr_t end = (uintptr_t)(x + (rows - 1) * ld + cols);
-    for (size_t r = (size_t)blockIdx.x * W + wave; r < rows; r += (size_t)gridDim.x * W) {
+    for (size_t r = work_block(xmap) * W + wave; r < rows; r += (size_t)gridDim.x * W) {
         acc_t acc[4] = {Op::identity(), Op::identity(), Op::identity(), Op::identity()};
         fold_row_cover<Op, UNROLL, NT>(x, r, cols, ld, end, acc);
         acc_t v = Op::combine(Op::combine(acc[0], acc[1]), Op::combine(acc[2], acc[3]));
@@ -251,7 +264,7 @@ __global__ __launch_bounds__(BLOCK) void rows_cover_kernel(const typename Op::el
 template <class Op, int UNROLL, bool NT>
 __global__ __launch_bounds__(kWave) void rows_stream_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, size_t ld,
-                                                            typename Op::out_t* __restrict__ out) {
+                                                            typename Op::out_t* __restrict__ out, int xmap) {
     using acc_t = typename Op::acc_t;
     using vec_t = typename Op::vec_t;
     using elem_t = typename Op::elem_t;
@@ -260,7 +273,7 @@ __global__ __launch_bounds__(kWave) void rows_stream_kernel(const typename Op::e
     const unsigned int lane = threadIdx.x;
     const size_t G = gridDim.x;
     const uintptr_t end = (uintptr_t)(x + (rows - 1) * ld + cols);
-    size_t r = blockIdx.x;  // wave-uniform
+    size_t r = work_block(xmap);  // wave-uniform
     if (r >= rows) return;
     CoverGeom<Op> g = cover_geom<Op, UNROLL>(x, r, cols, ld, end);
     size_t t = 0;
@@ -371,7 +384,7 @@ __device__ __forceinline__ typename Op::acc_t segment_reduce(typename Op::acc_t 
 template <class Op, int LOG2L, int V, bool SCALAR, bool NT>
 __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, size_t ld,
-                                                            typename Op::out_t* __restrict__ out) {
+                                                            typename Op::out_t* __restrict__ out, int xmap) {
     using acc_t = typename Op::acc_t;
     using unit_t = std::conditional_t<SCALAR, typename Op::elem_t, typename Op::vec_t>;
     constexpr size_t E = SCALAR ? 1 : Op::kPerVec;  // elements per unit
@@ -435,7 +448,7 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
     // the compiler joins the exits in a block that also leads back to the
     // loop head, and on that path the other buffer's loads are still in
     // flight, so the head waited for them before issuing the next loads.
-    size_t g0 = blockIdx.x;  // wave-uniform
+    size_t g0 = work_block(xmap);  // wave-uniform
     if (g0 >= ngroups) return;
     const size_t step = G * U;
     size_t n = (ngroups - g0 + step - 1) / step;
@@ -495,7 +508,7 @@ template <class Op, int LOG2S, int U, bool NT, bool VREAD, bool HOLD, bool SPREA
 __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, size_t ld,
                                                             unsigned int sh, unsigned int R,
-                                                            typename Op::out_t* __restrict__ out) {
+                                                            typename Op::out_t* __restrict__ out, int xmap) {
     using acc_t = typename Op::acc_t;
     using elem_t = typename Op::elem_t;
     using vec_t = typename Op::vec_t;
@@ -656,7 +669,7 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
     // The wave's n tiles t0, t0 + G, ... run two per loop pass, one register
     // buffer each, with the odd or last two after the loop (a loop with one
     // exit, as in rows_packed_kernel, so that its head never waits for loads).
-    const size_t first = blockIdx.x;  // wave-uniform
+    const size_t first = work_block(xmap);  // wave-uniform
     if (first >= ntiles) return;
     const size_t mine = (ntiles - first + G - 1) / G;
     size_t n = mine, k = 0, t0 = first;
@@ -721,14 +734,16 @@ __global__ __launch_bounds__(kRowsCombineBlock) void rows_combine_kernel(
 
 template <class Op, int BLOCK, int UNROLL>
 inline hipError_t rows_bu(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
-                          typename Op::out_t* out, int grid, bool nt, bool pf, bool cover, hipStream_t stream) {
+                          typename Op::out_t* out, int grid, bool nt, bool pf, bool cover, int xmap,
+                          hipStream_t stream) {
+    const int xm = xmap > 0 && grid % (kXcds * xmap) == 0 ? xmap : 0;
     if (cover && !pf) {
         if (nt)
             hipLaunchKernelGGL((rows_cover_kernel<Op, BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0, stream, x,
-                               rows, cols, ld, out);
+                               rows, cols, ld, out, xm);
         else
             hipLaunchKernelGGL((rows_cover_kernel<Op, BLOCK, UNROLL, false>), dim3(grid), dim3(BLOCK), 0, stream,
-                               x, rows, cols, ld, out);
+                               x, rows, cols, ld, out, xm);
         return hipGetLastError();
     }
     if (pf) {
@@ -736,33 +751,35 @@ inline hipError_t rows_bu(const typename Op::elem_t* x, size_t rows, size_t cols
         // BLOCK-thread grid holds, at most one per row.
         size_t waves = (size_t)grid * (BLOCK / kWave);
         if (waves > rows) waves = rows;
+        const int xw = xmap > 0 && waves % (kXcds * (size_t)xmap) == 0 ? xmap : 0;
         if (nt)
             hipLaunchKernelGGL((rows_stream_kernel<Op, UNROLL, true>), dim3((unsigned int)waves), dim3(kWave), 0,
-                               stream, x, rows, cols, ld, out);
+                               stream, x, rows, cols, ld, out, xw);
         else
             hipLaunchKernelGGL((rows_stream_kernel<Op, UNROLL, false>), dim3((unsigned int)waves), dim3(kWave), 0,
-                               stream, x, rows, cols, ld, out);
+                               stream, x, rows, cols, ld, out, xw);
     } else if (nt) {
         hipLaunchKernelGGL((rows_reduce_kernel<Op, BLOCK, UNROLL, true>), dim3(grid), dim3(BLOCK), 0,
-                           stream, x, rows, cols, ld, out);
+                           stream, x, rows, cols, ld, out, xm);
     } else {
         hipLaunchKernelGGL((rows_reduce_kernel<Op, BLOCK, UNROLL, false>), dim3(grid), dim3(BLOCK), 0,
-                           stream, x, rows, cols, ld, out);
+                           stream, x, rows, cols, ld, out, xm);
     }
     return hipGetLastError();
 }
 
 template <class Op, int BLOCK>
 inline hipError_t rows_b(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
-                         typename Op::out_t* out, int grid, bool cover, const RowsPolicy& p, hipStream_t stream) {
+                         typename Op::out_t* out, int grid, bool cover, int xmap, const RowsPolicy& p,
+                         hipStream_t stream) {
     const bool nt = p.nontemporal != 0;
     const bool pf = p.prefetch != 0;
     switch (p.unroll) {
-        case 1: return rows_bu<Op, BLOCK, 1>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
-        case 2: return rows_bu<Op, BLOCK, 2>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
-        case 4: return rows_bu<Op, BLOCK, 4>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
-        case 8: return rows_bu<Op, BLOCK, 8>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
-        case 16: return rows_bu<Op, BLOCK, 16>(x, rows, cols, ld, out, grid, nt, pf, cover, stream);
+        case 1: return rows_bu<Op, BLOCK, 1>(x, rows, cols, ld, out, grid, nt, pf, cover, xmap, stream);
+        case 2: return rows_bu<Op, BLOCK, 2>(x, rows, cols, ld, out, grid, nt, pf, cover, xmap, stream);
+        case 4: return rows_bu<Op, BLOCK, 4>(x, rows, cols, ld, out, grid, nt, pf, cover, xmap, stream);
+        case 8: return rows_bu<Op, BLOCK, 8>(x, rows, cols, ld, out, grid, nt, pf, cover, xmap, stream);
+        case 16: return rows_bu<Op, BLOCK, 16>(x, rows, cols, ld, out, grid, nt, pf, cover, xmap, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -789,13 +806,14 @@ inline hipError_t rows_split_u(const typename Op::elem_t* x, size_t rows, size_t
 
 template <class Op, int LOG2L, int V, bool SCALAR>
 inline hipError_t rows_packed_lv(const typename Op::elem_t* x, size_t rows, size_t cols, size_t ld,
-                                 typename Op::out_t* out, int grid, bool nt, hipStream_t stream) {
+                                 typename Op::out_t* out, int grid, bool nt, int xmap, hipStream_t stream) {
+    const int xm = xmap > 0 && grid % (kXcds * xmap) == 0 ? xmap : 0;
     if (nt)
         hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, SCALAR, true>), dim3(grid), dim3(kWave), 0, stream,
-                           x, rows, cols, ld, out);
+                           x, rows, cols, ld, out, xm);
     else
         hipLaunchKernelGGL((rows_packed_kernel<Op, LOG2L, V, SCALAR, false>), dim3(grid), dim3(kWave), 0, stream,
-                           x, rows, cols, ld, out);
+                           x, rows, cols, ld, out, xm);
     return hipGetLastError();
 }
 
@@ -806,15 +824,15 @@ inline hipError_t rows_packed_v(const typename Op::elem_t* x, size_t rows, size_
                                 typename Op::out_t* out, const RowsLaunch& L, bool nt, hipStream_t stream) {
     if constexpr (LOG2L == (SCALAR ? 6 : 4)) {
         switch (L.packed_v) {
-            case 1: return rows_packed_lv<Op, LOG2L, 1, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
-            case 2: return rows_packed_lv<Op, LOG2L, 2, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
-            case 4: return rows_packed_lv<Op, LOG2L, 4, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
-            case 8: return rows_packed_lv<Op, LOG2L, 8, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
+            case 1: return rows_packed_lv<Op, LOG2L, 1, SCALAR>(x, rows, cols, ld, out, L.grid, nt, L.xmap, stream);
+            case 2: return rows_packed_lv<Op, LOG2L, 2, SCALAR>(x, rows, cols, ld, out, L.grid, nt, L.xmap, stream);
+            case 4: return rows_packed_lv<Op, LOG2L, 4, SCALAR>(x, rows, cols, ld, out, L.grid, nt, L.xmap, stream);
+            case 8: return rows_packed_lv<Op, LOG2L, 8, SCALAR>(x, rows, cols, ld, out, L.grid, nt, L.xmap, stream);
             default: return hipErrorInvalidValue;
         }
     } else {
         if (L.packed_v != 1) return hipErrorInvalidValue;
-        return rows_packed_lv<Op, LOG2L, 1, SCALAR>(x, rows, cols, ld, out, L.grid, nt, stream);
+        return rows_packed_lv<Op, LOG2L, 1, SCALAR>(x, rows, cols, ld, out, L.grid, nt, L.xmap, stream);
     }
 }
 
@@ -845,12 +863,13 @@ inline hipError_t rows_staged_go(const typename Op::elem_t* x, size_t rows, size
     // The staged tiles are always loaded non-temporally (the default of every
     // row shape): built only that way, which halves this kernel's variants.
     (void)nt;
+    const int xm = L.xmap > 0 && L.grid % (kXcds * L.xmap) == 0 ? L.xmap : 0;
     if (L.staged_hold > 0)
         hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true, SPREAD>), dim3(L.grid),
-                           dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out);
+                           dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out, xm);
     else
         hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, false, SPREAD>), dim3(L.grid),
-                           dim3(kWave), 0, stream, x, rows, cols, ld, sh, L.staged_rows, out);
+                           dim3(kWave), 0, stream, x, rows, cols, ld, sh, L.staged_rows, out, xm);
     return hipGetLastError();
 }
 
@@ -921,10 +940,10 @@ inline hipError_t rows_op(const typename Op::elem_t* x, size_t rows, size_t cols
         }
     }
     switch (p.block) {
-        case 64: return rows_b<Op, 64>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
-        case 128: return rows_b<Op, 128>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
-        case 256: return rows_b<Op, 256>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
-        case 512: return rows_b<Op, 512>(x, rows, cols, ld, out, L.grid, L.cover != 0, p, stream);
+        case 64: return rows_b<Op, 64>(x, rows, cols, ld, out, L.grid, L.cover != 0, L.xmap, p, stream);
+        case 128: return rows_b<Op, 128>(x, rows, cols, ld, out, L.grid, L.cover != 0, L.xmap, p, stream);
+        case 256: return rows_b<Op, 256>(x, rows, cols, ld, out, L.grid, L.cover != 0, L.xmap, p, stream);
+        case 512: return rows_b<Op, 512>(x, rows, cols, ld, out, L.grid, L.cover != 0, L.xmap, p, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -612,7 +612,8 @@ ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023
               (200, 33), (100, 511), (1000, 100), (3000, 2), (1, 3), (2, 2), (5, 6), (1001, 6),
               (1, 2048), (2, 1023), (3, 1025), (300, 7), (9, 510), (20_001, 5), (5, 1021), (40, 700), (3, 1023),
               (1, 5000), (2, 1030), (7, 1031), (1, 16), (17, 16), (100_003, 16), (60_001, 7), (50_000, 6),
-              (40_001, 25), (30_007, 12), (700, 1028), (300, 1100), (129, 4100), (257, 2052)]
+              (40_001, 25), (30_007, 12), (700, 1028), (300, 1100), (129, 4100), (257, 2052),
+              (5000, 1020), (3000, 1025), (2000, 3001)]
 ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1, max_blocks=3, short_rows=1),
                 dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
                 dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0),
@@ -627,7 +628,10 @@ ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1,
                 dict(short_rows=3, lines=1), dict(short_rows=11, lines=1, unroll=8),
                 dict(short_rows=17, max_blocks=1), dict(short_rows=17, defer=2),
                 dict(short_rows=17, defer=2, max_blocks=3), dict(short_rows=17, defer=1), dict(defer=2),
-                dict(short_rows=17, defer=2, max_blocks=5, nontemporal=0))
+                dict(short_rows=17, defer=2, max_blocks=5, nontemporal=0),
+                dict(xcd=1), dict(xcd=2), dict(xcd=3, max_blocks=48), dict(xcd=2, short_rows=1, max_blocks=17),
+                dict(xcd=2, cover=2, short_rows=1, max_blocks=40), dict(xcd=4, prefetch=1, short_rows=1, max_blocks=33),
+                dict(xcd=2, short_rows=3, max_blocks=20))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
@@ -694,7 +698,8 @@ def test_rows_staged_any_offset(rows, cols, gap):
 
 @pytest.mark.parametrize("rows,cols,ld", [(3, 5, 7), (10, 1000, 1003), (257, 4096, 4100), (64, 63, 64),
                                           (1, 10, 10), (5, 0, 3), (1000, 129, 1024), (300, 16, 20),
-                                          (100, 64, 68), (40, 128, 132), (65, 4, 8)])
+                                          (100, 64, 68), (40, 128, 132), (65, 4, 8), (2000, 1000, 1003),
+                                          (1500, 1025, 1028), (1200, 2000, 2001)])
 def test_rows_strided(rows, cols, ld):
     # Rows spaced ld apart: the gap holds NaN, which must never enter a result.
     rng = np.random.default_rng(rows + cols + ld)
@@ -1321,7 +1326,7 @@ def test_full_rows_short_1gib():
     # identical.
     a, x = _load("rows_f32_65536x4096")
     flat = a.reshape(-1)
-    for cols in (1, 3, 4, 7, 12, 16, 17, 21, 32, 64, 100, 256, 1000):
+    for cols in (1, 3, 4, 7, 12, 16, 17, 21, 32, 64, 100, 256, 1000, 1025, 3001):
         rows = flat.size // cols
         say(f"red_rows_sum_f32 / red_rows_max_f32 rows_f32_65536x4096 as {rows}x{cols}, held and tile by tile")
         v = x.view(-1)[: rows * cols].view(rows, cols)
