@@ -256,6 +256,14 @@ constexpr size_t kLineBytes = 128;
 // At power-of-two pitches (contiguous 1, 4, 16, 32, 64, 256, 512, 1024, 4096
 // and 16384 columns, 1000 columns at ld 1024) grouping ran 5-7% slower.
 constexpr size_t kXcdGroupMinPhases = 8;
+// ... and only when rounding the phases down to a multiple of 8 keeps this
+// share of them: 300 contiguous columns (38 blocks per view row, 14 phases,
+// cut to 8) ran 16-25% slower grouped. Rounding up instead lost more where
+// the default grids sit just under 1024 single-wave blocks (4 per CU): 9
+// blocks per row and 120 phases instead of 112 took 4096 columns at ld 4097
+// from 6.3 to 4.7 TB/s, 1020 at 1021 (344 phases instead of 336) from 6.4
+// to 4.6, as the grid passed 1024 and some CUs held a fifth wave.
+constexpr double kXcdGroupKeepPhases = 0.75;
 
 // ------------------------------------------------------------ columns: shapes
 // Short-wide matrices (more than this many blocks of 256 columns), and rows

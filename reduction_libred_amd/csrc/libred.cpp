@@ -891,11 +891,14 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         if (nchunks < 1) nchunks = 1;
     }
     // Blocks grouped per XCD (see ColsLaunch::xmap and
-    // kXcdGroupMinPhases): a whole number of phases per XCD.
+    // kXcdGroupMinPhases): a whole number of phases per XCD, rounded down
+    // (kXcdGroupKeepPhases).
     const size_t pitch = ld * sizeof(float);
     const bool pow2_pitch = pitch != 0 && (pitch & (pitch - 1)) == 0;
-    if ((p.xcd == 2 || (p.xcd == 0 && !pow2_pitch)) && nchunks >= libred::table::kXcdGroupMinPhases) {
-        nchunks = nchunks / libred::kXcds * libred::kXcds;
+    const size_t down = nchunks / libred::kXcds * libred::kXcds;
+    const bool keeps = (double)down >= libred::table::kXcdGroupKeepPhases * (double)nchunks;
+    if ((p.xcd == 2 || (p.xcd == 0 && !pow2_pitch && keeps)) && down >= libred::table::kXcdGroupMinPhases) {
+        nchunks = down;
         L.xmap = 1;
     }
     L.nchunks = nchunks;
