@@ -197,8 +197,9 @@ typedef struct red_rows_policy {
  * block b starts at its (b mod m)-th of m groups and wraps around to the
  * first, so the waves read rows spread over the matrix; 3 = one run of
  * consecutive rows per phase (about rows / n); 0 = the library's choice
- * (2 when the row pitch as read, ld or the view's, is a multiple of 255 or
- * 257 floats, pitches whose band reads fill a few memory channels' queues;
+ * (when the row pitch as read, ld or the view's, is a multiple of 255 or
+ * 257 floats, pitches whose band reads fill a few memory channels' queues:
+ * 3 for a matrix read unfolded, 2 through an m-row view;
  * 3 when a wave's load covers several rows (fewer than 64 column groups)
  * whose bytes are not a whole number of 128-byte lines, so that the line two
  * loads share is read by one wave; else 1). The order changes the order in which a column's elements are

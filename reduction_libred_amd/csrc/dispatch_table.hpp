@@ -225,6 +225,15 @@ constexpr double kFoldGain = 0.05;
 // 765 and 1530 columns (32640- and 97920-byte view rows) at 6.0-6.2 (+0.5),
 // 1028, 2056, 3084 and 4112 at 5.4-5.6 (+0.1-0.4); at the other widths of
 // that scan the rotated order ran up to 3% slower, so it stays off there.
+// That holds for the views (32-row views of 765, 2040, 2056, 3060, 3084,
+// 4080 and 5100 columns: rotated 4-15% faster than runs of rows, with the
+// blocks grouped per XCD). A matrix read unfolded at such a pitch takes one
+// run of rows per phase instead: with the XCD grouping, runs against
+// rotated, sums TB/s, 1024 columns at ld 1028: 6.23 -> 6.87, 2000 at 2056:
+// 6.11 -> 6.65, 1016 at 1020: 6.14 -> 6.85, 508 at 510: 6.04 -> 6.54, 500 at
+// 514: 5.97 -> 6.42, 512 at 514: 4.87 -> 5.13, 4096 at 4112: 6.21 -> 6.41,
+// contiguous 8160 (unfolded): 6.31 -> 6.57; 255 and 256 at ld 257 within
+// 2% either way.
 constexpr size_t kRotateRowsPitchFactorA = 255;
 constexpr size_t kRotateRowsPitchFactorB = 257;
 // A narrow matrix (or view) whose wave loads each cover several rows

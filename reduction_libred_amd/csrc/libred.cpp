@@ -910,7 +910,7 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         L.order = p.order - 1;
     else if (rows > 1 && (ld % libred::table::kRotateRowsPitchFactorA == 0 ||
                           ld % libred::table::kRotateRowsPitchFactorB == 0))
-        L.order = 1;
+        L.order = (L.fold_m == 1 && L.rot == 0) ? 2 : 1;  // runs unfolded, rotated through views
     else if (rows > 1 && L.ngroups < 64 && load_rows * ld * sizeof(float) % libred::table::kLineBytes != 0)
         L.order = 2;
     else
