@@ -140,7 +140,11 @@ typedef struct red_flat_policy {
  * which share the 128-byte line where one ends, are mostly read on one XCD;
  * 0 = the library's choice (runs of 64 for rows of 768 to 4095 floats that
  * do not all start on a 128-byte line, else 1). The results are the same
- * either way. */
+ * either way; and `max_fold`, how the LDS-staged kernel's maxima fold a
+ * lane's elements: 1 = a compare and a select, 2 = a hardware max of the
+ * canonicalized element (a signalling NaN is made quiet first, so a NaN
+ * never wins either way), 0 = the library's choice (2 for rows of fewer
+ * than 64 floats, else 1). The results are the same either way. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
@@ -153,6 +157,7 @@ typedef struct red_rows_policy {
     int defer;
     int lines;
     int xcd;
+    int max_fold;
 } red_rows_policy;
 
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,

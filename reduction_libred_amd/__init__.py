@@ -54,7 +54,8 @@ class RowsPolicy(ctypes.Structure):
                 ("nontemporal", ctypes.c_int), ("max_blocks", ctypes.c_int),
                 ("split", ctypes.c_int), ("prefetch", ctypes.c_int), ("short_rows", ctypes.c_int),
                 ("cover", ctypes.c_int),
-                ("defer", ctypes.c_int), ("lines", ctypes.c_int), ("xcd", ctypes.c_int)]
+                ("defer", ctypes.c_int), ("lines", ctypes.c_int), ("xcd", ctypes.c_int),
+                ("max_fold", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -164,6 +164,20 @@ constexpr size_t kSplitRowsBelow = 1024;
 constexpr size_t kSplitMinCols = 8192;
 constexpr size_t kSplitTargetWaves = 1024;
 
+// ------------------------------------------------------------ rows: max fold
+// The LDS-staged kernel's maxima fold each lane's elements with a hardware
+// max of the canonicalized element (v_max3_f32 over two elements, 29
+// instructions per 8 elements) instead of a compare and a select through
+// an SGPR pair with a wait state between them (41), for rows of fewer than
+// this many floats. Two builds alternating over 1 GiB maxima (three rounds,
+// spread under 1%): 14 shapes of 33-63 floats +5.7% on average (33: 4.95 ->
+// 5.56, 35: 5.47 -> 6.11, 52: 5.63 -> 6.37, 60: 5.66 -> 6.46 TB/s; 33 at an
+// unaligned x -4.9%); 64 shapes of 64-1023 floats +2.2% on average but 16
+// of them 2-8% slower (64: 6.82 -> 6.50, 65: 6.55 -> 6.11, 100: 6.69 ->
+// 6.14, 256: 6.90 -> 6.73), with no launch shape or LDS bank pattern that
+// separates them from the gainers (120, 160, 208, 304, 376: +8-13%).
+constexpr size_t kStagedMaxFmaxBelowCols = 64;
+
 // ------------------------------------------------------------ rows: XCD grouping
 // Rows of kGroupRowsMinCols to kGroupRowsMaxCols - 1 floats that do not all
 // start on kRowLineBytes lines are read by grid-stride kernels whose block

@@ -48,6 +48,7 @@ struct RowsPolicy {
     int defer;
     int lines;
     int xcd;
+    int max_fold;
 };
 
 // How one row call launches: `grid` blocks of the one-wave-per-row kernel,
@@ -74,6 +75,7 @@ struct RowsLaunch {
                         //   stored in bursts
     int xmap;           // grid-stride row kernels: the blocks of each XCD take consecutive
                         //   block indices (used when the grid is a multiple of kXcds)
+    int staged_fmax;    // maxima in the LDS-staged kernel fold with a hardware max
 };
 
 // Narrow rows: a contiguous, 16-byte aligned matrix of rows of 1 to

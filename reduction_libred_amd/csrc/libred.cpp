@@ -339,7 +339,7 @@ RowsPolicy default_rows(size_t cols) {
 RowsPolicy to_rows(const red_rows_policy* p, size_t cols) {
     if (!p) return default_rows(cols);
     RowsPolicy r = {p->block,      p->unroll, p->nontemporal, p->max_blocks, p->split,
-                    p->prefetch,   p->short_rows, p->cover,   p->defer,      p->lines, p->xcd};
+                    p->prefetch,   p->short_rows, p->cover,   p->defer,      p->lines, p->xcd, p->max_fold};
     return r;
 }
 
@@ -396,7 +396,7 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (st != RED_OK) return st;
     namespace T = libred::table;
 
-    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    libred::RowsLaunch L = {0, 0, nullptr, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     // Grid-stride kernels with the blocks of each XCD on consecutive rows
     // (RowsLaunch::xmap): the grid rounded up to a multiple of kXcds, so a
     // wave keeps its number of rows or gets one fewer.
@@ -587,6 +587,9 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         const size_t tiles = (rows + L.staged_rows - 1) / L.staged_rows;
         L.grid = (int)(tiles < max_blocks ? tiles : max_blocks);
         group();
+        // Maxima fold with a hardware max (max_fold 2), or where the table
+        // says so (max_fold 0); the row sums ignore this.
+        L.staged_fmax = p.max_fold == 2 || (p.max_fold == 0 && cols < T::kStagedMaxFmaxBelowCols) ? 1 : 0;
         // A wave's results are held in LDS and stored after its last tile
         // (defer 0) when they fit beside its staging tile in one wave's share
         // of a CU's LDS (the grid's waves spread evenly over the CUs) and in
@@ -1124,6 +1127,7 @@ void red_default_rows_policy(red_rows_policy* p) {
     p->defer = kDefaultRows.defer;
     p->lines = kDefaultRows.lines;
     p->xcd = kDefaultRows.xcd;
+    p->max_fold = kDefaultRows.max_fold;
 }
 
 size_t red_flat_grid(size_t n, const red_flat_policy* pol) {

@@ -504,7 +504,11 @@ __global__ __launch_bounds__(kWave) void rows_packed_kernel(const typename Op::e
 //
 // The host ensures that a tile's span plus 3 fits 256 * U elements, that the
 // matrix spans at least 8 elements, and that R * ld >= 4.
-template <class Op, int LOG2S, int U, bool NT, bool VREAD, bool HOLD, bool SPREAD>
+// FMAX (maxima only): each lane folds its elements with a hardware max of the
+// canonicalized element (a signalling NaN made quiet, so that a NaN never
+// wins, as with the compare-and-select), not a compare and a select through
+// VCC.
+template <class Op, int LOG2S, int U, bool NT, bool VREAD, bool HOLD, bool SPREAD, bool FMAX = false>
 __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::elem_t* __restrict__ x,
                                                             size_t rows, size_t cols, size_t ld,
                                                             unsigned int sh, unsigned int R,
@@ -521,6 +525,13 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
     // 256 and 384 floats: 6.1-6.5 -> 6.6-6.9 TB/s). Float64 sums, and maxima
     // with one or two lanes per row, measured as fast or faster with four.
     constexpr bool kEightReads = sizeof(acc_t) == 4 && LOG2S >= 2;
+    static_assert(!FMAX || std::is_same_v<Op, MaxF32>, "the fmax fold is the float32 max's");
+    auto fold = [](acc_t a, acc_t b) -> acc_t {
+        if constexpr (FMAX)
+            return __builtin_fmaxf(a, __builtin_canonicalizef(b));
+        else
+            return Op::combine(a, b);
+    };
     __shared__ vec_t stage[kWave * U];
     extern __shared__ __align__(16) unsigned char rows_staged_held[];
     typename Op::out_t* held = reinterpret_cast<typename Op::out_t*>(rows_staged_held);
@@ -605,15 +616,15 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
                         for (; j + S < V; j += 2 * S) {
                             const vec_t v0 = rowv[j], v1 = rowv[j + S];
 #pragma unroll
-                            for (int k = 0; k < (int)E; ++k) a = Op::combine(a, Op::lift(v0[k], j * E + k));
+                            for (int k = 0; k < (int)E; ++k) a = fold(a, Op::lift(v0[k], j * E + k));
 #pragma unroll
-                            for (int k = 0; k < (int)E; ++k) a = Op::combine(a, Op::lift(v1[k], (j + S) * E + k));
+                            for (int k = 0; k < (int)E; ++k) a = fold(a, Op::lift(v1[k], (j + S) * E + k));
                         }
                     }
                     for (; j < V; j += S) {
                         const vec_t v = rowv[j];
 #pragma unroll
-                        for (int k = 0; k < (int)E; ++k) a = Op::combine(a, Op::lift(v[k], j * E + k));
+                        for (int k = 0; k < (int)E; ++k) a = fold(a, Op::lift(v[k], j * E + k));
                     }
                 }
             } else if constexpr (SPREAD) {
@@ -624,14 +635,14 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
                     for (; i + 4 <= m_lane; i += 4) {
                         const unsigned int j1 = next(j), j2 = next(j1), j3 = next(j2);
                         const elem_t e0 = row[j], e1 = row[j1], e2 = row[j2], e3 = row[j3];
-                        a = Op::combine(a, Op::lift(e0, j));
-                        a = Op::combine(a, Op::lift(e1, j1));
-                        a = Op::combine(a, Op::lift(e2, j2));
-                        a = Op::combine(a, Op::lift(e3, j3));
+                        a = fold(a, Op::lift(e0, j));
+                        a = fold(a, Op::lift(e1, j1));
+                        a = fold(a, Op::lift(e2, j2));
+                        a = fold(a, Op::lift(e3, j3));
                         j = next(j3);
                     }
                     for (; i < m_lane; ++i) {
-                        a = Op::combine(a, Op::lift(row[j], j));
+                        a = fold(a, Op::lift(row[j], j));
                         j = next(j);
                     }
                 }
@@ -644,17 +655,17 @@ __global__ __launch_bounds__(kWave) void rows_staged_kernel(const typename Op::e
 #pragma unroll
                         for (int k = 0; k < 8; ++k) e[k] = row[j + k * S];
 #pragma unroll
-                        for (int k = 0; k < 8; ++k) a = Op::combine(a, Op::lift(e[k], j + k * S));
+                        for (int k = 0; k < 8; ++k) a = fold(a, Op::lift(e[k], j + k * S));
                     }
                 }
                 for (; j + 3 * S < C; j += 4 * S) {  // four LDS reads in flight
                     const elem_t e0 = row[j], e1 = row[j + S], e2 = row[j + 2 * S], e3 = row[j + 3 * S];
-                    a = Op::combine(a, Op::lift(e0, j));
-                    a = Op::combine(a, Op::lift(e1, j + S));
-                    a = Op::combine(a, Op::lift(e2, j + 2 * S));
-                    a = Op::combine(a, Op::lift(e3, j + 3 * S));
+                    a = fold(a, Op::lift(e0, j));
+                    a = fold(a, Op::lift(e1, j + S));
+                    a = fold(a, Op::lift(e2, j + 2 * S));
+                    a = fold(a, Op::lift(e3, j + 3 * S));
                 }
-                for (; j < C; j += S) a = Op::combine(a, Op::lift(row[j], j));
+                for (; j < C; j += S) a = fold(a, Op::lift(row[j], j));
             }
             a = segment_reduce<Op, LOG2S>(a);
             if (r < rows_t && leader) {
@@ -864,6 +875,17 @@ inline hipError_t rows_staged_go(const typename Op::elem_t* x, size_t rows, size
     // row shape): built only that way, which halves this kernel's variants.
     (void)nt;
     const int xm = L.xmap > 0 && L.grid % (kXcds * L.xmap) == 0 ? L.xmap : 0;
+    if constexpr (std::is_same_v<Op, MaxF32>) {
+        if (L.staged_fmax) {
+            if (L.staged_hold > 0)
+                hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true, SPREAD, true>), dim3(L.grid),
+                                   dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out, xm);
+            else
+                hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, false, SPREAD, true>), dim3(L.grid),
+                                   dim3(kWave), 0, stream, x, rows, cols, ld, sh, L.staged_rows, out, xm);
+            return hipGetLastError();
+        }
+    }
     if (L.staged_hold > 0)
         hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true, SPREAD>), dim3(L.grid),
                            dim3(kWave), held_bytes, stream, x, rows, cols, ld, sh, L.staged_rows, out, xm);

@@ -11,7 +11,8 @@ bool rows_policy_supported(const RowsPolicy& p) {
     return b && u && (p.nontemporal == 0 || p.nontemporal == 1) && p.max_blocks >= 1 && p.split >= 0 &&
            p.split <= 2 && (p.prefetch == 0 || p.prefetch == 1) && p.cover >= 0 && p.cover <= 2 &&
            p.short_rows >= 0 && p.short_rows <= 17 && p.defer >= 0 && p.defer <= 2 && p.lines >= 0 &&
-           p.lines <= 2 && p.xcd >= 0 && p.xcd <= 4096;
+           p.lines <= 2 && p.xcd >= 0 && p.xcd <= 4096 &&
+           p.max_fold >= 0 && p.max_fold <= 2;
 }
 
 hipError_t launch_rows_sum_f32(const float* x, size_t rows, size_t cols, size_t ld, float* out,

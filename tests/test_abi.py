@@ -122,13 +122,14 @@ def test_rows_argument_errors():
     # no-op).
     base = rl.red_default_rows_policy()
     assert base.cover == 0 and base.prefetch == 0 and base.short_rows == 0 and base.defer == 0
-    assert base.xcd == 0
+    assert base.xcd == 0 and base.max_fold == 0
     for field, value, ok in (("cover", 3, False), ("cover", -1, False), ("cover", 2, True),
                              ("defer", 1, True), ("defer", 2, True), ("defer", 3, False), ("defer", -1, False),
                              ("prefetch", 2, False), ("prefetch", 1, True), ("short_rows", 10, True),
                              ("short_rows", 9, True), ("short_rows", 16, True), ("short_rows", 17, True), ("short_rows", 18, False),
                              ("split", 3, False), ("xcd", -1, False), ("xcd", 1, True), ("xcd", 2, True),
-                             ("xcd", 64, True), ("xcd", 4096, True), ("xcd", 4097, False)):
+                             ("xcd", 64, True), ("xcd", 4096, True), ("xcd", 4097, False),
+                             ("max_fold", 3, False), ("max_fold", -1, False), ("max_fold", 2, True)):
         pol = rl.red_default_rows_policy()
         setattr(pol, field, value)
         want = rl.RED_OK if ok else INVALID

@@ -631,7 +631,8 @@ ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1,
                 dict(short_rows=17, defer=2, max_blocks=5, nontemporal=0),
                 dict(xcd=1), dict(xcd=2), dict(xcd=3, max_blocks=48), dict(xcd=2, short_rows=1, max_blocks=17),
                 dict(xcd=2, cover=2, short_rows=1, max_blocks=40), dict(xcd=4, prefetch=1, short_rows=1, max_blocks=33),
-                dict(xcd=2, short_rows=3, max_blocks=20))
+                dict(xcd=2, short_rows=3, max_blocks=20), dict(max_fold=1), dict(max_fold=2),
+                dict(max_fold=2, short_rows=3), dict(max_fold=2, short_rows=12, defer=1))
 
 
 @pytest.mark.parametrize("rows,cols", ROW_SHAPES)
@@ -891,11 +892,12 @@ def test_rows_nonfinite(rows, cols, ld):
 def test_rows_signalling_nan():
     # Signalling NaNs (quiet bit clear, either sign) never win a row's max,
     # whichever way the kernel folds the row (compare-and-select, or a
-    # maximum instruction that quiets its inputs first), and make the sum
-    # NaN like any other NaN.
+    # maximum instruction that quiets its inputs first: the narrow kernel at
+    # some widths, the LDS-staged kernel below 64 floats or with max_fold 2),
+    # and make the sum NaN like any other NaN.
     rng = np.random.default_rng(4242)
     snans = np.array([0x7F800001, 0x7FA00000, 0xFF800123, 0x7FBFFFFF], np.uint32)
-    for cols in list(range(1, 34)) + [64]:
+    for cols in list(range(1, 34)) + [40, 48, 52, 60, 63, 64, 100, 260]:
         rows = 1500 if cols > 8 else 6000
         a = rng.standard_normal((rows, cols)).astype(np.float32)
         bits = a.view(np.uint32)
@@ -909,7 +911,8 @@ def test_rows_signalling_nan():
         M = oracle.rows_max_f32(a)
         assert M[3] == -np.inf and not np.isnan(M).any()
         x = torch.from_numpy(a).to(DEV)
-        for p in (None, dict(short_rows=17, defer=1), dict(short_rows=17, defer=2), dict(short_rows=1)):
+        for p in (None, dict(short_rows=17, defer=1), dict(short_rows=17, defer=2), dict(short_rows=1),
+                  dict(max_fold=1), dict(max_fold=2)):
             say(f"rows signalling NaN {rows}x{cols} policy={p}")
             s_ = rl.red_rows_sum_f32(x, policy=p)
             m_ = rl.red_rows_max_f32(x, policy=p)
