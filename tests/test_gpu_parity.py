@@ -1411,7 +1411,8 @@ def test_beyond_2p32_elements():
     """More than 2^32 elements (16 GiB of float32), so every element index and
     count needs 64 bits: sparse ones with one planted maximum past index 2^32,
     read as float32, as int32 bit patterns, as a 65536 x 65536 matrix by rows
-    and by columns, and as two rows of 2^31 (the split-row path)."""
+    and by columns, as two rows of 2^31 (the split-row path), by columns at
+    an odd leading dimension, and as rows of 1025 floats from x and x + 1."""
     n = (1 << 32) + 7
     p = (1 << 32) + 3                       # past 2^32, not a multiple of 64
     say(f"n = 2^32 + 7 ({4 * n / 2**30:.1f} GiB)")
@@ -1445,7 +1446,39 @@ def test_beyond_2p32_elements():
     say("two rows of 2^31 (split rows)")
     r2 = x[: 1 << 32].view(2, 1 << 31)
     assert torch.all(rl.red_rows_sum_f32(r2) == float(1 << 25))
-    del x, m, r2
+    # Columns at an odd leading dimension (shifted vectors, blocks grouped
+    # per XCD): 65535 rows of 65537 floats span 2^32 - 1 elements. Element
+    # r * 65537 + c is a one when r + c is a multiple of 64 (65537 = 1 mod 64).
+    ld = 65537
+    rows_s = n // ld
+    say(f"columns of a {rows_s} x 65536 view at ld {ld}")
+    ms = x[: rows_s * ld].view(rows_s, ld)[:, : 1 << 16]
+    r0 = (-np.arange(1 << 16)) % 64
+    want_s = np.where(r0 < rows_s, (rows_s - 1 - r0) // 64 + 1, 0).astype(np.float32)
+    assert np.array_equal(rl.red_cols_sum_f32(ms).cpu().numpy(), want_s)
+    assert np.array_equal(rl.red_cols_max_f32(ms).cpu().numpy(), (want_s > 0).astype(np.float32))
+    # Rows of 1025 floats (the cover kernel, blocks dealt to the XCDs in
+    # runs): 4190212 rows span more than 2^32 elements; the planted 5.0 sits
+    # in the last row.
+    rows_r = n // 1025
+    say(f"rows of a {rows_r} x 1025 view")
+    mr = x[: rows_r * 1025].view(rows_r, 1025)
+    lo = np.arange(rows_r, dtype=np.int64) * 1025
+    want_r = ((lo + 1024) // 64 - (lo + 63) // 64 + 1).astype(np.float64)
+    last = p // 1025
+    want_r[last] += 5.0
+    want_m = np.where(want_r > 0, 1.0, 0.0).astype(np.float32)
+    want_m[last] = 5.0
+    assert np.array_equal(rl.red_rows_sum_f32(mr).cpu().numpy(), want_r.astype(np.float32))
+    assert np.array_equal(rl.red_rows_max_f32(mr).cpu().numpy(), want_m)
+    # The same rows from x + 1 (rows that do not start 16-byte aligned).
+    mr1 = x[1: 1 + rows_r * 1025].view(rows_r, 1025)
+    lo1 = lo + 1
+    want_r1 = ((lo1 + 1024) // 64 - (lo1 + 63) // 64 + 1).astype(np.float64)
+    if (p - 1) // 1025 < rows_r:
+        want_r1[(p - 1) // 1025] += 5.0
+    assert np.array_equal(rl.red_rows_sum_f32(mr1).cpu().numpy(), want_r1.astype(np.float32))
+    del x, m, r2, ms, mr, mr1
     torch.cuda.empty_cache()
 
 
