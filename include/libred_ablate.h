@@ -211,11 +211,13 @@ typedef struct red_rows_policy {
  * added, never the fact that the result is fixed by the shape. `xcd`: which
  * blocks run on which of the 8 XCDs (the launch deals block b to XCD
  * b mod 8): 1 = block b takes column block b mod n of phase b / n (n column
- * blocks); 2 = the blocks of each XCD take every column block of a run of
- * consecutive phases (the phases rounded down to a multiple of 8), so that
- * the 128-byte line two column blocks, or two adjacent rows, share is
- * fetched into one XCD's L2; 0 = the library's choice (2 with at least 8
- * phases unless the row pitch as read is a power of two bytes, else 1). */
+ * blocks); 2 = the blocks of each XCD take one contiguous range of the
+ * indices j + k * n (column block j of phase k), so that the 128-byte line
+ * two column blocks, or two adjacent rows, share is fetched into one XCD's
+ * L2; 0 = the library's choice: 2 with at least 8 phases, rounded down to a
+ * multiple of 8 (each XCD then holds every column block of whole phases)
+ * when that keeps three quarters of them, unless the row pitch as read is
+ * a power of two bytes; else 1. */
 typedef struct red_cols_policy {
     int unroll;
     int nontemporal;

@@ -124,13 +124,19 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
     const unsigned int lane = threadIdx.x;
     const size_t nphases = gridDim.x / ncb;
     // xmap: the blocks of one XCD (blocks are dealt to the kXcds XCDs in
-    // turn, block b to XCD b mod kXcds) take every column block of a run of
-    // nphases / kXcds consecutive phases, so that a line two column blocks,
-    // or two adjacent rows, share is fetched into one XCD's L2 (nphases is
-    // then a multiple of kXcds).
-    const size_t xi = xmap ? blockIdx.x / kXcds : blockIdx.x;
-    const size_t j = xi % ncb;
-    const size_t k = xmap ? blockIdx.x % kXcds * (nphases / kXcds) + xi / ncb : xi / ncb;
+    // turn, block b to XCD b mod kXcds) take one contiguous range of block
+    // indices i = j + k * ncb, XCD x the range from x * (G / kXcds) +
+    // min(x, G mod kXcds), so that a line two neighbouring column blocks, or
+    // two adjacent rows, share is fetched into one XCD's L2. With nphases a
+    // multiple of kXcds each XCD holds every column block of a run of whole
+    // phases.
+    size_t bi = blockIdx.x;
+    if (xmap) {
+        const size_t x = blockIdx.x % kXcds, per = gridDim.x / kXcds, extra = gridDim.x % kXcds;
+        bi = x * per + (x < extra ? x : extra) + blockIdx.x / kXcds;
+    }
+    const size_t j = bi % ncb;
+    const size_t k = bi / ncb;
     const unsigned int g = lane % ngroups;
     const size_t group = kWave / ngroups;  // rows per load
     const size_t q = lane / ngroups;

@@ -287,6 +287,11 @@ constexpr size_t kXcdGroupMinPhases = 8;
 // from 6.3 to 4.7 TB/s, 1020 at 1021 (344 phases instead of 336) from 6.4
 // to 4.6, as the grid passed 1024 and some CUs held a fifth wave.
 constexpr double kXcdGroupKeepPhases = 0.75;
+// Launches with fewer phases stay in launch order. Grouping them as well
+// (contiguous ranges of column blocks per XCD, any grid) was measured on 16-row
+// views of odd widths, one or two phases each: +2 to +4% at 20001, 24577,
+// 50257 and 100003 columns, -4 to -8% at 8193, 12289, 16385, 65537 and
+// 131073, whose view pitches lie 64 bytes past a multiple of 256 KiB.
 
 // ------------------------------------------------------------ columns: shapes
 // Short-wide matrices (more than this many blocks of 256 columns), and rows

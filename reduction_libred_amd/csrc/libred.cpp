@@ -900,7 +900,9 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     const bool pow2_pitch = pitch != 0 && (pitch & (pitch - 1)) == 0;
     const size_t down = nchunks / libred::kXcds * libred::kXcds;
     const bool keeps = (double)down >= libred::table::kXcdGroupKeepPhases * (double)nchunks;
-    if ((p.xcd == 2 || (p.xcd == 0 && !pow2_pitch && keeps)) && down >= libred::table::kXcdGroupMinPhases) {
+    if (p.xcd == 2) {
+        L.xmap = 1;  // the kernel deals any grid
+    } else if (p.xcd == 0 && !pow2_pitch && keeps && down >= libred::table::kXcdGroupMinPhases) {
         nchunks = down;
         L.xmap = 1;
     }
