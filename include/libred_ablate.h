@@ -93,7 +93,8 @@ typedef struct red_flat_policy {
  *      16-byte aligned matrix go to the narrow kernel (17); other rows of
  *      fewer than 1024 floats go to the
  *      LDS-staged kernel when they are contiguous or their gaps (ld - cols)
- *      hold at most a quarter of a row, and the matrix spans at least 8
+ *      hold at most a quarter of a row (or, for rows of 3 to 128 floats,
+ *      at most 64 floats), and the matrix spans at least 8
  *      elements (any alignment of x: the first and last vectors of the
  *      matrix are read element by element when they reach outside it); it
  *      loads tiles of rows, gaps included, as 16-byte vectors whatever the

@@ -164,6 +164,24 @@ constexpr size_t kSplitRowsBelow = 1024;
 constexpr size_t kSplitMinCols = 8192;
 constexpr size_t kSplitTargetWaves = 1024;
 
+// ------------------------------------------------------------ rows: strided, staged
+// Strided rows of kStagedGapMinCols to kStagedGapMaxCols floats whose gaps
+// (ld - cols) hold at most kStagedGapMaxFloats floats go to the LDS-staged
+// kernel, which loads the gaps along, like rows whose gaps hold at most a
+// quarter of the row; the packed kernel, which reads each row's elements,
+// took the rest. Two builds alternating, 1 GiB (2^28 floats of rows of ld),
+// TB/s of matrix bytes, packed against staged: 3 at ld 5: 1.7 -> 2.7, 5 at 7:
+// 1.5 -> 3.4, 7 at 9: 2.0 -> 3.8, 7 at 16: 1.7 -> 2.5, 12 at 17: 1.7 -> 3.5,
+// 17 at 24: 1.2 -> 3.7, 17 at 32: 1.2 -> 3.3, 33 at 48: 1.3 -> 4.0, 40 at
+// 64: 2.7 -> 4.1, 60 at 80: 4.2 -> 4.5, 100 at 128: 3.8 -> 5.2, 100 at 150:
+// 1.9 -> 4.3 (19 shapes, +6 to +230%). Staged lost where the gaps are long or
+// the rows wide (100 at 300: 4.2 -> 2.3, 200 at 300: -13%, 300 at 400:
+// -10%, 200 at 256: -3%) and for rows of 1 or 2 floats one float apart
+// (-8 to -10%).
+constexpr size_t kStagedGapMinCols = 3;
+constexpr size_t kStagedGapMaxCols = 128;
+constexpr size_t kStagedGapMaxFloats = 64;
+
 // ------------------------------------------------------------ rows: max fold
 // The LDS-staged kernel's maxima fold each lane's elements with a hardware
 // max of the canonicalized element (v_max3_f32 over two elements, 29

@@ -413,7 +413,9 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // Rows of fewer than 1024 floats go to the LDS-staged kernel (short_rows
     // 0), or do so with 2^(short_rows - 3) lanes per row (short_rows 3-9),
     // when the rows are contiguous or their gaps hold at most a quarter of a
-    // row's elements (the tiles read the gaps along), the matrix spans at
+    // row's elements, or at most kStagedGapMaxFloats for rows of
+    // kStagedGapMinCols to kStagedGapMaxCols floats (the tiles read the gaps
+    // along), the matrix spans at
     // least 8 elements, and a tile fits 4096 floats. A contiguous, 16-byte
     // aligned matrix ("dense") is tiled in 16-byte aligned spans of rows;
     // other matrices in spans that start anywhere.
@@ -456,7 +458,11 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     if (p.short_rows == 17) p.short_rows = 0;  // where the register kernel does not apply: the default
     const bool staged_ok =
         cols > 0 && (dense ? rows * cols >= 4 && fold * cols <= T::kStagedMaxTileFloats
-                           : span_all >= 8 && (step - cols) * 4 <= cols && cols + 3 <= T::kStagedMaxTileFloats &&
+                           : span_all >= 8 &&
+                                 ((step - cols) * 4 <= cols ||
+                                  (cols >= T::kStagedGapMinCols && cols <= T::kStagedGapMaxCols &&
+                                   step - cols <= T::kStagedGapMaxFloats)) &&
+                                 cols + 3 <= T::kStagedMaxTileFloats &&
                                  (step == cols || cols < T::kStagedStridedBelowCols));
     const bool staged_default = p.short_rows == 0 && cols < T::kStagedBelowCols;
     if (staged_ok && (staged_default || p.short_rows >= 3)) {

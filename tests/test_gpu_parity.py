@@ -700,7 +700,9 @@ def test_rows_staged_any_offset(rows, cols, gap):
 @pytest.mark.parametrize("rows,cols,ld", [(3, 5, 7), (10, 1000, 1003), (257, 4096, 4100), (64, 63, 64),
                                           (1, 10, 10), (5, 0, 3), (1000, 129, 1024), (300, 16, 20),
                                           (100, 64, 68), (40, 128, 132), (65, 4, 8), (2000, 1000, 1003),
-                                          (1500, 1025, 1028), (1200, 2000, 2001)])
+                                          (1500, 1025, 1028), (1200, 2000, 2001), (3000, 17, 24), (700, 33, 48),
+                                          (400, 100, 150), (2500, 7, 16), (1777, 3, 8), (900, 128, 192),
+                                          (333, 129, 193), (200, 100, 300), (5000, 2, 3)])
 def test_rows_strided(rows, cols, ld):
     # Rows spaced ld apart: the gap holds NaN, which must never enter a result.
     rng = np.random.default_rng(rows + cols + ld)
