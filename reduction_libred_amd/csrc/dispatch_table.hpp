@@ -97,11 +97,13 @@ constexpr size_t kVectorReadMaxCols = 64;
 // Vector-read rows from this width take 4096-float tiles on 1024 waves, and
 // 64 floats 2048-float tiles (48: 5.9 -> 6.3, 60: 5.4 -> 6.4, 64: 6.5 -> 6.8).
 constexpr size_t kVectorReadBigTileFromCols = 44;
-// Element-read rows from 32 to 512 floats take the largest tile whose passes
-// are within this share as full as the fullest tile's (over 54 widths of
-// 33-512 floats: 97.3% of the best of four shapes on geometric mean).
+// Element-read rows from 32 to 1023 floats take the largest tile whose
+// passes are within this share as full as the fullest tile's (over 54 widths
+// of 33-512 floats: 97.3% of the best of four shapes on geometric mean).
+// Rows of 513-1023 floats joined the rule together with their lanes per row
+// (kWholeWaveAboveCols); see there.
 constexpr size_t kElementTileRuleMinCols = 32;
-constexpr size_t kElementTileRuleMaxCols = 512;
+constexpr size_t kElementTileRuleMaxCols = 1023;
 constexpr double kPassUseSlack = 0.02;
 // Rows of 33-39 floats: 2048-float tiles on 1024 waves when 4096-float tiles
 // leave no room to hold the results and their passes are within this share
@@ -115,13 +117,20 @@ constexpr int kStagedWaves = 2048;
 // Lanes per row, element reads: the largest power of two up to cols / 8
 // below 32 floats, cols / 16 for whole-vector rows from 128 floats, else
 // cols / 24 (a sweep of lanes per row: 8-16 elements per lane best); rows
-// over 512 floats take the whole wave.
+// over kWholeWaveAboveCols floats take the whole wave. Rows of 513-1023
+// floats took the whole wave and 1024-float tiles (one row per tile); with
+// these lanes (32 per row) and the tile rule above they ran +5.2% on average
+// over 12 widths (1 GiB, sums and maxima, two builds alternating: 520: 5.26
+// -> 5.80, 640: 6.13 -> 6.96, 900: 6.38 -> 6.92, 1023: 6.43 -> 7.07 TB/s;
+// 700, 768, 800 and 960 floats 2-3% slower). At 260 and 300 floats 8 lanes
+// instead of 16 ran 5% and 24-28% faster, but the divisor that picks them
+// (24) cost up to 8.5% at 128, 256, 320 and 512 floats, so it stays 16.
 constexpr size_t kLanesDivNarrow = 8;
 constexpr size_t kLanesDivWholeVec = 16;
 constexpr size_t kLanesDivOther = 24;
 constexpr size_t kLanesNarrowBelowCols = 32;
 constexpr size_t kLanesWholeVecFromCols = 128;
-constexpr size_t kWholeWaveAboveCols = 512;
+constexpr size_t kWholeWaveAboveCols = 1023;
 // Results held in LDS to the end of the wave under this width (with one or
 // two rows per tile, at 960-1020 floats, holding measured 1-10% slower).
 constexpr size_t kHoldBelowCols = 960;
