@@ -115,8 +115,9 @@ constexpr double kHoldSmallTileSlack = 0.05;
 constexpr int kStagedBigTileWaves = 1024;
 constexpr int kStagedWaves = 2048;
 // Lanes per row, element reads: the largest power of two up to cols / 8
-// below 32 floats, cols / 16 for whole-vector rows from 128 floats, else
-// cols / 24 (a sweep of lanes per row: 8-16 elements per lane best); rows
+// below 32 floats, cols / 16 for whole-vector rows from 128 floats that are
+// a multiple of kLanesWholeVecEvenCols floats, else cols / 24 (a sweep of
+// lanes per row: 8-16 elements per lane best); rows
 // over kWholeWaveAboveCols floats take the whole wave. Rows of 513-1023
 // floats took the whole wave and 1024-float tiles (one row per tile); with
 // these lanes (32 per row) and the tile rule above they ran +5.2% on average
@@ -124,12 +125,19 @@ constexpr int kStagedWaves = 2048;
 // -> 5.80, 640: 6.13 -> 6.96, 900: 6.38 -> 6.92, 1023: 6.43 -> 7.07 TB/s;
 // 700, 768, 800 and 960 floats 2-3% slower). At 260 and 300 floats 8 lanes
 // instead of 16 ran 5% and 24-28% faster, but the divisor that picks them
-// (24) cost up to 8.5% at 128, 256, 320 and 512 floats, so it stays 16.
+// (24) cost up to 8.5% at 128, 256, 320 and 512 floats, so whole-vector rows
+// take it only when they are not a multiple of 16 floats. Where 16 lanes
+// would leave lanes with unequal counts of elements, 24 ran faster (1 GiB,
+// two builds alternating, sums / maxima: 140: +10 / +10%, 148: +10 / +13%,
+// 276: +19 / +21%, 300: +24 / +28%, 308: +29 / +33%, 372: +5 / +12%;
+// 18 of 20 such widths of 132-500 floats within -3% or faster, 132 and 340
+// sums -3%); the multiples of 16 were unchanged.
 constexpr size_t kLanesDivNarrow = 8;
 constexpr size_t kLanesDivWholeVec = 16;
 constexpr size_t kLanesDivOther = 24;
 constexpr size_t kLanesNarrowBelowCols = 32;
 constexpr size_t kLanesWholeVecFromCols = 128;
+constexpr size_t kLanesWholeVecEvenCols = 16;
 constexpr size_t kWholeWaveAboveCols = 1023;
 // Results held in LDS to the end of the wave under this width (with one or
 // two rows per tile, at 960-1020 floats, holding measured 1-10% slower).

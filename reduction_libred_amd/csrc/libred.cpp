@@ -497,8 +497,9 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             // for rows of whole vectors from 128 floats (4096-float tiles);
             // longer rows take the whole wave.
             const size_t per = cols < T::kLanesNarrowBelowCols ? T::kLanesDivNarrow
-                               : (cols % 4 == 0 && cols >= T::kLanesWholeVecFromCols) ? T::kLanesDivWholeVec
-                                                                                        : T::kLanesDivOther;
+                               : (cols % 4 == 0 && cols >= T::kLanesWholeVecFromCols &&
+                                  cols % T::kLanesWholeVecEvenCols == 0) ? T::kLanesDivWholeVec
+                                                                          : T::kLanesDivOther;
             int lg = 0;
             while (lg < 6 && ((size_t)2 << lg) <= cols / per) ++lg;
             L.staged_log2s = cols > T::kWholeWaveAboveCols ? 6 : lg;

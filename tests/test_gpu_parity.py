@@ -613,7 +613,8 @@ ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023
               (1, 2048), (2, 1023), (3, 1025), (300, 7), (9, 510), (20_001, 5), (5, 1021), (40, 700), (3, 1023),
               (1, 5000), (2, 1030), (7, 1031), (1, 16), (17, 16), (100_003, 16), (60_001, 7), (50_000, 6),
               (40_001, 25), (30_007, 12), (700, 1028), (300, 1100), (129, 4100), (257, 2052),
-              (5000, 1020), (3000, 1025), (2000, 3001)]
+              (5000, 1020), (3000, 1025), (2000, 3001), (500, 300), (301, 276), (257, 148), (100, 372),
+              (77, 520), (65, 700), (33, 1000)]
 ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1, max_blocks=3, short_rows=1),
                 dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
                 dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0),
