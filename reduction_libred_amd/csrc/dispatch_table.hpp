@@ -120,10 +120,11 @@ constexpr int kStagedWaves = 2048;
 // lanes per row: 8-16 elements per lane best); rows
 // over kWholeWaveAboveCols floats take the whole wave. Rows of 513-1023
 // floats took the whole wave and 1024-float tiles (one row per tile); with
-// these lanes (32 per row) and the tile rule above they ran +5.2% on average
+// these lanes (16 or 32 per row) and the tile rule above they ran +5.2% on average
 // over 12 widths (1 GiB, sums and maxima, two builds alternating: 520: 5.26
 // -> 5.80, 640: 6.13 -> 6.96, 900: 6.38 -> 6.92, 1023: 6.43 -> 7.07 TB/s;
-// 700, 768, 800 and 960 floats 2-3% slower). At 260 and 300 floats 8 lanes
+// 700, 768, 800 and 960 floats 2-3% slower; they now take their lanes by
+// the rows of a tile, below). At 260 and 300 floats 8 lanes
 // instead of 16 ran 5% and 24-28% faster, but the divisor that picks them
 // (24) cost up to 8.5% at 128, 256, 320 and 512 floats, so whole-vector rows
 // take it only when they are not a multiple of 16 floats. Where 16 lanes
@@ -132,6 +133,23 @@ constexpr int kStagedWaves = 2048;
 // 276: +19 / +21%, 300: +24 / +28%, 308: +29 / +33%, 372: +5 / +12%;
 // 18 of 20 such widths of 132-500 floats within -3% or faster, 132 and 340
 // sums -3%); the multiples of 16 were unchanged.
+// Rows of kLanesByTileFromCols to kWholeWaveAboveCols floats (element
+// reads, 4096-float tiles on 1024 waves) take their lanes by the rows R such
+// a tile holds: 16 for R >= 7 (two passes of four rows), 8 for R = 5 and for
+// R = 6 below kLanesSixRowsWideFromCols floats (one pass), 32 for R = 6 from
+// there (three passes of two rows), 16 for R = 4 below
+// kLanesFourRowsWideFromCols floats (one pass) and 32 from there (two
+// passes). Sweep on 1 GiB (sums and maxima, medians of three alternating
+// rounds of 8, 16 and 32 lanes on 1024 and 2048 waves, 81 widths of 514-1022
+// floats of all four residues mod 4): cols / 24 lanes left R = 5 and R = 6
+// with 16 (two passes, the second 1/4 or 1/2 full), 10-20% slower than 8
+// lanes, and R = 4 with 32 from 768 floats, 3-8% slower than 16 below 900.
+constexpr size_t kLanesByTileFromCols = 513;
+constexpr size_t kLanesSixRowsWideFromCols = 640;
+constexpr size_t kLanesFourRowsWideFromCols = 900;
+// ... and where such a tile's rows span fewer floats than this (odd widths up
+// to 583 floats: four rows), 2048 waves ran 5-7% faster than 1024.
+constexpr size_t kStagedSparseTileFloats = 2336;
 constexpr size_t kLanesDivNarrow = 8;
 constexpr size_t kLanesDivWholeVec = 16;
 constexpr size_t kLanesDivOther = 24;

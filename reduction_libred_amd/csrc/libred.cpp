@@ -475,38 +475,6 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         const bool vec_rows = cols % 4 == 0 && sh == 0 && step % 4 == 0;
         size_t max_blocks = (size_t)p.max_blocks;
         const bool vread_default = vec_rows && cols <= T::kVectorReadMaxCols;
-        // Lanes per row first: the tile size below depends on them.
-        if (p.short_rows >= 10) {  // vector reads (rows of whole vectors), 2^(short_rows - 10) lanes
-            L.staged_log2s = p.short_rows - 10;
-            L.staged_vread = vec_rows ? 1 : 0;
-        } else if (p.short_rows >= 3) {
-            L.staged_log2s = p.short_rows - 3;
-        } else if (vread_default) {
-            // Rows of up to 16 whole vectors: 16-byte reads from LDS, one lane
-            // per 2 vectors of the row (per 4 from 16 vectors). Element reads
-            // at a stride of cols words put the rows of a pass on the same
-            // LDS banks (8-32 floats: 5.1-5.5 -> 5.4-5.9 TB/s).
-            const size_t v = cols / 4, per = v >= 16 ? 4 : 2;
-            int lg = 0;
-            while (((size_t)2 << lg) <= v / per) ++lg;
-            L.staged_log2s = lg;
-            L.staged_vread = 1;
-        } else {
-            // Lanes per row: the largest power of two up to cols / 8 below
-            // 32 floats (1024-float tiles), cols / 24 from there, or cols / 16
-            // for rows of whole vectors from 128 floats (4096-float tiles);
-            // longer rows take the whole wave.
-            const size_t per = cols < T::kLanesNarrowBelowCols ? T::kLanesDivNarrow
-                               : (cols % 4 == 0 && cols >= T::kLanesWholeVecFromCols &&
-                                  cols % T::kLanesWholeVecEvenCols == 0) ? T::kLanesDivWholeVec
-                                                                          : T::kLanesDivOther;
-            int lg = 0;
-            while (lg < 6 && ((size_t)2 << lg) <= cols / per) ++lg;
-            L.staged_log2s = cols > T::kWholeWaveAboveCols ? 6 : lg;
-        }
-        // Tile size: 16-byte vectors per lane (4, 8 or 16, at least base_u
-        // so that a tile holds one aligned span of rows).
-        const size_t pass = (size_t)64 >> L.staged_log2s;  // rows reduced at a time
         // Rows per tile: dense, a whole number of aligned spans in 256 * u
         // elements; otherwise as many rows as fit with room for a span that
         // starts 3 elements into its first vector.
@@ -526,6 +494,51 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             if (whole_lines && (256 * u) / (32 * cols) >= 1) return (256 * u) / (32 * cols) * 32;
             return (256 * u) / (fold * cols) * fold;
         };
+        // Lanes per row first: the tile size below depends on them.
+        bool lanes_by_tile = false;
+        if (p.short_rows >= 10) {  // vector reads (rows of whole vectors), 2^(short_rows - 10) lanes
+            L.staged_log2s = p.short_rows - 10;
+            L.staged_vread = vec_rows ? 1 : 0;
+        } else if (p.short_rows >= 3) {
+            L.staged_log2s = p.short_rows - 3;
+        } else if (vread_default) {
+            // Rows of up to 16 whole vectors: 16-byte reads from LDS, one lane
+            // per 2 vectors of the row (per 4 from 16 vectors). Element reads
+            // at a stride of cols words put the rows of a pass on the same
+            // LDS banks (8-32 floats: 5.1-5.5 -> 5.4-5.9 TB/s).
+            const size_t v = cols / 4, per = v >= 16 ? 4 : 2;
+            int lg = 0;
+            while (((size_t)2 << lg) <= v / per) ++lg;
+            L.staged_log2s = lg;
+            L.staged_vread = 1;
+        } else if (pol == nullptr && cols >= T::kLanesByTileFromCols && cols <= T::kWholeWaveAboveCols) {
+            // Rows of 513-1023 floats: lanes per row by the rows R that a
+            // 4096-float tile holds, so that few of a tile's row slots go
+            // unused and the passes are few.
+            const size_t r16 = tile_rows(16);
+            const int lg = r16 >= 7   ? 4
+                           : r16 == 6 ? (cols < T::kLanesSixRowsWideFromCols ? 3 : 5)
+                           : r16 == 5 ? 3
+                           : r16 == 4 ? (cols < T::kLanesFourRowsWideFromCols ? 4 : 5)
+                                      : 5;
+            L.staged_log2s = lg;
+            lanes_by_tile = true;
+        } else {
+            // Lanes per row: the largest power of two up to cols / 8 below
+            // 32 floats (1024-float tiles), cols / 24 from there, or cols / 16
+            // for rows of whole vectors from 128 floats (4096-float tiles);
+            // longer rows take the whole wave.
+            const size_t per = cols < T::kLanesNarrowBelowCols ? T::kLanesDivNarrow
+                               : (cols % 4 == 0 && cols >= T::kLanesWholeVecFromCols &&
+                                  cols % T::kLanesWholeVecEvenCols == 0) ? T::kLanesDivWholeVec
+                                                                          : T::kLanesDivOther;
+            int lg = 0;
+            while (lg < 6 && ((size_t)2 << lg) <= cols / per) ++lg;
+            L.staged_log2s = cols > T::kWholeWaveAboveCols ? 6 : lg;
+        }
+        // Tile size: 16-byte vectors per lane (4, 8 or 16, at least base_u
+        // so that a tile holds one aligned span of rows).
+        const size_t pass = (size_t)64 >> L.staged_log2s;  // rows reduced at a time
         auto pass_use = [&](size_t u) {  // share of the passes' row slots that hold a row
             const size_t r = tile_rows(u);
             return r == 0 ? 0.0 : (double)r / (double)(pass * ((r + pass - 1) / pass));
@@ -559,6 +572,11 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
                     u = c;
                 }
             max_blocks = u == 16 ? T::kStagedBigTileWaves : T::kStagedWaves;
+            // Rows of 513-1023 floats whose 4096-float tile holds fewer floats
+            // of rows than kStagedSparseTileFloats (odd widths to 583: four
+            // rows): 2048 waves.
+            if (lanes_by_tile && u == 16 && tile_rows(16) * step < T::kStagedSparseTileFloats)
+                max_blocks = T::kStagedWaves;
             // Rows of 33-39 floats: when 4096-float tiles leave no room to
             // hold the results in LDS but 2048-float tiles on 1024 waves do,
             // and their passes are within 5% as full, take those (1 GiB: sums

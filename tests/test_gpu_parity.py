@@ -614,7 +614,11 @@ ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023
               (1, 5000), (2, 1030), (7, 1031), (1, 16), (17, 16), (100_003, 16), (60_001, 7), (50_000, 6),
               (40_001, 25), (30_007, 12), (700, 1028), (300, 1100), (129, 4100), (257, 2052),
               (5000, 1020), (3000, 1025), (2000, 3001), (500, 300), (301, 276), (257, 148), (100, 372),
-              (77, 520), (65, 700), (33, 1000)]
+              (77, 520), (65, 700), (33, 1000),
+              # 513-1023 floats: lanes by the rows a 4096-float tile holds (8, 16 or 32),
+              # and four-row tiles of odd widths under 584 floats on 2048 waves
+              (301, 600), (257, 550), (129, 660), (97, 670), (203, 740), (99, 850), (77, 775),
+              (51, 935), (257, 515)]
 ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1, max_blocks=3, short_rows=1),
                 dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
                 dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0),
@@ -1332,7 +1336,7 @@ def test_full_rows_short_1gib():
     # identical.
     a, x = _load("rows_f32_65536x4096")
     flat = a.reshape(-1)
-    for cols in (1, 3, 4, 7, 12, 16, 17, 21, 32, 64, 100, 256, 1000, 1025, 3001):
+    for cols in (1, 3, 4, 7, 12, 16, 17, 21, 32, 64, 100, 256, 515, 600, 700, 850, 1000, 1025, 3001):
         rows = flat.size // cols
         say(f"red_rows_sum_f32 / red_rows_max_f32 rows_f32_65536x4096 as {rows}x{cols}, held and tile by tile")
         v = x.view(-1)[: rows * cols].view(rows, cols)
