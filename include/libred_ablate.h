@@ -240,7 +240,10 @@ typedef struct red_cols_policy {
  * prefetch and target_waves 2048; and on rows that do not start 16-byte
  * aligned (four columns per lane from shifted vectors), which use unroll 4,
  * width 2, prefetch and target_waves 1024 with at least 63 groups of four
- * columns, else unroll 8, prefetch and target_waves 2048. */
+ * columns, else unroll 8, prefetch and target_waves 2048; and on m-row views
+ * (see `fold`) of at most 320 blocks of 256 view columns whose default
+ * launch would leave too few row phases for the XCD grouping of `xcd` 0,
+ * which use unroll 4, prefetch and target_waves 1024. */
 void red_default_cols_policy(red_cols_policy *p);
 red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_cols_policy *p, hipStream_t stream);

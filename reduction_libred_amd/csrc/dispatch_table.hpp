@@ -332,6 +332,18 @@ constexpr size_t kLineBytes = 128;
 // At power-of-two pitches (contiguous 1, 4, 16, 32, 64, 256, 512, 1024, 4096
 // and 16384 columns, 1000 columns at ld 1024) grouping ran 5-7% slower.
 constexpr size_t kXcdGroupMinPhases = 8;
+// Folded views (m-row views of 256 or more columns) of at most this many
+// 256-column blocks whose default launch (512 waves) leaves too few row
+// phases to be grouped per XCD take 4 rows in flight on 1024 waves
+// (kFoldPhasesCols), which gives them 4 or more phases, grouped from 8. On
+// 1 GiB (sums and maxima, two builds alternating, medians of three
+// rounds), the 14 widths of 300-2500 columns it changed: +3.7% on
+// geometric mean (300: 6.3 / 6.4 -> 6.8 / 6.9, 388: 6.1 / 6.3 -> 6.8 / 6.6,
+// 1020: 6.2 / 6.3 -> 6.6 / 6.7, 1025: 6.3 / 6.4 -> 6.7 / 6.9 TB/s; 777
+// columns -1%). At 2700
+// columns (338 blocks) it ran 4.5% slower and at 3000 (375) 0-2% slower, so
+// wider views keep the default.
+constexpr size_t kFoldFewPhasesMaxBlocks = 320;
 // ... and only when rounding the phases down to a multiple of 8 keeps this
 // share of them: 300 contiguous columns (38 blocks per view row, 14 phases,
 // cut to 8) ran 16-25% slower grouped. Rounding up instead lost more where

@@ -291,6 +291,9 @@ constexpr libred::ColsPolicy kScalarCols = {8, 1, 2048, 0, 2, 0, 0, 0};
 static_assert(libred::table::kXcdGroupMinPhases >= (size_t)libred::kXcds, "a whole number of phases per XCD");
 constexpr libred::ColsPolicy kShiftWideCols = {4, 1, 1024, 0, 2, 1, 0, 0};
 constexpr libred::ColsPolicy kShiftNarrowCols = {8, 1, 2048, 0, 1, 1, 0, 0};
+// Folded views whose default launch leaves too few row phases to group the
+// blocks per XCD (kFoldFewPhasesMaxBlocks): 4 rows in flight, 1024 waves.
+constexpr libred::ColsPolicy kFoldPhasesCols = {4, 1, 1024, 0, 1, 1, 0, 0};
 
 libred::ColsPolicy to_cols(const red_cols_policy* p) {
     if (!p) return kDefaultCols;
@@ -900,6 +903,18 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     L.ngroups = 64;
     if (groups + spare < 64) L.ngroups = (unsigned int)(groups + spare);
     if (pol == nullptr && L.vec == 1 && L.ngroups == 64) p = kScalarCols;
+    if (pol == nullptr && L.fold_m > 1 && L.vec == 4 && !L.shift && L.ngroups == 64) {
+        // The default's row phases (one column block per 256 view columns),
+        // and whether they would be grouped per XCD as below.
+        const size_t ncb1 = (cols + 255) / 256;
+        const size_t ph = ((size_t)kDefaultCols.target_waves + ncb1 - 1) / ncb1;
+        const size_t dn = ph / libred::kXcds * libred::kXcds;
+        const size_t vpitch = cols * sizeof(float);
+        const bool grouped = dn >= libred::table::kXcdGroupMinPhases &&
+                             (double)dn >= libred::table::kXcdGroupKeepPhases * (double)ph;
+        if (!grouped && (vpitch & (vpitch - 1)) != 0 && ncb1 <= libred::table::kFoldFewPhasesMaxBlocks)
+            p = kFoldPhasesCols;
+    }
     if (pol == nullptr && L.shift) p = L.ngroups == 64 ? kShiftWideCols : kShiftNarrowCols;
     L.width = L.ngroups == 64 ? p.width : 1;
     if (!L.shift)

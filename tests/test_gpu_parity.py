@@ -757,6 +757,9 @@ COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260)
               (1000, 260, 260), (333, 516, 516), (41, 300, 300), (3001, 33, 33), (70, 65, 65), (63, 97, 97),
               (300, 1020, 1020), (129, 2040, 2040), (500, 1000, 1020), (77, 765, 765), (45, 1028, 1028),
               (1203, 255, 255), (31, 510, 514),
+              # 16-row views whose default launch leaves too few row phases to
+              # group per XCD: 4 rows in flight on 1024 waves
+              (3001, 1999, 1999), (1700, 2502, 2502),
               # rows not 16-byte aligned: four columns per lane from shifted
               # vectors, with and without a spare group per packed row, the
               # wide form's last block past a width of 252 columns per block
@@ -1387,6 +1390,32 @@ def test_full_cols_strided_1gib():
         assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), (cols, ld)
         assert np.array_equal(m.cpu().numpy(), oracle.cols_max_f32(mat)), (cols, ld)
         del mat
+    del x
+    torch.cuda.empty_cache()
+
+
+def test_full_cols_folded_1gib():
+    # The 1 GiB rows workload viewed as contiguous (2^28 // cols) x cols
+    # matrices that the column kernels read through 32- or 16-row views.
+    # Views of at most 320 blocks of 256 columns whose default launch has too
+    # few row phases to group per XCD (300, 1000, 1025 and 2500 columns in
+    # 32-row views, 2502 in 16-row views) take 4 rows in flight on 1024
+    # waves; 3000 columns keeps the default. Every column is compared with
+    # the oracle.
+    a, x = _load("rows_f32_65536x4096")
+    flat = a.reshape(-1)
+    for cols in (300, 1000, 1025, 2500, 2502, 3000):
+        rows = flat.size // cols
+        say(f"red_cols_sum_f32 / red_cols_max_f32 rows_f32_65536x4096 as {rows}x{cols}")
+        v = x.view(-1)[: rows * cols].view(rows, cols)
+        s = rl.red_cols_sum_f32(v)
+        m = rl.red_cols_max_f32(v)
+        torch.cuda.synchronize()
+        mat = flat[: rows * cols].reshape(rows, cols)
+        say(f"oracle cols {rows}x{cols}")
+        S, A = oracle.cols_sum_f32(mat)
+        assert sums_ok(s.cpu().numpy().astype(np.float64), S, A), cols
+        assert np.array_equal(m.cpu().numpy(), oracle.cols_max_f32(mat)), cols
     del x
     torch.cuda.empty_cache()
 
