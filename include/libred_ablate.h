@@ -243,7 +243,11 @@ typedef struct red_cols_policy {
  * columns, else unroll 8, prefetch and target_waves 2048; and on m-row views
  * (see `fold`) of at most 320 blocks of 256 view columns whose default
  * launch would leave too few row phases for the XCD grouping of `xcd` 0,
- * which use unroll 4, prefetch and target_waves 1024. */
+ * which use unroll 4, prefetch and target_waves 1024; and on unfolded
+ * rows of more than 8192 columns (at most 1024 blocks of 256, a pitch that
+ * is not a power of two bytes), which use unroll 4, width 2, no prefetch
+ * and target_waves 1024, unless the shape above would have its blocks
+ * grouped per XCD and this one would not. */
 void red_default_cols_policy(red_cols_policy *p);
 red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_cols_policy *p, hipStream_t stream);

@@ -344,6 +344,17 @@ constexpr size_t kXcdGroupMinPhases = 8;
 // columns (338 blocks) it ran 4.5% slower and at 3000 (375) 0-2% slower, so
 // wider views keep the default.
 constexpr size_t kFoldFewPhasesMaxBlocks = 320;
+// Unfolded rows of more than this many columns, up to kWideColBlocks blocks
+// of 256, at a pitch that is not a power of two bytes, take 4 rows in flight
+// with 2 KiB of a row per wave on 1024 waves (kUnfoldedWideCols). Multiples
+// of 32 there had 7-11 row phases under the default, too few to group per
+// XCD, and other widths took the short-wide shape. Sweep of 54 shapes on
+// 1 GiB, sums / maxima against those: 12000: +8.6 / +7.2%, 20000: +8.0 /
+// +5.8%, 100000: +5.3 / +6.4%, 8200: +4.8 / +0.6%, 9000: +4.7 / +1.9%, 10000:
+// +2.6 / +0.3%, 200000: +2.6 / +2.7%. Where the shape it replaces has its
+// blocks grouped per XCD and this one would not, the old shape stays (50000
+// columns: 21 phases grouped against 11 not, 6% slower).
+constexpr size_t kUnfoldedWideAboveCols = 8192;
 // ... and only when rounding the phases down to a multiple of 8 keeps this
 // share of them: 300 contiguous columns (38 blocks per view row, 14 phases,
 // cut to 8) ran 16-25% slower grouped. Rounding up instead lost more where

@@ -294,6 +294,9 @@ constexpr libred::ColsPolicy kShiftNarrowCols = {8, 1, 2048, 0, 1, 1, 0, 0};
 // Folded views whose default launch leaves too few row phases to group the
 // blocks per XCD (kFoldFewPhasesMaxBlocks): 4 rows in flight, 1024 waves.
 constexpr libred::ColsPolicy kFoldPhasesCols = {4, 1, 1024, 0, 1, 1, 0, 0};
+// Unfolded rows of more than kUnfoldedWideAboveCols columns (up to the
+// short-wide limit): 4 rows in flight, 2 KiB of a row per wave, 1024 waves.
+constexpr libred::ColsPolicy kUnfoldedWideCols = {4, 1, 1024, 0, 2, 0, 0, 0};
 
 libred::ColsPolicy to_cols(const red_cols_policy* p) {
     if (!p) return kDefaultCols;
@@ -886,6 +889,23 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // 3000 and 6000 columns ran 8-12% faster than with the default shape.
     if (pol == nullptr && L.vec == 4 && L.fold_m == 1 && cols % 32 != 0 && cols >= libred::table::kFoldWideFromCols)
         p = kWideCols;
+    // Whether a launch shape q (64 groups of four columns per block) would
+    // have its blocks grouped per XCD below (at xcd 0).
+    auto grouped_with = [&](const libred::ColsPolicy& q) {
+        const size_t pitch_b = ld * sizeof(float);
+        if (pitch_b == 0 || (pitch_b & (pitch_b - 1)) == 0) return false;
+        const size_t ncb_q = (cols + 256 * (size_t)q.width - 1) / (256 * (size_t)q.width);
+        size_t ph = ((size_t)q.target_waves + ncb_q - 1) / ncb_q;
+        const size_t by_rows = (rows + 7) / 8;
+        if (ph > by_rows) ph = by_rows;
+        const size_t dn = ph / libred::kXcds * libred::kXcds;
+        return dn >= libred::table::kXcdGroupMinPhases &&
+               (double)dn >= libred::table::kXcdGroupKeepPhases * (double)ph;
+    };
+    if (pol == nullptr && L.vec == 4 && L.fold_m == 1 && cols > libred::table::kUnfoldedWideAboveCols &&
+        cols / 256 <= libred::table::kWideColBlocks && ((ld * sizeof(float)) & (ld * sizeof(float) - 1)) != 0 &&
+        (grouped_with(kUnfoldedWideCols) || !grouped_with(p)))
+        p = kUnfoldedWideCols;
     // Narrow matrix: if the column groups divide a wave, pack several rows
     // into each load.
     // With shift, a packed row's last group reaches into the vector after
@@ -903,18 +923,10 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     L.ngroups = 64;
     if (groups + spare < 64) L.ngroups = (unsigned int)(groups + spare);
     if (pol == nullptr && L.vec == 1 && L.ngroups == 64) p = kScalarCols;
-    if (pol == nullptr && L.fold_m > 1 && L.vec == 4 && !L.shift && L.ngroups == 64) {
-        // The default's row phases (one column block per 256 view columns),
-        // and whether they would be grouped per XCD as below.
-        const size_t ncb1 = (cols + 255) / 256;
-        const size_t ph = ((size_t)kDefaultCols.target_waves + ncb1 - 1) / ncb1;
-        const size_t dn = ph / libred::kXcds * libred::kXcds;
-        const size_t vpitch = cols * sizeof(float);
-        const bool grouped = dn >= libred::table::kXcdGroupMinPhases &&
-                             (double)dn >= libred::table::kXcdGroupKeepPhases * (double)ph;
-        if (!grouped && (vpitch & (vpitch - 1)) != 0 && ncb1 <= libred::table::kFoldFewPhasesMaxBlocks)
-            p = kFoldPhasesCols;
-    }
+    if (pol == nullptr && L.fold_m > 1 && L.vec == 4 && !L.shift && L.ngroups == 64 &&
+        (cols + 255) / 256 <= libred::table::kFoldFewPhasesMaxBlocks &&
+        ((ld * sizeof(float)) & (ld * sizeof(float) - 1)) != 0 && !grouped_with(kDefaultCols))
+        p = kFoldPhasesCols;
     if (pol == nullptr && L.shift) p = L.ngroups == 64 ? kShiftWideCols : kShiftNarrowCols;
     L.width = L.ngroups == 64 ? p.width : 1;
     if (!L.shift)

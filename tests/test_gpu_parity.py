@@ -760,6 +760,10 @@ COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260)
               # 16-row views whose default launch leaves too few row phases to
               # group per XCD: 4 rows in flight on 1024 waves
               (3001, 1999, 1999), (1700, 2502, 2502),
+              # unfolded rows of more than 8192 columns: 4 rows in flight, 2 KiB of
+              # a row per wave, unless the shape it replaces is grouped per XCD
+              # and this one would not be
+              (9, 12000, 12000), (7, 9000, 9004), (40, 50000, 50000), (3, 100000, 100000),
               # rows not 16-byte aligned: four columns per lane from shifted
               # vectors, with and without a spare group per packed row, the
               # wide form's last block past a width of 252 columns per block
@@ -1400,11 +1404,13 @@ def test_full_cols_folded_1gib():
     # Views of at most 320 blocks of 256 columns whose default launch has too
     # few row phases to group per XCD (300, 1000, 1025 and 2500 columns in
     # 32-row views, 2502 in 16-row views) take 4 rows in flight on 1024
-    # waves; 3000 columns keeps the default. Every column is compared with
-    # the oracle.
+    # waves; 3000 columns keeps the default. Unfolded rows of more than 8192
+    # columns (12000, 100000) take 4 rows in flight with 2 KiB of a row per
+    # wave; 50000 keeps the short-wide shape, whose blocks are grouped per
+    # XCD. Every column is compared with the oracle.
     a, x = _load("rows_f32_65536x4096")
     flat = a.reshape(-1)
-    for cols in (300, 1000, 1025, 2500, 2502, 3000):
+    for cols in (300, 1000, 1025, 2500, 2502, 3000, 12000, 50000, 100000):
         rows = flat.size // cols
         say(f"red_cols_sum_f32 / red_cols_max_f32 rows_f32_65536x4096 as {rows}x{cols}")
         v = x.view(-1)[: rows * cols].view(rows, cols)
