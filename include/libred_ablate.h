@@ -241,7 +241,7 @@ typedef struct red_cols_policy {
  * aligned (four columns per lane from shifted vectors), which use unroll 4,
  * width 2, prefetch and target_waves 1024 with at least 63 groups of four
  * columns, else unroll 8, prefetch and target_waves 2048; and on m-row views
- * (see `fold`) of at most 320 blocks of 256 view columns whose default
+ * (see `fold`) of at most 224 blocks of 256 view columns whose default
  * launch would leave too few row phases for the XCD grouping of `xcd` 0,
  * which use unroll 4, prefetch and target_waves 1024; and on unfolded
  * rows of more than 8192 columns (at most 1024 blocks of 256, a pitch that

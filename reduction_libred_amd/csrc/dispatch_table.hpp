@@ -335,15 +335,14 @@ constexpr size_t kXcdGroupMinPhases = 8;
 // Folded views (m-row views of 256 or more columns) of at most this many
 // 256-column blocks whose default launch (512 waves) leaves too few row
 // phases to be grouped per XCD take 4 rows in flight on 1024 waves
-// (kFoldPhasesCols), which gives them 4 or more phases, grouped from 8. On
-// 1 GiB (sums and maxima, two builds alternating, medians of three
-// rounds), the 14 widths of 300-2500 columns it changed: +3.7% on
-// geometric mean (300: 6.3 / 6.4 -> 6.8 / 6.9, 388: 6.1 / 6.3 -> 6.8 / 6.6,
-// 1020: 6.2 / 6.3 -> 6.6 / 6.7, 1025: 6.3 / 6.4 -> 6.7 / 6.9 TB/s; 777
-// columns -1%). At 2700
-// columns (338 blocks) it ran 4.5% slower and at 3000 (375) 0-2% slower, so
-// wider views keep the default.
-constexpr size_t kFoldFewPhasesMaxBlocks = 320;
+// (kFoldPhasesCols), which gives them 5 or more phases, grouped from 8. On
+// 1 GiB (sums and maxima, medians of three alternating rounds), 22 such
+// widths of 276-1756 columns (35-220 blocks of their 32-row views): +3.6%
+// on geometric mean (340: 5.6 / 5.5 -> 6.2 / 6.4, 1052: 5.4 / 5.5 -> 6.0 /
+// 6.2, 1700: 5.4 / 5.4 -> 6.4 / 6.6 TB/s; worst 652 columns, -4 / -5%).
+// Over 20 widths of 1800-2556 columns (225-320 blocks) it came to -0.4%,
+// with 1900 and 2350 columns 9-11% slower, so wider views keep the default.
+constexpr size_t kFoldFewPhasesMaxBlocks = 224;
 // Unfolded rows of more than this many columns, up to kWideColBlocks blocks
 // of 256, at a pitch that is not a power of two bytes, take 4 rows in flight
 // with 2 KiB of a row per wave on 1024 waves (kUnfoldedWideCols). Multiples

@@ -1401,10 +1401,10 @@ def test_full_cols_strided_1gib():
 def test_full_cols_folded_1gib():
     # The 1 GiB rows workload viewed as contiguous (2^28 // cols) x cols
     # matrices that the column kernels read through 32- or 16-row views.
-    # Views of at most 320 blocks of 256 columns whose default launch has too
-    # few row phases to group per XCD (300, 1000, 1025 and 2500 columns in
-    # 32-row views, 2502 in 16-row views) take 4 rows in flight on 1024
-    # waves; 3000 columns keeps the default. Unfolded rows of more than 8192
+    # Views of at most 224 blocks of 256 columns whose default launch has too
+    # few row phases to group per XCD (300, 1000 and 1025 columns in 32-row
+    # views, 2502 in 16-row views) take 4 rows in flight on 1024 waves; 2500
+    # and 3000 columns keep the default. Unfolded rows of more than 8192
     # columns (12000, 100000) take 4 rows in flight with 2 KiB of a row per
     # wave; 50000 keeps the short-wide shape, whose blocks are grouped per
     # XCD. Every column is compared with the oracle.
