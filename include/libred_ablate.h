@@ -144,8 +144,9 @@ typedef struct red_flat_policy {
  * either way; and `max_fold`, how the LDS-staged kernel's maxima fold a
  * lane's elements: 1 = a compare and a select, 2 = a hardware max of the
  * canonicalized element (a signalling NaN is made quiet first, so a NaN
- * never wins either way), 0 = the library's choice (2 for rows of fewer
- * than 64 floats, else 1). The results are the same either way. */
+ * never wins either way) with up to 4 lanes per row, and the compare and
+ * select with more, 0 = the library's choice (2 for rows of fewer than 64
+ * floats, else 1). The results are the same either way. */
 typedef struct red_rows_policy {
     int block;
     int unroll;
@@ -162,7 +163,8 @@ typedef struct red_rows_policy {
 } red_rows_policy;
 
 /* Launch shape of the column kernels: `unroll` rows in flight per lane (1, 2,
- * 4, 8 or 16), `nontemporal`, `target_waves` (the rows are cut into chunks
+ * 4, 8 or 16), `nontemporal` (the shifted vectors described under `vec` are
+ * always loaded non-temporally), `target_waves` (the rows are cut into chunks
  * until about this many single-wave blocks run), `vec`: 0 = four adjacent
  * columns per lane: from one aligned 16-byte load per row when x is 16-byte
  * aligned and cols and ld are multiples of 4, or through an m-row view (see

@@ -427,12 +427,14 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
     auto* partials = static_cast<typename Op::acc_t*>(L.partials);
     const dim3 grid((unsigned int)(L.ncb * L.nchunks));
     typename Op::out_t* direct = (L.nchunks == 1 && L.fold_m <= 1 && L.rot == 0) ? out : nullptr;
-    if (nt)
+    // Shifted loads are built non-temporal only (the default of every shape
+    // that takes them), which halves their variants.
+    if (nt || SH)
         hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF, SH>), grid, dim3(kWave), 0, stream,
                            x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials, direct);
-    else
-        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF, SH>), grid, dim3(kWave), 0, stream,
-                           x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials, direct);
+    else if constexpr (!SH)
+        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF, false>), grid, dim3(kWave), 0,
+                           stream, x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials, direct);
     hipError_t e = hipGetLastError();
     const size_t W = kColsCombineBlock / kWave;
     if (e != hipSuccess) return e;

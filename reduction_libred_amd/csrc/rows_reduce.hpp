@@ -875,7 +875,10 @@ inline hipError_t rows_staged_go(const typename Op::elem_t* x, size_t rows, size
     // row shape): built only that way, which halves this kernel's variants.
     (void)nt;
     const int xm = L.xmap > 0 && L.grid % (kXcds * L.xmap) == 0 ? L.xmap : 0;
-    if constexpr (std::is_same_v<Op, MaxF32>) {
+    // The hardware max fold is built for up to 4 lanes per row (the default
+    // takes it with at most 2); wider segments fold with the compare and
+    // select, which gives the same results.
+    if constexpr (std::is_same_v<Op, MaxF32> && LOG2S <= 2) {
         if (L.staged_fmax) {
             if (L.staged_hold > 0)
                 hipLaunchKernelGGL((rows_staged_kernel<Op, LOG2S, U, true, VREAD, true, SPREAD, true>), dim3(L.grid),
