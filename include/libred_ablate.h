@@ -237,7 +237,9 @@ typedef struct red_cols_policy {
  * short-wide matrices (four columns per lane and cols / 256 > 1024, cols of
  * the m-row view when folded), and on unfolded matrices of at least 256
  * columns whose rows are not a whole number of 128-byte lines, which use
- * unroll 2, width 4, no prefetch and target_waves 1024; with one column
+ * unroll 2, width 4, no prefetch and target_waves 1024 (short-wide ones
+ * with their row phases rounded down so that the grid holds at most 1024
+ * blocks, and with the prefetch where it then holds at most 640); with one column
  * per lane and at least 64 columns, which use unroll 8, width 2, no
  * prefetch and target_waves 2048; and on rows that do not start 16-byte
  * aligned (four columns per lane from shifted vectors), which use unroll 4,

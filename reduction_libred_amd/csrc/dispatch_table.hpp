@@ -374,6 +374,17 @@ constexpr double kXcdGroupKeepPhases = 0.75;
 // take the wide shape (256 x 1M: 5.9 -> 7.1 TB/s; 1020, 1500, 3000, 6000
 // columns 8-12% faster).
 constexpr size_t kWideColBlocks = 1024;
+// The short-wide shape rounds its row phases down so that the grid holds at
+// most this many single-wave blocks (4 per CU); rounded up, 16385, 30001
+// and 50257 columns took 1028, 1407 and 1572. Where that leaves at most
+// kShortWidePrefetchMaxWaves blocks (about 2 per CU), the prefetch goes on.
+// On 1 GiB, two builds alternating (sums / maxima, medians of three
+// rounds): 20001: +4 / +4%, 24577: +8 / -3%, 30001: +9 / +8%, 50257: +10 /
+// +3%, 300000: +8 / +4%, 524292 (513 blocks, prefetch): +14 / +8%, 40003
+// (626 blocks, prefetch): 0 / -1%; without the prefetch 524292 and 40003
+// ran 6-29% slower.
+constexpr int kShortWideMaxWaves = 1024;
+constexpr int kShortWidePrefetchMaxWaves = 640;
 
 }  // namespace table
 }  // namespace libred

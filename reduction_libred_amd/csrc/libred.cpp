@@ -883,7 +883,8 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         L.vec = 4;
         L.shift = 1;
     }
-    if (pol == nullptr && L.vec == 4 && cols / 256 > libred::table::kWideColBlocks) p = kWideCols;
+    const bool short_wide = pol == nullptr && L.vec == 4 && cols / 256 > libred::table::kWideColBlocks;
+    if (short_wide) p = kWideCols;
     // Rows that are not a whole number of 128-byte lines (and not a folded
     // view) also read best 4 KiB at a time, 2 rows in flight: 1020, 1500,
     // 3000 and 6000 columns ran 8-12% faster than with the default shape.
@@ -945,6 +946,13 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         if (nchunks > by_scratch) nchunks = by_scratch;
         if (nchunks < 1) nchunks = 1;
     }
+    // The short-wide shape keeps its grid within kShortWideMaxWaves
+    // single-wave blocks (row phases rounded down, not up), with the
+    // prefetch on where that leaves kShortWidePrefetchMaxWaves or fewer.
+    if (short_wide && L.ncb <= (size_t)libred::table::kShortWideMaxWaves &&
+        L.ncb * nchunks > (size_t)libred::table::kShortWideMaxWaves)
+        nchunks = (size_t)libred::table::kShortWideMaxWaves / L.ncb;
+    if (short_wide && L.ncb * nchunks <= (size_t)libred::table::kShortWidePrefetchMaxWaves) p.prefetch = 1;
     // Blocks grouped per XCD (see ColsLaunch::xmap and
     // kXcdGroupMinPhases): a whole number of phases per XCD, rounded down
     // (kXcdGroupKeepPhases).

@@ -764,6 +764,9 @@ COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260)
               # a row per wave, unless the shape it replaces is grouped per XCD
               # and this one would not be
               (9, 12000, 12000), (7, 9000, 9004), (40, 50000, 50000), (3, 100000, 100000),
+              # short-wide views: row phases rounded down to at most 1024 blocks,
+              # with the prefetch where that leaves at most 640
+              (272, 30001, 30001), (20, 524292, 524292), (300, 50257, 50257),
               # rows not 16-byte aligned: four columns per lane from shifted
               # vectors, with and without a spare group per packed row, the
               # wide form's last block past a width of 252 columns per block
