@@ -251,7 +251,9 @@ typedef struct red_cols_policy {
  * rows of more than 8192 columns (at most 1024 blocks of 256, a pitch that
  * is not a power of two bytes), which use unroll 4, width 2, no prefetch
  * and target_waves 1024, unless the shape above would have its blocks
- * grouped per XCD and this one would not. */
+ * grouped per XCD and this one would not (with 128 or more blocks per
+ * phase, their phases are rounded down where that keeps at least 864
+ * blocks, or leaves at most 640, then with the prefetch). */
 void red_default_cols_policy(red_cols_policy *p);
 red_status red_cols_sum_f32_with(const float *x, size_t rows, size_t cols, size_t ld, float *out,
                                  const red_cols_policy *p, hipStream_t stream);

@@ -385,6 +385,18 @@ constexpr size_t kWideColBlocks = 1024;
 // ran 6-29% slower.
 constexpr int kShortWideMaxWaves = 1024;
 constexpr int kShortWidePrefetchMaxWaves = 640;
+// The unfolded-wide shape (kUnfoldedWideAboveCols) with at least this many
+// blocks per phase rounds its phases down too, where the rounded grid keeps
+// at least kUnfoldedRoundMinWaves blocks (or leaves at most
+// kShortWidePrefetchMaxWaves, with the prefetch). Sums / maxima against
+// rounding up: 100000 columns (980 blocks): +9 / +9%, 150000 (879): +7 /
+// +6%, 250000 (978): +6 / +7%, 262148 (513, prefetch): +15 / +15%. At 704
+// and 782 blocks (180000, 200000 columns) it ran 2-12% slower without the
+// prefetch and 0-3% faster or 7-9% slower with it, so those keep their
+// grids; with fewer blocks per phase (24000 columns, 47 blocks in 21
+// phases) the maxima ran 9% slower.
+constexpr size_t kUnfoldedRoundMinBlocks = 128;
+constexpr size_t kUnfoldedRoundMinWaves = 864;
 
 }  // namespace table
 }  // namespace libred

@@ -883,7 +883,7 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         L.vec = 4;
         L.shift = 1;
     }
-    const bool short_wide = pol == nullptr && L.vec == 4 && cols / 256 > libred::table::kWideColBlocks;
+    const bool short_wide = pol == nullptr && L.vec == 4 && !L.shift && cols / 256 > libred::table::kWideColBlocks;
     if (short_wide) p = kWideCols;
     // Rows that are not a whole number of 128-byte lines (and not a folded
     // view) also read best 4 KiB at a time, 2 rows in flight: 1020, 1500,
@@ -903,10 +903,12 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         return dn >= libred::table::kXcdGroupMinPhases &&
                (double)dn >= libred::table::kXcdGroupKeepPhases * (double)ph;
     };
-    if (pol == nullptr && L.vec == 4 && L.fold_m == 1 && cols > libred::table::kUnfoldedWideAboveCols &&
-        cols / 256 <= libred::table::kWideColBlocks && ((ld * sizeof(float)) & (ld * sizeof(float) - 1)) != 0 &&
-        (grouped_with(kUnfoldedWideCols) || !grouped_with(p)))
-        p = kUnfoldedWideCols;
+    const bool unfolded_wide = pol == nullptr && L.vec == 4 && !L.shift && L.fold_m == 1 &&
+                               cols > libred::table::kUnfoldedWideAboveCols &&
+                               cols / 256 <= libred::table::kWideColBlocks &&
+                               ((ld * sizeof(float)) & (ld * sizeof(float) - 1)) != 0 &&
+                               (grouped_with(kUnfoldedWideCols) || !grouped_with(p));
+    if (unfolded_wide) p = kUnfoldedWideCols;
     // Narrow matrix: if the column groups divide a wave, pack several rows
     // into each load.
     // With shift, a packed row's last group reaches into the vector after
@@ -953,6 +955,20 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         L.ncb * nchunks > (size_t)libred::table::kShortWideMaxWaves)
         nchunks = (size_t)libred::table::kShortWideMaxWaves / L.ncb;
     if (short_wide && L.ncb * nchunks <= (size_t)libred::table::kShortWidePrefetchMaxWaves) p.prefetch = 1;
+    // The unfolded-wide shape does the same with few phases of many blocks,
+    // but only where the rounded grid keeps kUnfoldedRoundMinWaves blocks or
+    // leaves at most kShortWidePrefetchMaxWaves (then with the prefetch).
+    if (unfolded_wide && L.ncb >= libred::table::kUnfoldedRoundMinBlocks &&
+        L.ncb <= (size_t)libred::table::kShortWideMaxWaves &&
+        L.ncb * nchunks > (size_t)libred::table::kShortWideMaxWaves) {
+        const size_t down = (size_t)libred::table::kShortWideMaxWaves / L.ncb;
+        if (L.ncb * down >= libred::table::kUnfoldedRoundMinWaves) {
+            nchunks = down;
+        } else if (L.ncb * down <= (size_t)libred::table::kShortWidePrefetchMaxWaves) {
+            nchunks = down;
+            p.prefetch = 1;
+        }
+    }
     // Blocks grouped per XCD (see ColsLaunch::xmap and
     // kXcdGroupMinPhases): a whole number of phases per XCD, rounded down
     // (kXcdGroupKeepPhases).

@@ -767,6 +767,9 @@ COL_SHAPES = [(1, 1, 1), (3, 5, 5), (100, 7, 9), (1000, 64, 64), (257, 256, 260)
               # short-wide views: row phases rounded down to at most 1024 blocks,
               # with the prefetch where that leaves at most 640
               (272, 30001, 30001), (20, 524292, 524292), (300, 50257, 50257),
+              # unfolded wide rows with few phases of many blocks: rounded down
+              # (980 blocks), or to 513 blocks with the prefetch
+              (48, 100000, 100000), (16, 262148, 262148),
               # rows not 16-byte aligned: four columns per lane from shifted
               # vectors, with and without a spare group per packed row, the
               # wide form's last block past a width of 252 columns per block
