@@ -890,8 +890,10 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     // 3000 and 6000 columns ran 8-12% faster than with the default shape.
     if (pol == nullptr && L.vec == 4 && L.fold_m == 1 && cols % 32 != 0 && cols >= libred::table::kFoldWideFromCols)
         p = kWideCols;
-    // Whether a launch shape q (64 groups of four columns per block) would
-    // have its blocks grouped per XCD below (at xcd 0).
+    // Whether a launch shape q would have its blocks grouped per XCD below
+    // (at xcd 0), for rows of 64 groups of four columns per block (8 rows
+    // per phase at least; the scratch cap on the phases, far above the
+    // phases these shapes reach, is left out).
     auto grouped_with = [&](const libred::ColsPolicy& q) {
         const size_t pitch_b = ld * sizeof(float);
         if (pitch_b == 0 || (pitch_b & (pitch_b - 1)) == 0) return false;
