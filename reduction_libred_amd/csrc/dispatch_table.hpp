@@ -145,6 +145,20 @@ constexpr int kStagedWaves = 2048;
 // with 16 (two passes, the second 1/4 or 1/2 full), 10-20% slower than 8
 // lanes, and R = 4 with 32 from 768 floats, 3-8% slower than 16 below 900.
 constexpr size_t kLanesByTileFromCols = 513;
+// Rows of kLanesFourFromCols to 512 floats that are not a multiple of 16
+// and whose 4096-float tile holds kLanesFourMinRows to kLanesFourMaxRows
+// rows (12 only below kLanesFourMaxRowsBelowCols floats) take 4 lanes per
+// row: one pass of up to 16 rows, where cols / 24 lanes (8) took two, the
+// second a quarter to a half full. On 1 GiB, two builds alternating (sums /
+// maxima): 259: +15 / +22%, 283: +16 / +17%, 314: +15 / +15%, 342: +12 /
+// +15%, 350: +14 / +13%, 378: +14 / +20%, 380: +16 / +20%, 33 shapes of
+// 259-480 floats +6.6% on geometric mean. With 12 rows from 320 floats
+// (324-340) the maxima ran 1-5% slower for sums 0-4% faster, so those keep
+// their lanes, as do the multiples of 16.
+constexpr size_t kLanesFourFromCols = 257;
+constexpr size_t kLanesFourMinRows = 10;
+constexpr size_t kLanesFourMaxRows = 12;
+constexpr size_t kLanesFourMaxRowsBelowCols = 320;
 constexpr size_t kLanesSixRowsWideFromCols = 640;
 constexpr size_t kLanesFourRowsWideFromCols = 900;
 // ... and where such a tile's rows span fewer floats than this (odd widths up

@@ -517,6 +517,14 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
             while (((size_t)2 << lg) <= v / per) ++lg;
             L.staged_log2s = lg;
             L.staged_vread = 1;
+        } else if (pol == nullptr && cols >= T::kLanesFourFromCols && cols < T::kLanesByTileFromCols &&
+                   cols % T::kLanesWholeVecEvenCols != 0 && tile_rows(16) >= T::kLanesFourMinRows &&
+                   (tile_rows(16) < T::kLanesFourMaxRows ||
+                    (tile_rows(16) == T::kLanesFourMaxRows && cols < T::kLanesFourMaxRowsBelowCols))) {
+            // Rows of 257-511 floats whose 4096-float tile holds 10-12 rows:
+            // 4 lanes per row reduce them in one pass (cols / 24 lanes took
+            // two, the second a quarter to a half full).
+            L.staged_log2s = 2;
         } else if (pol == nullptr && cols >= T::kLanesByTileFromCols && cols <= T::kWholeWaveAboveCols) {
             // Rows of 513-1023 floats: lanes per row by the rows R that a
             // 4096-float tile holds, so that few of a tile's row slots go
