@@ -155,6 +155,16 @@ constexpr size_t kLanesByTileFromCols = 513;
 // 259-480 floats +6.6% on geometric mean. With 12 rows from 320 floats
 // (324-340) the maxima ran 1-5% slower for sums 0-4% faster, so those keep
 // their lanes, as do the multiples of 16.
+// In the tile rule for rows of kThinPassFromCols to 512 floats, a tile
+// that takes more than one pass with its last at most 1 / kThinPassDivisor
+// full yields to the largest smaller tile that takes one pass or fills its
+// last better, on 2048 waves. From the sweep of every width (sums and
+// maxima against the tile rule's choice, the same lanes): 24 widths changed,
+// +9.1% on geometric mean (odd 171-191 floats, 4 lanes, 4096-float tiles
+// of 20 rows, passes of 16 and 4 -> 2048-float tiles of 8: +10 to +24%;
+// 120 floats: +11%); 112 floats 4-5% slower, every other width faster.
+constexpr size_t kThinPassFromCols = 40;
+constexpr size_t kThinPassDivisor = 4;
 constexpr size_t kLanesFourFromCols = 257;
 constexpr size_t kLanesFourMinRows = 10;
 constexpr size_t kLanesFourMaxRows = 12;

@@ -586,6 +586,24 @@ red_status rows_call(const float* x, size_t rows, size_t cols, size_t ld, float*
                     u = c;
                 }
             max_blocks = u == 16 ? T::kStagedBigTileWaves : T::kStagedWaves;
+            // A tile that takes more than one pass, the last at most a quarter
+            // full, yields to the largest smaller one that takes one pass or
+            // fills its last better (on 2048 waves), for rows of
+            // kThinPassFromCols to 512 floats.
+            auto thin_last_pass = [&](size_t c) {
+                const size_t r = tile_rows(c);
+                if (r == 0) return false;
+                const size_t n = (r + pass - 1) / pass, last = r - (n - 1) * pass;
+                return n > 1 && last * T::kThinPassDivisor <= pass;
+            };
+            if (cols >= T::kThinPassFromCols && cols < T::kLanesByTileFromCols && thin_last_pass(u)) {
+                for (size_t c : {(size_t)8, (size_t)4})
+                    if (c < u && c >= base_u && tile_rows(c) > 0 && !thin_last_pass(c)) {
+                        u = c;
+                        max_blocks = T::kStagedWaves;
+                        break;
+                    }
+            }
             // Rows of 513-1023 floats whose 4096-float tile holds fewer floats
             // of rows than kStagedSparseTileFloats (odd widths to 583: four
             // rows): 2048 waves.

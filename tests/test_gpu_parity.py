@@ -620,7 +620,10 @@ ROW_SHAPES = [(70_001, 1), (33_333, 2), (20_011, 4), (2047, 1), (2048, 1), (1023
               (301, 600), (257, 550), (129, 660), (97, 670), (203, 740), (99, 850), (77, 775),
               (51, 935), (257, 515),
               # 257-511 floats whose 4096-float tile holds 10-12 rows: 4 lanes per row
-              (301, 283), (257, 350), (129, 344), (77, 316)]
+              (301, 283), (257, 350), (129, 344), (77, 316),
+              # a 4096-float tile whose last pass is at most a quarter full yields
+              # to a smaller one (2048- or 1024-float tiles on 2048 waves)
+              (301, 173), (200, 120), (150, 304), (333, 55)]
 ROW_POLICIES = (None, dict(prefetch=1, short_rows=1), dict(prefetch=1, unroll=1, max_blocks=3, short_rows=1),
                 dict(prefetch=1, block=256, unroll=4, max_blocks=2, nontemporal=0, short_rows=1),
                 dict(short_rows=1), dict(max_blocks=3), dict(max_blocks=1, nontemporal=0),
@@ -1351,7 +1354,8 @@ def test_full_rows_short_1gib():
     # identical.
     a, x = _load("rows_f32_65536x4096")
     flat = a.reshape(-1)
-    for cols in (1, 3, 4, 7, 12, 16, 17, 21, 32, 64, 100, 256, 283, 378, 515, 600, 700, 850, 1000, 1025, 3001):
+    for cols in (1, 3, 4, 7, 12, 16, 17, 21, 32, 64, 100, 120, 173, 256, 283, 378, 515, 600, 700, 850, 1000, 1025,
+                 3001):
         rows = flat.size // cols
         say(f"red_rows_sum_f32 / red_rows_max_f32 rows_f32_65536x4096 as {rows}x{cols}, held and tile by tile")
         v = x.view(-1)[: rows * cols].view(rows, cols)
