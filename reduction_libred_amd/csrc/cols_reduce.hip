@@ -32,15 +32,27 @@ struct ColVec<4, Op> {
     using type = typename Op::vec_t;
 };
 
-template <class Op, int VEC>
+// One element into a column's accumulator. With FMAX (maxima only) the fold
+// is a hardware max of the canonicalized element (a signalling NaN is made
+// quiet first, so a NaN never wins; between -0 and +0 either may remain, as
+// the max rule allows) instead of a compare and a select.
+template <class Op, bool FMAX>
+__device__ __forceinline__ typename Op::acc_t col_combine(typename Op::acc_t a, typename Op::elem_t e) {
+    if constexpr (FMAX)
+        return __builtin_fmaxf(a, __builtin_canonicalizef(e));
+    else
+        return Op::combine(a, Op::lift(e, 0));
+}
+
+template <class Op, int VEC, bool FMAX = false>
 __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typename ColVec<VEC, Op>::type v) {
     if constexpr (VEC == 1) {
-        acc[0] = Op::combine(acc[0], Op::lift(v, 0));
+        acc[0] = col_combine<Op, FMAX>(acc[0], v);
     } else {
-        acc[0] = Op::combine(acc[0], Op::lift(v.x, 0));
-        acc[1] = Op::combine(acc[1], Op::lift(v.y, 0));
-        acc[2] = Op::combine(acc[2], Op::lift(v.z, 0));
-        acc[3] = Op::combine(acc[3], Op::lift(v.w, 0));
+        acc[0] = col_combine<Op, FMAX>(acc[0], v.x);
+        acc[1] = col_combine<Op, FMAX>(acc[1], v.y);
+        acc[2] = col_combine<Op, FMAX>(acc[2], v.z);
+        acc[3] = col_combine<Op, FMAX>(acc[3], v.w);
     }
 }
 
@@ -51,7 +63,7 @@ __device__ __forceinline__ void col_fold(typename Op::acc_t (&acc)[VEC], typenam
 // chain of conditionals on s the compiler branched on every element. The
 // vectors are reinterpreted whole (a bit cast of one vector component, as
 // in __builtin_bit_cast(uint32_t, v.y), compiled to a read of component 0).
-template <class Op>
+template <class Op, bool FMAX = false>
 __device__ __forceinline__ void col_fold_shift(typename Op::acc_t (&acc)[4], typename Op::vec_t v0,
                                                typename Op::vec_t v1, unsigned int s) {
     using elem_t = typename Op::elem_t;
@@ -64,7 +76,7 @@ __device__ __forceinline__ void col_fold_shift(typename Op::acc_t (&acc)[4], typ
         const uint32_t lo = (e[i + 1] & m1) | (e[i] & ~m1);      // element i + (s & 1)
         const uint32_t hi = (e[i + 3] & m1) | (e[i + 2] & ~m1);  // element i + 2 + (s & 1)
         const elem_t t = __builtin_bit_cast(elem_t, (hi & m2) | (lo & ~m2));
-        acc[i] = Op::combine(acc[i], Op::lift(t, 0));
+        acc[i] = col_combine<Op, FMAX>(acc[i], t);
     }
 }
 
@@ -112,7 +124,7 @@ __device__ __forceinline__ V next_lane_vec(V v, V after, unsigned int lane) {
 // holding the row's last column, so no load reaches past the matrix; the
 // first vector can begin before x, but only within the aligned vector
 // holding x[0]. Columns past cols, and spare groups, are never stored.
-template <class Op, int VEC, int CW, int UNROLL, bool NT, bool PREFETCH, bool SHIFT = false>
+template <class Op, int VEC, int CW, int UNROLL, bool NT, bool PREFETCH, bool SHIFT = false, bool FMAX = false>
 __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::elem_t* __restrict__ x,
                                                              size_t rows, size_t cols, size_t ld,
                                                              size_t ncb, unsigned int ngroups, size_t cspan,
@@ -198,7 +210,7 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
             if constexpr (SHIFT) {
 #pragma unroll
                 for (int w = 0; w < CW; ++w)
-                    col_fold_shift<Op>(acc[w], v0[w], next_lane_vec(v0[w], v0[w + 1 < CW ? w + 1 : w], lane), sh);
+                    col_fold_shift<Op, FMAX>(acc[w], v0[w], next_lane_vec(v0[w], v0[w + 1 < CW ? w + 1 : w], lane), sh);
             }
         };
         // Fold rows r, r + rpl, ... below rend. Groups of UNROLL rows; with
@@ -231,7 +243,7 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
                         fold_shift(b.v[u], b.s[u]);
                     } else {
 #pragma unroll
-                        for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], b.v[u][w]);
+                        for (int w = 0; w < CW; ++w) col_fold<Op, VEC, FMAX>(acc[w], b.v[u][w]);
                     }
                 }
             };
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(kWave) void cols_partial_kernel(const typename Op::
                     fold_shift(v0, sh);
                 } else {
 #pragma unroll
-                    for (int w = 0; w < CW; ++w) col_fold<Op, VEC>(acc[w], load_vec<NT>(p + off[w]));
+                    for (int w = 0; w < CW; ++w) col_fold<Op, VEC, FMAX>(acc[w], load_vec<NT>(p + off[w]));
                 }
             }
         };
@@ -427,14 +439,32 @@ static hipError_t cols_vwup(const typename Op::elem_t* x, size_t rows, size_t co
     auto* partials = static_cast<typename Op::acc_t*>(L.partials);
     const dim3 grid((unsigned int)(L.ncb * L.nchunks));
     typename Op::out_t* direct = (L.nchunks == 1 && L.fold_m <= 1 && L.rot == 0) ? out : nullptr;
+    // The hardware max fold is built for the shapes whose launches take it
+    // by default (folded views of fewer than 256 real columns: 8 rows in
+    // flight, one load per row, prefetch; short-wide matrices: 2 rows in
+    // flight, four loads per row); other shapes fold with the compare and
+    // select, which gives the same results.
+    bool launched = false;
+    if constexpr (std::is_same_v<Op, MaxF32> && VEC == 4 && !SH &&
+                  ((CW == 1 && UNROLL == 8 && PF) || (CW == 4 && UNROLL == 2))) {
+        if (L.col_fmax && nt) {
+            hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF, false, true>), grid, dim3(kWave), 0,
+                               stream, x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials,
+                               direct);
+            launched = true;
+        }
+    }
     // Shifted loads are built non-temporal only (the default of every shape
     // that takes them), which halves their variants.
-    if (nt || SH)
-        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF, SH>), grid, dim3(kWave), 0, stream,
-                           x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials, direct);
-    else if constexpr (!SH)
-        hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF, false>), grid, dim3(kWave), 0,
-                           stream, x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials, direct);
+    if (!launched) {
+        if (nt || SH)
+            hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, true, PF, SH>), grid, dim3(kWave), 0, stream,
+                               x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials, direct);
+        else if constexpr (!SH)
+            hipLaunchKernelGGL((cols_partial_kernel<Op, VEC, CW, UNROLL, false, PF, false>), grid, dim3(kWave), 0,
+                               stream, x, rows, cols, ld, L.ncb, L.ngroups, L.cspan, L.order, L.xmap, partials,
+                               direct);
+    }
     hipError_t e = hipGetLastError();
     const size_t W = kColsCombineBlock / kWave;
     if (e != hipSuccess) return e;

@@ -419,6 +419,13 @@ constexpr int kShortWidePrefetchMaxWaves = 640;
 // prefetch and 0-3% faster or 7-9% slower with it, so those keep their
 // grids; with fewer blocks per phase (24000 columns, 47 blocks in 21
 // phases) the maxima ran 9% slower.
+// Column maxima fold with a hardware max of the canonicalized element
+// instead of a compare and a select in folded views of fewer than this many
+// real columns and in short-wide matrices. Two builds alternating, 1 GiB,
+// maxima: 7 columns +5%, 17: +8%, 33: +3%, 65: +4%, 100: +4%, 50257: +6%;
+// at 260, 1000, 1025, 4096 and 100000 columns it ran 1-1.5% slower, so
+// those keep the compare and select.
+constexpr size_t kColsFmaxBelowCols = 256;
 constexpr size_t kUnfoldedRoundMinBlocks = 128;
 constexpr size_t kUnfoldedRoundMinWaves = 864;
 

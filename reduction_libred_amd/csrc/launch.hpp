@@ -162,6 +162,9 @@ struct ColsLaunch {
     // 1: the blocks on each XCD take all column blocks of consecutive phases
     // (nchunks a multiple of kXcds); 0: column block b mod ncb, phase b / ncb.
     int xmap;
+    // 1: maxima fold with the hardware max (see cols_partial_kernel's FMAX),
+    // where the launch shape has that variant.
+    int col_fmax;
 };
 
 bool flat_policy_supported(const FlatPolicy& p);

@@ -862,6 +862,7 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
     L.order = 0;
     L.shift = 0;
     L.xmap = 0;
+    L.col_fmax = 0;
     // A contiguous matrix may be viewed with m consecutive rows as one row
     // of m * cols columns (see fold_rows): for a width that is not a
     // multiple of 4 this makes every view row start 16-byte aligned, so four
@@ -959,6 +960,11 @@ red_status cols_call(const float* x, size_t rows, size_t cols, size_t ld, float*
         ((ld * sizeof(float)) & (ld * sizeof(float) - 1)) != 0 && !grouped_with(kDefaultCols))
         p = kFoldPhasesCols;
     if (pol == nullptr && L.shift) p = L.ngroups == 64 ? kShiftWideCols : kShiftNarrowCols;
+    // Maxima of folded views of fewer than kColsFmaxBelowCols real columns
+    // and of short-wide matrices fold with the hardware max.
+    if (pol == nullptr && L.vec == 4 && !L.shift &&
+        ((L.fold_m > 1 && L.real_cols < libred::table::kColsFmaxBelowCols) || short_wide))
+        L.col_fmax = 1;
     L.width = L.ngroups == 64 ? p.width : 1;
     if (!L.shift)
         L.cspan = (size_t)L.ngroups * L.vec * L.width;

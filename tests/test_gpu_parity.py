@@ -914,6 +914,29 @@ def test_rows_nonfinite(rows, cols, ld):
         assert np.array_equal(m_.cpu().numpy(), M), p
 
 
+def test_cols_signalling_nan():
+    # Signalling NaNs (quiet bit clear, either sign) never win a column's max,
+    # with the hardware max fold (folded views of fewer than 256 columns and
+    # short-wide matrices) and with the compare and select; a column of
+    # signalling NaNs only gives -inf.
+    snans = np.array([0x7F800001, 0x7FA00000, 0xFF800123, 0x7FBFFFFF], np.uint32)
+    for rows, cols in ((4000, 7), (3000, 17), (2000, 100), (600, 260), (40, 50257), (300, 4096)):
+        rng = np.random.default_rng(rows * 3 + cols)
+        a = rng.standard_normal((rows, cols)).astype(np.float32)
+        bits = a.view(np.uint32)
+        k = max(1, rows * cols // 50)
+        idx = rng.choice(rows * cols, size=k, replace=False)
+        bits.reshape(-1)[idx] = snans[np.arange(k) % snans.size]
+        bits[:, 3] = snans[np.arange(rows) % snans.size]          # a column of signalling NaNs only
+        M = oracle.cols_max_f32(a)
+        assert M[3] == -np.inf and not np.isnan(M).any()
+        for p in (None, dict(unroll=2, width=4), dict(fold=1)):
+            say(f"cols signalling NaN {rows}x{cols} policy={p}")
+            m = rl.red_cols_max_f32(torch.from_numpy(a).to(DEV), policy=p)
+            torch.cuda.synchronize()
+            assert np.array_equal(m.cpu().numpy(), M), (rows, cols, p)
+
+
 def test_rows_signalling_nan():
     # Signalling NaNs (quiet bit clear, either sign) never win a row's max,
     # whichever way the kernel folds the row (compare-and-select, or a
